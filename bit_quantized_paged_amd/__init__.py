@@ -1,0 +1,204 @@
+"""NVFP4-quantised paged KV cache for AMD Instinct MI355X (gfx950).
+
+Thin ctypes binding of ``libnvfp4kv.so`` (built from ``csrc/`` by
+``bit_quantized_paged_amd.build``). The functions here only marshal torch
+tensors (device memory and the current HIP stream) into the C ABI declared in
+``include/nvfp4kv.h``; every step of the computation runs in the HIP kernels.
+There is no CPU fallback: without the built library every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "NVFP4KVError", "library", "full_dim", "alloc_pool", "append", "dequant_paged",
+    "decode_workspace_size", "paged_attention_decode", "paged_attention_prefill",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnvfp4kv.so")
+
+EXPORTS = [
+    "nvfp4_kv_full_dim", "nvfp4_kv_append", "nvfp4_kv_dequant_paged",
+    "nvfp4_paged_attention_decode_workspace_size", "nvfp4_paged_attention_decode",
+    "nvfp4_paged_attention_prefill", "nvfp4kv_status_string", "nvfp4kv_last_error",
+]
+
+
+class NVFP4KVError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"nvfp4kv status {status}: {message}")
+        self.status = status
+
+
+class CacheDesc(ctypes.Structure):
+    _fields_ = [
+        ("data", ctypes.c_void_p), ("num_blocks", ctypes.c_int64), ("block_size", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32), ("head_size", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("stride_block", ctypes.c_int64), ("stride_kv", ctypes.c_int64), ("stride_token", ctypes.c_int64),
+        ("stride_head", ctypes.c_int64),
+    ]
+
+
+_lib = None
+_P, _I32, _I64, _F32, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+_DESC = ctypes.POINTER(CacheDesc)
+
+
+def library():
+    """The loaded libnvfp4kv.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m bit_quantized_paged_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        sig = {
+            "nvfp4_kv_full_dim": (_I32, [_I32]),
+            "nvfp4_kv_append": (_I32, [_DESC, _P, _I64, _I64, _P, _I64, _I64, _P, _I64, _P, _P, _P]),
+            "nvfp4_kv_dequant_paged": (_I32, [_DESC, _P, _I32, _P, _P, _I32, _I32, _P, _P, _P, _P, _I64, _P]),
+            "nvfp4_paged_attention_decode_workspace_size": (_SZ, [_I32, _I32, _I32, _I32]),
+            "nvfp4_paged_attention_decode": (_I32, [_DESC, _P, _I64, _I64, _I32, _P, _I32, _P, _I32, _I32, _P, _P,
+                                                    _F32, _P, _P, _SZ, _P]),
+            "nvfp4_paged_attention_prefill": (_I32, [_DESC, _P, _I64, _I64, _I32, _P, _I32, _I32, _P, _I32, _P, _I32,
+                                                     _I32, _P, _P, _F32, _I32, _P, _P, _SZ, _P]),
+            "nvfp4kv_status_string": (ctypes.c_char_p, [_I32]),
+            "nvfp4kv_last_error": (ctypes.c_char_p, []),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        lib = library()
+        raise NVFP4KVError(status, lib.nvfp4kv_last_error().decode() or lib.nvfp4kv_status_string(status).decode())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _dev(t, name, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def full_dim(head_size: int) -> int:
+    return int(library().nvfp4_kv_full_dim(head_size))
+
+
+def alloc_pool(num_blocks: int, block_size: int, num_kv_heads: int, head_size: int,
+               layout: str = "HND", device="cuda") -> torch.Tensor:
+    """Zeroed uint8 pool, returned as the logical view (num_blocks, 2,
+    block_size, num_kv_heads, full_dim). ``layout`` picks the physical order:
+    "HND" stores (num_blocks, 2, num_kv_heads, block_size, full_dim)."""
+    fd = head_size // 2 + head_size // 16
+    if layout == "HND":
+        return torch.zeros((num_blocks, 2, num_kv_heads, block_size, fd), dtype=torch.uint8,
+                           device=device).permute(0, 1, 3, 2, 4)
+    if layout == "NHD":
+        return torch.zeros((num_blocks, 2, block_size, num_kv_heads, fd), dtype=torch.uint8, device=device)
+    raise ValueError(layout)
+
+
+def _desc(pool: torch.Tensor) -> CacheDesc:
+    _dev(pool, "pool", torch.uint8)
+    if pool.dim() != 5 or pool.shape[1] != 2 or pool.stride(4) != 1:
+        raise ValueError("pool must be a (num_blocks, 2, block_size, num_kv_heads, full_dim) uint8 view "
+                         "with a contiguous last axis")
+    nb, _, bs, hkv, fd = pool.shape
+    D = fd * 16 // 9
+    if D // 2 + D // 16 != fd:
+        raise ValueError(f"last axis {fd} is not a packed NVFP4 row width")
+    st = pool.stride()
+    return CacheDesc(pool.data_ptr(), nb, bs, hkv, D, 0, st[0], st[1], st[2], st[3])
+
+
+def append(pool, key, value, slot_mapping, k_scale, v_scale) -> None:
+    """Quantise bf16 key/value [N, Hkv, D] into the pool at slot_mapping (int64 [N])."""
+    _dev(key, "key", torch.bfloat16)
+    _dev(value, "value", torch.bfloat16)
+    _dev(slot_mapping, "slot_mapping", torch.int64)
+    _dev(k_scale, "k_scale", torch.float32)
+    _dev(v_scale, "v_scale", torch.float32)
+    if key.stride(-1) != 1 or value.stride(-1) != 1 or not slot_mapping.is_contiguous():
+        raise ValueError("key/value need a contiguous last axis and slot_mapping must be contiguous")
+    d = _desc(pool)
+    n = key.shape[0]
+    _check(library().nvfp4_kv_append(ctypes.byref(d), _ptr(key), key.stride(0), key.stride(1), _ptr(value),
+                                      value.stride(0), value.stride(1), _ptr(slot_mapping), n, _ptr(k_scale),
+                                      _ptr(v_scale), _stream()))
+
+
+def dequant_paged(pool, block_table, seq_lens, cu_seqlens_out, max_seq_len, k_scale, v_scale,
+                  out_key, out_value) -> None:
+    """Gather every sequence's cache as bf16 rows [sum(seq_lens), Hkv, D]."""
+    for t, nm, dt in ((block_table, "block_table", torch.int32), (seq_lens, "seq_lens", torch.int32),
+                      (cu_seqlens_out, "cu_seqlens_out", torch.int32), (out_key, "out_key", torch.bfloat16),
+                      (out_value, "out_value", torch.bfloat16)):
+        _dev(t, nm, dt)
+        if not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous")
+    d = _desc(pool)
+    if out_key.shape != out_value.shape:
+        raise ValueError("out_key and out_value must have the same shape")
+    _check(library().nvfp4_kv_dequant_paged(ctypes.byref(d), _ptr(block_table), block_table.shape[1],
+                                             _ptr(seq_lens), _ptr(cu_seqlens_out), seq_lens.shape[0],
+                                             int(max_seq_len), _ptr(k_scale), _ptr(v_scale), _ptr(out_key),
+                                             _ptr(out_value), out_key.shape[0], _stream()))
+
+
+def decode_workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_size: int) -> int:
+    return int(library().nvfp4_paged_attention_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads,
+                                                                      head_size))
+
+
+def paged_attention_decode(pool, q, block_table, seq_lens, max_seq_len, k_scale, v_scale, sm_scale,
+                           out, workspace) -> None:
+    """One query token per sequence: q, out bf16 [B, Hq, D]; workspace uint8."""
+    _dev(q, "q", torch.bfloat16)
+    _dev(out, "out", torch.bfloat16)
+    _dev(workspace, "workspace", torch.uint8)
+    for t, nm in ((block_table, "block_table"), (seq_lens, "seq_lens")):
+        _dev(t, nm, torch.int32)
+        if not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous")
+    if not out.is_contiguous() or q.stride(-1) != 1:
+        raise ValueError("out must be contiguous and q needs a contiguous last axis")
+    d = _desc(pool)
+    _check(library().nvfp4_paged_attention_decode(
+        ctypes.byref(d), _ptr(q), q.stride(0), q.stride(1), q.shape[1], _ptr(block_table), block_table.shape[1],
+        _ptr(seq_lens), seq_lens.shape[0], int(max_seq_len), _ptr(k_scale), _ptr(v_scale), float(sm_scale),
+        _ptr(out), _ptr(workspace), workspace.numel(), _stream()))
+
+
+def paged_attention_prefill(pool, q, cu_seqlens_q, max_q_len, block_table, seq_lens, max_seq_len,
+                            k_scale, v_scale, sm_scale, out, causal: bool = True) -> None:
+    """Chunked prefill: q, out bf16 [total_q, Hq, D]; cu_seqlens_q int32 [B + 1]."""
+    _dev(q, "q", torch.bfloat16)
+    _dev(out, "out", torch.bfloat16)
+    for t, nm in ((block_table, "block_table"), (seq_lens, "seq_lens"), (cu_seqlens_q, "cu_seqlens_q")):
+        _dev(t, nm, torch.int32)
+        if not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous")
+    if not out.is_contiguous() or q.stride(-1) != 1:
+        raise ValueError("out must be contiguous and q needs a contiguous last axis")
+    d = _desc(pool)
+    _check(library().nvfp4_paged_attention_prefill(
+        ctypes.byref(d), _ptr(q), q.stride(0), q.stride(1), q.shape[1], _ptr(cu_seqlens_q), int(max_q_len),
+        q.shape[0], _ptr(block_table), block_table.shape[1], _ptr(seq_lens), seq_lens.shape[0],
+        int(max_seq_len), _ptr(k_scale), _ptr(v_scale), float(sm_scale), 1 if causal else 0, _ptr(out),
+        ctypes.c_void_p(0), 0, _stream()))

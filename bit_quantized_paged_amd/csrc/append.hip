@@ -1,0 +1,102 @@
+// Quantize-append with a slot mapping [P40177 "Key source snippets",
+// _create_nvfp4_hnd_kv_cache; RFC47684 "Fix steps"].
+//
+// One lane owns one 16-element block of one (token, kv head, K|V) row, so the
+// block amax needs no cross-lane traffic: it reads 32 bytes of bf16 and
+// writes 8 bytes of codes plus its scale byte.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace nvfp4kv {
+
+template <int D>
+__global__ __launch_bounds__(256) void append_kernel(Pool pool, const uint16_t* __restrict__ key,
+                                                     int64_t k_st, int64_t k_sh,
+                                                     const uint16_t* __restrict__ value, int64_t v_st,
+                                                     int64_t v_sh, const int64_t* __restrict__ slots,
+                                                     int64_t num_tokens, const float* __restrict__ k_scale,
+                                                     const float* __restrict__ v_scale) {
+  constexpr int LPR = D / 16;  // lanes per row
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t row = gid / LPR;
+  const int blk16 = (int)(gid % LPR);
+  const int hkv = pool.hkv;
+  // row = (t * 2 + kv) * hkv + h
+  const int64_t rows_total = num_tokens * 2 * hkv;
+  if (row >= rows_total) return;
+  const int h = (int)(row % hkv);
+  const int kv = (int)((row / hkv) & 1);
+  const int64_t t = row / (2 * (int64_t)hkv);
+
+  const int64_t slot = slots[t];
+  const int64_t cap = pool.num_blocks * pool.bs;
+  if (slot < 0 || slot >= cap) return;
+
+  const uint16_t* src = kv ? value + t * v_st + h * v_sh : key + t * k_st + h * k_sh;
+  const u32x4* s4 = reinterpret_cast<const u32x4*>(src + blk16 * 16);
+  const u32x4 a = s4[0];
+  const u32x4 b = s4[1];
+  float x[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = bf16_lo(a[i]);
+    x[2 * i + 1] = bf16_hi(a[i]);
+    x[8 + 2 * i] = bf16_lo(b[i]);
+    x[8 + 2 * i + 1] = bf16_hi(b[i]);
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[i]));
+
+  const float g = kv ? *v_scale : *k_scale;
+  // Each line is a single fp32 operation with round-to-nearest-even.
+  const float t6 = 6.0f * g;
+  const float s32 = __fdiv_rn(amax, t6);
+  const uint32_t s8 = e4m3_from_f32_sat(s32);
+  const float d = e4m3_to_f32(s8) * g;
+  const float r = (d == 0.0f) ? 0.0f : __fdiv_rn(1.0f, d);
+
+  uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    w0 |= e2m1_code(x[i] * r) << (4 * i);
+    w1 |= e2m1_code(x[8 + i] * r) << (4 * i);
+  }
+
+  const int64_t blk = slot / pool.bs;
+  const int64_t off = slot % pool.bs;
+  uint8_t* dst = pool.data + blk * pool.sb + kv * pool.skv + off * pool.st + h * pool.sh;
+  st_u32x2(dst + blk16 * 8, u32x2{w0, w1});
+  dst[D / 2 + blk16] = (uint8_t)s8;
+}
+
+hipError_t launch_append(const Pool& pool, int head_size, const void* key, int64_t k_st, int64_t k_sh,
+                         const void* value, int64_t v_st, int64_t v_sh, const int64_t* slots,
+                         int64_t num_tokens, const float* k_scale, const float* v_scale,
+                         hipStream_t stream) {
+  if (num_tokens == 0) return hipSuccess;
+  const int64_t lanes = num_tokens * 2 * pool.hkv * (head_size / 16);
+  const int64_t blocks = (lanes + 255) / 256;
+  const dim3 grid((unsigned)blocks);
+  const uint16_t* k = static_cast<const uint16_t*>(key);
+  const uint16_t* v = static_cast<const uint16_t*>(value);
+  switch (head_size) {
+    case 64:
+      append_kernel<64><<<grid, 256, 0, stream>>>(pool, k, k_st, k_sh, v, v_st, v_sh, slots, num_tokens,
+                                                  k_scale, v_scale);
+      break;
+    case 128:
+      append_kernel<128><<<grid, 256, 0, stream>>>(pool, k, k_st, k_sh, v, v_st, v_sh, slots, num_tokens,
+                                                   k_scale, v_scale);
+      break;
+    case 256:
+      append_kernel<256><<<grid, 256, 0, stream>>>(pool, k, k_st, k_sh, v, v_st, v_sh, slots, num_tokens,
+                                                   k_scale, v_scale);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4kv

@@ -1,0 +1,456 @@
+// Paged attention over the NVFP4 cache: split-K decode (+ combine) and
+// chunked prefill [P40177 "Implementation breakdown" 1 and 3; RFC47684
+// "Cause analysis": the paged read path].
+#include "attn_core.hpp"
+#include "launch.hpp"
+
+namespace nvfp4kv {
+
+// ---------------------------------------------------------------------------
+// Decode schedule. A unit is (sequence, split, kv head); a split is a run of
+// `tps` 32-key steps. tps is chosen on the device from the actual lengths so
+// that the batch yields about kDecodeTarget units of equal size, which keeps
+// ragged batches balanced without a host round trip. Every workgroup (and
+// the combine kernel) derives the same schedule: per-sequence unit counts
+// and their exclusive prefix sum in LDS.
+// ---------------------------------------------------------------------------
+constexpr int kDecodeTarget = 1024;
+constexpr int kDecodeMinTps = 4;
+constexpr int kStep = 32;
+
+__device__ __forceinline__ int clamp_len(int L, int cap) { return L < 0 ? 0 : (L > cap ? cap : L); }
+
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int t = __shfl_up(v, d);
+    if (lane >= d) v += t;
+  }
+  return v;
+}
+
+// Block-wide exclusive scan (256 threads); also returns the total.
+__device__ __forceinline__ int block_excl_scan(int v, int* s_red, int& total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int incl = wave_incl_scan(v);
+  if (lane == 63) s_red[w] = incl;
+  __syncthreads();
+  int off = 0;
+  total = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int t = s_red[k];
+    off += (k < w) ? t : 0;
+    total += t;
+  }
+  __syncthreads();
+  return incl - v + off;
+}
+
+// s_pref[b] = first unit (per head) of sequence b, s_pref[B] = units per head.
+__device__ void decode_schedule(const int32_t* __restrict__ seq_lens, int B, int cap, int hkv, int* s_pref,
+                                int* s_red, int& tps, int& total_units) {
+  const int per = ceil_div(B, 256);
+  const int b0 = threadIdx.x * per;
+  const int b1 = (b0 + per < B) ? b0 + per : B;
+  int steps_local = 0;
+  for (int b = b0; b < b1; ++b) {
+    const int s = ceil_div(clamp_len(seq_lens[b], cap), kStep);
+    s_pref[b] = s;
+    steps_local += s;
+  }
+  int total_steps;
+  (void)block_excl_scan(steps_local, s_red, total_steps);
+  const int64_t work = (int64_t)total_steps * hkv;
+  int t = (int)((work + kDecodeTarget - 1) / kDecodeTarget);
+  tps = t < kDecodeMinTps ? kDecodeMinTps : t;
+  int units_local = 0;
+  for (int b = b0; b < b1; ++b) units_local += ceil_div(s_pref[b], tps);
+  int total;
+  int run = block_excl_scan(units_local, s_red, total);
+  for (int b = b0; b < b1; ++b) {
+    const int n = ceil_div(s_pref[b], tps);
+    s_pref[b] = run;
+    run += n;
+  }
+  if (threadIdx.x == 0) s_pref[B] = total;
+  total_units = total;
+  __syncthreads();
+}
+
+struct DecodeArgs {
+  Pool pool;
+  const uint16_t* q;
+  int64_t q_st, q_sh;
+  int hq, grp;
+  const int32_t* bt;
+  int32_t max_blocks;
+  const int32_t* seq_lens;
+  int B;
+  const float* k_scale;
+  const float* v_scale;
+  float sm_scale;
+  uint16_t* out;
+  float* ws_o;   // [slot][grp][D]   normalised partial outputs
+  float* ws_ml;  // [slot][grp][2]   (max, sum) of each partial, base-2 scores
+};
+
+__host__ __device__ inline int decode_lds_pref_ints(int B) { return ((B + 1 + 3) / 4) * 4; }
+
+template <int D>
+__global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
+  using G = Geo<D>;
+  extern __shared__ __align__(16) char smem[];
+  int* s_pref = reinterpret_cast<int*>(smem);
+  int* s_red = s_pref + decode_lds_pref_ints(a.B);
+  float* s_ml = reinterpret_cast<float*>(s_red + 16);  // [4 waves][16 cols][2]
+  float* s_o = s_ml + 4 * 16 * 2;                       // [4 waves][grp][D]
+
+  const int hkv = a.pool.hkv;
+  const int cap = a.max_blocks * a.pool.bs;
+  int tps, total;
+  decode_schedule(a.seq_lens, a.B, cap, hkv, s_pref, s_red, tps, total);
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int i = lane & 15, j = lane >> 4;
+  const int grp = a.grp;
+  const float qk_factor = a.sm_scale * (*a.k_scale) * kLog2e;
+  const float gv = *a.v_scale;
+
+  for (int u = blockIdx.x; u < total * hkv; u += gridDim.x) {
+    const int ubs = u / hkv;
+    const int h = u - ubs * hkv;
+    int lo = 0, hi = a.B;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_pref[mid] <= ubs) lo = mid; else hi = mid;
+    }
+    const int b = lo;
+    const int split = ubs - s_pref[b];
+    const int nsplit = s_pref[b + 1] - s_pref[b];
+    const int L = clamp_len(a.seq_lens[b], cap);
+    const int steps = ceil_div(L, kStep);
+    const int st0 = split * tps;
+    const int st1 = (st0 + tps < steps) ? st0 + tps : steps;
+
+    WaveAttn<D, 1> W;
+    W.init();
+    const bool valid = i < grp;
+    const uint16_t* qrow = valid ? a.q + (int64_t)b * a.q_st + (int64_t)(h * grp + i) * a.q_sh : nullptr;
+    W.load_q(0, qrow, j, qk_factor);
+    W.lim[0] = valid ? L - 1 : -1;
+    const int32_t* bt_row = a.bt + (int64_t)b * a.max_blocks;
+
+    SubRaw<D> cur[2], nxt[2];
+    int k = st0 + w;
+    if (k < st1) load_step<D>(cur, a.pool, bt_row, h, k * kStep, L, i, j);
+    for (; k < st1; k += 4) {
+      const int kn = k + 4;
+      if (kn < st1) load_step<D>(nxt, a.pool, bt_row, h, kn * kStep, L, i, j);
+      mask_step<D>(cur, k * kStep, L, j);
+      W.step(cur, k * kStep, j);
+      cur[0] = nxt[0];
+      cur[1] = nxt[1];
+    }
+
+    // ---- merge the four waves' partial softmax states through LDS
+    const float lsum = wave_sum_j(W.l[0]);
+    if (j == 0) {
+      s_ml[(w * 16 + i) * 2] = W.m[0];
+      s_ml[(w * 16 + i) * 2 + 1] = lsum;
+    }
+    if (valid) {
+      float* dst = s_o + (w * grp + i) * D;
+#pragma unroll
+      for (int t = 0; t < G::DPL; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dst[(4 * j + r) * G::DPL + t] = W.acc[0][t][r];
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < grp * D; e += 256) {
+      const int col = e / D;
+      const int d = e - col * D;
+      float M = -__builtin_inff();
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww) M = __builtin_fmaxf(M, s_ml[(ww * 16 + col) * 2]);
+      float lt = 0.0f, o = 0.0f;
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww) {
+        const float mw = s_ml[(ww * 16 + col) * 2];
+        const float f = (mw == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
+        lt += f * s_ml[(ww * 16 + col) * 2 + 1];
+        o += f * s_o[(ww * grp + col) * D + d];
+      }
+      const float on = lt > 0.0f ? o / lt : 0.0f;
+      if (nsplit == 1) {
+        const float y = on * gv;
+        a.out[((int64_t)b * a.hq + h * grp + col) * D + d] = (uint16_t)(pack_bf16x2(y, 0.0f) & 0xFFFFu);
+      } else {
+        const int64_t slot = (int64_t)ubs * hkv + h;
+        a.ws_o[(slot * grp + col) * D + d] = on;
+        if (d == 0) {
+          a.ws_ml[(slot * grp + col) * 2] = M;
+          a.ws_ml[(slot * grp + col) * 2 + 1] = lt;
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
+  extern __shared__ __align__(16) char smem[];
+  int* s_pref = reinterpret_cast<int*>(smem);
+  int* s_red = s_pref + decode_lds_pref_ints(a.B);
+  float* s_w = reinterpret_cast<float*>(s_red + 16);  // [16 cols][2]: max, 1/sum
+  const int hkv = a.pool.hkv;
+  const int cap = a.max_blocks * a.pool.bs;
+  int tps, total;
+  decode_schedule(a.seq_lens, a.B, cap, hkv, s_pref, s_red, tps, total);
+  const int grp = a.grp;
+  const float gv = *a.v_scale;
+  for (int u = blockIdx.x; u < a.B * hkv; u += gridDim.x) {
+    const int b = u / hkv;
+    const int h = u - b * hkv;
+    const int n = s_pref[b + 1] - s_pref[b];
+    if (n == 1) continue;  // the split kernel wrote this output directly
+    uint16_t* out = a.out + ((int64_t)b * a.hq + h * grp) * D;
+    if (n == 0) {  // no keys: zeros
+      for (int e = threadIdx.x; e < grp * D; e += 256) out[e] = 0;
+      continue;
+    }
+    const int64_t slot0 = (int64_t)s_pref[b] * hkv + h;
+    if ((int)threadIdx.x < grp) {
+      const int col = threadIdx.x;
+      float M = -__builtin_inff();
+      for (int s = 0; s < n; ++s) M = __builtin_fmaxf(M, a.ws_ml[((slot0 + (int64_t)s * hkv) * grp + col) * 2]);
+      float lt = 0.0f;
+      for (int s = 0; s < n; ++s) {
+        const float* ml = a.ws_ml + ((slot0 + (int64_t)s * hkv) * grp + col) * 2;
+        lt += (ml[0] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(ml[0] - M) * ml[1];
+      }
+      s_w[2 * col] = M;
+      s_w[2 * col + 1] = lt > 0.0f ? 1.0f / lt : 0.0f;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < grp * D; e += 256) {
+      const int col = e / D;
+      const int d = e - col * D;
+      const float M = s_w[2 * col];
+      const float inv = s_w[2 * col + 1];
+      float o = 0.0f;
+      for (int s = 0; s < n; ++s) {
+        const int64_t sl = (slot0 + (int64_t)s * hkv) * grp + col;
+        const float* ml = a.ws_ml + sl * 2;
+        const float f = (ml[0] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(ml[0] - M) * ml[1];
+        o += f * a.ws_o[sl * D + d];
+      }
+      out[e] = (uint16_t)(pack_bf16x2(o * inv * gv, 0.0f) & 0xFFFFu);
+    }
+    __syncthreads();
+  }
+}
+
+size_t decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_size) {
+  const int64_t grp = num_q_heads / num_kv_heads;
+  const int64_t slots = kDecodeTarget + (int64_t)num_seqs * num_kv_heads;
+  return (size_t)(slots * grp * head_size * 4 + slots * grp * 2 * 4);
+}
+
+size_t decode_lds_bytes(int num_seqs, int grp, int head_size) {
+  return (size_t)(decode_lds_pref_ints(num_seqs) + 16) * 4 + 4 * 16 * 2 * 4 + (size_t)4 * grp * head_size * 4;
+}
+
+template <int D>
+static hipError_t launch_decode_t(const DecodeArgs& a, int max_seq_len, hipStream_t stream) {
+  const int hkv = a.pool.hkv;
+  const int64_t cap = (int64_t)a.max_blocks * a.pool.bs;
+  int64_t lens = max_seq_len > 0 ? (max_seq_len < cap ? max_seq_len : cap) : cap;
+  const int64_t steps = (lens + kStep - 1) / kStep;
+  int64_t want = (int64_t)a.B * hkv * ((steps + kDecodeMinTps - 1) / kDecodeMinTps);
+  if (want < 1) want = 1;
+  const int grid = (int)(want < kDecodeTarget ? want : kDecodeTarget);
+  const size_t lds_split = decode_lds_bytes(a.B, a.grp, D);
+  decode_split_kernel<D><<<grid, 256, lds_split, stream>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t lds_comb = (size_t)(decode_lds_pref_ints(a.B) + 16) * 4 + 16 * 2 * 4;
+  const int cgrid = a.B * hkv;
+  decode_combine_kernel<D><<<cgrid, 256, lds_comb, stream>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const Pool& pool, int head_size, const void* q, int64_t q_st, int64_t q_sh,
+                         int num_q_heads, const int32_t* block_table, int32_t max_blocks,
+                         const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len, const float* k_scale,
+                         const float* v_scale, float sm_scale, void* out, void* workspace, hipStream_t stream) {
+  if (num_seqs == 0) return hipSuccess;
+  DecodeArgs a;
+  a.pool = pool;
+  a.q = static_cast<const uint16_t*>(q);
+  a.q_st = q_st;
+  a.q_sh = q_sh;
+  a.hq = num_q_heads;
+  a.grp = num_q_heads / pool.hkv;
+  a.bt = block_table;
+  a.max_blocks = max_blocks;
+  a.seq_lens = seq_lens;
+  a.B = num_seqs;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.sm_scale = sm_scale;
+  a.out = static_cast<uint16_t*>(out);
+  const int64_t slots = kDecodeTarget + (int64_t)num_seqs * pool.hkv;
+  a.ws_o = static_cast<float*>(workspace);
+  a.ws_ml = a.ws_o + slots * a.grp * head_size;
+  switch (head_size) {
+    case 64: return launch_decode_t<64>(a, max_seq_len, stream);
+    case 128: return launch_decode_t<128>(a, max_seq_len, stream);
+    case 256: return launch_decode_t<256>(a, max_seq_len, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Chunked prefill. Columns of (sequence b, kv head h) are (token, group head)
+// pairs, token-major; a wave owns 16*NT consecutive columns and walks keys
+// 0 .. its last visible key. No split-K: long chunks already give many waves.
+// ---------------------------------------------------------------------------
+struct PrefillArgs {
+  Pool pool;
+  const uint16_t* q;
+  int64_t q_st, q_sh;
+  int hq, grp;
+  const int32_t* cu_q;
+  int total_q;
+  const int32_t* bt;
+  int32_t max_blocks;
+  const int32_t* seq_lens;
+  const float* k_scale;
+  const float* v_scale;
+  float sm_scale;
+  int causal;
+  uint16_t* out;
+};
+
+template <int D>
+__device__ __forceinline__ void store_column(uint16_t* orow, const f4 (&acc)[Geo<D>::DPL], float scale, int j) {
+  constexpr int DPL = Geo<D>::DPL;
+  // lane (i, j) holds d = (4j + r) * DPL + t, a contiguous run of 4*DPL values
+  uint32_t pk[2 * DPL];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int t = 0; t < DPL; t += 2)
+      pk[(r * DPL + t) / 2] = pack_bf16x2(acc[t][r] * scale, acc[t + 1][r] * scale);
+  u32x4* dst = reinterpret_cast<u32x4*>(orow + 4 * j * DPL);
+#pragma unroll
+  for (int c = 0; c < DPL / 2; ++c) dst[c] = u32x4{pk[4 * c], pk[4 * c + 1], pk[4 * c + 2], pk[4 * c + 3]};
+}
+
+template <int D, int NT>
+__global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
+  const int b = blockIdx.z, h = blockIdx.y, cb = blockIdx.x;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int i = lane & 15, j = lane >> 4;
+  int q0 = a.cu_q[b], q1 = a.cu_q[b + 1];
+  q0 = q0 < 0 ? 0 : (q0 > a.total_q ? a.total_q : q0);
+  q1 = q1 < q0 ? q0 : (q1 > a.total_q ? a.total_q : q1);
+  const int qlen = q1 - q0;
+  const int cap = a.max_blocks * a.pool.bs;
+  const int L = clamp_len(a.seq_lens[b], cap);
+  const int grp = a.grp;
+  const int ncols = qlen * grp;
+  const int col_base = (cb * 4 + w) * 16 * NT;
+  if (col_base >= ncols) return;
+
+  WaveAttn<D, NT> W;
+  W.init();
+  const float qk_factor = a.sm_scale * (*a.k_scale) * kLog2e;
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    const int c = col_base + 16 * n + i;
+    const bool valid = c < ncols;
+    const int tok = c / grp, g = c - (c / grp) * grp;
+    const uint16_t* qrow =
+        valid ? a.q + (int64_t)(q0 + tok) * a.q_st + (int64_t)(h * grp + g) * a.q_sh : nullptr;
+    W.load_q(n, qrow, j, qk_factor);
+    int lim = a.causal ? L - qlen + tok : L - 1;
+    lim = lim > L - 1 ? L - 1 : lim;
+    W.lim[n] = valid ? lim : -1;
+  }
+  const int c_last = ((col_base + 16 * NT < ncols) ? col_base + 16 * NT : ncols) - 1;
+  int kmax = a.causal ? L - qlen + c_last / grp + 1 : L;
+  kmax = kmax > L ? L : (kmax < 0 ? 0 : kmax);
+  const int steps = ceil_div(kmax, kStep);
+  const int32_t* bt_row = a.bt + (int64_t)b * a.max_blocks;
+
+  SubRaw<D> cur[2], nxt[2];
+  if (steps > 0) load_step<D>(cur, a.pool, bt_row, h, 0, L, i, j);
+  for (int k = 0; k < steps; ++k) {
+    if (k + 1 < steps) load_step<D>(nxt, a.pool, bt_row, h, (k + 1) * kStep, L, i, j);
+    mask_step<D>(cur, k * kStep, L, j);
+    W.step(cur, k * kStep, j);
+    cur[0] = nxt[0];
+    cur[1] = nxt[1];
+  }
+
+  const float gv = *a.v_scale;
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    const float lt = wave_sum_j(W.l[n]);
+    const int c = col_base + 16 * n + i;
+    if (c < ncols) {
+      const int tok = c / grp, g = c - (c / grp) * grp;
+      uint16_t* orow = a.out + ((int64_t)(q0 + tok) * a.hq + h * grp + g) * D;
+      store_column<D>(orow, W.acc[n], lt > 0.0f ? gv / lt : 0.0f, j);
+    }
+  }
+}
+
+template <int D, int NT>
+static hipError_t launch_prefill_t(const PrefillArgs& a, int num_seqs, int max_q_len, hipStream_t stream) {
+  const int64_t cols = (int64_t)max_q_len * a.grp;
+  const int64_t per_wg = 4 * 16 * NT;
+  const int64_t gx = (cols + per_wg - 1) / per_wg;
+  if (gx == 0) return hipSuccess;
+  const dim3 grid((unsigned)gx, (unsigned)a.pool.hkv, (unsigned)num_seqs);
+  prefill_kernel<D, NT><<<grid, 256, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill(const Pool& pool, int head_size, const void* q, int64_t q_st, int64_t q_sh,
+                          int num_q_heads, const int32_t* cu_q, int32_t max_q_len, int32_t total_q,
+                          const int32_t* block_table, int32_t max_blocks, const int32_t* seq_lens,
+                          int32_t num_seqs, int32_t max_seq_len, const float* k_scale, const float* v_scale,
+                          float sm_scale, int causal, void* out, hipStream_t stream) {
+  (void)max_seq_len;
+  if (num_seqs == 0 || max_q_len <= 0 || total_q <= 0) return hipSuccess;
+  PrefillArgs a;
+  a.pool = pool;
+  a.q = static_cast<const uint16_t*>(q);
+  a.q_st = q_st;
+  a.q_sh = q_sh;
+  a.hq = num_q_heads;
+  a.grp = num_q_heads / pool.hkv;
+  a.cu_q = cu_q;
+  a.total_q = total_q;
+  a.bt = block_table;
+  a.max_blocks = max_blocks;
+  a.seq_lens = seq_lens;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.sm_scale = sm_scale;
+  a.causal = causal;
+  a.out = static_cast<uint16_t*>(out);
+  switch (head_size) {
+    case 64: return launch_prefill_t<64, 4>(a, num_seqs, max_q_len, stream);
+    case 128: return launch_prefill_t<128, 2>(a, num_seqs, max_q_len, stream);
+    case 256: return launch_prefill_t<256, 1>(a, num_seqs, max_q_len, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace nvfp4kv

@@ -1,0 +1,356 @@
+// Wave-level paged attention engine over the NVFP4 cache (gfx950).
+//
+// Attention reads the packed pages and their block-scale bytes directly
+// [P40177 "Implementation breakdown" 1 and 3: prefill/decode wrappers run on
+// the packed cache plus its block-scale view].
+//
+// A wave owns 16*NT "query columns" (q rows; in decode the GQA heads of one
+// token) and walks the keys of one sequence/kv head in steps of 32 keys
+// (two 16-key subtiles). With lane = 16*j + i:
+//
+//  * S^T = K^ . Q^T on v_mfma_f32_16x16x32_f16. Lane (i, j) loads key i's
+//    code bytes [j*D/8, (j+1)*D/8) with one wide load; chunk c of the
+//    reduction uses its word c. Q is laid out with the same (j, c) -> element
+//    map, so the contraction is over a fixed permutation of d and needs no
+//    shuffles. Codes become f16 with the hardware FP4 convert and are scaled
+//    by their E4M3 block scale (both exact in f16), g_K is folded into the
+//    per-column score factor.
+//  * The MFMA result gives lane (i, j) the scores of column i for keys
+//    4j..4j+3 of the subtile: the row max needs two cross-lane steps and the
+//    probabilities are already in the B-operand layout of the PV product.
+//  * O^T = V^ T . P^T on the same MFMA. Lane (i, j) needs, for one d, keys
+//    4j..4j+3 of each subtile: it loads D/32 bytes of each of those four rows
+//    (d in [i*D/16, (i+1)*D/16)), and a nibble transpose (two masks and a
+//    shift per key pair) puts the two keys of a pair into one byte, which the
+//    FP4 convert turns into the f16 pair the MFMA wants. PV product t covers
+//    d = i*D/16 + t.
+//  * Online softmax in base 2 with a lazy maximum: the running max of a
+//    column only moves (and the accumulators are only rescaled) when a score
+//    exceeds it by more than 8, so probabilities stay <= 256 in f16.
+#pragma once
+
+#include "device_common.hpp"
+
+namespace nvfp4kv {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazyMax = 8.0f;
+
+template <int D>
+struct Geo {
+  static constexpr int DPL = D / 16;                // V: d per lane = PV products
+  static constexpr int KW = D / 32;                 // K: code words per lane = QK chunks
+  static constexpr int VB = DPL / 2;                // V: code bytes per key per lane
+  static constexpr int VW = VB >= 4 ? VB / 4 : 1;   // V: words per key per lane
+};
+
+template <int D>
+struct SubRaw {  // raw bytes of one 16-key subtile for one lane
+  uint32_t k[Geo<D>::KW];
+  uint32_t ks;
+  uint32_t v[4][Geo<D>::VW];
+  uint32_t vs[4];
+};
+
+template <int D>
+__device__ __forceinline__ void zero_sub(SubRaw<D>& R) {
+#pragma unroll
+  for (int c = 0; c < Geo<D>::KW; ++c) R.k[c] = 0;
+  R.ks = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+#pragma unroll
+    for (int w = 0; w < Geo<D>::VW; ++w) R.v[r][w] = 0;
+    R.vs[r] = 0;
+  }
+}
+
+// kpage / vpage: first row of the (block, K|V, head) page; row0: first row of
+// the subtile inside the page.
+template <int D>
+__device__ __forceinline__ void load_sub(SubRaw<D>& R, const uint8_t* kpage, const uint8_t* vpage, int64_t st,
+                                         int row0, int i, int j) {
+  const uint8_t* krow = kpage + (int64_t)(row0 + i) * st;
+  if constexpr (D == 64) {
+    const u32x2 w = ld_u32x2(krow + j * 8);
+    R.k[0] = w[0];
+    R.k[1] = w[1];
+    R.ks = ld_u8(krow + 32 + j);
+  } else if constexpr (D == 128) {
+    const u32x4 w = ld_u32x4(krow + j * 16);
+    R.k[0] = w[0];
+    R.k[1] = w[1];
+    R.k[2] = w[2];
+    R.k[3] = w[3];
+    R.ks = ld_u16(krow + 64 + 2 * j);
+  } else {
+    const u32x4 w0 = ld_u32x4(krow + j * 32);
+    const u32x4 w1 = ld_u32x4(krow + j * 32 + 16);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      R.k[c] = w0[c];
+      R.k[4 + c] = w1[c];
+    }
+    R.ks = ld_u32(krow + 128 + 4 * j);
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint8_t* vrow = vpage + (int64_t)(row0 + 4 * j + r) * st;
+    if constexpr (D == 64) {
+      R.v[r][0] = ld_u16(vrow + 2 * i);
+      R.vs[r] = ld_u8(vrow + 32 + (i >> 2));
+    } else if constexpr (D == 128) {
+      R.v[r][0] = ld_u32(vrow + 4 * i);
+      R.vs[r] = ld_u8(vrow + 64 + (i >> 1));
+    } else {
+      const u32x2 w = ld_u32x2(vrow + 8 * i);
+      R.v[r][0] = w[0];
+      R.v[r][1] = w[1];
+      R.vs[r] = ld_u8(vrow + 128 + i);
+    }
+  }
+}
+
+// Zero the value rows of keys >= L (unwritten rows may hold NaN scale bytes;
+// their probability is 0 but 0 * NaN would poison the accumulator).
+template <int D>
+__device__ __forceinline__ void mask_sub_values(SubRaw<D>& R, int key0, int L, int j) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const bool ok = key0 + 4 * j + r < L;
+#pragma unroll
+    for (int w = 0; w < Geo<D>::VW; ++w) R.v[r][w] = ok ? R.v[r][w] : 0u;
+    R.vs[r] = ok ? R.vs[r] : 0u;
+  }
+}
+
+// Dequantised K chunk c of this lane: 8 f16 = codes * block scale.
+template <int D, int C>
+__device__ __forceinline__ h8 k_chunk(const SubRaw<D>& R) {
+  constexpr int SI = C / 2;  // scale byte index within the lane's scales
+  const h2 sp = (SI < 2) ? fp8x2_to_h2<false>(R.ks) : fp8x2_to_h2<true>(R.ks);
+  const _Float16 s = sp[SI & 1];
+  const h2 ss = {s, s};
+  const uint32_t w = R.k[C];
+  const h2 a0 = fp4x2_to_h2<0>(w) * ss;
+  const h2 a1 = fp4x2_to_h2<1>(w) * ss;
+  const h2 a2 = fp4x2_to_h2<2>(w) * ss;
+  const h2 a3 = fp4x2_to_h2<3>(w) * ss;
+  return h8{a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
+}
+
+// Value rows of one subtile rearranged so that each byte holds the codes of
+// two keys (4j+2p, 4j+2p+1) at one d.
+template <int D>
+struct VPairs {
+  uint32_t ev[2][Geo<D>::VW];  // [pair][word]: byte b <-> d offset 8w + 2b
+  uint32_t od[2][Geo<D>::VW];  //                byte b <-> d offset 8w + 2b + 1
+  h2 s[2];                     // block scales of the pair's two keys
+};
+
+template <int D>
+__device__ __forceinline__ void make_pairs(const SubRaw<D>& R, VPairs<D>& P) {
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+#pragma unroll
+    for (int w = 0; w < Geo<D>::VW; ++w) {
+      const uint32_t a = R.v[2 * p][w];
+      const uint32_t b = R.v[2 * p + 1][w];
+      P.ev[p][w] = (a & 0x0F0F0F0Fu) | ((b & 0x0F0F0F0Fu) << 4);
+      P.od[p][w] = ((a >> 4) & 0x0F0F0F0Fu) | (b & 0xF0F0F0F0u);
+    }
+  }
+  const uint32_t sw = R.vs[0] | (R.vs[1] << 8) | (R.vs[2] << 16) | (R.vs[3] << 24);
+  P.s[0] = fp8x2_to_h2<false>(sw);
+  P.s[1] = fp8x2_to_h2<true>(sw);
+}
+
+template <int D, int T>
+__device__ __forceinline__ h4 v_operand(const VPairs<D>& P) {
+  constexpr int W = T / 8;
+  constexpr int BYTE = (T % 8) / 2;
+  const uint32_t w0 = (T & 1) ? P.od[0][W] : P.ev[0][W];
+  const uint32_t w1 = (T & 1) ? P.od[1][W] : P.ev[1][W];
+  const h2 a = fp4x2_to_h2<BYTE>(w0) * P.s[0];
+  const h2 b = fp4x2_to_h2<BYTE>(w1) * P.s[1];
+  return h4{a[0], a[1], b[0], b[1]};
+}
+
+__device__ __forceinline__ float wave_max_j(float v) {
+  v = __builtin_fmaxf(v, __shfl_xor(v, 16));
+  return __builtin_fmaxf(v, __shfl_xor(v, 32));
+}
+__device__ __forceinline__ float wave_sum_j(float v) {
+  v += __shfl_xor(v, 16);
+  return v + __shfl_xor(v, 32);
+}
+
+template <int D, int NT>
+struct WaveAttn {
+  using G = Geo<D>;
+  h8 q[NT][G::KW];       // B operand of S^T, per column tile and chunk
+  float sf[NT];          // per-column factor: sm_scale * g_K * log2(e) / qscale
+  int lim[NT];           // last visible key of the column (-1: none)
+  f4 acc[NT][G::DPL];    // O^T accumulators
+  float m[NT];           // running max (base-2 scores)
+  float l[NT];           // this lane's share of the running sum
+
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      m[n] = -__builtin_inff();
+      l[n] = 0.0f;
+#pragma unroll
+      for (int t = 0; t < G::DPL; ++t) acc[n][t] = f4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+
+  // Load column tile n: qrow points at the column's D bf16 values (nullptr:
+  // padding column). The row is scaled by a power of two so that its largest
+  // magnitude lies in [1, 2) before the exact-range f16 conversion; the
+  // inverse goes into sf.
+  __device__ __forceinline__ void load_q(int n, const uint16_t* qrow, int j, float base_factor) {
+    constexpr int E = D / 4;  // bf16 elements per lane
+    uint32_t w[E / 2];
+    if (qrow != nullptr) {
+      const u32x4* p = reinterpret_cast<const u32x4*>(qrow + j * E);
+#pragma unroll
+      for (int c = 0; c < E / 8; ++c) {
+        const u32x4 x = p[c];
+        w[4 * c] = x[0];
+        w[4 * c + 1] = x[1];
+        w[4 * c + 2] = x[2];
+        w[4 * c + 3] = x[3];
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < E / 2; ++c) w[c] = 0;
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int c = 0; c < E / 2; ++c)
+      amax = __builtin_fmaxf(amax, __builtin_fmaxf(__builtin_fabsf(bf16_lo(w[c])), __builtin_fabsf(bf16_hi(w[c]))));
+    amax = wave_max_j(amax);
+    int e = (int)((__float_as_uint(amax) >> 23) & 0xFFu) - 127;
+    e = (amax == 0.0f) ? 0 : (e < -120 ? -120 : e);
+    sf[n] = __builtin_ldexpf(base_factor, e);
+#pragma unroll
+    for (int c = 0; c < G::KW; ++c) {
+      h8 v;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        v[2 * t] = (_Float16)__builtin_ldexpf(bf16_lo(w[4 * c + t]), -e);
+        v[2 * t + 1] = (_Float16)__builtin_ldexpf(bf16_hi(w[4 * c + t]), -e);
+      }
+      q[n][c] = v;
+    }
+  }
+
+  // One 32-key step starting at absolute key kb; R[0], R[1] hold the two
+  // subtiles' raw bytes (keys >= L already zeroed in the value rows).
+  __device__ __forceinline__ void step(const SubRaw<D> (&R)[2], int kb, int j) {
+    // ---- S^T = K^ . Q^T for both subtiles
+    f4 s[2][NT];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+      for (int n = 0; n < NT; ++n) s[sb][n] = f4{0.f, 0.f, 0.f, 0.f};
+      chunks<0>(R[sb], s[sb]);
+    }
+    // ---- online softmax
+    h8 p[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      float x[8];
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = kb + 16 * sb + 4 * j + r;
+          const float v = s[sb][n][r] * sf[n];
+          x[4 * sb + r] = (key <= lim[n]) ? v : -__builtin_inff();
+        }
+      }
+      float mx = x[0];
+#pragma unroll
+      for (int k = 1; k < 8; ++k) mx = __builtin_fmaxf(mx, x[k]);
+      mx = wave_max_j(mx);
+      const bool grow = mx > m[n] + kLazyMax;
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+        const float mnew = grow ? mx : m[n];
+        const float alpha = grow ? __builtin_amdgcn_exp2f(m[n] - mnew) : 1.0f;  // exp2(-inf) = 0
+        l[n] *= alpha;
+#pragma unroll
+        for (int t = 0; t < G::DPL; ++t) acc[n][t] *= alpha;
+        m[n] = mnew;
+      }
+      const float mu = (m[n] == -__builtin_inff()) ? 0.0f : m[n];
+      // the running sum adds the f16-rounded probabilities the PV product
+      // uses, so that constant values come back unchanged
+      float ps = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const _Float16 e = (_Float16)__builtin_amdgcn_exp2f(x[k] - mu);
+        ps += (float)e;
+        p[n][k] = e;
+      }
+      l[n] += ps;
+    }
+    // ---- O^T += V^ T . P^T
+    VPairs<D> vp[2];
+    make_pairs(R[0], vp[0]);
+    make_pairs(R[1], vp[1]);
+    pv<0>(vp, p);
+  }
+
+  template <int C>
+  __device__ __forceinline__ void chunks(const SubRaw<D>& R, f4 (&s)[NT]) {
+    if constexpr (C < G::KW) {
+      const h8 a = k_chunk<D, C>(R);
+#pragma unroll
+      for (int n = 0; n < NT; ++n) s[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, q[n][C], s[n], 0, 0, 0);
+      chunks<C + 1>(R, s);
+    }
+  }
+
+  template <int T>
+  __device__ __forceinline__ void pv(const VPairs<D> (&vp)[2], const h8 (&p)[NT]) {
+    if constexpr (T < G::DPL) {
+      const h4 a0 = v_operand<D, T>(vp[0]);
+      const h4 a1 = v_operand<D, T>(vp[1]);
+      const h8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+#pragma unroll
+      for (int n = 0; n < NT; ++n) acc[n][T] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, p[n], acc[n][T], 0, 0, 0);
+      pv<T + 1>(vp, p);
+    }
+  }
+};
+
+// Issue the loads of the 32-key step at kb (subtiles past L are zeroed).
+template <int D>
+__device__ __forceinline__ void load_step(SubRaw<D> (&R)[2], const Pool& pool, const int32_t* bt_row, int h, int kb,
+                                          int L, int i, int j) {
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb) {
+    const int k0 = kb + 16 * sb;
+    if (k0 < L) {
+      const int page = k0 / pool.bs;
+      const int row0 = k0 - page * pool.bs;
+      const int64_t blk = clamp_block(bt_row[page], pool.num_blocks);
+      const uint8_t* kpage = pool.data + blk * pool.sb + (int64_t)h * pool.sh;
+      load_sub<D>(R[sb], kpage, kpage + pool.skv, pool.st, row0, i, j);
+    } else {
+      zero_sub<D>(R[sb]);
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void mask_step(SubRaw<D> (&R)[2], int kb, int L, int j) {
+  if (kb + 32 > L) {
+    mask_sub_values<D>(R[0], kb, L, j);
+    mask_sub_values<D>(R[1], kb + 16, L, j);
+  }
+}
+
+}  // namespace nvfp4kv

@@ -1,0 +1,102 @@
+// Paged dequantize [RFC47684 "Fix steps": nvfp4_kv_dequantize_paged].
+//
+// One workgroup per (page, sequence). A lane turns one 16-element block (8
+// code bytes + 1 scale byte) into 16 bf16 values: codes -> f16 with the
+// hardware FP4 convert, times the E4M3 scale (exact in f16: at most 6
+// significant bits), widened to fp32, times g (one fp32 RNE multiply), then
+// bf16 RNE. Consecutive lanes take consecutive blocks of one output row, so
+// both the 32-byte stores and the 8-byte loads are coalesced.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace nvfp4kv {
+
+template <int D>
+__global__ __launch_bounds__(256) void dequant_kernel(Pool pool, const int32_t* __restrict__ block_table,
+                                                      int32_t max_blocks, const int32_t* __restrict__ seq_lens,
+                                                      const int32_t* __restrict__ cu_out, int32_t cap_len,
+                                                      const float* __restrict__ k_scale,
+                                                      const float* __restrict__ v_scale,
+                                                      uint16_t* __restrict__ out_k, uint16_t* __restrict__ out_v,
+                                                      int64_t out_rows) {
+  constexpr int NB = D / 16;  // blocks per row
+  const int b = blockIdx.y;
+  const int p = blockIdx.x;
+  const int bs = pool.bs;
+  int L = seq_lens[b];
+  L = L < 0 ? 0 : (L > cap_len ? cap_len : L);
+  const int tok0 = p * bs;
+  if (tok0 >= L) return;
+  const int rows = (L - tok0) < bs ? (L - tok0) : bs;
+  const int64_t blk = clamp_block(block_table[(int64_t)b * max_blocks + p], pool.num_blocks);
+  const int hkv = pool.hkv;
+  const int64_t out0 = (int64_t)cu_out[b] + tok0;
+  const float gk = *k_scale;
+  const float gv = *v_scale;
+  const int per_kv = rows * hkv * NB;
+  for (int w = threadIdx.x; w < 2 * per_kv; w += blockDim.x) {
+    const int kv = w / per_kv;
+    const int rem = w - kv * per_kv;
+    const int jb = rem % NB;
+    const int h = (rem / NB) % hkv;
+    const int r = rem / (NB * hkv);
+    const int64_t orow = out0 + r;
+    if (orow < 0 || orow >= out_rows) continue;
+    const uint8_t* src = pool.data + blk * pool.sb + kv * pool.skv + r * pool.st + h * pool.sh;
+    const u32x2 codes = ld_u32x2(src + jb * 8);
+    const uint32_t sbyte = ld_u8(src + D / 2 + jb);
+    const h2 s = fp8x2_to_h2<false>(sbyte);
+    const h2 ss = {s[0], s[0]};
+    const float g = kv ? gv : gk;
+    uint32_t o[8];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const uint32_t c = codes[q];
+      h2 v0 = fp4x2_to_h2<0>(c) * ss;
+      h2 v1 = fp4x2_to_h2<1>(c) * ss;
+      h2 v2 = fp4x2_to_h2<2>(c) * ss;
+      h2 v3 = fp4x2_to_h2<3>(c) * ss;
+      o[4 * q + 0] = pack_bf16x2((float)v0[0] * g, (float)v0[1] * g);
+      o[4 * q + 1] = pack_bf16x2((float)v1[0] * g, (float)v1[1] * g);
+      o[4 * q + 2] = pack_bf16x2((float)v2[0] * g, (float)v2[1] * g);
+      o[4 * q + 3] = pack_bf16x2((float)v3[0] * g, (float)v3[1] * g);
+    }
+    uint16_t* dst = (kv ? out_v : out_k) + (orow * hkv + h) * D + jb * 16;
+    u32x4* d4 = reinterpret_cast<u32x4*>(dst);
+    d4[0] = u32x4{o[0], o[1], o[2], o[3]};
+    d4[1] = u32x4{o[4], o[5], o[6], o[7]};
+  }
+}
+
+hipError_t launch_dequant(const Pool& pool, int head_size, const int32_t* block_table, int32_t max_blocks,
+                          const int32_t* seq_lens, const int32_t* cu_out, int32_t num_seqs, int32_t max_seq_len,
+                          const float* k_scale, const float* v_scale, void* out_k, void* out_v,
+                          int64_t out_rows, hipStream_t stream) {
+  if (num_seqs == 0 || max_seq_len <= 0) return hipSuccess;
+  int64_t cap = (int64_t)max_blocks * pool.bs;
+  if (cap > max_seq_len) cap = max_seq_len;
+  const int pages = (int)((cap + pool.bs - 1) / pool.bs);
+  if (pages == 0) return hipSuccess;
+  const dim3 grid((unsigned)pages, (unsigned)num_seqs);
+  uint16_t* ok = static_cast<uint16_t*>(out_k);
+  uint16_t* ov = static_cast<uint16_t*>(out_v);
+  switch (head_size) {
+    case 64:
+      dequant_kernel<64><<<grid, 256, 0, stream>>>(pool, block_table, max_blocks, seq_lens, cu_out, (int32_t)cap,
+                                                   k_scale, v_scale, ok, ov, out_rows);
+      break;
+    case 128:
+      dequant_kernel<128><<<grid, 256, 0, stream>>>(pool, block_table, max_blocks, seq_lens, cu_out, (int32_t)cap,
+                                                    k_scale, v_scale, ok, ov, out_rows);
+      break;
+    case 256:
+      dequant_kernel<256><<<grid, 256, 0, stream>>>(pool, block_table, max_blocks, seq_lens, cu_out, (int32_t)cap,
+                                                    k_scale, v_scale, ok, ov, out_rows);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4kv

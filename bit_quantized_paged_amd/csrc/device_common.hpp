@@ -1,0 +1,114 @@
+// Device helpers for the NVFP4 paged KV cache kernels (gfx950).
+//
+// Format [P39129 NvFp4LinearLayerConfig docstring; P40177 get_kv_cache_shape,
+// get_dtype_for_flashinfer]: a (token, kv head) row is D/2 bytes of E2M1 codes
+// (element 2k in the low nibble of byte k) followed by D/16 E4M3FN scales.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4kv {
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f2 __attribute__((ext_vector_type(2)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Pool rows are only guaranteed 4-byte aligned (36-byte rows at D=64); these
+// wrappers state that alignment so the compiler may still emit wide loads.
+struct __attribute__((packed, aligned(4))) A4x2 { u32x2 v; };
+struct __attribute__((packed, aligned(4))) A4x4 { u32x4 v; };
+
+__device__ __forceinline__ uint32_t ld_u8(const uint8_t* p) { return *p; }
+__device__ __forceinline__ uint32_t ld_u16(const uint8_t* p) { return *reinterpret_cast<const uint16_t*>(p); }
+__device__ __forceinline__ uint32_t ld_u32(const uint8_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
+__device__ __forceinline__ u32x2 ld_u32x2(const uint8_t* p) { return reinterpret_cast<const A4x2*>(p)->v; }
+__device__ __forceinline__ u32x4 ld_u32x4(const uint8_t* p) { return reinterpret_cast<const A4x4*>(p)->v; }
+__device__ __forceinline__ void st_u32x2(uint8_t* p, u32x2 v) { reinterpret_cast<A4x2*>(p)->v = v; }
+
+// Pool geometry, strides in bytes (see nvfp4kv_cache).
+struct Pool {
+  uint8_t* data;
+  int64_t num_blocks;
+  int64_t sb, skv, st, sh;
+  int32_t bs;
+  int32_t hkv;
+};
+
+__device__ __forceinline__ int64_t clamp_block(int32_t id, int64_t num_blocks) {
+  // Out-of-range ids are a caller error; clamping keeps every access inside
+  // the pool so that bad metadata cannot fault the device.
+  int64_t v = id;
+  v = v < 0 ? 0 : v;
+  return v >= num_blocks ? num_blocks - 1 : v;
+}
+
+// bf16 bits -> fp32 (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 pair -> packed bf16 pair, round to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  f2 v = {a, b};
+  bf2 r = __builtin_convertvector(v, bf2);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// ---- E4M3FN --------------------------------------------------------------
+
+// Non-negative finite fp32 -> E4M3FN byte, round to nearest even, values at
+// or above 448 saturate to 0x7E. In binade [2^e, 2^(e+1)) (e clamped to >= -6,
+// where the subnormal step 2^-9 takes over) the significand count is
+// n = rint(s * 2^(3-e)) in [8, 16] (or [0, 8] below 2^-6) and the byte is
+// (e + 6) * 8 + n; a round-up to 16 lands on the next binade's first code.
+__device__ __forceinline__ uint32_t e4m3_from_f32_sat(float s) {
+  if (!(s < 448.0f)) return 0x7Eu;
+  int e = (int)((__float_as_uint(s) >> 23) & 0xFFu) - 127;
+  e = e < -6 ? -6 : e;
+  float n = __builtin_rintf(__builtin_ldexpf(s, 3 - e));
+  return (uint32_t)((e + 6) * 8 + (int)n);
+}
+
+// E4M3FN byte (never NaN here) -> fp32, exact.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+  int e = (int)((b >> 3) & 15u);
+  int m = (int)(b & 7u);
+  float v = e ? __builtin_ldexpf((float)(8 + m), e - 10) : __builtin_ldexpf((float)m, -9);
+  return (b & 0x80u) ? -v : v;
+}
+
+// ---- E2M1 ----------------------------------------------------------------
+
+// fp32 -> 4-bit code (sign | magnitude index), round to nearest, ties to the
+// even index, |v| > 6 -> 6. The magnitude index counts the midpoints
+// 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5 that |v| has passed. A value exactly on
+// a midpoint goes to the even neighbour, so the test is '>' where the index
+// above the midpoint is odd and '>=' where it is even.
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+  float a = __builtin_fabsf(v);
+  uint32_t idx = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                 (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                 (uint32_t)(a > 5.0f);
+  return ((__float_as_uint(v) >> 28) & 8u) | idx;
+}
+
+// Two E2M1 codes in byte `sel` of w -> f16 pair (low nibble first), exact.
+template <int SEL>
+__device__ __forceinline__ h2 fp4x2_to_h2(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL);
+}
+
+// Two E4M3 bytes (bytes 0,1 or 2,3 of w) -> f16 pair, exact.
+template <bool HI>
+__device__ __forceinline__ h2 fp8x2_to_h2(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI);
+}
+
+__device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+}  // namespace nvfp4kv

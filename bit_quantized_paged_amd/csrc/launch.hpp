@@ -1,0 +1,38 @@
+// Host-side launchers of the HIP kernels (one per operation); the C ABI in
+// api.hip validates arguments and calls these.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "device_common.hpp"
+
+namespace nvfp4kv {
+
+hipError_t launch_append(const Pool& pool, int head_size, const void* key, int64_t k_st, int64_t k_sh,
+                         const void* value, int64_t v_st, int64_t v_sh, const int64_t* slots,
+                         int64_t num_tokens, const float* k_scale, const float* v_scale, hipStream_t stream);
+
+hipError_t launch_dequant(const Pool& pool, int head_size, const int32_t* block_table, int32_t max_blocks,
+                          const int32_t* seq_lens, const int32_t* cu_out, int32_t num_seqs, int32_t max_seq_len,
+                          const float* k_scale, const float* v_scale, void* out_k, void* out_v,
+                          int64_t out_rows, hipStream_t stream);
+
+size_t decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_size);
+
+hipError_t launch_decode(const Pool& pool, int head_size, const void* q, int64_t q_st, int64_t q_sh,
+                         int num_q_heads, const int32_t* block_table, int32_t max_blocks,
+                         const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len, const float* k_scale,
+                         const float* v_scale, float sm_scale, void* out, void* workspace, hipStream_t stream);
+
+// Dynamic LDS bytes of the decode split kernel (must stay within 64 KiB).
+size_t decode_lds_bytes(int num_seqs, int grp, int head_size);
+
+hipError_t launch_prefill(const Pool& pool, int head_size, const void* q, int64_t q_st, int64_t q_sh,
+                          int num_q_heads, const int32_t* cu_q, int32_t max_q_len, int32_t total_q,
+                          const int32_t* block_table, int32_t max_blocks, const int32_t* seq_lens,
+                          int32_t num_seqs, int32_t max_seq_len, const float* k_scale, const float* v_scale,
+                          float sm_scale, int causal, void* out, hipStream_t stream);
+
+}  // namespace nvfp4kv

@@ -1,0 +1,194 @@
+/*
+ * nvfp4kv — NVFP4-quantised paged KV cache for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libnvfp4kv.so. Every buffer argument is a DEVICE pointer owned by
+ * the caller; the library allocates nothing and keeps no state. Every call is
+ * asynchronous and ordered on the given HIP stream (pass a hipStream_t as
+ * `stream`; NULL means the default stream). Calls return a status; on a
+ * non-zero status nothing was launched (argument errors) or a launch failed
+ * (NVFP4KV_HIP_ERROR), and nvfp4kv_last_error() describes why.
+ *
+ * Sources of the operations (pages the method is described on):
+ *   [P40177] "FlashInfer backend adds end-to-end NVFP4 KV cache support"
+ *            (vLLM PR 40177 summary): "Key source snippets" —
+ *            get_kv_cache_shape (pool shape, packed width D/2 + D/16),
+ *            get_dtype_for_flashinfer (uint8 holding FP4 data and the FP8
+ *            block scale), _create_nvfp4_hnd_kv_cache (slot-mapping writer
+ *            with per-tensor kv scales, HND physical order);
+ *            "Implementation breakdown" 1 and 3 (prefill/decode attention
+ *            reading the packed cache and its block-scale view).
+ *   [P39129] "Move NVFP4 GEMM management into NvFp4LinearKernel" (vLLM PR
+ *            39129 report): NvFp4LinearLayerConfig docstring — two FP4
+ *            values per byte, FP8-E4M3 scale per 16 elements, fp32 global
+ *            scale.
+ *   [RFC47684] "[RFC]: FlashInfer NVFP4 KV serving on pre-SM100 GPUs":
+ *            "Cause analysis" / "Fix steps" — quantize-append with slot
+ *            mapping and the paged dequantize of the fallback read path.
+ *
+ * Cache row format (readings of the pages, which print no bit layout): a
+ * (token, kv head) row of head_size D elements is D/2 bytes of E2M1 codes
+ * (element 2k in the low nibble of byte k, code = sign | e1 e0 | m) followed
+ * by D/16 E4M3FN block scales (block j covers elements 16j..16j+15). An
+ * element decodes as e2m1(code) * e4m3(scale) * g, with g the per-tensor
+ * fp32 kv scale (k_scale for keys, v_scale for values).
+ */
+#ifndef NVFP4KV_H
+#define NVFP4KV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t nvfp4kv_status;
+#define NVFP4KV_OK 0
+#define NVFP4KV_INVALID_ARGUMENT 1   /* null pointer, bad size, bad stride */
+#define NVFP4KV_UNSUPPORTED 2        /* shape the kernels are not built for */
+#define NVFP4KV_WORKSPACE_TOO_SMALL 3
+#define NVFP4KV_HIP_ERROR 4          /* a kernel launch failed */
+
+/*
+ * KV pool descriptor. Logical shape (num_blocks, 2, block_size,
+ * num_kv_heads, full_dim) uint8 [P40177 get_kv_cache_shape]; index 0 of the
+ * second axis holds keys, 1 values. Strides are in BYTES for the first four
+ * axes; the last axis is contiguous. The HND physical order of [P40177
+ * _create_nvfp4_hnd_kv_cache] (num_blocks, 2, num_kv_heads, block_size,
+ * full_dim) is this descriptor with stride_token = full_dim and
+ * stride_head = block_size * full_dim; NHD is stride_head = full_dim.
+ * Requirements: data 16-byte aligned, every stride a multiple of 4.
+ */
+typedef struct nvfp4kv_cache {
+  uint8_t* data;
+  int64_t num_blocks;
+  int32_t block_size;     /* 16, 32 or 64 */
+  int32_t num_kv_heads;
+  int32_t head_size;      /* 64, 128 or 256 */
+  int32_t reserved;       /* must be 0 */
+  int64_t stride_block;
+  int64_t stride_kv;
+  int64_t stride_token;
+  int64_t stride_head;
+} nvfp4kv_cache;
+
+/* Packed row width in bytes: head_size/2 + head_size/16 [P40177
+ * get_kv_cache_shape]; -1 if head_size is not a positive multiple of 16. */
+int32_t nvfp4_kv_full_dim(int32_t head_size);
+
+/*
+ * Quantize-append with a slot mapping [P40177 _create_nvfp4_hnd_kv_cache;
+ * RFC47684 "Fix steps": nvfp4_quantize_append_paged_kv_cache_with_slot_mapping].
+ *
+ * key, value: bf16 [num_tokens, num_kv_heads, head_size]; strides in
+ *   ELEMENTS for the token and head axes (multiples of 8), last axis
+ *   contiguous, 16-byte aligned base.
+ * slot_mapping: int64 [num_tokens]; token t is written to block
+ *   slot / block_size, row slot % block_size. Slots < 0 or >= num_blocks *
+ *   block_size are skipped. Slots must be unique within a call.
+ * k_scale, v_scale: device fp32 scalars g (> 0, finite), the dequantisation
+ *   multipliers. Per 16-element block: s = E4M3_RNE_sat(amax / (6 g)),
+ *   codes = E2M1_RNE_sat(x * (1 / (s g))), each step one fp32 RNE operation.
+ * num_tokens == 0 is a no-op.
+ */
+nvfp4kv_status nvfp4_kv_append(const nvfp4kv_cache* cache,
+                               const void* key, int64_t key_stride_token, int64_t key_stride_head,
+                               const void* value, int64_t value_stride_token, int64_t value_stride_head,
+                               const int64_t* slot_mapping, int64_t num_tokens,
+                               const float* k_scale, const float* v_scale, void* stream);
+
+/*
+ * Paged dequantize [RFC47684 "Fix steps": nvfp4_kv_dequantize_paged]: every
+ * sequence's keys and values, gathered through the block table, written as
+ * bf16 rows. Sequence b's token j (j < seq_lens[b]) lives in block
+ * block_table[b * max_blocks_per_seq + j / block_size], row j % block_size,
+ * and is written to row cu_seqlens_out[b] + j of out_key / out_value
+ * (bf16 [out_rows, num_kv_heads, head_size], contiguous). Values are
+ * bf16_RNE(fp32(e2m1 * e4m3) * g).
+ *
+ * block_table: int32 [num_seqs, max_blocks_per_seq]; seq_lens: int32
+ * [num_seqs]; cu_seqlens_out: int32 [num_seqs] (first output row per
+ * sequence). max_seq_len: host upper bound of seq_lens (sizes the grid).
+ * Device-side, lengths are clamped to min(max_seq_len, max_blocks_per_seq *
+ * block_size), block ids to [0, num_blocks) and rows past out_rows are
+ * dropped, so bad metadata yields wrong values, never an out-of-range access.
+ */
+nvfp4kv_status nvfp4_kv_dequant_paged(const nvfp4kv_cache* cache,
+                                      const int32_t* block_table, int32_t max_blocks_per_seq,
+                                      const int32_t* seq_lens, const int32_t* cu_seqlens_out,
+                                      int32_t num_seqs, int32_t max_seq_len,
+                                      const float* k_scale, const float* v_scale,
+                                      void* out_key, void* out_value, int64_t out_rows, void* stream);
+
+/*
+ * Workspace (bytes) that nvfp4_paged_attention_decode needs for a batch of
+ * num_seqs sequences; it does not depend on the sequence lengths.
+ */
+size_t nvfp4_paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                                   int32_t num_kv_heads, int32_t head_size);
+
+/*
+ * Decode attention over the quantised pages [P40177 "Implementation
+ * breakdown" 1 and 3; RFC47684 "Cause analysis": the paged read path].
+ *
+ * One query token per sequence, attending to all seq_lens[b] cached keys of
+ * its sequence (the token's own key must already be appended). q head h
+ * reads kv head h / (num_q_heads / num_kv_heads). Scores are
+ * (q . k^) * sm_scale with k^ = e2m1 * e4m3 * k_scale; the output is
+ * softmax(scores) . v^ with v^ = e2m1 * e4m3 * v_scale, rounded to bf16.
+ *
+ * q: bf16 [num_seqs, num_q_heads, head_size], strides in ELEMENTS (multiples
+ *   of 8), last axis contiguous, 16-byte aligned. out: bf16 [num_seqs,
+ *   num_q_heads, head_size] contiguous. A sequence with no key yields zeros.
+ * num_q_heads / num_kv_heads must be an integer in [1, 16]; num_seqs <= 4096.
+ * max_seq_len is ignored by the schedule (kept for symmetry with prefill);
+ * lengths are clamped to max_blocks_per_seq * block_size on the device.
+ * workspace: device scratch of at least
+ *   nvfp4_paged_attention_decode_workspace_size(...) bytes, 16-byte aligned;
+ *   its contents need not be initialised. Calls that share a workspace must
+ *   be ordered on one stream.
+ */
+nvfp4kv_status nvfp4_paged_attention_decode(const nvfp4kv_cache* cache,
+                                            const void* q, int64_t q_stride_token, int64_t q_stride_head,
+                                            int32_t num_q_heads,
+                                            const int32_t* block_table, int32_t max_blocks_per_seq,
+                                            const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
+                                            const float* k_scale, const float* v_scale, float sm_scale,
+                                            void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Chunked-prefill attention over the quantised pages [P40177
+ * "Implementation breakdown" 1 and 3]. Sequence b has q_b = cu_seqlens_q[b+1]
+ * - cu_seqlens_q[b] new query tokens, the last q_b of its seq_lens[b]
+ * tokens; its keys and values (including the new chunk) must already be
+ * appended. With causal != 0 query i of the chunk sees keys
+ * j <= seq_lens[b] - q_b + i (bottom-right alignment), otherwise all keys.
+ * Same scores, softmax and GQA mapping as decode.
+ *
+ * q: bf16 [total_q, num_q_heads, head_size] (element strides, multiples of
+ *   8, last axis contiguous); cu_seqlens_q: int32 [num_seqs + 1];
+ *   max_q_len: host upper bound of the q_b (sizes the grid); rows past
+ *   total_q are neither read nor written. out: bf16 [total_q, num_q_heads,
+ *   head_size] contiguous. The workspace arguments are reserved: pass NULL, 0.
+ */
+nvfp4kv_status nvfp4_paged_attention_prefill(const nvfp4kv_cache* cache,
+                                             const void* q, int64_t q_stride_token, int64_t q_stride_head,
+                                             int32_t num_q_heads, const int32_t* cu_seqlens_q,
+                                             int32_t max_q_len, int32_t total_q,
+                                             const int32_t* block_table, int32_t max_blocks_per_seq,
+                                             const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
+                                             const float* k_scale, const float* v_scale, float sm_scale,
+                                             int32_t causal, void* out,
+                                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* nvfp4kv_status_string(nvfp4kv_status status);
+
+/* Message of the last failing call on this host thread ("" if none). */
+const char* nvfp4kv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4KV_H */
