@@ -1,0 +1,333 @@
+#!/usr/bin/env python3
+"""Benchmark of the NVFP4 paged KV cache hot path on one MI355X.
+
+A step is one serving pass over the batch: quantize-append every sequence's
+new tokens into the pool (slot mapping), then paged attention over the
+quantised cache (decode for 1-token sequences, chunked prefill for the
+rest). K steps are captured into one HIP graph and timed as a whole; pool
+copies rotate between steps so that no step finds its cache in the 256 MB
+Infinity Cache (every copy holds identical bytes). Decode-only and
+append-only graphs over the same rotation give the per-kernel times used for
+the roofline, and a paged-dequantize graph reports that operation's rate.
+
+Prints one JSON line. `value` is the decode attention's effective HBM
+bandwidth (cache bytes + q + out + block ids + lengths over the decode
+kernel's time); append Mtokens/s and the other rates are extra fields.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0
+MALL_BYTES = 256 << 20
+WORKLOADS = {"tiny_decode": 1, "small_decode": 2, "long_decode": 3, "chunked_prefill": 4, "mixed_serving": 5}
+METRIC = "decode attention effective HBM GB/s (% of peak) + append Mtokens/s, NVFP4 KV"
+KERNEL_SOURCES = ["bit_quantized_paged_amd/csrc/attn.hip", "bit_quantized_paged_amd/csrc/attn_core.hpp",
+                  "bit_quantized_paged_amd/csrc/device_common.hpp"]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="small_decode", choices=sorted(WORKLOADS))
+    ap.add_argument("--copies", type=int, default=0, help="pool copies to rotate (0: enough to exceed the MALL 3x)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a 512 MiB device copy (to scale rocprofv3 FETCH_SIZE/WRITE_SIZE)")
+    return ap.parse_args()
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str):
+    """HBM bytes per decode launch from the committed counter summary, if it
+    was taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", f"decode_split_kernel_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    for line in open(path):
+        if line.startswith("traffic:"):
+            for kv in line[len("traffic:"):].split():
+                k, v = kv.split("=")
+                rec[k] = v
+    if rec.get("source_hash") != source_hash():
+        return None
+    return float(rec["bytes_per_launch"])
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported (the NVFP4 KV path here is "
+              "single-GPU; see the design notes for how it would shard)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import bit_quantized_paged_amd as nvk
+    from workloads import make_config
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.calibrate_copy:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": src.numel()}))
+        return
+
+    cfg = WORKLOADS[args.workload]
+    t_gen = time.perf_counter()
+    w = make_config(cfg)
+    gen_s = time.perf_counter() - t_gen
+    B, Hq, Hkv, D, bs = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_size, w.block_size
+    fd = D // 2 + D // 16
+    sm_scale = 1.0 / math.sqrt(D)
+
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+    i64 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int64)).to(dev)
+
+    cached = w.cached_mask()
+    new = ~cached
+    k_scale = torch.tensor([float(w.k_scale)], device=dev)
+    v_scale = torch.tensor([float(w.v_scale)], device=dev)
+
+    # ---- pool copies, filled with the cached prefix (outside any timing)
+    base = torch.zeros((w.num_blocks, 2, Hkv, bs, fd), dtype=torch.uint8, device=dev)
+    pool0 = base.permute(0, 1, 3, 2, 4)
+    if cached.any():
+        kc, vc, sc = bf(w.key[cached]), bf(w.value[cached]), i64(w.slot_mapping[cached])
+        nvk.append(pool0, kc, vc, sc, k_scale, v_scale)
+        del kc, vc, sc
+    pool_bytes = base.numel()
+    copies = args.copies or max(2, math.ceil(3 * MALL_BYTES / pool_bytes))
+    bases = [base] + [base.clone() for _ in range(copies - 1)]
+    pools = [b_.permute(0, 1, 3, 2, 4) for b_ in bases]
+
+    k_new, v_new, s_new = bf(w.key[new]), bf(w.value[new]), i64(w.slot_mapping[new])
+    n_new = int(new.sum())
+
+    dec_idx = np.nonzero(w.q_lens == 1)[0]
+    pre_idx = np.nonzero(w.q_lens != 1)[0]
+    wd = w.subset(dec_idx) if len(dec_idx) else None
+    wp = w.subset(pre_idx) if len(pre_idx) else None
+    if wd is not None:
+        qd, btd, sld = bf(wd.query), i32(wd.block_table), i32(wd.seq_lens)
+        outd = torch.empty((wd.num_seqs, Hq, D), dtype=torch.bfloat16, device=dev)
+        wsd = torch.zeros(nvk.decode_workspace_size(wd.num_seqs, Hq, Hkv, D), dtype=torch.uint8, device=dev)
+        maxd = int(wd.seq_lens.max())
+    if wp is not None:
+        qp, btp, slp, cup = bf(wp.query), i32(wp.block_table), i32(wp.seq_lens), i32(wp.cu_q)
+        outp = torch.empty((int(wp.cu_q[-1]), Hq, D), dtype=torch.bfloat16, device=dev)
+        maxq, maxp = int(wp.q_lens.max()), int(wp.seq_lens.max())
+
+    def do_append(r):
+        nvk.append(pools[r], k_new, v_new, s_new, k_scale, v_scale)
+
+    def do_decode(r):
+        nvk.paged_attention_decode(pools[r], qd, btd, sld, maxd, k_scale, v_scale, sm_scale, outd, wsd)
+
+    def do_prefill(r):
+        nvk.paged_attention_prefill(pools[r], qp, cup, maxq, btp, slp, maxp, k_scale, v_scale, sm_scale, outp)
+
+    def step(r):
+        do_append(r)
+        if wd is not None:
+            do_decode(r)
+        if wp is not None:
+            do_prefill(r)
+
+    # ---- eager warmup, then a reference result for the graph check
+    for s in range(args.warmup):
+        step(s % copies)
+    torch.cuda.synchronize()
+    ref_d = outd.clone() if wd is not None else None
+    ref_p = outp.clone() if wp is not None else None
+
+    K = args.steps
+    cap_stream = torch.cuda.Stream()
+
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        cap_stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap_stream):
+            with torch.cuda.graph(g, stream=cap_stream):
+                for s in range(K):
+                    fn(s % copies)
+        torch.cuda.current_stream().wait_stream(cap_stream)
+        return g
+
+    def time_graph(g):
+        g.replay()  # warm replay
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        stream = torch.cuda.current_stream()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return e0.elapsed_time(e1) / 1e3, wall
+
+    g_step = capture(step)
+    step_gpu_s, step_wall_s = time_graph(g_step)
+    if wd is not None:
+        assert torch.equal(outd, ref_d), "graph replay of the step differs from the eager decode"
+    if wp is not None:
+        assert torch.equal(outp, ref_p), "graph replay of the step differs from the eager prefill"
+    res = {}
+    g_app = capture(do_append)
+    res["append_s"], _ = time_graph(g_app)
+    del g_app
+    if wd is not None:
+        g_dec = capture(do_decode)
+        res["decode_s"], _ = time_graph(g_dec)
+        assert torch.equal(outd, ref_d), "graph replay of decode differs from eager"
+        del g_dec
+    if wp is not None:
+        g_pre = capture(do_prefill)
+        res["prefill_s"], _ = time_graph(g_pre)
+        del g_pre
+
+    # ---- paged dequantize of the decode batch (reported, not part of the step)
+    deq = None
+    if wd is not None:
+        rows = int(wd.seq_lens.sum())
+        cu = np.zeros(wd.num_seqs, np.int32)
+        cu[1:] = np.cumsum(wd.seq_lens)[:-1]
+        cud = i32(cu)
+        ok = torch.empty((rows, Hkv, D), dtype=torch.bfloat16, device=dev)
+        ov = torch.empty_like(ok)
+        do_deq = lambda r: nvk.dequant_paged(pools[r], btd, sld, cud, maxd, k_scale, v_scale, ok, ov)
+        g_deq = capture(do_deq)
+        deq_s, _ = time_graph(g_deq)
+        del g_deq
+        deq_bytes = rows * Hkv * 2 * (fd + 2 * D) + 4 * int(np.sum((wd.seq_lens + bs - 1) // bs))
+        deq = {"gbs": round(deq_bytes / (deq_s / K) / 1e9, 1), "us": round(deq_s / K * 1e6, 2)}
+        del ok, ov
+
+    # ---- algorithmic work
+    out = {"metric": METRIC, "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+           "ms_per_step": round(step_wall_s / K * 1e3, 5), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "f16", "data": "synthetic"}
+    app_bytes = n_new * (Hkv * (2 * 2 * D + 2 * fd) + 8)
+    app_us = res["append_s"] / K * 1e6
+    extra = {"append_mtok_s": round(n_new / (res["append_s"] / K) / 1e6, 3), "append_us": round(app_us, 2),
+             "append_gbs": round(app_bytes / (res["append_s"] / K) / 1e9, 1),
+             "step_gpu_us": round(step_gpu_s / K * 1e6, 2)}
+    roof = None
+    if wd is not None:
+        dec_bytes = (int(wd.seq_lens.astype(np.int64).sum()) * Hkv * 2 * fd + 2 * wd.num_seqs * Hq * D * 2
+                     + 4 * int(np.sum((wd.seq_lens + bs - 1) // bs)) + 4 * wd.num_seqs)
+        dec_s = res["decode_s"] / K
+        gbs = dec_bytes / dec_s / 1e9
+        out["value"] = round(gbs, 1)
+        extra.update({"decode_us": round(dec_s * 1e6, 2), "decode_pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
+                      "decode_bytes": dec_bytes})
+        traffic = read_traffic(args.workload)
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": "decode_split_kernel",
+                "bytes_per_launch": dec_bytes, "avg_launch_us": round(dec_s * 1e6, 3)}
+    if wp is not None:
+        pairs = 0
+        for b in range(wp.num_seqs):
+            L, q = int(wp.seq_lens[b]), int(wp.q_lens[b])
+            pairs += q * (L - q) + q * (q + 1) // 2
+        flops = 4.0 * D * Hq * pairs
+        pre_s = res["prefill_s"] / K
+        extra.update({"prefill_us": round(pre_s * 1e6, 2), "prefill_tflops": round(flops / pre_s / 1e12, 2),
+                      "prefill_pct_of_mfma_peak": round(100 * flops / pre_s / 1e12 / MFMA_F16_PEAK_TFLOPS, 2)})
+        if wd is None:
+            out["value"] = round(flops / pre_s / 1e12, 2)
+            out["unit"] = "TFLOP/s"
+            roof = {"bound": "mfma", "achieved": round(flops / pre_s / 1e12, 2), "peak": MFMA_F16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(flops / pre_s / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+                    "traffic": None, "kernel": "prefill_kernel", "flops_per_launch": flops,
+                    "avg_launch_us": round(pre_s * 1e6, 3)}
+    if deq is not None:
+        extra["dequant_gbs"] = deq["gbs"]
+        extra["dequant_us"] = deq["us"]
+    out["config"] = {"workload": w.name, "num_seqs": B, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
+                     "block_size": bs, "total_tokens": int(w.seq_lens.sum()), "new_tokens": n_new,
+                     "decode_seqs": int(len(dec_idx)), "prefill_seqs": int(len(pre_idx)), "kv_dtype": "nvfp4",
+                     "pool_copies": copies, "pool_bytes": pool_bytes, "seed": cfg}
+    out["roofline"] = roof
+    out.update(extra)
+    out["source_hash"] = source_hash()
+    out["input_gen_s"] = round(gen_s, 2)
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, dec_idx, pre_idx, cached, sm_scale)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(w, dec_idx, pre_idx, cached, sm_scale):
+    """The oracle, untuned, on a bounded sample of the same step: quantize-
+    append of the sampled sequences' new tokens, then their attention. The
+    cached prefix of the sample is quantised beforehand (not timed)."""
+    import numpy as np
+    from oracle import nvfp4_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    # sample: whole sequences, decode ones first, up to ~300k (token, kv head) rows
+    order = list(dec_idx) + list(pre_idx)
+    budget, picked = 300_000, []
+    for b in order:
+        if picked and sum(int(w.seq_lens[x]) for x in picked) * w.num_kv_heads + int(w.seq_lens[b]) * w.num_kv_heads > budget:
+            break
+        picked.append(b)
+    ws = w.subset(np.array(picked))
+    cm = ws.cached_mask()
+    pool = np.zeros(O.pool_shape(ws.num_blocks, ws.block_size, ws.num_kv_heads, ws.head_size), np.uint8)
+    O.append(pool, ws.key[cm], ws.value[cm], ws.slot_mapping[cm], ws.k_scale, ws.v_scale)
+    fd = ws.full_dim
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        O.append(pool, ws.key[~cm], ws.value[~cm], ws.slot_mapping[~cm], ws.k_scale, ws.v_scale)
+        O.paged_attention(pool, ws.query, ws.cu_q, ws.block_table, ws.seq_lens, ws.k_scale, ws.v_scale,
+                          np.float32(sm_scale), ws.head_size)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= 10.0 or reps >= 20:
+            break
+    per = el / reps
+    dec_bytes = int(ws.seq_lens.astype(np.int64).sum()) * ws.num_kv_heads * 2 * fd
+    return {"value": round(dec_bytes / per / 1e9, 4), "unit": "GB/s", "cores": int(blas_threads),
+            "kind": "oracle", "seconds_per_step": round(per, 3),
+            "sample": f"{len(picked)} of {w.num_seqs} sequences ({int(ws.seq_lens.sum())} tokens): oracle append "
+                      f"of their new tokens + attention, {reps} reps; value = their cache bytes / time"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,5 +1,5 @@
-// Paged attention over the NVFP4 cache: split-K decode (+ combine) and
-// chunked prefill [P40177 "Implementation breakdown" 1 and 3; RFC47684
+// Paged attention over the NVFP4 cache: split-K decode (the split merge is
+// done by the last-arriving workgroup of each sequence) and chunked prefill [P40177 "Implementation breakdown" 1 and 3; RFC47684
 // "Cause analysis": the paged read path].
 #include "attn_core.hpp"
 #include "launch.hpp"
@@ -10,13 +10,14 @@ namespace nvfp4kv {
 // Decode schedule. A unit is (sequence, split, kv head); a split is a run of
 // `tps` 32-key steps. tps is chosen on the device from the actual lengths so
 // that the batch yields about kDecodeTarget units of equal size, which keeps
-// ragged batches balanced without a host round trip. Every workgroup (and
-// the combine kernel) derives the same schedule: per-sequence unit counts
-// and their exclusive prefix sum in LDS.
+// ragged batches balanced without a host round trip. Every workgroup derives
+// the same schedule: per-sequence unit counts and their exclusive prefix sum
+// in LDS.
 // ---------------------------------------------------------------------------
 constexpr int kDecodeTarget = 1024;
 constexpr int kDecodeMinTps = 4;
 constexpr int kStep = 32;
+constexpr int kMergeCols = 8;  // columns merged per LDS round
 
 __device__ __forceinline__ int clamp_len(int L, int cap) { return L < 0 ? 0 : (L > cap ? cap : L); }
 
@@ -66,11 +67,12 @@ __device__ void decode_schedule(const int32_t* __restrict__ seq_lens, int B, int
   int t = (int)((work + kDecodeTarget - 1) / kDecodeTarget);
   tps = t < kDecodeMinTps ? kDecodeMinTps : t;
   int units_local = 0;
-  for (int b = b0; b < b1; ++b) units_local += ceil_div(s_pref[b], tps);
+  // a sequence without keys still gets one (empty) unit, which writes zeros
+  for (int b = b0; b < b1; ++b) units_local += max(1, ceil_div(s_pref[b], tps));
   int total;
   int run = block_excl_scan(units_local, s_red, total);
   for (int b = b0; b < b1; ++b) {
-    const int n = ceil_div(s_pref[b], tps);
+    const int n = max(1, ceil_div(s_pref[b], tps));
     s_pref[b] = run;
     run += n;
   }
@@ -92,11 +94,49 @@ struct DecodeArgs {
   const float* v_scale;
   float sm_scale;
   uint16_t* out;
-  float* ws_o;   // [slot][grp][D]   normalised partial outputs
-  float* ws_ml;  // [slot][grp][2]   (max, sum) of each partial, base-2 scores
+  uint32_t* ws_cnt;  // [B * hkv] arrival counters; zero between calls
+  float* ws_o;       // [slot][grp][D]   normalised partial outputs
+  float* ws_ml;      // [slot][grp][2]   (max, sum) of each partial, base-2 scores
 };
 
 __host__ __device__ inline int decode_lds_pref_ints(int B) { return ((B + 1 + 3) / 4) * 4; }
+
+// Merge the n partial results of (b, h) (slots slot0, slot0 + hkv, ...) into
+// the bf16 output. s_w: 2 * grp floats of scratch LDS.
+template <int D>
+__device__ void combine_splits(const DecodeArgs& a, int b, int h, int64_t slot0, int n, float* s_w) {
+  const int hkv = a.pool.hkv;
+  const int grp = a.grp;
+  if ((int)threadIdx.x < grp) {
+    const int col = threadIdx.x;
+    float M = -__builtin_inff();
+    for (int s = 0; s < n; ++s) M = __builtin_fmaxf(M, a.ws_ml[((slot0 + (int64_t)s * hkv) * grp + col) * 2]);
+    float lt = 0.0f;
+    for (int s = 0; s < n; ++s) {
+      const float* ml = a.ws_ml + ((slot0 + (int64_t)s * hkv) * grp + col) * 2;
+      lt += (ml[0] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(ml[0] - M) * ml[1];
+    }
+    s_w[2 * col] = M;
+    s_w[2 * col + 1] = lt > 0.0f ? 1.0f / lt : 0.0f;
+  }
+  __syncthreads();
+  const float gv = *a.v_scale;
+  uint16_t* out = a.out + ((int64_t)b * a.hq + h * grp) * D;
+  for (int e = threadIdx.x; e < grp * D; e += 256) {
+    const int col = e / D;
+    const int d = e - col * D;
+    const float M = s_w[2 * col];
+    const float inv = s_w[2 * col + 1];
+    float o = 0.0f;
+    for (int s = 0; s < n; ++s) {
+      const int64_t sl = (slot0 + (int64_t)s * hkv) * grp + col;
+      const float* ml = a.ws_ml + sl * 2;
+      const float f = (ml[0] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(ml[0] - M) * ml[1];
+      o += f * a.ws_o[sl * D + d];
+    }
+    out[e] = (uint16_t)(pack_bf16x2(o * inv * gv, 0.0f) & 0xFFFFu);
+  }
+}
 
 template <int D>
 __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
@@ -105,7 +145,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   int* s_pref = reinterpret_cast<int*>(smem);
   int* s_red = s_pref + decode_lds_pref_ints(a.B);
   float* s_ml = reinterpret_cast<float*>(s_red + 16);  // [4 waves][16 cols][2]
-  float* s_o = s_ml + 4 * 16 * 2;                       // [4 waves][grp][D]
+  float* s_o = s_ml + 4 * 16 * 2;                       // [4 waves][kMergeCols][D]
 
   const int hkv = a.pool.hkv;
   const int cap = a.max_blocks * a.pool.bs;
@@ -154,113 +194,84 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
       cur[1] = nxt[1];
     }
 
-    // ---- merge the four waves' partial softmax states through LDS
+    // ---- merge the four waves' partial softmax states through LDS, eight
+    // columns at a time
     const float lsum = wave_sum_j(W.l[0]);
     if (j == 0) {
       s_ml[(w * 16 + i) * 2] = W.m[0];
       s_ml[(w * 16 + i) * 2 + 1] = lsum;
     }
-    if (valid) {
-      float* dst = s_o + (w * grp + i) * D;
+    for (int c0 = 0; c0 < grp; c0 += kMergeCols) {
+      const int nc = (grp - c0 < kMergeCols) ? grp - c0 : kMergeCols;
+      if (i >= c0 && i < c0 + nc) {
+        float* dst = s_o + (w * kMergeCols + (i - c0)) * D;
 #pragma unroll
-      for (int t = 0; t < G::DPL; ++t)
+        for (int t = 0; t < G::DPL; ++t)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) dst[(4 * j + r) * G::DPL + t] = W.acc[0][t][r];
-    }
-    __syncthreads();
-    for (int e = threadIdx.x; e < grp * D; e += 256) {
-      const int col = e / D;
-      const int d = e - col * D;
-      float M = -__builtin_inff();
-#pragma unroll
-      for (int ww = 0; ww < 4; ++ww) M = __builtin_fmaxf(M, s_ml[(ww * 16 + col) * 2]);
-      float lt = 0.0f, o = 0.0f;
-#pragma unroll
-      for (int ww = 0; ww < 4; ++ww) {
-        const float mw = s_ml[(ww * 16 + col) * 2];
-        const float f = (mw == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
-        lt += f * s_ml[(ww * 16 + col) * 2 + 1];
-        o += f * s_o[(ww * grp + col) * D + d];
+          for (int r = 0; r < 4; ++r) dst[(4 * j + r) * G::DPL + t] = W.acc[0][t][r];
       }
-      const float on = lt > 0.0f ? o / lt : 0.0f;
-      if (nsplit == 1) {
-        const float y = on * gv;
-        a.out[((int64_t)b * a.hq + h * grp + col) * D + d] = (uint16_t)(pack_bf16x2(y, 0.0f) & 0xFFFFu);
-      } else {
-        const int64_t slot = (int64_t)ubs * hkv + h;
-        a.ws_o[(slot * grp + col) * D + d] = on;
-        if (d == 0) {
-          a.ws_ml[(slot * grp + col) * 2] = M;
-          a.ws_ml[(slot * grp + col) * 2 + 1] = lt;
+      __syncthreads();
+      for (int e = threadIdx.x; e < nc * D; e += 256) {
+        const int cc = e / D;
+        const int col = c0 + cc;
+        const int d = e - cc * D;
+        float M = -__builtin_inff();
+#pragma unroll
+        for (int ww = 0; ww < 4; ++ww) M = __builtin_fmaxf(M, s_ml[(ww * 16 + col) * 2]);
+        float lt = 0.0f, o = 0.0f;
+#pragma unroll
+        for (int ww = 0; ww < 4; ++ww) {
+          const float mw = s_ml[(ww * 16 + col) * 2];
+          const float f = (mw == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
+          lt += f * s_ml[(ww * 16 + col) * 2 + 1];
+          o += f * s_o[(ww * kMergeCols + cc) * D + d];
+        }
+        const float on = lt > 0.0f ? o / lt : 0.0f;
+        if (nsplit == 1) {
+          const float y = on * gv;
+          a.out[((int64_t)b * a.hq + h * grp + col) * D + d] = (uint16_t)(pack_bf16x2(y, 0.0f) & 0xFFFFu);
+        } else {
+          const int64_t slot = (int64_t)ubs * hkv + h;
+          a.ws_o[(slot * grp + col) * D + d] = on;
+          if (d == 0) {
+            a.ws_ml[(slot * grp + col) * 2] = M;
+            a.ws_ml[(slot * grp + col) * 2 + 1] = lt;
+          }
         }
       }
+      __syncthreads();
     }
-    __syncthreads();
+    if (nsplit > 1) {
+      // The last of the sequence's splits to arrive merges all of them
+      // (log-sum-exp weights) and resets the counter for the next call.
+      __threadfence();
+      __syncthreads();
+      if (threadIdx.x == 0) s_red[8] = (atomicAdd(&a.ws_cnt[(int64_t)b * hkv + h], 1u) == (uint32_t)(nsplit - 1));
+      __syncthreads();
+      if (s_red[8]) {
+        __threadfence();
+        combine_splits<D>(a, b, h, (int64_t)s_pref[b] * hkv + h, nsplit, s_ml);
+        if (threadIdx.x == 0) atomicExch(&a.ws_cnt[(int64_t)b * hkv + h], 0u);
+      }
+      __syncthreads();
+    }
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
-  extern __shared__ __align__(16) char smem[];
-  int* s_pref = reinterpret_cast<int*>(smem);
-  int* s_red = s_pref + decode_lds_pref_ints(a.B);
-  float* s_w = reinterpret_cast<float*>(s_red + 16);  // [16 cols][2]: max, 1/sum
-  const int hkv = a.pool.hkv;
-  const int cap = a.max_blocks * a.pool.bs;
-  int tps, total;
-  decode_schedule(a.seq_lens, a.B, cap, hkv, s_pref, s_red, tps, total);
-  const int grp = a.grp;
-  const float gv = *a.v_scale;
-  for (int u = blockIdx.x; u < a.B * hkv; u += gridDim.x) {
-    const int b = u / hkv;
-    const int h = u - b * hkv;
-    const int n = s_pref[b + 1] - s_pref[b];
-    if (n == 1) continue;  // the split kernel wrote this output directly
-    uint16_t* out = a.out + ((int64_t)b * a.hq + h * grp) * D;
-    if (n == 0) {  // no keys: zeros
-      for (int e = threadIdx.x; e < grp * D; e += 256) out[e] = 0;
-      continue;
-    }
-    const int64_t slot0 = (int64_t)s_pref[b] * hkv + h;
-    if ((int)threadIdx.x < grp) {
-      const int col = threadIdx.x;
-      float M = -__builtin_inff();
-      for (int s = 0; s < n; ++s) M = __builtin_fmaxf(M, a.ws_ml[((slot0 + (int64_t)s * hkv) * grp + col) * 2]);
-      float lt = 0.0f;
-      for (int s = 0; s < n; ++s) {
-        const float* ml = a.ws_ml + ((slot0 + (int64_t)s * hkv) * grp + col) * 2;
-        lt += (ml[0] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(ml[0] - M) * ml[1];
-      }
-      s_w[2 * col] = M;
-      s_w[2 * col + 1] = lt > 0.0f ? 1.0f / lt : 0.0f;
-    }
-    __syncthreads();
-    for (int e = threadIdx.x; e < grp * D; e += 256) {
-      const int col = e / D;
-      const int d = e - col * D;
-      const float M = s_w[2 * col];
-      const float inv = s_w[2 * col + 1];
-      float o = 0.0f;
-      for (int s = 0; s < n; ++s) {
-        const int64_t sl = (slot0 + (int64_t)s * hkv) * grp + col;
-        const float* ml = a.ws_ml + sl * 2;
-        const float f = (ml[0] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(ml[0] - M) * ml[1];
-        o += f * a.ws_o[sl * D + d];
-      }
-      out[e] = (uint16_t)(pack_bf16x2(o * inv * gv, 0.0f) & 0xFFFFu);
-    }
-    __syncthreads();
-  }
+// Workspace: [counters, padded to 256 B][partial outputs][partial (max, sum)].
+static int64_t counter_bytes(int num_seqs, int num_kv_heads) {
+  return (((int64_t)num_seqs * num_kv_heads * 4 + 255) / 256) * 256;
 }
 
 size_t decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_size) {
   const int64_t grp = num_q_heads / num_kv_heads;
   const int64_t slots = kDecodeTarget + (int64_t)num_seqs * num_kv_heads;
-  return (size_t)(slots * grp * head_size * 4 + slots * grp * 2 * 4);
+  return (size_t)(counter_bytes(num_seqs, num_kv_heads) + slots * grp * head_size * 4 + slots * grp * 2 * 4);
 }
 
 size_t decode_lds_bytes(int num_seqs, int grp, int head_size) {
-  return (size_t)(decode_lds_pref_ints(num_seqs) + 16) * 4 + 4 * 16 * 2 * 4 + (size_t)4 * grp * head_size * 4;
+  (void)grp;
+  return (size_t)(decode_lds_pref_ints(num_seqs) + 16) * 4 + 4 * 16 * 2 * 4 + (size_t)4 * kMergeCols * head_size * 4;
 }
 
 template <int D>
@@ -274,11 +285,6 @@ static hipError_t launch_decode_t(const DecodeArgs& a, int max_seq_len, hipStrea
   const int grid = (int)(want < kDecodeTarget ? want : kDecodeTarget);
   const size_t lds_split = decode_lds_bytes(a.B, a.grp, D);
   decode_split_kernel<D><<<grid, 256, lds_split, stream>>>(a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const size_t lds_comb = (size_t)(decode_lds_pref_ints(a.B) + 16) * 4 + 16 * 2 * 4;
-  const int cgrid = a.B * hkv;
-  decode_combine_kernel<D><<<cgrid, 256, lds_comb, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -303,7 +309,8 @@ hipError_t launch_decode(const Pool& pool, int head_size, const void* q, int64_t
   a.sm_scale = sm_scale;
   a.out = static_cast<uint16_t*>(out);
   const int64_t slots = kDecodeTarget + (int64_t)num_seqs * pool.hkv;
-  a.ws_o = static_cast<float*>(workspace);
+  a.ws_cnt = static_cast<uint32_t*>(workspace);
+  a.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + counter_bytes(num_seqs, pool.hkv));
   a.ws_ml = a.ws_o + slots * a.grp * head_size;
   switch (head_size) {
     case 64: return launch_decode_t<64>(a, max_seq_len, stream);

@@ -141,12 +141,15 @@ size_t nvfp4_paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num
  *   of 8), last axis contiguous, 16-byte aligned. out: bf16 [num_seqs,
  *   num_q_heads, head_size] contiguous. A sequence with no key yields zeros.
  * num_q_heads / num_kv_heads must be an integer in [1, 16]; num_seqs <= 4096.
- * max_seq_len is ignored by the schedule (kept for symmetry with prefill);
- * lengths are clamped to max_blocks_per_seq * block_size on the device.
+ * max_seq_len: host upper bound of seq_lens, used only to size the grid (a
+ * wrong value costs speed, not correctness); lengths are clamped to
+ * max_blocks_per_seq * block_size on the device.
  * workspace: device scratch of at least
- *   nvfp4_paged_attention_decode_workspace_size(...) bytes, 16-byte aligned;
- *   its contents need not be initialised. Calls that share a workspace must
- *   be ordered on one stream.
+ *   nvfp4_paged_attention_decode_workspace_size(...) bytes, 16-byte aligned,
+ *   ZERO-FILLED before its first use. It holds per-(sequence, kv head)
+ *   arrival counters that every completed call leaves at zero again, so one
+ *   zero fill at allocation suffices. Calls that share a workspace must be
+ *   ordered on one stream.
  */
 nvfp4kv_status nvfp4_paged_attention_decode(const nvfp4kv_cache* cache,
                                             const void* q, int64_t q_stride_token, int64_t q_stride_head,

@@ -59,7 +59,7 @@ class Dev:
         w = self.w
         q = self.query if q is None else q
         out = torch.empty((w.num_seqs, w.num_q_heads, w.head_size), dtype=torch.bfloat16, device=q.device)
-        ws = torch.empty(nvk.decode_workspace_size(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_size),
+        ws = torch.zeros(nvk.decode_workspace_size(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_size),
                          dtype=torch.uint8, device=q.device)
         nvk.paged_attention_decode(self.pool, q, self.bt, self.seq_lens, int(w.seq_lens.max(initial=0)),
                                    self.k_scale, self.v_scale, self.sm_scale, out, ws)

@@ -215,3 +215,64 @@ def test_append_strided_inputs():
     append(d.pool, big_k[:, :, 1], big_v[:, :, 2], d.slots, d.k_scale, d.v_scale)
     torch.cuda.synchronize()
     assert np.array_equal(d.pool_logical(), oracle_pool(w))
+
+
+def _decode_setup(scale=0.05):
+    w = make_config(2, scale=scale)
+    d = Dev(w, "HND")
+    d.append_all()
+    ws = torch.zeros(__import__("bit_quantized_paged_amd").decode_workspace_size(
+        w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_size), dtype=torch.uint8, device="cuda")
+    return w, d, ws
+
+
+def _decode_into(d, ws, out, max_len):
+    import bit_quantized_paged_amd as nvk
+    nvk.paged_attention_decode(d.pool, d.query, d.bt, d.seq_lens, max_len, d.k_scale, d.v_scale, d.sm_scale,
+                               out, ws)
+
+
+def test_decode_workspace_reuse_is_stable():
+    """The split-merge counters are left at zero: repeated calls on one
+    workspace, with a different batch in between, give identical results and
+    leave the counter region zeroed."""
+    w, d, ws = _decode_setup()
+    out1 = torch.empty((w.num_seqs, w.num_q_heads, w.head_size), dtype=torch.bfloat16, device="cuda")
+    out2 = torch.empty_like(out1)
+    _decode_into(d, ws, out1, int(w.seq_lens.max()))
+    w3 = make_config(3, scale=0.004)
+    d3 = Dev(w3, "HND")
+    d3.append_all()
+    d3.decode()
+    for _ in range(3):
+        _decode_into(d, ws, out2, int(w.seq_lens.max()))
+        torch.cuda.synchronize()
+        assert torch.equal(out1, out2)
+    cnt_bytes = ((w.num_seqs * w.num_kv_heads * 4 + 255) // 256) * 256
+    assert int(ws[:cnt_bytes].sum().item()) == 0
+
+
+def test_decode_graph_replays_match_eager():
+    """Captured into a HIP graph (as the benchmark runs it), every replay
+    reproduces the eager result, with eager work between replays."""
+    w, d, ws = _decode_setup()
+    eager = torch.empty((w.num_seqs, w.num_q_heads, w.head_size), dtype=torch.bfloat16, device="cuda")
+    _decode_into(d, ws, eager, int(w.seq_lens.max()))
+    torch.cuda.synchronize()
+    out = torch.zeros_like(eager)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            _decode_into(d, ws, out, int(w.seq_lens.max()))
+    torch.cuda.current_stream().wait_stream(s)
+    for k in range(4):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {k}"
+        tmp = torch.empty_like(eager)
+        _decode_into(d, ws, tmp, int(w.seq_lens.max()))
+        torch.cuda.synchronize()
+        assert torch.equal(tmp, eager)
