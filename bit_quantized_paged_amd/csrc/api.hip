@@ -47,6 +47,8 @@ nvfp4kv_status check_cache(const nvfp4kv_cache* c, nvfp4kv::Pool& p) {
   for (int k = 0; k < 4; ++k)
     if (s[k] < 0 || s[k] % 4 != 0)
       return fail(NVFP4KV_INVALID_ARGUMENT, "cache strides must be non-negative multiples of 4 bytes");
+  // rows of a page are addressed with 32-bit offsets
+  if (c->stride_token > (1 << 26)) return fail(NVFP4KV_UNSUPPORTED, "stride_token above 2^26 bytes");
   p.data = c->data;
   p.num_blocks = c->num_blocks;
   p.sb = c->stride_block;
@@ -54,6 +56,7 @@ nvfp4kv_status check_cache(const nvfp4kv_cache* c, nvfp4kv::Pool& p) {
   p.st = c->stride_token;
   p.sh = c->stride_head;
   p.bs = c->block_size;
+  p.bs_log2 = c->block_size == 16 ? 4 : (c->block_size == 32 ? 5 : 6);
   p.hkv = c->num_kv_heads;
   return ok();
 }

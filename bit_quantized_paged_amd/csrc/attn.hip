@@ -21,6 +21,21 @@ constexpr int kMergeCols = 8;  // columns merged per LDS round
 
 __device__ __forceinline__ int clamp_len(int L, int cap) { return L < 0 ? 0 : (L > cap ? cap : L); }
 
+// Agent-scope (all XCDs) coherent store / load of a split-K partial.
+__device__ __forceinline__ void st_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until this wave's stores have completed (s_waitcnt vmcnt(0)); the
+// signal fences keep the compiler from moving memory operations across it.
+__device__ __forceinline__ void wait_stores() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 __device__ __forceinline__ int wave_incl_scan(int v) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
@@ -110,11 +125,12 @@ __device__ void combine_splits(const DecodeArgs& a, int b, int h, int64_t slot0,
   if ((int)threadIdx.x < grp) {
     const int col = threadIdx.x;
     float M = -__builtin_inff();
-    for (int s = 0; s < n; ++s) M = __builtin_fmaxf(M, a.ws_ml[((slot0 + (int64_t)s * hkv) * grp + col) * 2]);
+    for (int s = 0; s < n; ++s) M = __builtin_fmaxf(M, ld_agent(a.ws_ml + ((slot0 + (int64_t)s * hkv) * grp + col) * 2));
     float lt = 0.0f;
     for (int s = 0; s < n; ++s) {
       const float* ml = a.ws_ml + ((slot0 + (int64_t)s * hkv) * grp + col) * 2;
-      lt += (ml[0] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(ml[0] - M) * ml[1];
+      const float m0 = ld_agent(ml);
+      lt += (m0 == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(m0 - M) * ld_agent(ml + 1);
     }
     s_w[2 * col] = M;
     s_w[2 * col + 1] = lt > 0.0f ? 1.0f / lt : 0.0f;
@@ -130,9 +146,9 @@ __device__ void combine_splits(const DecodeArgs& a, int b, int h, int64_t slot0,
     float o = 0.0f;
     for (int s = 0; s < n; ++s) {
       const int64_t sl = (slot0 + (int64_t)s * hkv) * grp + col;
-      const float* ml = a.ws_ml + sl * 2;
-      const float f = (ml[0] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(ml[0] - M) * ml[1];
-      o += f * a.ws_o[sl * D + d];
+      const float m0 = ld_agent(a.ws_ml + sl * 2);
+      const float f = (m0 == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(m0 - M) * ld_agent(a.ws_ml + sl * 2 + 1);
+      o += f * ld_agent(a.ws_o + sl * D + d);
     }
     out[e] = (uint16_t)(pack_bf16x2(o * inv * gv, 0.0f) & 0xFFFFu);
   }
@@ -151,24 +167,31 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   const int cap = a.max_blocks * a.pool.bs;
   int tps, total;
   decode_schedule(a.seq_lens, a.B, cap, hkv, s_pref, s_red, tps, total);
+  tps = __builtin_amdgcn_readfirstlane(tps);
+  total = __builtin_amdgcn_readfirstlane(total);
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int i = lane & 15, j = lane >> 4;
   const int grp = a.grp;
   const float qk_factor = a.sm_scale * (*a.k_scale) * kLog2e;
   const float gv = *a.v_scale;
+  const LaneOffsets<D> off = lane_offsets<D>(a.pool.st, i, j);
 
   for (int u = blockIdx.x; u < total * hkv; u += gridDim.x) {
     const int ubs = u / hkv;
     const int h = u - ubs * hkv;
+    // sequence of this unit: last b with s_pref[b] <= ubs (values read from
+    // LDS are made wave-uniform so that everything below stays scalar)
     int lo = 0, hi = a.B;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (s_pref[mid] <= ubs) lo = mid; else hi = mid;
+      if (__builtin_amdgcn_readfirstlane(s_pref[mid]) <= ubs) lo = mid; else hi = mid;
     }
     const int b = lo;
-    const int split = ubs - s_pref[b];
-    const int nsplit = s_pref[b + 1] - s_pref[b];
+    const int pb = __builtin_amdgcn_readfirstlane(s_pref[b]);
+    const int split = ubs - pb;
+    const int nsplit = __builtin_amdgcn_readfirstlane(s_pref[b + 1]) - pb;
     const int L = clamp_len(a.seq_lens[b], cap);
     const int steps = ceil_div(L, kStep);
     const int st0 = split * tps;
@@ -182,16 +205,27 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     W.lim[0] = valid ? L - 1 : -1;
     const int32_t* bt_row = a.bt + (int64_t)b * a.max_blocks;
 
-    SubRaw<D> cur[2], nxt[2];
+    // Software pipeline over the wave's steps (k, k+4, ...): two register
+    // buffers, data one step ahead, block ids two steps ahead. Loads past the
+    // wave's range read nothing (zero-size descriptors).
     int k = st0 + w;
-    if (k < st1) load_step<D>(cur, a.pool, bt_row, h, k * kStep, L, i, j);
-    for (; k < st1; k += 4) {
-      const int kn = k + 4;
-      if (kn < st1) load_step<D>(nxt, a.pool, bt_row, h, kn * kStep, L, i, j);
-      mask_step<D>(cur, k * kStep, L, j);
-      W.step(cur, k * kStep, j);
-      cur[0] = nxt[0];
-      cur[1] = nxt[1];
+    if (k < st1) {
+      SubRaw<D> A[2], B[2];
+      load_step<D>(A, a.pool, step_ids(bt_row, k * kStep, L, a.pool), h, k * kStep, off);
+      StepIds ib = step_ids(bt_row, (k + 4) * kStep, k + 4 < st1 ? L : 0, a.pool);
+      while (true) {
+        load_step<D>(B, a.pool, ib, h, (k + 4) * kStep, off);
+        const StepIds ia = step_ids(bt_row, (k + 8) * kStep, k + 8 < st1 ? L : 0, a.pool);
+        mask_step<D>(A, k * kStep, L, j);
+        W.step(A, k * kStep, j);
+        if (k + 4 >= st1) break;
+        load_step<D>(A, a.pool, ia, h, (k + 8) * kStep, off);
+        ib = step_ids(bt_row, (k + 12) * kStep, k + 12 < st1 ? L : 0, a.pool);
+        mask_step<D>(B, (k + 4) * kStep, L, j);
+        W.step(B, (k + 4) * kStep, j);
+        k += 8;
+        if (k >= st1) break;
+      }
     }
 
     // ---- merge the four waves' partial softmax states through LDS, eight
@@ -232,10 +266,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
           a.out[((int64_t)b * a.hq + h * grp + col) * D + d] = (uint16_t)(pack_bf16x2(y, 0.0f) & 0xFFFFu);
         } else {
           const int64_t slot = (int64_t)ubs * hkv + h;
-          a.ws_o[(slot * grp + col) * D + d] = on;
+          st_agent(a.ws_o + (slot * grp + col) * D + d, on);
           if (d == 0) {
-            a.ws_ml[(slot * grp + col) * 2] = M;
-            a.ws_ml[(slot * grp + col) * 2 + 1] = lt;
+            st_agent(a.ws_ml + (slot * grp + col) * 2, M);
+            st_agent(a.ws_ml + (slot * grp + col) * 2 + 1, lt);
           }
         }
       }
@@ -244,14 +278,19 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     if (nsplit > 1) {
       // The last of the sequence's splits to arrive merges all of them
       // (log-sum-exp weights) and resets the counter for the next call.
-      __threadfence();
+      // Partials travel through agent-coherent stores and loads (they
+      // bypass the per-XCD L2), so the hand-off needs only every store to
+      // have completed before the counter moves, not an L2 flush.
+      wait_stores();
       __syncthreads();
-      if (threadIdx.x == 0) s_red[8] = (atomicAdd(&a.ws_cnt[(int64_t)b * hkv + h], 1u) == (uint32_t)(nsplit - 1));
+      if (threadIdx.x == 0)
+        s_red[8] = (__hip_atomic_fetch_add(&a.ws_cnt[(int64_t)b * hkv + h], 1u, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(nsplit - 1));
       __syncthreads();
       if (s_red[8]) {
-        __threadfence();
         combine_splits<D>(a, b, h, (int64_t)s_pref[b] * hkv + h, nsplit, s_ml);
-        if (threadIdx.x == 0) atomicExch(&a.ws_cnt[(int64_t)b * hkv + h], 0u);
+        if (threadIdx.x == 0)
+          __hip_atomic_store(&a.ws_cnt[(int64_t)b * hkv + h], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       __syncthreads();
     }
@@ -360,7 +399,8 @@ __device__ __forceinline__ void store_column(uint16_t* orow, const f4 (&acc)[Geo
 template <int D, int NT>
 __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   const int b = blockIdx.z, h = blockIdx.y, cb = blockIdx.x;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int i = lane & 15, j = lane >> 4;
   int q0 = a.cu_q[b], q1 = a.cu_q[b + 1];
   q0 = q0 < 0 ? 0 : (q0 > a.total_q ? a.total_q : q0);
@@ -394,14 +434,25 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   const int steps = ceil_div(kmax, kStep);
   const int32_t* bt_row = a.bt + (int64_t)b * a.max_blocks;
 
-  SubRaw<D> cur[2], nxt[2];
-  if (steps > 0) load_step<D>(cur, a.pool, bt_row, h, 0, L, i, j);
-  for (int k = 0; k < steps; ++k) {
-    if (k + 1 < steps) load_step<D>(nxt, a.pool, bt_row, h, (k + 1) * kStep, L, i, j);
-    mask_step<D>(cur, k * kStep, L, j);
-    W.step(cur, k * kStep, j);
-    cur[0] = nxt[0];
-    cur[1] = nxt[1];
+  const LaneOffsets<D> off = lane_offsets<D>(a.pool.st, i, j);
+  if (steps > 0) {
+    SubRaw<D> A[2], B[2];
+    load_step<D>(A, a.pool, step_ids(bt_row, 0, L, a.pool), h, 0, off);
+    StepIds ib = step_ids(bt_row, kStep, 1 < steps ? L : 0, a.pool);
+    int k = 0;
+    while (true) {
+      load_step<D>(B, a.pool, ib, h, (k + 1) * kStep, off);
+      const StepIds ia = step_ids(bt_row, (k + 2) * kStep, k + 2 < steps ? L : 0, a.pool);
+      mask_step<D>(A, k * kStep, L, j);
+      W.step(A, k * kStep, j);
+      if (k + 1 >= steps) break;
+      load_step<D>(A, a.pool, ia, h, (k + 2) * kStep, off);
+      ib = step_ids(bt_row, (k + 3) * kStep, k + 3 < steps ? L : 0, a.pool);
+      mask_step<D>(B, (k + 1) * kStep, L, j);
+      W.step(B, (k + 1) * kStep, j);
+      k += 2;
+      if (k >= steps) break;
+    }
   }
 
   const float gv = *a.v_scale;

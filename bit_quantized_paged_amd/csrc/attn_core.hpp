@@ -65,49 +65,76 @@ __device__ __forceinline__ void zero_sub(SubRaw<D>& R) {
   }
 }
 
-// kpage / vpage: first row of the (block, K|V, head) page; row0: first row of
-// the subtile inside the page.
+// Byte offsets of this lane's loads inside a 16-row subtile; they depend only
+// on the lane and the row stride, so a wave computes them once.
 template <int D>
-__device__ __forceinline__ void load_sub(SubRaw<D>& R, const uint8_t* kpage, const uint8_t* vpage, int64_t st,
-                                         int row0, int i, int j) {
-  const uint8_t* krow = kpage + (int64_t)(row0 + i) * st;
+struct LaneOffsets {
+  uint32_t k, ks, v[4], vs[4];
+};
+
+template <int D>
+__device__ __forceinline__ LaneOffsets<D> lane_offsets(int64_t st, int i, int j) {
+  LaneOffsets<D> o;
+  const uint32_t s = (uint32_t)st;
+  o.k = i * s + j * (D / 8);
+  o.ks = i * s + D / 2 + j * (D / 64);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    o.v[r] = (4 * j + r) * s + i * Geo<D>::VB;
+    o.vs[r] = (4 * j + r) * s + D / 2 + (i * Geo<D>::DPL) / 16;
+  }
+  return o;
+}
+
+// Pages are read with raw buffer loads: a wave-uniform descriptor per
+// subtile (base = first row of the subtile, size = the bytes its 16 rows
+// span) plus the lane offsets above. A subtile with nothing to read gets size
+// 0, which makes the hardware return zeros without touching memory, so the
+// loads of a step are issued unconditionally and every access is
+// range-checked against its own page.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;  // raw (unformatted) buffer, gfx9 family
+
+__device__ __forceinline__ rsrc_t make_rsrc(const uint8_t* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, bytes, kRsrcWord3);
+}
+
+template <int D>
+__device__ __forceinline__ void load_sub(SubRaw<D>& R, rsrc_t kr, rsrc_t vr, const LaneOffsets<D>& o) {
   if constexpr (D == 64) {
-    const u32x2 w = ld_u32x2(krow + j * 8);
+    const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(kr, o.k, 0, 0);
     R.k[0] = w[0];
     R.k[1] = w[1];
-    R.ks = ld_u8(krow + 32 + j);
+    R.ks = __builtin_amdgcn_raw_buffer_load_b8(kr, o.ks, 0, 0);
   } else if constexpr (D == 128) {
-    const u32x4 w = ld_u32x4(krow + j * 16);
+    const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(kr, o.k, 0, 0);
     R.k[0] = w[0];
     R.k[1] = w[1];
     R.k[2] = w[2];
     R.k[3] = w[3];
-    R.ks = ld_u16(krow + 64 + 2 * j);
+    R.ks = __builtin_amdgcn_raw_buffer_load_b16(kr, o.ks, 0, 0);
   } else {
-    const u32x4 w0 = ld_u32x4(krow + j * 32);
-    const u32x4 w1 = ld_u32x4(krow + j * 32 + 16);
+    const u32x4 w0 = __builtin_amdgcn_raw_buffer_load_b128(kr, o.k, 0, 0);
+    const u32x4 w1 = __builtin_amdgcn_raw_buffer_load_b128(kr, o.k + 16, 0, 0);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       R.k[c] = w0[c];
       R.k[4 + c] = w1[c];
     }
-    R.ks = ld_u32(krow + 128 + 4 * j);
+    R.ks = __builtin_amdgcn_raw_buffer_load_b32(kr, o.ks, 0, 0);
   }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const uint8_t* vrow = vpage + (int64_t)(row0 + 4 * j + r) * st;
     if constexpr (D == 64) {
-      R.v[r][0] = ld_u16(vrow + 2 * i);
-      R.vs[r] = ld_u8(vrow + 32 + (i >> 2));
+      R.v[r][0] = __builtin_amdgcn_raw_buffer_load_b16(vr, o.v[r], 0, 0);
     } else if constexpr (D == 128) {
-      R.v[r][0] = ld_u32(vrow + 4 * i);
-      R.vs[r] = ld_u8(vrow + 64 + (i >> 1));
+      R.v[r][0] = __builtin_amdgcn_raw_buffer_load_b32(vr, o.v[r], 0, 0);
     } else {
-      const u32x2 w = ld_u32x2(vrow + 8 * i);
+      const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(vr, o.v[r], 0, 0);
       R.v[r][0] = w[0];
       R.v[r][1] = w[1];
-      R.vs[r] = ld_u8(vrow + 128 + i);
     }
+    R.vs[r] = __builtin_amdgcn_raw_buffer_load_b8(vr, o.vs[r], 0, 0);
   }
 }
 
@@ -326,23 +353,49 @@ struct WaveAttn {
   }
 };
 
-// Issue the loads of the 32-key step at kb (subtiles past L are zeroed).
+// Block ids of the two 16-key subtiles of the step at kb and whether they
+// hold keys below `lim` (L for a step of this wave, 0 for a prefetch past the
+// wave's range). kb, lim and bt_row are wave-uniform.
+struct StepIds {
+  int32_t id[2];
+  bool ok[2];
+};
+
+// The block table is read-only for the whole kernel; reading it through the
+// constant address space lets these wave-uniform loads use the scalar cache,
+// so waiting for them never waits on the vector loads of the data pipeline.
+typedef __attribute__((address_space(4))) const int32_t const_i32;
+
+__device__ __forceinline__ int32_t ld_uniform(const int32_t* p, int idx) {
+  return ((const const_i32*)(uintptr_t)p)[idx];
+}
+
+__device__ __forceinline__ StepIds step_ids(const int32_t* bt_row, int kb, int lim, const Pool& pool) {
+  StepIds s;
+  s.ok[0] = kb < lim;
+  s.ok[1] = kb + 16 < lim;
+  const int page = kb >> pool.bs_log2;
+  s.id[0] = ld_uniform(bt_row, s.ok[0] ? page : 0);
+  s.id[1] = (pool.bs == 16) ? ld_uniform(bt_row, s.ok[1] ? page + 1 : 0) : s.id[0];
+  return s;
+}
+
+// Issue the loads of the 32-key step at kb.
 template <int D>
-__device__ __forceinline__ void load_step(SubRaw<D> (&R)[2], const Pool& pool, const int32_t* bt_row, int h, int kb,
-                                          int L, int i, int j) {
+__device__ __forceinline__ void load_step(SubRaw<D> (&R)[2], const Pool& pool, const StepIds& ids, int h, int kb,
+                                          const LaneOffsets<D>& o) {
+  const int extent = 15 * (int)pool.st + D / 2 + D / 16;
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb) {
-    const int k0 = kb + 16 * sb;
-    if (k0 < L) {
-      const int page = k0 / pool.bs;
-      const int row0 = k0 - page * pool.bs;
-      const int64_t blk = clamp_block(bt_row[page], pool.num_blocks);
-      const uint8_t* kpage = pool.data + blk * pool.sb + (int64_t)h * pool.sh;
-      load_sub<D>(R[sb], kpage, kpage + pool.skv, pool.st, row0, i, j);
-    } else {
-      zero_sub<D>(R[sb]);
-    }
+    const int row0 = (kb + 16 * sb) & (pool.bs - 1);
+    const int64_t blk = clamp_block(ids.id[sb], pool.num_blocks);
+    const uint8_t* kbase = pool.data + blk * pool.sb + (int64_t)h * pool.sh + (int64_t)row0 * pool.st;
+    const int n = ids.ok[sb] ? extent : 0;
+    load_sub<D>(R[sb], make_rsrc(kbase, n), make_rsrc(kbase + pool.skv, n), o);
   }
+  // keep the scheduler from hoisting work on the previous step's data above
+  // these loads (that would make their issue wait for that data)
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 template <int D>

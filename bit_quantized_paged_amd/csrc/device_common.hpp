@@ -37,15 +37,19 @@ struct Pool {
   int64_t num_blocks;
   int64_t sb, skv, st, sh;
   int32_t bs;
+  int32_t bs_log2;  // block_size is a power of two
   int32_t hkv;
 };
 
 __device__ __forceinline__ int64_t clamp_block(int32_t id, int64_t num_blocks) {
   // Out-of-range ids are a caller error; clamping keeps every access inside
-  // the pool so that bad metadata cannot fault the device.
-  int64_t v = id;
-  v = v < 0 ? 0 : v;
-  return v >= num_blocks ? num_blocks - 1 : v;
+  // the pool so that bad metadata cannot fault the device. num_blocks is
+  // below 2^31 (checked on the host), so 32-bit arithmetic suffices and stays
+  // on the scalar unit for wave-uniform ids.
+  const int32_t nb = (int32_t)num_blocks;
+  int32_t v = id < 0 ? 0 : id;
+  v = v >= nb ? nb - 1 : v;
+  return (int64_t)v;
 }
 
 // bf16 bits -> fp32 (exact).
