@@ -167,7 +167,7 @@ nvfp4kv_status nvfp4_paged_attention_decode(const nvfp4kv_cache* cache, const vo
   if (!block_table || !seq_lens) return fail(NVFP4KV_INVALID_ARGUMENT, "metadata pointer is NULL");
   if (!k_scale || !v_scale) return fail(NVFP4KV_INVALID_ARGUMENT, "k_scale/v_scale is NULL");
   if (out == nullptr || !aligned(out, 16)) return fail(NVFP4KV_INVALID_ARGUMENT, "out must be a 16-byte aligned pointer");
-  if (nvfp4kv::decode_lds_bytes(num_seqs, grp, cache->head_size) > 65536)
+  if (nvfp4kv::decode_lds_bytes(num_seqs, grp, cache->head_size) > 163840)
     return fail(NVFP4KV_UNSUPPORTED, "num_seqs / group size / head_size combination exceeds the LDS budget");
   const size_t need = nvfp4kv::decode_workspace_bytes(num_seqs, num_q_heads, p.hkv, cache->head_size);
   if (workspace == nullptr || workspace_bytes < need)

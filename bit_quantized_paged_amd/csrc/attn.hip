@@ -116,52 +116,107 @@ struct DecodeArgs {
 
 __host__ __device__ inline int decode_lds_pref_ints(int B) { return ((B + 1 + 3) / 4) * 4; }
 
+__device__ __forceinline__ float wave_max64(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum64(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// 16 agent-coherent bytes at byte offset `off` from the wave-uniform base.
+__device__ __forceinline__ f4 ld_agent4(const float* base, uint32_t off) {
+  const rsrc_t r = make_rsrc(reinterpret_cast<const uint8_t*>(base), 0x7FFFFFFF);
+  return __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 16 /* sc1 */));
+}
+
 // Merge the n partial results of (b, h) (slots slot0, slot0 + hkv, ...) into
-// the bf16 output. s_w: 2 * grp floats of scratch LDS.
+// the bf16 output with log-sum-exp weights. s_w: LDS scratch of `cap` floats.
+// One wave per column finds the max and the per-split weights (lanes over
+// splits); then every thread owns 4 consecutive outputs and sums its splits
+// with 16-byte loads, several in flight.
 template <int D>
-__device__ void combine_splits(const DecodeArgs& a, int b, int h, int64_t slot0, int n, float* s_w) {
+__device__ void combine_splits(const DecodeArgs& a, int b, int h, int64_t slot0, int n, float* s_w, int cap) {
   const int hkv = a.pool.hkv;
   const int grp = a.grp;
-  if ((int)threadIdx.x < grp) {
-    const int col = threadIdx.x;
-    float M = -__builtin_inff();
-    for (int s = 0; s < n; ++s) M = __builtin_fmaxf(M, ld_agent(a.ws_ml + ((slot0 + (int64_t)s * hkv) * grp + col) * 2));
-    float lt = 0.0f;
-    for (int s = 0; s < n; ++s) {
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int nw = (cap - 32) / grp;  // splits whose weights fit in LDS
+  for (int col = w; col < grp; col += 4) {
+    float mloc = -__builtin_inff();
+    for (int s = lane; s < n; s += 64) mloc = __builtin_fmaxf(mloc, ld_agent(a.ws_ml + ((slot0 + (int64_t)s * hkv) * grp + col) * 2));
+    const float M = wave_max64(mloc);
+    float lloc = 0.0f;
+    for (int s = lane; s < n; s += 64) {
       const float* ml = a.ws_ml + ((slot0 + (int64_t)s * hkv) * grp + col) * 2;
       const float m0 = ld_agent(ml);
-      lt += (m0 == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(m0 - M) * ld_agent(ml + 1);
+      const float f = (m0 == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(m0 - M) * ld_agent(ml + 1);
+      lloc += f;
+      if (s < nw) s_w[32 + col * nw + s] = f;
     }
-    s_w[2 * col] = M;
-    s_w[2 * col + 1] = lt > 0.0f ? 1.0f / lt : 0.0f;
+    const float lt = wave_sum64(lloc);
+    if (lane == 0) {
+      s_w[2 * col] = M;
+      s_w[2 * col + 1] = lt > 0.0f ? 1.0f / lt : 0.0f;
+    }
   }
   __syncthreads();
   const float gv = *a.v_scale;
   uint16_t* out = a.out + ((int64_t)b * a.hq + h * grp) * D;
-  for (int e = threadIdx.x; e < grp * D; e += 256) {
-    const int col = e / D;
-    const int d = e - col * D;
+  constexpr int D4 = D / 4;
+  for (int e = threadIdx.x; e < grp * D4; e += 256) {
+    const int col = e / D4;
+    const int d4 = e - col * D4;
     const float M = s_w[2 * col];
-    const float inv = s_w[2 * col + 1];
-    float o = 0.0f;
-    for (int s = 0; s < n; ++s) {
-      const int64_t sl = (slot0 + (int64_t)s * hkv) * grp + col;
-      const float m0 = ld_agent(a.ws_ml + sl * 2);
-      const float f = (m0 == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(m0 - M) * ld_agent(a.ws_ml + sl * 2 + 1);
-      o += f * ld_agent(a.ws_o + sl * D + d);
+    const uint32_t off = (uint32_t)((col * D + 4 * d4) * 4);
+    f4 o = {0.f, 0.f, 0.f, 0.f};
+    int s = 0;
+    for (; s + 4 <= n && s + 4 <= nw; s += 4) {
+      f4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = ld_agent4(a.ws_o + (slot0 + (int64_t)(s + u) * hkv) * grp * D, off);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) o += s_w[32 + col * nw + s + u] * v[u];
     }
-    out[e] = (uint16_t)(pack_bf16x2(o * inv * gv, 0.0f) & 0xFFFFu);
+    for (; s < n; ++s) {
+      float f;
+      if (s < nw) {
+        f = s_w[32 + col * nw + s];
+      } else {
+        const float* ml = a.ws_ml + ((slot0 + (int64_t)s * hkv) * grp + col) * 2;
+        const float m0 = ld_agent(ml);
+        f = (m0 == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(m0 - M) * ld_agent(ml + 1);
+      }
+      o += f * ld_agent4(a.ws_o + (slot0 + (int64_t)s * hkv) * grp * D, off);
+    }
+    const float sc = s_w[2 * col + 1] * gv;
+    uint32_t* dst = reinterpret_cast<uint32_t*>(out + col * D + 4 * d4);
+    dst[0] = pack_bf16x2(o[0] * sc, o[1] * sc);
+    dst[1] = pack_bf16x2(o[2] * sc, o[3] * sc);
   }
 }
 
+// Stages of the per-wave LDS ring: enough bytes in flight per CU while two
+// workgroups fit in the 160 KB of LDS.
 template <int D>
+struct DecodeStages {
+  static constexpr int NS = (D == 256) ? 2 : (D == 128 ? 3 : 4);
+};
+
+template <int D, bool COMPACT>
 __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   using G = Geo<D>;
+  using SG = StageGeo<D, COMPACT>;
+  constexpr int NS = DecodeStages<D>::NS;
   extern __shared__ __align__(16) char smem[];
   int* s_pref = reinterpret_cast<int*>(smem);
   int* s_red = s_pref + decode_lds_pref_ints(a.B);
   float* s_ml = reinterpret_cast<float*>(s_red + 16);  // [4 waves][16 cols][2]
-  float* s_o = s_ml + 4 * 16 * 2;                       // [4 waves][kMergeCols][D]
+  uint8_t* rings = reinterpret_cast<uint8_t*>(s_ml + 4 * 16 * 2);  // [4 waves][NS][stage]
+  float* s_o = reinterpret_cast<float*>(rings);         // [4 waves][kMergeCols][D], after the streams
 
   const int hkv = a.pool.hkv;
   const int cap = a.max_blocks * a.pool.bs;
@@ -176,7 +231,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   const int grp = a.grp;
   const float qk_factor = a.sm_scale * (*a.k_scale) * kLog2e;
   const float gv = *a.v_scale;
-  const LaneOffsets<D> off = lane_offsets<D>(a.pool.st, i, j);
+  const DmaOffsets<D, COMPACT> dof = dma_offsets<D, COMPACT>(a.pool.st, lane);
+  uint8_t* ring = rings + w * NS * SG::STAGE;
 
   for (int u = blockIdx.x; u < total * hkv; u += gridDim.x) {
     const int ubs = u / hkv;
@@ -205,28 +261,16 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     W.lim[0] = valid ? L - 1 : -1;
     const int32_t* bt_row = a.bt + (int64_t)b * a.max_blocks;
 
-    // Software pipeline over the wave's steps (k, k+4, ...): two register
-    // buffers, data one step ahead, block ids two steps ahead. Loads past the
-    // wave's range read nothing (zero-size descriptors).
-    int k = st0 + w;
-    if (k < st1) {
-      SubRaw<D> A[2], B[2];
-      load_step<D>(A, a.pool, step_ids(bt_row, k * kStep, L, a.pool), h, k * kStep, off);
-      StepIds ib = step_ids(bt_row, (k + 4) * kStep, k + 4 < st1 ? L : 0, a.pool);
-      while (true) {
-        load_step<D>(B, a.pool, ib, h, (k + 4) * kStep, off);
-        const StepIds ia = step_ids(bt_row, (k + 8) * kStep, k + 8 < st1 ? L : 0, a.pool);
-        mask_step<D>(A, k * kStep, L, j);
-        W.step(A, k * kStep, j);
-        if (k + 4 >= st1) break;
-        load_step<D>(A, a.pool, ia, h, (k + 8) * kStep, off);
-        ib = step_ids(bt_row, (k + 12) * kStep, k + 12 < st1 ? L : 0, a.pool);
-        mask_step<D>(B, (k + 4) * kStep, L, j);
-        W.step(B, (k + 4) * kStep, j);
-        k += 8;
-        if (k >= st1) break;
-      }
-    }
+    // The wave's steps are st0 + w, st0 + w + 4, ... below st1.
+    auto ids_at = [&](int kk) { return step_ids(bt_row, kk * kStep, kk < st1 ? L : 0, a.pool); };
+    auto run = [&](SubRaw<D>(&R)[2], int kk) {
+      const int kb = kk * kStep;
+      const bool partial = kb + kStep > L;
+      if (partial) mask_step<D>(R, kb, L, j);
+      W.step(R, kb, j, partial);
+    };
+    stream_steps_lds<D, COMPACT, NS>(ring, st0 + w, 4, st1, a.pool, h, dof, i, j, ids_at, run);
+    __syncthreads();  // every wave's ring is drained before the rings become the merge buffer
 
     // ---- merge the four waves' partial softmax states through LDS, eight
     // columns at a time
@@ -288,7 +332,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
                                            __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(nsplit - 1));
       __syncthreads();
       if (s_red[8]) {
-        combine_splits<D>(a, b, h, (int64_t)s_pref[b] * hkv + h, nsplit, s_ml);
+        combine_splits<D>(a, b, h, (int64_t)s_pref[b] * hkv + h, nsplit, s_o,
+                          (4 * NS * SG::STAGE) / 4);
         if (threadIdx.x == 0)
           __hip_atomic_store(&a.ws_cnt[(int64_t)b * hkv + h], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
@@ -308,9 +353,21 @@ size_t decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, i
   return (size_t)(counter_bytes(num_seqs, num_kv_heads) + slots * grp * head_size * 4 + slots * grp * 2 * 4);
 }
 
+template <int D>
+static size_t decode_lds_bytes_t(int num_seqs) {
+  const size_t sc = StageGeo<D, true>::STAGE, sn = StageGeo<D, false>::STAGE;
+  const size_t ring = (size_t)4 * DecodeStages<D>::NS * (sc > sn ? sc : sn);
+  const size_t merge = (size_t)4 * kMergeCols * D * 4;
+  return (size_t)(decode_lds_pref_ints(num_seqs) + 16) * 4 + 4 * 16 * 2 * 4 + (ring > merge ? ring : merge);
+}
+
 size_t decode_lds_bytes(int num_seqs, int grp, int head_size) {
   (void)grp;
-  return (size_t)(decode_lds_pref_ints(num_seqs) + 16) * 4 + 4 * 16 * 2 * 4 + (size_t)4 * kMergeCols * head_size * 4;
+  switch (head_size) {
+    case 64: return decode_lds_bytes_t<64>(num_seqs);
+    case 128: return decode_lds_bytes_t<128>(num_seqs);
+    default: return decode_lds_bytes_t<256>(num_seqs);
+  }
 }
 
 template <int D>
@@ -322,8 +379,14 @@ static hipError_t launch_decode_t(const DecodeArgs& a, int max_seq_len, hipStrea
   int64_t want = (int64_t)a.B * hkv * ((steps + kDecodeMinTps - 1) / kDecodeMinTps);
   if (want < 1) want = 1;
   const int grid = (int)(want < kDecodeTarget ? want : kDecodeTarget);
-  const size_t lds_split = decode_lds_bytes(a.B, a.grp, D);
-  decode_split_kernel<D><<<grid, 256, lds_split, stream>>>(a);
+  const size_t lds_split = decode_lds_bytes_t<D>(a.B);
+  // 16-byte copies need contiguous, 16-byte aligned page rows (HND layout)
+  const bool compact = a.pool.st == D / 2 + D / 16 && a.pool.sb % 16 == 0 && a.pool.skv % 16 == 0 &&
+                       a.pool.sh % 16 == 0 && (reinterpret_cast<uintptr_t>(a.pool.data) % 16) == 0;
+  if (compact)
+    decode_split_kernel<D, true><<<grid, 256, lds_split, stream>>>(a);
+  else
+    decode_split_kernel<D, false><<<grid, 256, lds_split, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -434,26 +497,17 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   const int steps = ceil_div(kmax, kStep);
   const int32_t* bt_row = a.bt + (int64_t)b * a.max_blocks;
 
+  // keys below min_full are visible to every valid column of the wave
+  const int c_first = col_base;
+  const int min_full = a.causal ? L - qlen + c_first / grp + 1 : L;
   const LaneOffsets<D> off = lane_offsets<D>(a.pool.st, i, j);
-  if (steps > 0) {
-    SubRaw<D> A[2], B[2];
-    load_step<D>(A, a.pool, step_ids(bt_row, 0, L, a.pool), h, 0, off);
-    StepIds ib = step_ids(bt_row, kStep, 1 < steps ? L : 0, a.pool);
-    int k = 0;
-    while (true) {
-      load_step<D>(B, a.pool, ib, h, (k + 1) * kStep, off);
-      const StepIds ia = step_ids(bt_row, (k + 2) * kStep, k + 2 < steps ? L : 0, a.pool);
-      mask_step<D>(A, k * kStep, L, j);
-      W.step(A, k * kStep, j);
-      if (k + 1 >= steps) break;
-      load_step<D>(A, a.pool, ia, h, (k + 2) * kStep, off);
-      ib = step_ids(bt_row, (k + 3) * kStep, k + 3 < steps ? L : 0, a.pool);
-      mask_step<D>(B, (k + 1) * kStep, L, j);
-      W.step(B, (k + 1) * kStep, j);
-      k += 2;
-      if (k >= steps) break;
-    }
-  }
+  auto ids_at = [&](int kk) { return step_ids(bt_row, kk * kStep, kk < steps ? L : 0, a.pool); };
+  auto run = [&](SubRaw<D>(&R)[2], int kk) {
+    const int kb = kk * kStep;
+    if (kb + kStep > L) mask_step<D>(R, kb, L, j);
+    W.step(R, kb, j, kb + kStep > min_full);
+  };
+  stream_steps<D>(0, 1, steps, a.pool, h, off, ids_at, run);
 
   const float gv = *a.v_scale;
 #pragma unroll

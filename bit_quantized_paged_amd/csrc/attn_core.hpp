@@ -69,7 +69,8 @@ __device__ __forceinline__ void zero_sub(SubRaw<D>& R) {
 // on the lane and the row stride, so a wave computes them once.
 template <int D>
 struct LaneOffsets {
-  uint32_t k, ks, v[4], vs[4];
+  uint32_t k, ks, v, vs;  // v / vs: row 4j of the lane's four value rows
+  int32_t st;             // row stride; value row 4j + r adds r * st (scalar)
 };
 
 template <int D>
@@ -78,11 +79,9 @@ __device__ __forceinline__ LaneOffsets<D> lane_offsets(int64_t st, int i, int j)
   const uint32_t s = (uint32_t)st;
   o.k = i * s + j * (D / 8);
   o.ks = i * s + D / 2 + j * (D / 64);
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    o.v[r] = (4 * j + r) * s + i * Geo<D>::VB;
-    o.vs[r] = (4 * j + r) * s + D / 2 + (i * Geo<D>::DPL) / 16;
-  }
+  o.v = 4 * j * s + i * Geo<D>::VB;
+  o.vs = 4 * j * s + D / 2 + (i * Geo<D>::DPL) / 16;
+  o.st = (int32_t)st;
   return o;
 }
 
@@ -125,16 +124,17 @@ __device__ __forceinline__ void load_sub(SubRaw<D>& R, rsrc_t kr, rsrc_t vr, con
   }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
+    const int so = r * o.st;
     if constexpr (D == 64) {
-      R.v[r][0] = __builtin_amdgcn_raw_buffer_load_b16(vr, o.v[r], 0, 0);
+      R.v[r][0] = __builtin_amdgcn_raw_buffer_load_b16(vr, o.v, so, 0);
     } else if constexpr (D == 128) {
-      R.v[r][0] = __builtin_amdgcn_raw_buffer_load_b32(vr, o.v[r], 0, 0);
+      R.v[r][0] = __builtin_amdgcn_raw_buffer_load_b32(vr, o.v, so, 0);
     } else {
-      const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(vr, o.v[r], 0, 0);
+      const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(vr, o.v, so, 0);
       R.v[r][0] = w[0];
       R.v[r][1] = w[1];
     }
-    R.vs[r] = __builtin_amdgcn_raw_buffer_load_b8(vr, o.vs[r], 0, 0);
+    R.vs[r] = __builtin_amdgcn_raw_buffer_load_b8(vr, o.vs, so, 0);
   }
 }
 
@@ -274,8 +274,10 @@ struct WaveAttn {
   }
 
   // One 32-key step starting at absolute key kb; R[0], R[1] hold the two
-  // subtiles' raw bytes (keys >= L already zeroed in the value rows).
-  __device__ __forceinline__ void step(const SubRaw<D> (&R)[2], int kb, int j) {
+  // subtiles' raw bytes (keys >= L already zeroed in the value rows). With
+  // masked false (wave-uniform) every key of the step is visible to every
+  // valid column and the per-key limit test is skipped.
+  __device__ __forceinline__ void step(const SubRaw<D> (&R)[2], int kb, int j, bool masked) {
     // ---- S^T = K^ . Q^T for both subtiles
     f4 s[2][NT];
 #pragma unroll
@@ -292,10 +294,13 @@ struct WaveAttn {
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = kb + 16 * sb + 4 * j + r;
-          const float v = s[sb][n][r] * sf[n];
-          x[4 * sb + r] = (key <= lim[n]) ? v : -__builtin_inff();
+        for (int r = 0; r < 4; ++r) x[4 * sb + r] = s[sb][n][r] * sf[n];
+      }
+      if (masked) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int key = kb + 16 * (k >> 2) + 4 * j + (k & 3);
+          x[k] = (key <= lim[n]) ? x[k] : -__builtin_inff();
         }
       }
       float mx = x[0];
@@ -312,16 +317,20 @@ struct WaveAttn {
         m[n] = mnew;
       }
       const float mu = (m[n] == -__builtin_inff()) ? 0.0f : m[n];
-      // the running sum adds the f16-rounded probabilities the PV product
-      // uses, so that constant values come back unchanged
-      float ps = 0.0f;
+      // probabilities go to f16 in pairs; the running sum adds exactly the
+      // f16 values the PV product uses (dot with (1, 1)), so constant values
+      // come back unchanged
+      const h2 one = {(_Float16)1.0f, (_Float16)1.0f};
+      float ps = l[n];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const _Float16 e = (_Float16)__builtin_amdgcn_exp2f(x[k] - mu);
-        ps += (float)e;
-        p[n][k] = e;
+      for (int k = 0; k < 8; k += 2) {
+        const h2 e = __builtin_bit_cast(
+            h2, __builtin_amdgcn_cvt_pkrtz(__builtin_amdgcn_exp2f(x[k] - mu), __builtin_amdgcn_exp2f(x[k + 1] - mu)));
+        ps = __builtin_amdgcn_fdot2(e, one, ps, false);
+        p[n][k] = e[0];
+        p[n][k + 1] = e[1];
       }
-      l[n] += ps;
+      l[n] = ps;
     }
     // ---- O^T += V^ T . P^T
     VPairs<D> vp[2];
@@ -396,6 +405,206 @@ __device__ __forceinline__ void load_step(SubRaw<D> (&R)[2], const Pool& pool, c
   // keep the scheduler from hoisting work on the previous step's data above
   // these loads (that would make their issue wait for that data)
   __builtin_amdgcn_sched_barrier(0);
+}
+
+// Stream the steps k0, k0 + ks, ... (< kend) through two register buffers:
+// the data of the next step is in flight while a step is computed, and block
+// ids are read one step further ahead. ids_at(k) must return not-ok ids for
+// k >= kend; run(R, k) consumes step k.
+template <int D, typename IdsAt, typename Run>
+__device__ __forceinline__ void stream_steps(int k0, int ks, int kend, const Pool& pool, int h,
+                                             const LaneOffsets<D>& off, IdsAt ids_at, Run run) {
+  if (k0 >= kend) return;
+  SubRaw<D> A[2], B[2];
+  load_step<D>(A, pool, ids_at(k0), h, k0 * 32, off);
+  StepIds ib = ids_at(k0 + ks);
+  int k = k0;
+  while (true) {
+    load_step<D>(B, pool, ib, h, (k + ks) * 32, off);
+    const StepIds ia = ids_at(k + 2 * ks);
+    run(A, k);
+    if (k + ks >= kend) break;
+    load_step<D>(A, pool, ia, h, (k + 2 * ks) * 32, off);
+    ib = ids_at(k + 3 * ks);
+    run(B, k + ks);
+    k += 2 * ks;
+    if (k >= kend) break;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// LDS-staged stream (decode). Each wave owns a ring of NS stages in LDS; a
+// stage holds one 32-key step: for each 16-key subtile its K rows then its V
+// rows, each 16 x full_dim bytes, densely. The copy into a stage is a fixed
+// number of direct global->LDS buffer loads (no registers held while in
+// flight): 16-byte chunks when a page's rows are contiguous (HND layout),
+// 4-byte chunks for any other row stride. Lane l of a load lands at the
+// load's LDS base + l * chunk; a subtile's K and V chunks form one list (V
+// lanes add the K->V stride to their offset), and the lanes past the end of
+// the list read out of range, which writes zeros to the padding after the
+// subtile. No load is ever predicated, so every step issues exactly the same
+// number of loads (a step past the wave's range uses zero-size descriptors:
+// zeros, no memory traffic) and the wait before reading stage i is the
+// constant vmcnt <= (NS - 1) * loads_per_step. The compiler does not order
+// these loads against LDS reads, so that wait is explicit and fenced.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int D, bool COMPACT>
+struct StageGeo {
+  static constexpr int FD = D / 2 + D / 16;
+  static constexpr int SLAB = 16 * FD;                       // bytes of 16 rows
+  static constexpr int CHUNK = COMPACT ? 16 : 4;             // bytes per lane per load
+  static constexpr int CH = SLAB / CHUNK;                    // chunks per slab
+  static constexpr int NCS = (2 * CH + 63) / 64;             // loads per subtile (K + V)
+  static constexpr int NC = 2 * NCS;                         // loads per step
+  static constexpr int SUB = NCS * 64 * CHUNK;               // LDS bytes per subtile (padded)
+  static constexpr int STAGE = 2 * SUB;                      // LDS bytes per stage
+};
+
+// Per-lane byte offsets (relative to the subtile's first K row) of this
+// lane's chunk in each load of a subtile, and whether it is a V chunk (which
+// adds the K->V stride); loop invariant.
+template <int D, bool COMPACT>
+struct DmaOffsets {
+  uint32_t v[StageGeo<D, COMPACT>::NCS];
+  uint32_t isv;  // bit t: load t's chunk of this lane is a V chunk
+};
+
+constexpr uint32_t kOutOfRange = 0x7FFFFFF0u;  // >= any descriptor size used here
+
+template <int D, bool COMPACT>
+__device__ __forceinline__ DmaOffsets<D, COMPACT> dma_offsets(int64_t st, int lane) {
+  using SG = StageGeo<D, COMPACT>;
+  DmaOffsets<D, COMPACT> o;
+  o.isv = 0;
+#pragma unroll
+  for (int t = 0; t < SG::NCS; ++t) {
+    const int c = 64 * t + lane;
+    const int cc = c < SG::CH ? c : c - SG::CH;  // chunk within its slab
+    uint32_t off;
+    if constexpr (COMPACT) {
+      off = (uint32_t)(cc * 16);
+    } else {
+      constexpr int WPR = SG::FD / 4;  // dwords per row
+      off = (uint32_t)((cc / WPR) * (int)st + 4 * (cc % WPR));
+    }
+    o.v[t] = (c < 2 * SG::CH) ? off : kOutOfRange;
+    o.isv |= (c >= SG::CH && c < 2 * SG::CH) ? (1u << t) : 0u;
+  }
+  return o;
+}
+
+__device__ __forceinline__ lds_void* to_lds(uint8_t* p) { return (lds_void*)p; }
+
+// Copy the step at kb (ids from step_ids) into the stage at dst.
+template <int D, bool COMPACT>
+__device__ __forceinline__ void dma_step(uint8_t* dst, const Pool& pool, const StepIds& ids, int h, int kb,
+                                         const DmaOffsets<D, COMPACT>& o) {
+  using SG = StageGeo<D, COMPACT>;
+  const int extent = (int)pool.skv + 15 * (int)pool.st + SG::FD;
+  const uint32_t skv = (uint32_t)pool.skv;
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb) {
+    const int row0 = (kb + 16 * sb) & (pool.bs - 1);
+    const int64_t blk = clamp_block(ids.id[sb], pool.num_blocks);
+    const uint8_t* base = pool.data + blk * pool.sb + (int64_t)h * pool.sh + (int64_t)row0 * pool.st;
+    const rsrc_t r = make_rsrc(base, ids.ok[sb] ? extent : 0);
+#pragma unroll
+    for (int t = 0; t < SG::NCS; ++t) {
+      const uint32_t voff = o.v[t] + (((o.isv >> t) & 1u) ? skv : 0u);
+      if constexpr (COMPACT)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, to_lds(dst + sb * SG::SUB + t * 64 * 16), 16, voff, 0, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, to_lds(dst + sb * SG::SUB + t * 64 * 4), 4, voff, 0, 0, 0);
+    }
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
+  __builtin_amdgcn_sched_barrier(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// This lane's raw bytes of one subtile, read from its two slabs in LDS (the
+// same per-lane pattern the direct global loads use).
+template <int D>
+__device__ __forceinline__ void lds_read_sub(SubRaw<D>& R, const uint8_t* kslab, const uint8_t* vslab, int i,
+                                             int j) {
+  constexpr int FD = D / 2 + D / 16;
+  const uint8_t* krow = kslab + i * FD;
+  if constexpr (D == 64) {
+    const u32x2 w = ld_u32x2(krow + j * 8);
+    R.k[0] = w[0];
+    R.k[1] = w[1];
+    R.ks = ld_u8(krow + 32 + j);
+  } else if constexpr (D == 128) {
+    const u32x4 w = ld_u32x4(krow + j * 16);
+    R.k[0] = w[0];
+    R.k[1] = w[1];
+    R.k[2] = w[2];
+    R.k[3] = w[3];
+    R.ks = ld_u16(krow + 64 + 2 * j);
+  } else {
+    const u32x4 w0 = ld_u32x4(krow + j * 32);
+    const u32x4 w1 = ld_u32x4(krow + j * 32 + 16);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      R.k[c] = w0[c];
+      R.k[4 + c] = w1[c];
+    }
+    R.ks = ld_u32(krow + 128 + 4 * j);
+  }
+  const uint8_t* vrow = vslab + 4 * j * FD;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    if constexpr (D == 64) {
+      R.v[r][0] = ld_u16(vrow + r * FD + 2 * i);
+      R.vs[r] = ld_u8(vrow + r * FD + 32 + (i >> 2));
+    } else if constexpr (D == 128) {
+      R.v[r][0] = ld_u32(vrow + r * FD + 4 * i);
+      R.vs[r] = ld_u8(vrow + r * FD + 64 + (i >> 1));
+    } else {
+      const u32x2 w = ld_u32x2(vrow + r * FD + 8 * i);
+      R.v[r][0] = w[0];
+      R.v[r][1] = w[1];
+      R.vs[r] = ld_u8(vrow + r * FD + 128 + i);
+    }
+  }
+}
+
+// Stream steps k0, k0 + ks, ... (< kend) through the wave's LDS ring `ring`
+// (NS stages). ids_at(k) must return not-ok ids for k >= kend; run(R, k)
+// consumes step k. Leaves no copy in flight.
+template <int D, bool COMPACT, int NS, typename IdsAt, typename Run>
+__device__ __forceinline__ void stream_steps_lds(uint8_t* ring, int k0, int ks, int kend, const Pool& pool, int h,
+                                                 const DmaOffsets<D, COMPACT>& dof, int i, int j,
+                                                 IdsAt ids_at, Run run) {
+  using SG = StageGeo<D, COMPACT>;
+  if (k0 >= kend) return;
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    dma_step<D, COMPACT>(ring + s * SG::STAGE, pool, ids_at(k0 + s * ks), h, (k0 + s * ks) * 32, dof);
+  StepIds nxt = ids_at(k0 + (NS - 1) * ks);
+  int slot = 0;
+  for (int k = k0; k < kend; k += ks) {
+    const int fill = (slot + NS - 1) % NS;
+    dma_step<D, COMPACT>(ring + fill * SG::STAGE, pool, nxt, h, (k + (NS - 1) * ks) * 32, dof);
+    nxt = ids_at(k + NS * ks);
+    wait_vmcnt<(NS - 1) * SG::NC>();
+    const uint8_t* st = ring + slot * SG::STAGE;
+    SubRaw<D> R[2];
+    lds_read_sub<D>(R[0], st, st + SG::SLAB, i, j);
+    lds_read_sub<D>(R[1], st + SG::SUB, st + SG::SUB + SG::SLAB, i, j);
+    run(R, k);
+    slot = (slot + 1 == NS) ? 0 : slot + 1;
+  }
+  wait_vmcnt<0>();
 }
 
 template <int D>
