@@ -9,12 +9,14 @@ namespace nvfp4kv {
 // ---------------------------------------------------------------------------
 // Decode schedule. A unit is (sequence, split, kv head); a split is a run of
 // `tps` 32-key steps. tps is chosen on the device from the actual lengths so
-// that the batch yields about kDecodeTarget units of equal size, which keeps
+// that the batch yields about `target` units of equal size (target = the
+// number of decode workgroups the GPU holds at once, so that all units run in
+// a single round), which keeps
 // ragged batches balanced without a host round trip. Every workgroup derives
 // the same schedule: per-sequence unit counts and their exclusive prefix sum
 // in LDS.
 // ---------------------------------------------------------------------------
-constexpr int kDecodeTarget = 1024;
+constexpr int kDecodeTargetMax = 2048;  // upper bound of `target` (sizes the workspace)
 constexpr int kDecodeMinTps = 4;
 constexpr int kStep = 32;
 constexpr int kMergeCols = 8;  // columns merged per LDS round
@@ -65,8 +67,8 @@ __device__ __forceinline__ int block_excl_scan(int v, int* s_red, int& total) {
 }
 
 // s_pref[b] = first unit (per head) of sequence b, s_pref[B] = units per head.
-__device__ void decode_schedule(const int32_t* __restrict__ seq_lens, int B, int cap, int hkv, int* s_pref,
-                                int* s_red, int& tps, int& total_units) {
+__device__ void decode_schedule(const int32_t* __restrict__ seq_lens, int B, int cap, int hkv, int target,
+                                int* s_pref, int* s_red, int& tps, int& total_units) {
   const int per = ceil_div(B, 256);
   const int b0 = threadIdx.x * per;
   const int b1 = (b0 + per < B) ? b0 + per : B;
@@ -79,7 +81,7 @@ __device__ void decode_schedule(const int32_t* __restrict__ seq_lens, int B, int
   int total_steps;
   (void)block_excl_scan(steps_local, s_red, total_steps);
   const int64_t work = (int64_t)total_steps * hkv;
-  int t = (int)((work + kDecodeTarget - 1) / kDecodeTarget);
+  int t = (int)((work + target - 1) / target);
   tps = t < kDecodeMinTps ? kDecodeMinTps : t;
   int units_local = 0;
   // a sequence without keys still gets one (empty) unit, which writes zeros
@@ -112,6 +114,7 @@ struct DecodeArgs {
   uint32_t* ws_cnt;  // [B * hkv] arrival counters; zero between calls
   float* ws_o;       // [slot][grp][D]   normalised partial outputs
   float* ws_ml;      // [slot][grp][2]   (max, sum) of each partial, base-2 scores
+  int target;        // units the schedule aims for (<= kDecodeTargetMax)
 };
 
 __host__ __device__ inline int decode_lds_pref_ints(int B) { return ((B + 1 + 3) / 4) * 4; }
@@ -203,7 +206,7 @@ __device__ void combine_splits(const DecodeArgs& a, int b, int h, int64_t slot0,
 // workgroups fit in the 160 KB of LDS.
 template <int D>
 struct DecodeStages {
-  static constexpr int NS = (D == 256) ? 2 : (D == 128 ? 3 : 4);
+  static constexpr int NS = (D == 64) ? 3 : 2;
 };
 
 template <int D, bool COMPACT>
@@ -221,7 +224,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   const int hkv = a.pool.hkv;
   const int cap = a.max_blocks * a.pool.bs;
   int tps, total;
-  decode_schedule(a.seq_lens, a.B, cap, hkv, s_pref, s_red, tps, total);
+  decode_schedule(a.seq_lens, a.B, cap, hkv, a.target, s_pref, s_red, tps, total);
   tps = __builtin_amdgcn_readfirstlane(tps);
   total = __builtin_amdgcn_readfirstlane(total);
 
@@ -253,23 +256,35 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     const int st0 = split * tps;
     const int st1 = (st0 + tps < steps) ? st0 + tps : steps;
 
+    const int32_t* bt_row = a.bt + (int64_t)b * a.max_blocks;
+    // The wave's steps are st0 + w, st0 + w + 4, ... below st1 (a wave with
+    // none issues only zero-size copies).
+    const StepIds first = lds_prologue<D, COMPACT, NS>(ring, st0 + w, 4, st1, bt_row, L, a.pool, h, dof);
+
     WaveAttn<D, 1> W;
     W.init();
     const bool valid = i < grp;
     const uint16_t* qrow = valid ? a.q + (int64_t)b * a.q_st + (int64_t)(h * grp + i) * a.q_sh : nullptr;
     W.load_q(0, qrow, j, qk_factor);
     W.lim[0] = valid ? L - 1 : -1;
-    const int32_t* bt_row = a.bt + (int64_t)b * a.max_blocks;
-
-    // The wave's steps are st0 + w, st0 + w + 4, ... below st1.
-    auto ids_at = [&](int kk) { return step_ids(bt_row, kk * kStep, kk < st1 ? L : 0, a.pool); };
-    auto run = [&](SubRaw<D>(&R)[2], int kk) {
-      const int kb = kk * kStep;
-      const bool partial = kb + kStep > L;
-      if (partial) mask_step<D>(R, kb, L, j);
-      W.step(R, kb, j, partial);
-    };
-    stream_steps_lds<D, COMPACT, NS>(ring, st0 + w, 4, st1, a.pool, h, dof, i, j, ids_at, run);
+    {
+      StepIds nxt = first;
+      int slot = 0;
+      for (int k = st0 + w; k < st1; k += 4) {
+        const int fill = (slot + NS - 1) % NS;
+        dma_step<D, COMPACT>(ring + fill * SG::STAGE, a.pool, nxt, h, (k + (NS - 1) * 4) * kStep, dof);
+        nxt = ids_for_step(bt_row, k + NS * 4, st1, L, a.pool);
+        wait_vmcnt<(NS - 1) * SG::NC>();
+        SubRaw<D> R[2];
+        lds_read_step<D, COMPACT>(R, ring + slot * SG::STAGE, i, j);
+        const int kb = k * kStep;
+        const bool partial = kb + kStep > L;
+        if (partial) mask_step<D>(R, kb, L, j);
+        W.step(R, kb, j, partial);
+        slot = (slot + 1 == NS) ? 0 : slot + 1;
+      }
+      wait_vmcnt<0>();
+    }
     __syncthreads();  // every wave's ring is drained before the rings become the merge buffer
 
     // ---- merge the four waves' partial softmax states through LDS, eight
@@ -349,7 +364,7 @@ static int64_t counter_bytes(int num_seqs, int num_kv_heads) {
 
 size_t decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_size) {
   const int64_t grp = num_q_heads / num_kv_heads;
-  const int64_t slots = kDecodeTarget + (int64_t)num_seqs * num_kv_heads;
+  const int64_t slots = kDecodeTargetMax + (int64_t)num_seqs * num_kv_heads;
   return (size_t)(counter_bytes(num_seqs, num_kv_heads) + slots * grp * head_size * 4 + slots * grp * 2 * 4);
 }
 
@@ -370,24 +385,49 @@ size_t decode_lds_bytes(int num_seqs, int grp, int head_size) {
   }
 }
 
+// Workgroups of the decode kernel that the device holds at once (cached per
+// device and kernel variant; an occupancy query, not a device sync).
+template <int D, bool COMPACT>
+static int resident_workgroups(size_t lds) {
+  static int cached[64] = {0};
+  static size_t cached_lds[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cached[dev] > 0 && cached_lds[dev] == lds) return cached[dev];
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<D, COMPACT>, 256, lds) != hipSuccess ||
+      per_cu < 1)
+    per_cu = 1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+  int n = per_cu * cus;
+  n = n > kDecodeTargetMax ? kDecodeTargetMax : n;
+  cached[dev] = n;
+  cached_lds[dev] = lds;
+  return n;
+}
+
+template <int D, bool COMPACT>
+static hipError_t launch_decode_v(DecodeArgs a, int max_seq_len, hipStream_t stream) {
+  const int hkv = a.pool.hkv;
+  const size_t lds = decode_lds_bytes_t<D>(a.B);
+  a.target = resident_workgroups<D, COMPACT>(lds);
+  const int64_t cap = (int64_t)a.max_blocks * a.pool.bs;
+  const int64_t lens = max_seq_len > 0 ? (max_seq_len < cap ? max_seq_len : cap) : cap;
+  const int64_t steps = (lens + kStep - 1) / kStep;
+  // an upper bound of the units the schedule can produce for this batch
+  int64_t want = (int64_t)a.B * hkv * ((steps + kDecodeMinTps - 1) / kDecodeMinTps);
+  want = want < (int64_t)a.B * hkv ? (int64_t)a.B * hkv : want;
+  const int grid = (int)(want < a.target ? want : a.target);
+  decode_split_kernel<D, COMPACT><<<grid, 256, lds, stream>>>(a);
+  return hipGetLastError();
+}
+
 template <int D>
 static hipError_t launch_decode_t(const DecodeArgs& a, int max_seq_len, hipStream_t stream) {
-  const int hkv = a.pool.hkv;
-  const int64_t cap = (int64_t)a.max_blocks * a.pool.bs;
-  int64_t lens = max_seq_len > 0 ? (max_seq_len < cap ? max_seq_len : cap) : cap;
-  const int64_t steps = (lens + kStep - 1) / kStep;
-  int64_t want = (int64_t)a.B * hkv * ((steps + kDecodeMinTps - 1) / kDecodeMinTps);
-  if (want < 1) want = 1;
-  const int grid = (int)(want < kDecodeTarget ? want : kDecodeTarget);
-  const size_t lds_split = decode_lds_bytes_t<D>(a.B);
   // 16-byte copies need contiguous, 16-byte aligned page rows (HND layout)
   const bool compact = a.pool.st == D / 2 + D / 16 && a.pool.sb % 16 == 0 && a.pool.skv % 16 == 0 &&
                        a.pool.sh % 16 == 0 && (reinterpret_cast<uintptr_t>(a.pool.data) % 16) == 0;
-  if (compact)
-    decode_split_kernel<D, true><<<grid, 256, lds_split, stream>>>(a);
-  else
-    decode_split_kernel<D, false><<<grid, 256, lds_split, stream>>>(a);
-  return hipGetLastError();
+  return compact ? launch_decode_v<D, true>(a, max_seq_len, stream) : launch_decode_v<D, false>(a, max_seq_len, stream);
 }
 
 hipError_t launch_decode(const Pool& pool, int head_size, const void* q, int64_t q_st, int64_t q_sh,
@@ -410,7 +450,7 @@ hipError_t launch_decode(const Pool& pool, int head_size, const void* q, int64_t
   a.v_scale = v_scale;
   a.sm_scale = sm_scale;
   a.out = static_cast<uint16_t*>(out);
-  const int64_t slots = kDecodeTarget + (int64_t)num_seqs * pool.hkv;
+  const int64_t slots = kDecodeTargetMax + (int64_t)num_seqs * pool.hkv;
   a.ws_cnt = static_cast<uint32_t*>(workspace);
   a.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + counter_bytes(num_seqs, pool.hkv));
   a.ws_ml = a.ws_o + slots * a.grp * head_size;

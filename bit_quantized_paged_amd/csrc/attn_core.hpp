@@ -578,33 +578,33 @@ __device__ __forceinline__ void lds_read_sub(SubRaw<D>& R, const uint8_t* kslab,
   }
 }
 
-// Stream steps k0, k0 + ks, ... (< kend) through the wave's LDS ring `ring`
-// (NS stages). ids_at(k) must return not-ok ids for k >= kend; run(R, k)
-// consumes step k. Leaves no copy in flight.
-template <int D, bool COMPACT, int NS, typename IdsAt, typename Run>
-__device__ __forceinline__ void stream_steps_lds(uint8_t* ring, int k0, int ks, int kend, const Pool& pool, int h,
-                                                 const DmaOffsets<D, COMPACT>& dof, int i, int j,
-                                                 IdsAt ids_at, Run run) {
+// Stream steps k0, k0 + ks, ... (< kend) of a sequence with L keys (block
+// table row bt_row) through the wave's LDS ring `ring` (NS stages).
+// lds_prologue issues the first NS - 1 copies (so that other loads, e.g. the
+// queries, overlap them) and returns the ids of the next step to copy; the
+// caller's loop then copies step k + (NS - 1) * ks, waits for stage k and
+// computes it, and drains with wait_vmcnt<0>() at the end.
+__device__ __forceinline__ StepIds ids_for_step(const int32_t* bt_row, int k, int kend, int L, const Pool& pool) {
+  return step_ids(bt_row, k * 32, k < kend ? L : 0, pool);
+}
+
+template <int D, bool COMPACT, int NS>
+__device__ __forceinline__ StepIds lds_prologue(uint8_t* ring, int k0, int ks, int kend, const int32_t* bt_row, int L,
+                                                const Pool& pool, int h, const DmaOffsets<D, COMPACT>& dof) {
   using SG = StageGeo<D, COMPACT>;
-  if (k0 >= kend) return;
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
-    dma_step<D, COMPACT>(ring + s * SG::STAGE, pool, ids_at(k0 + s * ks), h, (k0 + s * ks) * 32, dof);
-  StepIds nxt = ids_at(k0 + (NS - 1) * ks);
-  int slot = 0;
-  for (int k = k0; k < kend; k += ks) {
-    const int fill = (slot + NS - 1) % NS;
-    dma_step<D, COMPACT>(ring + fill * SG::STAGE, pool, nxt, h, (k + (NS - 1) * ks) * 32, dof);
-    nxt = ids_at(k + NS * ks);
-    wait_vmcnt<(NS - 1) * SG::NC>();
-    const uint8_t* st = ring + slot * SG::STAGE;
-    SubRaw<D> R[2];
-    lds_read_sub<D>(R[0], st, st + SG::SLAB, i, j);
-    lds_read_sub<D>(R[1], st + SG::SUB, st + SG::SUB + SG::SLAB, i, j);
-    run(R, k);
-    slot = (slot + 1 == NS) ? 0 : slot + 1;
-  }
-  wait_vmcnt<0>();
+    dma_step<D, COMPACT>(ring + s * SG::STAGE, pool, ids_for_step(bt_row, k0 + s * ks, kend, L, pool), h,
+                         (k0 + s * ks) * 32, dof);
+  return ids_for_step(bt_row, k0 + (NS - 1) * ks, kend, L, pool);
+}
+
+// Read this lane's raw bytes of both subtiles of the stage at `stage`.
+template <int D, bool COMPACT>
+__device__ __forceinline__ void lds_read_step(SubRaw<D> (&R)[2], const uint8_t* stage, int i, int j) {
+  using SG = StageGeo<D, COMPACT>;
+  lds_read_sub<D>(R[0], stage, stage + SG::SLAB, i, j);
+  lds_read_sub<D>(R[1], stage + SG::SUB, stage + SG::SUB + SG::SLAB, i, j);
 }
 
 template <int D>
