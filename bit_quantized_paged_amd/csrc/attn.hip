@@ -202,23 +202,47 @@ __device__ void combine_splits(const DecodeArgs& a, int b, int h, int64_t slot0,
   }
 }
 
-// Stages of the per-wave LDS ring: enough bytes in flight per CU while two
-// workgroups fit in the 160 KB of LDS.
+// How a decode kernel streams pages into its per-wave ring of NS LDS stages
+// (see attn_core.hpp):
+//  kModeDmaCompact: contiguous 16-byte aligned rows: 16-byte global->LDS copies;
+//  kModeDmaGeneral: any row stride: 4-byte global->LDS copies.
+constexpr int kModeDmaGeneral = 0;
+constexpr int kModeDmaCompact = 1;
+
+// Stages of the per-wave LDS ring (DMA modes): enough bytes in flight per CU
+// while several workgroups fit in the 160 KB of LDS.
 template <int D>
 struct DecodeStages {
   static constexpr int NS = (D == 64) ? 3 : 2;
 };
 
-template <int D, bool COMPACT>
-__global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
+template <int D, int MODE>
+struct DecodeLds {
+  static constexpr int dma_stage = StageGeo<D, MODE == kModeDmaCompact>::STAGE;
+  static constexpr int stream = 4 * DecodeStages<D>::NS * dma_stage;
+  static constexpr int merge = 4 * kMergeCols * D * 4;
+  static constexpr int area = stream > merge ? stream : merge;  // streams, then merge and combine scratch
+};
+
+// Waves per SIMD the register budget is sized for (the loads in flight live
+// in LDS, so registers hold one step's working set; D = 256 needs more).
+template <int D, int MODE>
+struct DecodeOcc {
+  static constexpr int waves = (D == 256) ? 2 : 3;
+};
+
+template <int D, int MODE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DecodeOcc<D, MODE>::waves))) void
+decode_split_kernel(DecodeArgs a) {
   using G = Geo<D>;
+  constexpr bool COMPACT = MODE != kModeDmaGeneral;
   using SG = StageGeo<D, COMPACT>;
   constexpr int NS = DecodeStages<D>::NS;
   extern __shared__ __align__(16) char smem[];
   int* s_pref = reinterpret_cast<int*>(smem);
   int* s_red = s_pref + decode_lds_pref_ints(a.B);
   float* s_ml = reinterpret_cast<float*>(s_red + 16);  // [4 waves][16 cols][2]
-  uint8_t* rings = reinterpret_cast<uint8_t*>(s_ml + 4 * 16 * 2);  // [4 waves][NS][stage]
+  uint8_t* rings = reinterpret_cast<uint8_t*>(s_ml + 4 * 16 * 2);  // per-wave stream area
   float* s_o = reinterpret_cast<float*>(rings);         // [4 waves][kMergeCols][D], after the streams
 
   const int hkv = a.pool.hkv;
@@ -236,6 +260,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   const float gv = *a.v_scale;
   const DmaOffsets<D, COMPACT> dof = dma_offsets<D, COMPACT>(a.pool.st, lane);
   uint8_t* ring = rings + w * NS * SG::STAGE;
+  const LdsLane ll = lds_lane<D>(i, j);
 
   for (int u = blockIdx.x; u < total * hkv; u += gridDim.x) {
     const int ubs = u / hkv;
@@ -257,34 +282,32 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     const int st1 = (st0 + tps < steps) ? st0 + tps : steps;
 
     const int32_t* bt_row = a.bt + (int64_t)b * a.max_blocks;
-    // The wave's steps are st0 + w, st0 + w + 4, ... below st1 (a wave with
-    // none issues only zero-size copies).
-    const StepIds first = lds_prologue<D, COMPACT, NS>(ring, st0 + w, 4, st1, bt_row, L, a.pool, h, dof);
-
+    const int k0 = st0 + w;  // the wave's steps: k0, k0 + 4, ... below st1
     WaveAttn<D, 1> W;
     W.init();
     const bool valid = i < grp;
     const uint16_t* qrow = valid ? a.q + (int64_t)b * a.q_st + (int64_t)(h * grp + i) * a.q_sh : nullptr;
-    W.load_q(0, qrow, j, qk_factor);
     W.lim[0] = valid ? L - 1 : -1;
-    {
-      StepIds nxt = first;
-      int slot = 0;
-      for (int k = st0 + w; k < st1; k += 4) {
-        const int fill = (slot + NS - 1) % NS;
-        dma_step<D, COMPACT>(ring + fill * SG::STAGE, a.pool, nxt, h, (k + (NS - 1) * 4) * kStep, dof);
-        nxt = ids_for_step(bt_row, k + NS * 4, st1, L, a.pool);
-        wait_vmcnt<(NS - 1) * SG::NC>();
-        SubRaw<D> R[2];
-        lds_read_step<D, COMPACT>(R, ring + slot * SG::STAGE, i, j);
-        const int kb = k * kStep;
-        const bool partial = kb + kStep > L;
-        if (partial) mask_step<D>(R, kb, L, j);
-        W.step(R, kb, j, partial);
-        slot = (slot + 1 == NS) ? 0 : slot + 1;
-      }
-      wait_vmcnt<0>();
+
+    // ---- stream the wave's steps through its ring of NS stages: copy step
+    // k + (NS - 1) * 4 while step k, already in LDS, is computed
+    StepIds nxt = lds_prologue<D, COMPACT, NS>(ring, k0, 4, st1, bt_row, L, a.pool, h, dof);
+    W.load_q(0, qrow, j, qk_factor);
+    int slot = 0;
+    for (int k = k0; k < st1; k += 4) {
+      const int fill = (slot + NS - 1) % NS;
+      dma_step<D, COMPACT>(ring + fill * SG::STAGE, a.pool, nxt, h, (k + (NS - 1) * 4) * kStep, dof);
+      nxt = ids_for_step(bt_row, k + NS * 4, st1, L, a.pool);
+      wait_vmcnt<(NS - 1) * SG::NC>();
+      SubRaw<D> R[2];
+      lds_read_step_async_safe<D>(R, ring + slot * SG::STAGE, ll);
+      const int kb = k * kStep;
+      const bool partial = kb + kStep > L;
+      if (partial) mask_step<D>(R, kb, L, j);
+      W.step(R, kb, j, partial);
+      slot = (slot + 1 == NS) ? 0 : slot + 1;
     }
+    wait_vmcnt<0>();
     __syncthreads();  // every wave's ring is drained before the rings become the merge buffer
 
     // ---- merge the four waves' partial softmax states through LDS, eight
@@ -347,13 +370,17 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
                                            __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(nsplit - 1));
       __syncthreads();
       if (s_red[8]) {
-        combine_splits<D>(a, b, h, (int64_t)s_pref[b] * hkv + h, nsplit, s_o,
-                          (4 * NS * SG::STAGE) / 4);
+        combine_splits<D>(a, b, h, (int64_t)s_pref[b] * hkv + h, nsplit, s_o, DecodeLds<D, MODE>::area / 4);
         if (threadIdx.x == 0)
           __hip_atomic_store(&a.ws_cnt[(int64_t)b * hkv + h], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       __syncthreads();
     }
+    // Retire this unit's stores here: the compiler's wait tracking does not
+    // order stores against loads, so a store still counted as pending when
+    // the next unit's pipelined loop starts makes it wait for every load in
+    // flight at the top of each iteration.
+    wait_stores();
   }
 }
 
@@ -368,12 +395,16 @@ size_t decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, i
   return (size_t)(counter_bytes(num_seqs, num_kv_heads) + slots * grp * head_size * 4 + slots * grp * 2 * 4);
 }
 
+template <int D, int MODE>
+static size_t decode_lds_bytes_m(int num_seqs) {
+  return (size_t)(decode_lds_pref_ints(num_seqs) + 16) * 4 + 4 * 16 * 2 * 4 + DecodeLds<D, MODE>::area;
+}
+
 template <int D>
 static size_t decode_lds_bytes_t(int num_seqs) {
-  const size_t sc = StageGeo<D, true>::STAGE, sn = StageGeo<D, false>::STAGE;
-  const size_t ring = (size_t)4 * DecodeStages<D>::NS * (sc > sn ? sc : sn);
-  const size_t merge = (size_t)4 * kMergeCols * D * 4;
-  return (size_t)(decode_lds_pref_ints(num_seqs) + 16) * 4 + 4 * 16 * 2 * 4 + (ring > merge ? ring : merge);
+  // both modes use the same stage geometry
+  static_assert(DecodeLds<D, kModeDmaGeneral>::area == DecodeLds<D, kModeDmaCompact>::area, "mode LDS sizes");
+  return decode_lds_bytes_m<D, kModeDmaCompact>(num_seqs);
 }
 
 size_t decode_lds_bytes(int num_seqs, int grp, int head_size) {
@@ -385,9 +416,9 @@ size_t decode_lds_bytes(int num_seqs, int grp, int head_size) {
   }
 }
 
-// Workgroups of the decode kernel that the device holds at once (cached per
-// device and kernel variant; an occupancy query, not a device sync).
-template <int D, bool COMPACT>
+// Workgroups of a decode kernel variant that the device holds at once
+// (cached per device and variant; an occupancy query, not a device sync).
+template <int D, int MODE>
 static int resident_workgroups(size_t lds) {
   static int cached[64] = {0};
   static size_t cached_lds[64] = {0};
@@ -395,7 +426,7 @@ static int resident_workgroups(size_t lds) {
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
   if (cached[dev] > 0 && cached_lds[dev] == lds) return cached[dev];
   int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<D, COMPACT>, 256, lds) != hipSuccess ||
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<D, MODE>, 256, lds) != hipSuccess ||
       per_cu < 1)
     per_cu = 1;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
@@ -406,11 +437,11 @@ static int resident_workgroups(size_t lds) {
   return n;
 }
 
-template <int D, bool COMPACT>
+template <int D, int MODE>
 static hipError_t launch_decode_v(DecodeArgs a, int max_seq_len, hipStream_t stream) {
   const int hkv = a.pool.hkv;
-  const size_t lds = decode_lds_bytes_t<D>(a.B);
-  a.target = resident_workgroups<D, COMPACT>(lds);
+  const size_t lds = decode_lds_bytes_m<D, MODE>(a.B);
+  a.target = resident_workgroups<D, MODE>(lds);
   const int64_t cap = (int64_t)a.max_blocks * a.pool.bs;
   const int64_t lens = max_seq_len > 0 ? (max_seq_len < cap ? max_seq_len : cap) : cap;
   const int64_t steps = (lens + kStep - 1) / kStep;
@@ -418,16 +449,17 @@ static hipError_t launch_decode_v(DecodeArgs a, int max_seq_len, hipStream_t str
   int64_t want = (int64_t)a.B * hkv * ((steps + kDecodeMinTps - 1) / kDecodeMinTps);
   want = want < (int64_t)a.B * hkv ? (int64_t)a.B * hkv : want;
   const int grid = (int)(want < a.target ? want : a.target);
-  decode_split_kernel<D, COMPACT><<<grid, 256, lds, stream>>>(a);
+  decode_split_kernel<D, MODE><<<grid, 256, lds, stream>>>(a);
   return hipGetLastError();
 }
 
 template <int D>
-static hipError_t launch_decode_t(const DecodeArgs& a, int max_seq_len, hipStream_t stream) {
-  // 16-byte copies need contiguous, 16-byte aligned page rows (HND layout)
+static hipError_t launch_decode_t(DecodeArgs a, int max_seq_len, hipStream_t stream) {
+  // 16-byte chunks need contiguous, 16-byte aligned page rows (HND layout)
   const bool compact = a.pool.st == D / 2 + D / 16 && a.pool.sb % 16 == 0 && a.pool.skv % 16 == 0 &&
                        a.pool.sh % 16 == 0 && (reinterpret_cast<uintptr_t>(a.pool.data) % 16) == 0;
-  return compact ? launch_decode_v<D, true>(a, max_seq_len, stream) : launch_decode_v<D, false>(a, max_seq_len, stream);
+  return compact ? launch_decode_v<D, kModeDmaCompact>(a, max_seq_len, stream)
+                 : launch_decode_v<D, kModeDmaGeneral>(a, max_seq_len, stream);
 }
 
 hipError_t launch_decode(const Pool& pool, int head_size, const void* q, int64_t q_st, int64_t q_sh,

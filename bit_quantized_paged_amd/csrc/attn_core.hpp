@@ -232,31 +232,42 @@ struct WaveAttn {
     }
   }
 
-  // Load column tile n: qrow points at the column's D bf16 values (nullptr:
-  // padding column). The row is scaled by a power of two so that its largest
-  // magnitude lies in [1, 2) before the exact-range f16 conversion; the
-  // inverse goes into sf.
-  __device__ __forceinline__ void load_q(int n, const uint16_t* qrow, int j, float base_factor) {
+  // Query columns are loaded in two halves so that other loads can be
+  // issued while these are in flight: load_q_raw issues this lane's share of
+  // the column's D bf16 values (qrow nullptr: padding column), set_q turns
+  // them into column tile n. The row is scaled by a power of two so that its
+  // largest magnitude lies in [1, 2) before the exact-range f16 conversion;
+  // the inverse goes into sf.
+  struct QRaw {
+    uint32_t w[D / 8];
+  };
+
+  __device__ __forceinline__ static QRaw load_q_raw(const uint16_t* qrow, int j) {
     constexpr int E = D / 4;  // bf16 elements per lane
-    uint32_t w[E / 2];
+    QRaw r;
     if (qrow != nullptr) {
       const u32x4* p = reinterpret_cast<const u32x4*>(qrow + j * E);
 #pragma unroll
       for (int c = 0; c < E / 8; ++c) {
         const u32x4 x = p[c];
-        w[4 * c] = x[0];
-        w[4 * c + 1] = x[1];
-        w[4 * c + 2] = x[2];
-        w[4 * c + 3] = x[3];
+        r.w[4 * c] = x[0];
+        r.w[4 * c + 1] = x[1];
+        r.w[4 * c + 2] = x[2];
+        r.w[4 * c + 3] = x[3];
       }
     } else {
 #pragma unroll
-      for (int c = 0; c < E / 2; ++c) w[c] = 0;
+      for (int c = 0; c < E / 2; ++c) r.w[c] = 0;
     }
+    return r;
+  }
+
+  __device__ __forceinline__ void set_q(int n, const QRaw& r, float base_factor) {
+    constexpr int E = D / 4;
     float amax = 0.0f;
 #pragma unroll
     for (int c = 0; c < E / 2; ++c)
-      amax = __builtin_fmaxf(amax, __builtin_fmaxf(__builtin_fabsf(bf16_lo(w[c])), __builtin_fabsf(bf16_hi(w[c]))));
+      amax = __builtin_fmaxf(amax, __builtin_fmaxf(__builtin_fabsf(bf16_lo(r.w[c])), __builtin_fabsf(bf16_hi(r.w[c]))));
     amax = wave_max_j(amax);
     int e = (int)((__float_as_uint(amax) >> 23) & 0xFFu) - 127;
     e = (amax == 0.0f) ? 0 : (e < -120 ? -120 : e);
@@ -266,11 +277,15 @@ struct WaveAttn {
       h8 v;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        v[2 * t] = (_Float16)__builtin_ldexpf(bf16_lo(w[4 * c + t]), -e);
-        v[2 * t + 1] = (_Float16)__builtin_ldexpf(bf16_hi(w[4 * c + t]), -e);
+        v[2 * t] = (_Float16)__builtin_ldexpf(bf16_lo(r.w[4 * c + t]), -e);
+        v[2 * t + 1] = (_Float16)__builtin_ldexpf(bf16_hi(r.w[4 * c + t]), -e);
       }
       q[n][c] = v;
     }
+  }
+
+  __device__ __forceinline__ void load_q(int n, const uint16_t* qrow, int j, float base_factor) {
+    set_q(n, load_q_raw(qrow, j), base_factor);
   }
 
   // One 32-key step starting at absolute key kb; R[0], R[1] hold the two
@@ -458,8 +473,12 @@ struct StageGeo {
   static constexpr int CH = SLAB / CHUNK;                    // chunks per slab
   static constexpr int NCS = (2 * CH + 63) / 64;             // loads per subtile (K + V)
   static constexpr int NC = 2 * NCS;                         // loads per step
-  static constexpr int SUB = NCS * 64 * CHUNK;               // LDS bytes per subtile (padded)
+  // LDS bytes per subtile: the padded size of the 16-byte-chunk layout for
+  // both chunk widths (the 4-byte layout needs less), so that the stage
+  // geometry, and the step reader's immediate offsets, depend on D only.
+  static constexpr int SUB = ((2 * (SLAB / 16) + 63) / 64) * 64 * 16;
   static constexpr int STAGE = 2 * SUB;                      // LDS bytes per stage
+  static_assert(NCS * 64 * CHUNK <= SUB, "stage too small for the chunk layout");
 };
 
 // Per-lane byte offsets (relative to the subtile's first K row) of this
@@ -531,53 +550,6 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// This lane's raw bytes of one subtile, read from its two slabs in LDS (the
-// same per-lane pattern the direct global loads use).
-template <int D>
-__device__ __forceinline__ void lds_read_sub(SubRaw<D>& R, const uint8_t* kslab, const uint8_t* vslab, int i,
-                                             int j) {
-  constexpr int FD = D / 2 + D / 16;
-  const uint8_t* krow = kslab + i * FD;
-  if constexpr (D == 64) {
-    const u32x2 w = ld_u32x2(krow + j * 8);
-    R.k[0] = w[0];
-    R.k[1] = w[1];
-    R.ks = ld_u8(krow + 32 + j);
-  } else if constexpr (D == 128) {
-    const u32x4 w = ld_u32x4(krow + j * 16);
-    R.k[0] = w[0];
-    R.k[1] = w[1];
-    R.k[2] = w[2];
-    R.k[3] = w[3];
-    R.ks = ld_u16(krow + 64 + 2 * j);
-  } else {
-    const u32x4 w0 = ld_u32x4(krow + j * 32);
-    const u32x4 w1 = ld_u32x4(krow + j * 32 + 16);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      R.k[c] = w0[c];
-      R.k[4 + c] = w1[c];
-    }
-    R.ks = ld_u32(krow + 128 + 4 * j);
-  }
-  const uint8_t* vrow = vslab + 4 * j * FD;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    if constexpr (D == 64) {
-      R.v[r][0] = ld_u16(vrow + r * FD + 2 * i);
-      R.vs[r] = ld_u8(vrow + r * FD + 32 + (i >> 2));
-    } else if constexpr (D == 128) {
-      R.v[r][0] = ld_u32(vrow + r * FD + 4 * i);
-      R.vs[r] = ld_u8(vrow + r * FD + 64 + (i >> 1));
-    } else {
-      const u32x2 w = ld_u32x2(vrow + r * FD + 8 * i);
-      R.v[r][0] = w[0];
-      R.v[r][1] = w[1];
-      R.vs[r] = ld_u8(vrow + r * FD + 128 + i);
-    }
-  }
-}
-
 // Stream steps k0, k0 + ks, ... (< kend) of a sequence with L keys (block
 // table row bt_row) through the wave's LDS ring `ring` (NS stages).
 // lds_prologue issues the first NS - 1 copies (so that other loads, e.g. the
@@ -599,12 +571,183 @@ __device__ __forceinline__ StepIds lds_prologue(uint8_t* ring, int k0, int ks, i
   return ids_for_step(bt_row, k0 + (NS - 1) * ks, kend, L, pool);
 }
 
-// Read this lane's raw bytes of both subtiles of the stage at `stage`.
-template <int D, bool COMPACT>
-__device__ __forceinline__ void lds_read_step(SubRaw<D> (&R)[2], const uint8_t* stage, int i, int j) {
-  using SG = StageGeo<D, COMPACT>;
-  lds_read_sub<D>(R[0], stage, stage + SG::SLAB, i, j);
-  lds_read_sub<D>(R[1], stage + SG::SUB, stage + SG::SUB + SG::SLAB, i, j);
+// ---- step reader for stages filled by direct-to-LDS loads ----------------
+// The compiler cannot tell which LDS bytes an in-flight direct-to-LDS load
+// will write, so before any LDS read it would wait for every load in flight,
+// including the stages still streaming in. The step's reads are therefore
+// issued from one asm block, which the compiler does not inspect for LDS
+// accesses, and which itself waits for its reads (lgkmcnt(0)) before it
+// returns; the caller orders it after the stage's wait_vmcnt.
+
+// Per-lane byte offsets, within a stage, of what lane (i, j) reads of
+// subtile 0 (subtile 1 is StageGeo::SUB further): K row i, quarter j of its
+// codes (the k_chunk operands) and the scales of that quarter; V rows
+// 4j..4j+3, the codes of the lane's D/16 dims (2 bytes for D = 64, 4 for
+// 128, 8 for 256, one scale block) and that block's scale byte.
+struct LdsLane {
+  uint32_t k, ks, v, vs;
+};
+
+template <int D>
+__device__ __forceinline__ LdsLane lds_lane(int i, int j) {
+  constexpr int FD = D / 2 + D / 16;
+  LdsLane o;
+  o.k = (uint32_t)(i * FD + (D / 8) * j);
+  o.ks = (uint32_t)(i * FD + D / 2 + (D / 64) * j);
+  o.v = (uint32_t)(16 * FD + 4 * j * FD + (D / 32) * i);
+  o.vs = (uint32_t)(16 * FD + 4 * j * FD + D / 2 + ((i * D) >> 8));
+  return o;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
+}
+
+template <int D>
+__device__ __forceinline__ void lds_read_step_async_safe(SubRaw<D> (&R)[2], const uint8_t* stage, const LdsLane& o);
+
+static_assert(StageGeo<64, true>::SUB == 2048 && StageGeo<64, false>::SUB == 2048, "D = 64 reader offsets");
+static_assert(StageGeo<128, true>::SUB == 3072 && StageGeo<128, false>::SUB == 3072, "D = 128 reader offsets");
+static_assert(StageGeo<256, true>::SUB == 5120 && StageGeo<256, false>::SUB == 5120, "D = 256 reader offsets");
+
+// D = 64: row 36 bytes, subtile 2048 bytes.
+template <>
+__device__ __forceinline__ void lds_read_step_async_safe<64>(SubRaw<64> (&R)[2], const uint8_t* stage,
+                                                             const LdsLane& o) {
+  const uint32_t s = lds_addr(stage);
+  const uint32_t ak = s + o.k, aks = s + o.ks, av = s + o.v, avs = s + o.vs;
+  asm volatile(
+      "ds_read_b32 %0, %22\n\t"
+      "ds_read_b32 %1, %22 offset:4\n\t"
+      "ds_read_u8 %2, %23\n\t"
+      "ds_read_u16 %3, %24\n\t"
+      "ds_read_u16 %4, %24 offset:36\n\t"
+      "ds_read_u16 %5, %24 offset:72\n\t"
+      "ds_read_u16 %6, %24 offset:108\n\t"
+      "ds_read_u8 %7, %25\n\t"
+      "ds_read_u8 %8, %25 offset:36\n\t"
+      "ds_read_u8 %9, %25 offset:72\n\t"
+      "ds_read_u8 %10, %25 offset:108\n\t"
+      "ds_read_b32 %11, %22 offset:2048\n\t"
+      "ds_read_b32 %12, %22 offset:2052\n\t"
+      "ds_read_u8 %13, %23 offset:2048\n\t"
+      "ds_read_u16 %14, %24 offset:2048\n\t"
+      "ds_read_u16 %15, %24 offset:2084\n\t"
+      "ds_read_u16 %16, %24 offset:2120\n\t"
+      "ds_read_u16 %17, %24 offset:2156\n\t"
+      "ds_read_u8 %18, %25 offset:2048\n\t"
+      "ds_read_u8 %19, %25 offset:2084\n\t"
+      "ds_read_u8 %20, %25 offset:2120\n\t"
+      "ds_read_u8 %21, %25 offset:2156\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(R[0].k[0]), "=&v"(R[0].k[1]), "=&v"(R[0].ks), "=&v"(R[0].v[0][0]), "=&v"(R[0].v[1][0]),
+        "=&v"(R[0].v[2][0]), "=&v"(R[0].v[3][0]), "=&v"(R[0].vs[0]), "=&v"(R[0].vs[1]), "=&v"(R[0].vs[2]),
+        "=&v"(R[0].vs[3]), "=&v"(R[1].k[0]), "=&v"(R[1].k[1]), "=&v"(R[1].ks), "=&v"(R[1].v[0][0]),
+        "=&v"(R[1].v[1][0]), "=&v"(R[1].v[2][0]), "=&v"(R[1].v[3][0]), "=&v"(R[1].vs[0]), "=&v"(R[1].vs[1]),
+        "=&v"(R[1].vs[2]), "=&v"(R[1].vs[3])
+      : "v"(ak), "v"(aks), "v"(av), "v"(avs)
+      : "memory");
+}
+
+// D = 128: row 72 bytes, subtile 3072 bytes.
+template <>
+__device__ __forceinline__ void lds_read_step_async_safe<128>(SubRaw<128> (&R)[2], const uint8_t* stage,
+                                                              const LdsLane& o) {
+  const uint32_t s = lds_addr(stage);
+  const uint32_t ak = s + o.k, aks = s + o.ks, av = s + o.v, avs = s + o.vs;
+  u32x2 k0a, k0b, k1a, k1b;
+  asm volatile(
+      "ds_read_b64 %0, %22\n\t"
+      "ds_read_b64 %1, %22 offset:8\n\t"
+      "ds_read_u16 %2, %23\n\t"
+      "ds_read_b32 %3, %24\n\t"
+      "ds_read_b32 %4, %24 offset:72\n\t"
+      "ds_read_b32 %5, %24 offset:144\n\t"
+      "ds_read_b32 %6, %24 offset:216\n\t"
+      "ds_read_u8 %7, %25\n\t"
+      "ds_read_u8 %8, %25 offset:72\n\t"
+      "ds_read_u8 %9, %25 offset:144\n\t"
+      "ds_read_u8 %10, %25 offset:216\n\t"
+      "ds_read_b64 %11, %22 offset:3072\n\t"
+      "ds_read_b64 %12, %22 offset:3080\n\t"
+      "ds_read_u16 %13, %23 offset:3072\n\t"
+      "ds_read_b32 %14, %24 offset:3072\n\t"
+      "ds_read_b32 %15, %24 offset:3144\n\t"
+      "ds_read_b32 %16, %24 offset:3216\n\t"
+      "ds_read_b32 %17, %24 offset:3288\n\t"
+      "ds_read_u8 %18, %25 offset:3072\n\t"
+      "ds_read_u8 %19, %25 offset:3144\n\t"
+      "ds_read_u8 %20, %25 offset:3216\n\t"
+      "ds_read_u8 %21, %25 offset:3288\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(k0a), "=&v"(k0b), "=&v"(R[0].ks), "=&v"(R[0].v[0][0]), "=&v"(R[0].v[1][0]), "=&v"(R[0].v[2][0]),
+        "=&v"(R[0].v[3][0]), "=&v"(R[0].vs[0]), "=&v"(R[0].vs[1]), "=&v"(R[0].vs[2]), "=&v"(R[0].vs[3]),
+        "=&v"(k1a), "=&v"(k1b), "=&v"(R[1].ks), "=&v"(R[1].v[0][0]), "=&v"(R[1].v[1][0]), "=&v"(R[1].v[2][0]),
+        "=&v"(R[1].v[3][0]), "=&v"(R[1].vs[0]), "=&v"(R[1].vs[1]), "=&v"(R[1].vs[2]), "=&v"(R[1].vs[3])
+      : "v"(ak), "v"(aks), "v"(av), "v"(avs)
+      : "memory");
+  R[0].k[0] = k0a[0];
+  R[0].k[1] = k0a[1];
+  R[0].k[2] = k0b[0];
+  R[0].k[3] = k0b[1];
+  R[1].k[0] = k1a[0];
+  R[1].k[1] = k1a[1];
+  R[1].k[2] = k1b[0];
+  R[1].k[3] = k1b[1];
+}
+
+// D = 256: row 144 bytes, subtile 5120 bytes.
+template <>
+__device__ __forceinline__ void lds_read_step_async_safe<256>(SubRaw<256> (&R)[2], const uint8_t* stage,
+                                                              const LdsLane& o) {
+  const uint32_t s = lds_addr(stage);
+  const uint32_t ak = s + o.k, aks = s + o.ks, av = s + o.v, avs = s + o.vs;
+  u32x4 k0a, k0b, k1a, k1b;
+  u32x2 v0[4], v1[4];
+  asm volatile(
+      "ds_read_b128 %0, %22\n\t"
+      "ds_read_b128 %1, %22 offset:16\n\t"
+      "ds_read_b32 %2, %23\n\t"
+      "ds_read_b64 %3, %24\n\t"
+      "ds_read_b64 %4, %24 offset:144\n\t"
+      "ds_read_b64 %5, %24 offset:288\n\t"
+      "ds_read_b64 %6, %24 offset:432\n\t"
+      "ds_read_u8 %7, %25\n\t"
+      "ds_read_u8 %8, %25 offset:144\n\t"
+      "ds_read_u8 %9, %25 offset:288\n\t"
+      "ds_read_u8 %10, %25 offset:432\n\t"
+      "ds_read_b128 %11, %22 offset:5120\n\t"
+      "ds_read_b128 %12, %22 offset:5136\n\t"
+      "ds_read_b32 %13, %23 offset:5120\n\t"
+      "ds_read_b64 %14, %24 offset:5120\n\t"
+      "ds_read_b64 %15, %24 offset:5264\n\t"
+      "ds_read_b64 %16, %24 offset:5408\n\t"
+      "ds_read_b64 %17, %24 offset:5552\n\t"
+      "ds_read_u8 %18, %25 offset:5120\n\t"
+      "ds_read_u8 %19, %25 offset:5264\n\t"
+      "ds_read_u8 %20, %25 offset:5408\n\t"
+      "ds_read_u8 %21, %25 offset:5552\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(k0a), "=&v"(k0b), "=&v"(R[0].ks), "=&v"(v0[0]), "=&v"(v0[1]), "=&v"(v0[2]), "=&v"(v0[3]),
+        "=&v"(R[0].vs[0]), "=&v"(R[0].vs[1]), "=&v"(R[0].vs[2]), "=&v"(R[0].vs[3]), "=&v"(k1a), "=&v"(k1b),
+        "=&v"(R[1].ks), "=&v"(v1[0]), "=&v"(v1[1]), "=&v"(v1[2]), "=&v"(v1[3]), "=&v"(R[1].vs[0]),
+        "=&v"(R[1].vs[1]), "=&v"(R[1].vs[2]), "=&v"(R[1].vs[3])
+      : "v"(ak), "v"(aks), "v"(av), "v"(avs)
+      : "memory");
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    R[0].k[c] = k0a[c];
+    R[0].k[4 + c] = k0b[c];
+    R[1].k[c] = k1a[c];
+    R[1].k[4 + c] = k1b[c];
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    R[0].v[r][0] = v0[r][0];
+    R[0].v[r][1] = v0[r][1];
+    R[1].v[r][0] = v1[r][0];
+    R[1].v[r][1] = v1[r][1];
+  }
 }
 
 template <int D>
