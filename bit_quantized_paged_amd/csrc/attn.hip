@@ -68,13 +68,15 @@ __device__ __forceinline__ int block_excl_scan(int v, int* s_red, int& total) {
 
 // s_pref[b] = first unit (per head) of sequence b, s_pref[B] = units per head.
 __device__ void decode_schedule(const int32_t* __restrict__ seq_lens, int B, int cap, int hkv, int target,
-                                int* s_pref, int* s_red, int& tps, int& total_units) {
+                                int* s_pref, int* s_len, int* s_red, int& tps, int& total_units) {
   const int per = ceil_div(B, 256);
   const int b0 = threadIdx.x * per;
   const int b1 = (b0 + per < B) ? b0 + per : B;
   int steps_local = 0;
   for (int b = b0; b < b1; ++b) {
-    const int s = ceil_div(clamp_len(seq_lens[b], cap), kStep);
+    const int L = clamp_len(seq_lens[b], cap);
+    const int s = ceil_div(L, kStep);
+    s_len[b] = L;
     s_pref[b] = s;
     steps_local += s;
   }
@@ -98,6 +100,10 @@ __device__ void decode_schedule(const int32_t* __restrict__ seq_lens, int B, int
   __syncthreads();
 }
 
+__device__ __forceinline__ float uniform_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+}
+
 struct DecodeArgs {
   Pool pool;
   const uint16_t* q;
@@ -117,7 +123,9 @@ struct DecodeArgs {
   int target;        // units the schedule aims for (<= kDecodeTargetMax)
 };
 
-__host__ __device__ inline int decode_lds_pref_ints(int B) { return ((B + 1 + 3) / 4) * 4; }
+// LDS ints of the schedule: unit prefix [B + 1] and clamped lengths [B],
+// each padded to 16 bytes.
+__host__ __device__ inline int decode_lds_pref_ints(int B) { return ((B + 1 + 3) / 4) * 4 + ((B + 3) / 4) * 4; }
 
 __device__ __forceinline__ float wave_max64(float v) {
 #pragma unroll
@@ -240,24 +248,32 @@ decode_split_kernel(DecodeArgs a) {
   constexpr int NS = DecodeStages<D>::NS;
   extern __shared__ __align__(16) char smem[];
   int* s_pref = reinterpret_cast<int*>(smem);
+  int* s_len = s_pref + ((a.B + 1 + 3) / 4) * 4;
   int* s_red = s_pref + decode_lds_pref_ints(a.B);
   float* s_ml = reinterpret_cast<float*>(s_red + 16);  // [4 waves][16 cols][2]
   uint8_t* rings = reinterpret_cast<uint8_t*>(s_ml + 4 * 16 * 2);  // per-wave stream area
   float* s_o = reinterpret_cast<float*>(rings);         // [4 waves][kMergeCols][D], after the streams
 
+  // The scales are read with vector loads issued first: their latency then
+  // overlaps the schedule's own loads (a scalar load here would be waited
+  // for together with the kernel arguments the schedule needs).
+  const float ksc = __builtin_bit_cast(
+      float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(reinterpret_cast<const uint8_t*>(a.k_scale), 4), 0, 0, 0));
+  const float vsc = __builtin_bit_cast(
+      float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(reinterpret_cast<const uint8_t*>(a.v_scale), 4), 0, 0, 0));
   const int hkv = a.pool.hkv;
   const int cap = a.max_blocks * a.pool.bs;
   int tps, total;
-  decode_schedule(a.seq_lens, a.B, cap, hkv, a.target, s_pref, s_red, tps, total);
+  decode_schedule(a.seq_lens, a.B, cap, hkv, a.target, s_pref, s_len, s_red, tps, total);
   tps = __builtin_amdgcn_readfirstlane(tps);
   total = __builtin_amdgcn_readfirstlane(total);
+  const float qk_factor = a.sm_scale * uniform_f32(ksc) * kLog2e;
+  const float gv = uniform_f32(vsc);
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int i = lane & 15, j = lane >> 4;
   const int grp = a.grp;
-  const float qk_factor = a.sm_scale * (*a.k_scale) * kLog2e;
-  const float gv = *a.v_scale;
   const DmaOffsets<D, COMPACT> dof = dma_offsets<D, COMPACT>(a.pool.st, lane);
   uint8_t* ring = rings + w * NS * SG::STAGE;
   const LdsLane ll = lds_lane<D>(i, j);
@@ -265,18 +281,21 @@ decode_split_kernel(DecodeArgs a) {
   for (int u = blockIdx.x; u < total * hkv; u += gridDim.x) {
     const int ubs = u / hkv;
     const int h = u - ubs * hkv;
-    // sequence of this unit: last b with s_pref[b] <= ubs (values read from
-    // LDS are made wave-uniform so that everything below stays scalar)
-    int lo = 0, hi = a.B;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (__builtin_amdgcn_readfirstlane(s_pref[mid]) <= ubs) lo = mid; else hi = mid;
-    }
-    const int b = lo;
+    // sequence of this unit: the last b with s_pref[b] <= ubs (the prefix
+    // rises strictly and starts at 0), found by a 64-way search of two LDS
+    // rounds: the lanes test every stride-th entry, then the entries of the
+    // chosen stride (B <= 4096, so the stride is at most 64)
+    const int stride = (a.B + 63) >> 6;
+    int idx = lane * stride;
+    uint64_t hits = __builtin_amdgcn_ballot_w64(idx < a.B && s_pref[idx] <= ubs);
+    const int c0 = (__builtin_popcountll(hits) - 1) * stride;
+    idx = c0 + lane;
+    hits = __builtin_amdgcn_ballot_w64(lane < stride && idx < a.B && s_pref[idx] <= ubs);
+    const int b = c0 + __builtin_popcountll(hits) - 1;
     const int pb = __builtin_amdgcn_readfirstlane(s_pref[b]);
     const int split = ubs - pb;
     const int nsplit = __builtin_amdgcn_readfirstlane(s_pref[b + 1]) - pb;
-    const int L = clamp_len(a.seq_lens[b], cap);
+    const int L = __builtin_amdgcn_readfirstlane(s_len[b]);
     const int steps = ceil_div(L, kStep);
     const int st0 = split * tps;
     const int st1 = (st0 + tps < steps) ? st0 + tps : steps;
@@ -290,9 +309,12 @@ decode_split_kernel(DecodeArgs a) {
     W.lim[0] = valid ? L - 1 : -1;
 
     // ---- stream the wave's steps through its ring of NS stages: copy step
-    // k + (NS - 1) * 4 while step k, already in LDS, is computed
+    // k + (NS - 1) * 4 while step k, already in LDS, is computed. The query
+    // load is issued first so that it is in flight with the block-table
+    // reads the first copies wait for.
+    const auto qraw = WaveAttn<D, 1>::load_q_raw(qrow, j);
     StepIds nxt = lds_prologue<D, COMPACT, NS>(ring, k0, 4, st1, bt_row, L, a.pool, h, dof);
-    W.load_q(0, qrow, j, qk_factor);
+    W.set_q(0, qraw, qk_factor);
     int slot = 0;
     for (int k = k0; k < st1; k += 4) {
       const int fill = (slot + NS - 1) % NS;
