@@ -49,6 +49,8 @@ nvfp4kv_status check_cache(const nvfp4kv_cache* c, nvfp4kv::Pool& p) {
       return fail(NVFP4KV_INVALID_ARGUMENT, "cache strides must be non-negative multiples of 4 bytes");
   // rows of a page are addressed with 32-bit offsets
   if (c->stride_token > (1 << 26)) return fail(NVFP4KV_UNSUPPORTED, "stride_token above 2^26 bytes");
+  // the decode copies address a page's K and V rows from one 32-bit window
+  if (c->stride_kv > (1 << 30)) return fail(NVFP4KV_UNSUPPORTED, "stride_kv above 2^30 bytes");
   p.data = c->data;
   p.num_blocks = c->num_blocks;
   p.sb = c->stride_block;

@@ -274,7 +274,7 @@ decode_split_kernel(DecodeArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int i = lane & 15, j = lane >> 4;
   const int grp = a.grp;
-  const DmaOffsets<D, COMPACT> dof = dma_offsets<D, COMPACT>(a.pool.st, lane);
+  const DmaOffsets<D, COMPACT> dof = dma_offsets<D, COMPACT>(a.pool.st, a.pool.skv, lane);
   uint8_t* ring = rings + w * NS * SG::STAGE;
   const LdsLane ll = lds_lane<D>(i, j);
 

@@ -465,56 +465,75 @@ __device__ __forceinline__ void stream_steps(int k0, int ks, int kend, const Poo
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void lds_void;
 
+// LDS stage of one 32-key step: two subtiles, each its K slab (16 rows x
+// full_dim bytes) followed by its V slab, packed densely (a subtile is padded
+// only to 256 bytes). A subtile is copied by direct-to-LDS loads in which
+// lane l of load t writes LDS byte off(t) + l * size(t) of the subtile:
+//  compact (contiguous 16-byte aligned rows): N16 loads of 16 bytes per lane
+//    (1 KB each), then N4 loads of 4 bytes per lane (256 B each) for the rest;
+//  general (any row stride): loads of 4 bytes per lane, 256 B each.
+// Lanes past the subtile's bytes read out of range, which writes zeros.
 template <int D, bool COMPACT>
 struct StageGeo {
   static constexpr int FD = D / 2 + D / 16;
   static constexpr int SLAB = 16 * FD;                       // bytes of 16 rows
-  static constexpr int CHUNK = COMPACT ? 16 : 4;             // bytes per lane per load
-  static constexpr int CH = SLAB / CHUNK;                    // chunks per slab
-  static constexpr int NCS = (2 * CH + 63) / 64;             // loads per subtile (K + V)
-  static constexpr int NC = 2 * NCS;                         // loads per step
-  // LDS bytes per subtile: the padded size of the 16-byte-chunk layout for
-  // both chunk widths (the 4-byte layout needs less), so that the stage
-  // geometry, and the step reader's immediate offsets, depend on D only.
-  static constexpr int SUB = ((2 * (SLAB / 16) + 63) / 64) * 64 * 16;
+  static constexpr int BYTES = 2 * SLAB;                     // K and V of a subtile
+  static constexpr int SUB = (BYTES + 255) / 256 * 256;      // LDS bytes per subtile
   static constexpr int STAGE = 2 * SUB;                      // LDS bytes per stage
-  static_assert(NCS * 64 * CHUNK <= SUB, "stage too small for the chunk layout");
+  static constexpr int N16 = COMPACT ? BYTES / 1024 : 0;     // 16-byte loads per subtile
+  static constexpr int N4 = (BYTES - 1024 * N16 + 255) / 256;  // 4-byte loads per subtile
+  static constexpr int NCS = N16 + N4;                       // loads per subtile
+  static constexpr int NC = 2 * NCS;                         // loads per step
+  static constexpr int size(int t) { return t < N16 ? 16 : 4; }
+  static constexpr int off(int t) { return t < N16 ? 1024 * t : 1024 * N16 + 256 * (t - N16); }
+  static_assert(off(NCS - 1) + 256 <= SUB, "loads overrun the subtile");
 };
 
-// Per-lane byte offsets (relative to the subtile's first K row) of this
-// lane's chunk in each load of a subtile, and whether it is a V chunk (which
-// adds the K->V stride); loop invariant.
+// Per-lane byte offset, relative to the subtile's first K row in the pool, of
+// the bytes lane `lane` copies in each load of a subtile (V bytes include the
+// K->V stride); loop invariant.
 template <int D, bool COMPACT>
 struct DmaOffsets {
   uint32_t v[StageGeo<D, COMPACT>::NCS];
-  uint32_t isv;  // bit t: load t's chunk of this lane is a V chunk
 };
 
 constexpr uint32_t kOutOfRange = 0x7FFFFFF0u;  // >= any descriptor size used here
 
 template <int D, bool COMPACT>
-__device__ __forceinline__ DmaOffsets<D, COMPACT> dma_offsets(int64_t st, int lane) {
+__device__ __forceinline__ DmaOffsets<D, COMPACT> dma_offsets(int64_t st, int64_t skv, int lane) {
   using SG = StageGeo<D, COMPACT>;
   DmaOffsets<D, COMPACT> o;
-  o.isv = 0;
 #pragma unroll
   for (int t = 0; t < SG::NCS; ++t) {
-    const int c = 64 * t + lane;
-    const int cc = c < SG::CH ? c : c - SG::CH;  // chunk within its slab
+    const int x = SG::off(t) + SG::size(t) * lane;  // byte of the subtile's [K slab | V slab]
+    const bool isv = x >= SG::SLAB;
+    const int y = isv ? x - SG::SLAB : x;           // byte within its slab
     uint32_t off;
     if constexpr (COMPACT) {
-      off = (uint32_t)(cc * 16);
+      off = (uint32_t)y;                             // rows are contiguous
     } else {
-      constexpr int WPR = SG::FD / 4;  // dwords per row
-      off = (uint32_t)((cc / WPR) * (int)st + 4 * (cc % WPR));
+      off = (uint32_t)((y / SG::FD) * (int)st + y % SG::FD);
     }
-    o.v[t] = (c < 2 * SG::CH) ? off : kOutOfRange;
-    o.isv |= (c >= SG::CH && c < 2 * SG::CH) ? (1u << t) : 0u;
+    off += isv ? (uint32_t)skv : 0u;
+    o.v[t] = (x < SG::BYTES) ? off : kOutOfRange;
   }
   return o;
 }
 
 __device__ __forceinline__ lds_void* to_lds(uint8_t* p) { return (lds_void*)p; }
+
+// Loads T, T + 1, ... of one subtile (the load width must be a literal).
+template <int D, bool COMPACT, int T>
+__device__ __forceinline__ void dma_sub(uint8_t* dst, rsrc_t r, const DmaOffsets<D, COMPACT>& o) {
+  using SG = StageGeo<D, COMPACT>;
+  if constexpr (T < SG::NCS) {
+    if constexpr (SG::size(T) == 16)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, to_lds(dst + SG::off(T)), 16, o.v[T], 0, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, to_lds(dst + SG::off(T)), 4, o.v[T], 0, 0, 0);
+    dma_sub<D, COMPACT, T + 1>(dst, r, o);
+  }
+}
 
 // Copy the step at kb (ids from step_ids) into the stage at dst.
 template <int D, bool COMPACT>
@@ -522,21 +541,12 @@ __device__ __forceinline__ void dma_step(uint8_t* dst, const Pool& pool, const S
                                          const DmaOffsets<D, COMPACT>& o) {
   using SG = StageGeo<D, COMPACT>;
   const int extent = (int)pool.skv + 15 * (int)pool.st + SG::FD;
-  const uint32_t skv = (uint32_t)pool.skv;
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb) {
     const int row0 = (kb + 16 * sb) & (pool.bs - 1);
     const int64_t blk = clamp_block(ids.id[sb], pool.num_blocks);
     const uint8_t* base = pool.data + blk * pool.sb + (int64_t)h * pool.sh + (int64_t)row0 * pool.st;
-    const rsrc_t r = make_rsrc(base, ids.ok[sb] ? extent : 0);
-#pragma unroll
-    for (int t = 0; t < SG::NCS; ++t) {
-      const uint32_t voff = o.v[t] + (((o.isv >> t) & 1u) ? skv : 0u);
-      if constexpr (COMPACT)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, to_lds(dst + sb * SG::SUB + t * 64 * 16), 16, voff, 0, 0, 0);
-      else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, to_lds(dst + sb * SG::SUB + t * 64 * 4), 4, voff, 0, 0, 0);
-    }
+    dma_sub<D, COMPACT, 0>(dst + sb * SG::SUB, make_rsrc(base, ids.ok[sb] ? extent : 0), o);
   }
 }
 
@@ -606,11 +616,11 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
 template <int D>
 __device__ __forceinline__ void lds_read_step_async_safe(SubRaw<D> (&R)[2], const uint8_t* stage, const LdsLane& o);
 
-static_assert(StageGeo<64, true>::SUB == 2048 && StageGeo<64, false>::SUB == 2048, "D = 64 reader offsets");
-static_assert(StageGeo<128, true>::SUB == 3072 && StageGeo<128, false>::SUB == 3072, "D = 128 reader offsets");
-static_assert(StageGeo<256, true>::SUB == 5120 && StageGeo<256, false>::SUB == 5120, "D = 256 reader offsets");
+static_assert(StageGeo<64, true>::SUB == 1280 && StageGeo<64, false>::SUB == 1280, "D = 64 reader offsets");
+static_assert(StageGeo<128, true>::SUB == 2304 && StageGeo<128, false>::SUB == 2304, "D = 128 reader offsets");
+static_assert(StageGeo<256, true>::SUB == 4608 && StageGeo<256, false>::SUB == 4608, "D = 256 reader offsets");
 
-// D = 64: row 36 bytes, subtile 2048 bytes.
+// D = 64: row 36 bytes, subtile 1280 bytes.
 template <>
 __device__ __forceinline__ void lds_read_step_async_safe<64>(SubRaw<64> (&R)[2], const uint8_t* stage,
                                                              const LdsLane& o) {
@@ -628,17 +638,17 @@ __device__ __forceinline__ void lds_read_step_async_safe<64>(SubRaw<64> (&R)[2],
       "ds_read_u8 %8, %25 offset:36\n\t"
       "ds_read_u8 %9, %25 offset:72\n\t"
       "ds_read_u8 %10, %25 offset:108\n\t"
-      "ds_read_b32 %11, %22 offset:2048\n\t"
-      "ds_read_b32 %12, %22 offset:2052\n\t"
-      "ds_read_u8 %13, %23 offset:2048\n\t"
-      "ds_read_u16 %14, %24 offset:2048\n\t"
-      "ds_read_u16 %15, %24 offset:2084\n\t"
-      "ds_read_u16 %16, %24 offset:2120\n\t"
-      "ds_read_u16 %17, %24 offset:2156\n\t"
-      "ds_read_u8 %18, %25 offset:2048\n\t"
-      "ds_read_u8 %19, %25 offset:2084\n\t"
-      "ds_read_u8 %20, %25 offset:2120\n\t"
-      "ds_read_u8 %21, %25 offset:2156\n\t"
+      "ds_read_b32 %11, %22 offset:1280\n\t"
+      "ds_read_b32 %12, %22 offset:1284\n\t"
+      "ds_read_u8 %13, %23 offset:1280\n\t"
+      "ds_read_u16 %14, %24 offset:1280\n\t"
+      "ds_read_u16 %15, %24 offset:1316\n\t"
+      "ds_read_u16 %16, %24 offset:1352\n\t"
+      "ds_read_u16 %17, %24 offset:1388\n\t"
+      "ds_read_u8 %18, %25 offset:1280\n\t"
+      "ds_read_u8 %19, %25 offset:1316\n\t"
+      "ds_read_u8 %20, %25 offset:1352\n\t"
+      "ds_read_u8 %21, %25 offset:1388\n\t"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(R[0].k[0]), "=&v"(R[0].k[1]), "=&v"(R[0].ks), "=&v"(R[0].v[0][0]), "=&v"(R[0].v[1][0]),
         "=&v"(R[0].v[2][0]), "=&v"(R[0].v[3][0]), "=&v"(R[0].vs[0]), "=&v"(R[0].vs[1]), "=&v"(R[0].vs[2]),
@@ -649,7 +659,7 @@ __device__ __forceinline__ void lds_read_step_async_safe<64>(SubRaw<64> (&R)[2],
       : "memory");
 }
 
-// D = 128: row 72 bytes, subtile 3072 bytes.
+// D = 128: row 72 bytes, subtile 2304 bytes.
 template <>
 __device__ __forceinline__ void lds_read_step_async_safe<128>(SubRaw<128> (&R)[2], const uint8_t* stage,
                                                               const LdsLane& o) {
@@ -668,17 +678,17 @@ __device__ __forceinline__ void lds_read_step_async_safe<128>(SubRaw<128> (&R)[2
       "ds_read_u8 %8, %25 offset:72\n\t"
       "ds_read_u8 %9, %25 offset:144\n\t"
       "ds_read_u8 %10, %25 offset:216\n\t"
-      "ds_read_b64 %11, %22 offset:3072\n\t"
-      "ds_read_b64 %12, %22 offset:3080\n\t"
-      "ds_read_u16 %13, %23 offset:3072\n\t"
-      "ds_read_b32 %14, %24 offset:3072\n\t"
-      "ds_read_b32 %15, %24 offset:3144\n\t"
-      "ds_read_b32 %16, %24 offset:3216\n\t"
-      "ds_read_b32 %17, %24 offset:3288\n\t"
-      "ds_read_u8 %18, %25 offset:3072\n\t"
-      "ds_read_u8 %19, %25 offset:3144\n\t"
-      "ds_read_u8 %20, %25 offset:3216\n\t"
-      "ds_read_u8 %21, %25 offset:3288\n\t"
+      "ds_read_b64 %11, %22 offset:2304\n\t"
+      "ds_read_b64 %12, %22 offset:2312\n\t"
+      "ds_read_u16 %13, %23 offset:2304\n\t"
+      "ds_read_b32 %14, %24 offset:2304\n\t"
+      "ds_read_b32 %15, %24 offset:2376\n\t"
+      "ds_read_b32 %16, %24 offset:2448\n\t"
+      "ds_read_b32 %17, %24 offset:2520\n\t"
+      "ds_read_u8 %18, %25 offset:2304\n\t"
+      "ds_read_u8 %19, %25 offset:2376\n\t"
+      "ds_read_u8 %20, %25 offset:2448\n\t"
+      "ds_read_u8 %21, %25 offset:2520\n\t"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(k0a), "=&v"(k0b), "=&v"(R[0].ks), "=&v"(R[0].v[0][0]), "=&v"(R[0].v[1][0]), "=&v"(R[0].v[2][0]),
         "=&v"(R[0].v[3][0]), "=&v"(R[0].vs[0]), "=&v"(R[0].vs[1]), "=&v"(R[0].vs[2]), "=&v"(R[0].vs[3]),
@@ -696,7 +706,7 @@ __device__ __forceinline__ void lds_read_step_async_safe<128>(SubRaw<128> (&R)[2
   R[1].k[3] = k1b[1];
 }
 
-// D = 256: row 144 bytes, subtile 5120 bytes.
+// D = 256: row 144 bytes, subtile 4608 bytes.
 template <>
 __device__ __forceinline__ void lds_read_step_async_safe<256>(SubRaw<256> (&R)[2], const uint8_t* stage,
                                                               const LdsLane& o) {
@@ -716,17 +726,17 @@ __device__ __forceinline__ void lds_read_step_async_safe<256>(SubRaw<256> (&R)[2
       "ds_read_u8 %8, %25 offset:144\n\t"
       "ds_read_u8 %9, %25 offset:288\n\t"
       "ds_read_u8 %10, %25 offset:432\n\t"
-      "ds_read_b128 %11, %22 offset:5120\n\t"
-      "ds_read_b128 %12, %22 offset:5136\n\t"
-      "ds_read_b32 %13, %23 offset:5120\n\t"
-      "ds_read_b64 %14, %24 offset:5120\n\t"
-      "ds_read_b64 %15, %24 offset:5264\n\t"
-      "ds_read_b64 %16, %24 offset:5408\n\t"
-      "ds_read_b64 %17, %24 offset:5552\n\t"
-      "ds_read_u8 %18, %25 offset:5120\n\t"
-      "ds_read_u8 %19, %25 offset:5264\n\t"
-      "ds_read_u8 %20, %25 offset:5408\n\t"
-      "ds_read_u8 %21, %25 offset:5552\n\t"
+      "ds_read_b128 %11, %22 offset:4608\n\t"
+      "ds_read_b128 %12, %22 offset:4624\n\t"
+      "ds_read_b32 %13, %23 offset:4608\n\t"
+      "ds_read_b64 %14, %24 offset:4608\n\t"
+      "ds_read_b64 %15, %24 offset:4752\n\t"
+      "ds_read_b64 %16, %24 offset:4896\n\t"
+      "ds_read_b64 %17, %24 offset:5040\n\t"
+      "ds_read_u8 %18, %25 offset:4608\n\t"
+      "ds_read_u8 %19, %25 offset:4752\n\t"
+      "ds_read_u8 %20, %25 offset:4896\n\t"
+      "ds_read_u8 %21, %25 offset:5040\n\t"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(k0a), "=&v"(k0b), "=&v"(R[0].ks), "=&v"(v0[0]), "=&v"(v0[1]), "=&v"(v0[2]), "=&v"(v0[3]),
         "=&v"(R[0].vs[0]), "=&v"(R[0].vs[1]), "=&v"(R[0].vs[2]), "=&v"(R[0].vs[3]), "=&v"(k1a), "=&v"(k1b),

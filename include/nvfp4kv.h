@@ -57,7 +57,9 @@ typedef int32_t nvfp4kv_status;
  * _create_nvfp4_hnd_kv_cache] (num_blocks, 2, num_kv_heads, block_size,
  * full_dim) is this descriptor with stride_token = full_dim and
  * stride_head = block_size * full_dim; NHD is stride_head = full_dim.
- * Requirements: data 16-byte aligned, every stride a multiple of 4.
+ * Requirements: data 16-byte aligned, every stride a multiple of 4,
+ * stride_token <= 2^26 and stride_kv <= 2^30 bytes (NVFP4KV_UNSUPPORTED
+ * otherwise).
  */
 typedef struct nvfp4kv_cache {
   uint8_t* data;

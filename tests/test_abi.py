@@ -62,6 +62,8 @@ def test_append_validation():
     assert _append(_desc(block_size=8)) == 2
     assert _append(_desc(reserved=1)) == 1
     assert _append(_desc(stride_token=70)) == 1
+    assert _append(_desc(stride_token=(1 << 26) + 4)) == 2
+    assert _append(_desc(stride_kv=(1 << 30) + 4)) == 2
     assert _append(_desc(data=16 * 1024 + 4)) == 1
     assert _append(_desc(), key=None) == 1
     assert b"key" in lib.nvfp4kv_last_error()
