@@ -153,7 +153,8 @@ nvfp4kv_status nvfp4_paged_attention_decode(const nvfp4kv_cache* cache, const vo
   nvfp4kv::Pool p;
   nvfp4kv_status s = check_cache(cache, p);
   if (s) return s;
-  if (num_seqs < 0 || num_seqs > 4096) return fail(NVFP4KV_UNSUPPORTED, "num_seqs must be in [0, 4096]");
+  if (num_seqs < 0 || num_seqs > nvfp4kv::kDecodeMaxSeqs)
+    return fail(NVFP4KV_UNSUPPORTED, "num_seqs must be in [0, %d]", nvfp4kv::kDecodeMaxSeqs);
   if (num_q_heads < 1 || num_q_heads % p.hkv != 0)
     return fail(NVFP4KV_INVALID_ARGUMENT, "num_q_heads must be a positive multiple of num_kv_heads");
   const int grp = num_q_heads / p.hkv;

@@ -284,7 +284,7 @@ decode_split_kernel(DecodeArgs a) {
     // sequence of this unit: the last b with s_pref[b] <= ubs (the prefix
     // rises strictly and starts at 0), found by a 64-way search of two LDS
     // rounds: the lanes test every stride-th entry, then the entries of the
-    // chosen stride (B <= 4096, so the stride is at most 64)
+    // chosen stride (B <= kDecodeMaxSeqs = 4096, so the stride is at most 64)
     const int stride = (a.B + 63) >> 6;
     int idx = lane * stride;
     uint64_t hits = __builtin_amdgcn_ballot_w64(idx < a.B && s_pref[idx] <= ubs);
@@ -406,15 +406,18 @@ decode_split_kernel(DecodeArgs a) {
   }
 }
 
-// Workspace: [counters, padded to 256 B][partial outputs][partial (max, sum)].
-static int64_t counter_bytes(int num_seqs, int num_kv_heads) {
-  return (((int64_t)num_seqs * num_kv_heads * 4 + 255) / 256) * 256;
+// Workspace: [arrival counters][partial outputs][partial (max, sum)]. The
+// counters are sized for the largest batch a call may have, so their place
+// depends only on num_kv_heads: calls with different batch sizes can share a
+// workspace without one call's partials landing on another's counters.
+static int64_t counter_bytes(int num_kv_heads) {
+  return (((int64_t)kDecodeMaxSeqs * num_kv_heads * 4 + 255) / 256) * 256;
 }
 
 size_t decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_size) {
   const int64_t grp = num_q_heads / num_kv_heads;
   const int64_t slots = kDecodeTargetMax + (int64_t)num_seqs * num_kv_heads;
-  return (size_t)(counter_bytes(num_seqs, num_kv_heads) + slots * grp * head_size * 4 + slots * grp * 2 * 4);
+  return (size_t)(counter_bytes(num_kv_heads) + slots * grp * head_size * 4 + slots * grp * 2 * 4);
 }
 
 template <int D, int MODE>
@@ -506,7 +509,7 @@ hipError_t launch_decode(const Pool& pool, int head_size, const void* q, int64_t
   a.out = static_cast<uint16_t*>(out);
   const int64_t slots = kDecodeTargetMax + (int64_t)num_seqs * pool.hkv;
   a.ws_cnt = static_cast<uint32_t*>(workspace);
-  a.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + counter_bytes(num_seqs, pool.hkv));
+  a.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + counter_bytes(pool.hkv));
   a.ws_ml = a.ws_o + slots * a.grp * head_size;
   switch (head_size) {
     case 64: return launch_decode_t<64>(a, max_seq_len, stream);

@@ -19,6 +19,9 @@ hipError_t launch_dequant(const Pool& pool, int head_size, const int32_t* block_
                           const float* k_scale, const float* v_scale, void* out_k, void* out_v,
                           int64_t out_rows, hipStream_t stream);
 
+// Largest batch of one decode call.
+constexpr int kDecodeMaxSeqs = 4096;
+
 size_t decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_size);
 
 hipError_t launch_decode(const Pool& pool, int head_size, const void* q, int64_t q_st, int64_t q_sh,
@@ -26,7 +29,7 @@ hipError_t launch_decode(const Pool& pool, int head_size, const void* q, int64_t
                          const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len, const float* k_scale,
                          const float* v_scale, float sm_scale, void* out, void* workspace, hipStream_t stream);
 
-// Dynamic LDS bytes of the decode split kernel (must stay within 64 KiB).
+// Dynamic LDS bytes of the decode split kernel (must stay within 160 KiB).
 size_t decode_lds_bytes(int num_seqs, int grp, int head_size);
 
 hipError_t launch_prefill(const Pool& pool, int head_size, const void* q, int64_t q_st, int64_t q_sh,

@@ -146,12 +146,16 @@ size_t nvfp4_paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num
  * max_seq_len: host upper bound of seq_lens, used only to size the grid (a
  * wrong value costs speed, not correctness); lengths are clamped to
  * max_blocks_per_seq * block_size on the device.
+ * The result is deterministic: the same inputs give the same bits.
  * workspace: device scratch of at least
  *   nvfp4_paged_attention_decode_workspace_size(...) bytes, 16-byte aligned,
  *   ZERO-FILLED before its first use. It holds per-(sequence, kv head)
- *   arrival counters that every completed call leaves at zero again, so one
- *   zero fill at allocation suffices. Calls that share a workspace must be
- *   ordered on one stream.
+ *   arrival counters, at places that depend only on num_kv_heads, which
+ *   every completed call leaves at zero again: one zero fill at allocation
+ *   suffices for any later call with the same num_kv_heads and a batch the
+ *   workspace is large enough for. Calls that share a workspace must be
+ *   ordered on one stream. A workspace that breaks this contract gives wrong
+ *   outputs, never an out-of-range access.
  */
 nvfp4kv_status nvfp4_paged_attention_decode(const nvfp4kv_cache* cache,
                                             const void* q, int64_t q_stride_token, int64_t q_stride_head,

@@ -232,24 +232,63 @@ def _decode_into(d, ws, out, max_len):
                                out, ws)
 
 
+def _counter_region_bytes(num_kv_heads):
+    # the workspace starts with the arrival counters, sized for the largest
+    # batch (4096 sequences) and padded to 256 bytes
+    return (((4096 * num_kv_heads * 4) + 255) // 256) * 256
+
+
 def test_decode_workspace_reuse_is_stable():
     """The split-merge counters are left at zero: repeated calls on one
-    workspace, with a different batch in between, give identical results and
-    leave the counter region zeroed."""
+    workspace, with a call of a different batch size on the same workspace
+    in between, give identical results and leave the counter region zeroed."""
+    import bit_quantized_paged_amd as nvk
     w, d, ws = _decode_setup()
     out1 = torch.empty((w.num_seqs, w.num_q_heads, w.head_size), dtype=torch.bfloat16, device="cuda")
     out2 = torch.empty_like(out1)
     _decode_into(d, ws, out1, int(w.seq_lens.max()))
-    w3 = make_config(3, scale=0.004)
-    d3 = Dev(w3, "HND")
-    d3.append_all()
-    d3.decode()
+    # a batch of 2 of the same sequences, through the same workspace
+    sub = w.subset([0, w.num_seqs - 1])
+    ds = Dev(sub, "HND")
+    ds.append_all()
+    out_s = torch.empty((2, w.num_q_heads, w.head_size), dtype=torch.bfloat16, device="cuda")
+    nvk.paged_attention_decode(ds.pool, ds.query, ds.bt, ds.seq_lens, int(sub.seq_lens.max()), ds.k_scale,
+                               ds.v_scale, ds.sm_scale, out_s, ws)
     for _ in range(3):
         _decode_into(d, ws, out2, int(w.seq_lens.max()))
         torch.cuda.synchronize()
         assert torch.equal(out1, out2)
-    cnt_bytes = ((w.num_seqs * w.num_kv_heads * 4 + 255) // 256) * 256
-    assert int(ws[:cnt_bytes].sum().item()) == 0
+    ref_s = O.paged_attention(oracle_pool(sub), sub.query, sub.cu_q, sub.block_table, sub.seq_lens, sub.k_scale,
+                              sub.v_scale, ds.sm_scale, sub.head_size)
+    assert_attn_close(out_s, ref_s, "sub-batch through the shared workspace")
+    assert int(ws[:_counter_region_bytes(w.num_kv_heads)].sum().item()) == 0
+
+
+def test_decode_long_sequences_many_splits():
+    """Long sequences split over many workgroups: parity with the oracle on
+    three consecutive calls through one workspace (counters reset each time,
+    identical bits every call), lengths that end inside a step and a page."""
+    import bit_quantized_paged_amd as nvk
+    w = make_workload(seed=31, name="claims", seq_lens=[32768, 20011, 9000, 1], q_lens=[1, 1, 1, 1],
+                      num_q_heads=16, num_kv_heads=8, head_size=128, block_size=16)
+    d = Dev(w, "HND")
+    d.append_all()
+    ref = O.paged_attention(oracle_pool(w), w.query, w.cu_q, w.block_table, w.seq_lens, w.k_scale, w.v_scale,
+                            d.sm_scale, w.head_size)
+    ws = torch.zeros(nvk.decode_workspace_size(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_size),
+                     dtype=torch.uint8, device="cuda")
+    first = None
+    for k in range(3):
+        out = torch.full((w.num_seqs, w.num_q_heads, w.head_size), float("nan"), dtype=torch.bfloat16,
+                         device="cuda")
+        nvk.paged_attention_decode(d.pool, d.query, d.bt, d.seq_lens, int(w.seq_lens.max()), d.k_scale,
+                                   d.v_scale, d.sm_scale, out, ws)
+        torch.cuda.synchronize()
+        assert_attn_close(out, ref, f"call {k}")
+        if first is None:
+            first = out.clone()
+        assert torch.equal(out, first)
+    assert int(ws[:_counter_region_bytes(w.num_kv_heads)].sum().item()) == 0
 
 
 def test_decode_graph_replays_match_eager():
