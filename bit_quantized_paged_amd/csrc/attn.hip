@@ -521,8 +521,10 @@ hipError_t launch_decode(const Pool& pool, int head_size, const void* q, int64_t
 
 // ---------------------------------------------------------------------------
 // Chunked prefill. Columns of (sequence b, kv head h) are (token, group head)
-// pairs, token-major; a wave owns 16*NT consecutive columns and walks keys
-// 0 .. its last visible key. No split-K: long chunks already give many waves.
+// pairs, token-major; a workgroup owns 64*NT consecutive columns (16*NT per
+// wave) and walks keys 0 .. the last key its columns see, its four waves
+// sharing the dequantisation of each step. No split-K: long chunks already
+// give many workgroups.
 // ---------------------------------------------------------------------------
 struct PrefillArgs {
   Pool pool;
@@ -556,8 +558,24 @@ __device__ __forceinline__ void store_column(uint16_t* orow, const f4 (&acc)[Geo
   for (int c = 0; c < DPL / 2; ++c) dst[c] = u32x4{pk[4 * c], pk[4 * c + 1], pk[4 * c + 2], pk[4 * c + 3]};
 }
 
-template <int D, int NT>
+// Prefill ring stages: the step being dequantised and up to three in flight
+// (as many as the 6-bit wait counter can cover).
+template <int D, bool COMPACT>
+struct PrefillStages {
+  static constexpr int NC = StageGeo<D, COMPACT>::NC;
+  static constexpr int NS = (63 / NC + 1) < 4 ? (63 / NC + 1) : 4;
+};
+
+template <int D, int NT, bool COMPACT>
 __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
+  using G = Geo<D>;
+  using SG = StageGeo<D, COMPACT>;
+  using OG = OpGeo<D>;
+  constexpr int NS = PrefillStages<D, COMPACT>::NS;
+  extern __shared__ __align__(16) char smem[];
+  uint8_t* ring = reinterpret_cast<uint8_t*>(smem);  // [NS] raw steps
+  uint8_t* opbuf = ring + NS * SG::STAGE;             // [2] operand buffers
+
   const int b = blockIdx.z, h = blockIdx.y, cb = blockIdx.x;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -570,8 +588,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   const int L = clamp_len(a.seq_lens[b], cap);
   const int grp = a.grp;
   const int ncols = qlen * grp;
-  const int col_base = (cb * 4 + w) * 16 * NT;
-  if (col_base >= ncols) return;
+  const int wg_col = cb * 4 * 16 * NT;
+  if (wg_col >= ncols) return;  // the whole workgroup
+  const int col_base = wg_col + w * 16 * NT;
 
   WaveAttn<D, NT> W;
   W.init();
@@ -588,23 +607,69 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     lim = lim > L - 1 ? L - 1 : lim;
     W.lim[n] = valid ? lim : -1;
   }
-  const int c_last = ((col_base + 16 * NT < ncols) ? col_base + 16 * NT : ncols) - 1;
-  int kmax = a.causal ? L - qlen + c_last / grp + 1 : L;
+  // keys the workgroup streams: up to the last visible key of its last column
+  const int wg_last = ((wg_col + 64 * NT < ncols) ? wg_col + 64 * NT : ncols) - 1;
+  int kmax = a.causal ? L - qlen + wg_last / grp + 1 : L;
   kmax = kmax > L ? L : (kmax < 0 ? 0 : kmax);
   const int steps = ceil_div(kmax, kStep);
+  // keys this wave's columns see (none if it has no column), and below
+  // min_full every valid column of the wave sees every key
+  const bool has_cols = col_base < ncols;
+  const int c_last = ((col_base + 16 * NT < ncols) ? col_base + 16 * NT : ncols) - 1;
+  int kw = has_cols ? (a.causal ? L - qlen + c_last / grp + 1 : L) : 0;
+  kw = kw > L ? L : (kw < 0 ? 0 : kw);
+  const int min_full = a.causal ? L - qlen + col_base / grp + 1 : L;
   const int32_t* bt_row = a.bt + (int64_t)b * a.max_blocks;
+  const DmaOffsets<D, COMPACT> dof = dma_offsets<D, COMPACT>(a.pool.st, a.pool.skv, lane);
+  const LdsLane ll = lds_lane<D>(i, j);
+  const uint32_t op_lane = lds_addr(opbuf) + lane * 16;
 
-  // keys below min_full are visible to every valid column of the wave
-  const int c_first = col_base;
-  const int min_full = a.causal ? L - qlen + c_first / grp + 1 : L;
-  const LaneOffsets<D> off = lane_offsets<D>(a.pool.st, i, j);
-  auto ids_at = [&](int kk) { return step_ids(bt_row, kk * kStep, kk < steps ? L : 0, a.pool); };
-  auto run = [&](SubRaw<D>(&R)[2], int kk) {
-    const int kb = kk * kStep;
+  // ---- the four waves share each 32-key step: wave 0 copies it into the
+  // ring (NS - 1 steps ahead), every wave reads the raw step
+  // and dequantises a quarter of its MFMA operands into the step's operand
+  // buffer, and every wave then runs its own columns' products from all of
+  // them. Two barriers per step: the raw step has landed; the operands are
+  // in place. Ring stage k % NS is refilled only after the second barrier of
+  // step k (every wave has read it), operand buffer k % 2 only after the
+  // first barrier of step k + 1 (every wave has used step k's).
+  const bool copier = w == 0;
+  if (copier) {
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s)
+      dma_step<D, COMPACT>(ring + s * SG::STAGE, a.pool, ids_for_step(bt_row, s, steps, L, a.pool), h, s * kStep,
+                           dof);
+  }
+  StepIds nxt = ids_for_step(bt_row, NS - 1, steps, L, a.pool);
+  for (int k = 0; k < steps; ++k) {
+    if (copier)
+      dma_step<D, COMPACT>(ring + ((k + NS - 1) % NS) * SG::STAGE, a.pool, nxt, h, (k + NS - 1) * kStep, dof);
+    nxt = ids_for_step(bt_row, k + NS, steps, L, a.pool);
+    wait_vmcnt<(NS - 1) * SG::NC>();  // the copier: step k has landed (others: no-op)
+    lds_barrier();          // every wave may read step k
+    SubRaw<D> R[2];
+    lds_read_step_async_safe<D>(R, ring + (k % NS) * SG::STAGE, ll);
+    const int kb = k * kStep;
     if (kb + kStep > L) mask_step<D>(R, kb, L, j);
-    W.step(R, kb, j, kb + kStep > min_full);
-  };
-  stream_steps<D>(0, 1, steps, a.pool, h, off, ids_at, run);
+    VPairs<D> vp[2];
+    make_pairs(R[0], vp[0]);
+    make_pairs(R[1], vp[1]);
+    const uint32_t slot = op_lane + (uint32_t)((k & 1) * OG::BYTES);
+    make_ops<D, 0>(R, vp, w, slot);
+    lds_barrier();          // every operand of step k is in place
+    if (kb < kw) {
+      h8 ka[2][G::KW], va[G::DPL];
+      f4 sc[2][NT];
+      // K operands first (D = 64: one group of 8 holds K and V), then V
+      constexpr int KEND = OG::NK < 8 ? 8 : OG::NK;
+      load_ops<D, 0, KEND>(ka, va, slot);
+      W.scores_ops(ka, sc);
+      h8 p[NT];
+      W.softmax(sc, kb, j, kb + kStep > min_full, p);
+      load_ops<D, KEND, OG::NE>(ka, va, slot);
+      W.pv_ops(va, p);
+    }
+  }
+  wait_vmcnt<0>();
 
   const float gv = *a.v_scale;
 #pragma unroll
@@ -619,6 +684,11 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   }
 }
 
+template <int D, bool COMPACT>
+size_t prefill_lds_bytes() {
+  return (size_t)PrefillStages<D, COMPACT>::NS * StageGeo<D, COMPACT>::STAGE + 2 * OpGeo<D>::BYTES;
+}
+
 template <int D, int NT>
 static hipError_t launch_prefill_t(const PrefillArgs& a, int num_seqs, int max_q_len, hipStream_t stream) {
   const int64_t cols = (int64_t)max_q_len * a.grp;
@@ -626,7 +696,13 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, int num_seqs, int max_q
   const int64_t gx = (cols + per_wg - 1) / per_wg;
   if (gx == 0) return hipSuccess;
   const dim3 grid((unsigned)gx, (unsigned)a.pool.hkv, (unsigned)num_seqs);
-  prefill_kernel<D, NT><<<grid, 256, 0, stream>>>(a);
+  // 16-byte copies need contiguous, 16-byte aligned page rows (HND layout)
+  const bool compact = a.pool.st == D / 2 + D / 16 && a.pool.sb % 16 == 0 && a.pool.skv % 16 == 0 &&
+                       a.pool.sh % 16 == 0 && (reinterpret_cast<uintptr_t>(a.pool.data) % 16) == 0;
+  if (compact)
+    prefill_kernel<D, NT, true><<<grid, 256, prefill_lds_bytes<D, true>(), stream>>>(a);
+  else
+    prefill_kernel<D, NT, false><<<grid, 256, prefill_lds_bytes<D, false>(), stream>>>(a);
   return hipGetLastError();
 }
 
@@ -657,7 +733,7 @@ hipError_t launch_prefill(const Pool& pool, int head_size, const void* q, int64_
   switch (head_size) {
     case 64: return launch_prefill_t<64, 4>(a, num_seqs, max_q_len, stream);
     case 128: return launch_prefill_t<128, 2>(a, num_seqs, max_q_len, stream);
-    case 256: return launch_prefill_t<256, 1>(a, num_seqs, max_q_len, stream);
+    case 256: return launch_prefill_t<256, 2>(a, num_seqs, max_q_len, stream);
     default: return hipErrorInvalidValue;
   }
 }

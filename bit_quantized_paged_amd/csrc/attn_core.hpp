@@ -65,30 +65,10 @@ __device__ __forceinline__ void zero_sub(SubRaw<D>& R) {
   }
 }
 
-// Byte offsets of this lane's loads inside a 16-row subtile; they depend only
-// on the lane and the row stride, so a wave computes them once.
-template <int D>
-struct LaneOffsets {
-  uint32_t k, ks, v, vs;  // v / vs: row 4j of the lane's four value rows
-  int32_t st;             // row stride; value row 4j + r adds r * st (scalar)
-};
-
-template <int D>
-__device__ __forceinline__ LaneOffsets<D> lane_offsets(int64_t st, int i, int j) {
-  LaneOffsets<D> o;
-  const uint32_t s = (uint32_t)st;
-  o.k = i * s + j * (D / 8);
-  o.ks = i * s + D / 2 + j * (D / 64);
-  o.v = 4 * j * s + i * Geo<D>::VB;
-  o.vs = 4 * j * s + D / 2 + (i * Geo<D>::DPL) / 16;
-  o.st = (int32_t)st;
-  return o;
-}
-
 // Pages are read with raw buffer loads: a wave-uniform descriptor per
 // subtile (base = first row of the subtile, size = the bytes its 16 rows
-// span) plus the lane offsets above. A subtile with nothing to read gets size
-// 0, which makes the hardware return zeros without touching memory, so the
+// span) plus per-lane offsets. A subtile with nothing to read gets size 0,
+// which makes the hardware return zeros without touching memory, so the
 // loads of a step are issued unconditionally and every access is
 // range-checked against its own page.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
@@ -96,46 +76,6 @@ constexpr int kRsrcWord3 = 0x00020000;  // raw (unformatted) buffer, gfx9 family
 
 __device__ __forceinline__ rsrc_t make_rsrc(const uint8_t* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, bytes, kRsrcWord3);
-}
-
-template <int D>
-__device__ __forceinline__ void load_sub(SubRaw<D>& R, rsrc_t kr, rsrc_t vr, const LaneOffsets<D>& o) {
-  if constexpr (D == 64) {
-    const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(kr, o.k, 0, 0);
-    R.k[0] = w[0];
-    R.k[1] = w[1];
-    R.ks = __builtin_amdgcn_raw_buffer_load_b8(kr, o.ks, 0, 0);
-  } else if constexpr (D == 128) {
-    const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(kr, o.k, 0, 0);
-    R.k[0] = w[0];
-    R.k[1] = w[1];
-    R.k[2] = w[2];
-    R.k[3] = w[3];
-    R.ks = __builtin_amdgcn_raw_buffer_load_b16(kr, o.ks, 0, 0);
-  } else {
-    const u32x4 w0 = __builtin_amdgcn_raw_buffer_load_b128(kr, o.k, 0, 0);
-    const u32x4 w1 = __builtin_amdgcn_raw_buffer_load_b128(kr, o.k + 16, 0, 0);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      R.k[c] = w0[c];
-      R.k[4 + c] = w1[c];
-    }
-    R.ks = __builtin_amdgcn_raw_buffer_load_b32(kr, o.ks, 0, 0);
-  }
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int so = r * o.st;
-    if constexpr (D == 64) {
-      R.v[r][0] = __builtin_amdgcn_raw_buffer_load_b16(vr, o.v, so, 0);
-    } else if constexpr (D == 128) {
-      R.v[r][0] = __builtin_amdgcn_raw_buffer_load_b32(vr, o.v, so, 0);
-    } else {
-      const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(vr, o.v, so, 0);
-      R.v[r][0] = w[0];
-      R.v[r][1] = w[1];
-    }
-    R.vs[r] = __builtin_amdgcn_raw_buffer_load_b8(vr, o.vs, so, 0);
-  }
 }
 
 // Zero the value rows of keys >= L (unwritten rows may hold NaN scale bytes;
@@ -301,8 +241,40 @@ struct WaveAttn {
       for (int n = 0; n < NT; ++n) s[sb][n] = f4{0.f, 0.f, 0.f, 0.f};
       chunks<0>(R[sb], s[sb]);
     }
-    // ---- online softmax
     h8 p[NT];
+    softmax(s, kb, j, masked, p);
+    // ---- O^T += V^ T . P^T
+    VPairs<D> vp[2];
+    make_pairs(R[0], vp[0]);
+    make_pairs(R[1], vp[1]);
+    pv<0>(vp, p);
+  }
+
+  // The step's halves from operands already dequantised into the MFMA lane
+  // layout: ka[sb][c] = k_chunk<c>(subtile sb); va[t] = the V^T tile t that
+  // pv builds (both subtiles' keys).
+  __device__ __forceinline__ void scores_ops(const h8 (&ka)[2][G::KW], f4 (&s)[2][NT]) {
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+      for (int n = 0; n < NT; ++n) s[sb][n] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < G::KW; ++c)
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+          s[sb][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[sb][c], q[n][c], s[sb][n], 0, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void pv_ops(const h8 (&va)[G::DPL], const h8 (&p)[NT]) {
+#pragma unroll
+    for (int t = 0; t < G::DPL; ++t)
+#pragma unroll
+      for (int n = 0; n < NT; ++n) acc[n][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[t], p[n], acc[n][t], 0, 0, 0);
+  }
+
+  // Online softmax of a step's scores (base 2, lazy rescale) into the f16
+  // probabilities p of each column tile.
+  __device__ __forceinline__ void softmax(const f4 (&s)[2][NT], int kb, int j, bool masked, h8 (&p)[NT]) {
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
       float x[8];
@@ -347,11 +319,6 @@ struct WaveAttn {
       }
       l[n] = ps;
     }
-    // ---- O^T += V^ T . P^T
-    VPairs<D> vp[2];
-    make_pairs(R[0], vp[0]);
-    make_pairs(R[1], vp[1]);
-    pv<0>(vp, p);
   }
 
   template <int C>
@@ -402,49 +369,6 @@ __device__ __forceinline__ StepIds step_ids(const int32_t* bt_row, int kb, int l
   s.id[0] = ld_uniform(bt_row, s.ok[0] ? page : 0);
   s.id[1] = (pool.bs == 16) ? ld_uniform(bt_row, s.ok[1] ? page + 1 : 0) : s.id[0];
   return s;
-}
-
-// Issue the loads of the 32-key step at kb.
-template <int D>
-__device__ __forceinline__ void load_step(SubRaw<D> (&R)[2], const Pool& pool, const StepIds& ids, int h, int kb,
-                                          const LaneOffsets<D>& o) {
-  const int extent = 15 * (int)pool.st + D / 2 + D / 16;
-#pragma unroll
-  for (int sb = 0; sb < 2; ++sb) {
-    const int row0 = (kb + 16 * sb) & (pool.bs - 1);
-    const int64_t blk = clamp_block(ids.id[sb], pool.num_blocks);
-    const uint8_t* kbase = pool.data + blk * pool.sb + (int64_t)h * pool.sh + (int64_t)row0 * pool.st;
-    const int n = ids.ok[sb] ? extent : 0;
-    load_sub<D>(R[sb], make_rsrc(kbase, n), make_rsrc(kbase + pool.skv, n), o);
-  }
-  // keep the scheduler from hoisting work on the previous step's data above
-  // these loads (that would make their issue wait for that data)
-  __builtin_amdgcn_sched_barrier(0);
-}
-
-// Stream the steps k0, k0 + ks, ... (< kend) through two register buffers:
-// the data of the next step is in flight while a step is computed, and block
-// ids are read one step further ahead. ids_at(k) must return not-ok ids for
-// k >= kend; run(R, k) consumes step k.
-template <int D, typename IdsAt, typename Run>
-__device__ __forceinline__ void stream_steps(int k0, int ks, int kend, const Pool& pool, int h,
-                                             const LaneOffsets<D>& off, IdsAt ids_at, Run run) {
-  if (k0 >= kend) return;
-  SubRaw<D> A[2], B[2];
-  load_step<D>(A, pool, ids_at(k0), h, k0 * 32, off);
-  StepIds ib = ids_at(k0 + ks);
-  int k = k0;
-  while (true) {
-    load_step<D>(B, pool, ib, h, (k + ks) * 32, off);
-    const StepIds ia = ids_at(k + 2 * ks);
-    run(A, k);
-    if (k + ks >= kend) break;
-    load_step<D>(A, pool, ia, h, (k + 2 * ks) * 32, off);
-    ib = ids_at(k + 3 * ks);
-    run(B, k + ks);
-    k += 2 * ks;
-    if (k >= kend) break;
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -765,6 +689,100 @@ __device__ __forceinline__ void mask_step(SubRaw<D> (&R)[2], int kb, int L, int 
   if (kb + 32 > L) {
     mask_sub_values<D>(R[0], kb, L, j);
     mask_sub_values<D>(R[1], kb + 16, L, j);
+  }
+}
+
+}  // namespace nvfp4kv
+
+namespace nvfp4kv {
+
+// ---------------------------------------------------------------------------
+// Shared operand tiles (prefill). The four waves of a workgroup dequantise a
+// step together: operand e of the step (K chunks e < 2 * KW, in the order
+// (subtile, chunk); then the V^T tiles) is 64 lanes x 16 bytes in the lane
+// layout the MFMA takes, stored at e * 1024 + lane * 16 of an operand
+// buffer, so that every write and read is one conflict-free 16-byte LDS
+// access per lane. The accesses are asm for the reason the step reader is:
+// direct-to-LDS copies are in flight around them.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void lds_store_op(uint32_t addr, const h8& v) {
+  asm volatile("ds_write_b128 %0, %1" : : "v"(addr), "v"(v) : "memory");
+}
+
+// Eight consecutive operands starting at the operand whose lane slot is addr.
+__device__ __forceinline__ void lds_load_ops8(h8 (&o)[8], uint32_t addr) {
+  asm volatile(
+      "ds_read_b128 %0, %8\n\t"
+      "ds_read_b128 %1, %8 offset:1024\n\t"
+      "ds_read_b128 %2, %8 offset:2048\n\t"
+      "ds_read_b128 %3, %8 offset:3072\n\t"
+      "ds_read_b128 %4, %8 offset:4096\n\t"
+      "ds_read_b128 %5, %8 offset:5120\n\t"
+      "ds_read_b128 %6, %8 offset:6144\n\t"
+      "ds_read_b128 %7, %8 offset:7168\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7])
+      : "v"(addr)
+      : "memory");
+}
+
+// Workgroup barrier after this wave's LDS accesses have completed.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory"); }
+
+template <int D>
+struct OpGeo {
+  static constexpr int NK = 2 * Geo<D>::KW;           // K operands per step
+  static constexpr int NE = NK + Geo<D>::DPL;         // all operands per step
+  static constexpr int BYTES = NE * 1024;             // one operand buffer
+  static_assert(NK % 8 == 0 || D == 64, "K operands come in groups of 8");
+};
+
+// Operand E of the step, from its raw bytes (vp: make_pairs of both subtiles).
+template <int D, int E>
+__device__ __forceinline__ h8 make_op(const SubRaw<D> (&R)[2], const VPairs<D> (&vp)[2]) {
+  using G = Geo<D>;
+  if constexpr (E < 2 * G::KW) {
+    return k_chunk<D, E % G::KW>(R[E / G::KW]);
+  } else {
+    constexpr int T = E - 2 * G::KW;
+    const h4 a0 = v_operand<D, T>(vp[0]);
+    const h4 a1 = v_operand<D, T>(vp[1]);
+    return h8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+  }
+}
+
+// Build and store this wave's share of the step's operands (E = w, w + 4, ...)
+// at slot + E * 1024 (slot: this lane's place in the operand buffer).
+template <int D, int E>
+__device__ __forceinline__ void make_ops(const SubRaw<D> (&R)[2], const VPairs<D> (&vp)[2], int w, uint32_t slot) {
+  if constexpr (E < OpGeo<D>::NE) {
+    if ((E & 3) == w) lds_store_op(slot + E * 1024, make_op<D, E>(R, vp));
+    make_ops<D, E + 1>(R, vp, w, slot);
+  }
+}
+
+template <int D, int E0>
+__device__ __forceinline__ void load_ops8(h8 (&ka)[2][Geo<D>::KW], h8 (&va)[Geo<D>::DPL], uint32_t slot) {
+  using G = Geo<D>;
+  h8 t[8];
+  lds_load_ops8(t, slot + E0 * 1024);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int E = E0 + e;
+    if (E < 2 * G::KW)
+      ka[E / G::KW][E % G::KW] = t[e];
+    else if (E < OpGeo<D>::NE)
+      va[E - 2 * G::KW] = t[e];
+  }
+}
+
+// Operands [E0, E1) of the buffer (groups of 8; slot: this lane's place in
+// the buffer) into ka (K operands) or va (V^T tiles).
+template <int D, int E0, int E1>
+__device__ __forceinline__ void load_ops(h8 (&ka)[2][Geo<D>::KW], h8 (&va)[Geo<D>::DPL], uint32_t slot) {
+  if constexpr (E0 < E1) {
+    load_ops8<D, E0>(ka, va, slot);
+    load_ops<D, E0 + 8, E1>(ka, va, slot);
   }
 }
 
