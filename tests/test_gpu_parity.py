@@ -99,15 +99,16 @@ def test_decode_parity(case, layout):
 
 
 @pytest.mark.parametrize("causal", [True, False])
-def test_prefill_parity(case, causal):
+@pytest.mark.parametrize("layout", ["HND", "NHD"])
+def test_prefill_parity(case, causal, layout):
     name, w, ref_pool = case
-    d = Dev(w, "HND")
+    d = Dev(w, layout)
     d.append_all()
     out = d.prefill(causal=causal)
     torch.cuda.synchronize()
     ref = O.paged_attention(ref_pool, w.query, w.cu_q, w.block_table, w.seq_lens, w.k_scale, w.v_scale,
                             np.float32(d.sm_scale), w.head_size, causal=causal)
-    assert_attn_close(out, ref, f"{name} prefill causal={causal}")
+    assert_attn_close(out, ref, f"{name} {layout} prefill causal={causal}")
 
 
 def test_decode_equals_prefill_with_one_query(case):
