@@ -7,8 +7,9 @@
 namespace nvfp4kv {
 
 // ---------------------------------------------------------------------------
-// Decode schedule. A unit is (sequence, split, kv head); a split is a run of
-// `tps` 32-key steps. tps is chosen on the device from the actual lengths so
+// Decode schedule. A unit is (sequence, split, kv head); a sequence of s
+// 32-key steps has ceil(s / tps) splits that share its steps evenly. tps is
+// chosen on the device from the actual lengths so
 // that the batch yields about `target` units of equal size (target = the
 // number of decode workgroups the GPU holds at once, so that all units run in
 // a single round), which keeps
@@ -265,7 +266,6 @@ decode_split_kernel(DecodeArgs a) {
   const int cap = a.max_blocks * a.pool.bs;
   int tps, total;
   decode_schedule(a.seq_lens, a.B, cap, hkv, a.target, s_pref, s_len, s_red, tps, total);
-  tps = __builtin_amdgcn_readfirstlane(tps);
   total = __builtin_amdgcn_readfirstlane(total);
   const float qk_factor = a.sm_scale * uniform_f32(ksc) * kLog2e;
   const float gv = uniform_f32(vsc);
@@ -297,8 +297,11 @@ decode_split_kernel(DecodeArgs a) {
     const int nsplit = __builtin_amdgcn_readfirstlane(s_pref[b + 1]) - pb;
     const int L = __builtin_amdgcn_readfirstlane(s_len[b]);
     const int steps = ceil_div(L, kStep);
-    const int st0 = split * tps;
-    const int st1 = (st0 + tps < steps) ? st0 + tps : steps;
+    // the sequence's steps are dealt evenly over its nsplit units: the first
+    // steps % nsplit units take one step more (nsplit <= steps when steps > 0)
+    const int sq = steps / nsplit, sr = steps - sq * nsplit;
+    const int st0 = split * sq + (split < sr ? split : sr);
+    const int st1 = st0 + sq + (split < sr ? 1 : 0);
 
     const int32_t* bt_row = a.bt + (int64_t)b * a.max_blocks;
     const int k0 = st0 + w;  // the wave's steps: k0, k0 + 4, ... below st1
