@@ -240,10 +240,86 @@ struct DecodeOcc {
   static constexpr int waves = (D == 256) ? 2 : 3;
 };
 
+// One wave's share of a (sequence, kv head) unit: steps k0, k0 + NWS, ...
+// below st1, streamed through the wave's ring of NS stages (step k + (NS - 1)
+// * NWS is copied while step k, already in LDS, is computed). The query load
+// is issued first so that it is in flight with the block-table reads the
+// first copies wait for. Leaves the wave's softmax state in W; every copy has
+// landed when it returns.
+template <int D, bool COMPACT, int NS, int NWS>
+__device__ __forceinline__ void decode_stream(WaveAttn<D, 1>& W, uint8_t* ring, const Pool& pool,
+                                              const int32_t* bt_row, int L, int h, int k0, int st1,
+                                              const uint16_t* qrow, float qk_factor,
+                                              const DmaOffsets<D, COMPACT>& dof, const LdsLane& ll, int j) {
+  using SG = StageGeo<D, COMPACT>;
+  const auto qraw = WaveAttn<D, 1>::load_q_raw(qrow, j);
+  StepIds nxt = lds_prologue<D, COMPACT, NS>(ring, k0, NWS, st1, bt_row, L, pool, h, dof);
+  W.set_q(0, qraw, qk_factor);
+  int slot = 0;
+  for (int k = k0; k < st1; k += NWS) {
+    const int fill = (slot + NS - 1) % NS;
+    dma_step<D, COMPACT>(ring + fill * SG::STAGE, pool, nxt, h, (k + (NS - 1) * NWS) * kStep, dof);
+    nxt = ids_for_step(bt_row, k + NS * NWS, st1, L, pool);
+    wait_vmcnt<(NS - 1) * SG::NC>();
+    SubRaw<D> R[2];
+    lds_read_step_async_safe<D>(R, ring + slot * SG::STAGE, ll);
+    const int kb = k * kStep;
+    const bool partial = kb + kStep > L;
+    if (partial) mask_step<D>(R, kb, L, j);
+    W.step(R, kb, j, partial);
+    slot = (slot + 1 == NS) ? 0 : slot + 1;
+  }
+  wait_vmcnt<0>();
+}
+
+// Merge the NWS waves' softmax states of a unit through LDS (s_ml: [NWS][16]
+// (max, sum); s_o: [NWS][kMergeCols][D], which may overlap the drained
+// rings), kMergeCols columns at a time. emit(col, d, on, M, lt) gets every
+// output element: on = o / lt (0 when lt == 0), with the column's merged max
+// M and sum lt.
+template <int D, int NWS, typename Emit>
+__device__ __forceinline__ void merge_waves(const WaveAttn<D, 1>& W, float* s_ml, float* s_o, int grp, int w, int i,
+                                            int j, Emit&& emit) {
+  using G = Geo<D>;
+  const float lsum = wave_sum_j(W.l[0]);
+  if (j == 0) {
+    s_ml[(w * 16 + i) * 2] = W.m[0];
+    s_ml[(w * 16 + i) * 2 + 1] = lsum;
+  }
+  for (int c0 = 0; c0 < grp; c0 += kMergeCols) {
+    const int nc = (grp - c0 < kMergeCols) ? grp - c0 : kMergeCols;
+    if (i >= c0 && i < c0 + nc) {
+      float* dst = s_o + (w * kMergeCols + (i - c0)) * D;
+#pragma unroll
+      for (int t = 0; t < G::DPL; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dst[(4 * j + r) * G::DPL + t] = W.acc[0][t][r];
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < nc * D; e += 64 * NWS) {
+      const int cc = e / D;
+      const int col = c0 + cc;
+      const int d = e - cc * D;
+      float M = -__builtin_inff();
+#pragma unroll
+      for (int ww = 0; ww < NWS; ++ww) M = __builtin_fmaxf(M, s_ml[(ww * 16 + col) * 2]);
+      float lt = 0.0f, o = 0.0f;
+#pragma unroll
+      for (int ww = 0; ww < NWS; ++ww) {
+        const float mw = s_ml[(ww * 16 + col) * 2];
+        const float f = (mw == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
+        lt += f * s_ml[(ww * 16 + col) * 2 + 1];
+        o += f * s_o[(ww * kMergeCols + cc) * D + d];
+      }
+      emit(col, d, lt > 0.0f ? o / lt : 0.0f, M, lt);
+    }
+    __syncthreads();
+  }
+}
+
 template <int D, int MODE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DecodeOcc<D, MODE>::waves))) void
 decode_split_kernel(DecodeArgs a) {
-  using G = Geo<D>;
   constexpr bool COMPACT = MODE != kModeDmaGeneral;
   using SG = StageGeo<D, COMPACT>;
   constexpr int NS = DecodeStages<D>::NS;
@@ -311,77 +387,21 @@ decode_split_kernel(DecodeArgs a) {
     const uint16_t* qrow = valid ? a.q + (int64_t)b * a.q_st + (int64_t)(h * grp + i) * a.q_sh : nullptr;
     W.lim[0] = valid ? L - 1 : -1;
 
-    // ---- stream the wave's steps through its ring of NS stages: copy step
-    // k + (NS - 1) * 4 while step k, already in LDS, is computed. The query
-    // load is issued first so that it is in flight with the block-table
-    // reads the first copies wait for.
-    const auto qraw = WaveAttn<D, 1>::load_q_raw(qrow, j);
-    StepIds nxt = lds_prologue<D, COMPACT, NS>(ring, k0, 4, st1, bt_row, L, a.pool, h, dof);
-    W.set_q(0, qraw, qk_factor);
-    int slot = 0;
-    for (int k = k0; k < st1; k += 4) {
-      const int fill = (slot + NS - 1) % NS;
-      dma_step<D, COMPACT>(ring + fill * SG::STAGE, a.pool, nxt, h, (k + (NS - 1) * 4) * kStep, dof);
-      nxt = ids_for_step(bt_row, k + NS * 4, st1, L, a.pool);
-      wait_vmcnt<(NS - 1) * SG::NC>();
-      SubRaw<D> R[2];
-      lds_read_step_async_safe<D>(R, ring + slot * SG::STAGE, ll);
-      const int kb = k * kStep;
-      const bool partial = kb + kStep > L;
-      if (partial) mask_step<D>(R, kb, L, j);
-      W.step(R, kb, j, partial);
-      slot = (slot + 1 == NS) ? 0 : slot + 1;
-    }
-    wait_vmcnt<0>();
+    decode_stream<D, COMPACT, NS, 4>(W, ring, a.pool, bt_row, L, h, k0, st1, qrow, qk_factor, dof, ll, j);
     __syncthreads();  // every wave's ring is drained before the rings become the merge buffer
-
-    // ---- merge the four waves' partial softmax states through LDS, eight
-    // columns at a time
-    const float lsum = wave_sum_j(W.l[0]);
-    if (j == 0) {
-      s_ml[(w * 16 + i) * 2] = W.m[0];
-      s_ml[(w * 16 + i) * 2 + 1] = lsum;
-    }
-    for (int c0 = 0; c0 < grp; c0 += kMergeCols) {
-      const int nc = (grp - c0 < kMergeCols) ? grp - c0 : kMergeCols;
-      if (i >= c0 && i < c0 + nc) {
-        float* dst = s_o + (w * kMergeCols + (i - c0)) * D;
-#pragma unroll
-        for (int t = 0; t < G::DPL; ++t)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) dst[(4 * j + r) * G::DPL + t] = W.acc[0][t][r];
-      }
-      __syncthreads();
-      for (int e = threadIdx.x; e < nc * D; e += 256) {
-        const int cc = e / D;
-        const int col = c0 + cc;
-        const int d = e - cc * D;
-        float M = -__builtin_inff();
-#pragma unroll
-        for (int ww = 0; ww < 4; ++ww) M = __builtin_fmaxf(M, s_ml[(ww * 16 + col) * 2]);
-        float lt = 0.0f, o = 0.0f;
-#pragma unroll
-        for (int ww = 0; ww < 4; ++ww) {
-          const float mw = s_ml[(ww * 16 + col) * 2];
-          const float f = (mw == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
-          lt += f * s_ml[(ww * 16 + col) * 2 + 1];
-          o += f * s_o[(ww * kMergeCols + cc) * D + d];
-        }
-        const float on = lt > 0.0f ? o / lt : 0.0f;
-        if (nsplit == 1) {
-          const float y = on * gv;
-          a.out[((int64_t)b * a.hq + h * grp + col) * D + d] = (uint16_t)(pack_bf16x2(y, 0.0f) & 0xFFFFu);
-        } else {
-          const int64_t slot = (int64_t)ubs * hkv + h;
-          st_agent(a.ws_o + (slot * grp + col) * D + d, on);
-          if (d == 0) {
-            st_agent(a.ws_ml + (slot * grp + col) * 2, M);
-            st_agent(a.ws_ml + (slot * grp + col) * 2 + 1, lt);
-          }
+    merge_waves<D, 4>(W, s_ml, s_o, grp, w, i, j, [&](int col, int d, float on, float M, float lt) {
+      if (nsplit == 1) {
+        const float y = on * gv;
+        a.out[((int64_t)b * a.hq + h * grp + col) * D + d] = (uint16_t)(pack_bf16x2(y, 0.0f) & 0xFFFFu);
+      } else {
+        const int64_t slot = (int64_t)ubs * hkv + h;
+        st_agent(a.ws_o + (slot * grp + col) * D + d, on);
+        if (d == 0) {
+          st_agent(a.ws_ml + (slot * grp + col) * 2, M);
+          st_agent(a.ws_ml + (slot * grp + col) * 2 + 1, lt);
         }
       }
-      __syncthreads();
-    }
+    });
     if (nsplit > 1) {
       // The last of the sequence's splits to arrive merges all of them
       // (log-sum-exp weights) and resets the counter for the next call.
@@ -407,6 +427,72 @@ decode_split_kernel(DecodeArgs a) {
     // flight at the top of each iteration.
     wait_stores();
   }
+}
+
+// ---------------------------------------------------------------------------
+// Decode without split-K: one workgroup of NW waves per (sequence, kv head).
+// The waves take interleaved steps and merge in LDS, and the workgroup writes
+// the bf16 output itself: no schedule, no partials, no combine. Chosen when
+// the batch alone gives every CU a (sequence, kv head) pair and no sequence
+// needs more than a few steps per wave; longer or fewer sequences go to the
+// split kernel.
+// ---------------------------------------------------------------------------
+template <int D>
+struct PairGeo {
+  static constexpr int NW = (D == 256) ? 8 : 12;  // waves per workgroup (LDS holds one workgroup per CU)
+  static constexpr int kMaxStepsPerWave = 8;
+};
+
+template <int D, int MODE>
+struct PairLds {
+  static constexpr int NW = PairGeo<D>::NW;
+  static constexpr int stream = NW * DecodeStages<D>::NS * StageGeo<D, MODE == kModeDmaCompact>::STAGE;
+  static constexpr int merge = NW * kMergeCols * D * 4;
+  static constexpr int bytes = NW * 16 * 2 * 4 + (stream > merge ? stream : merge);
+  static_assert(bytes <= 160 * 1024, "one workgroup per CU");
+};
+
+template <int D, int MODE>
+__global__ __launch_bounds__(64 * PairGeo<D>::NW) void decode_pair_kernel(DecodeArgs a) {
+  constexpr int NW = PairGeo<D>::NW;
+  constexpr bool COMPACT = MODE != kModeDmaGeneral;
+  using SG = StageGeo<D, COMPACT>;
+  constexpr int NS = DecodeStages<D>::NS;
+  extern __shared__ __align__(16) char smem[];
+  float* s_ml = reinterpret_cast<float*>(smem);                     // [NW waves][16 cols][2]
+  uint8_t* rings = reinterpret_cast<uint8_t*>(s_ml + NW * 16 * 2);  // per-wave stream area
+  float* s_o = reinterpret_cast<float*>(rings);                     // [NW][kMergeCols][D], after the streams
+
+  const float ksc = __builtin_bit_cast(
+      float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(reinterpret_cast<const uint8_t*>(a.k_scale), 4), 0, 0, 0));
+  const float vsc = __builtin_bit_cast(
+      float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(reinterpret_cast<const uint8_t*>(a.v_scale), 4), 0, 0, 0));
+  const int hkv = a.pool.hkv;
+  const int b = blockIdx.x / hkv;
+  const int h = blockIdx.x - b * hkv;
+  const int L = clamp_len(ld_uniform(a.seq_lens, b), a.max_blocks * a.pool.bs);
+  const float qk_factor = a.sm_scale * uniform_f32(ksc) * kLog2e;
+  const float gv = uniform_f32(vsc);
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int i = lane & 15, j = lane >> 4;
+  const int grp = a.grp;
+  const DmaOffsets<D, COMPACT> dof = dma_offsets<D, COMPACT>(a.pool.st, a.pool.skv, lane);
+  uint8_t* ring = rings + w * NS * SG::STAGE;
+  const LdsLane ll = lds_lane<D>(i, j);
+  WaveAttn<D, 1> W;
+  W.init();
+  const bool valid = i < grp;
+  const uint16_t* qrow = valid ? a.q + (int64_t)b * a.q_st + (int64_t)(h * grp + i) * a.q_sh : nullptr;
+  W.lim[0] = valid ? L - 1 : -1;
+  decode_stream<D, COMPACT, NS, NW>(W, ring, a.pool, a.bt + (int64_t)b * a.max_blocks, L, h, w, ceil_div(L, kStep),
+                                    qrow, qk_factor, dof, ll, j);
+  __syncthreads();  // every wave's ring is drained before the rings become the merge buffer
+  merge_waves<D, NW>(W, s_ml, s_o, grp, w, i, j, [&](int col, int d, float on, float, float) {
+    const float y = on * gv;
+    a.out[((int64_t)b * a.hq + h * grp + col) * D + d] = (uint16_t)(pack_bf16x2(y, 0.0f) & 0xFFFFu);
+  });
 }
 
 // Workspace: [arrival counters][partial outputs][partial (max, sum)]. The
@@ -465,14 +551,29 @@ static int resident_workgroups(size_t lds) {
   return n;
 }
 
+static int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cached[dev] > 0) return cached[dev];
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+  cached[dev] = cus;
+  return cus;
+}
+
 template <int D, int MODE>
 static hipError_t launch_decode_v(DecodeArgs a, int max_seq_len, hipStream_t stream) {
   const int hkv = a.pool.hkv;
-  const size_t lds = decode_lds_bytes_m<D, MODE>(a.B);
-  a.target = resident_workgroups<D, MODE>(lds);
   const int64_t cap = (int64_t)a.max_blocks * a.pool.bs;
   const int64_t lens = max_seq_len > 0 ? (max_seq_len < cap ? max_seq_len : cap) : cap;
   const int64_t steps = (lens + kStep - 1) / kStep;
+  if ((int64_t)a.B * hkv >= device_cus() && steps <= (int64_t)PairGeo<D>::NW * PairGeo<D>::kMaxStepsPerWave) {
+    decode_pair_kernel<D, MODE><<<a.B * hkv, 64 * PairGeo<D>::NW, PairLds<D, MODE>::bytes, stream>>>(a);
+    return hipGetLastError();
+  }
+  const size_t lds = decode_lds_bytes_m<D, MODE>(a.B);
+  a.target = resident_workgroups<D, MODE>(lds);
   // an upper bound of the units the schedule can produce for this batch
   int64_t want = (int64_t)a.B * hkv * ((steps + kDecodeMinTps - 1) / kDecodeMinTps);
   want = want < (int64_t)a.B * hkv ? (int64_t)a.B * hkv : want;

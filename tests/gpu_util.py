@@ -55,14 +55,18 @@ class Dev:
     def pool_logical(self) -> np.ndarray:
         return self.pool.contiguous().cpu().numpy()
 
-    def decode(self, q=None):
+    def decode(self, q=None, max_seq_len=None, ws=None):
+        """Decode over the whole batch. max_seq_len defaults to the longest
+        sequence (0 lets the library bound lengths by the block table)."""
         w = self.w
         q = self.query if q is None else q
         out = torch.empty((w.num_seqs, w.num_q_heads, w.head_size), dtype=torch.bfloat16, device=q.device)
-        ws = torch.zeros(nvk.decode_workspace_size(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_size),
-                         dtype=torch.uint8, device=q.device)
-        nvk.paged_attention_decode(self.pool, q, self.bt, self.seq_lens, int(w.seq_lens.max(initial=0)),
-                                   self.k_scale, self.v_scale, self.sm_scale, out, ws)
+        if ws is None:
+            ws = torch.zeros(nvk.decode_workspace_size(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_size),
+                             dtype=torch.uint8, device=q.device)
+        msl = int(w.seq_lens.max(initial=0)) if max_seq_len is None else max_seq_len
+        nvk.paged_attention_decode(self.pool, q, self.bt, self.seq_lens, msl, self.k_scale, self.v_scale,
+                                   self.sm_scale, out, ws)
         return out
 
     def prefill(self, causal=True):

@@ -7,6 +7,7 @@ import numpy as np
 import pytest
 import torch
 
+import bit_quantized_paged_amd as nvk
 from oracle import nvfp4_oracle as O
 from workloads import make_config, make_workload
 from gpu_util import Dev, assert_attn_close, bf16_to_np, oracle_pool
@@ -364,3 +365,66 @@ def test_prefill_graph_replays_match_eager():
         step(0)
         torch.cuda.synchronize()
         assert torch.equal(outs[0], eager)
+
+
+def _decode_batch(seed, lens, hq, hkv, D, bs):
+    """A decode batch with one query row per sequence, empty sequences included."""
+    import dataclasses
+    lens = np.asarray(lens, np.int32)
+    w = make_workload(seed=seed, name="pairs", seq_lens=lens, q_lens=np.minimum(lens, 1), num_q_heads=hq,
+                      num_kv_heads=hkv, head_size=D, block_size=bs)
+    qall = make_workload(seed=seed + 1, name="q", seq_lens=np.ones(len(lens), np.int32),
+                         q_lens=np.ones(len(lens), np.int32), num_q_heads=hq, num_kv_heads=hkv, head_size=D,
+                         block_size=bs).query
+    return dataclasses.replace(w, query=qall, q_lens=np.ones(len(lens), np.int32),
+                               cu_q=np.arange(len(lens) + 1, dtype=np.int32))
+
+
+# Batches with at least one (sequence, kv head) pair per CU and short sequences,
+# which the library runs without split-K (one workgroup per pair); the longest
+# length is the most that path takes (8 steps of 32 keys for each of its 12
+# waves, 8 at head size 256).
+PAIR_CASES = {
+    "d128_gqa2_bs16": (128, 16, 8, 16, 32, 3072),
+    "d64_gqa4_bs32": (64, 16, 4, 32, 64, 3072),
+    "d256_gqa8_bs16": (256, 16, 2, 16, 128, 2048),
+    "d128_mha_bs16": (128, 8, 8, 16, 32, 1500),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PAIR_CASES))
+@pytest.mark.parametrize("layout", ["HND", "NHD"])
+def test_decode_without_split_parity(name, layout):
+    """Many short sequences: the one-workgroup-per-pair path matches the oracle,
+    leaves the workspace untouched, is deterministic, and agrees with the
+    split-K path on the same batch within the attention tolerance."""
+    import dataclasses
+    D, hq, hkv, bs, B, lmax = PAIR_CASES[name]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert B * hkv >= cus, "the case must give every CU a pair"
+    rng = np.random.default_rng(41)
+    lens = rng.integers(1, lmax + 1, size=B)
+    lens[:8] = [0, 1, 31, 32, 33, bs - 1, bs + 1, lmax]
+    w = _decode_batch(51, lens, hq, hkv, D, bs)
+    d = Dev(w, layout)
+    d.append_all()
+    sentinel = 0xA7
+    ws = torch.full((nvk.decode_workspace_size(w.num_seqs, hq, hkv, D),), sentinel, dtype=torch.uint8,
+                    device="cuda")
+    out = d.decode(ws=ws)
+    again = d.decode(ws=ws)
+    torch.cuda.synchronize()
+    assert bool(torch.all(ws == sentinel)), "the per-pair path touched the workspace"
+    assert torch.equal(out, again)
+    assert torch.all(out[0] == 0)
+    ref = O.paged_attention(oracle_pool(w), w.query, w.cu_q, w.block_table, w.seq_lens, w.k_scale, w.v_scale,
+                            np.float32(d.sm_scale), D)
+    assert_attn_close(out, ref, f"{name}/{layout} decode without split")
+    # the same batch through split-K: a block table wide enough that the
+    # length bound taken from it exceeds what the per-pair path takes
+    extra = (lmax * 4) // bs
+    wide = np.pad(w.block_table, ((0, 0), (0, extra)), constant_values=0)
+    d.bt = torch.from_numpy(np.ascontiguousarray(wide, dtype=np.int32)).cuda()
+    out_split = d.decode(max_seq_len=0)
+    torch.cuda.synchronize()
+    assert_attn_close(out_split, ref, f"{name}/{layout} decode with split-K")
