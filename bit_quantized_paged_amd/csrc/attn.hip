@@ -281,7 +281,7 @@ template <int D, int NWS, typename Emit>
 __device__ __forceinline__ void merge_waves(const WaveAttn<D, 1>& W, float* s_ml, float* s_o, int grp, int w, int i,
                                             int j, Emit&& emit) {
   using G = Geo<D>;
-  const float lsum = wave_sum_j(W.l[0]);
+  const float lsum = W.lsum(0);
   if (j == 0) {
     s_ml[(w * 16 + i) * 2] = W.m[0];
     s_ml[(w * 16 + i) * 2 + 1] = lsum;
@@ -670,8 +670,17 @@ struct PrefillStages {
   static constexpr int NS = (63 / NC + 1) < 4 ? (63 / NC + 1) : 4;
 };
 
+// Waves per SIMD the prefill register budget is sized for: without the hint
+// the compiler spends the whole 256-register budget of two waves (or more)
+// at head sizes 64 and 128; at 256 two waves would spill.
+template <int D>
+struct PrefillOcc {
+  static constexpr int waves = (D == 256) ? 1 : 2;
+};
+
 template <int D, int NT, bool COMPACT>
-__global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PrefillOcc<D>::waves))) void prefill_kernel(
+    PrefillArgs a) {
   using G = Geo<D>;
   using SG = StageGeo<D, COMPACT>;
   using OG = OpGeo<D>;
@@ -778,7 +787,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   const float gv = *a.v_scale;
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
-    const float lt = wave_sum_j(W.l[n]);
+    const float lt = W.lsum(n);
     const int c = col_base + 16 * n + i;
     if (c < ncols) {
       const int tok = c / grp, g = c - (c / grp) * grp;

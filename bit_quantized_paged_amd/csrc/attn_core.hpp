@@ -127,9 +127,9 @@ __device__ __forceinline__ void make_pairs(const SubRaw<D>& R, VPairs<D>& P) {
       P.od[p][w] = ((a >> 4) & 0x0F0F0F0Fu) | (b & 0xF0F0F0F0u);
     }
   }
-  const uint32_t sw = R.vs[0] | (R.vs[1] << 8) | (R.vs[2] << 16) | (R.vs[3] << 24);
-  P.s[0] = fp8x2_to_h2<false>(sw);
-  P.s[1] = fp8x2_to_h2<true>(sw);
+  // (vs0, vs1) and (vs2, vs3) side by side in the low bytes: one permute each
+  P.s[0] = fp8x2_to_h2<false>(__builtin_amdgcn_perm(R.vs[1], R.vs[0], 0x0C0C0400u));
+  P.s[1] = fp8x2_to_h2<false>(__builtin_amdgcn_perm(R.vs[3], R.vs[2], 0x0C0C0400u));
 }
 
 template <int D, int T>
@@ -156,17 +156,24 @@ template <int D, int NT>
 struct WaveAttn {
   using G = Geo<D>;
   h8 q[NT][G::KW];       // B operand of S^T, per column tile and chunk
-  float sf[NT];          // per-column factor: sm_scale * g_K * log2(e) / qscale
+  float sf[NT];          // per-column factor |sm_scale * g_K| * log2(e) / qscale (> 0)
   int lim[NT];           // last visible key of the column (-1: none)
   f4 acc[NT][G::DPL];    // O^T accumulators
   float m[NT];           // running max (base-2 scores)
-  float l[NT];           // this lane's share of the running sum
+  // Running sums. With one column tile (decode) they come from the matrix
+  // unit: a ones tile times P^T (every entry = the lane's column sum). With
+  // several (prefill) the four extra accumulators per tile would cost
+  // occupancy, so each lane sums its own probabilities on the vector unit.
+  static constexpr bool kMfmaSum = (NT == 1);
+  f4 lacc[NT];           // kMfmaSum
+  float l[NT];           // otherwise: this lane's share of the running sum
 
   __device__ __forceinline__ void init() {
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
       m[n] = -__builtin_inff();
-      l[n] = 0.0f;
+      if constexpr (kMfmaSum) lacc[n] = f4{0.f, 0.f, 0.f, 0.f};
+      else l[n] = 0.0f;
 #pragma unroll
       for (int t = 0; t < G::DPL; ++t) acc[n][t] = f4{0.f, 0.f, 0.f, 0.f};
     }
@@ -177,7 +184,10 @@ struct WaveAttn {
   // the column's D bf16 values (qrow nullptr: padding column), set_q turns
   // them into column tile n. The row is scaled by a power of two so that its
   // largest magnitude lies in [1, 2) before the exact-range f16 conversion;
-  // the inverse goes into sf.
+  // the inverse goes into sf. The softmax folds sf into its max and exp2
+  // argument, which needs sf > 0: a negative factor's sign moves into the
+  // query (exact), and a zero one becomes the smallest normal float (every
+  // logit is then 0 to within 2^-100, as it should be).
   struct QRaw {
     uint32_t w[D / 8];
   };
@@ -211,14 +221,15 @@ struct WaveAttn {
     amax = wave_max_j(amax);
     int e = (int)((__float_as_uint(amax) >> 23) & 0xFFu) - 127;
     e = (amax == 0.0f) ? 0 : (e < -120 ? -120 : e);
-    sf[n] = __builtin_ldexpf(base_factor, e);
+    const float sgn = base_factor < 0.0f ? -1.0f : 1.0f;
+    sf[n] = __builtin_fmaxf(__builtin_ldexpf(base_factor * sgn, e), 1.17549435e-38f);
 #pragma unroll
     for (int c = 0; c < G::KW; ++c) {
       h8 v;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        v[2 * t] = (_Float16)__builtin_ldexpf(bf16_lo(r.w[4 * c + t]), -e);
-        v[2 * t + 1] = (_Float16)__builtin_ldexpf(bf16_hi(r.w[4 * c + t]), -e);
+        v[2 * t] = (_Float16)(__builtin_ldexpf(bf16_lo(r.w[4 * c + t]), -e) * sgn);
+        v[2 * t + 1] = (_Float16)(__builtin_ldexpf(bf16_hi(r.w[4 * c + t]), -e) * sgn);
       }
       q[n][c] = v;
     }
@@ -270,10 +281,26 @@ struct WaveAttn {
     for (int t = 0; t < G::DPL; ++t)
 #pragma unroll
       for (int n = 0; n < NT; ++n) acc[n][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[t], p[n], acc[n][t], 0, 0, 0);
+    if constexpr (kMfmaSum) sum_ops(p);
+  }
+  // Column sums of P^T (the exact f16 values the PV product uses) on the
+  // matrix unit: a ones tile times P^T, accumulated in fp32.
+  __device__ __forceinline__ void sum_ops(const h8 (&p)[NT]) {
+    const _Float16 o = (_Float16)1.0f;
+    const h8 ones = {o, o, o, o, o, o, o, o};
+#pragma unroll
+    for (int n = 0; n < NT; ++n) lacc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, p[n], lacc[n], 0, 0, 0);
+  }
+  // The running sum of column tile n for this lane's column (the same value
+  // in the four lanes of the column).
+  __device__ __forceinline__ float lsum(int n) const {
+    if constexpr (kMfmaSum) return lacc[n][0];
+    else return wave_sum_j(l[n]);
   }
 
   // Online softmax of a step's scores (base 2, lazy rescale) into the f16
-  // probabilities p of each column tile.
+  // probabilities p of each column tile. The scale sf (> 0) is applied once
+  // to the raw max and inside each exp2 argument (one fma per score).
   __device__ __forceinline__ void softmax(const f4 (&s)[2][NT], int kb, int j, bool masked, h8 (&p)[NT]) {
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
@@ -281,7 +308,7 @@ struct WaveAttn {
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) x[4 * sb + r] = s[sb][n][r] * sf[n];
+        for (int r = 0; r < 4; ++r) x[4 * sb + r] = s[sb][n][r];
       }
       if (masked) {
 #pragma unroll
@@ -290,34 +317,36 @@ struct WaveAttn {
           x[k] = (key <= lim[n]) ? x[k] : -__builtin_inff();
         }
       }
-      float mx = x[0];
+      float rmx = x[0];
 #pragma unroll
-      for (int k = 1; k < 8; ++k) mx = __builtin_fmaxf(mx, x[k]);
-      mx = wave_max_j(mx);
+      for (int k = 1; k < 8; ++k) rmx = __builtin_fmaxf(rmx, x[k]);
+      rmx = wave_max_j(rmx);
+      const float mx = (rmx == -__builtin_inff()) ? rmx : rmx * sf[n];
       const bool grow = mx > m[n] + kLazyMax;
       if (__builtin_amdgcn_ballot_w64(grow) != 0) {
         const float mnew = grow ? mx : m[n];
         const float alpha = grow ? __builtin_amdgcn_exp2f(m[n] - mnew) : 1.0f;  // exp2(-inf) = 0
-        l[n] *= alpha;
+        if constexpr (kMfmaSum) lacc[n] *= alpha;
+        else l[n] *= alpha;
 #pragma unroll
         for (int t = 0; t < G::DPL; ++t) acc[n][t] *= alpha;
         m[n] = mnew;
       }
-      const float mu = (m[n] == -__builtin_inff()) ? 0.0f : m[n];
-      // probabilities go to f16 in pairs; the running sum adds exactly the
-      // f16 values the PV product uses (dot with (1, 1)), so constant values
-      // come back unchanged
+      const float nmu = (m[n] == -__builtin_inff()) ? 0.0f : -m[n];
+      // the sum adds exactly the f16 values the PV product uses (dot with
+      // (1, 1)), so constant values come back unchanged
       const h2 one = {(_Float16)1.0f, (_Float16)1.0f};
-      float ps = l[n];
+      float ps = kMfmaSum ? 0.0f : l[n];
 #pragma unroll
       for (int k = 0; k < 8; k += 2) {
         const h2 e = __builtin_bit_cast(
-            h2, __builtin_amdgcn_cvt_pkrtz(__builtin_amdgcn_exp2f(x[k] - mu), __builtin_amdgcn_exp2f(x[k + 1] - mu)));
-        ps = __builtin_amdgcn_fdot2(e, one, ps, false);
+            h2, __builtin_amdgcn_cvt_pkrtz(__builtin_amdgcn_exp2f(__builtin_fmaf(x[k], sf[n], nmu)),
+                                           __builtin_amdgcn_exp2f(__builtin_fmaf(x[k + 1], sf[n], nmu))));
+        if constexpr (!kMfmaSum) ps = __builtin_amdgcn_fdot2(e, one, ps, false);
         p[n][k] = e[0];
         p[n][k + 1] = e[1];
       }
-      l[n] = ps;
+      if constexpr (!kMfmaSum) l[n] = ps;
     }
   }
 
@@ -333,6 +362,7 @@ struct WaveAttn {
 
   template <int T>
   __device__ __forceinline__ void pv(const VPairs<D> (&vp)[2], const h8 (&p)[NT]) {
+    if constexpr (T == 0 && kMfmaSum) sum_ops(p);
     if constexpr (T < G::DPL) {
       const h4 a0 = v_operand<D, T>(vp[0]);
       const h4 a1 = v_operand<D, T>(vp[1]);
