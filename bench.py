@@ -57,10 +57,10 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload: str):
+def read_traffic(kernel: str, workload: str):
     """HBM bytes per decode launch from the committed counter summary, if it
     was taken on the current kernel sources (else None)."""
-    path = os.path.join(ROOT, "profiles", f"decode_split_kernel_{workload}_traffic.md")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.md")
     if not os.path.exists(path):
         return None
     rec = {}
@@ -182,19 +182,28 @@ def main():
         torch.cuda.current_stream().wait_stream(cap_stream)
         return g
 
-    def time_graph(g):
-        g.replay()  # warm replay
+    def time_graph(g, reps=1):
+        """Seconds for one replay of g (K steps): the median of `reps` timed
+        replays on the current stream, after untimed warm replays (the first
+        replays on a fresh GPU run slower while its clocks ramp up)."""
+        for _ in range(3):
+            g.replay()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         stream = torch.cuda.current_stream()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        e0.record(stream)
-        g.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        return e0.elapsed_time(e1) / 1e3, wall
+        gpu, wall = [], []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            wall.append(time.perf_counter() - t0)
+            gpu.append(e0.elapsed_time(e1) / 1e3)
+        order = sorted(range(reps), key=lambda r: gpu[r])
+        mid = order[reps // 2]
+        return gpu[mid], wall[mid]
 
     g_step = capture(step)
     step_gpu_s, step_wall_s = time_graph(g_step)
@@ -204,16 +213,16 @@ def main():
         assert torch.equal(outp, ref_p), "graph replay of the step differs from the eager prefill"
     res = {}
     g_app = capture(do_append)
-    res["append_s"], _ = time_graph(g_app)
+    res["append_s"], _ = time_graph(g_app, reps=3)
     del g_app
     if wd is not None:
         g_dec = capture(do_decode)
-        res["decode_s"], _ = time_graph(g_dec)
+        res["decode_s"], _ = time_graph(g_dec, reps=3)
         assert torch.equal(outd, ref_d), "graph replay of decode differs from eager"
         del g_dec
     if wp is not None:
         g_pre = capture(do_prefill)
-        res["prefill_s"], _ = time_graph(g_pre)
+        res["prefill_s"], _ = time_graph(g_pre, reps=3)
         del g_pre
 
     # ---- paged dequantize of the decode batch (reported, not part of the step)
@@ -227,7 +236,7 @@ def main():
         ov = torch.empty_like(ok)
         do_deq = lambda r: nvk.dequant_paged(pools[r], btd, sld, cud, maxd, k_scale, v_scale, ok, ov)
         g_deq = capture(do_deq)
-        deq_s, _ = time_graph(g_deq)
+        deq_s, _ = time_graph(g_deq, reps=3)
         del g_deq
         deq_bytes = rows * Hkv * 2 * (fd + 2 * D) + 4 * int(np.sum((wd.seq_lens + bs - 1) // bs))
         deq = {"gbs": round(deq_bytes / (deq_s / K) / 1e9, 1), "us": round(deq_s / K * 1e6, 2)}
@@ -251,9 +260,11 @@ def main():
         out["value"] = round(gbs, 1)
         extra.update({"decode_us": round(dec_s * 1e6, 2), "decode_pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
                       "decode_bytes": dec_bytes})
-        traffic = read_traffic(args.workload)
+        plan = nvk.decode_plan(wd.num_seqs, Hkv, D, bs, int(wd.block_table.shape[1]), maxd)
+        dec_kernel = "decode_pair_kernel" if plan == nvk.DECODE_PER_PAIR else "decode_split_kernel"
+        traffic = read_traffic(dec_kernel, args.workload)
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": "decode_split_kernel",
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": dec_kernel,
                 "bytes_per_launch": dec_bytes, "avg_launch_us": round(dec_s * 1e6, 3)}
     if wp is not None:
         pairs = 0

@@ -23,7 +23,8 @@ LIB_PATH = os.path.join(_HERE, "libnvfp4kv.so")
 
 EXPORTS = [
     "nvfp4_kv_full_dim", "nvfp4_kv_append", "nvfp4_kv_dequant_paged",
-    "nvfp4_paged_attention_decode_workspace_size", "nvfp4_paged_attention_decode",
+    "nvfp4_paged_attention_decode_workspace_size", "nvfp4_paged_attention_decode_plan",
+    "nvfp4_paged_attention_decode",
     "nvfp4_paged_attention_prefill", "nvfp4kv_status_string", "nvfp4kv_last_error",
 ]
 
@@ -60,6 +61,7 @@ def library():
             "nvfp4_kv_append": (_I32, [_DESC, _P, _I64, _I64, _P, _I64, _I64, _P, _I64, _P, _P, _P]),
             "nvfp4_kv_dequant_paged": (_I32, [_DESC, _P, _I32, _P, _P, _I32, _I32, _P, _P, _P, _P, _I64, _P]),
             "nvfp4_paged_attention_decode_workspace_size": (_SZ, [_I32, _I32, _I32, _I32]),
+            "nvfp4_paged_attention_decode_plan": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32]),
             "nvfp4_paged_attention_decode": (_I32, [_DESC, _P, _I64, _I64, _I32, _P, _I32, _P, _I32, _I32, _P, _P,
                                                     _F32, _P, _P, _SZ, _P]),
             "nvfp4_paged_attention_prefill": (_I32, [_DESC, _P, _I64, _I64, _I32, _P, _I32, _I32, _P, _I32, _P, _I32,
@@ -164,6 +166,17 @@ def dequant_paged(pool, block_table, seq_lens, cu_seqlens_out, max_seq_len, k_sc
 def decode_workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_size: int) -> int:
     return int(library().nvfp4_paged_attention_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads,
                                                                       head_size))
+
+
+DECODE_SPLIT_K, DECODE_PER_PAIR = 0, 1
+
+
+def decode_plan(num_seqs: int, num_kv_heads: int, head_size: int, block_size: int, max_blocks_per_seq: int,
+                max_seq_len: int) -> int:
+    """Which decode kernel a call with these sizes launches on the current
+    device: DECODE_PER_PAIR, DECODE_SPLIT_K, or -1 for an unsupported head size."""
+    return int(library().nvfp4_paged_attention_decode_plan(num_seqs, num_kv_heads, head_size, block_size,
+                                                            max_blocks_per_seq, max_seq_len))
 
 
 def paged_attention_decode(pool, q, block_table, seq_lens, max_seq_len, k_scale, v_scale, sm_scale,

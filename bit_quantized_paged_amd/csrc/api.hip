@@ -144,6 +144,12 @@ size_t nvfp4_paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num
   return nvfp4kv::decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_size);
 }
 
+int32_t nvfp4_paged_attention_decode_plan(int32_t num_seqs, int32_t num_kv_heads, int32_t head_size,
+                                          int32_t block_size, int32_t max_blocks_per_seq, int32_t max_seq_len) {
+  if (num_seqs < 0 || num_kv_heads < 1 || block_size < 1 || max_blocks_per_seq < 1) return -1;
+  return nvfp4kv::decode_plan(num_seqs, num_kv_heads, head_size, block_size, max_blocks_per_seq, max_seq_len);
+}
+
 nvfp4kv_status nvfp4_paged_attention_decode(const nvfp4kv_cache* cache, const void* q, int64_t q_stride_token,
                                             int64_t q_stride_head, int32_t num_q_heads,
                                             const int32_t* block_table, int32_t max_blocks_per_seq,

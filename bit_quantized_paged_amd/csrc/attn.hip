@@ -562,13 +562,36 @@ static int device_cus() {
   return cus;
 }
 
+// 32-key steps of the longest sequence, as far as the host knows it.
+static int64_t host_max_steps(int max_blocks, int bs, int max_seq_len) {
+  const int64_t cap = (int64_t)max_blocks * bs;
+  const int64_t lens = max_seq_len > 0 ? (max_seq_len < cap ? max_seq_len : cap) : cap;
+  return (lens + kStep - 1) / kStep;
+}
+
+// The per-pair kernel when the batch alone gives every CU a (sequence, kv
+// head) pair and no sequence needs more than kMaxStepsPerWave steps per wave.
+template <int D>
+static bool use_pair_kernel(int num_seqs, int hkv, int64_t max_steps) {
+  return (int64_t)num_seqs * hkv >= device_cus() &&
+         max_steps <= (int64_t)PairGeo<D>::NW * PairGeo<D>::kMaxStepsPerWave;
+}
+
+int decode_plan(int num_seqs, int num_kv_heads, int head_size, int block_size, int max_blocks, int max_seq_len) {
+  const int64_t steps = host_max_steps(max_blocks, block_size, max_seq_len);
+  switch (head_size) {
+    case 64: return use_pair_kernel<64>(num_seqs, num_kv_heads, steps) ? 1 : 0;
+    case 128: return use_pair_kernel<128>(num_seqs, num_kv_heads, steps) ? 1 : 0;
+    case 256: return use_pair_kernel<256>(num_seqs, num_kv_heads, steps) ? 1 : 0;
+    default: return -1;
+  }
+}
+
 template <int D, int MODE>
 static hipError_t launch_decode_v(DecodeArgs a, int max_seq_len, hipStream_t stream) {
   const int hkv = a.pool.hkv;
-  const int64_t cap = (int64_t)a.max_blocks * a.pool.bs;
-  const int64_t lens = max_seq_len > 0 ? (max_seq_len < cap ? max_seq_len : cap) : cap;
-  const int64_t steps = (lens + kStep - 1) / kStep;
-  if ((int64_t)a.B * hkv >= device_cus() && steps <= (int64_t)PairGeo<D>::NW * PairGeo<D>::kMaxStepsPerWave) {
+  const int64_t steps = host_max_steps(a.max_blocks, a.pool.bs, max_seq_len);
+  if (use_pair_kernel<D>(a.B, hkv, steps)) {
     decode_pair_kernel<D, MODE><<<a.B * hkv, 64 * PairGeo<D>::NW, PairLds<D, MODE>::bytes, stream>>>(a);
     return hipGetLastError();
   }

@@ -29,6 +29,10 @@ hipError_t launch_decode(const Pool& pool, int head_size, const void* q, int64_t
                          const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len, const float* k_scale,
                          const float* v_scale, float sm_scale, void* out, void* workspace, hipStream_t stream);
 
+// Decode kernel a call with these sizes launches on the current device:
+// 1 = one workgroup per (sequence, kv head), 0 = split-K, -1 = bad head size.
+int decode_plan(int num_seqs, int num_kv_heads, int head_size, int block_size, int max_blocks, int max_seq_len);
+
 // Dynamic LDS bytes of the decode split kernel (must stay within 160 KiB).
 size_t decode_lds_bytes(int num_seqs, int grp, int head_size);
 

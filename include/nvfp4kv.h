@@ -130,6 +130,27 @@ size_t nvfp4_paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num
                                                    int32_t num_kv_heads, int32_t head_size);
 
 /*
+ * Which decode kernel nvfp4_paged_attention_decode launches for a batch of
+ * these sizes on the current device (arguments as in that call):
+ *   NVFP4KV_DECODE_PER_PAIR (1): one workgroup per (sequence, kv head) whose
+ *     waves share the sequence's keys; no split-K, the workspace is not
+ *     touched. Chosen when num_seqs * num_kv_heads is at least the device's
+ *     compute-unit count and the longest sequence (max_seq_len, or
+ *     max_blocks_per_seq * block_size when max_seq_len <= 0) needs at most 8
+ *     steps of 32 keys per wave (12 waves per workgroup, 8 at head_size 256).
+ *   NVFP4KV_DECODE_SPLIT_K (0): every other batch; sequences are cut into
+ *     units of about equal size, one per resident workgroup, and the last
+ *     unit of a (sequence, kv head) to finish merges the others' partials.
+ * Returns -1 for a head_size the library does not build. Both kernels give
+ * results within the same tolerance of the exact attention; bits may differ
+ * between them.
+ */
+#define NVFP4KV_DECODE_SPLIT_K 0
+#define NVFP4KV_DECODE_PER_PAIR 1
+int32_t nvfp4_paged_attention_decode_plan(int32_t num_seqs, int32_t num_kv_heads, int32_t head_size,
+                                          int32_t block_size, int32_t max_blocks_per_seq, int32_t max_seq_len);
+
+/*
  * Decode attention over the quantised pages [P40177 "Implementation
  * breakdown" 1 and 3; RFC47684 "Cause analysis": the paged read path].
  *
@@ -143,9 +164,9 @@ size_t nvfp4_paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num
  *   of 8), last axis contiguous, 16-byte aligned. out: bf16 [num_seqs,
  *   num_q_heads, head_size] contiguous. A sequence with no key yields zeros.
  * num_q_heads / num_kv_heads must be an integer in [1, 16]; num_seqs <= 4096.
- * max_seq_len: host upper bound of seq_lens, used only to size the grid (a
- * wrong value costs speed, not correctness); lengths are clamped to
- * max_blocks_per_seq * block_size on the device.
+ * max_seq_len: host upper bound of seq_lens, used only to pick the kernel
+ * and size the grid (a wrong value costs speed, not correctness); lengths
+ * are clamped to max_blocks_per_seq * block_size on the device.
  * The result is deterministic: the same inputs give the same bits.
  * workspace: device scratch of at least
  *   nvfp4_paged_attention_decode_workspace_size(...) bytes, 16-byte aligned,

@@ -110,3 +110,13 @@ def test_prefill_and_dequant_validation():
     assert r == 1
     r = lib.nvfp4_kv_dequant_paged(ctypes.byref(d), 64, 4, 96, 128, 70000, 64, 32, 48, 4096, 8192, 10, None)
     assert r == 1
+
+
+def test_decode_plan_rejects_bad_sizes():
+    """The plan query validates its sizes on the host (no device needed for
+    these paths)."""
+    assert nvk.decode_plan(4, 2, 96, 16, 8, 100) == -1   # head size not built
+    assert nvk.decode_plan(4, 0, 128, 16, 8, 100) == -1  # no kv heads
+    assert nvk.decode_plan(-1, 2, 128, 16, 8, 100) == -1
+    assert nvk.decode_plan(4, 2, 128, 0, 8, 100) == -1
+    assert nvk.decode_plan(4, 2, 128, 16, 0, 100) == -1

@@ -406,6 +406,8 @@ def test_decode_without_split_parity(name, layout):
     lens = rng.integers(1, lmax + 1, size=B)
     lens[:8] = [0, 1, 31, 32, 33, bs - 1, bs + 1, lmax]
     w = _decode_batch(51, lens, hq, hkv, D, bs)
+    mb = w.block_table.shape[1]
+    assert nvk.decode_plan(B, hkv, D, bs, mb, int(lens.max())) == nvk.DECODE_PER_PAIR
     d = Dev(w, layout)
     d.append_all()
     sentinel = 0xA7
@@ -424,6 +426,7 @@ def test_decode_without_split_parity(name, layout):
     # length bound taken from it exceeds what the per-pair path takes
     extra = (lmax * 4) // bs
     wide = np.pad(w.block_table, ((0, 0), (0, extra)), constant_values=0)
+    assert nvk.decode_plan(B, hkv, D, bs, wide.shape[1], 0) == nvk.DECODE_SPLIT_K
     d.bt = torch.from_numpy(np.ascontiguousarray(wide, dtype=np.int32)).cuda()
     out_split = d.decode(max_seq_len=0)
     torch.cuda.synchronize()
