@@ -49,7 +49,8 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
-// Block-wide exclusive scan (256 threads); also returns the total.
+// Block-wide exclusive scan (NW waves); also returns the total.
+template <int NW>
 __device__ __forceinline__ int block_excl_scan(int v, int* s_red, int& total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int incl = wave_incl_scan(v);
@@ -58,7 +59,7 @@ __device__ __forceinline__ int block_excl_scan(int v, int* s_red, int& total) {
   int off = 0;
   total = 0;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
+  for (int k = 0; k < NW; ++k) {
     const int t = s_red[k];
     off += (k < w) ? t : 0;
     total += t;
@@ -68,9 +69,10 @@ __device__ __forceinline__ int block_excl_scan(int v, int* s_red, int& total) {
 }
 
 // s_pref[b] = first unit (per head) of sequence b, s_pref[B] = units per head.
+template <int NW>
 __device__ void decode_schedule(const int32_t* __restrict__ seq_lens, int B, int cap, int hkv, int target,
                                 int* s_pref, int* s_len, int* s_red, int& tps, int& total_units) {
-  const int per = ceil_div(B, 256);
+  const int per = ceil_div(B, 64 * NW);
   const int b0 = threadIdx.x * per;
   const int b1 = (b0 + per < B) ? b0 + per : B;
   int steps_local = 0;
@@ -82,7 +84,7 @@ __device__ void decode_schedule(const int32_t* __restrict__ seq_lens, int B, int
     steps_local += s;
   }
   int total_steps;
-  (void)block_excl_scan(steps_local, s_red, total_steps);
+  (void)block_excl_scan<NW>(steps_local, s_red, total_steps);
   const int64_t work = (int64_t)total_steps * hkv;
   int t = (int)((work + target - 1) / target);
   tps = t < kDecodeMinTps ? kDecodeMinTps : t;
@@ -90,7 +92,7 @@ __device__ void decode_schedule(const int32_t* __restrict__ seq_lens, int B, int
   // a sequence without keys still gets one (empty) unit, which writes zeros
   for (int b = b0; b < b1; ++b) units_local += max(1, ceil_div(s_pref[b], tps));
   int total;
-  int run = block_excl_scan(units_local, s_red, total);
+  int run = block_excl_scan<NW>(units_local, s_red, total);
   for (int b = b0; b < b1; ++b) {
     const int n = max(1, ceil_div(s_pref[b], tps));
     s_pref[b] = run;
@@ -150,14 +152,14 @@ __device__ __forceinline__ f4 ld_agent4(const float* base, uint32_t off) {
 // One wave per column finds the max and the per-split weights (lanes over
 // splits); then every thread owns 4 consecutive outputs and sums its splits
 // with 16-byte loads, several in flight.
-template <int D>
+template <int D, int NW>
 __device__ void combine_splits(const DecodeArgs& a, int b, int h, int64_t slot0, int n, float* s_w, int cap) {
   const int hkv = a.pool.hkv;
   const int grp = a.grp;
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int nw = (cap - 32) / grp;  // splits whose weights fit in LDS
-  for (int col = w; col < grp; col += 4) {
+  for (int col = w; col < grp; col += NW) {
     float mloc = -__builtin_inff();
     for (int s = lane; s < n; s += 64) mloc = __builtin_fmaxf(mloc, ld_agent(a.ws_ml + ((slot0 + (int64_t)s * hkv) * grp + col) * 2));
     const float M = wave_max64(mloc);
@@ -179,7 +181,7 @@ __device__ void combine_splits(const DecodeArgs& a, int b, int h, int64_t slot0,
   const float gv = *a.v_scale;
   uint16_t* out = a.out + ((int64_t)b * a.hq + h * grp) * D;
   constexpr int D4 = D / 4;
-  for (int e = threadIdx.x; e < grp * D4; e += 256) {
+  for (int e = threadIdx.x; e < grp * D4; e += 64 * NW) {
     const int col = e / D4;
     const int d4 = e - col * D4;
     const float M = s_w[2 * col];
@@ -225,11 +227,18 @@ struct DecodeStages {
   static constexpr int NS = (D == 64) ? 3 : 2;
 };
 
+// Waves per split-kernel workgroup.
+template <int D>
+struct SplitWaves {
+  static constexpr int NW = 4;
+};
+
 template <int D, int MODE>
 struct DecodeLds {
+  static constexpr int NW = SplitWaves<D>::NW;
   static constexpr int dma_stage = StageGeo<D, MODE == kModeDmaCompact>::STAGE;
-  static constexpr int stream = 4 * DecodeStages<D>::NS * dma_stage;
-  static constexpr int merge = 4 * kMergeCols * D * 4;
+  static constexpr int stream = NW * DecodeStages<D>::NS * dma_stage;
+  static constexpr int merge = NW * kMergeCols * D * 4;
   static constexpr int area = stream > merge ? stream : merge;  // streams, then merge and combine scratch
 };
 
@@ -318,8 +327,9 @@ __device__ __forceinline__ void merge_waves(const WaveAttn<D, 1>& W, float* s_ml
 }
 
 template <int D, int MODE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DecodeOcc<D, MODE>::waves))) void
+__global__ __launch_bounds__(64 * SplitWaves<D>::NW) __attribute__((amdgpu_waves_per_eu(DecodeOcc<D, MODE>::waves))) void
 decode_split_kernel(DecodeArgs a) {
+  constexpr int NW = SplitWaves<D>::NW;
   constexpr bool COMPACT = MODE != kModeDmaGeneral;
   using SG = StageGeo<D, COMPACT>;
   constexpr int NS = DecodeStages<D>::NS;
@@ -327,9 +337,9 @@ decode_split_kernel(DecodeArgs a) {
   int* s_pref = reinterpret_cast<int*>(smem);
   int* s_len = s_pref + ((a.B + 1 + 3) / 4) * 4;
   int* s_red = s_pref + decode_lds_pref_ints(a.B);
-  float* s_ml = reinterpret_cast<float*>(s_red + 16);  // [4 waves][16 cols][2]
-  uint8_t* rings = reinterpret_cast<uint8_t*>(s_ml + 4 * 16 * 2);  // per-wave stream area
-  float* s_o = reinterpret_cast<float*>(rings);         // [4 waves][kMergeCols][D], after the streams
+  float* s_ml = reinterpret_cast<float*>(s_red + 16);  // [NW waves][16 cols][2]
+  uint8_t* rings = reinterpret_cast<uint8_t*>(s_ml + NW * 16 * 2);  // per-wave stream area
+  float* s_o = reinterpret_cast<float*>(rings);         // [NW waves][kMergeCols][D], after the streams
 
   // The scales are read with vector loads issued first: their latency then
   // overlaps the schedule's own loads (a scalar load here would be waited
@@ -341,7 +351,7 @@ decode_split_kernel(DecodeArgs a) {
   const int hkv = a.pool.hkv;
   const int cap = a.max_blocks * a.pool.bs;
   int tps, total;
-  decode_schedule(a.seq_lens, a.B, cap, hkv, a.target, s_pref, s_len, s_red, tps, total);
+  decode_schedule<NW>(a.seq_lens, a.B, cap, hkv, a.target, s_pref, s_len, s_red, tps, total);
   total = __builtin_amdgcn_readfirstlane(total);
   const float qk_factor = a.sm_scale * uniform_f32(ksc) * kLog2e;
   const float gv = uniform_f32(vsc);
@@ -380,16 +390,16 @@ decode_split_kernel(DecodeArgs a) {
     const int st1 = st0 + sq + (split < sr ? 1 : 0);
 
     const int32_t* bt_row = a.bt + (int64_t)b * a.max_blocks;
-    const int k0 = st0 + w;  // the wave's steps: k0, k0 + 4, ... below st1
+    const int k0 = st0 + w;  // the wave's steps: k0, k0 + NW, ... below st1
     WaveAttn<D, 1> W;
     W.init();
     const bool valid = i < grp;
     const uint16_t* qrow = valid ? a.q + (int64_t)b * a.q_st + (int64_t)(h * grp + i) * a.q_sh : nullptr;
     W.lim[0] = valid ? L - 1 : -1;
 
-    decode_stream<D, COMPACT, NS, 4>(W, ring, a.pool, bt_row, L, h, k0, st1, qrow, qk_factor, dof, ll, j);
+    decode_stream<D, COMPACT, NS, NW>(W, ring, a.pool, bt_row, L, h, k0, st1, qrow, qk_factor, dof, ll, j);
     __syncthreads();  // every wave's ring is drained before the rings become the merge buffer
-    merge_waves<D, 4>(W, s_ml, s_o, grp, w, i, j, [&](int col, int d, float on, float M, float lt) {
+    merge_waves<D, NW>(W, s_ml, s_o, grp, w, i, j, [&](int col, int d, float on, float M, float lt) {
       if (nsplit == 1) {
         const float y = on * gv;
         a.out[((int64_t)b * a.hq + h * grp + col) * D + d] = (uint16_t)(pack_bf16x2(y, 0.0f) & 0xFFFFu);
@@ -411,11 +421,11 @@ decode_split_kernel(DecodeArgs a) {
       wait_stores();
       __syncthreads();
       if (threadIdx.x == 0)
-        s_red[8] = (__hip_atomic_fetch_add(&a.ws_cnt[(int64_t)b * hkv + h], 1u, __ATOMIC_RELAXED,
+        s_red[15] = (__hip_atomic_fetch_add(&a.ws_cnt[(int64_t)b * hkv + h], 1u, __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(nsplit - 1));
       __syncthreads();
-      if (s_red[8]) {
-        combine_splits<D>(a, b, h, (int64_t)s_pref[b] * hkv + h, nsplit, s_o, DecodeLds<D, MODE>::area / 4);
+      if (s_red[15]) {
+        combine_splits<D, NW>(a, b, h, (int64_t)s_pref[b] * hkv + h, nsplit, s_o, DecodeLds<D, MODE>::area / 4);
         if (threadIdx.x == 0)
           __hip_atomic_store(&a.ws_cnt[(int64_t)b * hkv + h], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
@@ -511,7 +521,7 @@ size_t decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, i
 
 template <int D, int MODE>
 static size_t decode_lds_bytes_m(int num_seqs) {
-  return (size_t)(decode_lds_pref_ints(num_seqs) + 16) * 4 + 4 * 16 * 2 * 4 + DecodeLds<D, MODE>::area;
+  return (size_t)(decode_lds_pref_ints(num_seqs) + 16) * 4 + SplitWaves<D>::NW * 16 * 2 * 4 + DecodeLds<D, MODE>::area;
 }
 
 template <int D>
@@ -540,7 +550,8 @@ static int resident_workgroups(size_t lds) {
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
   if (cached[dev] > 0 && cached_lds[dev] == lds) return cached[dev];
   int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<D, MODE>, 256, lds) != hipSuccess ||
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<D, MODE>, 64 * SplitWaves<D>::NW,
+                                                   lds) != hipSuccess ||
       per_cu < 1)
     per_cu = 1;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
@@ -601,7 +612,7 @@ static hipError_t launch_decode_v(DecodeArgs a, int max_seq_len, hipStream_t str
   int64_t want = (int64_t)a.B * hkv * ((steps + kDecodeMinTps - 1) / kDecodeMinTps);
   want = want < (int64_t)a.B * hkv ? (int64_t)a.B * hkv : want;
   const int grid = (int)(want < a.target ? want : a.target);
-  decode_split_kernel<D, MODE><<<grid, 256, lds, stream>>>(a);
+  decode_split_kernel<D, MODE><<<grid, 64 * SplitWaves<D>::NW, lds, stream>>>(a);
   return hipGetLastError();
 }
 
