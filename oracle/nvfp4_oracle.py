@@ -235,6 +235,34 @@ def dequant_paged(pool: np.ndarray, block_table: np.ndarray, seq_lens: np.ndarra
 
 
 # ---------------------------------------------------------------------------
+# The codec on its own, for paths without native FP4 attention
+# [P40177 "Related context": the NVFP4 dequantization and quantize-dequantize
+#  (QDQ) emulation kernels for Hopper / AMD Instinct; RFC47684 "Fix steps":
+#  nvfp4_kv_dequantize_paged]
+# ---------------------------------------------------------------------------
+
+
+def dequant_pages(pool: np.ndarray, page_ids, k_scale, v_scale, head_size: int) -> np.ndarray:
+    """Page-form dequantize: every listed page of the logical pool (num_blocks,
+    2, bs, Hkv, full_dim) becomes a bf16 page (2, bs, Hkv, D) whose rows are
+    dequantize_rows of the packed rows, rounded to bf16, so that one block
+    table addresses both caches. Returns [len(page_ids), 2, bs, Hkv, D] bf16
+    bits in the order given."""
+    ids = np.asarray(page_ids, dtype=np.int64)
+    pages = pool[ids]                                       # [P, 2, bs, Hkv, fd]
+    k = f32_to_bf16(dequantize_rows(pages[:, 0], k_scale, head_size))
+    v = f32_to_bf16(dequantize_rows(pages[:, 1], v_scale, head_size))
+    return np.stack([k, v], axis=1)
+
+
+def qdq_rows(x_bits: np.ndarray, g, head_size: int) -> np.ndarray:
+    """Quantize-dequantize emulation of bf16 rows [..., D]: the rows are
+    quantised as the append writes them and read back as the dequantize
+    returns them (bf16 bits)."""
+    return f32_to_bf16(dequantize_rows(quantize_rows(x_bits, g), g, head_size))
+
+
+# ---------------------------------------------------------------------------
 # Paged attention over the quantised cache (decode and chunked prefill)
 # [P40177 "Implementation breakdown" items 1 and 3: prefill/decode wrappers
 #  reading the packed cache plus its block-scale view; RFC47684 "Cause
