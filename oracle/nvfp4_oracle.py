@@ -89,8 +89,9 @@ def e4m3_decode(b: np.ndarray) -> np.ndarray:
 
 
 def e4m3_encode_sat(s: np.ndarray) -> np.ndarray:
-    """Non-negative finite fp32 -> E4M3FN byte, round to nearest, ties to even,
-    saturating to 448 (0x7E) instead of producing NaN.
+    """Non-negative fp32 -> E4M3FN byte, round to nearest, ties to even,
+    saturating to 448 (0x7E) instead of producing NaN; +inf (an overflowed
+    amax / (6 g)) saturates too.
 
     Within the binade [2^e, 2^(e+1)) (e >= -6; below that the subnormal step
     2^-9 continues) the step is 2^(e-3); n = rint(s / step) is the significand
@@ -98,7 +99,8 @@ def e4m3_encode_sat(s: np.ndarray) -> np.ndarray:
     the next binade (n = 16) and the subnormal/normal boundary correctly.
     """
     s = np.asarray(s, dtype=np.float64)  # fp32 values are exact in fp64
-    assert np.all(s >= 0) and np.all(np.isfinite(s))
+    assert np.all(s >= 0)                # also rejects NaN
+    s = np.minimum(s, 448.0)             # everything from 448 up, +inf included, saturates
     pos = s > 0
     e = np.floor(np.log2(np.where(pos, s, 1.0)))
     # guard log2 rounding near powers of two

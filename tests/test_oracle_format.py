@@ -104,8 +104,13 @@ def test_e4m3_encode_matches_torch_cast():
 
 
 def test_e4m3_encode_saturates():
-    x = np.array([448.0, 449.0, 463.99, 464.0, 500.0, 1e20], np.float32)
+    x = np.array([448.0, 449.0, 463.99, 464.0, 500.0, 1e20, np.inf], np.float32)
     assert np.all(O.e4m3_encode_sat(x) == 0x7E)
+    # just below the saturation point rounding still applies (the binade
+    # [256, 512) steps by 32): 420 -> 416 (0x7D); 432 ties between 416 and 448
+    # and goes to the even mantissa, 448 (0x7E)
+    assert O.e4m3_encode_sat(np.array([420.0], np.float32))[0] == 0x7D
+    assert O.e4m3_encode_sat(np.array([432.0], np.float32))[0] == 0x7E
     # torch agrees up to 464 (the tie between 448 and the missing 480 goes to
     # the even 448) and returns NaN (0x7F) past it
     assert np.all(_torch_e4m3(x[:4]) == 0x7E) and _torch_e4m3(x[4:5])[0] == 0x7F
