@@ -242,6 +242,31 @@ def main():
         deq = {"gbs": round(deq_bytes / (deq_s / K) / 1e9, 1), "us": round(deq_s / K * 1e6, 2)}
         del ok, ov
 
+    # ---- the codec on its own (reported, not part of the step): page-form
+    # dequantize of the pages the decode batch uses, and quantize-dequantize
+    # emulation of the workload's K/V rows in place
+    codec = {}
+    if wd is not None:
+        used = np.unique(np.concatenate([wd.block_table[b, :(int(wd.seq_lens[b]) + bs - 1) // bs]
+                                         for b in range(wd.num_seqs)])).astype(np.int32)
+        ids = i32(used)
+        pages_out = torch.empty((w.num_blocks, 2, bs, Hkv, D), dtype=torch.bfloat16, device=dev)
+        g_pg = capture(lambda r: nvk.dequant_pages(pools[r], ids, k_scale, v_scale, pages_out))
+        pg_s, _ = time_graph(g_pg, reps=3)
+        del g_pg, pages_out
+        pg_bytes = len(used) * 2 * bs * Hkv * (fd + 2 * D) + 4 * len(used)
+        codec["dequant_pages_gbs"] = round(pg_bytes / (pg_s / K) / 1e9, 1)
+        codec["dequant_pages_us"] = round(pg_s / K * 1e6, 2)
+    kq, vq = bf(w.key), bf(w.value)
+    g_qdq = capture(lambda r: nvk.qdq(kq, vq, k_scale, v_scale))
+    qdq_s, _ = time_graph(g_qdq, reps=3)
+    del g_qdq
+    qdq_bytes = 2 * 2 * kq.numel() * 2
+    codec["qdq_gbs"] = round(qdq_bytes / (qdq_s / K) / 1e9, 1)
+    codec["qdq_us"] = round(qdq_s / K * 1e6, 2)
+    codec["qdq_tokens"] = int(kq.shape[0])
+    del kq, vq
+
     # ---- algorithmic work
     out = {"metric": METRIC, "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
            "ms_per_step": round(step_wall_s / K * 1e3, 5), "higher_is_better": True, "scaling": "weak",
@@ -285,6 +310,7 @@ def main():
     if deq is not None:
         extra["dequant_gbs"] = deq["gbs"]
         extra["dequant_us"] = deq["us"]
+    extra.update(codec)
     out["config"] = {"workload": w.name, "num_seqs": B, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
                      "block_size": bs, "total_tokens": int(w.seq_lens.sum()), "new_tokens": n_new,
                      "decode_seqs": int(len(dec_idx)), "prefill_seqs": int(len(pre_idx)), "kv_dtype": "nvfp4",

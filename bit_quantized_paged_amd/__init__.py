@@ -22,7 +22,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libnvfp4kv.so")
 
 EXPORTS = [
-    "nvfp4_kv_full_dim", "nvfp4_kv_append", "nvfp4_kv_dequant_paged",
+    "nvfp4_kv_full_dim", "nvfp4_kv_append", "nvfp4_kv_dequant_paged", "nvfp4_kv_dequant_pages", "nvfp4_kv_qdq",
     "nvfp4_paged_attention_decode_workspace_size", "nvfp4_paged_attention_decode_plan",
     "nvfp4_paged_attention_decode",
     "nvfp4_paged_attention_prefill", "nvfp4kv_status_string", "nvfp4kv_last_error",
@@ -60,6 +60,8 @@ def library():
             "nvfp4_kv_full_dim": (_I32, [_I32]),
             "nvfp4_kv_append": (_I32, [_DESC, _P, _I64, _I64, _P, _I64, _I64, _P, _I64, _P, _P, _P]),
             "nvfp4_kv_dequant_paged": (_I32, [_DESC, _P, _I32, _P, _P, _I32, _I32, _P, _P, _P, _P, _I64, _P]),
+            "nvfp4_kv_dequant_pages": (_I32, [_DESC, _P, _I32, _P, _P, _P, _I64, _I64, _I64, _I64, _P]),
+            "nvfp4_kv_qdq": (_I32, [_P, _I64, _I64, _P, _I64, _I64, _I64, _I32, _I32, _P, _P, _P]),
             "nvfp4_paged_attention_decode_workspace_size": (_SZ, [_I32, _I32, _I32, _I32]),
             "nvfp4_paged_attention_decode_plan": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32]),
             "nvfp4_paged_attention_decode": (_I32, [_DESC, _P, _I64, _I64, _I32, _P, _I32, _P, _I32, _I32, _P, _P,
@@ -161,6 +163,37 @@ def dequant_paged(pool, block_table, seq_lens, cu_seqlens_out, max_seq_len, k_sc
                                              _ptr(seq_lens), _ptr(cu_seqlens_out), seq_lens.shape[0],
                                              int(max_seq_len), _ptr(k_scale), _ptr(v_scale), _ptr(out_key),
                                              _ptr(out_value), out_key.shape[0], _stream()))
+
+
+def dequant_pages(pool, page_ids, k_scale, v_scale, out) -> None:
+    """Page-form dequantize: listed pages of the quantised pool (logical view)
+    into the bf16 pages of ``out``, a tensor of logical shape (num_blocks, 2,
+    block_size, num_kv_heads, head_size) with any strides (multiples of 8
+    elements, last axis contiguous). ``page_ids`` int32 (None: pages
+    0 .. num_blocks - 1)."""
+    _dev(out, "out", torch.bfloat16)
+    if page_ids is not None:
+        _dev(page_ids, "page_ids", torch.int32)
+        if not page_ids.is_contiguous():
+            raise ValueError("page_ids must be contiguous")
+    d = _desc(pool)
+    if tuple(out.shape) != (d.num_blocks, 2, d.block_size, d.num_kv_heads, d.head_size) or out.stride(4) != 1:
+        raise ValueError("out must have the pool's logical shape with head_size contiguous")
+    n = page_ids.numel() if page_ids is not None else d.num_blocks
+    st = out.stride()
+    _check(library().nvfp4_kv_dequant_pages(ctypes.byref(d), _ptr(page_ids), n, _ptr(k_scale), _ptr(v_scale),
+                                             _ptr(out), st[0], st[1], st[2], st[3], _stream()))
+
+
+def qdq(key, value, k_scale, v_scale) -> None:
+    """Quantize-dequantize emulation, in place: key, value bf16 [T, Hkv, D]."""
+    _dev(key, "key", torch.bfloat16)
+    _dev(value, "value", torch.bfloat16)
+    if key.shape != value.shape or key.dim() != 3 or key.stride(2) != 1 or value.stride(2) != 1:
+        raise ValueError("key and value must be [T, Hkv, D] with D contiguous")
+    T, H, D = key.shape
+    _check(library().nvfp4_kv_qdq(_ptr(key), key.stride(0), key.stride(1), _ptr(value), value.stride(0),
+                                   value.stride(1), T, H, D, _ptr(k_scale), _ptr(v_scale), _stream()))
 
 
 def decode_workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_size: int) -> int:

@@ -136,6 +136,48 @@ nvfp4kv_status nvfp4_kv_dequant_paged(const nvfp4kv_cache* cache, const int32_t*
                     "nvfp4_kv_dequant_paged launch");
 }
 
+nvfp4kv_status nvfp4_kv_dequant_pages(const nvfp4kv_cache* cache, const int32_t* page_ids, int32_t num_pages,
+                                      const float* k_scale, const float* v_scale, void* out,
+                                      int64_t out_stride_block, int64_t out_stride_kv, int64_t out_stride_token,
+                                      int64_t out_stride_head, void* stream) {
+  nvfp4kv::Pool p;
+  nvfp4kv_status s = check_cache(cache, p);
+  if (s) return s;
+  if (num_pages < 0) return fail(NVFP4KV_INVALID_ARGUMENT, "num_pages must be >= 0");
+  if (num_pages == 0) return ok();
+  if (!k_scale || !v_scale) return fail(NVFP4KV_INVALID_ARGUMENT, "k_scale/v_scale is NULL");
+  if (out == nullptr || !aligned(out, 16)) return fail(NVFP4KV_INVALID_ARGUMENT, "out must be a 16-byte aligned pointer");
+  const int64_t st[4] = {out_stride_block, out_stride_kv, out_stride_token, out_stride_head};
+  for (int64_t v : st)
+    if (v < 0 || v % 8 != 0)
+      return fail(NVFP4KV_INVALID_ARGUMENT, "out strides must be non-negative multiples of 8 elements");
+  return hip_status(nvfp4kv::launch_dequant_pages(p, cache->head_size, page_ids, num_pages, k_scale, v_scale, out,
+                                                  out_stride_block, out_stride_kv, out_stride_token, out_stride_head,
+                                                  static_cast<hipStream_t>(stream)),
+                    "nvfp4_kv_dequant_pages launch");
+}
+
+nvfp4kv_status nvfp4_kv_qdq(void* key, int64_t key_stride_token, int64_t key_stride_head, void* value,
+                            int64_t value_stride_token, int64_t value_stride_head, int64_t num_tokens,
+                            int32_t num_kv_heads, int32_t head_size, const float* k_scale, const float* v_scale,
+                            void* stream) {
+  if (head_size != 64 && head_size != 128 && head_size != 256)
+    return fail(NVFP4KV_UNSUPPORTED, "head_size must be 64, 128 or 256");
+  if (num_kv_heads < 1) return fail(NVFP4KV_INVALID_ARGUMENT, "num_kv_heads must be >= 1");
+  if (num_tokens < 0) return fail(NVFP4KV_INVALID_ARGUMENT, "num_tokens must be >= 0");
+  if (num_tokens == 0) return ok();
+  nvfp4kv_status s;
+  if ((s = check_bf16_rows(key, key_stride_token, key_stride_head, "key"))) return s;
+  if ((s = check_bf16_rows(value, value_stride_token, value_stride_head, "value"))) return s;
+  if (k_scale == nullptr || v_scale == nullptr) return fail(NVFP4KV_INVALID_ARGUMENT, "k_scale/v_scale is NULL");
+  const int64_t lanes = num_tokens * 2 * num_kv_heads * (head_size / 16);
+  if (lanes / 256 >= (int64_t)INT32_MAX) return fail(NVFP4KV_UNSUPPORTED, "too many tokens for one call");
+  return hip_status(nvfp4kv::launch_qdq(head_size, key, key_stride_token, key_stride_head, value, value_stride_token,
+                                        value_stride_head, num_tokens, num_kv_heads, k_scale, v_scale,
+                                        static_cast<hipStream_t>(stream)),
+                    "nvfp4_kv_qdq launch");
+}
+
 size_t nvfp4_paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                                    int32_t head_size) {
   if (num_seqs <= 0 || num_kv_heads <= 0 || num_q_heads <= 0 || num_q_heads % num_kv_heads != 0 ||

@@ -34,34 +34,10 @@ __global__ __launch_bounds__(256) void append_kernel(Pool pool, const uint16_t* 
 
   const uint16_t* src = kv ? value + t * v_st + h * v_sh : key + t * k_st + h * k_sh;
   const u32x4* s4 = reinterpret_cast<const u32x4*>(src + blk16 * 16);
-  const u32x4 a = s4[0];
-  const u32x4 b = s4[1];
   float x[16];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    x[2 * i] = bf16_lo(a[i]);
-    x[2 * i + 1] = bf16_hi(a[i]);
-    x[8 + 2 * i] = bf16_lo(b[i]);
-    x[8 + 2 * i + 1] = bf16_hi(b[i]);
-  }
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[i]));
-
-  const float g = kv ? *v_scale : *k_scale;
-  // Each line is a single fp32 operation with round-to-nearest-even.
-  const float t6 = 6.0f * g;
-  const float s32 = __fdiv_rn(amax, t6);
-  const uint32_t s8 = e4m3_from_f32_sat(s32);
-  const float d = e4m3_to_f32(s8) * g;
-  const float r = (d == 0.0f) ? 0.0f : __fdiv_rn(1.0f, d);
-
-  uint32_t w0 = 0, w1 = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    w0 |= e2m1_code(x[i] * r) << (4 * i);
-    w1 |= e2m1_code(x[8 + i] * r) << (4 * i);
-  }
+  bf16_block16(s4[0], s4[1], x);
+  uint32_t w0, w1;
+  const uint32_t s8 = quantize_block16(x, kv ? *v_scale : *k_scale, w0, w1);
 
   const int64_t blk = slot / pool.bs;
   const int64_t off = slot % pool.bs;

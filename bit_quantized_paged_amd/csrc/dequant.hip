@@ -45,22 +45,8 @@ __global__ __launch_bounds__(256) void dequant_kernel(Pool pool, const int32_t* 
     const uint8_t* src = pool.data + blk * pool.sb + kv * pool.skv + r * pool.st + h * pool.sh;
     const u32x2 codes = ld_u32x2(src + jb * 8);
     const uint32_t sbyte = ld_u8(src + D / 2 + jb);
-    const h2 s = fp8x2_to_h2<false>(sbyte);
-    const h2 ss = {s[0], s[0]};
-    const float g = kv ? gv : gk;
     uint32_t o[8];
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const uint32_t c = codes[q];
-      h2 v0 = fp4x2_to_h2<0>(c) * ss;
-      h2 v1 = fp4x2_to_h2<1>(c) * ss;
-      h2 v2 = fp4x2_to_h2<2>(c) * ss;
-      h2 v3 = fp4x2_to_h2<3>(c) * ss;
-      o[4 * q + 0] = pack_bf16x2((float)v0[0] * g, (float)v0[1] * g);
-      o[4 * q + 1] = pack_bf16x2((float)v1[0] * g, (float)v1[1] * g);
-      o[4 * q + 2] = pack_bf16x2((float)v2[0] * g, (float)v2[1] * g);
-      o[4 * q + 3] = pack_bf16x2((float)v3[0] * g, (float)v3[1] * g);
-    }
+    dequant_block16(codes, sbyte, kv ? gv : gk, o);
     uint16_t* dst = (kv ? out_v : out_k) + (orow * hkv + h) * D + jb * 16;
     u32x4* d4 = reinterpret_cast<u32x4*>(dst);
     d4[0] = u32x4{o[0], o[1], o[2], o[3]};

@@ -115,4 +115,62 @@ __device__ __forceinline__ h2 fp8x2_to_h2(uint32_t w) {
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// ---- one 16-element block -------------------------------------------------
+
+// The 16 bf16 values of one block (two 16-byte words) -> fp32.
+__device__ __forceinline__ void bf16_block16(u32x4 a, u32x4 b, float (&x)[16]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = bf16_lo(a[i]);
+    x[2 * i + 1] = bf16_hi(a[i]);
+    x[8 + 2 * i] = bf16_lo(b[i]);
+    x[8 + 2 * i + 1] = bf16_hi(b[i]);
+  }
+}
+
+// Quantise one block under the per-tensor scale g: returns the E4M3 scale
+// byte and sets the two code words (element 2k in the low nibble of byte k).
+// Each line is a single fp32 operation with round-to-nearest-even: block
+// scale s = E4M3(amax / (6 g)), step d = s * g, r = 1 / d (0 when d = 0),
+// code = E2M1(x * r).
+__device__ __forceinline__ uint32_t quantize_block16(const float (&x)[16], float g, uint32_t& w0, uint32_t& w1) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[i]));
+  const float t6 = 6.0f * g;
+  const float s32 = __fdiv_rn(amax, t6);
+  const uint32_t s8 = e4m3_from_f32_sat(s32);
+  const float d = e4m3_to_f32(s8) * g;
+  const float r = (d == 0.0f) ? 0.0f : __fdiv_rn(1.0f, d);
+  w0 = 0;
+  w1 = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    w0 |= e2m1_code(x[i] * r) << (4 * i);
+    w1 |= e2m1_code(x[8 + i] * r) << (4 * i);
+  }
+  return s8;
+}
+
+// Dequantise one block into 8 words of bf16 pairs: codes -> f16 with the
+// hardware FP4 convert, times the E4M3 scale (exact in f16: at most 6
+// significant bits), widened to fp32, times g (one fp32 RNE multiply), then
+// bf16 RNE.
+__device__ __forceinline__ void dequant_block16(u32x2 codes, uint32_t sbyte, float g, uint32_t (&o)[8]) {
+  const h2 s = fp8x2_to_h2<false>(sbyte);
+  const h2 ss = {s[0], s[0]};
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const uint32_t c = codes[q];
+    const h2 v0 = fp4x2_to_h2<0>(c) * ss;
+    const h2 v1 = fp4x2_to_h2<1>(c) * ss;
+    const h2 v2 = fp4x2_to_h2<2>(c) * ss;
+    const h2 v3 = fp4x2_to_h2<3>(c) * ss;
+    o[4 * q + 0] = pack_bf16x2((float)v0[0] * g, (float)v0[1] * g);
+    o[4 * q + 1] = pack_bf16x2((float)v1[0] * g, (float)v1[1] * g);
+    o[4 * q + 2] = pack_bf16x2((float)v2[0] * g, (float)v2[1] * g);
+    o[4 * q + 3] = pack_bf16x2((float)v3[0] * g, (float)v3[1] * g);
+  }
+}
+
 }  // namespace nvfp4kv

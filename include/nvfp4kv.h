@@ -123,6 +123,44 @@ nvfp4kv_status nvfp4_kv_dequant_paged(const nvfp4kv_cache* cache,
                                       void* out_key, void* out_value, int64_t out_rows, void* stream);
 
 /*
+ * Page-form dequantize [P40177 "Related context": the NVFP4 dequantization
+ * kernels for Hopper / AMD Instinct; RFC47684 "Fix steps":
+ * nvfp4_kv_dequantize_paged]: page p of the quantised cache becomes page p
+ * of a bf16 cache of the same geometry, so one block table addresses both
+ * (an attention kernel without FP4 support can then read the bf16 pages).
+ * out[p][kv][t][h][d] = bf16_RNE(fp32(e2m1 * e4m3) * g), g = k_scale for
+ * kv = 0 and v_scale for kv = 1: the values nvfp4_kv_dequant_paged returns.
+ *
+ * page_ids: device int32 [num_pages], the pages to convert (NULL converts
+ *   pages 0 .. num_pages - 1); ids outside [0, num_blocks) are skipped.
+ * out: caller-owned bf16 pages addressed as out + p * out_stride_block +
+ *   kv * out_stride_kv + t * out_stride_token + h * out_stride_head + d
+ *   (strides in ELEMENTS, non-negative multiples of 8; d contiguous;
+ *   16-byte aligned). Pages not listed are left untouched.
+ */
+nvfp4kv_status nvfp4_kv_dequant_pages(const nvfp4kv_cache* cache, const int32_t* page_ids, int32_t num_pages,
+                                      const float* k_scale, const float* v_scale, void* out,
+                                      int64_t out_stride_block, int64_t out_stride_kv, int64_t out_stride_token,
+                                      int64_t out_stride_head, void* stream);
+
+/*
+ * Quantize-dequantize emulation in place [P40177 "Related context": the QDQ
+ * emulation kernels for Hopper / AMD Instinct]: every 16-element block of
+ * every K and V row is quantised exactly as nvfp4_kv_append writes it and
+ * replaced by the bf16 values nvfp4_kv_dequant_paged would return for it,
+ * so a bf16 cache sees the same values an NVFP4 cache would hold.
+ *
+ * key, value: bf16 [num_tokens, num_kv_heads, head_size], strides in
+ * ELEMENTS (non-negative multiples of 8), last axis contiguous, 16-byte
+ * aligned; modified in place. Rows must not overlap (key and value must be
+ * distinct memory). head_size: 64, 128 or 256.
+ */
+nvfp4kv_status nvfp4_kv_qdq(void* key, int64_t key_stride_token, int64_t key_stride_head,
+                            void* value, int64_t value_stride_token, int64_t value_stride_head,
+                            int64_t num_tokens, int32_t num_kv_heads, int32_t head_size,
+                            const float* k_scale, const float* v_scale, void* stream);
+
+/*
  * Workspace (bytes) that nvfp4_paged_attention_decode needs for a batch of
  * num_seqs sequences; it does not depend on the sequence lengths.
  */

@@ -431,3 +431,79 @@ def test_decode_without_split_parity(name, layout):
     out_split = d.decode(max_seq_len=0)
     torch.cuda.synchronize()
     assert_attn_close(out_split, ref, f"{name}/{layout} decode with split-K")
+
+
+def _bf16_sentinel(shape):
+    """bf16 tensor filled with a NaN pattern that no dequantised value has."""
+    return torch.full(shape, -1, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+
+
+@pytest.mark.parametrize("out_layout", ["HND", "NHD"])
+def test_dequant_pages_bitexact(case, out_layout):
+    """Page-form dequantize: all pages, then a subset with repeats and ids
+    outside the pool (skipped); unlisted pages stay untouched."""
+    name, w, ref_pool = case
+    nb, bs, hkv, D = w.num_blocks, w.block_size, w.num_kv_heads, w.head_size
+    d = Dev(w, "NHD" if out_layout == "HND" else "HND")
+    d.append_all()
+    if out_layout == "HND":
+        out = _bf16_sentinel((nb, 2, hkv, bs, D)).permute(0, 1, 3, 2, 4)
+    else:
+        out = _bf16_sentinel((nb, 2, bs, hkv, D))
+    nvk.dequant_pages(d.pool, None, d.k_scale, d.v_scale, out)
+    torch.cuda.synchronize()
+    ref = O.dequant_pages(ref_pool, np.arange(nb), w.k_scale, w.v_scale, D)
+    assert np.array_equal(bf16_to_np(out), ref), name
+    ids = np.array([nb - 1, 0, -1, nb, nb + 7, min(2, nb - 1), 0], np.int32)
+    out2 = _bf16_sentinel((nb, 2, bs, hkv, D))
+    nvk.dequant_pages(d.pool, torch.from_numpy(ids).cuda(), d.k_scale, d.v_scale, out2)
+    torch.cuda.synchronize()
+    got = bf16_to_np(out2)
+    listed = sorted({int(p) for p in ids if 0 <= p < nb})
+    assert np.array_equal(got[listed], ref[listed])
+    rest = [p for p in range(nb) if p not in listed]
+    assert np.all(got[rest] == 0xFFFF)
+
+
+def test_qdq_bitexact(case):
+    """Quantize-dequantize in place equals the oracle's QDQ of the same rows,
+    with K and V as strided views of larger buffers."""
+    name, w, _ = case
+    T, hkv, D = w.key.shape
+    kbuf = torch.zeros((T, hkv + 1, D + 16), dtype=torch.int16, device="cuda")
+    vbuf = torch.zeros((T, hkv, D + 32), dtype=torch.int16, device="cuda")
+    kbuf[:, :hkv, :D] = torch.from_numpy(np.ascontiguousarray(w.key).view(np.int16)).cuda()
+    vbuf[:, :, 8:8 + D] = torch.from_numpy(np.ascontiguousarray(w.value).view(np.int16)).cuda()
+    k = kbuf.view(torch.bfloat16)[:, :hkv, :D]
+    v = vbuf.view(torch.bfloat16)[:, :, 8:8 + D]
+    ks = torch.tensor([float(w.k_scale)], device="cuda")
+    vs = torch.tensor([float(w.v_scale)], device="cuda")
+    nvk.qdq(k, v, ks, vs)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_to_np(k), O.qdq_rows(w.key, w.k_scale, D)), name
+    assert np.array_equal(bf16_to_np(v), O.qdq_rows(w.value, w.v_scale, D)), name
+    # bytes outside the views are untouched
+    assert torch.all(kbuf[:, hkv] == 0) and torch.all(kbuf[:, :, D:] == 0)
+    assert torch.all(vbuf[:, :, :8] == 0) and torch.all(vbuf[:, :, 8 + D:] == 0)
+
+
+def test_qdq_extreme_blocks():
+    """Zeros, saturating magnitudes, bf16 subnormals and a tiny global scale."""
+    rng = np.random.default_rng(61)
+    D, hkv, T = 128, 2, 64
+    x = rng.standard_normal((T, hkv, D)).astype(np.float32)
+    x[0] = 0.0
+    x[1] *= 1e30
+    x[2] *= 1e-39
+    x[3, :, ::16] = 3e38
+    x[4] = -x[4] * 1e-3
+    bits = torch.tensor(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    for g in (np.float32(1.0), np.float32(2.0 ** -20), np.float32(7.5e-3)):
+        k = torch.from_numpy(bits.view(np.int16).copy()).cuda().view(torch.bfloat16)
+        v = torch.from_numpy(bits.view(np.int16).copy()).cuda().view(torch.bfloat16)
+        gs = torch.tensor([float(g)], device="cuda")
+        nvk.qdq(k, v, gs, gs)
+        torch.cuda.synchronize()
+        want = O.qdq_rows(bits, g, D)
+        assert np.array_equal(bf16_to_np(k), want), float(g)
+        assert np.array_equal(bf16_to_np(v), want), float(g)
