@@ -30,19 +30,21 @@ __global__ __launch_bounds__(256) void dequant_pages_kernel(Pool pool, const int
   const int hkv = pool.hkv;
   const float gk = *k_scale;
   const float gv = *v_scale;
-  const int per_kv = pool.bs * hkv * NB;
+  // A lane owns half a block (8 elements: one code word and the block's
+  // scale byte) and writes its 16 output bytes with one store, so a wave's
+  // store covers 1 KB of consecutive output.
+  constexpr int NH = 2 * NB;  // half blocks per row
+  const int per_kv = pool.bs * hkv * NH;
   for (int w = threadIdx.x; w < 2 * per_kv; w += blockDim.x) {
     const int kv = w / per_kv;
     const int rem = w - kv * per_kv;
-    const int jb = rem % NB;
-    const int h = (rem / NB) % hkv;
-    const int r = rem / (NB * hkv);
+    const int hb = rem % NH;
+    const int h = (rem / NH) % hkv;
+    const int r = rem / (NH * hkv);
     const uint8_t* src = pool.data + p * pool.sb + kv * pool.skv + r * pool.st + h * pool.sh;
-    uint32_t o[8];
-    dequant_block16(ld_u32x2(src + jb * 8), ld_u8(src + D / 2 + jb), kv ? gv : gk, o);
-    u32x4* d4 = reinterpret_cast<u32x4*>(out + p * ob + kv * okv + r * ot + h * oh + jb * 16);
-    d4[0] = u32x4{o[0], o[1], o[2], o[3]};
-    d4[1] = u32x4{o[4], o[5], o[6], o[7]};
+    uint32_t o[4];
+    dequant_half8(ld_u32(src + hb * 4), ld_u8(src + D / 2 + hb / 2), kv ? gv : gk, o);
+    *reinterpret_cast<u32x4*>(out + p * ob + kv * okv + r * ot + h * oh + hb * 8) = u32x4{o[0], o[1], o[2], o[3]};
   }
 }
 

@@ -1,11 +1,11 @@
 // Paged dequantize [RFC47684 "Fix steps": nvfp4_kv_dequantize_paged].
 //
-// One workgroup per (page, sequence). A lane turns one 16-element block (8
-// code bytes + 1 scale byte) into 16 bf16 values: codes -> f16 with the
-// hardware FP4 convert, times the E4M3 scale (exact in f16: at most 6
-// significant bits), widened to fp32, times g (one fp32 RNE multiply), then
-// bf16 RNE. Consecutive lanes take consecutive blocks of one output row, so
-// both the 32-byte stores and the 8-byte loads are coalesced.
+// One workgroup per (page, sequence). A lane turns half a 16-element block
+// (4 code bytes + the block's scale byte) into 8 bf16 values: codes -> f16
+// with the hardware FP4 convert, times the E4M3 scale (exact in f16: at most
+// 6 significant bits), widened to fp32, times g (one fp32 RNE multiply), then
+// bf16 RNE. Consecutive lanes take consecutive halves of one output row, so
+// the 16-byte stores and the 4-byte loads are coalesced.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -33,24 +33,24 @@ __global__ __launch_bounds__(256) void dequant_kernel(Pool pool, const int32_t* 
   const int64_t out0 = (int64_t)cu_out[b] + tok0;
   const float gk = *k_scale;
   const float gv = *v_scale;
-  const int per_kv = rows * hkv * NB;
+  // A lane owns half a block (8 elements: one code word and the block's
+  // scale byte) and writes its 16 output bytes with one store, so a wave's
+  // store covers 1 KB of consecutive output.
+  constexpr int NH = 2 * NB;  // half blocks per row
+  const int per_kv = rows * hkv * NH;
   for (int w = threadIdx.x; w < 2 * per_kv; w += blockDim.x) {
     const int kv = w / per_kv;
     const int rem = w - kv * per_kv;
-    const int jb = rem % NB;
-    const int h = (rem / NB) % hkv;
-    const int r = rem / (NB * hkv);
+    const int hb = rem % NH;
+    const int h = (rem / NH) % hkv;
+    const int r = rem / (NH * hkv);
     const int64_t orow = out0 + r;
     if (orow < 0 || orow >= out_rows) continue;
     const uint8_t* src = pool.data + blk * pool.sb + kv * pool.skv + r * pool.st + h * pool.sh;
-    const u32x2 codes = ld_u32x2(src + jb * 8);
-    const uint32_t sbyte = ld_u8(src + D / 2 + jb);
-    uint32_t o[8];
-    dequant_block16(codes, sbyte, kv ? gv : gk, o);
-    uint16_t* dst = (kv ? out_v : out_k) + (orow * hkv + h) * D + jb * 16;
-    u32x4* d4 = reinterpret_cast<u32x4*>(dst);
-    d4[0] = u32x4{o[0], o[1], o[2], o[3]};
-    d4[1] = u32x4{o[4], o[5], o[6], o[7]};
+    uint32_t o[4];
+    dequant_half8(ld_u32(src + hb * 4), ld_u8(src + D / 2 + hb / 2), kv ? gv : gk, o);
+    uint16_t* dst = (kv ? out_v : out_k) + (orow * hkv + h) * D + hb * 8;
+    *reinterpret_cast<u32x4*>(dst) = u32x4{o[0], o[1], o[2], o[3]};
   }
 }
 

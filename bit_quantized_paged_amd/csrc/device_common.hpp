@@ -173,4 +173,19 @@ __device__ __forceinline__ void dequant_block16(u32x2 codes, uint32_t sbyte, flo
   }
 }
 
+// Half a block (8 elements: one code word) into 4 words of bf16 pairs, with
+// the same arithmetic as dequant_block16.
+__device__ __forceinline__ void dequant_half8(uint32_t c, uint32_t sbyte, float g, uint32_t (&o)[4]) {
+  const h2 s = fp8x2_to_h2<false>(sbyte);
+  const h2 ss = {s[0], s[0]};
+  const h2 v0 = fp4x2_to_h2<0>(c) * ss;
+  const h2 v1 = fp4x2_to_h2<1>(c) * ss;
+  const h2 v2 = fp4x2_to_h2<2>(c) * ss;
+  const h2 v3 = fp4x2_to_h2<3>(c) * ss;
+  o[0] = pack_bf16x2((float)v0[0] * g, (float)v0[1] * g);
+  o[1] = pack_bf16x2((float)v1[0] * g, (float)v1[1] * g);
+  o[2] = pack_bf16x2((float)v2[0] * g, (float)v2[1] * g);
+  o[3] = pack_bf16x2((float)v3[0] * g, (float)v3[1] * g);
+}
+
 }  // namespace nvfp4kv
