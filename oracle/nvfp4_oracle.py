@@ -316,3 +316,27 @@ def paged_attention(pool: np.ndarray, query_bits: np.ndarray, cu_q: np.ndarray,
             o = (w @ V[:, kvh, :]) / np.where(den > 0, den, 1.0)
             out[q0:q1, h, :] = np.where(has[:, None], o, 0.0)
     return out
+
+
+# ---------------------------------------------------------------------------
+# FP8 attention output and its dequantize-to-bf16 epilogue [P40177
+# "Implementation breakdown" item 2: the NVFP4 attention kernel emits FP8
+# into a preallocated buffer and the forward pass dequantises it back to the
+# model dtype; "Risks and impact": that FP8 output adds a rounding step]
+# ---------------------------------------------------------------------------
+
+
+def fp8_out(o: np.ndarray, o_scale) -> np.ndarray:
+    """Attention output -> FP8-E4M3 codes under a per-tensor output scale:
+    q = RN32(RN32(o) / o_scale) (fp32 division), then E4M3 RNE of |q|
+    saturating to 448, with the sign of q in bit 7."""
+    o32 = np.asarray(o).astype(F32)
+    q = (o32 / F32(o_scale)).astype(F32)
+    mag = e4m3_encode_sat(np.abs(q))
+    sign = (q.view(np.uint32) >> np.uint32(31)).astype(np.uint8)
+    return (sign << np.uint8(7)) | mag
+
+
+def fp8_to_bf16(codes: np.ndarray, o_scale) -> np.ndarray:
+    """The epilogue: bf16 RNE of fp32(e4m3(code) * o_scale) (bf16 bits)."""
+    return f32_to_bf16((e4m3_decode(codes).astype(F32) * F32(o_scale)).astype(F32))
