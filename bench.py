@@ -257,6 +257,28 @@ def main():
         pg_bytes = len(used) * 2 * bs * Hkv * (fd + 2 * D) + 4 * len(used)
         codec["dequant_pages_gbs"] = round(pg_bytes / (pg_s / K) / 1e9, 1)
         codec["dequant_pages_us"] = round(pg_s / K * 1e6, 2)
+    if wd is not None:
+        # FP8-E4M3 output (output scale 1) and its bf16 epilogue; the extra
+        # rounding is measured against the bf16 output of the same decode
+        o_s = torch.ones(1, dtype=torch.float32, device=dev)
+        codes = torch.empty(outd.shape, dtype=torch.uint8, device=dev)
+        g_f8 = capture(lambda r: nvk.paged_attention_decode(pools[r], qd, btd, sld, maxd, k_scale, v_scale, sm_scale,
+                                                            codes, wsd, o_scale=o_s))
+        f8_s, _ = time_graph(g_f8, reps=3)
+        del g_f8
+        back = torch.empty_like(outd)
+        g_ep = capture(lambda r: nvk.fp8_to_bf16(codes, o_s, back))
+        ep_s, _ = time_graph(g_ep, reps=3)
+        del g_ep
+        torch.cuda.synchronize()
+        ref16 = ref_d.float()
+        diff = (back.float() - ref16).abs()
+        rel = diff / ref16.abs().clamp_min(1e-2)
+        codec["decode_fp8out_us"] = round(f8_s / K * 1e6, 2)
+        codec["fp8_epilogue_us"] = round(ep_s / K * 1e6, 2)
+        codec["fp8_out_extra_err"] = {"max_abs": round(float(diff.max()), 5), "rms_abs": round(float(diff.pow(2).mean().sqrt()), 6),
+                                      "max_rel": round(float(rel.max()), 5), "ref": "bf16 output of the same decode"}
+        del codes, back
     kq, vq = bf(w.key), bf(w.value)
     g_qdq = capture(lambda r: nvk.qdq(kq, vq, k_scale, v_scale))
     qdq_s, _ = time_graph(g_qdq, reps=3)

@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(_HERE, "libnvfp4kv.so")
 EXPORTS = [
     "nvfp4_kv_full_dim", "nvfp4_kv_append", "nvfp4_kv_dequant_paged", "nvfp4_kv_dequant_pages", "nvfp4_kv_qdq",
     "nvfp4_paged_attention_decode_workspace_size", "nvfp4_paged_attention_decode_plan",
-    "nvfp4_paged_attention_decode",
+    "nvfp4_paged_attention_decode", "nvfp4_paged_attention_decode_fp8", "nvfp4_fp8_to_bf16",
     "nvfp4_paged_attention_prefill", "nvfp4kv_status_string", "nvfp4kv_last_error",
 ]
 
@@ -66,6 +66,9 @@ def library():
             "nvfp4_paged_attention_decode_plan": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32]),
             "nvfp4_paged_attention_decode": (_I32, [_DESC, _P, _I64, _I64, _I32, _P, _I32, _P, _I32, _I32, _P, _P,
                                                     _F32, _P, _P, _SZ, _P]),
+            "nvfp4_paged_attention_decode_fp8": (_I32, [_DESC, _P, _I64, _I64, _I32, _P, _I32, _P, _I32, _I32, _P,
+                                                        _P, _F32, _P, _P, _P, _SZ, _P]),
+            "nvfp4_fp8_to_bf16": (_I32, [_P, _I64, _P, _P, _P]),
             "nvfp4_paged_attention_prefill": (_I32, [_DESC, _P, _I64, _I64, _I32, _P, _I32, _I32, _P, _I32, _P, _I32,
                                                      _I32, _P, _P, _F32, _I32, _P, _P, _SZ, _P]),
             "nvfp4kv_status_string": (ctypes.c_char_p, [_I32]),
@@ -213,10 +216,12 @@ def decode_plan(num_seqs: int, num_kv_heads: int, head_size: int, block_size: in
 
 
 def paged_attention_decode(pool, q, block_table, seq_lens, max_seq_len, k_scale, v_scale, sm_scale,
-                           out, workspace) -> None:
-    """One query token per sequence: q, out bf16 [B, Hq, D]; workspace uint8."""
+                           out, workspace, o_scale=None) -> None:
+    """One query token per sequence: q bf16 [B, Hq, D]; workspace uint8. out is
+    bf16 [B, Hq, D], or, with an output scale ``o_scale`` (device fp32
+    scalar), uint8 [B, Hq, D] of FP8-E4M3 codes (see fp8_to_bf16)."""
     _dev(q, "q", torch.bfloat16)
-    _dev(out, "out", torch.bfloat16)
+    _dev(out, "out", torch.bfloat16 if o_scale is None else torch.uint8)
     _dev(workspace, "workspace", torch.uint8)
     for t, nm in ((block_table, "block_table"), (seq_lens, "seq_lens")):
         _dev(t, nm, torch.int32)
@@ -225,10 +230,25 @@ def paged_attention_decode(pool, q, block_table, seq_lens, max_seq_len, k_scale,
     if not out.is_contiguous() or q.stride(-1) != 1:
         raise ValueError("out must be contiguous and q needs a contiguous last axis")
     d = _desc(pool)
-    _check(library().nvfp4_paged_attention_decode(
-        ctypes.byref(d), _ptr(q), q.stride(0), q.stride(1), q.shape[1], _ptr(block_table), block_table.shape[1],
-        _ptr(seq_lens), seq_lens.shape[0], int(max_seq_len), _ptr(k_scale), _ptr(v_scale), float(sm_scale),
-        _ptr(out), _ptr(workspace), workspace.numel(), _stream()))
+    if o_scale is None:
+        _check(library().nvfp4_paged_attention_decode(
+            ctypes.byref(d), _ptr(q), q.stride(0), q.stride(1), q.shape[1], _ptr(block_table), block_table.shape[1],
+            _ptr(seq_lens), seq_lens.shape[0], int(max_seq_len), _ptr(k_scale), _ptr(v_scale), float(sm_scale),
+            _ptr(out), _ptr(workspace), workspace.numel(), _stream()))
+    else:
+        _check(library().nvfp4_paged_attention_decode_fp8(
+            ctypes.byref(d), _ptr(q), q.stride(0), q.stride(1), q.shape[1], _ptr(block_table), block_table.shape[1],
+            _ptr(seq_lens), seq_lens.shape[0], int(max_seq_len), _ptr(k_scale), _ptr(v_scale), float(sm_scale),
+            _ptr(o_scale), _ptr(out), _ptr(workspace), workspace.numel(), _stream()))
+
+
+def fp8_to_bf16(codes, o_scale, out) -> None:
+    """The FP8 output's epilogue: uint8 codes -> bf16 of the same shape."""
+    _dev(codes, "codes", torch.uint8)
+    _dev(out, "out", torch.bfloat16)
+    if codes.shape != out.shape or not codes.is_contiguous() or not out.is_contiguous():
+        raise ValueError("codes and out must be contiguous and of one shape")
+    _check(library().nvfp4_fp8_to_bf16(_ptr(codes), codes.numel(), _ptr(o_scale), _ptr(out), _stream()))
 
 
 def paged_attention_prefill(pool, q, cu_seqlens_q, max_q_len, block_table, seq_lens, max_seq_len,

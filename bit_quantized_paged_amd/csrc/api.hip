@@ -192,12 +192,13 @@ int32_t nvfp4_paged_attention_decode_plan(int32_t num_seqs, int32_t num_kv_heads
   return nvfp4kv::decode_plan(num_seqs, num_kv_heads, head_size, block_size, max_blocks_per_seq, max_seq_len);
 }
 
-nvfp4kv_status nvfp4_paged_attention_decode(const nvfp4kv_cache* cache, const void* q, int64_t q_stride_token,
+static nvfp4kv_status decode_impl(const nvfp4kv_cache* cache, const void* q, int64_t q_stride_token,
                                             int64_t q_stride_head, int32_t num_q_heads,
                                             const int32_t* block_table, int32_t max_blocks_per_seq,
                                             const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
                                             const float* k_scale, const float* v_scale, float sm_scale,
-                                            void* out, void* workspace, size_t workspace_bytes, void* stream) {
+                                            const float* o_scale, void* out, void* workspace,
+                                            size_t workspace_bytes, void* stream) {
   nvfp4kv::Pool p;
   nvfp4kv_status s = check_cache(cache, p);
   if (s) return s;
@@ -226,9 +227,44 @@ nvfp4kv_status nvfp4_paged_attention_decode(const nvfp4kv_cache* cache, const vo
   if (!aligned(workspace, 16)) return fail(NVFP4KV_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
   return hip_status(nvfp4kv::launch_decode(p, cache->head_size, q, q_stride_token, q_stride_head, num_q_heads,
                                            block_table, max_blocks_per_seq, seq_lens, num_seqs, max_seq_len,
-                                           k_scale, v_scale, sm_scale, out, workspace,
+                                           k_scale, v_scale, sm_scale, o_scale, out, workspace,
                                            static_cast<hipStream_t>(stream)),
                     "nvfp4_paged_attention_decode launch");
+}
+
+nvfp4kv_status nvfp4_paged_attention_decode(const nvfp4kv_cache* cache, const void* q, int64_t q_stride_token,
+                                            int64_t q_stride_head, int32_t num_q_heads,
+                                            const int32_t* block_table, int32_t max_blocks_per_seq,
+                                            const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
+                                            const float* k_scale, const float* v_scale, float sm_scale,
+                                            void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(cache, q, q_stride_token, q_stride_head, num_q_heads, block_table, max_blocks_per_seq, seq_lens,
+                     num_seqs, max_seq_len, k_scale, v_scale, sm_scale, nullptr, out, workspace, workspace_bytes,
+                     stream);
+}
+
+nvfp4kv_status nvfp4_paged_attention_decode_fp8(const nvfp4kv_cache* cache, const void* q, int64_t q_stride_token,
+                                                int64_t q_stride_head, int32_t num_q_heads,
+                                                const int32_t* block_table, int32_t max_blocks_per_seq,
+                                                const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
+                                                const float* k_scale, const float* v_scale, float sm_scale,
+                                                const float* o_scale, void* out_fp8, void* workspace,
+                                                size_t workspace_bytes, void* stream) {
+  if (o_scale == nullptr) return fail(NVFP4KV_INVALID_ARGUMENT, "o_scale is NULL");
+  return decode_impl(cache, q, q_stride_token, q_stride_head, num_q_heads, block_table, max_blocks_per_seq, seq_lens,
+                     num_seqs, max_seq_len, k_scale, v_scale, sm_scale, o_scale, out_fp8, workspace,
+                     workspace_bytes, stream);
+}
+
+nvfp4kv_status nvfp4_fp8_to_bf16(const void* in, int64_t n, const float* o_scale, void* out, void* stream) {
+  if (n < 0 || n % 8 != 0) return fail(NVFP4KV_INVALID_ARGUMENT, "n must be a non-negative multiple of 8");
+  if (n == 0) return ok();
+  if (in == nullptr || !aligned(in, 8)) return fail(NVFP4KV_INVALID_ARGUMENT, "in must be an 8-byte aligned pointer");
+  if (out == nullptr || !aligned(out, 16))
+    return fail(NVFP4KV_INVALID_ARGUMENT, "out must be a 16-byte aligned pointer");
+  if (o_scale == nullptr) return fail(NVFP4KV_INVALID_ARGUMENT, "o_scale is NULL");
+  return hip_status(nvfp4kv::launch_fp8_to_bf16(in, n, o_scale, out, static_cast<hipStream_t>(stream)),
+                    "nvfp4_fp8_to_bf16 launch");
 }
 
 nvfp4kv_status nvfp4_paged_attention_prefill(const nvfp4kv_cache* cache, const void* q, int64_t q_stride_token,

@@ -119,12 +119,29 @@ struct DecodeArgs {
   const float* k_scale;
   const float* v_scale;
   float sm_scale;
-  uint16_t* out;
+  uint16_t* out;           // bf16 output [B, hq, D] (when o_scale is null)
+  uint8_t* out8;           // FP8-E4M3 output [B, hq, D] (when o_scale is set)
+  const float* o_scale;    // per-tensor FP8 output scale, or null for bf16 output
   uint32_t* ws_cnt;  // [B * hkv] arrival counters; zero between calls
   float* ws_o;       // [slot][grp][D]   normalised partial outputs
   float* ws_ml;      // [slot][grp][2]   (max, sum) of each partial, base-2 scores
   int target;        // units the schedule aims for (<= kDecodeTargetMax)
 };
+
+// Attention output element idx (of [B, hq, D]) with value y: bf16 RNE, or
+// with an output scale os the FP8-E4M3 byte of RN32(y / os), round to
+// nearest even, saturating at 448, sign in bit 7 [P40177 "Implementation
+// breakdown" item 2: the FP8 output of the NVFP4 attention kernel].
+__device__ __forceinline__ uint32_t fp8_e4m3_out(float y, float os) {
+  const float q = __fdiv_rn(y, os);
+  return e4m3_from_f32_sat(__builtin_fabsf(q)) | ((__float_as_uint(q) >> 24) & 0x80u);
+}
+__device__ __forceinline__ void store_out(const DecodeArgs& a, float os, int64_t idx, float y) {
+  if (a.o_scale)
+    a.out8[idx] = (uint8_t)fp8_e4m3_out(y, os);
+  else
+    a.out[idx] = (uint16_t)(pack_bf16x2(y, 0.0f) & 0xFFFFu);
+}
 
 // LDS ints of the schedule: unit prefix [B + 1] and clamped lengths [B],
 // each padded to 16 bytes.
@@ -179,7 +196,8 @@ __device__ void combine_splits(const DecodeArgs& a, int b, int h, int64_t slot0,
   }
   __syncthreads();
   const float gv = *a.v_scale;
-  uint16_t* out = a.out + ((int64_t)b * a.hq + h * grp) * D;
+  const float os = a.o_scale ? *a.o_scale : 1.0f;
+  const int64_t out0 = ((int64_t)b * a.hq + h * grp) * D;
   constexpr int D4 = D / 4;
   for (int e = threadIdx.x; e < grp * D4; e += 64 * NW) {
     const int col = e / D4;
@@ -207,9 +225,16 @@ __device__ void combine_splits(const DecodeArgs& a, int b, int h, int64_t slot0,
       o += f * ld_agent4(a.ws_o + (slot0 + (int64_t)s * hkv) * grp * D, off);
     }
     const float sc = s_w[2 * col + 1] * gv;
-    uint32_t* dst = reinterpret_cast<uint32_t*>(out + col * D + 4 * d4);
-    dst[0] = pack_bf16x2(o[0] * sc, o[1] * sc);
-    dst[1] = pack_bf16x2(o[2] * sc, o[3] * sc);
+    const int64_t idx = out0 + col * D + 4 * d4;
+    if (a.o_scale) {
+      *reinterpret_cast<uint32_t*>(a.out8 + idx) =
+          fp8_e4m3_out(o[0] * sc, os) | (fp8_e4m3_out(o[1] * sc, os) << 8) | (fp8_e4m3_out(o[2] * sc, os) << 16) |
+          (fp8_e4m3_out(o[3] * sc, os) << 24);
+    } else {
+      uint32_t* dst = reinterpret_cast<uint32_t*>(a.out + idx);
+      dst[0] = pack_bf16x2(o[0] * sc, o[1] * sc);
+      dst[1] = pack_bf16x2(o[2] * sc, o[3] * sc);
+    }
   }
 }
 
@@ -355,6 +380,7 @@ decode_split_kernel(DecodeArgs a) {
   total = __builtin_amdgcn_readfirstlane(total);
   const float qk_factor = a.sm_scale * uniform_f32(ksc) * kLog2e;
   const float gv = uniform_f32(vsc);
+  const float os = a.o_scale ? *a.o_scale : 1.0f;
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -401,8 +427,7 @@ decode_split_kernel(DecodeArgs a) {
     __syncthreads();  // every wave's ring is drained before the rings become the merge buffer
     merge_waves<D, NW>(W, s_ml, s_o, grp, w, i, j, [&](int col, int d, float on, float M, float lt) {
       if (nsplit == 1) {
-        const float y = on * gv;
-        a.out[((int64_t)b * a.hq + h * grp + col) * D + d] = (uint16_t)(pack_bf16x2(y, 0.0f) & 0xFFFFu);
+        store_out(a, os, ((int64_t)b * a.hq + h * grp + col) * D + d, on * gv);
       } else {
         const int64_t slot = (int64_t)ubs * hkv + h;
         st_agent(a.ws_o + (slot * grp + col) * D + d, on);
@@ -483,6 +508,7 @@ __global__ __launch_bounds__(64 * PairGeo<D>::NW) void decode_pair_kernel(Decode
   const int L = clamp_len(ld_uniform(a.seq_lens, b), a.max_blocks * a.pool.bs);
   const float qk_factor = a.sm_scale * uniform_f32(ksc) * kLog2e;
   const float gv = uniform_f32(vsc);
+  const float os = a.o_scale ? *a.o_scale : 1.0f;
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -500,8 +526,7 @@ __global__ __launch_bounds__(64 * PairGeo<D>::NW) void decode_pair_kernel(Decode
                                     qrow, qk_factor, dof, ll, j);
   __syncthreads();  // every wave's ring is drained before the rings become the merge buffer
   merge_waves<D, NW>(W, s_ml, s_o, grp, w, i, j, [&](int col, int d, float on, float, float) {
-    const float y = on * gv;
-    a.out[((int64_t)b * a.hq + h * grp + col) * D + d] = (uint16_t)(pack_bf16x2(y, 0.0f) & 0xFFFFu);
+    store_out(a, os, ((int64_t)b * a.hq + h * grp + col) * D + d, on * gv);
   });
 }
 
@@ -628,7 +653,8 @@ static hipError_t launch_decode_t(DecodeArgs a, int max_seq_len, hipStream_t str
 hipError_t launch_decode(const Pool& pool, int head_size, const void* q, int64_t q_st, int64_t q_sh,
                          int num_q_heads, const int32_t* block_table, int32_t max_blocks,
                          const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len, const float* k_scale,
-                         const float* v_scale, float sm_scale, void* out, void* workspace, hipStream_t stream) {
+                         const float* v_scale, float sm_scale, const float* o_scale, void* out, void* workspace,
+                         hipStream_t stream) {
   if (num_seqs == 0) return hipSuccess;
   DecodeArgs a;
   a.pool = pool;
@@ -645,6 +671,8 @@ hipError_t launch_decode(const Pool& pool, int head_size, const void* q, int64_t
   a.v_scale = v_scale;
   a.sm_scale = sm_scale;
   a.out = static_cast<uint16_t*>(out);
+  a.out8 = static_cast<uint8_t*>(out);
+  a.o_scale = o_scale;
   const int64_t slots = kDecodeTargetMax + (int64_t)num_seqs * pool.hkv;
   a.ws_cnt = static_cast<uint32_t*>(workspace);
   a.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + counter_bytes(pool.hkv));

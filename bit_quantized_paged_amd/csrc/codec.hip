@@ -74,6 +74,37 @@ __global__ __launch_bounds__(256) void qdq_kernel(uint16_t* __restrict__ key, in
   p4[1] = u32x4{o[4], o[5], o[6], o[7]};
 }
 
+// FP8-E4M3 attention output -> bf16 [P40177 "Implementation breakdown" item
+// 2: the forward pass dequantises the kernel's FP8 output back to the model
+// dtype]. A lane converts 8 bytes: bf16 RNE of fp32(e4m3 * o_scale); the
+// E4M3FN codes 0x7F and 0xFF are NaN.
+__global__ __launch_bounds__(256) void fp8_to_bf16_kernel(const uint8_t* __restrict__ in, int64_t n8,
+                                                          const float* __restrict__ o_scale,
+                                                          uint16_t* __restrict__ out) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= n8) return;
+  const u32x2 w = ld_u32x2(in + gid * 8);
+  const float os = *o_scale;
+  uint32_t o[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t b0 = (w[k / 2] >> (16 * (k & 1))) & 0xFFu;
+    const uint32_t b1 = (w[k / 2] >> (16 * (k & 1) + 8)) & 0xFFu;
+    const float v0 = ((b0 & 0x7Fu) == 0x7Fu) ? __builtin_nanf("") : e4m3_to_f32(b0);
+    const float v1 = ((b1 & 0x7Fu) == 0x7Fu) ? __builtin_nanf("") : e4m3_to_f32(b1);
+    o[k] = pack_bf16x2(v0 * os, v1 * os);
+  }
+  *reinterpret_cast<u32x4*>(out + gid * 8) = u32x4{o[0], o[1], o[2], o[3]};
+}
+
+hipError_t launch_fp8_to_bf16(const void* in, int64_t n, const float* o_scale, void* out, hipStream_t stream) {
+  const int64_t n8 = n / 8;
+  if (n8 == 0) return hipSuccess;
+  fp8_to_bf16_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, stream>>>(static_cast<const uint8_t*>(in), n8, o_scale,
+                                                                      static_cast<uint16_t*>(out));
+  return hipGetLastError();
+}
+
 hipError_t launch_dequant_pages(const Pool& pool, int head_size, const int32_t* page_ids, int32_t num_pages,
                                 const float* k_scale, const float* v_scale, void* out, int64_t ob, int64_t okv,
                                 int64_t ot, int64_t oh, hipStream_t stream) {

@@ -35,7 +35,11 @@ size_t decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, i
 hipError_t launch_decode(const Pool& pool, int head_size, const void* q, int64_t q_st, int64_t q_sh,
                          int num_q_heads, const int32_t* block_table, int32_t max_blocks,
                          const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len, const float* k_scale,
-                         const float* v_scale, float sm_scale, void* out, void* workspace, hipStream_t stream);
+                         const float* v_scale, float sm_scale, const float* o_scale, void* out, void* workspace,
+                         hipStream_t stream);
+
+// FP8-E4M3 bytes -> bf16: bf16 RNE of fp32(e4m3 * o_scale); n a multiple of 8.
+hipError_t launch_fp8_to_bf16(const void* in, int64_t n, const float* o_scale, void* out, hipStream_t stream);
 
 // Decode kernel a call with these sizes launches on the current device:
 // 1 = one workgroup per (sequence, kv head), 0 = split-K, -1 = bad head size.

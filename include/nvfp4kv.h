@@ -225,6 +225,34 @@ nvfp4kv_status nvfp4_paged_attention_decode(const nvfp4kv_cache* cache,
                                             void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Decode attention with FP8-E4M3 output [P40177 "Implementation breakdown"
+ * item 2: the NVFP4 attention kernel emits FP8 into a preallocated buffer
+ * and the forward pass dequantises it to the model dtype; "Risks and
+ * impact": that adds a rounding step]. Same inputs, kernels and contract as
+ * nvfp4_paged_attention_decode; instead of bf16 it writes, for each output
+ * value y, the E4M3FN byte of RN32(y / o_scale) rounded to nearest even and
+ * saturating at 448 (sign in bit 7). o_scale: device fp32 scalar (> 0).
+ * out_fp8: uint8 [num_seqs, num_q_heads, head_size] contiguous, 16-byte
+ * aligned. nvfp4_fp8_to_bf16 turns it back into bf16.
+ */
+nvfp4kv_status nvfp4_paged_attention_decode_fp8(const nvfp4kv_cache* cache,
+                                                const void* q, int64_t q_stride_token, int64_t q_stride_head,
+                                                int32_t num_q_heads,
+                                                const int32_t* block_table, int32_t max_blocks_per_seq,
+                                                const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
+                                                const float* k_scale, const float* v_scale, float sm_scale,
+                                                const float* o_scale, void* out_fp8, void* workspace,
+                                                size_t workspace_bytes, void* stream);
+
+/*
+ * The FP8 output's epilogue [P40177 "Implementation breakdown" item 2]:
+ * out[i] = bf16_RNE(fp32(e4m3(in[i]) * o_scale)); the E4M3FN NaN codes 0x7F
+ * and 0xFF give NaN. in: n bytes, 8-byte aligned; out: bf16 [n], 16-byte
+ * aligned; n a multiple of 8.
+ */
+nvfp4kv_status nvfp4_fp8_to_bf16(const void* in, int64_t n, const float* o_scale, void* out, void* stream);
+
+/*
  * Chunked-prefill attention over the quantised pages [P40177
  * "Implementation breakdown" 1 and 3]. Sequence b has q_b = cu_seqlens_q[b+1]
  * - cu_seqlens_q[b] new query tokens, the last q_b of its seq_lens[b]

@@ -507,3 +507,69 @@ def test_qdq_extreme_blocks():
         want = O.qdq_rows(bits, g, D)
         assert np.array_equal(bf16_to_np(k), want), float(g)
         assert np.array_equal(bf16_to_np(v), want), float(g)
+
+
+def _fp8_close(codes, ref, os, what):
+    """FP8 output codes against the fp64 reference: the decoded value may be
+    off by half an E4M3 step of the reference (the output rounding) plus the
+    attention tolerance (the two sides round at slightly different inputs)."""
+    got = O.e4m3_decode(codes.cpu().numpy()) * float(np.float32(os))
+    q = np.abs(ref) / float(np.float32(os))
+    step = np.where(q < 2.0 ** -6, 2.0 ** -9, 2.0 ** (np.floor(np.log2(np.maximum(q, 2.0 ** -6))) - 3))
+    step = step * float(np.float32(os))
+    bound = step / 2 + 2e-3 + 1e-2 * np.abs(ref) + 2 ** -7 * np.abs(ref)
+    err = np.abs(got - ref)
+    bad = err > bound
+    assert not np.any(bad), f"{what}: {int(bad.sum())} outside, worst excess {float(np.max(err - bound)):.3g}"
+
+
+def test_fp8_epilogue_bitexact():
+    codes = np.tile(np.arange(256, dtype=np.uint8), 5)
+    for os in (1.0, 0.375, 6.0):
+        c = torch.from_numpy(codes).cuda()
+        out = torch.empty(codes.shape, dtype=torch.bfloat16, device="cuda")
+        s = torch.tensor([os], dtype=torch.float32, device="cuda")
+        nvk.fp8_to_bf16(c, s, out)
+        torch.cuda.synchronize()
+        got = bf16_to_np(out)
+        want = O.fp8_to_bf16(codes, np.float32(os))
+        nan = (codes & 0x7F) == 0x7F
+        assert np.array_equal(got[~nan], want[~nan]), os
+        assert np.all(np.isnan(out.float().cpu().numpy()[nan]))
+
+
+@pytest.mark.parametrize("os", [1.0, 0.03125])
+def test_decode_fp8_output(case, os):
+    """FP8 output of the split-K kernel (cases with one and several splits)."""
+    name, w, _ = case
+    wd = _decode_view(w)
+    d = Dev(wd, "HND")
+    d.append_all()
+    codes = torch.empty((wd.num_seqs, wd.num_q_heads, wd.head_size), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(nvk.decode_workspace_size(wd.num_seqs, wd.num_q_heads, wd.num_kv_heads, wd.head_size),
+                     dtype=torch.uint8, device="cuda")
+    s = torch.tensor([os], dtype=torch.float32, device="cuda")
+    nvk.paged_attention_decode(d.pool, d.query, d.bt, d.seq_lens, int(wd.seq_lens.max()), d.k_scale, d.v_scale,
+                               d.sm_scale, codes, ws, o_scale=s)
+    torch.cuda.synchronize()
+    ref = O.paged_attention(oracle_pool(wd), wd.query, wd.cu_q, wd.block_table, wd.seq_lens, wd.k_scale,
+                            wd.v_scale, np.float32(d.sm_scale), wd.head_size)
+    _fp8_close(codes, ref, os, f"{name} fp8 decode")
+
+
+def test_decode_fp8_output_many_splits_and_per_pair():
+    """FP8 output through the split combine (long sequences) and through the
+    per-pair kernel (many short ones); both against the oracle."""
+    for lens, hq, hkv in (([3000, 1, 1700], 16, 8), (list(np.random.default_rng(62).integers(1, 2000, 32)), 16, 8)):
+        w = _decode_batch(63, lens, hq, hkv, 128, 16)
+        d = Dev(w, "HND")
+        d.append_all()
+        codes = torch.empty((w.num_seqs, hq, 128), dtype=torch.uint8, device="cuda")
+        ws = torch.zeros(nvk.decode_workspace_size(w.num_seqs, hq, hkv, 128), dtype=torch.uint8, device="cuda")
+        s = torch.tensor([0.25], dtype=torch.float32, device="cuda")
+        nvk.paged_attention_decode(d.pool, d.query, d.bt, d.seq_lens, int(max(lens)), d.k_scale, d.v_scale,
+                                   d.sm_scale, codes, ws, o_scale=s)
+        torch.cuda.synchronize()
+        ref = O.paged_attention(oracle_pool(w), w.query, w.cu_q, w.block_table, w.seq_lens, w.k_scale, w.v_scale,
+                                np.float32(d.sm_scale), 128)
+        _fp8_close(codes, ref, 0.25, f"fp8 decode lens {lens[:3]}")
