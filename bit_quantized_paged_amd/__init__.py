@@ -25,6 +25,7 @@ EXPORTS = [
     "nvfp4_kv_full_dim", "nvfp4_kv_append", "nvfp4_kv_dequant_paged", "nvfp4_kv_dequant_pages", "nvfp4_kv_qdq",
     "nvfp4_paged_attention_decode_workspace_size", "nvfp4_paged_attention_decode_plan",
     "nvfp4_paged_attention_decode", "nvfp4_paged_attention_decode_fp8", "nvfp4_fp8_to_bf16",
+    "nvfp4_paged_attention_prefill_fp8",
     "nvfp4_paged_attention_prefill", "nvfp4kv_status_string", "nvfp4kv_last_error",
 ]
 
@@ -69,6 +70,8 @@ def library():
             "nvfp4_paged_attention_decode_fp8": (_I32, [_DESC, _P, _I64, _I64, _I32, _P, _I32, _P, _I32, _I32, _P,
                                                         _P, _F32, _P, _P, _P, _SZ, _P]),
             "nvfp4_fp8_to_bf16": (_I32, [_P, _I64, _P, _P, _P]),
+            "nvfp4_paged_attention_prefill_fp8": (_I32, [_DESC, _P, _I64, _I64, _I32, _P, _I32, _I32, _P, _I32, _P,
+                                                         _I32, _I32, _P, _P, _F32, _I32, _P, _P, _P, _SZ, _P]),
             "nvfp4_paged_attention_prefill": (_I32, [_DESC, _P, _I64, _I64, _I32, _P, _I32, _I32, _P, _I32, _P, _I32,
                                                      _I32, _P, _P, _F32, _I32, _P, _P, _SZ, _P]),
             "nvfp4kv_status_string": (ctypes.c_char_p, [_I32]),
@@ -252,10 +255,11 @@ def fp8_to_bf16(codes, o_scale, out) -> None:
 
 
 def paged_attention_prefill(pool, q, cu_seqlens_q, max_q_len, block_table, seq_lens, max_seq_len,
-                            k_scale, v_scale, sm_scale, out, causal: bool = True) -> None:
-    """Chunked prefill: q, out bf16 [total_q, Hq, D]; cu_seqlens_q int32 [B + 1]."""
+                            k_scale, v_scale, sm_scale, out, causal: bool = True, o_scale=None) -> None:
+    """Chunked prefill: q bf16 [total_q, Hq, D]; cu_seqlens_q int32 [B + 1]. out is
+    bf16 [total_q, Hq, D], or with an output scale ``o_scale`` uint8 FP8-E4M3 codes."""
     _dev(q, "q", torch.bfloat16)
-    _dev(out, "out", torch.bfloat16)
+    _dev(out, "out", torch.bfloat16 if o_scale is None else torch.uint8)
     for t, nm in ((block_table, "block_table"), (seq_lens, "seq_lens"), (cu_seqlens_q, "cu_seqlens_q")):
         _dev(t, nm, torch.int32)
         if not t.is_contiguous():
@@ -263,8 +267,11 @@ def paged_attention_prefill(pool, q, cu_seqlens_q, max_q_len, block_table, seq_l
     if not out.is_contiguous() or q.stride(-1) != 1:
         raise ValueError("out must be contiguous and q needs a contiguous last axis")
     d = _desc(pool)
-    _check(library().nvfp4_paged_attention_prefill(
-        ctypes.byref(d), _ptr(q), q.stride(0), q.stride(1), q.shape[1], _ptr(cu_seqlens_q), int(max_q_len),
-        q.shape[0], _ptr(block_table), block_table.shape[1], _ptr(seq_lens), seq_lens.shape[0],
-        int(max_seq_len), _ptr(k_scale), _ptr(v_scale), float(sm_scale), 1 if causal else 0, _ptr(out),
-        ctypes.c_void_p(0), 0, _stream()))
+    common = (ctypes.byref(d), _ptr(q), q.stride(0), q.stride(1), q.shape[1], _ptr(cu_seqlens_q), int(max_q_len),
+              q.shape[0], _ptr(block_table), block_table.shape[1], _ptr(seq_lens), seq_lens.shape[0],
+              int(max_seq_len), _ptr(k_scale), _ptr(v_scale), float(sm_scale), 1 if causal else 0)
+    if o_scale is None:
+        _check(library().nvfp4_paged_attention_prefill(*common, _ptr(out), ctypes.c_void_p(0), 0, _stream()))
+    else:
+        _check(library().nvfp4_paged_attention_prefill_fp8(*common, _ptr(o_scale), _ptr(out), ctypes.c_void_p(0), 0,
+                                                           _stream()))

@@ -267,14 +267,14 @@ nvfp4kv_status nvfp4_fp8_to_bf16(const void* in, int64_t n, const float* o_scale
                     "nvfp4_fp8_to_bf16 launch");
 }
 
-nvfp4kv_status nvfp4_paged_attention_prefill(const nvfp4kv_cache* cache, const void* q, int64_t q_stride_token,
+static nvfp4kv_status prefill_impl(const nvfp4kv_cache* cache, const void* q, int64_t q_stride_token,
                                              int64_t q_stride_head, int32_t num_q_heads,
                                              const int32_t* cu_seqlens_q, int32_t max_q_len, int32_t total_q,
                                              const int32_t* block_table, int32_t max_blocks_per_seq,
                                              const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
                                              const float* k_scale, const float* v_scale, float sm_scale,
-                                             int32_t causal, void* out, void* workspace, size_t workspace_bytes,
-                                             void* stream) {
+                                             int32_t causal, const float* o_scale, void* out, void* workspace,
+                                             size_t workspace_bytes, void* stream) {
   (void)workspace;
   (void)workspace_bytes;
   nvfp4kv::Pool p;
@@ -298,8 +298,35 @@ nvfp4kv_status nvfp4_paged_attention_prefill(const nvfp4kv_cache* cache, const v
   return hip_status(nvfp4kv::launch_prefill(p, cache->head_size, q, q_stride_token, q_stride_head, num_q_heads,
                                             cu_seqlens_q, max_q_len, total_q, block_table, max_blocks_per_seq,
                                             seq_lens, num_seqs, max_seq_len, k_scale, v_scale, sm_scale,
-                                            causal ? 1 : 0, out, static_cast<hipStream_t>(stream)),
+                                            causal ? 1 : 0, o_scale, out, static_cast<hipStream_t>(stream)),
                     "nvfp4_paged_attention_prefill launch");
+}
+
+nvfp4kv_status nvfp4_paged_attention_prefill(const nvfp4kv_cache* cache, const void* q, int64_t q_stride_token,
+                                             int64_t q_stride_head, int32_t num_q_heads,
+                                             const int32_t* cu_seqlens_q, int32_t max_q_len, int32_t total_q,
+                                             const int32_t* block_table, int32_t max_blocks_per_seq,
+                                             const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
+                                             const float* k_scale, const float* v_scale, float sm_scale,
+                                             int32_t causal, void* out, void* workspace, size_t workspace_bytes,
+                                             void* stream) {
+  return prefill_impl(cache, q, q_stride_token, q_stride_head, num_q_heads, cu_seqlens_q, max_q_len, total_q,
+                      block_table, max_blocks_per_seq, seq_lens, num_seqs, max_seq_len, k_scale, v_scale, sm_scale,
+                      causal, nullptr, out, workspace, workspace_bytes, stream);
+}
+
+nvfp4kv_status nvfp4_paged_attention_prefill_fp8(const nvfp4kv_cache* cache, const void* q, int64_t q_stride_token,
+                                                 int64_t q_stride_head, int32_t num_q_heads,
+                                                 const int32_t* cu_seqlens_q, int32_t max_q_len, int32_t total_q,
+                                                 const int32_t* block_table, int32_t max_blocks_per_seq,
+                                                 const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
+                                                 const float* k_scale, const float* v_scale, float sm_scale,
+                                                 int32_t causal, const float* o_scale, void* out_fp8, void* workspace,
+                                                 size_t workspace_bytes, void* stream) {
+  if (o_scale == nullptr) return fail(NVFP4KV_INVALID_ARGUMENT, "o_scale is NULL");
+  return prefill_impl(cache, q, q_stride_token, q_stride_head, num_q_heads, cu_seqlens_q, max_q_len, total_q,
+                      block_table, max_blocks_per_seq, seq_lens, num_seqs, max_seq_len, k_scale, v_scale, sm_scale,
+                      causal, o_scale, out_fp8, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -706,7 +706,9 @@ struct PrefillArgs {
   const float* v_scale;
   float sm_scale;
   int causal;
-  uint16_t* out;
+  uint16_t* out;         // bf16 output (when o_scale is null)
+  uint8_t* out8;         // FP8-E4M3 output (when o_scale is set)
+  const float* o_scale;  // per-tensor FP8 output scale, or null
 };
 
 template <int D>
@@ -722,6 +724,33 @@ __device__ __forceinline__ void store_column(uint16_t* orow, const f4 (&acc)[Geo
   u32x4* dst = reinterpret_cast<u32x4*>(orow + 4 * j * DPL);
 #pragma unroll
   for (int c = 0; c < DPL / 2; ++c) dst[c] = u32x4{pk[4 * c], pk[4 * c + 1], pk[4 * c + 2], pk[4 * c + 3]};
+}
+
+// The same column as FP8-E4M3 bytes (fp8_e4m3_out of each value), stored
+// r by r: the DPL bytes (4j + r) * DPL + t, t < DPL, are consecutive.
+template <int D>
+__device__ __forceinline__ void store_column_fp8(uint8_t* orow, const f4 (&acc)[Geo<D>::DPL], float scale, float os,
+                                                 int j) {
+  constexpr int DPL = Geo<D>::DPL;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    uint32_t pk[DPL / 4];
+#pragma unroll
+    for (int k = 0; k < DPL / 4; ++k) {
+      pk[k] = fp8_e4m3_out(acc[4 * k][r] * scale, os) | (fp8_e4m3_out(acc[4 * k + 1][r] * scale, os) << 8) |
+              (fp8_e4m3_out(acc[4 * k + 2][r] * scale, os) << 16) | (fp8_e4m3_out(acc[4 * k + 3][r] * scale, os) << 24);
+    }
+    uint8_t* dst = orow + (4 * j + r) * DPL;
+    if constexpr (DPL == 4) {
+      *reinterpret_cast<uint32_t*>(dst) = pk[0];
+    } else if constexpr (DPL == 8) {
+      *reinterpret_cast<u32x2*>(dst) = u32x2{pk[0], pk[1]};
+    } else {
+#pragma unroll
+      for (int c = 0; c < DPL / 16; ++c)
+        reinterpret_cast<u32x4*>(dst)[c] = u32x4{pk[4 * c], pk[4 * c + 1], pk[4 * c + 2], pk[4 * c + 3]};
+    }
+  }
 }
 
 // Prefill ring stages: the step being dequantised and up to three in flight
@@ -740,7 +769,7 @@ struct PrefillOcc {
   static constexpr int waves = (D == 256) ? 1 : 2;
 };
 
-template <int D, int NT, bool COMPACT>
+template <int D, int NT, bool COMPACT, bool FP8OUT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PrefillOcc<D>::waves))) void prefill_kernel(
     PrefillArgs a) {
   using G = Geo<D>;
@@ -853,8 +882,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PrefillOcc<
     const int c = col_base + 16 * n + i;
     if (c < ncols) {
       const int tok = c / grp, g = c - (c / grp) * grp;
-      uint16_t* orow = a.out + ((int64_t)(q0 + tok) * a.hq + h * grp + g) * D;
-      store_column<D>(orow, W.acc[n], lt > 0.0f ? gv / lt : 0.0f, j);
+      const int64_t row = ((int64_t)(q0 + tok) * a.hq + h * grp + g) * D;
+      if constexpr (FP8OUT)
+        store_column_fp8<D>(a.out8 + row, W.acc[n], lt > 0.0f ? gv / lt : 0.0f, *a.o_scale, j);
+      else
+        store_column<D>(a.out + row, W.acc[n], lt > 0.0f ? gv / lt : 0.0f, j);
     }
   }
 }
@@ -874,10 +906,15 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, int num_seqs, int max_q
   // 16-byte copies need contiguous, 16-byte aligned page rows (HND layout)
   const bool compact = a.pool.st == D / 2 + D / 16 && a.pool.sb % 16 == 0 && a.pool.skv % 16 == 0 &&
                        a.pool.sh % 16 == 0 && (reinterpret_cast<uintptr_t>(a.pool.data) % 16) == 0;
-  if (compact)
-    prefill_kernel<D, NT, true><<<grid, 256, prefill_lds_bytes<D, true>(), stream>>>(a);
+  const bool fp8 = a.o_scale != nullptr;
+  if (compact && !fp8)
+    prefill_kernel<D, NT, true, false><<<grid, 256, prefill_lds_bytes<D, true>(), stream>>>(a);
+  else if (compact)
+    prefill_kernel<D, NT, true, true><<<grid, 256, prefill_lds_bytes<D, true>(), stream>>>(a);
+  else if (!fp8)
+    prefill_kernel<D, NT, false, false><<<grid, 256, prefill_lds_bytes<D, false>(), stream>>>(a);
   else
-    prefill_kernel<D, NT, false><<<grid, 256, prefill_lds_bytes<D, false>(), stream>>>(a);
+    prefill_kernel<D, NT, false, true><<<grid, 256, prefill_lds_bytes<D, false>(), stream>>>(a);
   return hipGetLastError();
 }
 
@@ -885,7 +922,7 @@ hipError_t launch_prefill(const Pool& pool, int head_size, const void* q, int64_
                           int num_q_heads, const int32_t* cu_q, int32_t max_q_len, int32_t total_q,
                           const int32_t* block_table, int32_t max_blocks, const int32_t* seq_lens,
                           int32_t num_seqs, int32_t max_seq_len, const float* k_scale, const float* v_scale,
-                          float sm_scale, int causal, void* out, hipStream_t stream) {
+                          float sm_scale, int causal, const float* o_scale, void* out, hipStream_t stream) {
   (void)max_seq_len;
   if (num_seqs == 0 || max_q_len <= 0 || total_q <= 0) return hipSuccess;
   PrefillArgs a;
@@ -905,6 +942,8 @@ hipError_t launch_prefill(const Pool& pool, int head_size, const void* q, int64_
   a.sm_scale = sm_scale;
   a.causal = causal;
   a.out = static_cast<uint16_t*>(out);
+  a.out8 = static_cast<uint8_t*>(out);
+  a.o_scale = o_scale;
   switch (head_size) {
     case 64: return launch_prefill_t<64, 4>(a, num_seqs, max_q_len, stream);
     case 128: return launch_prefill_t<128, 2>(a, num_seqs, max_q_len, stream);

@@ -277,6 +277,24 @@ nvfp4kv_status nvfp4_paged_attention_prefill(const nvfp4kv_cache* cache,
                                              int32_t causal, void* out,
                                              void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Chunked-prefill attention with FP8-E4M3 output [P40177 "Implementation
+ * breakdown" item 2]: same inputs, kernel and contract as
+ * nvfp4_paged_attention_prefill, writing the E4M3FN byte of RN32(y /
+ * o_scale) (round to nearest even, saturating at 448, sign in bit 7) for
+ * each output value y, like nvfp4_paged_attention_decode_fp8. out_fp8:
+ * uint8 [total_q, num_q_heads, head_size] contiguous, 16-byte aligned.
+ */
+nvfp4kv_status nvfp4_paged_attention_prefill_fp8(const nvfp4kv_cache* cache,
+                                                 const void* q, int64_t q_stride_token, int64_t q_stride_head,
+                                                 int32_t num_q_heads,
+                                                 const int32_t* cu_seqlens_q, int32_t max_q_len, int32_t total_q,
+                                                 const int32_t* block_table, int32_t max_blocks_per_seq,
+                                                 const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
+                                                 const float* k_scale, const float* v_scale, float sm_scale,
+                                                 int32_t causal, const float* o_scale, void* out_fp8,
+                                                 void* workspace, size_t workspace_bytes, void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* nvfp4kv_status_string(nvfp4kv_status status);
 

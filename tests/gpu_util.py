@@ -69,13 +69,15 @@ class Dev:
                                    self.sm_scale, out, ws)
         return out
 
-    def prefill(self, causal=True):
+    def prefill(self, causal=True, o_scale=None):
+        """bf16 output, or FP8-E4M3 codes (uint8) with an output scale."""
         w = self.w
-        out = torch.empty((int(w.cu_q[-1]), w.num_q_heads, w.head_size), dtype=torch.bfloat16,
-                          device=self.query.device)
+        out = torch.empty((int(w.cu_q[-1]), w.num_q_heads, w.head_size),
+                          dtype=torch.bfloat16 if o_scale is None else torch.uint8, device=self.query.device)
+        os_t = None if o_scale is None else torch.tensor([o_scale], dtype=torch.float32, device=self.query.device)
         nvk.paged_attention_prefill(self.pool, self.query, self.cu_q, int(w.q_lens.max(initial=0)), self.bt,
                                     self.seq_lens, int(w.seq_lens.max(initial=0)), self.k_scale, self.v_scale,
-                                    self.sm_scale, out, causal=causal)
+                                    self.sm_scale, out, causal=causal, o_scale=os_t)
         return out
 
     def dequant(self):

@@ -573,3 +573,18 @@ def test_decode_fp8_output_many_splits_and_per_pair():
         ref = O.paged_attention(oracle_pool(w), w.query, w.cu_q, w.block_table, w.seq_lens, w.k_scale, w.v_scale,
                                 np.float32(d.sm_scale), 128)
         _fp8_close(codes, ref, 0.25, f"fp8 decode lens {lens[:3]}")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_fp8_output(case, causal):
+    """FP8 output of chunked prefill against the fp64 oracle (half an E4M3
+    step plus the attention tolerance)."""
+    name, w, ref_pool = case
+    d = Dev(w, "HND")
+    d.append_all()
+    os = 0.5
+    codes = d.prefill(causal=causal, o_scale=os)
+    torch.cuda.synchronize()
+    ref = O.paged_attention(ref_pool, w.query, w.cu_q, w.block_table, w.seq_lens, w.k_scale, w.v_scale,
+                            np.float32(d.sm_scale), w.head_size, causal=causal)
+    _fp8_close(codes, ref, os, f"{name} fp8 prefill causal={causal}")
