@@ -340,3 +340,55 @@ def fp8_out(o: np.ndarray, o_scale) -> np.ndarray:
 def fp8_to_bf16(codes: np.ndarray, o_scale) -> np.ndarray:
     """The epilogue: bf16 RNE of fp32(e4m3(code) * o_scale) (bf16 bits)."""
     return f32_to_bf16((e4m3_decode(codes).astype(F32) * F32(o_scale)).astype(F32))
+
+
+# ---------------------------------------------------------------------------
+# Activation quantisation with swizzled block scales [P39129 "Implementation
+# breakdown", the CUTLASS and FlashInfer kernels' apply_weights: the
+# activation is quantised to NVFP4 under the layer's input global scale with
+# is_sf_swizzled_layout=True before the FP4 GEMM; process_weights_after_loading
+# rearranges block scales with swizzle_blockscale "to match the CUTLASS
+# layout"]
+#
+# Readings: the block codec is the one quantize_rows applies, with the input
+# global scale in the role of g (the inverse of the quantise-direction global
+# scale is the dequantisation multiplier). The swizzled layout is the
+# block-scaled GEMM operand layout of 128-row x 4-scale tiles: the scale
+# matrix is zero-padded to a multiple of 128 rows and of 4 columns; tile
+# (i, j) covers rows 128i..128i+127 and scale columns 4j..4j+3 and occupies
+# 512 consecutive bytes, tiles in row-major order of (i, j); inside a tile,
+# row 128i + 32a + b (a < 4, b < 32) puts its 4 scales at bytes 16b + 4a ..
+# 16b + 4a + 3.
+# ---------------------------------------------------------------------------
+
+
+def sf_swizzled_shape(m: int, k: int):
+    """(rows, scale columns) of the padded swizzled scale matrix."""
+    nc = k // 16
+    return ((m + 127) // 128) * 128, ((nc + 3) // 4) * 4
+
+
+def sf_swizzle_offset(r, c, k: int):
+    """Byte offset of the scale of row r, scale column c in the swizzled
+    buffer of an [m, k] activation."""
+    ncp = sf_swizzled_shape(0, k)[1]
+    tile = (r // 128) * (ncp // 4) + c // 4
+    return tile * 512 + (r % 32) * 16 + ((r % 128) // 32) * 4 + c % 4
+
+
+def quant_activations(x_bits: np.ndarray, g, swizzled: bool):
+    """bf16 activation [m, k] (k a multiple of 16) -> (codes [m, k/2] uint8,
+    scales uint8): the scales are [m, k/16] row-major, or the flat swizzled
+    buffer of size rows * cols of sf_swizzled_shape with zero padding."""
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    m, k = x_bits.shape
+    packed = quantize_rows(x_bits, g)
+    codes = np.ascontiguousarray(packed[:, : k // 2])
+    scales = np.ascontiguousarray(packed[:, k // 2:])
+    if not swizzled:
+        return codes, scales
+    mp, ncp = sf_swizzled_shape(m, k)
+    out = np.zeros(mp * ncp, np.uint8)
+    r, c = np.meshgrid(np.arange(m), np.arange(k // 16), indexing="ij")
+    out[sf_swizzle_offset(r, c, k)] = scales
+    return codes, out
