@@ -85,7 +85,7 @@ def main():
     import torch
 
     import bit_quantized_paged_amd as nvk
-    from workloads import make_config
+    from workloads import make_activations, make_config
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
@@ -172,13 +172,15 @@ def main():
     K = args.steps
     cap_stream = torch.cuda.Stream()
 
-    def capture(fn):
+    def capture(fn, n=None):
+        """A graph of K calls fn(s % n), n defaulting to the pool copies."""
+        n = n or copies
         g = torch.cuda.CUDAGraph()
         cap_stream.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(cap_stream):
             with torch.cuda.graph(g, stream=cap_stream):
                 for s in range(K):
-                    fn(s % copies)
+                    fn(s % n)
         torch.cuda.current_stream().wait_stream(cap_stream)
         return g
 
@@ -279,15 +281,39 @@ def main():
         codec["fp8_out_extra_err"] = {"max_abs": round(float(diff.max()), 5), "rms_abs": round(float(diff.pow(2).mean().sqrt()), 6),
                                       "max_rel": round(float(rel.max()), 5), "ref": "bf16 output of the same decode"}
         del codes, back
+    # in place on copies of the workload's K/V, rotated so that no call finds
+    # its rows in the MALL
     kq, vq = bf(w.key), bf(w.value)
-    g_qdq = capture(lambda r: nvk.qdq(kq, vq, k_scale, v_scale))
+    q_copies = max(2, math.ceil(3 * MALL_BYTES / (2 * kq.numel() * 2)))
+    kvs = [(kq, vq)] + [(kq.clone(), vq.clone()) for _ in range(q_copies - 1)]
+    g_qdq = capture(lambda r: nvk.qdq(kvs[r % q_copies][0], kvs[r % q_copies][1], k_scale, v_scale), n=q_copies)
     qdq_s, _ = time_graph(g_qdq, reps=3)
     del g_qdq
     qdq_bytes = 2 * 2 * kq.numel() * 2
     codec["qdq_gbs"] = round(qdq_bytes / (qdq_s / K) / 1e9, 1)
     codec["qdq_us"] = round(qdq_s / K * 1e6, 2)
     codec["qdq_tokens"] = int(kq.shape[0])
-    del kq, vq
+    del kq, vq, kvs
+
+    # ---- activation quantisation with swizzled scales (reported, not part
+    # of the step): the hidden states of a 4 x 2048-token prefill chunk,
+    # hidden size 32 heads x 128, rotated through enough copies to miss the
+    # MALL
+    am, ak = 8192, 4096
+    abits, ag = make_activations(seed=4, m=am, k=ak)
+    a0 = torch.from_numpy(abits.view(np.int16)).to(dev).view(torch.bfloat16)
+    a_copies = max(2, math.ceil(3 * MALL_BYTES / (am * ak * 2)))
+    acts = [a0] + [a0.clone() for _ in range(a_copies - 1)]
+    ags = torch.tensor([float(ag)], dtype=torch.float32, device=dev)
+    a_codes, a_sf = nvk.quant_activations(a0, ags, True)
+    g_aq = capture(lambda r: nvk.quant_activations(acts[r % a_copies], ags, True, a_codes, a_sf), n=a_copies)
+    aq_s, _ = time_graph(g_aq, reps=3)
+    del g_aq, acts, a0
+    aq_bytes = am * ak * 2 + am * ak // 2 + a_sf.numel()
+    codec["act_quant_us"] = round(aq_s / K * 1e6, 2)
+    codec["act_quant_gbs"] = round(aq_bytes / (aq_s / K) / 1e9, 1)
+    codec["act_quant_shape"] = [am, ak]
+    del a_codes, a_sf
 
     # ---- algorithmic work
     out = {"metric": METRIC, "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,

@@ -26,7 +26,8 @@ EXPORTS = [
     "nvfp4_paged_attention_decode_workspace_size", "nvfp4_paged_attention_decode_plan",
     "nvfp4_paged_attention_decode", "nvfp4_paged_attention_decode_fp8", "nvfp4_fp8_to_bf16",
     "nvfp4_paged_attention_prefill_fp8",
-    "nvfp4_paged_attention_prefill", "nvfp4kv_status_string", "nvfp4kv_last_error",
+    "nvfp4_paged_attention_prefill", "nvfp4_quant_activations", "nvfp4_quant_activations_scale_bytes",
+    "nvfp4kv_status_string", "nvfp4kv_last_error",
 ]
 
 
@@ -74,6 +75,8 @@ def library():
                                                          _I32, _I32, _P, _P, _F32, _I32, _P, _P, _P, _SZ, _P]),
             "nvfp4_paged_attention_prefill": (_I32, [_DESC, _P, _I64, _I64, _I32, _P, _I32, _I32, _P, _I32, _P, _I32,
                                                      _I32, _P, _P, _F32, _I32, _P, _P, _SZ, _P]),
+            "nvfp4_quant_activations": (_I32, [_P, _I64, _I64, _I32, _P, _I32, _P, _P, _P]),
+            "nvfp4_quant_activations_scale_bytes": (_I64, [_I64, _I32, _I32]),
             "nvfp4kv_status_string": (ctypes.c_char_p, [_I32]),
             "nvfp4kv_last_error": (ctypes.c_char_p, []),
         }
@@ -252,6 +255,35 @@ def fp8_to_bf16(codes, o_scale, out) -> None:
     if codes.shape != out.shape or not codes.is_contiguous() or not out.is_contiguous():
         raise ValueError("codes and out must be contiguous and of one shape")
     _check(library().nvfp4_fp8_to_bf16(_ptr(codes), codes.numel(), _ptr(o_scale), _ptr(out), _stream()))
+
+
+def quant_activations_scale_bytes(m: int, k: int, swizzled: bool = True) -> int:
+    return int(library().nvfp4_quant_activations_scale_bytes(int(m), int(k), 1 if swizzled else 0))
+
+
+def quant_activations(x, global_scale, swizzled: bool = True, codes=None, scales=None):
+    """bf16 [m, k] -> (codes uint8 [m, k/2], scales uint8): the scales are
+    [m, k/16] row-major, or the flat swizzled 128 x 4 tile buffer."""
+    _dev(x, "x", torch.bfloat16)
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with a contiguous last axis")
+    m, k = x.shape
+    nbytes = quant_activations_scale_bytes(m, k, swizzled)
+    if nbytes < 0:
+        raise ValueError("k must be a positive multiple of 16")
+    if codes is None:
+        codes = torch.empty((m, k // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(nbytes if swizzled else (m, k // 16), dtype=torch.uint8, device=x.device)
+    _dev(codes, "codes", torch.uint8)
+    _dev(scales, "scales", torch.uint8)
+    if codes.shape != (m, k // 2) or not codes.is_contiguous():
+        raise ValueError("codes must be contiguous [m, k/2]")
+    if scales.numel() != nbytes or not scales.is_contiguous():
+        raise ValueError(f"scales must be contiguous with {nbytes} bytes")
+    _check(library().nvfp4_quant_activations(_ptr(x), x.stride(0), m, k, _ptr(global_scale), 1 if swizzled else 0,
+                                             _ptr(codes), _ptr(scales), _stream()))
+    return codes, scales
 
 
 def paged_attention_prefill(pool, q, cu_seqlens_q, max_q_len, block_table, seq_lens, max_seq_len,

@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libnvfp4kv.so")
-SOURCES = ["append.hip", "dequant.hip", "codec.hip", "attn.hip", "api.hip"]
+SOURCES = ["append.hip", "dequant.hip", "codec.hip", "act_quant.hip", "attn.hip", "api.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

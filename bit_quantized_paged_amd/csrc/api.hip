@@ -267,6 +267,34 @@ nvfp4kv_status nvfp4_fp8_to_bf16(const void* in, int64_t n, const float* o_scale
                     "nvfp4_fp8_to_bf16 launch");
 }
 
+int64_t nvfp4_quant_activations_scale_bytes(int64_t m, int32_t k, int32_t swizzled) {
+  if (m < 0 || k <= 0 || k % 16 != 0) return -1;
+  const int64_t nc = k / 16;
+  if (!swizzled) return m * nc;
+  return ((m + 127) / 128) * 128 * ((nc + 3) / 4) * 4;
+}
+
+nvfp4kv_status nvfp4_quant_activations(const void* x, int64_t x_row_stride, int64_t m, int32_t k,
+                                       const float* global_scale, int32_t swizzled, void* codes, void* scales,
+                                       void* stream) {
+  if (k <= 0 || k % 16 != 0) return fail(NVFP4KV_INVALID_ARGUMENT, "k must be a positive multiple of 16");
+  if (m < 0) return fail(NVFP4KV_INVALID_ARGUMENT, "m must be >= 0");
+  if (m == 0) return ok();
+  if (m > INT32_MAX - 128) return fail(NVFP4KV_UNSUPPORTED, "m too large");
+  if (x == nullptr || !aligned(x, 16)) return fail(NVFP4KV_INVALID_ARGUMENT, "x must be a 16-byte aligned pointer");
+  if (x_row_stride < k || x_row_stride % 8 != 0)
+    return fail(NVFP4KV_INVALID_ARGUMENT, "x_row_stride must be a multiple of 8 and >= k");
+  if (global_scale == nullptr) return fail(NVFP4KV_INVALID_ARGUMENT, "global_scale is NULL");
+  if (codes == nullptr || !aligned(codes, 4) || scales == nullptr || !aligned(scales, 4))
+    return fail(NVFP4KV_INVALID_ARGUMENT, "codes and scales must be 4-byte aligned pointers");
+  // one workgroup per 128 rows and 128 columns
+  if (((m + 127) / 128) * ((k + 127) / 128) >= (int64_t)INT32_MAX)
+    return fail(NVFP4KV_UNSUPPORTED, "m * k too large for one call");
+  return hip_status(nvfp4kv::launch_act_quant(x, x_row_stride, (int32_t)m, k, global_scale, codes, scales,
+                                              swizzled != 0, static_cast<hipStream_t>(stream)),
+                    "nvfp4_quant_activations launch");
+}
+
 static nvfp4kv_status prefill_impl(const nvfp4kv_cache* cache, const void* q, int64_t q_stride_token,
                                              int64_t q_stride_head, int32_t num_q_heads,
                                              const int32_t* cu_seqlens_q, int32_t max_q_len, int32_t total_q,

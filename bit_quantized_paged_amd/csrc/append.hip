@@ -4,7 +4,7 @@
 // One lane owns one 16-element block of one (token, kv head, K|V) row, so the
 // block amax needs no cross-lane traffic: it reads 32 bytes of bf16 and
 // writes 8 bytes of codes plus its scale byte.
-#include "device_common.hpp"
+#include "quantize.hpp"
 #include "launch.hpp"
 
 namespace nvfp4kv {

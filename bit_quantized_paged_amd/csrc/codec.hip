@@ -11,7 +11,7 @@
 // Both are HBM-bound streams with one lane per 16-element block (8 code bytes
 // + 1 scale byte <-> 32 bytes of bf16); consecutive lanes take consecutive
 // blocks of one row, so the 32-byte bf16 accesses are coalesced.
-#include "device_common.hpp"
+#include "quantize.hpp"
 #include "launch.hpp"
 
 namespace nvfp4kv {

@@ -88,19 +88,6 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
 
 // ---- E2M1 ----------------------------------------------------------------
 
-// fp32 -> 4-bit code (sign | magnitude index), round to nearest, ties to the
-// even index, |v| > 6 -> 6. The magnitude index counts the midpoints
-// 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5 that |v| has passed. A value exactly on
-// a midpoint goes to the even neighbour, so the test is '>' where the index
-// above the midpoint is odd and '>=' where it is even.
-__device__ __forceinline__ uint32_t e2m1_code(float v) {
-  float a = __builtin_fabsf(v);
-  uint32_t idx = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
-                 (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
-                 (uint32_t)(a > 5.0f);
-  return ((__float_as_uint(v) >> 28) & 8u) | idx;
-}
-
 // Two E2M1 codes in byte `sel` of w -> f16 pair (low nibble first), exact.
 template <int SEL>
 __device__ __forceinline__ h2 fp4x2_to_h2(uint32_t w) {
@@ -116,41 +103,6 @@ __device__ __forceinline__ h2 fp8x2_to_h2(uint32_t w) {
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 // ---- one 16-element block -------------------------------------------------
-
-// The 16 bf16 values of one block (two 16-byte words) -> fp32.
-__device__ __forceinline__ void bf16_block16(u32x4 a, u32x4 b, float (&x)[16]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    x[2 * i] = bf16_lo(a[i]);
-    x[2 * i + 1] = bf16_hi(a[i]);
-    x[8 + 2 * i] = bf16_lo(b[i]);
-    x[8 + 2 * i + 1] = bf16_hi(b[i]);
-  }
-}
-
-// Quantise one block under the per-tensor scale g: returns the E4M3 scale
-// byte and sets the two code words (element 2k in the low nibble of byte k).
-// Each line is a single fp32 operation with round-to-nearest-even: block
-// scale s = E4M3(amax / (6 g)), step d = s * g, r = 1 / d (0 when d = 0),
-// code = E2M1(x * r).
-__device__ __forceinline__ uint32_t quantize_block16(const float (&x)[16], float g, uint32_t& w0, uint32_t& w1) {
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[i]));
-  const float t6 = 6.0f * g;
-  const float s32 = __fdiv_rn(amax, t6);
-  const uint32_t s8 = e4m3_from_f32_sat(s32);
-  const float d = e4m3_to_f32(s8) * g;
-  const float r = (d == 0.0f) ? 0.0f : __fdiv_rn(1.0f, d);
-  w0 = 0;
-  w1 = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    w0 |= e2m1_code(x[i] * r) << (4 * i);
-    w1 |= e2m1_code(x[8 + i] * r) << (4 * i);
-  }
-  return s8;
-}
 
 // Dequantise one block into 8 words of bf16 pairs: codes -> f16 with the
 // hardware FP4 convert, times the E4M3 scale (exact in f16: at most 6

@@ -40,6 +40,8 @@ hipError_t launch_decode(const Pool& pool, int head_size, const void* q, int64_t
 
 // FP8-E4M3 bytes -> bf16: bf16 RNE of fp32(e4m3 * o_scale); n a multiple of 8.
 hipError_t launch_fp8_to_bf16(const void* in, int64_t n, const float* o_scale, void* out, hipStream_t stream);
+hipError_t launch_act_quant(const void* x, int64_t x_row_stride, int32_t m, int32_t k, const float* global_scale,
+                            void* codes, void* scales, bool swizzled, hipStream_t stream);
 
 // Decode kernel a call with these sizes launches on the current device:
 // 1 = one workgroup per (sequence, kv head), 0 = split-K, -1 = bad head size.

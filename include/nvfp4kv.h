@@ -88,9 +88,11 @@ int32_t nvfp4_kv_full_dim(int32_t head_size);
  * slot_mapping: int64 [num_tokens]; token t is written to block
  *   slot / block_size, row slot % block_size. Slots < 0 or >= num_blocks *
  *   block_size are skipped. Slots must be unique within a call.
- * k_scale, v_scale: device fp32 scalars g (> 0, finite), the dequantisation
+ * k_scale, v_scale: device fp32 scalars g (finite, >= 2^-119 so that the
+ *   reciprocal of every non-zero block step is finite), the dequantisation
  *   multipliers. Per 16-element block: s = E4M3_RNE_sat(amax / (6 g)),
  *   codes = E2M1_RNE_sat(x * (1 / (s g))), each step one fp32 RNE operation.
+ *   Key and value values must be finite or infinite, never NaN.
  * num_tokens == 0 is a no-op.
  */
 nvfp4kv_status nvfp4_kv_append(const nvfp4kv_cache* cache,
@@ -294,6 +296,36 @@ nvfp4kv_status nvfp4_paged_attention_prefill_fp8(const nvfp4kv_cache* cache,
                                                  const float* k_scale, const float* v_scale, float sm_scale,
                                                  int32_t causal, const float* o_scale, void* out_fp8,
                                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * NVFP4 quantisation of an activation matrix [P39129 "Implementation
+ * breakdown": the FP4 linear kernels call scaled_fp4_quant(x,
+ * input_global_scale_inv, is_sf_swizzled_layout=True) on their input, and
+ * swizzle_blockscale rearranges block scales into the GEMM's layout]. The
+ * block codec is nvfp4_kv_append's: per 16 consecutive elements of a row,
+ * s = E4M3(amax / (6 g)) and code_i = E2M1(x_i / (s g)), with g the
+ * global_scale (the dequantisation multiplier, x ~ e2m1 * s * g).
+ *
+ * x: bf16 [m, k], row stride x_row_stride ELEMENTS (a multiple of 8, >= k),
+ *   16-byte aligned; k a positive multiple of 16.
+ * global_scale: device fp32 scalar (finite, >= 2^-119); x holds no NaN.
+ * codes: uint8 [m, k/2] contiguous, 4-byte aligned; element 2i of a row in
+ *   the low nibble of byte i.
+ * scales: uint8, 4-byte aligned, nvfp4_quant_activations_scale_bytes(m, k,
+ *   swizzled) bytes. swizzled = 0: row-major [m, k/16]. swizzled = 1: the
+ *   128 x 4 tile layout of block-scaled FP4 GEMM operands: the [m, k/16]
+ *   scale matrix padded with zeros to R = 128 * ceil(m / 128) rows and
+ *   C = 4 * ceil(k / 64) columns; the scale of row r, column c sits at byte
+ *   512 * ((r / 128) * (C / 4) + c / 4) + 16 * (r % 32) + 4 * ((r % 128) / 32)
+ *   + c % 4. Every byte of the buffer, padding included, is written.
+ * m = 0 is a no-op.
+ */
+nvfp4kv_status nvfp4_quant_activations(const void* x, int64_t x_row_stride, int64_t m, int32_t k,
+                                       const float* global_scale, int32_t swizzled, void* codes, void* scales,
+                                       void* stream);
+
+/* Bytes of the scale buffer nvfp4_quant_activations writes (-1 for bad m, k). */
+int64_t nvfp4_quant_activations_scale_bytes(int64_t m, int32_t k, int32_t swizzled);
 
 /* Human-readable name of a status code (static string). */
 const char* nvfp4kv_status_string(nvfp4kv_status status);

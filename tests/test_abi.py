@@ -120,3 +120,24 @@ def test_decode_plan_rejects_bad_sizes():
     assert nvk.decode_plan(-1, 2, 128, 16, 8, 100) == -1
     assert nvk.decode_plan(4, 2, 128, 0, 8, 100) == -1
     assert nvk.decode_plan(4, 2, 128, 16, 0, 100) == -1
+
+
+def test_quant_activations_sizes_and_rejects():
+    lib = nvk.library()
+    assert nvk.quant_activations_scale_bytes(200, 80, True) == 256 * 8
+    assert nvk.quant_activations_scale_bytes(200, 80, False) == 200 * 5
+    assert nvk.quant_activations_scale_bytes(1, 16, True) == 128 * 4
+    assert nvk.quant_activations_scale_bytes(8192, 4096, True) == 8192 * 256
+    assert nvk.quant_activations_scale_bytes(0, 64, True) == 0
+    assert nvk.quant_activations_scale_bytes(4, 40, True) == -1
+    assert nvk.quant_activations_scale_bytes(-1, 64, False) == -1
+    null = ctypes.c_void_p(0)
+    # bad k, negative m, misaligned x: rejected before any device work
+    assert lib.nvfp4_quant_activations(null, 64, 4, 40, null, 1, null, null, null) != 0
+    assert lib.nvfp4_quant_activations(null, 64, -1, 64, null, 1, null, null, null) != 0
+    assert lib.nvfp4_quant_activations(ctypes.c_void_p(8), 64, 4, 64, ctypes.c_void_p(16), 1, ctypes.c_void_p(16),
+                                       ctypes.c_void_p(16), null) != 0
+    assert lib.nvfp4_quant_activations(ctypes.c_void_p(16), 60, 4, 64, ctypes.c_void_p(16), 1, ctypes.c_void_p(16),
+                                       ctypes.c_void_p(16), null) != 0
+    # m = 0 is a no-op that touches nothing
+    assert lib.nvfp4_quant_activations(null, 64, 0, 64, null, 1, null, null, null) == 0

@@ -256,3 +256,20 @@ def make_config(cfg: int, scale: float = 1.0) -> Workload:
                              is_decode=is_decode, num_q_heads=16, num_kv_heads=2, head_size=256,
                              block_size=16, k_outlier_frac=0.01, k_outlier_gain=20.0)
     raise ValueError(f"unknown config {cfg}")
+
+
+def make_activations(seed: int, m: int, k: int, outlier_frac: float = 0.01, outlier_gain: float = 20.0,
+                     token_lognormal_sigma: float = 0.5):
+    """bf16 activation matrix [m, k] as uint16 bits, and its per-tensor scale
+    ``amax / (6 * 448)``. Draw order: outlier channels, per-row magnitudes
+    (lognormal), then fp32 standard normal values rounded to bf16."""
+    rng = np.random.default_rng(seed)
+    gain = np.ones(k, np.float32)
+    n_out = int(round(outlier_frac * k))
+    if n_out:
+        gain[rng.choice(k, n_out, replace=False)] = outlier_gain
+    mag = np.exp(rng.normal(0.0, token_lognormal_sigma, size=(m, 1))).astype(np.float32)
+    x = rng.standard_normal((m, k), dtype=np.float32) * mag * gain
+    bits = _to_bf16_bits(x)
+    g = np.float32(_bf16_bits_absmax(bits) / np.float32(6 * 448))
+    return bits, (g if g != 0 else np.float32(1.0))
