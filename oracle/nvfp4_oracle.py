@@ -48,9 +48,21 @@ def full_dim(head_size: int) -> int:
     return head_size // 2 + head_size // 16
 
 
-def pool_shape(num_blocks: int, block_size: int, num_kv_heads: int, head_size: int):
-    """Logical pool shape (num_blocks, 2, block_size, num_kv_heads, full_dim)."""
-    return (num_blocks, 2, block_size, num_kv_heads, full_dim(head_size))
+# Cache dtypes [P40177 "Key source snippets": the backend's supported KV cache
+# dtypes list fp8 / fp8_e4m3 / fp8_e5m2 beside nvfp4; get_dtype_for_flashinfer
+# maps them to float8_e4m3fn, float8_e5m2 and uint8]. An FP8 row is head_size
+# bytes, one code per element, under the per-tensor scale alone.
+KV_DTYPES = ("nvfp4", "fp8_e4m3", "fp8_e5m2")
+
+
+def row_bytes(head_size: int, kv_dtype: str = "nvfp4") -> int:
+    assert kv_dtype in KV_DTYPES
+    return full_dim(head_size) if kv_dtype == "nvfp4" else head_size
+
+
+def pool_shape(num_blocks: int, block_size: int, num_kv_heads: int, head_size: int, kv_dtype: str = "nvfp4"):
+    """Logical pool shape (num_blocks, 2, block_size, num_kv_heads, row bytes)."""
+    return (num_blocks, 2, block_size, num_kv_heads, row_bytes(head_size, kv_dtype))
 
 
 # ---------------------------------------------------------------------------
@@ -112,6 +124,59 @@ def e4m3_encode_sat(s: np.ndarray) -> np.ndarray:
     code = (e + 6.0) * 8.0 + n
     code = np.where(s >= 448.0, 0x7E, code)
     return code.astype(np.uint8)
+
+
+# OCP E5M2: 1 sign, 5 exponent bits (bias 15), 2 mantissa bits, infinities
+# (0x7C, 0xFC) and NaNs (exponent 31, mantissa != 0); largest finite 57344
+# (0x7B); smallest subnormal 2^-16.
+
+
+def e5m2_decode(b: np.ndarray) -> np.ndarray:
+    """E5M2 byte -> value (float64; +-inf and NaN where the format has them)."""
+    b = np.asarray(b, dtype=np.int64)
+    sign = np.where(b >> 7, -1.0, 1.0)
+    e = (b >> 2) & 31
+    m = b & 3
+    mag = np.where(e == 0, m * 2.0 ** -16, (1.0 + m / 4.0) * np.exp2(e - 15.0))
+    mag = np.where(e == 31, np.where(m == 0, np.inf, np.nan), mag)
+    return sign * mag
+
+
+def _fp8_encode_mag(a: np.ndarray, mbits: int, emin: int, maxv: float, maxcode: int) -> np.ndarray:
+    """Non-negative magnitudes -> FP8 magnitude codes (RNE, saturating to the
+    largest finite value): in binade [2^e, 2^(e+1)), e clamped to >= emin
+    (the subnormal step continues below), the significand count is
+    n = rint(a / 2^(e - mbits)) and the code is (e - emin) * 2^mbits + n."""
+    a = np.minimum(np.asarray(a, dtype=np.float64), maxv)
+    pos = a > 0
+    e = np.floor(np.log2(np.where(pos, a, 1.0)))
+    e = np.where(pos & (np.exp2(e) > a), e - 1, e)
+    e = np.where(pos & (np.exp2(e + 1) <= a), e + 1, e)
+    e = np.where(pos, np.maximum(e, float(emin)), float(emin))
+    n = np.rint(a / np.exp2(e - mbits))
+    code = (e - emin) * 2.0 ** mbits + n
+    return np.minimum(code, maxcode).astype(np.uint8)
+
+
+def fp8_encode(x: np.ndarray, kind: str) -> np.ndarray:
+    """fp32 -> FP8 byte ("e4m3": E4M3FN, "e5m2"), round to nearest, ties to
+    even, magnitudes from the largest finite value up (infinity included)
+    saturate to it; the sign bit is copied from x (-0 -> 0x80). NaN is outside
+    the contract."""
+    x = np.asarray(x, dtype=F32)
+    assert not np.any(np.isnan(x))
+    if kind == "e4m3":
+        mag = _fp8_encode_mag(np.abs(x), 3, -6, 448.0, 0x7E)
+    elif kind == "e5m2":
+        mag = _fp8_encode_mag(np.abs(x), 2, -14, 57344.0, 0x7B)
+    else:
+        raise ValueError(kind)
+    sign = (x.view(np.uint32) >> np.uint32(31)).astype(np.uint8)
+    return (sign << np.uint8(7)) | mag
+
+
+def fp8_decode(b: np.ndarray, kind: str) -> np.ndarray:
+    return e4m3_decode(b) if kind == "e4m3" else e5m2_decode(b)
 
 
 # ---------------------------------------------------------------------------
@@ -180,6 +245,34 @@ def quantize_rows(x_bits: np.ndarray, g) -> np.ndarray:
     return np.concatenate([data, s8], axis=-1)
 
 
+def quantize_rows_fp8(x_bits: np.ndarray, g, kind: str) -> np.ndarray:
+    """bf16 rows [..., D] -> FP8 rows [..., D] (uint8) under the per-tensor
+    scale g: code = FP8(RN32(x / g)), one fp32 division per element."""
+    x = bf16_to_f32(x_bits)
+    with np.errstate(over="ignore"):  # an overflowed quotient saturates
+        q = (x / F32(g)).astype(F32)
+    return fp8_encode(q, kind)
+
+
+def dequantize_rows_fp8(rows: np.ndarray, g, kind: str) -> np.ndarray:
+    """FP8 rows [..., D] -> fp32 values RN32(fp8 * g)."""
+    return (fp8_decode(rows, kind).astype(F32) * F32(g)).astype(F32)
+
+
+def quantize_kv(x_bits: np.ndarray, g, kv_dtype: str = "nvfp4") -> np.ndarray:
+    """Rows as the cache of kv_dtype stores them."""
+    if kv_dtype == "nvfp4":
+        return quantize_rows(x_bits, g)
+    return quantize_rows_fp8(x_bits, g, kv_dtype[4:])
+
+
+def dequantize_kv(rows: np.ndarray, g, head_size: int, kv_dtype: str = "nvfp4") -> np.ndarray:
+    """Stored rows of a cache of kv_dtype -> fp32 values."""
+    if kv_dtype == "nvfp4":
+        return dequantize_rows(rows, g, head_size)
+    return dequantize_rows_fp8(rows, g, kv_dtype[4:])
+
+
 def dequantize_rows(rows: np.ndarray, g, head_size: int) -> np.ndarray:
     """Packed rows [..., full_dim] -> fp32 values [..., D]:
     x = fp32( (E2M1(code) * E4M3(scale)) * g ); the inner product is exact."""
@@ -195,7 +288,7 @@ def dequantize_rows(rows: np.ndarray, g, head_size: int) -> np.ndarray:
 
 
 def append(pool: np.ndarray, key_bits: np.ndarray, value_bits: np.ndarray,
-           slot_mapping: np.ndarray, k_scale, v_scale) -> np.ndarray:
+           slot_mapping: np.ndarray, k_scale, v_scale, kv_dtype: str = "nvfp4") -> np.ndarray:
     """Slot-mapping writer on a logical pool (num_blocks, 2, bs, Hkv, fd).
 
     Token t goes to block slot // bs, row slot % bs; K at index 0 and V at 1
@@ -208,8 +301,8 @@ def append(pool: np.ndarray, key_bits: np.ndarray, value_bits: np.ndarray,
     slots = slots[ok]
     if slots.size == 0:
         return pool
-    kq = quantize_rows(np.asarray(key_bits)[ok], k_scale)
-    vq = quantize_rows(np.asarray(value_bits)[ok], v_scale)
+    kq = quantize_kv(np.asarray(key_bits)[ok], k_scale, kv_dtype)
+    vq = quantize_kv(np.asarray(value_bits)[ok], v_scale, kv_dtype)
     pool[slots // bs, 0, slots % bs] = kq
     pool[slots // bs, 1, slots % bs] = vq
     return pool
@@ -224,15 +317,15 @@ def gather_rows(pool: np.ndarray, block_table_row: np.ndarray, length: int, kv: 
 
 
 def dequant_paged(pool: np.ndarray, block_table: np.ndarray, seq_lens: np.ndarray,
-                  k_scale, v_scale, head_size: int):
+                  k_scale, v_scale, head_size: int, kv_dtype: str = "nvfp4"):
     """Paged dequantize [RFC47684 "Fix steps": nvfp4_kv_dequantize_paged]:
     every sequence's keys and values gathered through the block table and
     written, one sequence after another, as bf16 [sum(seq_lens), Hkv, D]."""
     ks, vs = [], []
     for b in range(len(seq_lens)):
         L = int(seq_lens[b])
-        ks.append(f32_to_bf16(dequantize_rows(gather_rows(pool, block_table[b], L, 0), k_scale, head_size)))
-        vs.append(f32_to_bf16(dequantize_rows(gather_rows(pool, block_table[b], L, 1), v_scale, head_size)))
+        ks.append(f32_to_bf16(dequantize_kv(gather_rows(pool, block_table[b], L, 0), k_scale, head_size, kv_dtype)))
+        vs.append(f32_to_bf16(dequantize_kv(gather_rows(pool, block_table[b], L, 1), v_scale, head_size, kv_dtype)))
     hkv = pool.shape[3]
     empty = np.zeros((0, hkv, head_size), np.uint16)
     return (np.concatenate(ks) if ks else empty, np.concatenate(vs) if vs else empty)
@@ -276,7 +369,7 @@ def qdq_rows(x_bits: np.ndarray, g, head_size: int) -> np.ndarray:
 
 def paged_attention(pool: np.ndarray, query_bits: np.ndarray, cu_q: np.ndarray,
                     block_table: np.ndarray, seq_lens: np.ndarray, k_scale, v_scale,
-                    sm_scale, head_size: int, causal: bool = True) -> np.ndarray:
+                    sm_scale, head_size: int, causal: bool = True, kv_dtype: str = "nvfp4") -> np.ndarray:
     """Softmax attention of each sequence's queries over all of its cached keys.
 
     Sequence b has L = seq_lens[b] keys and q = cu_q[b+1] - cu_q[b] queries,
@@ -298,8 +391,8 @@ def paged_attention(pool: np.ndarray, query_bits: np.ndarray, cu_q: np.ndarray,
         nq = q1 - q0
         if nq == 0 or L == 0:
             continue
-        K = dequantize_rows(gather_rows(pool, block_table[b], L, 0), k_scale, D).astype(np.float64)
-        V = dequantize_rows(gather_rows(pool, block_table[b], L, 1), v_scale, D).astype(np.float64)
+        K = dequantize_kv(gather_rows(pool, block_table[b], L, 0), k_scale, D, kv_dtype).astype(np.float64)
+        V = dequantize_kv(gather_rows(pool, block_table[b], L, 1), v_scale, D, kv_dtype).astype(np.float64)
         if causal:
             limit = L - nq + np.arange(nq)               # last visible key per query
             visible = np.arange(L)[None, :] <= limit[:, None]
