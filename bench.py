@@ -57,6 +57,29 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def exact_decode(wd, sm_scale, dev):
+    """fp32 softmax attention of each decode query over its sequence's
+    unquantised bf16 keys and values (the accuracy yardstick for the cache
+    formats; plain torch, not the oracle)."""
+    import numpy as np
+    import torch
+    B, Hq, D = wd.query.shape
+    Hkv = wd.key.shape[1]
+    grp = Hq // Hkv
+    f32 = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16).float()
+    q = f32(wd.query)
+    out = torch.zeros((B, Hq, D), dtype=torch.float32, device=dev)
+    for b in range(B):
+        t0, t1 = int(wd.token_offsets[b]), int(wd.token_offsets[b + 1])
+        if t1 == t0:
+            continue
+        k = f32(wd.key[t0:t1]).repeat_interleave(grp, dim=1).permute(1, 2, 0).contiguous()   # [Hq, D, L]
+        v = f32(wd.value[t0:t1]).repeat_interleave(grp, dim=1).permute(1, 0, 2).contiguous()  # [Hq, L, D]
+        p = torch.softmax(torch.bmm(q[b][:, None, :], k) * sm_scale, dim=-1)                   # [Hq, 1, L]
+        out[b] = torch.bmm(p, v)[:, 0, :]
+    return out
+
+
 def read_traffic(kernel: str, workload: str):
     """HBM bytes per decode launch from the committed counter summary, if it
     was taken on the current kernel sources (else None)."""
@@ -85,7 +108,7 @@ def main():
     import torch
 
     import bit_quantized_paged_amd as nvk
-    from workloads import make_activations, make_config
+    from workloads import fp8_kv_scales, make_activations, make_config
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
@@ -315,6 +338,44 @@ def main():
     codec["act_quant_shape"] = [am, ak]
     del a_codes, a_sf
 
+    # ---- the same decode over FP8 caches (E4M3, E5M2) of the same K/V, with
+    # the per-tensor scale amax / largest finite value: the kernel-level
+    # NVFP4-vs-FP8 comparison (reported, not part of the step)
+    if wd is not None:
+        exact = exact_decode(wd, sm_scale, dev)
+
+        def err_vs_exact(o):
+            e = (o.float() - exact).abs()
+            return {"max_abs": round(float(e.max()), 5), "rms": round(float(e.pow(2).mean().sqrt()), 6)}
+
+        codec["nvfp4_decode_err_vs_exact"] = err_vs_exact(ref_d)
+        fp8 = {}
+        all_k, all_v, all_s = bf(w.key), bf(w.value), i64(w.slot_mapping)
+        for kv in ("fp8_e4m3", "fp8_e5m2"):
+            ks8, vs8 = fp8_kv_scales(w, kv)
+            ks8_t = torch.tensor([float(ks8)], dtype=torch.float32, device=dev)
+            vs8_t = torch.tensor([float(vs8)], dtype=torch.float32, device=dev)
+            b8 = torch.zeros((w.num_blocks, 2, Hkv, bs, D), dtype=nvk.KV_DTYPES[kv][1], device=dev)
+            nvk.append(b8.permute(0, 1, 3, 2, 4), all_k, all_v, all_s, ks8_t, vs8_t)
+            n8 = max(2, math.ceil(3 * MALL_BYTES / b8.numel()))
+            p8s = [b8.permute(0, 1, 3, 2, 4)] + [b8.clone().permute(0, 1, 3, 2, 4) for _ in range(n8 - 1)]
+            out8 = torch.empty_like(outd)
+            g8 = capture(lambda r: nvk.paged_attention_decode(p8s[r % n8], qd, btd, sld, maxd, ks8_t, vs8_t,
+                                                              sm_scale, out8, wsd), n=n8)
+            t8, _ = time_graph(g8, reps=3)
+            del g8
+            torch.cuda.synchronize()
+            b8_bytes = (int(wd.seq_lens.astype(np.int64).sum()) * Hkv * 2 * D + 2 * wd.num_seqs * Hq * D * 2
+                        + 4 * int(np.sum((wd.seq_lens + bs - 1) // bs)) + 4 * wd.num_seqs)
+            plan8 = nvk.decode_plan(wd.num_seqs, Hkv, D, bs, int(wd.block_table.shape[1]), maxd, kv)
+            fp8[kv] = {"decode_us": round(t8 / K * 1e6, 2), "gbs": round(b8_bytes / (t8 / K) / 1e9, 1),
+                       "cache_bytes_per_launch": b8_bytes, "pool_copies": n8,
+                       "kernel": "decode_pair_kernel" if plan8 == nvk.DECODE_PER_PAIR else "decode_split_kernel",
+                       "time_vs_nvfp4": round(t8 / res["decode_s"], 3), "err_vs_exact": err_vs_exact(out8)}
+            del p8s, b8, out8
+        codec["fp8_kv_decode"] = fp8
+        del all_k, all_v, all_s
+
     # ---- algorithmic work
     out = {"metric": METRIC, "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
            "ms_per_step": round(step_wall_s / K * 1e3, 5), "higher_is_better": True, "scaling": "weak",
@@ -333,7 +394,7 @@ def main():
         out["value"] = round(gbs, 1)
         extra.update({"decode_us": round(dec_s * 1e6, 2), "decode_pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
                       "decode_bytes": dec_bytes})
-        plan = nvk.decode_plan(wd.num_seqs, Hkv, D, bs, int(wd.block_table.shape[1]), maxd)
+        plan = nvk.decode_plan(wd.num_seqs, Hkv, D, bs, int(wd.block_table.shape[1]), maxd, "nvfp4")
         dec_kernel = "decode_pair_kernel" if plan == nvk.DECODE_PER_PAIR else "decode_split_kernel"
         traffic = read_traffic(dec_kernel, args.workload)
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -40,7 +40,7 @@ class NVFP4KVError(RuntimeError):
 class CacheDesc(ctypes.Structure):
     _fields_ = [
         ("data", ctypes.c_void_p), ("num_blocks", ctypes.c_int64), ("block_size", ctypes.c_int32),
-        ("num_kv_heads", ctypes.c_int32), ("head_size", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32), ("head_size", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
         ("stride_block", ctypes.c_int64), ("stride_kv", ctypes.c_int64), ("stride_token", ctypes.c_int64),
         ("stride_head", ctypes.c_int64),
     ]
@@ -65,7 +65,7 @@ def library():
             "nvfp4_kv_dequant_pages": (_I32, [_DESC, _P, _I32, _P, _P, _P, _I64, _I64, _I64, _I64, _P]),
             "nvfp4_kv_qdq": (_I32, [_P, _I64, _I64, _P, _I64, _I64, _I64, _I32, _I32, _P, _P, _P]),
             "nvfp4_paged_attention_decode_workspace_size": (_SZ, [_I32, _I32, _I32, _I32]),
-            "nvfp4_paged_attention_decode_plan": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32]),
+            "nvfp4_paged_attention_decode_plan": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
             "nvfp4_paged_attention_decode": (_I32, [_DESC, _P, _I64, _I64, _I32, _P, _I32, _P, _I32, _I32, _P, _P,
                                                     _F32, _P, _P, _SZ, _P]),
             "nvfp4_paged_attention_decode_fp8": (_I32, [_DESC, _P, _I64, _I64, _I32, _P, _I32, _P, _I32, _I32, _P,
@@ -113,31 +113,56 @@ def full_dim(head_size: int) -> int:
     return int(library().nvfp4_kv_full_dim(head_size))
 
 
+# Cache formats and the torch dtype of their pools [P40177 "Key source
+# snippets", get_dtype_for_flashinfer: fp8_e4m3 -> float8_e4m3fn, fp8_e5m2 ->
+# float8_e5m2, nvfp4 -> uint8 holding packed FP4 data and FP8 block scales].
+KV_NVFP4, KV_FP8_E4M3, KV_FP8_E5M2 = 0, 1, 2
+KV_DTYPES = {"nvfp4": (KV_NVFP4, torch.uint8), "fp8_e4m3": (KV_FP8_E4M3, torch.float8_e4m3fn),
+             "fp8_e5m2": (KV_FP8_E5M2, torch.float8_e5m2)}
+_KV_OF_TORCH = {dt: code for code, dt in KV_DTYPES.values()}
+
+
+def row_bytes(head_size: int, kv_dtype: str = "nvfp4") -> int:
+    return head_size // 2 + head_size // 16 if kv_dtype == "nvfp4" else head_size
+
+
 def alloc_pool(num_blocks: int, block_size: int, num_kv_heads: int, head_size: int,
-               layout: str = "HND", device="cuda") -> torch.Tensor:
-    """Zeroed uint8 pool, returned as the logical view (num_blocks, 2,
-    block_size, num_kv_heads, full_dim). ``layout`` picks the physical order:
-    "HND" stores (num_blocks, 2, num_kv_heads, block_size, full_dim)."""
-    fd = head_size // 2 + head_size // 16
+               layout: str = "HND", device="cuda", kv_dtype: str = "nvfp4") -> torch.Tensor:
+    """Zeroed pool, returned as the logical view (num_blocks, 2, block_size,
+    num_kv_heads, row bytes) in the torch dtype of its format (uint8 for
+    NVFP4, float8_e4m3fn / float8_e5m2 for FP8). ``layout`` picks the
+    physical order: "HND" stores (num_blocks, 2, num_kv_heads, block_size, row)."""
+    fd = row_bytes(head_size, kv_dtype)
+    dt = KV_DTYPES[kv_dtype][1]
     if layout == "HND":
-        return torch.zeros((num_blocks, 2, num_kv_heads, block_size, fd), dtype=torch.uint8,
+        return torch.zeros((num_blocks, 2, num_kv_heads, block_size, fd), dtype=dt,
                            device=device).permute(0, 1, 3, 2, 4)
     if layout == "NHD":
-        return torch.zeros((num_blocks, 2, block_size, num_kv_heads, fd), dtype=torch.uint8, device=device)
+        return torch.zeros((num_blocks, 2, block_size, num_kv_heads, fd), dtype=dt, device=device)
     raise ValueError(layout)
 
 
+def kv_dtype_of(pool: torch.Tensor) -> int:
+    if pool.dtype not in _KV_OF_TORCH:
+        raise ValueError(f"pool dtype {pool.dtype} is not a cache format (uint8, float8_e4m3fn, float8_e5m2)")
+    return _KV_OF_TORCH[pool.dtype]
+
+
 def _desc(pool: torch.Tensor) -> CacheDesc:
-    _dev(pool, "pool", torch.uint8)
+    _dev(pool, "pool")
+    kv = kv_dtype_of(pool)
     if pool.dim() != 5 or pool.shape[1] != 2 or pool.stride(4) != 1:
-        raise ValueError("pool must be a (num_blocks, 2, block_size, num_kv_heads, full_dim) uint8 view "
+        raise ValueError("pool must be a (num_blocks, 2, block_size, num_kv_heads, row) view "
                          "with a contiguous last axis")
     nb, _, bs, hkv, fd = pool.shape
-    D = fd * 16 // 9
-    if D // 2 + D // 16 != fd:
-        raise ValueError(f"last axis {fd} is not a packed NVFP4 row width")
+    if kv == KV_NVFP4:
+        D = fd * 16 // 9
+        if D // 2 + D // 16 != fd:
+            raise ValueError(f"last axis {fd} is not a packed NVFP4 row width")
+    else:
+        D = fd
     st = pool.stride()
-    return CacheDesc(pool.data_ptr(), nb, bs, hkv, D, 0, st[0], st[1], st[2], st[3])
+    return CacheDesc(pool.data_ptr(), nb, bs, hkv, D, kv, st[0], st[1], st[2], st[3])
 
 
 def append(pool, key, value, slot_mapping, k_scale, v_scale) -> None:
@@ -214,11 +239,12 @@ DECODE_SPLIT_K, DECODE_PER_PAIR = 0, 1
 
 
 def decode_plan(num_seqs: int, num_kv_heads: int, head_size: int, block_size: int, max_blocks_per_seq: int,
-                max_seq_len: int) -> int:
+                max_seq_len: int, kv_dtype: str = "nvfp4") -> int:
     """Which decode kernel a call with these sizes launches on the current
     device: DECODE_PER_PAIR, DECODE_SPLIT_K, or -1 for an unsupported head size."""
     return int(library().nvfp4_paged_attention_decode_plan(num_seqs, num_kv_heads, head_size, block_size,
-                                                            max_blocks_per_seq, max_seq_len))
+                                                            max_blocks_per_seq, max_seq_len,
+                                                            KV_DTYPES[kv_dtype][0]))
 
 
 def paged_attention_decode(pool, q, block_table, seq_lens, max_seq_len, k_scale, v_scale, sm_scale,

@@ -30,10 +30,11 @@ nvfp4kv_status hip_status(hipError_t e, const char* what) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-nvfp4kv_status check_cache(const nvfp4kv_cache* c, nvfp4kv::Pool& p) {
+nvfp4kv_status check_cache(const nvfp4kv_cache* c, nvfp4kv::Pool& p, int* fmt = nullptr) {
   if (c == nullptr) return fail(NVFP4KV_INVALID_ARGUMENT, "cache descriptor is NULL");
   if (c->data == nullptr) return fail(NVFP4KV_INVALID_ARGUMENT, "cache data is NULL");
-  if (c->reserved != 0) return fail(NVFP4KV_INVALID_ARGUMENT, "cache.reserved must be 0");
+  if (c->kv_dtype != NVFP4KV_KV_NVFP4 && c->kv_dtype != NVFP4KV_KV_FP8_E4M3 && c->kv_dtype != NVFP4KV_KV_FP8_E5M2)
+    return fail(NVFP4KV_INVALID_ARGUMENT, "cache.kv_dtype %d is not a cache format", c->kv_dtype);
   if (c->head_size != 64 && c->head_size != 128 && c->head_size != 256)
     return fail(NVFP4KV_UNSUPPORTED, "head_size %d not supported (64, 128, 256)", c->head_size);
   if (c->block_size != 16 && c->block_size != 32 && c->block_size != 64)
@@ -47,6 +48,10 @@ nvfp4kv_status check_cache(const nvfp4kv_cache* c, nvfp4kv::Pool& p) {
   for (int k = 0; k < 4; ++k)
     if (s[k] < 0 || s[k] % 4 != 0)
       return fail(NVFP4KV_INVALID_ARGUMENT, "cache strides must be non-negative multiples of 4 bytes");
+  if (c->kv_dtype != NVFP4KV_KV_NVFP4)
+    for (int k = 0; k < 4; ++k)
+      if (s[k] % 16 != 0)
+        return fail(NVFP4KV_INVALID_ARGUMENT, "FP8 cache strides must be multiples of 16 bytes");
   // rows of a page are addressed with 32-bit offsets
   if (c->stride_token > (1 << 26)) return fail(NVFP4KV_UNSUPPORTED, "stride_token above 2^26 bytes");
   // the decode copies address a page's K and V rows from one 32-bit window
@@ -60,6 +65,8 @@ nvfp4kv_status check_cache(const nvfp4kv_cache* c, nvfp4kv::Pool& p) {
   p.bs = c->block_size;
   p.bs_log2 = c->block_size == 16 ? 4 : (c->block_size == 32 ? 5 : 6);
   p.hkv = c->num_kv_heads;
+  if (fmt) *fmt = c->kv_dtype == NVFP4KV_KV_NVFP4 ? nvfp4kv::kNvfp4
+                  : c->kv_dtype == NVFP4KV_KV_FP8_E4M3 ? nvfp4kv::kFp8E4M3 : nvfp4kv::kFp8E5M2;
   return ok();
 }
 
@@ -98,7 +105,8 @@ nvfp4kv_status nvfp4_kv_append(const nvfp4kv_cache* cache, const void* key, int6
                                int64_t value_stride_head, const int64_t* slot_mapping, int64_t num_tokens,
                                const float* k_scale, const float* v_scale, void* stream) {
   nvfp4kv::Pool p;
-  nvfp4kv_status s = check_cache(cache, p);
+  int fmt = 0;
+  nvfp4kv_status s = check_cache(cache, p, &fmt);
   if (s) return s;
   if (num_tokens < 0) return fail(NVFP4KV_INVALID_ARGUMENT, "num_tokens must be >= 0");
   if (num_tokens == 0) return ok();
@@ -110,7 +118,7 @@ nvfp4kv_status nvfp4_kv_append(const nvfp4kv_cache* cache, const void* key, int6
   if (lanes / 256 >= (int64_t)INT32_MAX) return fail(NVFP4KV_UNSUPPORTED, "too many tokens for one call");
   return hip_status(nvfp4kv::launch_append(p, cache->head_size, key, key_stride_token, key_stride_head, value,
                                            value_stride_token, value_stride_head, slot_mapping, num_tokens,
-                                           k_scale, v_scale, static_cast<hipStream_t>(stream)),
+                                           k_scale, v_scale, fmt, static_cast<hipStream_t>(stream)),
                     "nvfp4_kv_append launch");
 }
 
@@ -120,7 +128,8 @@ nvfp4kv_status nvfp4_kv_dequant_paged(const nvfp4kv_cache* cache, const int32_t*
                                       const float* k_scale, const float* v_scale, void* out_key,
                                       void* out_value, int64_t out_rows, void* stream) {
   nvfp4kv::Pool p;
-  nvfp4kv_status s = check_cache(cache, p);
+  int fmt = 0;
+  nvfp4kv_status s = check_cache(cache, p, &fmt);
   if (s) return s;
   if (num_seqs < 0 || num_seqs > 65535) return fail(NVFP4KV_INVALID_ARGUMENT, "num_seqs must be in [0, 65535]");
   if (num_seqs == 0 || max_seq_len <= 0 || out_rows <= 0) return ok();
@@ -132,7 +141,7 @@ nvfp4kv_status nvfp4_kv_dequant_paged(const nvfp4kv_cache* cache, const int32_t*
     return fail(NVFP4KV_INVALID_ARGUMENT, "outputs must be 16-byte aligned");
   return hip_status(nvfp4kv::launch_dequant(p, cache->head_size, block_table, max_blocks_per_seq, seq_lens,
                                             cu_seqlens_out, num_seqs, max_seq_len, k_scale, v_scale, out_key,
-                                            out_value, out_rows, static_cast<hipStream_t>(stream)),
+                                            out_value, out_rows, fmt, static_cast<hipStream_t>(stream)),
                     "nvfp4_kv_dequant_paged launch");
 }
 
@@ -141,8 +150,10 @@ nvfp4kv_status nvfp4_kv_dequant_pages(const nvfp4kv_cache* cache, const int32_t*
                                       int64_t out_stride_block, int64_t out_stride_kv, int64_t out_stride_token,
                                       int64_t out_stride_head, void* stream) {
   nvfp4kv::Pool p;
-  nvfp4kv_status s = check_cache(cache, p);
+  int fmt = 0;
+  nvfp4kv_status s = check_cache(cache, p, &fmt);
   if (s) return s;
+  if (fmt != nvfp4kv::kNvfp4) return fail(NVFP4KV_UNSUPPORTED, "page-form dequantize is for NVFP4 caches");
   if (num_pages < 0) return fail(NVFP4KV_INVALID_ARGUMENT, "num_pages must be >= 0");
   if (num_pages == 0) return ok();
   if (!k_scale || !v_scale) return fail(NVFP4KV_INVALID_ARGUMENT, "k_scale/v_scale is NULL");
@@ -187,9 +198,15 @@ size_t nvfp4_paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num
 }
 
 int32_t nvfp4_paged_attention_decode_plan(int32_t num_seqs, int32_t num_kv_heads, int32_t head_size,
-                                          int32_t block_size, int32_t max_blocks_per_seq, int32_t max_seq_len) {
+                                          int32_t block_size, int32_t max_blocks_per_seq, int32_t max_seq_len,
+                                          int32_t kv_dtype) {
   if (num_seqs < 0 || num_kv_heads < 1 || block_size < 1 || max_blocks_per_seq < 1) return -1;
-  return nvfp4kv::decode_plan(num_seqs, num_kv_heads, head_size, block_size, max_blocks_per_seq, max_seq_len);
+  const int fmt = kv_dtype == NVFP4KV_KV_NVFP4      ? nvfp4kv::kNvfp4
+                  : kv_dtype == NVFP4KV_KV_FP8_E4M3 ? nvfp4kv::kFp8E4M3
+                  : kv_dtype == NVFP4KV_KV_FP8_E5M2 ? nvfp4kv::kFp8E5M2
+                                                    : -1;
+  if (fmt < 0) return -1;
+  return nvfp4kv::decode_plan(num_seqs, num_kv_heads, head_size, block_size, max_blocks_per_seq, max_seq_len, fmt);
 }
 
 static nvfp4kv_status decode_impl(const nvfp4kv_cache* cache, const void* q, int64_t q_stride_token,
@@ -200,7 +217,8 @@ static nvfp4kv_status decode_impl(const nvfp4kv_cache* cache, const void* q, int
                                             const float* o_scale, void* out, void* workspace,
                                             size_t workspace_bytes, void* stream) {
   nvfp4kv::Pool p;
-  nvfp4kv_status s = check_cache(cache, p);
+  int fmt = 0;
+  nvfp4kv_status s = check_cache(cache, p, &fmt);
   if (s) return s;
   if (num_seqs < 0 || num_seqs > nvfp4kv::kDecodeMaxSeqs)
     return fail(NVFP4KV_UNSUPPORTED, "num_seqs must be in [0, %d]", nvfp4kv::kDecodeMaxSeqs);
@@ -219,7 +237,7 @@ static nvfp4kv_status decode_impl(const nvfp4kv_cache* cache, const void* q, int
   if (!block_table || !seq_lens) return fail(NVFP4KV_INVALID_ARGUMENT, "metadata pointer is NULL");
   if (!k_scale || !v_scale) return fail(NVFP4KV_INVALID_ARGUMENT, "k_scale/v_scale is NULL");
   if (out == nullptr || !aligned(out, 16)) return fail(NVFP4KV_INVALID_ARGUMENT, "out must be a 16-byte aligned pointer");
-  if (nvfp4kv::decode_lds_bytes(num_seqs, grp, cache->head_size) > 163840)
+  if (nvfp4kv::decode_lds_bytes(num_seqs, grp, cache->head_size, fmt) > 163840)
     return fail(NVFP4KV_UNSUPPORTED, "num_seqs / group size / head_size combination exceeds the LDS budget");
   const size_t need = nvfp4kv::decode_workspace_bytes(num_seqs, num_q_heads, p.hkv, cache->head_size);
   if (workspace == nullptr || workspace_bytes < need)
@@ -227,7 +245,7 @@ static nvfp4kv_status decode_impl(const nvfp4kv_cache* cache, const void* q, int
   if (!aligned(workspace, 16)) return fail(NVFP4KV_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
   return hip_status(nvfp4kv::launch_decode(p, cache->head_size, q, q_stride_token, q_stride_head, num_q_heads,
                                            block_table, max_blocks_per_seq, seq_lens, num_seqs, max_seq_len,
-                                           k_scale, v_scale, sm_scale, o_scale, out, workspace,
+                                           k_scale, v_scale, sm_scale, o_scale, out, workspace, fmt,
                                            static_cast<hipStream_t>(stream)),
                     "nvfp4_paged_attention_decode launch");
 }
@@ -306,8 +324,10 @@ static nvfp4kv_status prefill_impl(const nvfp4kv_cache* cache, const void* q, in
   (void)workspace;
   (void)workspace_bytes;
   nvfp4kv::Pool p;
-  nvfp4kv_status s = check_cache(cache, p);
+  int fmt = 0;
+  nvfp4kv_status s = check_cache(cache, p, &fmt);
   if (s) return s;
+  if (fmt != nvfp4kv::kNvfp4) return fail(NVFP4KV_UNSUPPORTED, "chunked prefill reads NVFP4 caches only");
   if (num_seqs < 0 || num_seqs > 65535) return fail(NVFP4KV_INVALID_ARGUMENT, "num_seqs must be in [0, 65535]");
   if (num_q_heads < 1 || num_q_heads % p.hkv != 0)
     return fail(NVFP4KV_INVALID_ARGUMENT, "num_q_heads must be a positive multiple of num_kv_heads");

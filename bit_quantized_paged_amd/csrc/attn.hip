@@ -240,10 +240,18 @@ __device__ void combine_splits(const DecodeArgs& a, int b, int h, int64_t slot0,
 
 // How a decode kernel streams pages into its per-wave ring of NS LDS stages
 // (see attn_core.hpp):
-//  kModeDmaCompact: contiguous 16-byte aligned rows: 16-byte global->LDS copies;
-//  kModeDmaGeneral: any row stride: 4-byte global->LDS copies.
+//  kModeDmaCompact: NVFP4, contiguous 16-byte aligned rows: 16-byte
+//    global->LDS copies;
+//  kModeDmaGeneral: NVFP4, any row stride: 4-byte global->LDS copies;
+//  kModeFp8E4M3, kModeFp8E5M2: FP8 rows (16-byte strides): 16-byte copies.
 constexpr int kModeDmaGeneral = 0;
 constexpr int kModeDmaCompact = 1;
+constexpr int kModeFp8E4M3 = 2;
+constexpr int kModeFp8E5M2 = 3;
+
+constexpr int mode_fmt(int mode) {
+  return mode == kModeFp8E4M3 ? kFp8E4M3 : mode == kModeFp8E5M2 ? kFp8E5M2 : kNvfp4;
+}
 
 // Stages of the per-wave LDS ring (DMA modes): enough bytes in flight per CU
 // while several workgroups fit in the 160 KB of LDS.
@@ -261,7 +269,7 @@ struct SplitWaves {
 template <int D, int MODE>
 struct DecodeLds {
   static constexpr int NW = SplitWaves<D>::NW;
-  static constexpr int dma_stage = StageGeo<D, MODE == kModeDmaCompact>::STAGE;
+  static constexpr int dma_stage = StageGeo<D, MODE == kModeDmaCompact, mode_fmt(MODE)>::STAGE;
   static constexpr int stream = NW * DecodeStages<D>::NS * dma_stage;
   static constexpr int merge = NW * kMergeCols * D * 4;
   static constexpr int area = stream > merge ? stream : merge;  // streams, then merge and combine scratch
@@ -280,26 +288,26 @@ struct DecodeOcc {
 // is issued first so that it is in flight with the block-table reads the
 // first copies wait for. Leaves the wave's softmax state in W; every copy has
 // landed when it returns.
-template <int D, bool COMPACT, int NS, int NWS>
-__device__ __forceinline__ void decode_stream(WaveAttn<D, 1>& W, uint8_t* ring, const Pool& pool,
+template <int D, bool COMPACT, int FMT, int NS, int NWS>
+__device__ __forceinline__ void decode_stream(WaveAttn<D, 1, FMT>& W, uint8_t* ring, const Pool& pool,
                                               const int32_t* bt_row, int L, int h, int k0, int st1,
                                               const uint16_t* qrow, float qk_factor,
-                                              const DmaOffsets<D, COMPACT>& dof, const LdsLane& ll, int j) {
-  using SG = StageGeo<D, COMPACT>;
-  const auto qraw = WaveAttn<D, 1>::load_q_raw(qrow, j);
-  StepIds nxt = lds_prologue<D, COMPACT, NS>(ring, k0, NWS, st1, bt_row, L, pool, h, dof);
+                                              const DmaOffsets<D, COMPACT, FMT>& dof, const LdsLane& ll, int j) {
+  using SG = StageGeo<D, COMPACT, FMT>;
+  const auto qraw = WaveAttn<D, 1, FMT>::load_q_raw(qrow, j);
+  StepIds nxt = lds_prologue<D, COMPACT, NS, FMT>(ring, k0, NWS, st1, bt_row, L, pool, h, dof);
   W.set_q(0, qraw, qk_factor);
   int slot = 0;
   for (int k = k0; k < st1; k += NWS) {
     const int fill = (slot + NS - 1) % NS;
-    dma_step<D, COMPACT>(ring + fill * SG::STAGE, pool, nxt, h, (k + (NS - 1) * NWS) * kStep, dof);
+    dma_step<D, COMPACT, FMT>(ring + fill * SG::STAGE, pool, nxt, h, (k + (NS - 1) * NWS) * kStep, dof);
     nxt = ids_for_step(bt_row, k + NS * NWS, st1, L, pool);
     wait_vmcnt<(NS - 1) * SG::NC>();
-    SubRaw<D> R[2];
-    lds_read_step_async_safe<D>(R, ring + slot * SG::STAGE, ll);
+    SubRaw<D, FMT> R[2];
+    lds_read_step<D, FMT>(R, ring + slot * SG::STAGE, ll);
     const int kb = k * kStep;
     const bool partial = kb + kStep > L;
-    if (partial) mask_step<D>(R, kb, L, j);
+    if (partial) mask_step(R, kb, L, j);
     W.step(R, kb, j, partial);
     slot = (slot + 1 == NS) ? 0 : slot + 1;
   }
@@ -311,9 +319,9 @@ __device__ __forceinline__ void decode_stream(WaveAttn<D, 1>& W, uint8_t* ring, 
 // rings), kMergeCols columns at a time. emit(col, d, on, M, lt) gets every
 // output element: on = o / lt (0 when lt == 0), with the column's merged max
 // M and sum lt.
-template <int D, int NWS, typename Emit>
-__device__ __forceinline__ void merge_waves(const WaveAttn<D, 1>& W, float* s_ml, float* s_o, int grp, int w, int i,
-                                            int j, Emit&& emit) {
+template <int D, int NWS, int FMT, typename Emit>
+__device__ __forceinline__ void merge_waves(const WaveAttn<D, 1, FMT>& W, float* s_ml, float* s_o, int grp, int w,
+                                            int i, int j, Emit&& emit) {
   using G = Geo<D>;
   const float lsum = W.lsum(0);
   if (j == 0) {
@@ -355,8 +363,9 @@ template <int D, int MODE>
 __global__ __launch_bounds__(64 * SplitWaves<D>::NW) __attribute__((amdgpu_waves_per_eu(DecodeOcc<D, MODE>::waves))) void
 decode_split_kernel(DecodeArgs a) {
   constexpr int NW = SplitWaves<D>::NW;
-  constexpr bool COMPACT = MODE != kModeDmaGeneral;
-  using SG = StageGeo<D, COMPACT>;
+  constexpr int FMT = mode_fmt(MODE);
+  constexpr bool COMPACT = MODE == kModeDmaCompact;
+  using SG = StageGeo<D, COMPACT, FMT>;
   constexpr int NS = DecodeStages<D>::NS;
   extern __shared__ __align__(16) char smem[];
   int* s_pref = reinterpret_cast<int*>(smem);
@@ -386,9 +395,9 @@ decode_split_kernel(DecodeArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int i = lane & 15, j = lane >> 4;
   const int grp = a.grp;
-  const DmaOffsets<D, COMPACT> dof = dma_offsets<D, COMPACT>(a.pool.st, a.pool.skv, lane);
+  const DmaOffsets<D, COMPACT, FMT> dof = dma_offsets<D, COMPACT, FMT>(a.pool.st, a.pool.skv, lane);
   uint8_t* ring = rings + w * NS * SG::STAGE;
-  const LdsLane ll = lds_lane<D>(i, j);
+  const LdsLane ll = lds_lane<D, FMT>(i, j);
 
   for (int u = blockIdx.x; u < total * hkv; u += gridDim.x) {
     const int ubs = u / hkv;
@@ -417,13 +426,13 @@ decode_split_kernel(DecodeArgs a) {
 
     const int32_t* bt_row = a.bt + (int64_t)b * a.max_blocks;
     const int k0 = st0 + w;  // the wave's steps: k0, k0 + NW, ... below st1
-    WaveAttn<D, 1> W;
+    WaveAttn<D, 1, FMT> W;
     W.init();
     const bool valid = i < grp;
     const uint16_t* qrow = valid ? a.q + (int64_t)b * a.q_st + (int64_t)(h * grp + i) * a.q_sh : nullptr;
     W.lim[0] = valid ? L - 1 : -1;
 
-    decode_stream<D, COMPACT, NS, NW>(W, ring, a.pool, bt_row, L, h, k0, st1, qrow, qk_factor, dof, ll, j);
+    decode_stream<D, COMPACT, FMT, NS, NW>(W, ring, a.pool, bt_row, L, h, k0, st1, qrow, qk_factor, dof, ll, j);
     __syncthreads();  // every wave's ring is drained before the rings become the merge buffer
     merge_waves<D, NW>(W, s_ml, s_o, grp, w, i, j, [&](int col, int d, float on, float M, float lt) {
       if (nsplit == 1) {
@@ -472,26 +481,30 @@ decode_split_kernel(DecodeArgs a) {
 // needs more than a few steps per wave; longer or fewer sequences go to the
 // split kernel.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, int FMT>
 struct PairGeo {
-  static constexpr int NW = (D == 256) ? 8 : 12;  // waves per workgroup (LDS holds one workgroup per CU)
+  // waves per workgroup: as many rings as the LDS of one CU holds (one
+  // workgroup per CU); FP8 stages are larger
+  static constexpr int NW = (FMT == kNvfp4) ? ((D == 256) ? 8 : 12) : ((D == 64) ? 12 : (D == 128) ? 8 : 4);
   static constexpr int kMaxStepsPerWave = 8;
 };
 
 template <int D, int MODE>
 struct PairLds {
-  static constexpr int NW = PairGeo<D>::NW;
-  static constexpr int stream = NW * DecodeStages<D>::NS * StageGeo<D, MODE == kModeDmaCompact>::STAGE;
+  static constexpr int NW = PairGeo<D, mode_fmt(MODE)>::NW;
+  static constexpr int stream =
+      NW * DecodeStages<D>::NS * StageGeo<D, MODE == kModeDmaCompact, mode_fmt(MODE)>::STAGE;
   static constexpr int merge = NW * kMergeCols * D * 4;
   static constexpr int bytes = NW * 16 * 2 * 4 + (stream > merge ? stream : merge);
   static_assert(bytes <= 160 * 1024, "one workgroup per CU");
 };
 
 template <int D, int MODE>
-__global__ __launch_bounds__(64 * PairGeo<D>::NW) void decode_pair_kernel(DecodeArgs a) {
-  constexpr int NW = PairGeo<D>::NW;
-  constexpr bool COMPACT = MODE != kModeDmaGeneral;
-  using SG = StageGeo<D, COMPACT>;
+__global__ __launch_bounds__((64 * PairGeo<D, mode_fmt(MODE)>::NW)) void decode_pair_kernel(DecodeArgs a) {
+  constexpr int FMT = mode_fmt(MODE);
+  constexpr int NW = PairGeo<D, FMT>::NW;
+  constexpr bool COMPACT = MODE == kModeDmaCompact;
+  using SG = StageGeo<D, COMPACT, FMT>;
   constexpr int NS = DecodeStages<D>::NS;
   extern __shared__ __align__(16) char smem[];
   float* s_ml = reinterpret_cast<float*>(smem);                     // [NW waves][16 cols][2]
@@ -514,15 +527,15 @@ __global__ __launch_bounds__(64 * PairGeo<D>::NW) void decode_pair_kernel(Decode
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int i = lane & 15, j = lane >> 4;
   const int grp = a.grp;
-  const DmaOffsets<D, COMPACT> dof = dma_offsets<D, COMPACT>(a.pool.st, a.pool.skv, lane);
+  const DmaOffsets<D, COMPACT, FMT> dof = dma_offsets<D, COMPACT, FMT>(a.pool.st, a.pool.skv, lane);
   uint8_t* ring = rings + w * NS * SG::STAGE;
-  const LdsLane ll = lds_lane<D>(i, j);
-  WaveAttn<D, 1> W;
+  const LdsLane ll = lds_lane<D, FMT>(i, j);
+  WaveAttn<D, 1, FMT> W;
   W.init();
   const bool valid = i < grp;
   const uint16_t* qrow = valid ? a.q + (int64_t)b * a.q_st + (int64_t)(h * grp + i) * a.q_sh : nullptr;
   W.lim[0] = valid ? L - 1 : -1;
-  decode_stream<D, COMPACT, NS, NW>(W, ring, a.pool, a.bt + (int64_t)b * a.max_blocks, L, h, w, ceil_div(L, kStep),
+  decode_stream<D, COMPACT, FMT, NS, NW>(W, ring, a.pool, a.bt + (int64_t)b * a.max_blocks, L, h, w, ceil_div(L, kStep),
                                     qrow, qk_factor, dof, ll, j);
   __syncthreads();  // every wave's ring is drained before the rings become the merge buffer
   merge_waves<D, NW>(W, s_ml, s_o, grp, w, i, j, [&](int col, int d, float on, float, float) {
@@ -550,18 +563,20 @@ static size_t decode_lds_bytes_m(int num_seqs) {
 }
 
 template <int D>
-static size_t decode_lds_bytes_t(int num_seqs) {
-  // both modes use the same stage geometry
+static size_t decode_lds_bytes_t(int num_seqs, int fmt) {
+  // both NVFP4 modes use the same stage geometry, both FP8 formats another
   static_assert(DecodeLds<D, kModeDmaGeneral>::area == DecodeLds<D, kModeDmaCompact>::area, "mode LDS sizes");
-  return decode_lds_bytes_m<D, kModeDmaCompact>(num_seqs);
+  static_assert(DecodeLds<D, kModeFp8E4M3>::area == DecodeLds<D, kModeFp8E5M2>::area, "mode LDS sizes");
+  return fmt == kNvfp4 ? decode_lds_bytes_m<D, kModeDmaCompact>(num_seqs)
+                       : decode_lds_bytes_m<D, kModeFp8E4M3>(num_seqs);
 }
 
-size_t decode_lds_bytes(int num_seqs, int grp, int head_size) {
+size_t decode_lds_bytes(int num_seqs, int grp, int head_size, int fmt) {
   (void)grp;
   switch (head_size) {
-    case 64: return decode_lds_bytes_t<64>(num_seqs);
-    case 128: return decode_lds_bytes_t<128>(num_seqs);
-    default: return decode_lds_bytes_t<256>(num_seqs);
+    case 64: return decode_lds_bytes_t<64>(num_seqs, fmt);
+    case 128: return decode_lds_bytes_t<128>(num_seqs, fmt);
+    default: return decode_lds_bytes_t<256>(num_seqs, fmt);
   }
 }
 
@@ -607,18 +622,29 @@ static int64_t host_max_steps(int max_blocks, int bs, int max_seq_len) {
 
 // The per-pair kernel when the batch alone gives every CU a (sequence, kv
 // head) pair and no sequence needs more than kMaxStepsPerWave steps per wave.
-template <int D>
+template <int D, int FMT>
 static bool use_pair_kernel(int num_seqs, int hkv, int64_t max_steps) {
   return (int64_t)num_seqs * hkv >= device_cus() &&
-         max_steps <= (int64_t)PairGeo<D>::NW * PairGeo<D>::kMaxStepsPerWave;
+         max_steps <= (int64_t)PairGeo<D, FMT>::NW * PairGeo<D, FMT>::kMaxStepsPerWave;
 }
 
-int decode_plan(int num_seqs, int num_kv_heads, int head_size, int block_size, int max_blocks, int max_seq_len) {
-  const int64_t steps = host_max_steps(max_blocks, block_size, max_seq_len);
+template <int FMT>
+static int decode_plan_f(int num_seqs, int num_kv_heads, int head_size, int64_t steps) {
   switch (head_size) {
-    case 64: return use_pair_kernel<64>(num_seqs, num_kv_heads, steps) ? 1 : 0;
-    case 128: return use_pair_kernel<128>(num_seqs, num_kv_heads, steps) ? 1 : 0;
-    case 256: return use_pair_kernel<256>(num_seqs, num_kv_heads, steps) ? 1 : 0;
+    case 64: return use_pair_kernel<64, FMT>(num_seqs, num_kv_heads, steps) ? 1 : 0;
+    case 128: return use_pair_kernel<128, FMT>(num_seqs, num_kv_heads, steps) ? 1 : 0;
+    case 256: return use_pair_kernel<256, FMT>(num_seqs, num_kv_heads, steps) ? 1 : 0;
+    default: return -1;
+  }
+}
+
+int decode_plan(int num_seqs, int num_kv_heads, int head_size, int block_size, int max_blocks, int max_seq_len,
+                int fmt) {
+  const int64_t steps = host_max_steps(max_blocks, block_size, max_seq_len);
+  switch (fmt) {
+    case kNvfp4: return decode_plan_f<kNvfp4>(num_seqs, num_kv_heads, head_size, steps);
+    case kFp8E4M3: return decode_plan_f<kFp8E4M3>(num_seqs, num_kv_heads, head_size, steps);
+    case kFp8E5M2: return decode_plan_f<kFp8E5M2>(num_seqs, num_kv_heads, head_size, steps);
     default: return -1;
   }
 }
@@ -627,8 +653,9 @@ template <int D, int MODE>
 static hipError_t launch_decode_v(DecodeArgs a, int max_seq_len, hipStream_t stream) {
   const int hkv = a.pool.hkv;
   const int64_t steps = host_max_steps(a.max_blocks, a.pool.bs, max_seq_len);
-  if (use_pair_kernel<D>(a.B, hkv, steps)) {
-    decode_pair_kernel<D, MODE><<<a.B * hkv, 64 * PairGeo<D>::NW, PairLds<D, MODE>::bytes, stream>>>(a);
+  constexpr int FMT = mode_fmt(MODE);
+  if (use_pair_kernel<D, FMT>(a.B, hkv, steps)) {
+    decode_pair_kernel<D, MODE><<<a.B * hkv, 64 * PairGeo<D, FMT>::NW, PairLds<D, MODE>::bytes, stream>>>(a);
     return hipGetLastError();
   }
   const size_t lds = decode_lds_bytes_m<D, MODE>(a.B);
@@ -642,7 +669,11 @@ static hipError_t launch_decode_v(DecodeArgs a, int max_seq_len, hipStream_t str
 }
 
 template <int D>
-static hipError_t launch_decode_t(DecodeArgs a, int max_seq_len, hipStream_t stream) {
+static hipError_t launch_decode_t(DecodeArgs a, int max_seq_len, int fmt, hipStream_t stream) {
+  // FP8 rows are copied in 16-byte chunks whatever their stride (the API
+  // requires 16-byte aligned strides for them)
+  if (fmt == kFp8E4M3) return launch_decode_v<D, kModeFp8E4M3>(a, max_seq_len, stream);
+  if (fmt == kFp8E5M2) return launch_decode_v<D, kModeFp8E5M2>(a, max_seq_len, stream);
   // 16-byte chunks need contiguous, 16-byte aligned page rows (HND layout)
   const bool compact = a.pool.st == D / 2 + D / 16 && a.pool.sb % 16 == 0 && a.pool.skv % 16 == 0 &&
                        a.pool.sh % 16 == 0 && (reinterpret_cast<uintptr_t>(a.pool.data) % 16) == 0;
@@ -654,7 +685,7 @@ hipError_t launch_decode(const Pool& pool, int head_size, const void* q, int64_t
                          int num_q_heads, const int32_t* block_table, int32_t max_blocks,
                          const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len, const float* k_scale,
                          const float* v_scale, float sm_scale, const float* o_scale, void* out, void* workspace,
-                         hipStream_t stream) {
+                         int fmt, hipStream_t stream) {
   if (num_seqs == 0) return hipSuccess;
   DecodeArgs a;
   a.pool = pool;
@@ -678,9 +709,9 @@ hipError_t launch_decode(const Pool& pool, int head_size, const void* q, int64_t
   a.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + counter_bytes(pool.hkv));
   a.ws_ml = a.ws_o + slots * a.grp * head_size;
   switch (head_size) {
-    case 64: return launch_decode_t<64>(a, max_seq_len, stream);
-    case 128: return launch_decode_t<128>(a, max_seq_len, stream);
-    case 256: return launch_decode_t<256>(a, max_seq_len, stream);
+    case 64: return launch_decode_t<64>(a, max_seq_len, fmt, stream);
+    case 128: return launch_decode_t<128>(a, max_seq_len, fmt, stream);
+    case 256: return launch_decode_t<256>(a, max_seq_len, fmt, stream);
     default: return hipErrorInvalidValue;
   }
 }

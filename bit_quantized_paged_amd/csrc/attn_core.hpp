@@ -36,6 +36,11 @@ namespace nvfp4kv {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazyMax = 8.0f;
 
+template <int D, int FMT>
+struct RowBytes {
+  static constexpr int value = (FMT == kNvfp4) ? D / 2 + D / 16 : D;
+};
+
 template <int D>
 struct Geo {
   static constexpr int DPL = D / 16;                // V: d per lane = PV products
@@ -44,26 +49,26 @@ struct Geo {
   static constexpr int VW = VB >= 4 ? VB / 4 : 1;   // V: words per key per lane
 };
 
+// Raw bytes of one 16-key subtile for lane (i, j) = (lane % 16, lane / 16):
+// K row i, the quarter j of its elements (d in [D/4 j, D/4 (j+1)), the
+// operands of k_chunk), and V rows 4j..4j+3, the D/16 elements
+// d in [D/16 i, D/16 (i+1)) of each (the lane's rows of the V^T tiles).
+// FP8 (this template): one byte per element.
+template <int D, int FMT = kNvfp4>
+struct SubRaw {
+  uint32_t k[D / 16];
+  uint32_t v[4][D / 64];
+};
+
+// NVFP4: the same elements as nibbles, plus the E4M3 scale bytes of their
+// 16-element blocks.
 template <int D>
-struct SubRaw {  // raw bytes of one 16-key subtile for one lane
+struct SubRaw<D, kNvfp4> {
   uint32_t k[Geo<D>::KW];
   uint32_t ks;
   uint32_t v[4][Geo<D>::VW];
   uint32_t vs[4];
 };
-
-template <int D>
-__device__ __forceinline__ void zero_sub(SubRaw<D>& R) {
-#pragma unroll
-  for (int c = 0; c < Geo<D>::KW; ++c) R.k[c] = 0;
-  R.ks = 0;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-#pragma unroll
-    for (int w = 0; w < Geo<D>::VW; ++w) R.v[r][w] = 0;
-    R.vs[r] = 0;
-  }
-}
 
 // Pages are read with raw buffer loads: a wave-uniform descriptor per
 // subtile (base = first row of the subtile, size = the bytes its 16 rows
@@ -78,22 +83,29 @@ __device__ __forceinline__ rsrc_t make_rsrc(const uint8_t* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, bytes, kRsrcWord3);
 }
 
-// Zero the value rows of keys >= L (unwritten rows may hold NaN scale bytes;
-// their probability is 0 but 0 * NaN would poison the accumulator).
-template <int D>
-__device__ __forceinline__ void mask_sub_values(SubRaw<D>& R, int key0, int L, int j) {
+// Zero the value rows of keys >= L (unwritten rows may hold NaN codes or
+// scale bytes; their probability is 0 but 0 * NaN would poison the
+// accumulator).
+template <int D, int FMT>
+__device__ __forceinline__ void mask_sub_values(SubRaw<D, FMT>& R, int key0, int L, int j) {
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const bool ok = key0 + 4 * j + r < L;
+    if constexpr (FMT == kNvfp4) {
 #pragma unroll
-    for (int w = 0; w < Geo<D>::VW; ++w) R.v[r][w] = ok ? R.v[r][w] : 0u;
-    R.vs[r] = ok ? R.vs[r] : 0u;
+      for (int w = 0; w < Geo<D>::VW; ++w) R.v[r][w] = ok ? R.v[r][w] : 0u;
+      R.vs[r] = ok ? R.vs[r] : 0u;
+    } else {
+#pragma unroll
+      for (int w = 0; w < D / 64; ++w) R.v[r][w] = ok ? R.v[r][w] : 0u;
+    }
   }
 }
 
-// Dequantised K chunk c of this lane: 8 f16 = codes * block scale.
+
+// Dequantised NVFP4 K chunk c of this lane: 8 f16 = codes * block scale.
 template <int D, int C>
-__device__ __forceinline__ h8 k_chunk(const SubRaw<D>& R) {
+__device__ __forceinline__ h8 k_chunk_nvfp4(const SubRaw<D, kNvfp4>& R) {
   constexpr int SI = C / 2;  // scale byte index within the lane's scales
   const h2 sp = (SI < 2) ? fp8x2_to_h2<false>(R.ks) : fp8x2_to_h2<true>(R.ks);
   const _Float16 s = sp[SI & 1];
@@ -106,40 +118,107 @@ __device__ __forceinline__ h8 k_chunk(const SubRaw<D>& R) {
   return h8{a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
 }
 
-// Value rows of one subtile rearranged so that each byte holds the codes of
-// two keys (4j+2p, 4j+2p+1) at one d.
-template <int D>
+// K chunk c of this lane as 8 f16 (the A operand of S^T = K^ Q^T): NVFP4
+// codes times their block scale, or FP8 codes converted exactly (the
+// per-tensor scale is applied to the scores).
+template <int D, int C, int FMT>
+__device__ __forceinline__ h8 k_chunk(const SubRaw<D, FMT>& R) {
+  if constexpr (FMT == kNvfp4) {
+    return k_chunk_nvfp4<D, C>(R);
+  } else {
+    const uint32_t w0 = R.k[2 * C], w1 = R.k[2 * C + 1];
+    h2 a0, a1, a2, a3;
+    if constexpr (FMT == kFp8E4M3) {
+      a0 = fp8x2_to_h2<false>(w0);
+      a1 = fp8x2_to_h2<true>(w0);
+      a2 = fp8x2_to_h2<false>(w1);
+      a3 = fp8x2_to_h2<true>(w1);
+    } else {
+      a0 = e5m2x2_to_h2<0, 1>(w0, w0);
+      a1 = e5m2x2_to_h2<2, 3>(w0, w0);
+      a2 = e5m2x2_to_h2<0, 1>(w1, w1);
+      a3 = e5m2x2_to_h2<2, 3>(w1, w1);
+    }
+    return h8{a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
+  }
+}
+
+// Value rows of one subtile arranged for the V^T tiles.
+// NVFP4: each byte holds the codes of two keys (4j+2p, 4j+2p+1) at one d.
+// FP8 E4M3: per key pair p and word w of their rows, lo holds (byte 0 of key
+// 4j+2p, byte 0 of key 4j+2p+1, byte 1 of each) and hi the same for bytes 2
+// and 3, so one pair convert gives both keys at one d. E5M2 keeps the rows.
+template <int D, int FMT = kNvfp4>
 struct VPairs {
+  uint32_t lo[2][D / 64];
+  uint32_t hi[2][D / 64];
+  uint32_t raw[4][D / 64];
+};
+
+template <int D>
+struct VPairs<D, kNvfp4> {
   uint32_t ev[2][Geo<D>::VW];  // [pair][word]: byte b <-> d offset 8w + 2b
   uint32_t od[2][Geo<D>::VW];  //                byte b <-> d offset 8w + 2b + 1
   h2 s[2];                     // block scales of the pair's two keys
 };
 
-template <int D>
-__device__ __forceinline__ void make_pairs(const SubRaw<D>& R, VPairs<D>& P) {
+template <int D, int FMT>
+__device__ __forceinline__ void make_pairs(const SubRaw<D, FMT>& R, VPairs<D, FMT>& P) {
+  if constexpr (FMT == kNvfp4) {
 #pragma unroll
-  for (int p = 0; p < 2; ++p) {
+    for (int p = 0; p < 2; ++p) {
 #pragma unroll
-    for (int w = 0; w < Geo<D>::VW; ++w) {
-      const uint32_t a = R.v[2 * p][w];
-      const uint32_t b = R.v[2 * p + 1][w];
-      P.ev[p][w] = (a & 0x0F0F0F0Fu) | ((b & 0x0F0F0F0Fu) << 4);
-      P.od[p][w] = ((a >> 4) & 0x0F0F0F0Fu) | (b & 0xF0F0F0F0u);
+      for (int w = 0; w < Geo<D>::VW; ++w) {
+        const uint32_t a = R.v[2 * p][w];
+        const uint32_t b = R.v[2 * p + 1][w];
+        P.ev[p][w] = (a & 0x0F0F0F0Fu) | ((b & 0x0F0F0F0Fu) << 4);
+        P.od[p][w] = ((a >> 4) & 0x0F0F0F0Fu) | (b & 0xF0F0F0F0u);
+      }
     }
+    // (vs0, vs1) and (vs2, vs3) side by side in the low bytes: one permute each
+    P.s[0] = fp8x2_to_h2<false>(__builtin_amdgcn_perm(R.vs[1], R.vs[0], 0x0C0C0400u));
+    P.s[1] = fp8x2_to_h2<false>(__builtin_amdgcn_perm(R.vs[3], R.vs[2], 0x0C0C0400u));
+  } else if constexpr (FMT == kFp8E4M3) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+#pragma unroll
+      for (int w = 0; w < D / 64; ++w) {
+        P.lo[p][w] = __builtin_amdgcn_perm(R.v[2 * p + 1][w], R.v[2 * p][w], 0x05010400u);
+        P.hi[p][w] = __builtin_amdgcn_perm(R.v[2 * p + 1][w], R.v[2 * p][w], 0x07030602u);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int w = 0; w < D / 64; ++w) P.raw[r][w] = R.v[r][w];
   }
-  // (vs0, vs1) and (vs2, vs3) side by side in the low bytes: one permute each
-  P.s[0] = fp8x2_to_h2<false>(__builtin_amdgcn_perm(R.vs[1], R.vs[0], 0x0C0C0400u));
-  P.s[1] = fp8x2_to_h2<false>(__builtin_amdgcn_perm(R.vs[3], R.vs[2], 0x0C0C0400u));
 }
 
-template <int D, int T>
-__device__ __forceinline__ h4 v_operand(const VPairs<D>& P) {
-  constexpr int W = T / 8;
-  constexpr int BYTE = (T % 8) / 2;
-  const uint32_t w0 = (T & 1) ? P.od[0][W] : P.ev[0][W];
-  const uint32_t w1 = (T & 1) ? P.od[1][W] : P.ev[1][W];
-  const h2 a = fp4x2_to_h2<BYTE>(w0) * P.s[0];
-  const h2 b = fp4x2_to_h2<BYTE>(w1) * P.s[1];
+// V^T tile T: this lane's row d = D/16 i + T, keys 4j..4j+3 as f16.
+template <int D, int T, int FMT>
+__device__ __forceinline__ h4 v_operand(const VPairs<D, FMT>& P) {
+  h2 a, b;
+  if constexpr (FMT == kNvfp4) {
+    constexpr int W = T / 8;
+    constexpr int BYTE = (T % 8) / 2;
+    const uint32_t w0 = (T & 1) ? P.od[0][W] : P.ev[0][W];
+    const uint32_t w1 = (T & 1) ? P.od[1][W] : P.ev[1][W];
+    a = fp4x2_to_h2<BYTE>(w0) * P.s[0];
+    b = fp4x2_to_h2<BYTE>(w1) * P.s[1];
+  } else if constexpr (FMT == kFp8E4M3) {
+    constexpr int W = T / 4;
+    constexpr int B = T % 4;
+    const uint32_t x0 = (B < 2) ? P.lo[0][W] : P.hi[0][W];
+    const uint32_t x1 = (B < 2) ? P.lo[1][W] : P.hi[1][W];
+    a = fp8x2_to_h2<(B & 1) != 0>(x0);
+    b = fp8x2_to_h2<(B & 1) != 0>(x1);
+  } else {
+    constexpr int W = T / 4;
+    constexpr int B = T % 4;
+    a = e5m2x2_to_h2<B, B>(P.raw[0][W], P.raw[1][W]);
+    b = e5m2x2_to_h2<B, B>(P.raw[2][W], P.raw[3][W]);
+  }
   return h4{a[0], a[1], b[0], b[1]};
 }
 
@@ -152,7 +231,7 @@ __device__ __forceinline__ float wave_sum_j(float v) {
   return v + __shfl_xor(v, 32);
 }
 
-template <int D, int NT>
+template <int D, int NT, int FMT = kNvfp4>
 struct WaveAttn {
   using G = Geo<D>;
   h8 q[NT][G::KW];       // B operand of S^T, per column tile and chunk
@@ -243,7 +322,7 @@ struct WaveAttn {
   // subtiles' raw bytes (keys >= L already zeroed in the value rows). With
   // masked false (wave-uniform) every key of the step is visible to every
   // valid column and the per-key limit test is skipped.
-  __device__ __forceinline__ void step(const SubRaw<D> (&R)[2], int kb, int j, bool masked) {
+  __device__ __forceinline__ void step(const SubRaw<D, FMT> (&R)[2], int kb, int j, bool masked) {
     // ---- S^T = K^ . Q^T for both subtiles
     f4 s[2][NT];
 #pragma unroll
@@ -255,7 +334,7 @@ struct WaveAttn {
     h8 p[NT];
     softmax(s, kb, j, masked, p);
     // ---- O^T += V^ T . P^T
-    VPairs<D> vp[2];
+    VPairs<D, FMT> vp[2];
     make_pairs(R[0], vp[0]);
     make_pairs(R[1], vp[1]);
     pv<0>(vp, p);
@@ -351,7 +430,7 @@ struct WaveAttn {
   }
 
   template <int C>
-  __device__ __forceinline__ void chunks(const SubRaw<D>& R, f4 (&s)[NT]) {
+  __device__ __forceinline__ void chunks(const SubRaw<D, FMT>& R, f4 (&s)[NT]) {
     if constexpr (C < G::KW) {
       const h8 a = k_chunk<D, C>(R);
 #pragma unroll
@@ -361,7 +440,7 @@ struct WaveAttn {
   }
 
   template <int T>
-  __device__ __forceinline__ void pv(const VPairs<D> (&vp)[2], const h8 (&p)[NT]) {
+  __device__ __forceinline__ void pv(const VPairs<D, FMT> (&vp)[2], const h8 (&p)[NT]) {
     if constexpr (T == 0 && kMfmaSum) sum_ops(p);
     if constexpr (T < G::DPL) {
       const h4 a0 = v_operand<D, T>(vp[0]);
@@ -427,14 +506,16 @@ typedef __attribute__((address_space(3))) void lds_void;
 //    (1 KB each), then N4 loads of 4 bytes per lane (256 B each) for the rest;
 //  general (any row stride): loads of 4 bytes per lane, 256 B each.
 // Lanes past the subtile's bytes read out of range, which writes zeros.
-template <int D, bool COMPACT>
+//  FP8 rows (D bytes, a multiple of 16; row strides multiples of 16): 16-byte
+//    loads only, whatever the row stride.
+template <int D, bool COMPACT, int FMT = kNvfp4>
 struct StageGeo {
-  static constexpr int FD = D / 2 + D / 16;
+  static constexpr int FD = RowBytes<D, FMT>::value;
   static constexpr int SLAB = 16 * FD;                       // bytes of 16 rows
   static constexpr int BYTES = 2 * SLAB;                     // K and V of a subtile
   static constexpr int SUB = (BYTES + 255) / 256 * 256;      // LDS bytes per subtile
   static constexpr int STAGE = 2 * SUB;                      // LDS bytes per stage
-  static constexpr int N16 = COMPACT ? BYTES / 1024 : 0;     // 16-byte loads per subtile
+  static constexpr int N16 = (COMPACT || FMT != kNvfp4) ? BYTES / 1024 : 0;  // 16-byte loads per subtile
   static constexpr int N4 = (BYTES - 1024 * N16 + 255) / 256;  // 4-byte loads per subtile
   static constexpr int NCS = N16 + N4;                       // loads per subtile
   static constexpr int NC = 2 * NCS;                         // loads per step
@@ -446,17 +527,17 @@ struct StageGeo {
 // Per-lane byte offset, relative to the subtile's first K row in the pool, of
 // the bytes lane `lane` copies in each load of a subtile (V bytes include the
 // K->V stride); loop invariant.
-template <int D, bool COMPACT>
+template <int D, bool COMPACT, int FMT = kNvfp4>
 struct DmaOffsets {
-  uint32_t v[StageGeo<D, COMPACT>::NCS];
+  uint32_t v[StageGeo<D, COMPACT, FMT>::NCS];
 };
 
 constexpr uint32_t kOutOfRange = 0x7FFFFFF0u;  // >= any descriptor size used here
 
-template <int D, bool COMPACT>
-__device__ __forceinline__ DmaOffsets<D, COMPACT> dma_offsets(int64_t st, int64_t skv, int lane) {
-  using SG = StageGeo<D, COMPACT>;
-  DmaOffsets<D, COMPACT> o;
+template <int D, bool COMPACT, int FMT = kNvfp4>
+__device__ __forceinline__ DmaOffsets<D, COMPACT, FMT> dma_offsets(int64_t st, int64_t skv, int lane) {
+  using SG = StageGeo<D, COMPACT, FMT>;
+  DmaOffsets<D, COMPACT, FMT> o;
 #pragma unroll
   for (int t = 0; t < SG::NCS; ++t) {
     const int x = SG::off(t) + SG::size(t) * lane;  // byte of the subtile's [K slab | V slab]
@@ -477,30 +558,30 @@ __device__ __forceinline__ DmaOffsets<D, COMPACT> dma_offsets(int64_t st, int64_
 __device__ __forceinline__ lds_void* to_lds(uint8_t* p) { return (lds_void*)p; }
 
 // Loads T, T + 1, ... of one subtile (the load width must be a literal).
-template <int D, bool COMPACT, int T>
-__device__ __forceinline__ void dma_sub(uint8_t* dst, rsrc_t r, const DmaOffsets<D, COMPACT>& o) {
-  using SG = StageGeo<D, COMPACT>;
+template <int D, bool COMPACT, int FMT, int T>
+__device__ __forceinline__ void dma_sub(uint8_t* dst, rsrc_t r, const DmaOffsets<D, COMPACT, FMT>& o) {
+  using SG = StageGeo<D, COMPACT, FMT>;
   if constexpr (T < SG::NCS) {
     if constexpr (SG::size(T) == 16)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, to_lds(dst + SG::off(T)), 16, o.v[T], 0, 0, 0);
     else
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, to_lds(dst + SG::off(T)), 4, o.v[T], 0, 0, 0);
-    dma_sub<D, COMPACT, T + 1>(dst, r, o);
+    dma_sub<D, COMPACT, FMT, T + 1>(dst, r, o);
   }
 }
 
 // Copy the step at kb (ids from step_ids) into the stage at dst.
-template <int D, bool COMPACT>
+template <int D, bool COMPACT, int FMT = kNvfp4>
 __device__ __forceinline__ void dma_step(uint8_t* dst, const Pool& pool, const StepIds& ids, int h, int kb,
-                                         const DmaOffsets<D, COMPACT>& o) {
-  using SG = StageGeo<D, COMPACT>;
+                                         const DmaOffsets<D, COMPACT, FMT>& o) {
+  using SG = StageGeo<D, COMPACT, FMT>;
   const int extent = (int)pool.skv + 15 * (int)pool.st + SG::FD;
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb) {
     const int row0 = (kb + 16 * sb) & (pool.bs - 1);
     const int64_t blk = clamp_block(ids.id[sb], pool.num_blocks);
     const uint8_t* base = pool.data + blk * pool.sb + (int64_t)h * pool.sh + (int64_t)row0 * pool.st;
-    dma_sub<D, COMPACT, 0>(dst + sb * SG::SUB, make_rsrc(base, ids.ok[sb] ? extent : 0), o);
+    dma_sub<D, COMPACT, FMT, 0>(dst + sb * SG::SUB, make_rsrc(base, ids.ok[sb] ? extent : 0), o);
   }
 }
 
@@ -524,14 +605,14 @@ __device__ __forceinline__ StepIds ids_for_step(const int32_t* bt_row, int k, in
   return step_ids(bt_row, k * 32, k < kend ? L : 0, pool);
 }
 
-template <int D, bool COMPACT, int NS>
+template <int D, bool COMPACT, int NS, int FMT = kNvfp4>
 __device__ __forceinline__ StepIds lds_prologue(uint8_t* ring, int k0, int ks, int kend, const int32_t* bt_row, int L,
-                                                const Pool& pool, int h, const DmaOffsets<D, COMPACT>& dof) {
-  using SG = StageGeo<D, COMPACT>;
+                                                const Pool& pool, int h, const DmaOffsets<D, COMPACT, FMT>& dof) {
+  using SG = StageGeo<D, COMPACT, FMT>;
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
-    dma_step<D, COMPACT>(ring + s * SG::STAGE, pool, ids_for_step(bt_row, k0 + s * ks, kend, L, pool), h,
-                         (k0 + s * ks) * 32, dof);
+    dma_step<D, COMPACT, FMT>(ring + s * SG::STAGE, pool, ids_for_step(bt_row, k0 + s * ks, kend, L, pool), h,
+                              (k0 + s * ks) * 32, dof);
   return ids_for_step(bt_row, k0 + (NS - 1) * ks, kend, L, pool);
 }
 
@@ -552,14 +633,21 @@ struct LdsLane {
   uint32_t k, ks, v, vs;
 };
 
-template <int D>
+template <int D, int FMT = kNvfp4>
 __device__ __forceinline__ LdsLane lds_lane(int i, int j) {
-  constexpr int FD = D / 2 + D / 16;
   LdsLane o;
-  o.k = (uint32_t)(i * FD + (D / 8) * j);
-  o.ks = (uint32_t)(i * FD + D / 2 + (D / 64) * j);
-  o.v = (uint32_t)(16 * FD + 4 * j * FD + (D / 32) * i);
-  o.vs = (uint32_t)(16 * FD + 4 * j * FD + D / 2 + ((i * D) >> 8));
+  if constexpr (FMT == kNvfp4) {
+    constexpr int FD = D / 2 + D / 16;
+    o.k = (uint32_t)(i * FD + (D / 8) * j);
+    o.ks = (uint32_t)(i * FD + D / 2 + (D / 64) * j);
+    o.v = (uint32_t)(16 * FD + 4 * j * FD + (D / 32) * i);
+    o.vs = (uint32_t)(16 * FD + 4 * j * FD + D / 2 + ((i * D) >> 8));
+  } else {
+    o.k = (uint32_t)(i * D + (D / 4) * j);
+    o.ks = 0;
+    o.v = (uint32_t)(16 * D + 4 * j * D + (D / 16) * i);
+    o.vs = 0;
+  }
   return o;
 }
 
@@ -714,11 +802,126 @@ __device__ __forceinline__ void lds_read_step_async_safe<256>(SubRaw<256> (&R)[2
   }
 }
 
-template <int D>
-__device__ __forceinline__ void mask_step(SubRaw<D> (&R)[2], int kb, int L, int j) {
+// FP8 stage readers: lane (i, j) reads D/4 bytes of K row i at i*D + D/4*j
+// and D/16 bytes of V rows 4j..4j+3 at 16*D + 4j*D + D/16*i (lds_lane), in
+// both subtiles (the second 32*D bytes further). All offsets are 16-byte
+// aligned for the 16-byte reads (the ring is).
+template <int D, int FMT>
+__device__ __forceinline__ void lds_read_step_fp8(SubRaw<D, FMT> (&R)[2], const uint8_t* stage, const LdsLane& o) {
+  const uint32_t s = lds_addr(stage);
+  const uint32_t ak = s + o.k, av = s + o.v;
+  if constexpr (D == 64) {
+    static_assert(StageGeo<64, false, FMT>::SUB == 2048, "D = 64 FP8 reader offsets");
+    u32x4 k0, k1;
+    asm volatile(
+        "ds_read_b128 %0, %10\n\t"
+        "ds_read_b32 %1, %11\n\t"
+        "ds_read_b32 %2, %11 offset:64\n\t"
+        "ds_read_b32 %3, %11 offset:128\n\t"
+        "ds_read_b32 %4, %11 offset:192\n\t"
+        "ds_read_b128 %5, %10 offset:2048\n\t"
+        "ds_read_b32 %6, %11 offset:2048\n\t"
+        "ds_read_b32 %7, %11 offset:2112\n\t"
+        "ds_read_b32 %8, %11 offset:2176\n\t"
+        "ds_read_b32 %9, %11 offset:2240\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(k0), "=&v"(R[0].v[0][0]), "=&v"(R[0].v[1][0]), "=&v"(R[0].v[2][0]), "=&v"(R[0].v[3][0]),
+          "=&v"(k1), "=&v"(R[1].v[0][0]), "=&v"(R[1].v[1][0]), "=&v"(R[1].v[2][0]), "=&v"(R[1].v[3][0])
+        : "v"(ak), "v"(av)
+        : "memory");
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      R[0].k[c] = k0[c];
+      R[1].k[c] = k1[c];
+    }
+  } else if constexpr (D == 128) {
+    static_assert(StageGeo<128, false, FMT>::SUB == 4096, "D = 128 FP8 reader offsets");
+    u32x4 k0a, k0b, k1a, k1b;
+    u32x2 v0[4], v1[4];
+    asm volatile(
+        "ds_read_b128 %0, %12\n\t"
+        "ds_read_b128 %1, %12 offset:16\n\t"
+        "ds_read_b64 %2, %13\n\t"
+        "ds_read_b64 %3, %13 offset:128\n\t"
+        "ds_read_b64 %4, %13 offset:256\n\t"
+        "ds_read_b64 %5, %13 offset:384\n\t"
+        "ds_read_b128 %6, %12 offset:4096\n\t"
+        "ds_read_b128 %7, %12 offset:4112\n\t"
+        "ds_read_b64 %8, %13 offset:4096\n\t"
+        "ds_read_b64 %9, %13 offset:4224\n\t"
+        "ds_read_b64 %10, %13 offset:4352\n\t"
+        "ds_read_b64 %11, %13 offset:4480\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(k0a), "=&v"(k0b), "=&v"(v0[0]), "=&v"(v0[1]), "=&v"(v0[2]), "=&v"(v0[3]), "=&v"(k1a),
+          "=&v"(k1b), "=&v"(v1[0]), "=&v"(v1[1]), "=&v"(v1[2]), "=&v"(v1[3])
+        : "v"(ak), "v"(av)
+        : "memory");
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      R[0].k[c] = k0a[c];
+      R[0].k[4 + c] = k0b[c];
+      R[1].k[c] = k1a[c];
+      R[1].k[4 + c] = k1b[c];
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      R[0].v[r][0] = v0[r][0];
+      R[0].v[r][1] = v0[r][1];
+      R[1].v[r][0] = v1[r][0];
+      R[1].v[r][1] = v1[r][1];
+    }
+  } else {
+    static_assert(D == 256 && StageGeo<256, false, FMT>::SUB == 8192, "D = 256 FP8 reader offsets");
+    u32x4 k0[4], k1[4], v0[4], v1[4];
+    asm volatile(
+        "ds_read_b128 %0, %16\n\t"
+        "ds_read_b128 %1, %16 offset:16\n\t"
+        "ds_read_b128 %2, %16 offset:32\n\t"
+        "ds_read_b128 %3, %16 offset:48\n\t"
+        "ds_read_b128 %4, %17\n\t"
+        "ds_read_b128 %5, %17 offset:256\n\t"
+        "ds_read_b128 %6, %17 offset:512\n\t"
+        "ds_read_b128 %7, %17 offset:768\n\t"
+        "ds_read_b128 %8, %16 offset:8192\n\t"
+        "ds_read_b128 %9, %16 offset:8208\n\t"
+        "ds_read_b128 %10, %16 offset:8224\n\t"
+        "ds_read_b128 %11, %16 offset:8240\n\t"
+        "ds_read_b128 %12, %17 offset:8192\n\t"
+        "ds_read_b128 %13, %17 offset:8448\n\t"
+        "ds_read_b128 %14, %17 offset:8704\n\t"
+        "ds_read_b128 %15, %17 offset:8960\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(k0[0]), "=&v"(k0[1]), "=&v"(k0[2]), "=&v"(k0[3]), "=&v"(v0[0]), "=&v"(v0[1]), "=&v"(v0[2]),
+          "=&v"(v0[3]), "=&v"(k1[0]), "=&v"(k1[1]), "=&v"(k1[2]), "=&v"(k1[3]), "=&v"(v1[0]), "=&v"(v1[1]),
+          "=&v"(v1[2]), "=&v"(v1[3])
+        : "v"(ak), "v"(av)
+        : "memory");
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        R[0].k[4 * q + c] = k0[q][c];
+        R[1].k[4 * q + c] = k1[q][c];
+        R[0].v[q][c] = v0[q][c];
+        R[1].v[q][c] = v1[q][c];
+      }
+  }
+}
+
+// The step's raw bytes for either format (see the readers above).
+template <int D, int FMT>
+__device__ __forceinline__ void lds_read_step(SubRaw<D, FMT> (&R)[2], const uint8_t* stage, const LdsLane& o) {
+  if constexpr (FMT == kNvfp4)
+    lds_read_step_async_safe<D>(R, stage, o);
+  else
+    lds_read_step_fp8<D, FMT>(R, stage, o);
+}
+
+template <int D, int FMT>
+__device__ __forceinline__ void mask_step(SubRaw<D, FMT> (&R)[2], int kb, int L, int j) {
   if (kb + 32 > L) {
-    mask_sub_values<D>(R[0], kb, L, j);
-    mask_sub_values<D>(R[1], kb + 16, L, j);
+    mask_sub_values(R[0], kb, L, j);
+    mask_sub_values(R[1], kb + 16, L, j);
   }
 }
 

@@ -5,13 +5,14 @@
 // with the hardware FP4 convert, times the E4M3 scale (exact in f16: at most
 // 6 significant bits), widened to fp32, times g (one fp32 RNE multiply), then
 // bf16 RNE. Consecutive lanes take consecutive halves of one output row, so
-// the 16-byte stores and the 4-byte loads are coalesced.
-#include "device_common.hpp"
+// the 16-byte stores and the 4-byte loads are coalesced. FP8 caches take the
+// same lanes: 8 code bytes -> bf16_RNE(fp32(fp8) * g).
+#include "quantize.hpp"
 #include "launch.hpp"
 
 namespace nvfp4kv {
 
-template <int D>
+template <int D, int FMT>
 __global__ __launch_bounds__(256) void dequant_kernel(Pool pool, const int32_t* __restrict__ block_table,
                                                       int32_t max_blocks, const int32_t* __restrict__ seq_lens,
                                                       const int32_t* __restrict__ cu_out, int32_t cap_len,
@@ -48,16 +49,20 @@ __global__ __launch_bounds__(256) void dequant_kernel(Pool pool, const int32_t* 
     if (orow < 0 || orow >= out_rows) continue;
     const uint8_t* src = pool.data + blk * pool.sb + kv * pool.skv + r * pool.st + h * pool.sh;
     uint32_t o[4];
-    dequant_half8(ld_u32(src + hb * 4), ld_u8(src + D / 2 + hb / 2), kv ? gv : gk, o);
+    if constexpr (FMT == kNvfp4)
+      dequant_half8(ld_u32(src + hb * 4), ld_u8(src + D / 2 + hb / 2), kv ? gv : gk, o);
+    else
+      dequant_fp8x8<FMT>(ld_u32x2(src + hb * 8), kv ? gv : gk, o);
     uint16_t* dst = (kv ? out_v : out_k) + (orow * hkv + h) * D + hb * 8;
     *reinterpret_cast<u32x4*>(dst) = u32x4{o[0], o[1], o[2], o[3]};
   }
 }
 
-hipError_t launch_dequant(const Pool& pool, int head_size, const int32_t* block_table, int32_t max_blocks,
-                          const int32_t* seq_lens, const int32_t* cu_out, int32_t num_seqs, int32_t max_seq_len,
-                          const float* k_scale, const float* v_scale, void* out_k, void* out_v,
-                          int64_t out_rows, hipStream_t stream) {
+template <int FMT>
+static hipError_t launch_dequant_f(const Pool& pool, int head_size, const int32_t* block_table, int32_t max_blocks,
+                                   const int32_t* seq_lens, const int32_t* cu_out, int32_t num_seqs,
+                                   int32_t max_seq_len, const float* k_scale, const float* v_scale, void* out_k,
+                                   void* out_v, int64_t out_rows, hipStream_t stream) {
   if (num_seqs == 0 || max_seq_len <= 0) return hipSuccess;
   int64_t cap = (int64_t)max_blocks * pool.bs;
   if (cap > max_seq_len) cap = max_seq_len;
@@ -68,21 +73,40 @@ hipError_t launch_dequant(const Pool& pool, int head_size, const int32_t* block_
   uint16_t* ov = static_cast<uint16_t*>(out_v);
   switch (head_size) {
     case 64:
-      dequant_kernel<64><<<grid, 256, 0, stream>>>(pool, block_table, max_blocks, seq_lens, cu_out, (int32_t)cap,
+      dequant_kernel<64, FMT><<<grid, 256, 0, stream>>>(pool, block_table, max_blocks, seq_lens, cu_out, (int32_t)cap,
                                                    k_scale, v_scale, ok, ov, out_rows);
       break;
     case 128:
-      dequant_kernel<128><<<grid, 256, 0, stream>>>(pool, block_table, max_blocks, seq_lens, cu_out, (int32_t)cap,
+      dequant_kernel<128, FMT><<<grid, 256, 0, stream>>>(pool, block_table, max_blocks, seq_lens, cu_out, (int32_t)cap,
                                                     k_scale, v_scale, ok, ov, out_rows);
       break;
     case 256:
-      dequant_kernel<256><<<grid, 256, 0, stream>>>(pool, block_table, max_blocks, seq_lens, cu_out, (int32_t)cap,
+      dequant_kernel<256, FMT><<<grid, 256, 0, stream>>>(pool, block_table, max_blocks, seq_lens, cu_out, (int32_t)cap,
                                                     k_scale, v_scale, ok, ov, out_rows);
       break;
     default:
       return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_dequant(const Pool& pool, int head_size, const int32_t* block_table, int32_t max_blocks,
+                          const int32_t* seq_lens, const int32_t* cu_out, int32_t num_seqs, int32_t max_seq_len,
+                          const float* k_scale, const float* v_scale, void* out_k, void* out_v,
+                          int64_t out_rows, int fmt, hipStream_t stream) {
+  switch (fmt) {
+    case kNvfp4:
+      return launch_dequant_f<kNvfp4>(pool, head_size, block_table, max_blocks, seq_lens, cu_out, num_seqs,
+                                      max_seq_len, k_scale, v_scale, out_k, out_v, out_rows, stream);
+    case kFp8E4M3:
+      return launch_dequant_f<kFp8E4M3>(pool, head_size, block_table, max_blocks, seq_lens, cu_out, num_seqs,
+                                        max_seq_len, k_scale, v_scale, out_k, out_v, out_rows, stream);
+    case kFp8E5M2:
+      return launch_dequant_f<kFp8E5M2>(pool, head_size, block_table, max_blocks, seq_lens, cu_out, num_seqs,
+                                        max_seq_len, k_scale, v_scale, out_k, out_v, out_rows, stream);
+    default:
+      return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace nvfp4kv

@@ -30,6 +30,15 @@ __device__ __forceinline__ uint32_t ld_u32(const uint8_t* p) { return *reinterpr
 __device__ __forceinline__ u32x2 ld_u32x2(const uint8_t* p) { return reinterpret_cast<const A4x2*>(p)->v; }
 __device__ __forceinline__ u32x4 ld_u32x4(const uint8_t* p) { return reinterpret_cast<const A4x4*>(p)->v; }
 __device__ __forceinline__ void st_u32x2(uint8_t* p, u32x2 v) { reinterpret_cast<A4x2*>(p)->v = v; }
+__device__ __forceinline__ void st_u32x4(uint8_t* p, u32x4 v) { reinterpret_cast<A4x4*>(p)->v = v; }
+
+// Cache formats [P40177 "Key source snippets": nvfp4 beside fp8_e4m3 and
+// fp8_e5m2 in the backend's KV cache dtypes]. An NVFP4 row is D/2 code bytes
+// then D/16 E4M3 block scales; an FP8 row is D codes under the per-tensor
+// scale alone.
+constexpr int kNvfp4 = 0;
+constexpr int kFp8E4M3 = 1;
+constexpr int kFp8E5M2 = 2;
 
 // Pool geometry, strides in bytes (see nvfp4kv_cache).
 struct Pool {
@@ -98,6 +107,14 @@ __device__ __forceinline__ h2 fp4x2_to_h2(uint32_t w) {
 template <bool HI>
 __device__ __forceinline__ h2 fp8x2_to_h2(uint32_t w) {
   return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI);
+}
+
+// f16 pair {byte A of a, byte B of b} of E5M2 codes: E5M2 is the upper byte
+// of a binary16, so one byte permute (zeros below) converts exactly.
+template <int A, int B>
+__device__ __forceinline__ h2 e5m2x2_to_h2(uint32_t a, uint32_t b) {
+  constexpr uint32_t sel = ((uint32_t)(4 + B) << 24) | (0x0Cu << 16) | ((uint32_t)A << 8) | 0x0Cu;
+  return __builtin_bit_cast(h2, __builtin_amdgcn_perm(b, a, sel));
 }
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }

@@ -10,14 +10,16 @@
 
 namespace nvfp4kv {
 
+// `fmt` below is the cache format: kNvfp4, kFp8E4M3 or kFp8E5M2.
 hipError_t launch_append(const Pool& pool, int head_size, const void* key, int64_t k_st, int64_t k_sh,
                          const void* value, int64_t v_st, int64_t v_sh, const int64_t* slots,
-                         int64_t num_tokens, const float* k_scale, const float* v_scale, hipStream_t stream);
+                         int64_t num_tokens, const float* k_scale, const float* v_scale, int fmt,
+                         hipStream_t stream);
 
 hipError_t launch_dequant(const Pool& pool, int head_size, const int32_t* block_table, int32_t max_blocks,
                           const int32_t* seq_lens, const int32_t* cu_out, int32_t num_seqs, int32_t max_seq_len,
                           const float* k_scale, const float* v_scale, void* out_k, void* out_v,
-                          int64_t out_rows, hipStream_t stream);
+                          int64_t out_rows, int fmt, hipStream_t stream);
 
 hipError_t launch_dequant_pages(const Pool& pool, int head_size, const int32_t* page_ids, int32_t num_pages,
                                 const float* k_scale, const float* v_scale, void* out, int64_t ob, int64_t okv,
@@ -36,7 +38,7 @@ hipError_t launch_decode(const Pool& pool, int head_size, const void* q, int64_t
                          int num_q_heads, const int32_t* block_table, int32_t max_blocks,
                          const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len, const float* k_scale,
                          const float* v_scale, float sm_scale, const float* o_scale, void* out, void* workspace,
-                         hipStream_t stream);
+                         int fmt, hipStream_t stream);
 
 // FP8-E4M3 bytes -> bf16: bf16 RNE of fp32(e4m3 * o_scale); n a multiple of 8.
 hipError_t launch_fp8_to_bf16(const void* in, int64_t n, const float* o_scale, void* out, hipStream_t stream);
@@ -45,10 +47,11 @@ hipError_t launch_act_quant(const void* x, int64_t x_row_stride, int32_t m, int3
 
 // Decode kernel a call with these sizes launches on the current device:
 // 1 = one workgroup per (sequence, kv head), 0 = split-K, -1 = bad head size.
-int decode_plan(int num_seqs, int num_kv_heads, int head_size, int block_size, int max_blocks, int max_seq_len);
+int decode_plan(int num_seqs, int num_kv_heads, int head_size, int block_size, int max_blocks, int max_seq_len,
+                int fmt);
 
 // Dynamic LDS bytes of the decode split kernel (must stay within 160 KiB).
-size_t decode_lds_bytes(int num_seqs, int grp, int head_size);
+size_t decode_lds_bytes(int num_seqs, int grp, int head_size, int fmt);
 
 hipError_t launch_prefill(const Pool& pool, int head_size, const void* q, int64_t q_st, int64_t q_sh,
                           int num_q_heads, const int32_t* cu_q, int32_t max_q_len, int32_t total_q,

@@ -55,4 +55,54 @@ __device__ __forceinline__ uint32_t quantize_block16(const float (&x)[16], float
   return s8;
 }
 
+// ---- FP8 KV rows [P40177 "Key source snippets": fp8_e4m3 / fp8_e5m2 cache
+// dtypes]: code = FP8(RN32(x / g)), value = RN32(fp8 * g) ----------------
+
+// fp32 -> FP8 byte, round to nearest even, magnitudes from the largest
+// finite value up (infinity included) saturating to it, sign copied. E5M2:
+// in binade [2^e, 2^(e+1)), e clamped to >= -14 (the subnormal step 2^-16
+// continues below), n = rint(|q| * 2^(2-e)) and the byte is (e + 14) * 4 + n.
+template <int FMT>
+__device__ __forceinline__ uint32_t fp8_from_f32_sat(float q) {
+  const float a = __builtin_fabsf(q);
+  const uint32_t sign = (__float_as_uint(q) >> 24) & 0x80u;
+  if constexpr (FMT == kFp8E4M3) {
+    return e4m3_from_f32_sat(a) | sign;
+  } else {
+    if (!(a < 57344.0f)) return 0x7Bu | sign;
+    int e = (int)((__float_as_uint(a) >> 23) & 0xFFu) - 127;
+    e = e < -14 ? -14 : e;
+    const float n = __builtin_rintf(__builtin_ldexpf(a, 2 - e));
+    return (uint32_t)((e + 14) * 4 + (int)n) | sign;
+  }
+}
+
+// Four elements -> one word of FP8 codes (element k in byte k); g divides
+// each element (one correctly rounded fp32 division).
+template <int FMT>
+__device__ __forceinline__ uint32_t fp8_pack4(float a0, float a1, float a2, float a3, float g) {
+  return fp8_from_f32_sat<FMT>(__fdiv_rn(a0, g)) | (fp8_from_f32_sat<FMT>(__fdiv_rn(a1, g)) << 8) |
+         (fp8_from_f32_sat<FMT>(__fdiv_rn(a2, g)) << 16) | (fp8_from_f32_sat<FMT>(__fdiv_rn(a3, g)) << 24);
+}
+
+// Eight FP8 codes (element k in byte k) -> 4 words of bf16 pairs:
+// bf16_RNE(RN32(fp8 * g)); the codes convert to f16 exactly.
+template <int FMT>
+__device__ __forceinline__ void dequant_fp8x8(u32x2 c, float g, uint32_t (&o)[4]) {
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const uint32_t w = c[q];
+    h2 a, b;
+    if constexpr (FMT == kFp8E4M3) {
+      a = fp8x2_to_h2<false>(w);
+      b = fp8x2_to_h2<true>(w);
+    } else {
+      a = e5m2x2_to_h2<0, 1>(w, w);
+      b = e5m2x2_to_h2<2, 3>(w, w);
+    }
+    o[2 * q] = pack_bf16x2((float)a[0] * g, (float)a[1] * g);
+    o[2 * q + 1] = pack_bf16x2((float)b[0] * g, (float)b[1] * g);
+  }
+}
+
 }  // namespace nvfp4kv

@@ -60,14 +60,29 @@ typedef int32_t nvfp4kv_status;
  * Requirements: data 16-byte aligned, every stride a multiple of 4,
  * stride_token <= 2^26 and stride_kv <= 2^30 bytes (NVFP4KV_UNSUPPORTED
  * otherwise).
+ *
+ * kv_dtype selects the row format [P40177 "Key source snippets": the
+ * backend's KV cache dtypes list fp8_e4m3 and fp8_e5m2 beside nvfp4, and
+ * get_dtype_for_flashinfer maps them to float8_e4m3fn, float8_e5m2 and
+ * uint8]:
+ *   NVFP4KV_KV_NVFP4: the packed row above, full_dim = D/2 + D/16;
+ *   NVFP4KV_KV_FP8_E4M3 / _FP8_E5M2: D bytes, one OCP FP8 code per element
+ *     (E4M3FN: bias 7, largest 448, 0x7F/0xFF NaN; E5M2: bias 15, largest
+ *     57344), value fp8 * g. Every stride must then be a multiple of 16.
+ *     append, dequant_paged and decode take FP8 caches; prefill and
+ *     dequant_pages return NVFP4KV_UNSUPPORTED for them.
  */
+#define NVFP4KV_KV_NVFP4 0
+#define NVFP4KV_KV_FP8_E4M3 1
+#define NVFP4KV_KV_FP8_E5M2 2
+
 typedef struct nvfp4kv_cache {
   uint8_t* data;
   int64_t num_blocks;
   int32_t block_size;     /* 16, 32 or 64 */
   int32_t num_kv_heads;
   int32_t head_size;      /* 64, 128 or 256 */
-  int32_t reserved;       /* must be 0 */
+  int32_t kv_dtype;       /* NVFP4KV_KV_NVFP4 (0), _FP8_E4M3 (1) or _FP8_E5M2 (2) */
   int64_t stride_block;
   int64_t stride_kv;
   int64_t stride_token;
@@ -92,6 +107,8 @@ int32_t nvfp4_kv_full_dim(int32_t head_size);
  *   reciprocal of every non-zero block step is finite), the dequantisation
  *   multipliers. Per 16-element block: s = E4M3_RNE_sat(amax / (6 g)),
  *   codes = E2M1_RNE_sat(x * (1 / (s g))), each step one fp32 RNE operation.
+ *   FP8 caches: code = FP8_RNE(x / g) (one fp32 division), magnitudes from
+ *   the format's largest finite value up saturating to it, sign kept.
  *   Key and value values must be finite or infinite, never NaN.
  * num_tokens == 0 is a no-op.
  */
@@ -177,18 +194,21 @@ size_t nvfp4_paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num
  *     touched. Chosen when num_seqs * num_kv_heads is at least the device's
  *     compute-unit count and the longest sequence (max_seq_len, or
  *     max_blocks_per_seq * block_size when max_seq_len <= 0) needs at most 8
- *     steps of 32 keys per wave (12 waves per workgroup, 8 at head_size 256).
+ *     steps of 32 keys per wave (waves per workgroup: NVFP4 12, 8 at
+ *     head_size 256; FP8 12 at head_size 64, 8 at 128, 4 at 256).
  *   NVFP4KV_DECODE_SPLIT_K (0): every other batch; sequences are cut into
  *     units of about equal size, one per resident workgroup, and the last
  *     unit of a (sequence, kv head) to finish merges the others' partials.
- * Returns -1 for a head_size the library does not build. Both kernels give
+ * kv_dtype: the cache's NVFP4KV_KV_* format. Returns -1 for a head_size
+ * the library does not build or an unknown kv_dtype. Both kernels give
  * results within the same tolerance of the exact attention; bits may differ
  * between them.
  */
 #define NVFP4KV_DECODE_SPLIT_K 0
 #define NVFP4KV_DECODE_PER_PAIR 1
 int32_t nvfp4_paged_attention_decode_plan(int32_t num_seqs, int32_t num_kv_heads, int32_t head_size,
-                                          int32_t block_size, int32_t max_blocks_per_seq, int32_t max_seq_len);
+                                          int32_t block_size, int32_t max_blocks_per_seq, int32_t max_seq_len,
+                                          int32_t kv_dtype);
 
 /*
  * Decode attention over the quantised pages [P40177 "Implementation

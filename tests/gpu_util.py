@@ -35,9 +35,11 @@ def scale_dev(s, device="cuda") -> torch.Tensor:
 class Dev:
     """Device copies of a workload's inputs plus a pool of the chosen layout."""
 
-    def __init__(self, w, layout="HND", device="cuda"):
+    def __init__(self, w, layout="HND", device="cuda", kv_dtype="nvfp4"):
         self.w = w
-        self.pool = nvk.alloc_pool(w.num_blocks, w.block_size, w.num_kv_heads, w.head_size, layout, device)
+        self.kv_dtype = kv_dtype
+        self.pool = nvk.alloc_pool(w.num_blocks, w.block_size, w.num_kv_heads, w.head_size, layout, device,
+                                   kv_dtype=kv_dtype)
         self.key = bf16_dev(w.key, device)
         self.value = bf16_dev(w.value, device)
         self.slots = i64_dev(w.slot_mapping, device)
@@ -53,7 +55,8 @@ class Dev:
         nvk.append(self.pool, self.key, self.value, self.slots, self.k_scale, self.v_scale)
 
     def pool_logical(self) -> np.ndarray:
-        return self.pool.contiguous().cpu().numpy()
+        """The pool's bytes in logical order (any format, as uint8)."""
+        return self.pool.contiguous().view(torch.uint8).cpu().numpy()
 
     def decode(self, q=None, max_seq_len=None, ws=None):
         """Decode over the whole batch. max_seq_len defaults to the longest
@@ -92,9 +95,9 @@ class Dev:
         return ok, ov
 
 
-def oracle_pool(w) -> np.ndarray:
-    pool = np.zeros(O.pool_shape(w.num_blocks, w.block_size, w.num_kv_heads, w.head_size), np.uint8)
-    O.append(pool, w.key, w.value, w.slot_mapping, w.k_scale, w.v_scale)
+def oracle_pool(w, kv_dtype="nvfp4") -> np.ndarray:
+    pool = np.zeros(O.pool_shape(w.num_blocks, w.block_size, w.num_kv_heads, w.head_size, kv_dtype), np.uint8)
+    O.append(pool, w.key, w.value, w.slot_mapping, w.k_scale, w.v_scale, kv_dtype)
     return pool
 
 

@@ -41,7 +41,7 @@ def test_full_dim_and_status_strings():
 
 
 def _desc(**kw):
-    base = dict(data=16 * 1024, num_blocks=4, block_size=16, num_kv_heads=2, head_size=128, reserved=0,
+    base = dict(data=16 * 1024, num_blocks=4, block_size=16, num_kv_heads=2, head_size=128, kv_dtype=0,
                 stride_block=2 * 2 * 16 * 72, stride_kv=2 * 16 * 72, stride_token=72, stride_head=16 * 72)
     base.update(kw)
     return nvk.CacheDesc(**base)
@@ -60,7 +60,9 @@ def test_append_validation():
     assert _append(_desc(data=None)) == 1
     assert _append(_desc(head_size=96)) == 2
     assert _append(_desc(block_size=8)) == 2
-    assert _append(_desc(reserved=1)) == 1
+    assert _append(_desc(kv_dtype=3)) == 1 and _append(_desc(kv_dtype=-1)) == 1
+    # FP8 rows need 16-byte strides (72 is a packed NVFP4 width)
+    assert _append(_desc(kv_dtype=1)) == 1
     assert _append(_desc(stride_token=70)) == 1
     assert _append(_desc(stride_token=(1 << 26) + 4)) == 2
     assert _append(_desc(stride_kv=(1 << 30) + 4)) == 2
@@ -120,6 +122,7 @@ def test_decode_plan_rejects_bad_sizes():
     assert nvk.decode_plan(-1, 2, 128, 16, 8, 100) == -1
     assert nvk.decode_plan(4, 2, 128, 0, 8, 100) == -1
     assert nvk.decode_plan(4, 2, 128, 16, 0, 100) == -1
+    assert nvk.library().nvfp4_paged_attention_decode_plan(4, 2, 128, 16, 8, 100, 3) == -1  # unknown format
 
 
 def test_quant_activations_sizes_and_rejects():

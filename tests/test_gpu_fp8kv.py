@@ -1,0 +1,153 @@
+"""Parity of FP8 (E4M3FN, E5M2) KV caches [P40177 "Key source snippets":
+fp8_e4m3 / fp8_e5m2 beside nvfp4] through the same append, paged dequantize
+and decode kernels as NVFP4: stored bytes and dequantised values bit-exact
+against the oracle, decode within |gpu - ref| <= 2e-3 + 1e-2 |ref| of the
+oracle's fp64 attention on the same FP8 cache, on the per-pair and the
+split-K paths."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import bit_quantized_paged_amd as nvk
+from oracle import nvfp4_oracle as O
+from workloads import fp8_kv_scales, make_config, make_workload
+from gpu_util import Dev, assert_attn_close, bf16_to_np, oracle_pool
+
+pytestmark = pytest.mark.gpu
+
+KV = ["fp8_e4m3", "fp8_e5m2"]
+
+CASES = {
+    "c1_d64_bs16": lambda: make_config(1),
+    "c2_d128_bs16": lambda: make_config(2, scale=0.08),
+    "c5_d256_bs16": lambda: make_config(5, scale=0.05),
+    "d128_bs64_gqa4": lambda: make_workload(seed=21, name="x", seq_lens=[1, 63, 64, 65, 200, 129],
+                                            q_lens=[1, 1, 1, 1, 1, 1], num_q_heads=16, num_kv_heads=4,
+                                            head_size=128, block_size=64),
+    "d64_bs32_mha": lambda: make_workload(seed=22, name="x", seq_lens=[33, 95, 7], q_lens=[1, 1, 1],
+                                          num_q_heads=3, num_kv_heads=3, head_size=64, block_size=32),
+}
+
+
+def _fp8(w, kv):
+    ks, vs = fp8_kv_scales(w, kv)
+    return dataclasses.replace(w, k_scale=ks, v_scale=vs)
+
+
+def _decode_rows(w):
+    """One decode query per sequence: the last query row of each."""
+    if np.all(w.q_lens == 1):
+        return w
+    qrows = w.cu_q[1:] - 1
+    return dataclasses.replace(w, q_lens=np.ones(w.num_seqs, np.int32), query=w.query[qrows],
+                               cu_q=np.arange(w.num_seqs + 1, dtype=np.int32))
+
+
+@pytest.mark.parametrize("layout", ["HND", "NHD"])
+@pytest.mark.parametrize("kv", KV)
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_fp8_append_and_dequant_bitexact(name, kv, layout):
+    w = _fp8(CASES[name](), kv)
+    d = Dev(w, layout, kv_dtype=kv)
+    d.append_all()
+    torch.cuda.synchronize()
+    ref = oracle_pool(w, kv)
+    got = d.pool_logical()
+    bad = np.argwhere(got != ref)
+    assert bad.size == 0, f"{name}/{kv}/{layout}: {len(bad)} bytes differ, first at {bad[:3].tolist()}"
+    ok, ov = d.dequant()
+    torch.cuda.synchronize()
+    rk, rv = O.dequant_paged(ref, w.block_table, w.seq_lens, w.k_scale, w.v_scale, w.head_size, kv)
+    assert np.array_equal(bf16_to_np(ok), rk) and np.array_equal(bf16_to_np(ov), rv)
+
+
+@pytest.mark.parametrize("kv", KV)
+def test_fp8_append_saturates_like_the_oracle(kv):
+    """A scale far below amax / max_finite: most values saturate to the
+    largest finite code (sign kept), small ones round into subnormals."""
+    w = CASES["c2_d128_bs16"]()
+    w = dataclasses.replace(w, k_scale=np.float32(w.k_scale) * np.float32(1e-3), v_scale=np.float32(1e-7))
+    d = Dev(w, "HND", kv_dtype=kv)
+    d.append_all()
+    torch.cuda.synchronize()
+    assert np.array_equal(d.pool_logical(), oracle_pool(w, kv))
+
+
+@pytest.mark.parametrize("layout", ["HND", "NHD"])
+@pytest.mark.parametrize("kv", KV)
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_fp8_decode_parity(name, kv, layout):
+    w = _decode_rows(_fp8(CASES[name](), kv))
+    d = Dev(w, layout, kv_dtype=kv)
+    d.append_all()
+    out = d.decode()
+    torch.cuda.synchronize()
+    ref = O.paged_attention(oracle_pool(w, kv), w.query, w.cu_q, w.block_table, w.seq_lens, w.k_scale,
+                            w.v_scale, np.float32(d.sm_scale), w.head_size, kv_dtype=kv)
+    assert_attn_close(out, ref, f"{name}/{kv}/{layout} decode")
+
+
+# (head size, q heads, kv heads, block size, batch, longest) with at least one
+# (sequence, kv head) pair per CU and lengths the per-pair path takes for FP8
+# (8 steps of 32 keys per wave: 12 waves at D = 64, 8 at 128, 4 at 256)
+PAIR_CASES = {
+    "d128_gqa2_bs16": (128, 16, 8, 16, 32, 2048),
+    "d64_gqa4_bs32": (64, 16, 4, 32, 64, 3072),
+    "d256_gqa8_bs16": (256, 16, 2, 16, 128, 1024),
+}
+
+
+@pytest.mark.parametrize("kv", KV)
+@pytest.mark.parametrize("name", sorted(PAIR_CASES))
+def test_fp8_decode_per_pair_and_split(name, kv):
+    D, hq, hkv, bs, B, lmax = PAIR_CASES[name]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert B * hkv >= cus
+    rng = np.random.default_rng(43)
+    lens = rng.integers(1, lmax + 1, size=B).astype(np.int32)
+    lens[:7] = [1, 31, 32, 33, bs - 1, bs + 1, lmax]
+    w = make_workload(seed=52, name="pairs", seq_lens=lens, q_lens=np.ones(B, np.int32), num_q_heads=hq,
+                      num_kv_heads=hkv, head_size=D, block_size=bs)
+    w = dataclasses.replace(w, query=w.query[w.cu_q[1:] - 1], cu_q=np.arange(B + 1, dtype=np.int32))
+    w = _fp8(w, kv)
+    mb = w.block_table.shape[1]
+    assert nvk.decode_plan(B, hkv, D, bs, mb, int(lens.max()), kv) == nvk.DECODE_PER_PAIR
+    d = Dev(w, "HND", kv_dtype=kv)
+    d.append_all()
+    out = d.decode()
+    torch.cuda.synchronize()
+    ref = O.paged_attention(oracle_pool(w, kv), w.query, w.cu_q, w.block_table, w.seq_lens, w.k_scale, w.v_scale,
+                            np.float32(d.sm_scale), D, kv_dtype=kv)
+    assert_attn_close(out, ref, f"{name}/{kv} per pair")
+    wide = np.pad(w.block_table, ((0, 0), (0, (lmax * 4) // bs)), constant_values=0)
+    assert nvk.decode_plan(B, hkv, D, bs, wide.shape[1], 0, kv) == nvk.DECODE_SPLIT_K
+    d.bt = torch.from_numpy(np.ascontiguousarray(wide, dtype=np.int32)).cuda()
+    out_split = d.decode(max_seq_len=0)
+    torch.cuda.synchronize()
+    assert_attn_close(out_split, ref, f"{name}/{kv} split-K")
+
+
+@pytest.mark.parametrize("kv", KV)
+def test_fp8_decode_long_sequences(kv):
+    w = _fp8(make_workload(seed=33, name="long", seq_lens=[16384, 9001, 1], q_lens=[1, 1, 1], num_q_heads=32,
+                           num_kv_heads=8, head_size=128, block_size=16), kv)
+    d = Dev(w, "HND", kv_dtype=kv)
+    d.append_all()
+    out = d.decode()
+    torch.cuda.synchronize()
+    ref = O.paged_attention(oracle_pool(w, kv), w.query, w.cu_q, w.block_table, w.seq_lens, w.k_scale, w.v_scale,
+                            np.float32(d.sm_scale), 128, kv_dtype=kv)
+    assert_attn_close(out, ref, f"{kv} long")
+
+
+def test_fp8_cache_rejected_where_not_built():
+    w = _fp8(CASES["c1_d64_bs16"](), "fp8_e4m3")
+    d = Dev(w, "HND", kv_dtype="fp8_e4m3")
+    with pytest.raises(nvk.NVFP4KVError):
+        d.prefill()
+    with pytest.raises(nvk.NVFP4KVError):
+        out = torch.empty((w.num_blocks, 2, w.block_size, w.num_kv_heads, w.head_size), dtype=torch.bfloat16,
+                          device="cuda")
+        nvk.dequant_pages(d.pool, None, d.k_scale, d.v_scale, out)

@@ -5,4 +5,4 @@ tables, slot mappings, bf16 K/V/Q, the per-tensor kv scale of the recipe).
 It holds none of the cache's arithmetic, so both the HIP path and the CPU
 oracle can take their inputs from it.
 """
-from .gen import Workload, make_workload, make_config, make_activations, CONFIG_NAMES  # noqa: F401
+from .gen import Workload, make_workload, make_config, make_activations, fp8_kv_scales, CONFIG_NAMES  # noqa: F401

@@ -273,3 +273,13 @@ def make_activations(seed: int, m: int, k: int, outlier_frac: float = 0.01, outl
     bits = _to_bf16_bits(x)
     g = np.float32(_bf16_bits_absmax(bits) / np.float32(6 * 448))
     return bits, (g if g != 0 else np.float32(1.0))
+
+
+def fp8_kv_scales(w: Workload, kv_dtype: str):
+    """Per-tensor kv scales for an FP8 cache of workload w: amax / 448
+    (E4M3) or amax / 57344 (E5M2) in fp32 over each whole bf16 tensor, so that
+    the largest magnitude lands on the format's largest finite value."""
+    top = {"fp8_e4m3": np.float32(448.0), "fp8_e5m2": np.float32(57344.0)}[kv_dtype]
+    ks = np.float32(_bf16_bits_absmax(w.key) / top)
+    vs = np.float32(_bf16_bits_absmax(w.value) / top)
+    return (ks if ks != 0 else np.float32(1.0)), (vs if vs != 0 else np.float32(1.0))
