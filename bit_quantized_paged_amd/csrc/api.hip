@@ -327,7 +327,6 @@ static nvfp4kv_status prefill_impl(const nvfp4kv_cache* cache, const void* q, in
   int fmt = 0;
   nvfp4kv_status s = check_cache(cache, p, &fmt);
   if (s) return s;
-  if (fmt != nvfp4kv::kNvfp4) return fail(NVFP4KV_UNSUPPORTED, "chunked prefill reads NVFP4 caches only");
   if (num_seqs < 0 || num_seqs > 65535) return fail(NVFP4KV_INVALID_ARGUMENT, "num_seqs must be in [0, 65535]");
   if (num_q_heads < 1 || num_q_heads % p.hkv != 0)
     return fail(NVFP4KV_INVALID_ARGUMENT, "num_q_heads must be a positive multiple of num_kv_heads");
@@ -346,7 +345,7 @@ static nvfp4kv_status prefill_impl(const nvfp4kv_cache* cache, const void* q, in
   return hip_status(nvfp4kv::launch_prefill(p, cache->head_size, q, q_stride_token, q_stride_head, num_q_heads,
                                             cu_seqlens_q, max_q_len, total_q, block_table, max_blocks_per_seq,
                                             seq_lens, num_seqs, max_seq_len, k_scale, v_scale, sm_scale,
-                                            causal ? 1 : 0, o_scale, out, static_cast<hipStream_t>(stream)),
+                                            causal ? 1 : 0, o_scale, out, fmt, static_cast<hipStream_t>(stream)),
                     "nvfp4_paged_attention_prefill launch");
 }
 

@@ -786,27 +786,31 @@ __device__ __forceinline__ void store_column_fp8(uint8_t* orow, const f4 (&acc)[
 
 // Prefill ring stages: the step being dequantised and up to three in flight
 // (as many as the 6-bit wait counter can cover).
-template <int D, bool COMPACT>
+// NVFP4: as many stages (up to 4) as the vmcnt counter can track. FP8
+// stages are 1.8x larger: 2 at D >= 128 keep three workgroups per CU at
+// D = 128 (48 KB each), as NVFP4 has.
+template <int D, bool COMPACT, int FMT = kNvfp4>
 struct PrefillStages {
-  static constexpr int NC = StageGeo<D, COMPACT>::NC;
-  static constexpr int NS = (63 / NC + 1) < 4 ? (63 / NC + 1) : 4;
+  static constexpr int NC = StageGeo<D, COMPACT, FMT>::NC;
+  static constexpr int NS_MAX = (FMT == kNvfp4 || D == 64) ? 4 : 2;
+  static constexpr int NS = (63 / NC + 1) < NS_MAX ? (63 / NC + 1) : NS_MAX;
 };
 
 // Waves per SIMD the prefill register budget is sized for: without the hint
 // the compiler spends the whole 256-register budget of two waves (or more)
 // at head sizes 64 and 128; at 256 two waves would spill.
-template <int D>
+template <int D, int FMT = kNvfp4>
 struct PrefillOcc {
   static constexpr int waves = (D == 256) ? 1 : 2;
 };
 
-template <int D, int NT, bool COMPACT, bool FP8OUT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PrefillOcc<D>::waves))) void prefill_kernel(
+template <int D, int NT, bool COMPACT, bool FP8OUT, int FMT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PrefillOcc<D, FMT>::waves))) void prefill_kernel(
     PrefillArgs a) {
   using G = Geo<D>;
-  using SG = StageGeo<D, COMPACT>;
+  using SG = StageGeo<D, COMPACT, FMT>;
   using OG = OpGeo<D>;
-  constexpr int NS = PrefillStages<D, COMPACT>::NS;
+  constexpr int NS = PrefillStages<D, COMPACT, FMT>::NS;
   extern __shared__ __align__(16) char smem[];
   uint8_t* ring = reinterpret_cast<uint8_t*>(smem);  // [NS] raw steps
   uint8_t* opbuf = ring + NS * SG::STAGE;             // [2] operand buffers
@@ -855,8 +859,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PrefillOcc<
   kw = kw > L ? L : (kw < 0 ? 0 : kw);
   const int min_full = a.causal ? L - qlen + col_base / grp + 1 : L;
   const int32_t* bt_row = a.bt + (int64_t)b * a.max_blocks;
-  const DmaOffsets<D, COMPACT> dof = dma_offsets<D, COMPACT>(a.pool.st, a.pool.skv, lane);
-  const LdsLane ll = lds_lane<D>(i, j);
+  const DmaOffsets<D, COMPACT, FMT> dof = dma_offsets<D, COMPACT, FMT>(a.pool.st, a.pool.skv, lane);
+  const LdsLane ll = lds_lane<D, FMT>(i, j);
   const uint32_t op_lane = lds_addr(opbuf) + lane * 16;
 
   // ---- the four waves share each 32-key step: wave 0 copies it into the
@@ -871,21 +875,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PrefillOcc<
   if (copier) {
 #pragma unroll
     for (int s = 0; s < NS - 1; ++s)
-      dma_step<D, COMPACT>(ring + s * SG::STAGE, a.pool, ids_for_step(bt_row, s, steps, L, a.pool), h, s * kStep,
-                           dof);
+      dma_step<D, COMPACT, FMT>(ring + s * SG::STAGE, a.pool, ids_for_step(bt_row, s, steps, L, a.pool), h,
+                                s * kStep, dof);
   }
   StepIds nxt = ids_for_step(bt_row, NS - 1, steps, L, a.pool);
   for (int k = 0; k < steps; ++k) {
     if (copier)
-      dma_step<D, COMPACT>(ring + ((k + NS - 1) % NS) * SG::STAGE, a.pool, nxt, h, (k + NS - 1) * kStep, dof);
+      dma_step<D, COMPACT, FMT>(ring + ((k + NS - 1) % NS) * SG::STAGE, a.pool, nxt, h, (k + NS - 1) * kStep, dof);
     nxt = ids_for_step(bt_row, k + NS, steps, L, a.pool);
     wait_vmcnt<(NS - 1) * SG::NC>();  // the copier: step k has landed (others: no-op)
     lds_barrier();          // every wave may read step k
-    SubRaw<D> R[2];
-    lds_read_step_async_safe<D>(R, ring + (k % NS) * SG::STAGE, ll);
+    SubRaw<D, FMT> R[2];
+    lds_read_step<D, FMT>(R, ring + (k % NS) * SG::STAGE, ll);
     const int kb = k * kStep;
-    if (kb + kStep > L) mask_step<D>(R, kb, L, j);
-    VPairs<D> vp[2];
+    if (kb + kStep > L) mask_step(R, kb, L, j);
+    VPairs<D, FMT> vp[2];
     make_pairs(R[0], vp[0]);
     make_pairs(R[1], vp[1]);
     const uint32_t slot = op_lane + (uint32_t)((k & 1) * OG::BYTES);
@@ -922,30 +926,47 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PrefillOcc<
   }
 }
 
-template <int D, bool COMPACT>
+template <int D, bool COMPACT, int FMT>
 size_t prefill_lds_bytes() {
-  return (size_t)PrefillStages<D, COMPACT>::NS * StageGeo<D, COMPACT>::STAGE + 2 * OpGeo<D>::BYTES;
+  return (size_t)PrefillStages<D, COMPACT, FMT>::NS * StageGeo<D, COMPACT, FMT>::STAGE + 2 * OpGeo<D>::BYTES;
+}
+
+template <int D, int NT, int FMT>
+static void launch_prefill_fp8(const PrefillArgs& a, const dim3& grid, hipStream_t stream) {
+  const size_t lds = prefill_lds_bytes<D, false, FMT>();
+  if (a.o_scale == nullptr)
+    prefill_kernel<D, NT, false, false, FMT><<<grid, 256, lds, stream>>>(a);
+  else
+    prefill_kernel<D, NT, false, true, FMT><<<grid, 256, lds, stream>>>(a);
 }
 
 template <int D, int NT>
-static hipError_t launch_prefill_t(const PrefillArgs& a, int num_seqs, int max_q_len, hipStream_t stream) {
+static hipError_t launch_prefill_t(const PrefillArgs& a, int num_seqs, int max_q_len, int fmt, hipStream_t stream) {
   const int64_t cols = (int64_t)max_q_len * a.grp;
   const int64_t per_wg = 4 * 16 * NT;
   const int64_t gx = (cols + per_wg - 1) / per_wg;
   if (gx == 0) return hipSuccess;
   const dim3 grid((unsigned)gx, (unsigned)a.pool.hkv, (unsigned)num_seqs);
+  if (fmt == kFp8E4M3 || fmt == kFp8E5M2) {
+    // FP8 rows are copied in 16-byte chunks whatever their stride
+    if (fmt == kFp8E4M3)
+      launch_prefill_fp8<D, NT, kFp8E4M3>(a, grid, stream);
+    else
+      launch_prefill_fp8<D, NT, kFp8E5M2>(a, grid, stream);
+    return hipGetLastError();
+  }
   // 16-byte copies need contiguous, 16-byte aligned page rows (HND layout)
   const bool compact = a.pool.st == D / 2 + D / 16 && a.pool.sb % 16 == 0 && a.pool.skv % 16 == 0 &&
                        a.pool.sh % 16 == 0 && (reinterpret_cast<uintptr_t>(a.pool.data) % 16) == 0;
   const bool fp8 = a.o_scale != nullptr;
   if (compact && !fp8)
-    prefill_kernel<D, NT, true, false><<<grid, 256, prefill_lds_bytes<D, true>(), stream>>>(a);
+    prefill_kernel<D, NT, true, false, kNvfp4><<<grid, 256, prefill_lds_bytes<D, true, kNvfp4>(), stream>>>(a);
   else if (compact)
-    prefill_kernel<D, NT, true, true><<<grid, 256, prefill_lds_bytes<D, true>(), stream>>>(a);
+    prefill_kernel<D, NT, true, true, kNvfp4><<<grid, 256, prefill_lds_bytes<D, true, kNvfp4>(), stream>>>(a);
   else if (!fp8)
-    prefill_kernel<D, NT, false, false><<<grid, 256, prefill_lds_bytes<D, false>(), stream>>>(a);
+    prefill_kernel<D, NT, false, false, kNvfp4><<<grid, 256, prefill_lds_bytes<D, false, kNvfp4>(), stream>>>(a);
   else
-    prefill_kernel<D, NT, false, true><<<grid, 256, prefill_lds_bytes<D, false>(), stream>>>(a);
+    prefill_kernel<D, NT, false, true, kNvfp4><<<grid, 256, prefill_lds_bytes<D, false, kNvfp4>(), stream>>>(a);
   return hipGetLastError();
 }
 
@@ -953,7 +974,8 @@ hipError_t launch_prefill(const Pool& pool, int head_size, const void* q, int64_
                           int num_q_heads, const int32_t* cu_q, int32_t max_q_len, int32_t total_q,
                           const int32_t* block_table, int32_t max_blocks, const int32_t* seq_lens,
                           int32_t num_seqs, int32_t max_seq_len, const float* k_scale, const float* v_scale,
-                          float sm_scale, int causal, const float* o_scale, void* out, hipStream_t stream) {
+                          float sm_scale, int causal, const float* o_scale, void* out, int fmt,
+                          hipStream_t stream) {
   (void)max_seq_len;
   if (num_seqs == 0 || max_q_len <= 0 || total_q <= 0) return hipSuccess;
   PrefillArgs a;
@@ -976,9 +998,9 @@ hipError_t launch_prefill(const Pool& pool, int head_size, const void* q, int64_
   a.out8 = static_cast<uint8_t*>(out);
   a.o_scale = o_scale;
   switch (head_size) {
-    case 64: return launch_prefill_t<64, 4>(a, num_seqs, max_q_len, stream);
-    case 128: return launch_prefill_t<128, 2>(a, num_seqs, max_q_len, stream);
-    case 256: return launch_prefill_t<256, 2>(a, num_seqs, max_q_len, stream);
+    case 64: return launch_prefill_t<64, 4>(a, num_seqs, max_q_len, fmt, stream);
+    case 128: return launch_prefill_t<128, 2>(a, num_seqs, max_q_len, fmt, stream);
+    case 256: return launch_prefill_t<256, 2>(a, num_seqs, max_q_len, fmt, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -145,13 +145,9 @@ __device__ __forceinline__ h8 k_chunk(const SubRaw<D, FMT>& R) {
 
 // Value rows of one subtile arranged for the V^T tiles.
 // NVFP4: each byte holds the codes of two keys (4j+2p, 4j+2p+1) at one d.
-// FP8 E4M3: per key pair p and word w of their rows, lo holds (byte 0 of key
-// 4j+2p, byte 0 of key 4j+2p+1, byte 1 of each) and hi the same for bytes 2
-// and 3, so one pair convert gives both keys at one d. E5M2 keeps the rows.
+// FP8: the rows as read; a tile takes its two keys' bytes with one permute.
 template <int D, int FMT = kNvfp4>
 struct VPairs {
-  uint32_t lo[2][D / 64];
-  uint32_t hi[2][D / 64];
   uint32_t raw[4][D / 64];
 };
 
@@ -178,15 +174,6 @@ __device__ __forceinline__ void make_pairs(const SubRaw<D, FMT>& R, VPairs<D, FM
     // (vs0, vs1) and (vs2, vs3) side by side in the low bytes: one permute each
     P.s[0] = fp8x2_to_h2<false>(__builtin_amdgcn_perm(R.vs[1], R.vs[0], 0x0C0C0400u));
     P.s[1] = fp8x2_to_h2<false>(__builtin_amdgcn_perm(R.vs[3], R.vs[2], 0x0C0C0400u));
-  } else if constexpr (FMT == kFp8E4M3) {
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-#pragma unroll
-      for (int w = 0; w < D / 64; ++w) {
-        P.lo[p][w] = __builtin_amdgcn_perm(R.v[2 * p + 1][w], R.v[2 * p][w], 0x05010400u);
-        P.hi[p][w] = __builtin_amdgcn_perm(R.v[2 * p + 1][w], R.v[2 * p][w], 0x07030602u);
-      }
-    }
   } else {
 #pragma unroll
     for (int r = 0; r < 4; ++r)
@@ -207,12 +194,11 @@ __device__ __forceinline__ h4 v_operand(const VPairs<D, FMT>& P) {
     a = fp4x2_to_h2<BYTE>(w0) * P.s[0];
     b = fp4x2_to_h2<BYTE>(w1) * P.s[1];
   } else if constexpr (FMT == kFp8E4M3) {
+    // byte B of keys (0, 1) and (2, 3) side by side, then one pair convert
     constexpr int W = T / 4;
-    constexpr int B = T % 4;
-    const uint32_t x0 = (B < 2) ? P.lo[0][W] : P.hi[0][W];
-    const uint32_t x1 = (B < 2) ? P.lo[1][W] : P.hi[1][W];
-    a = fp8x2_to_h2<(B & 1) != 0>(x0);
-    b = fp8x2_to_h2<(B & 1) != 0>(x1);
+    constexpr uint32_t sel = 0x0C0C0000u | ((uint32_t)(4 + T % 4) << 8) | (uint32_t)(T % 4);
+    a = fp8x2_to_h2<false>(__builtin_amdgcn_perm(P.raw[1][W], P.raw[0][W], sel));
+    b = fp8x2_to_h2<false>(__builtin_amdgcn_perm(P.raw[3][W], P.raw[2][W], sel));
   } else {
     constexpr int W = T / 4;
     constexpr int B = T % 4;
@@ -971,8 +957,8 @@ struct OpGeo {
 };
 
 // Operand E of the step, from its raw bytes (vp: make_pairs of both subtiles).
-template <int D, int E>
-__device__ __forceinline__ h8 make_op(const SubRaw<D> (&R)[2], const VPairs<D> (&vp)[2]) {
+template <int D, int E, int FMT>
+__device__ __forceinline__ h8 make_op(const SubRaw<D, FMT> (&R)[2], const VPairs<D, FMT> (&vp)[2]) {
   using G = Geo<D>;
   if constexpr (E < 2 * G::KW) {
     return k_chunk<D, E % G::KW>(R[E / G::KW]);
@@ -986,8 +972,9 @@ __device__ __forceinline__ h8 make_op(const SubRaw<D> (&R)[2], const VPairs<D> (
 
 // Build and store this wave's share of the step's operands (E = w, w + 4, ...)
 // at slot + E * 1024 (slot: this lane's place in the operand buffer).
-template <int D, int E>
-__device__ __forceinline__ void make_ops(const SubRaw<D> (&R)[2], const VPairs<D> (&vp)[2], int w, uint32_t slot) {
+template <int D, int E, int FMT>
+__device__ __forceinline__ void make_ops(const SubRaw<D, FMT> (&R)[2], const VPairs<D, FMT> (&vp)[2], int w,
+                                         uint32_t slot) {
   if constexpr (E < OpGeo<D>::NE) {
     if ((E & 3) == w) lds_store_op(slot + E * 1024, make_op<D, E>(R, vp));
     make_ops<D, E + 1>(R, vp, w, slot);

@@ -57,6 +57,6 @@ hipError_t launch_prefill(const Pool& pool, int head_size, const void* q, int64_
                           int num_q_heads, const int32_t* cu_q, int32_t max_q_len, int32_t total_q,
                           const int32_t* block_table, int32_t max_blocks, const int32_t* seq_lens,
                           int32_t num_seqs, int32_t max_seq_len, const float* k_scale, const float* v_scale,
-                          float sm_scale, int causal, const float* o_scale, void* out, hipStream_t stream);
+                          float sm_scale, int causal, const float* o_scale, void* out, int fmt, hipStream_t stream);
 
 }  // namespace nvfp4kv

@@ -142,11 +142,50 @@ def test_fp8_decode_long_sequences(kv):
     assert_attn_close(out, ref, f"{kv} long")
 
 
+PREFILL_CASES = {
+    "c4_d128_bs32": lambda: make_config(4, scale=0.06),
+    "c5_d256_bs16": lambda: make_config(5, scale=0.05),
+    "d128_bs64_gqa4": lambda: make_workload(seed=21, name="x", seq_lens=[1, 63, 64, 65, 200, 129],
+                                            q_lens=[1, 1, 5, 1, 17, 3], num_q_heads=16, num_kv_heads=4,
+                                            head_size=128, block_size=64),
+    "d64_bs32_mha": lambda: make_workload(seed=22, name="x", seq_lens=[33, 95, 7], q_lens=[1, 40, 7],
+                                          num_q_heads=3, num_kv_heads=3, head_size=64, block_size=32),
+}
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("kv", KV)
+@pytest.mark.parametrize("name", sorted(PREFILL_CASES))
+def test_fp8_prefill_parity(name, kv, causal):
+    w = _fp8(PREFILL_CASES[name](), kv)
+    d = Dev(w, "NHD" if causal else "HND", kv_dtype=kv)
+    d.append_all()
+    out = d.prefill(causal=causal)
+    torch.cuda.synchronize()
+    ref = O.paged_attention(oracle_pool(w, kv), w.query, w.cu_q, w.block_table, w.seq_lens, w.k_scale, w.v_scale,
+                            np.float32(d.sm_scale), w.head_size, causal=causal, kv_dtype=kv)
+    assert_attn_close(out, ref, f"{name}/{kv}/causal={causal} prefill")
+
+
+@pytest.mark.parametrize("kv", KV)
+def test_fp8_prefill_with_fp8_output(kv):
+    """FP8 cache in, FP8-E4M3 attention output out: decoded codes within half
+    an E4M3 step of the reference plus the attention tolerance."""
+    from test_gpu_parity import _fp8_close
+    w = _fp8(PREFILL_CASES["c4_d128_bs32"](), kv)
+    d = Dev(w, "HND", kv_dtype=kv)
+    d.append_all()
+    os = 0.03125
+    codes = d.prefill(o_scale=os)
+    torch.cuda.synchronize()
+    ref = O.paged_attention(oracle_pool(w, kv), w.query, w.cu_q, w.block_table, w.seq_lens, w.k_scale, w.v_scale,
+                            np.float32(d.sm_scale), w.head_size, kv_dtype=kv)
+    _fp8_close(codes, ref, os, f"{kv} prefill fp8 out")
+
+
 def test_fp8_cache_rejected_where_not_built():
     w = _fp8(CASES["c1_d64_bs16"](), "fp8_e4m3")
     d = Dev(w, "HND", kv_dtype="fp8_e4m3")
-    with pytest.raises(nvk.NVFP4KVError):
-        d.prefill()
     with pytest.raises(nvk.NVFP4KVError):
         out = torch.empty((w.num_blocks, 2, w.block_size, w.num_kv_heads, w.head_size), dtype=torch.bfloat16,
                           device="cuda")
