@@ -142,6 +142,48 @@ def test_fp8_decode_long_sequences(kv):
     assert_attn_close(out, ref, f"{kv} long")
 
 
+@pytest.mark.parametrize("kv", KV)
+def test_fp8_decode_fp8_output_and_graph_replays(kv):
+    """FP8 cache in, FP8-E4M3 output out (within half an E4M3 step plus the
+    attention tolerance); the bf16 decode captured in a HIP graph reproduces
+    the eager result on every replay, with eager work between replays."""
+    from test_gpu_parity import _fp8_close
+    w = _fp8(make_workload(seed=34, name="g", seq_lens=[700, 33, 4000, 129], q_lens=[1, 1, 1, 1],
+                           num_q_heads=16, num_kv_heads=8, head_size=128, block_size=16), kv)
+    d = Dev(w, "HND", kv_dtype=kv)
+    d.append_all()
+    ref = O.paged_attention(oracle_pool(w, kv), w.query, w.cu_q, w.block_table, w.seq_lens, w.k_scale, w.v_scale,
+                            np.float32(d.sm_scale), 128, kv_dtype=kv)
+    ws = torch.zeros(nvk.decode_workspace_size(w.num_seqs, 16, 8, 128), dtype=torch.uint8, device="cuda")
+    codes = torch.empty((w.num_seqs, 16, 128), dtype=torch.uint8, device="cuda")
+    os_t = torch.tensor([0.0625], dtype=torch.float32, device="cuda")
+    nvk.paged_attention_decode(d.pool, d.query, d.bt, d.seq_lens, int(w.seq_lens.max()), d.k_scale, d.v_scale,
+                               d.sm_scale, codes, ws, o_scale=os_t)
+    torch.cuda.synchronize()
+    _fp8_close(codes, ref, 0.0625, f"{kv} decode fp8 out")
+
+    eager = d.decode(ws=ws)
+    torch.cuda.synchronize()
+    assert_attn_close(eager, ref, f"{kv} eager")
+    out = torch.zeros_like(eager)
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(g, stream=st):
+            nvk.paged_attention_decode(d.pool, d.query, d.bt, d.seq_lens, int(w.seq_lens.max()), d.k_scale,
+                                       d.v_scale, d.sm_scale, out, ws)
+    torch.cuda.current_stream().wait_stream(st)
+    for k in range(3):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {k}"
+        again = d.decode(ws=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(again, eager)
+
+
 PREFILL_CASES = {
     "c4_d128_bs32": lambda: make_config(4, scale=0.06),
     "c5_d256_bs16": lambda: make_config(5, scale=0.05),
