@@ -153,7 +153,6 @@ nvfp4kv_status nvfp4_kv_dequant_pages(const nvfp4kv_cache* cache, const int32_t*
   int fmt = 0;
   nvfp4kv_status s = check_cache(cache, p, &fmt);
   if (s) return s;
-  if (fmt != nvfp4kv::kNvfp4) return fail(NVFP4KV_UNSUPPORTED, "page-form dequantize is for NVFP4 caches");
   if (num_pages < 0) return fail(NVFP4KV_INVALID_ARGUMENT, "num_pages must be >= 0");
   if (num_pages == 0) return ok();
   if (!k_scale || !v_scale) return fail(NVFP4KV_INVALID_ARGUMENT, "k_scale/v_scale is NULL");
@@ -164,7 +163,7 @@ nvfp4kv_status nvfp4_kv_dequant_pages(const nvfp4kv_cache* cache, const int32_t*
       return fail(NVFP4KV_INVALID_ARGUMENT, "out strides must be non-negative multiples of 8 elements");
   return hip_status(nvfp4kv::launch_dequant_pages(p, cache->head_size, page_ids, num_pages, k_scale, v_scale, out,
                                                   out_stride_block, out_stride_kv, out_stride_token, out_stride_head,
-                                                  static_cast<hipStream_t>(stream)),
+                                                  fmt, static_cast<hipStream_t>(stream)),
                     "nvfp4_kv_dequant_pages launch");
 }
 

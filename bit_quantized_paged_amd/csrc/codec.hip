@@ -8,6 +8,7 @@
 // QDQ: bf16 K/V rows are quantised exactly as the append writes them and
 // replaced, in place, by the values the dequantize returns for them.
 //
+// FP8 caches take the page-form dequantize with the same lanes (8 codes each).
 // Both are HBM-bound streams with one lane per 16-element block (8 code bytes
 // + 1 scale byte <-> 32 bytes of bf16); consecutive lanes take consecutive
 // blocks of one row, so the 32-byte bf16 accesses are coalesced.
@@ -16,7 +17,7 @@
 
 namespace nvfp4kv {
 
-template <int D>
+template <int D, int FMT>
 __global__ __launch_bounds__(256) void dequant_pages_kernel(Pool pool, const int32_t* __restrict__ page_ids,
                                                             int32_t num_pages, const float* __restrict__ k_scale,
                                                             const float* __restrict__ v_scale,
@@ -43,7 +44,10 @@ __global__ __launch_bounds__(256) void dequant_pages_kernel(Pool pool, const int
     const int r = rem / (NH * hkv);
     const uint8_t* src = pool.data + p * pool.sb + kv * pool.skv + r * pool.st + h * pool.sh;
     uint32_t o[4];
-    dequant_half8(ld_u32(src + hb * 4), ld_u8(src + D / 2 + hb / 2), kv ? gv : gk, o);
+    if constexpr (FMT == kNvfp4)
+      dequant_half8(ld_u32(src + hb * 4), ld_u8(src + D / 2 + hb / 2), kv ? gv : gk, o);
+    else
+      dequant_fp8x8<FMT>(ld_u32x2(src + hb * 8), kv ? gv : gk, o);
     *reinterpret_cast<u32x4*>(out + p * ob + kv * okv + r * ot + h * oh + hb * 8) = u32x4{o[0], o[1], o[2], o[3]};
   }
 }
@@ -105,28 +109,47 @@ hipError_t launch_fp8_to_bf16(const void* in, int64_t n, const float* o_scale, v
   return hipGetLastError();
 }
 
-hipError_t launch_dequant_pages(const Pool& pool, int head_size, const int32_t* page_ids, int32_t num_pages,
-                                const float* k_scale, const float* v_scale, void* out, int64_t ob, int64_t okv,
-                                int64_t ot, int64_t oh, hipStream_t stream) {
+template <int FMT>
+static hipError_t launch_dequant_pages_f(const Pool& pool, int head_size, const int32_t* page_ids, int32_t num_pages,
+                                         const float* k_scale, const float* v_scale, void* out, int64_t ob,
+                                         int64_t okv, int64_t ot, int64_t oh, hipStream_t stream) {
   if (num_pages == 0) return hipSuccess;
   uint16_t* o = static_cast<uint16_t*>(out);
   const dim3 grid((unsigned)num_pages);
   switch (head_size) {
     case 64:
-      dequant_pages_kernel<64><<<grid, 256, 0, stream>>>(pool, page_ids, num_pages, k_scale, v_scale, o, ob, okv, ot, oh);
+      dequant_pages_kernel<64, FMT><<<grid, 256, 0, stream>>>(pool, page_ids, num_pages, k_scale, v_scale, o, ob, okv, ot, oh);
       break;
     case 128:
-      dequant_pages_kernel<128><<<grid, 256, 0, stream>>>(pool, page_ids, num_pages, k_scale, v_scale, o, ob, okv, ot,
+      dequant_pages_kernel<128, FMT><<<grid, 256, 0, stream>>>(pool, page_ids, num_pages, k_scale, v_scale, o, ob, okv, ot,
                                                           oh);
       break;
     case 256:
-      dequant_pages_kernel<256><<<grid, 256, 0, stream>>>(pool, page_ids, num_pages, k_scale, v_scale, o, ob, okv, ot,
+      dequant_pages_kernel<256, FMT><<<grid, 256, 0, stream>>>(pool, page_ids, num_pages, k_scale, v_scale, o, ob, okv, ot,
                                                           oh);
       break;
     default:
       return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_dequant_pages(const Pool& pool, int head_size, const int32_t* page_ids, int32_t num_pages,
+                                const float* k_scale, const float* v_scale, void* out, int64_t ob, int64_t okv,
+                                int64_t ot, int64_t oh, int fmt, hipStream_t stream) {
+  switch (fmt) {
+    case kNvfp4:
+      return launch_dequant_pages_f<kNvfp4>(pool, head_size, page_ids, num_pages, k_scale, v_scale, out, ob, okv,
+                                            ot, oh, stream);
+    case kFp8E4M3:
+      return launch_dequant_pages_f<kFp8E4M3>(pool, head_size, page_ids, num_pages, k_scale, v_scale, out, ob, okv,
+                                              ot, oh, stream);
+    case kFp8E5M2:
+      return launch_dequant_pages_f<kFp8E5M2>(pool, head_size, page_ids, num_pages, k_scale, v_scale, out, ob, okv,
+                                              ot, oh, stream);
+    default:
+      return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_qdq(int head_size, void* key, int64_t k_st, int64_t k_sh, void* value, int64_t v_st, int64_t v_sh,

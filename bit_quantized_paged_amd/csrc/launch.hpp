@@ -23,7 +23,7 @@ hipError_t launch_dequant(const Pool& pool, int head_size, const int32_t* block_
 
 hipError_t launch_dequant_pages(const Pool& pool, int head_size, const int32_t* page_ids, int32_t num_pages,
                                 const float* k_scale, const float* v_scale, void* out, int64_t ob, int64_t okv,
-                                int64_t ot, int64_t oh, hipStream_t stream);
+                                int64_t ot, int64_t oh, int fmt, hipStream_t stream);
 
 hipError_t launch_qdq(int head_size, void* key, int64_t k_st, int64_t k_sh, void* value, int64_t v_st, int64_t v_sh,
                       int64_t num_tokens, int num_kv_heads, const float* k_scale, const float* v_scale,

@@ -69,8 +69,7 @@ typedef int32_t nvfp4kv_status;
  *   NVFP4KV_KV_FP8_E4M3 / _FP8_E5M2: D bytes, one OCP FP8 code per element
  *     (E4M3FN: bias 7, largest 448, 0x7F/0xFF NaN; E5M2: bias 15, largest
  *     57344), value fp8 * g. Every stride must then be a multiple of 16.
- *     append, dequant_paged, decode and prefill take FP8 caches;
- *     dequant_pages returns NVFP4KV_UNSUPPORTED for them.
+ *     Every entry point that takes a cache takes FP8 caches too.
  */
 #define NVFP4KV_KV_NVFP4 0
 #define NVFP4KV_KV_FP8_E4M3 1

@@ -339,7 +339,7 @@ def dequant_paged(pool: np.ndarray, block_table: np.ndarray, seq_lens: np.ndarra
 # ---------------------------------------------------------------------------
 
 
-def dequant_pages(pool: np.ndarray, page_ids, k_scale, v_scale, head_size: int) -> np.ndarray:
+def dequant_pages(pool: np.ndarray, page_ids, k_scale, v_scale, head_size: int, kv_dtype: str = "nvfp4") -> np.ndarray:
     """Page-form dequantize: every listed page of the logical pool (num_blocks,
     2, bs, Hkv, full_dim) becomes a bf16 page (2, bs, Hkv, D) whose rows are
     dequantize_rows of the packed rows, rounded to bf16, so that one block
@@ -347,8 +347,8 @@ def dequant_pages(pool: np.ndarray, page_ids, k_scale, v_scale, head_size: int) 
     bits in the order given."""
     ids = np.asarray(page_ids, dtype=np.int64)
     pages = pool[ids]                                       # [P, 2, bs, Hkv, fd]
-    k = f32_to_bf16(dequantize_rows(pages[:, 0], k_scale, head_size))
-    v = f32_to_bf16(dequantize_rows(pages[:, 1], v_scale, head_size))
+    k = f32_to_bf16(dequantize_kv(pages[:, 0], k_scale, head_size, kv_dtype))
+    v = f32_to_bf16(dequantize_kv(pages[:, 1], v_scale, head_size, kv_dtype))
     return np.stack([k, v], axis=1)
 
 

@@ -1,9 +1,9 @@
 """Parity of FP8 (E4M3FN, E5M2) KV caches [P40177 "Key source snippets":
-fp8_e4m3 / fp8_e5m2 beside nvfp4] through the same append, paged dequantize
-and decode kernels as NVFP4: stored bytes and dequantised values bit-exact
-against the oracle, decode within |gpu - ref| <= 2e-3 + 1e-2 |ref| of the
-oracle's fp64 attention on the same FP8 cache, on the per-pair and the
-split-K paths."""
+fp8_e4m3 / fp8_e5m2 beside nvfp4] through the same append, dequantize (paged
+and page-form), decode and chunked-prefill kernels as NVFP4: stored bytes and
+dequantised values bit-exact against the oracle, attention within
+|gpu - ref| <= 2e-3 + 1e-2 |ref| of the oracle's fp64 attention on the same
+FP8 cache, on the per-pair and split-K decode paths and in prefill."""
 import dataclasses
 
 import numpy as np
@@ -225,10 +225,27 @@ def test_fp8_prefill_with_fp8_output(kv):
     _fp8_close(codes, ref, os, f"{kv} prefill fp8 out")
 
 
-def test_fp8_cache_rejected_where_not_built():
-    w = _fp8(CASES["c1_d64_bs16"](), "fp8_e4m3")
-    d = Dev(w, "HND", kv_dtype="fp8_e4m3")
-    with pytest.raises(nvk.NVFP4KVError):
-        out = torch.empty((w.num_blocks, 2, w.block_size, w.num_kv_heads, w.head_size), dtype=torch.bfloat16,
-                          device="cuda")
-        nvk.dequant_pages(d.pool, None, d.k_scale, d.v_scale, out)
+@pytest.mark.parametrize("kv", KV)
+@pytest.mark.parametrize("name", ["c2_d128_bs16", "c5_d256_bs16", "d64_bs32_mha"])
+def test_fp8_dequant_pages_bitexact(name, kv):
+    """Page-form dequantize of an FP8 cache: all pages, then a subset with
+    repeats and ids outside the pool (skipped); unlisted pages untouched."""
+    from test_gpu_parity import _bf16_sentinel
+    w = _fp8(CASES[name](), kv)
+    nb, bs, hkv, D = w.num_blocks, w.block_size, w.num_kv_heads, w.head_size
+    d = Dev(w, "NHD", kv_dtype=kv)
+    d.append_all()
+    out = _bf16_sentinel((nb, 2, hkv, bs, D)).permute(0, 1, 3, 2, 4)
+    nvk.dequant_pages(d.pool, None, d.k_scale, d.v_scale, out)
+    torch.cuda.synchronize()
+    ref = O.dequant_pages(oracle_pool(w, kv), np.arange(nb), w.k_scale, w.v_scale, D, kv)
+    assert np.array_equal(bf16_to_np(out), ref), name
+    ids = np.array([nb - 1, 0, -1, nb, min(2, nb - 1)], np.int32)
+    out2 = _bf16_sentinel((nb, 2, bs, hkv, D))
+    nvk.dequant_pages(d.pool, torch.from_numpy(ids).cuda(), d.k_scale, d.v_scale, out2)
+    torch.cuda.synchronize()
+    got = bf16_to_np(out2)
+    listed = sorted({int(p) for p in ids if 0 <= p < nb})
+    assert np.array_equal(got[listed], ref[listed])
+    rest = [p for p in range(nb) if p not in listed]
+    assert np.all(got[rest] == 0xFFFF)
