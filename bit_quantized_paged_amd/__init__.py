@@ -1,4 +1,6 @@
-"""NVFP4-quantised paged KV cache for AMD Instinct MI355X (gfx950).
+"""NVFP4-quantised paged KV cache for AMD Instinct MI355X (gfx950), with FP8
+(E4M3FN, E5M2) caches through the same entry points and NVFP4 activation
+quantisation.
 
 Thin ctypes binding of ``libnvfp4kv.so`` (built from ``csrc/`` by
 ``bit_quantized_paged_amd.build``). The functions here only marshal torch
@@ -14,8 +16,9 @@ import os
 import torch
 
 __all__ = [
-    "NVFP4KVError", "library", "full_dim", "alloc_pool", "append", "dequant_paged",
-    "decode_workspace_size", "paged_attention_decode", "paged_attention_prefill",
+    "NVFP4KVError", "library", "full_dim", "row_bytes", "KV_DTYPES", "kv_dtype_of", "alloc_pool", "append",
+    "dequant_paged", "dequant_pages", "qdq", "decode_workspace_size", "decode_plan", "paged_attention_decode",
+    "paged_attention_prefill", "fp8_to_bf16", "quant_activations", "quant_activations_scale_bytes",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))

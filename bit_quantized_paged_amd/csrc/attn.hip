@@ -290,18 +290,18 @@ struct DecodeOcc {
 // landed when it returns.
 template <int D, bool COMPACT, int FMT, int NS, int NWS>
 __device__ __forceinline__ void decode_stream(WaveAttn<D, 1, FMT>& W, uint8_t* ring, const Pool& pool,
-                                              const int32_t* bt_row, int L, int h, int k0, int st1,
+                                              const int32_t* bt_row, int max_blocks, int L, int h, int k0, int st1,
                                               const uint16_t* qrow, float qk_factor,
                                               const DmaOffsets<D, COMPACT, FMT>& dof, const LdsLane& ll, int j) {
   using SG = StageGeo<D, COMPACT, FMT>;
   const auto qraw = WaveAttn<D, 1, FMT>::load_q_raw(qrow, j);
-  StepIds nxt = lds_prologue<D, COMPACT, NS, FMT>(ring, k0, NWS, st1, bt_row, L, pool, h, dof);
+  StepIds nxt = lds_prologue<D, COMPACT, NS, FMT>(ring, k0, NWS, st1, bt_row, L, max_blocks, pool, h, dof);
   W.set_q(0, qraw, qk_factor);
   int slot = 0;
   for (int k = k0; k < st1; k += NWS) {
     const int fill = (slot + NS - 1) % NS;
     dma_step<D, COMPACT, FMT>(ring + fill * SG::STAGE, pool, nxt, h, (k + (NS - 1) * NWS) * kStep, dof);
-    nxt = ids_for_step(bt_row, k + NS * NWS, st1, L, pool);
+    nxt = ids_for_step(bt_row, k + NS * NWS, st1, L, max_blocks, pool);
     wait_vmcnt<(NS - 1) * SG::NC>();
     SubRaw<D, FMT> R[2];
     lds_read_step<D, FMT>(R, ring + slot * SG::STAGE, ll);
@@ -432,7 +432,8 @@ decode_split_kernel(DecodeArgs a) {
     const uint16_t* qrow = valid ? a.q + (int64_t)b * a.q_st + (int64_t)(h * grp + i) * a.q_sh : nullptr;
     W.lim[0] = valid ? L - 1 : -1;
 
-    decode_stream<D, COMPACT, FMT, NS, NW>(W, ring, a.pool, bt_row, L, h, k0, st1, qrow, qk_factor, dof, ll, j);
+    decode_stream<D, COMPACT, FMT, NS, NW>(W, ring, a.pool, bt_row, a.max_blocks, L, h, k0, st1, qrow, qk_factor, dof,
+                                           ll, j);
     __syncthreads();  // every wave's ring is drained before the rings become the merge buffer
     merge_waves<D, NW>(W, s_ml, s_o, grp, w, i, j, [&](int col, int d, float on, float M, float lt) {
       if (nsplit == 1) {
@@ -535,7 +536,7 @@ __global__ __launch_bounds__((64 * PairGeo<D, mode_fmt(MODE)>::NW)) void decode_
   const bool valid = i < grp;
   const uint16_t* qrow = valid ? a.q + (int64_t)b * a.q_st + (int64_t)(h * grp + i) * a.q_sh : nullptr;
   W.lim[0] = valid ? L - 1 : -1;
-  decode_stream<D, COMPACT, FMT, NS, NW>(W, ring, a.pool, a.bt + (int64_t)b * a.max_blocks, L, h, w, ceil_div(L, kStep),
+  decode_stream<D, COMPACT, FMT, NS, NW>(W, ring, a.pool, a.bt + (int64_t)b * a.max_blocks, a.max_blocks, L, h, w, ceil_div(L, kStep),
                                     qrow, qk_factor, dof, ll, j);
   __syncthreads();  // every wave's ring is drained before the rings become the merge buffer
   merge_waves<D, NW>(W, s_ml, s_o, grp, w, i, j, [&](int col, int d, float on, float, float) {
@@ -875,14 +876,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PrefillOcc<
   if (copier) {
 #pragma unroll
     for (int s = 0; s < NS - 1; ++s)
-      dma_step<D, COMPACT, FMT>(ring + s * SG::STAGE, a.pool, ids_for_step(bt_row, s, steps, L, a.pool), h,
+      dma_step<D, COMPACT, FMT>(ring + s * SG::STAGE, a.pool, ids_for_step(bt_row, s, steps, L, a.max_blocks, a.pool), h,
                                 s * kStep, dof);
   }
-  StepIds nxt = ids_for_step(bt_row, NS - 1, steps, L, a.pool);
+  StepIds nxt = ids_for_step(bt_row, NS - 1, steps, L, a.max_blocks, a.pool);
   for (int k = 0; k < steps; ++k) {
     if (copier)
       dma_step<D, COMPACT, FMT>(ring + ((k + NS - 1) % NS) * SG::STAGE, a.pool, nxt, h, (k + NS - 1) * kStep, dof);
-    nxt = ids_for_step(bt_row, k + NS, steps, L, a.pool);
+    nxt = ids_for_step(bt_row, k + NS, steps, L, a.max_blocks, a.pool);
     wait_vmcnt<(NS - 1) * SG::NC>();  // the copier: step k has landed (others: no-op)
     lds_barrier();          // every wave may read step k
     SubRaw<D, FMT> R[2];

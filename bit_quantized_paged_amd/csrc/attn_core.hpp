@@ -1,4 +1,4 @@
-// Wave-level paged attention engine over the NVFP4 cache (gfx950).
+// Wave-level paged attention engine over the NVFP4 (and FP8) cache (gfx950).
 //
 // Attention reads the packed pages and their block-scale bytes directly
 // [P40177 "Implementation breakdown" 1 and 3: prefill/decode wrappers run on
@@ -24,6 +24,12 @@
 //    shift per key pair) puts the two keys of a pair into one byte, which the
 //    FP4 convert turns into the f16 pair the MFMA wants. PV product t covers
 //    d = i*D/16 + t.
+//  * FP8 caches [P40177 "Key source snippets": fp8_e4m3 / fp8_e5m2 beside
+//    nvfp4] take the same lanes and elements with one byte per element:
+//    K chunks and V tiles convert to f16 exactly (E4M3 by the hardware pair
+//    convert, E5M2 by a byte permute, being the upper byte of a binary16),
+//    with no block scale. The format is a template parameter (FMT) of the
+//    raw-step types, the stage geometry and WaveAttn.
 //  * Online softmax in base 2 with a lazy maximum: the running max of a
 //    column only moves (and the accumulators are only rescaled) when a score
 //    exceeds it by more than 8, so probabilities stay <= 256 in f16.
@@ -456,13 +462,19 @@ __device__ __forceinline__ int32_t ld_uniform(const int32_t* p, int idx) {
   return ((const const_i32*)(uintptr_t)p)[idx];
 }
 
-__device__ __forceinline__ StepIds step_ids(const int32_t* bt_row, int kb, int lim, const Pool& pool) {
+// The table index does not depend on lim (it is clamped to the row's last
+// entry instead), so the loads of the first steps can be in flight while the
+// sequence length is still on its way; an id read for a subtile that is not
+// ok is never used (its copy has size 0).
+__device__ __forceinline__ StepIds step_ids(const int32_t* bt_row, int kb, int lim, int max_blocks,
+                                            const Pool& pool) {
   StepIds s;
   s.ok[0] = kb < lim;
   s.ok[1] = kb + 16 < lim;
   const int page = kb >> pool.bs_log2;
-  s.id[0] = ld_uniform(bt_row, s.ok[0] ? page : 0);
-  s.id[1] = (pool.bs == 16) ? ld_uniform(bt_row, s.ok[1] ? page + 1 : 0) : s.id[0];
+  const int last = max_blocks - 1;
+  s.id[0] = ld_uniform(bt_row, page < last ? page : last);
+  s.id[1] = (pool.bs == 16) ? ld_uniform(bt_row, page + 1 < last ? page + 1 : last) : s.id[0];
   return s;
 }
 
@@ -587,19 +599,22 @@ __device__ __forceinline__ void wait_vmcnt() {
 // queries, overlap them) and returns the ids of the next step to copy; the
 // caller's loop then copies step k + (NS - 1) * ks, waits for stage k and
 // computes it, and drains with wait_vmcnt<0>() at the end.
-__device__ __forceinline__ StepIds ids_for_step(const int32_t* bt_row, int k, int kend, int L, const Pool& pool) {
-  return step_ids(bt_row, k * 32, k < kend ? L : 0, pool);
+__device__ __forceinline__ StepIds ids_for_step(const int32_t* bt_row, int k, int kend, int L, int max_blocks,
+                                                const Pool& pool) {
+  return step_ids(bt_row, k * 32, k < kend ? L : 0, max_blocks, pool);
 }
 
 template <int D, bool COMPACT, int NS, int FMT = kNvfp4>
 __device__ __forceinline__ StepIds lds_prologue(uint8_t* ring, int k0, int ks, int kend, const int32_t* bt_row, int L,
-                                                const Pool& pool, int h, const DmaOffsets<D, COMPACT, FMT>& dof) {
+                                                int max_blocks, const Pool& pool, int h,
+                                                const DmaOffsets<D, COMPACT, FMT>& dof) {
   using SG = StageGeo<D, COMPACT, FMT>;
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
-    dma_step<D, COMPACT, FMT>(ring + s * SG::STAGE, pool, ids_for_step(bt_row, k0 + s * ks, kend, L, pool), h,
-                              (k0 + s * ks) * 32, dof);
-  return ids_for_step(bt_row, k0 + (NS - 1) * ks, kend, L, pool);
+    dma_step<D, COMPACT, FMT>(ring + s * SG::STAGE, pool,
+                              ids_for_step(bt_row, k0 + s * ks, kend, L, max_blocks, pool), h, (k0 + s * ks) * 32,
+                              dof);
+  return ids_for_step(bt_row, k0 + (NS - 1) * ks, kend, L, max_blocks, pool);
 }
 
 // ---- step reader for stages filled by direct-to-LDS loads ----------------

@@ -3,6 +3,7 @@
 // Format [P39129 NvFp4LinearLayerConfig docstring; P40177 get_kv_cache_shape,
 // get_dtype_for_flashinfer]: a (token, kv head) row is D/2 bytes of E2M1 codes
 // (element 2k in the low nibble of byte k) followed by D/16 E4M3FN scales.
+// FP8 caches (kFp8E4M3, kFp8E5M2) hold one code per element instead.
 #pragma once
 
 #include <hip/hip_runtime.h>
