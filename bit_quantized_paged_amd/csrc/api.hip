@@ -114,7 +114,7 @@ nvfp4kv_status nvfp4_kv_append(const nvfp4kv_cache* cache, const void* key, int6
   if ((s = check_bf16_rows(value, value_stride_token, value_stride_head, "value"))) return s;
   if (slot_mapping == nullptr) return fail(NVFP4KV_INVALID_ARGUMENT, "slot_mapping is NULL");
   if (k_scale == nullptr || v_scale == nullptr) return fail(NVFP4KV_INVALID_ARGUMENT, "k_scale/v_scale is NULL");
-  const int64_t lanes = num_tokens * 2 * p.hkv * (cache->head_size / 16);
+  const int64_t lanes = nvfp4kv::append_lanes(num_tokens, p.hkv, cache->head_size);
   if (lanes / 256 >= (int64_t)INT32_MAX) return fail(NVFP4KV_UNSUPPORTED, "too many tokens for one call");
   return hip_status(nvfp4kv::launch_append(p, cache->head_size, key, key_stride_token, key_stride_head, value,
                                            value_stride_token, value_stride_head, slot_mapping, num_tokens,

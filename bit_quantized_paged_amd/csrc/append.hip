@@ -3,7 +3,11 @@
 //
 // One lane owns one 16-element block of one (token, kv head, K|V) row, so the
 // block amax needs no cross-lane traffic: it reads 32 bytes of bf16 and
-// writes 8 bytes of codes plus its scale byte. FP8 caches [P40177 "Key
+// writes 8 bytes of codes plus its scale byte. Rows are dealt out in tiles
+// of 16 tokens with the token fastest: consecutive lanes write consecutive
+// rows of one kv head, which a sequence's tokens keep adjacent in a page, so
+// a wave's stores fill whole cache lines (with the head fastest they spread
+// over the head slabs and each line was completed by other workgroups). FP8 caches [P40177 "Key
 // source snippets": fp8_e4m3 / fp8_e5m2] take the same lanes and write 16
 // code bytes of x / g.
 #include "quantize.hpp"
@@ -20,15 +24,19 @@ __global__ __launch_bounds__(256) void append_kernel(Pool pool, const uint16_t* 
                                                      const float* __restrict__ v_scale) {
   constexpr int LPR = D / 16;  // lanes per row
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  constexpr int TT = kAppendTile;
   const int64_t row = gid / LPR;
   const int blk16 = (int)(gid % LPR);
   const int hkv = pool.hkv;
-  // row = (t * 2 + kv) * hkv + h
-  const int64_t rows_total = num_tokens * 2 * hkv;
-  if (row >= rows_total) return;
-  const int h = (int)(row % hkv);
-  const int kv = (int)((row / hkv) & 1);
-  const int64_t t = row / (2 * (int64_t)hkv);
+  // row = ((tile * 2 + kv) * hkv + h) * TT + ti, token t = tile * TT + ti
+  const int64_t tiles = (num_tokens + TT - 1) / TT;
+  if (row >= tiles * TT * 2 * hkv) return;
+  const int ti = (int)(row % TT);
+  const int64_t rest = row / TT;
+  const int h = (int)(rest % hkv);
+  const int kv = (int)((rest / hkv) & 1);
+  const int64_t t = (rest / (2 * (int64_t)hkv)) * TT + ti;
+  if (t >= num_tokens) return;
 
   const int64_t slot = slots[t];
   const int64_t cap = pool.num_blocks * pool.bs;
@@ -61,7 +69,7 @@ static hipError_t launch_append_f(const Pool& pool, int head_size, const void* k
                                   int64_t num_tokens, const float* k_scale, const float* v_scale,
                                   hipStream_t stream) {
   if (num_tokens == 0) return hipSuccess;
-  const int64_t lanes = num_tokens * 2 * pool.hkv * (head_size / 16);
+  const int64_t lanes = append_lanes(num_tokens, pool.hkv, head_size);
   const int64_t blocks = (lanes + 255) / 256;
   const dim3 grid((unsigned)blocks);
   const uint16_t* k = static_cast<const uint16_t*>(key);

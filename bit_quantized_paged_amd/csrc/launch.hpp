@@ -11,6 +11,13 @@
 namespace nvfp4kv {
 
 // `fmt` below is the cache format: kNvfp4, kFp8E4M3 or kFp8E5M2.
+
+// Lanes of an append launch: tiles of kAppendTile tokens, K and V of every
+// kv head, one lane per 16 elements.
+constexpr int kAppendTile = 16;
+inline int64_t append_lanes(int64_t num_tokens, int hkv, int head_size) {
+  return (num_tokens + kAppendTile - 1) / kAppendTile * kAppendTile * 2 * hkv * (head_size / 16);
+}
 hipError_t launch_append(const Pool& pool, int head_size, const void* key, int64_t k_st, int64_t k_sh,
                          const void* value, int64_t v_st, int64_t v_sh, const int64_t* slots,
                          int64_t num_tokens, const float* k_scale, const float* v_scale, int fmt,
