@@ -505,7 +505,15 @@ typedef __attribute__((address_space(3))) void lds_void;
 //  general (any row stride): loads of 4 bytes per lane, 256 B each.
 // Lanes past the subtile's bytes read out of range, which writes zeros.
 //  FP8 rows (D bytes, a multiple of 16; row strides multiples of 16): 16-byte
-//    loads only, whatever the row stride.
+//    loads only, whatever the row stride. In the K slab, 16-byte chunk c of
+//    row r sits at chunk c ^ fp8_k_swizzle(r) of its LDS row, so that the 16
+//    lanes reading one chunk column of 16 rows (D-byte rows: same banks) hit
+//    eight different 16-byte bank groups.
+template <int D>
+__host__ __device__ constexpr int fp8_k_swizzle(int row) {
+  return (D == 64) ? ((row >> 1) & 3) : (row & 7);
+}
+
 template <int D, bool COMPACT, int FMT = kNvfp4>
 struct StageGeo {
   static constexpr int FD = RowBytes<D, FMT>::value;
@@ -540,7 +548,11 @@ __device__ __forceinline__ DmaOffsets<D, COMPACT, FMT> dma_offsets(int64_t st, i
   for (int t = 0; t < SG::NCS; ++t) {
     const int x = SG::off(t) + SG::size(t) * lane;  // byte of the subtile's [K slab | V slab]
     const bool isv = x >= SG::SLAB;
-    const int y = isv ? x - SG::SLAB : x;           // byte within its slab
+    int y = isv ? x - SG::SLAB : x;                 // byte within its slab
+    if constexpr (FMT != kNvfp4) {
+      // the K chunk this LDS chunk holds (the swizzle is its own inverse)
+      if (!isv) y = (y / D) * D + 16 * (((y % D) / 16) ^ fp8_k_swizzle<D>(y / D));
+    }
     uint32_t off;
     if constexpr (COMPACT) {
       off = (uint32_t)y;                             // rows are contiguous
@@ -632,6 +644,7 @@ __device__ __forceinline__ StepIds lds_prologue(uint8_t* ring, int k0, int ks, i
 // 128, 8 for 256, one scale block) and that block's scale byte.
 struct LdsLane {
   uint32_t k, ks, v, vs;
+  uint32_t k2, k3;  // FP8 at D = 256: the third and fourth K chunks
 };
 
 template <int D, int FMT = kNvfp4>
@@ -643,9 +656,19 @@ __device__ __forceinline__ LdsLane lds_lane(int i, int j) {
     o.ks = (uint32_t)(i * FD + D / 2 + (D / 64) * j);
     o.v = (uint32_t)(16 * FD + 4 * j * FD + (D / 32) * i);
     o.vs = (uint32_t)(16 * FD + 4 * j * FD + D / 2 + ((i * D) >> 8));
+    o.k2 = 0;
+    o.k3 = 0;
   } else {
-    o.k = (uint32_t)(i * D + (D / 4) * j);
-    o.ks = 0;
+    // K chunks (D/64) * j + c of row i, through the swizzle; for D = 64 one
+    // chunk, 128 two (k, ks), 256 four (k, ks, k2, k3)
+    constexpr int NKC = D / 64;
+    uint32_t a[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int c = 0; c < NKC; ++c) a[c] = (uint32_t)(i * D + 16 * ((NKC * j + c) ^ fp8_k_swizzle<D>(i)));
+    o.k = a[0];
+    o.ks = a[1];
+    o.k2 = a[2];
+    o.k3 = a[3];
     o.v = (uint32_t)(16 * D + 4 * j * D + (D / 16) * i);
     o.vs = 0;
   }
@@ -803,10 +826,11 @@ __device__ __forceinline__ void lds_read_step_async_safe<256>(SubRaw<256> (&R)[2
   }
 }
 
-// FP8 stage readers: lane (i, j) reads D/4 bytes of K row i at i*D + D/4*j
-// and D/16 bytes of V rows 4j..4j+3 at 16*D + 4j*D + D/16*i (lds_lane), in
-// both subtiles (the second 32*D bytes further). All offsets are 16-byte
-// aligned for the 16-byte reads (the ring is).
+// FP8 stage readers: lane (i, j) reads D/4 bytes of K row i (its D/64
+// 16-byte chunks, each at its swizzled place, addresses from lds_lane) and
+// D/16 bytes of V rows 4j..4j+3 at 16*D + 4j*D + D/16*i, in both subtiles
+// (the second 32*D bytes further). All offsets are 16-byte aligned for the
+// 16-byte reads (the ring is).
 template <int D, int FMT>
 __device__ __forceinline__ void lds_read_step_fp8(SubRaw<D, FMT> (&R)[2], const uint8_t* stage, const LdsLane& o) {
   const uint32_t s = lds_addr(stage);
@@ -837,17 +861,18 @@ __device__ __forceinline__ void lds_read_step_fp8(SubRaw<D, FMT> (&R)[2], const 
     }
   } else if constexpr (D == 128) {
     static_assert(StageGeo<128, false, FMT>::SUB == 4096, "D = 128 FP8 reader offsets");
+    const uint32_t ak1 = s + o.ks;
     u32x4 k0a, k0b, k1a, k1b;
     u32x2 v0[4], v1[4];
     asm volatile(
         "ds_read_b128 %0, %12\n\t"
-        "ds_read_b128 %1, %12 offset:16\n\t"
+        "ds_read_b128 %1, %14\n\t"
         "ds_read_b64 %2, %13\n\t"
         "ds_read_b64 %3, %13 offset:128\n\t"
         "ds_read_b64 %4, %13 offset:256\n\t"
         "ds_read_b64 %5, %13 offset:384\n\t"
         "ds_read_b128 %6, %12 offset:4096\n\t"
-        "ds_read_b128 %7, %12 offset:4112\n\t"
+        "ds_read_b128 %7, %14 offset:4096\n\t"
         "ds_read_b64 %8, %13 offset:4096\n\t"
         "ds_read_b64 %9, %13 offset:4224\n\t"
         "ds_read_b64 %10, %13 offset:4352\n\t"
@@ -855,7 +880,7 @@ __device__ __forceinline__ void lds_read_step_fp8(SubRaw<D, FMT> (&R)[2], const 
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(k0a), "=&v"(k0b), "=&v"(v0[0]), "=&v"(v0[1]), "=&v"(v0[2]), "=&v"(v0[3]), "=&v"(k1a),
           "=&v"(k1b), "=&v"(v1[0]), "=&v"(v1[1]), "=&v"(v1[2]), "=&v"(v1[3])
-        : "v"(ak), "v"(av)
+        : "v"(ak), "v"(av), "v"(ak1)
         : "memory");
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -873,20 +898,21 @@ __device__ __forceinline__ void lds_read_step_fp8(SubRaw<D, FMT> (&R)[2], const 
     }
   } else {
     static_assert(D == 256 && StageGeo<256, false, FMT>::SUB == 8192, "D = 256 FP8 reader offsets");
+    const uint32_t ak1 = s + o.ks, ak2 = s + o.k2, ak3 = s + o.k3;
     u32x4 k0[4], k1[4], v0[4], v1[4];
     asm volatile(
         "ds_read_b128 %0, %16\n\t"
-        "ds_read_b128 %1, %16 offset:16\n\t"
-        "ds_read_b128 %2, %16 offset:32\n\t"
-        "ds_read_b128 %3, %16 offset:48\n\t"
+        "ds_read_b128 %1, %18\n\t"
+        "ds_read_b128 %2, %19\n\t"
+        "ds_read_b128 %3, %20\n\t"
         "ds_read_b128 %4, %17\n\t"
         "ds_read_b128 %5, %17 offset:256\n\t"
         "ds_read_b128 %6, %17 offset:512\n\t"
         "ds_read_b128 %7, %17 offset:768\n\t"
         "ds_read_b128 %8, %16 offset:8192\n\t"
-        "ds_read_b128 %9, %16 offset:8208\n\t"
-        "ds_read_b128 %10, %16 offset:8224\n\t"
-        "ds_read_b128 %11, %16 offset:8240\n\t"
+        "ds_read_b128 %9, %18 offset:8192\n\t"
+        "ds_read_b128 %10, %19 offset:8192\n\t"
+        "ds_read_b128 %11, %20 offset:8192\n\t"
         "ds_read_b128 %12, %17 offset:8192\n\t"
         "ds_read_b128 %13, %17 offset:8448\n\t"
         "ds_read_b128 %14, %17 offset:8704\n\t"
@@ -895,7 +921,7 @@ __device__ __forceinline__ void lds_read_step_fp8(SubRaw<D, FMT> (&R)[2], const 
         : "=&v"(k0[0]), "=&v"(k0[1]), "=&v"(k0[2]), "=&v"(k0[3]), "=&v"(v0[0]), "=&v"(v0[1]), "=&v"(v0[2]),
           "=&v"(v0[3]), "=&v"(k1[0]), "=&v"(k1[1]), "=&v"(k1[2]), "=&v"(k1[3]), "=&v"(v1[0]), "=&v"(v1[1]),
           "=&v"(v1[2]), "=&v"(v1[3])
-        : "v"(ak), "v"(av)
+        : "v"(ak), "v"(av), "v"(ak1), "v"(ak2), "v"(ak3)
         : "memory");
 #pragma unroll
     for (int q = 0; q < 4; ++q)
