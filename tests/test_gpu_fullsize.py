@@ -1,0 +1,122 @@
+"""Parity at the full sizes of the four benchmark workloads (small-model
+decode, long-context decode, chunked prefill, mixed serving batch), in the
+launch configuration the benchmark times: an HND pool filled with the cached
+prefix, then one append of the new tokens, decode over the 1-token sequences
+and chunked prefill over the rest, with the same batch splits and length
+hints. The oracle computes a sample of the outputs one by one:
+
+- packed rows: every token of the sampled sequences plus a random sample of
+  all tokens, bit-exact against the oracle's own quantisation;
+- decode: every head of the sampled sequences (the longest, the shortest and
+  random ones);
+- prefill: single query rows of the sampled sequences (first, last and random
+  positions), each as a one-query sequence over its causal prefix (the key
+  limit L - q_len + i of bottom-right alignment).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import bit_quantized_paged_amd as nvk
+from oracle import nvfp4_oracle as O
+from workloads import make_config
+from gpu_util import assert_attn_close, bf16_dev, i32_dev, i64_dev, scale_dev
+
+pytestmark = pytest.mark.gpu
+
+FULL = {"small_decode": 2, "long_decode": 3, "chunked_prefill": 4, "mixed_serving": 5}
+
+
+def run_like_bench(w, dev):
+    """The benchmark's step on one pool: fill, append, decode, prefill."""
+    Hq, Hkv, D, bs = w.num_q_heads, w.num_kv_heads, w.head_size, w.block_size
+    fd = D // 2 + D // 16
+    sm = 1.0 / math.sqrt(D)
+    ks, vs = scale_dev(w.k_scale, dev), scale_dev(w.v_scale, dev)
+    base = torch.zeros((w.num_blocks, 2, Hkv, bs, fd), dtype=torch.uint8, device=dev)
+    pool = base.permute(0, 1, 3, 2, 4)  # logical (num_blocks, 2, bs, Hkv, fd), HND in memory
+    cached = w.cached_mask()
+    for sel in (cached, ~cached):
+        if sel.any():
+            nvk.append(pool, bf16_dev(w.key[sel], dev), bf16_dev(w.value[sel], dev), i64_dev(w.slot_mapping[sel], dev),
+                       ks, vs)
+    dec_idx = np.nonzero(w.q_lens == 1)[0]
+    pre_idx = np.nonzero(w.q_lens != 1)[0]
+    outd = outp = None
+    if len(dec_idx):
+        wd = w.subset(dec_idx)
+        outd = torch.empty((wd.num_seqs, Hq, D), dtype=torch.bfloat16, device=dev)
+        wsd = torch.zeros(nvk.decode_workspace_size(wd.num_seqs, Hq, Hkv, D), dtype=torch.uint8, device=dev)
+        nvk.paged_attention_decode(pool, bf16_dev(wd.query, dev), i32_dev(wd.block_table, dev),
+                                   i32_dev(wd.seq_lens, dev), int(wd.seq_lens.max()), ks, vs, sm, outd, wsd)
+    wp = None
+    if len(pre_idx):
+        wp = w.subset(pre_idx)
+        outp = torch.empty((int(wp.cu_q[-1]), Hq, D), dtype=torch.bfloat16, device=dev)
+        nvk.paged_attention_prefill(pool, bf16_dev(wp.query, dev), i32_dev(wp.cu_q, dev), int(wp.q_lens.max()),
+                                    i32_dev(wp.block_table, dev), i32_dev(wp.seq_lens, dev), int(wp.seq_lens.max()),
+                                    ks, vs, sm, outp)
+    torch.cuda.synchronize()
+    return pool, dec_idx, outd, pre_idx, wp, outp
+
+
+def sample_seqs(idx, lens, rng, n_random):
+    """The longest, the shortest and n_random other sequences of idx."""
+    if len(idx) == 0:
+        return []
+    pick = {int(idx[np.argmax(lens[idx])]), int(idx[np.argmin(lens[idx])])}
+    rest = [int(b) for b in idx if int(b) not in pick]
+    if rest:
+        pick.update(int(b) for b in rng.choice(rest, size=min(n_random, len(rest)), replace=False))
+    return sorted(pick)
+
+
+@pytest.mark.parametrize("name", sorted(FULL))
+def test_full_size_sampled_parity(name):
+    cfg = FULL[name]
+    w = make_config(cfg)
+    dev = torch.device("cuda")
+    print(f"full-size parity: {name} ({w.num_seqs} seqs, {int(w.seq_lens.sum())} tokens)", flush=True)
+    pool, dec_idx, outd, pre_idx, wp, outp = run_like_bench(w, dev)
+    rng = np.random.default_rng(100 + cfg)
+    sd = sample_seqs(dec_idx, w.seq_lens, rng, 2)
+    sp = sample_seqs(pre_idx, w.seq_lens, rng, 1)
+    assert sd or sp
+
+    # ---- packed rows of the sampled sequences' tokens and of a random token sample
+    off = w.token_offsets
+    toks = [np.arange(off[b], off[b + 1]) for b in sd + sp]
+    toks.append(rng.choice(int(off[-1]), size=4096, replace=False))
+    toks = np.unique(np.concatenate(toks))
+    ref_pool = np.zeros(O.pool_shape(w.num_blocks, w.block_size, w.num_kv_heads, w.head_size), np.uint8)
+    O.append(ref_pool, w.key[toks], w.value[toks], w.slot_mapping[toks], w.k_scale, w.v_scale)
+    slots = w.slot_mapping[toks]
+    blk, row = slots // w.block_size, slots % w.block_size
+    got_rows = pool[torch.from_numpy(blk).to(dev), :, torch.from_numpy(row).to(dev)].cpu().numpy()
+    ref_rows = ref_pool[blk, :, row]
+    bad = np.nonzero(np.any(got_rows != ref_rows, axis=(1, 2, 3)))[0]
+    assert bad.size == 0, f"{name}: {bad.size} of {toks.size} sampled tokens differ (first token {toks[bad[0]]})"
+
+    sm = np.float32(1.0 / math.sqrt(w.head_size))
+    # ---- decode: every head of each sampled sequence
+    for b in sd:
+        k = int(np.nonzero(dec_idx == b)[0][0])
+        q0 = int(w.cu_q[b])
+        ref = O.paged_attention(ref_pool, w.query[q0:q0 + 1], np.array([0, 1], np.int32), w.block_table[b:b + 1],
+                                w.seq_lens[b:b + 1], w.k_scale, w.v_scale, sm, w.head_size)
+        assert_attn_close(outd[k:k + 1], ref, f"{name} decode seq {b} (len {int(w.seq_lens[b])})")
+
+    # ---- prefill: single query rows over their causal prefix
+    for b in sp:
+        k = int(np.nonzero(pre_idx == b)[0][0])
+        L, nq = int(w.seq_lens[b]), int(w.q_lens[b])
+        rows = {0, nq - 1} | {int(i) for i in rng.integers(0, nq, size=2)}
+        for i in sorted(rows):
+            p = L - nq + i  # absolute position of query row i: it sees keys 0..p
+            qi = int(w.cu_q[b]) + i
+            ref = O.paged_attention(ref_pool, w.query[qi:qi + 1], np.array([0, 1], np.int32), w.block_table[b:b + 1],
+                                    np.array([p + 1], np.int32), w.k_scale, w.v_scale, sm, w.head_size)
+            r = int(wp.cu_q[k]) + i
+            assert_attn_close(outp[r:r + 1], ref, f"{name} prefill seq {b} row {i} of {nq} (keys 0..{p})")
