@@ -88,11 +88,33 @@ __device__ void decode_schedule(const int32_t* __restrict__ seq_lens, int B, int
   const int64_t work = (int64_t)total_steps * hkv;
   int t = (int)((work + target - 1) / target);
   tps = t < kDecodeMinTps ? kDecodeMinTps : t;
-  int units_local = 0;
-  // a sequence without keys still gets one (empty) unit, which writes zeros
-  for (int b = b0; b < b1; ++b) units_local += max(1, ceil_div(s_pref[b], tps));
-  int total;
-  int run = block_excl_scan<NW>(units_local, s_red, total);
+  // units (per kv head) at t steps per unit; a sequence without keys still
+  // gets one (empty) unit, which writes zeros
+  auto units_at = [&](int tt, int& run_out) {
+    int loc = 0;
+    for (int b = b0; b < b1; ++b) loc += max(1, ceil_div(s_pref[b], tt));
+    int tot;
+    run_out = block_excl_scan<NW>(loc, s_red, tot);
+    return tot;
+  };
+  int run;
+  int total = units_at(tps, run);
+  // Short sequences round their unit counts up, so the even share can yield
+  // more units than workgroups, and a second round then doubles some
+  // workgroups' work. Take instead the smallest unit size whose units fit one
+  // round (binary search; at total_steps every sequence is one unit, which
+  // fits whenever the batch alone does).
+  if ((int64_t)total * hkv > target && (int64_t)B * hkv <= target && total_steps > tps) {
+    int lo = tps, hi = total_steps;  // lo does not fit, hi fits
+    while (hi - lo > 1) {
+      const int mid = lo + (hi - lo) / 2;
+      int r;
+      if ((int64_t)units_at(mid, r) * hkv <= target) hi = mid;
+      else lo = mid;
+    }
+    tps = hi;
+    total = units_at(tps, run);
+  }
   for (int b = b0; b < b1; ++b) {
     const int n = max(1, ceil_div(s_pref[b], tps));
     s_pref[b] = run;
