@@ -11,7 +11,10 @@ hints. The oracle computes a sample of the outputs one by one:
   random ones);
 - prefill: single query rows of the sampled sequences (first, last and random
   positions), each as a one-query sequence over its causal prefix (the key
-  limit L - q_len + i of bottom-right alignment).
+  limit L - q_len + i of bottom-right alignment);
+- the paged dequantize of the decode batch and the page-form dequantize of
+  its pages, as the benchmark runs them: the sampled sequences' rows and
+  pages, bit-exact.
 """
 import math
 
@@ -62,6 +65,26 @@ def run_like_bench(w, dev):
     return pool, dec_idx, outd, pre_idx, wp, outp
 
 
+def dequant_like_bench(w, pool, dec_idx, dev):
+    """The benchmark's two dequantize calls over the decode batch: gathered
+    rows per sequence, and every page the batch uses."""
+    wd = w.subset(dec_idx)
+    Hkv, D, bs = w.num_kv_heads, w.head_size, w.block_size
+    ks, vs = scale_dev(w.k_scale, dev), scale_dev(w.v_scale, dev)
+    cu = np.zeros(wd.num_seqs, np.int32)
+    cu[1:] = np.cumsum(wd.seq_lens)[:-1]
+    ok = torch.empty((int(wd.seq_lens.sum()), Hkv, D), dtype=torch.bfloat16, device=dev)
+    ov = torch.empty_like(ok)
+    nvk.dequant_paged(pool, i32_dev(wd.block_table, dev), i32_dev(wd.seq_lens, dev), i32_dev(cu, dev),
+                      int(wd.seq_lens.max()), ks, vs, ok, ov)
+    used = np.unique(np.concatenate([wd.block_table[b, :(int(wd.seq_lens[b]) + bs - 1) // bs]
+                                     for b in range(wd.num_seqs)])).astype(np.int32)
+    pages = torch.empty((w.num_blocks, 2, bs, Hkv, D), dtype=torch.bfloat16, device=dev)
+    nvk.dequant_pages(pool, i32_dev(used, dev), ks, vs, pages)
+    torch.cuda.synchronize()
+    return cu, ok, ov, pages
+
+
 def sample_seqs(idx, lens, rng, n_random):
     """The longest, the shortest and n_random other sequences of idx."""
     if len(idx) == 0:
@@ -107,6 +130,24 @@ def test_full_size_sampled_parity(name):
         ref = O.paged_attention(ref_pool, w.query[q0:q0 + 1], np.array([0, 1], np.int32), w.block_table[b:b + 1],
                                 w.seq_lens[b:b + 1], w.k_scale, w.v_scale, sm, w.head_size)
         assert_attn_close(outd[k:k + 1], ref, f"{name} decode seq {b} (len {int(w.seq_lens[b])})")
+
+    # ---- paged and page-form dequantize of the decode batch
+    if sd:
+        cu, ok, ov, pages = dequant_like_bench(w, pool, dec_idx, dev)
+        bs = w.block_size
+        for b in sd:
+            k = int(np.nonzero(dec_idx == b)[0][0])
+            L = int(w.seq_lens[b])
+            kd, vd = O.dequant_paged(ref_pool, w.block_table[b:b + 1], w.seq_lens[b:b + 1], w.k_scale, w.v_scale,
+                                     w.head_size)
+            for got, want, nm in ((ok, kd, "K"), (ov, vd, "V")):
+                g = got[int(cu[k]):int(cu[k]) + L].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+                assert np.array_equal(g, want), f"{name} dequant {nm} of seq {b} differs"
+            ids = w.block_table[b, :(L + bs - 1) // bs].astype(np.int64)
+            want_pages = O.dequant_pages(ref_pool, ids, w.k_scale, w.v_scale, w.head_size)
+            g = pages[torch.from_numpy(ids).to(dev)].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+            assert np.array_equal(g, want_pages), f"{name} page-form dequant of seq {b}'s pages differs"
+        del ok, ov, pages
 
     # ---- prefill: single query rows over their causal prefix
     for b in sp:
