@@ -282,6 +282,14 @@ struct DecodeStages {
   static constexpr int NS = (D == 64) ? 3 : 2;
 };
 
+// Stages of the split kernel's rings. An FP8 step at D = 256 is 16 KB, so two
+// stages per wave would leave room for one workgroup per CU; with one stage,
+// refilled as soon as the step is in registers, two fit.
+template <int D, int MODE>
+struct SplitStages {
+  static constexpr int NS = (D == 256 && mode_fmt(MODE) != kNvfp4) ? 1 : DecodeStages<D>::NS;
+};
+
 // Waves per split-kernel workgroup.
 template <int D>
 struct SplitWaves {
@@ -292,7 +300,7 @@ template <int D, int MODE>
 struct DecodeLds {
   static constexpr int NW = SplitWaves<D>::NW;
   static constexpr int dma_stage = StageGeo<D, MODE == kModeDmaCompact, mode_fmt(MODE)>::STAGE;
-  static constexpr int stream = NW * DecodeStages<D>::NS * dma_stage;
+  static constexpr int stream = NW * SplitStages<D, MODE>::NS * dma_stage;
   static constexpr int merge = NW * kMergeCols * D * 4;
   static constexpr int area = stream > merge ? stream : merge;  // streams, then merge and combine scratch
 };
@@ -318,6 +326,28 @@ __device__ __forceinline__ void decode_stream(WaveAttn<D, 1, FMT>& W, uint8_t* r
   using SG = StageGeo<D, COMPACT, FMT>;
   const auto qraw = WaveAttn<D, 1, FMT>::load_q_raw(qrow, j);
   StepIds nxt = lds_prologue<D, COMPACT, NS, FMT>(ring, k0, NWS, st1, bt_row, L, max_blocks, pool, h, dof);
+  if constexpr (NS == 1) {
+    // One stage: step k0's copy goes out before the query conversion, and
+    // each later step's copy as soon as the previous step's bytes are in
+    // registers (the reader waits for its LDS reads), so the copy streams in
+    // while that step computes.
+    dma_step<D, COMPACT, FMT>(ring, pool, nxt, h, k0 * kStep, dof);
+    nxt = ids_for_step(bt_row, k0 + NWS, st1, L, max_blocks, pool);
+    W.set_q(0, qraw, qk_factor);
+    for (int k = k0; k < st1; k += NWS) {
+      wait_vmcnt<0>();
+      SubRaw<D, FMT> R[2];
+      lds_read_step<D, FMT>(R, ring, ll);
+      dma_step<D, COMPACT, FMT>(ring, pool, nxt, h, (k + NWS) * kStep, dof);
+      nxt = ids_for_step(bt_row, k + 2 * NWS, st1, L, max_blocks, pool);
+      const int kb = k * kStep;
+      const bool partial = kb + kStep > L;
+      if (partial) mask_step(R, kb, L, j);
+      W.step(R, kb, j, partial);
+    }
+    wait_vmcnt<0>();
+    return;
+  }
   W.set_q(0, qraw, qk_factor);
   int slot = 0;
   for (int k = k0; k < st1; k += NWS) {
@@ -388,7 +418,7 @@ decode_split_kernel(DecodeArgs a) {
   constexpr int FMT = mode_fmt(MODE);
   constexpr bool COMPACT = MODE == kModeDmaCompact;
   using SG = StageGeo<D, COMPACT, FMT>;
-  constexpr int NS = DecodeStages<D>::NS;
+  constexpr int NS = SplitStages<D, MODE>::NS;
   extern __shared__ __align__(16) char smem[];
   int* s_pref = reinterpret_cast<int*>(smem);
   int* s_len = s_pref + ((a.B + 1 + 3) / 4) * 4;
