@@ -96,6 +96,7 @@ def test_decode_validation():
     assert call(q=None) == 1
     assert call(out=8194) == 1
     assert call(B=5000) == 2
+    assert call(B=4097) == 2        # one past the largest batch a decode call takes
     assert call(B=0) == 0
 
 

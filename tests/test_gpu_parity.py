@@ -588,3 +588,30 @@ def test_prefill_fp8_output(case, causal):
     ref = O.paged_attention(ref_pool, w.query, w.cu_q, w.block_table, w.seq_lens, w.k_scale, w.v_scale,
                             np.float32(d.sm_scale), w.head_size, causal=causal)
     _fp8_close(codes, ref, os, f"{name} fp8 prefill causal={causal}")
+
+
+@pytest.mark.parametrize("kernel", ["pair", "split"])
+def test_decode_at_the_largest_batch(kernel):
+    """4096 sequences, the most one decode call takes, with ragged lengths of
+    1..64 keys. With one 4000-key sequence the host picks the split kernel,
+    whose 64-way unit lookup then runs at its largest stride; without it, the
+    per-pair kernel. Sampled sequences against the oracle."""
+    B = 4096
+    rng = np.random.default_rng(41)
+    lens = rng.integers(1, 65, size=B).astype(np.int32)
+    if kernel == "split":
+        lens[1234] = 4000
+    w = make_workload(seed=41, name="x", rng=rng, seq_lens=lens, q_lens=np.ones(B, np.int32), num_q_heads=2,
+                      num_kv_heads=1, head_size=64, block_size=16)
+    plan = nvk.decode_plan(B, 1, 64, 16, w.block_table.shape[1], int(lens.max()))
+    assert plan == (nvk.DECODE_SPLIT_K if kernel == "split" else nvk.DECODE_PER_PAIR)
+    d = Dev(w)
+    d.append_all()
+    out = d.decode()
+    torch.cuda.synchronize()
+    pool = oracle_pool(w)
+    pick = sorted({0, 1234, B - 1, *(int(b) for b in rng.choice(B, size=8, replace=False))})
+    sub = w.subset(pick)
+    ref = O.paged_attention(pool, sub.query, sub.cu_q, sub.block_table, sub.seq_lens, w.k_scale, w.v_scale,
+                            np.float32(d.sm_scale), 64)
+    assert_attn_close(out[torch.tensor(pick, device=out.device)], ref, f"largest batch ({kernel})")
