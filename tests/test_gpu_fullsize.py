@@ -24,7 +24,7 @@ import torch
 
 import bit_quantized_paged_amd as nvk
 from oracle import nvfp4_oracle as O
-from workloads import make_config
+from workloads import fp8_kv_scales, make_config
 from gpu_util import assert_attn_close, bf16_dev, i32_dev, i64_dev, scale_dev
 
 pytestmark = pytest.mark.gpu
@@ -161,3 +161,43 @@ def test_full_size_sampled_parity(name):
                                     np.array([p + 1], np.int32), w.k_scale, w.v_scale, sm, w.head_size)
             r = int(wp.cu_q[k]) + i
             assert_attn_close(outp[r:r + 1], ref, f"{name} prefill seq {b} row {i} of {nq} (keys 0..{p})")
+
+
+@pytest.mark.parametrize("name,kv", [("long_decode", "fp8_e4m3"), ("mixed_serving", "fp8_e4m3"),
+                                     ("mixed_serving", "fp8_e5m2")])
+def test_full_size_fp8_decode_sampled(name, kv):
+    """FP8 caches at full size through the split decode kernel (D = 128 and
+    D = 256): the whole batch appended into an FP8 pool, the decode
+    sequences decoded in one call, sampled sequences against the oracle on
+    its own FP8 pool of their tokens."""
+    cfg = FULL[name]
+    w = make_config(cfg)
+    dev = torch.device("cuda")
+    print(f"full-size FP8 decode: {name} {kv}", flush=True)
+    ksc, vsc = fp8_kv_scales(w, kv)
+    ks, vs = scale_dev(ksc, dev), scale_dev(vsc, dev)
+    pool = nvk.alloc_pool(w.num_blocks, w.block_size, w.num_kv_heads, w.head_size, "HND", dev, kv_dtype=kv)
+    nvk.append(pool, bf16_dev(w.key, dev), bf16_dev(w.value, dev), i64_dev(w.slot_mapping, dev), ks, vs)
+    dec_idx = np.nonzero(w.q_lens == 1)[0]
+    wd = w.subset(dec_idx)
+    Hq, Hkv, D = w.num_q_heads, w.num_kv_heads, w.head_size
+    assert nvk.decode_plan(wd.num_seqs, Hkv, D, w.block_size, wd.block_table.shape[1], int(wd.seq_lens.max()),
+                           kv) == nvk.DECODE_SPLIT_K
+    out = torch.empty((wd.num_seqs, Hq, D), dtype=torch.bfloat16, device=dev)
+    ws = torch.zeros(nvk.decode_workspace_size(wd.num_seqs, Hq, Hkv, D), dtype=torch.uint8, device=dev)
+    sm = np.float32(1.0 / math.sqrt(D))
+    nvk.paged_attention_decode(pool, bf16_dev(wd.query, dev), i32_dev(wd.block_table, dev), i32_dev(wd.seq_lens, dev),
+                               int(wd.seq_lens.max()), ks, vs, float(sm), out, ws)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(200 + cfg)
+    sd = sample_seqs(dec_idx, w.seq_lens, rng, 2)
+    off = w.token_offsets
+    toks = np.concatenate([np.arange(off[b], off[b + 1]) for b in sd])
+    ref_pool = np.zeros(O.pool_shape(w.num_blocks, w.block_size, Hkv, D, kv), np.uint8)
+    O.append(ref_pool, w.key[toks], w.value[toks], w.slot_mapping[toks], ksc, vsc, kv)
+    for b in sd:
+        k = int(np.nonzero(dec_idx == b)[0][0])
+        q0 = int(w.cu_q[b])
+        ref = O.paged_attention(ref_pool, w.query[q0:q0 + 1], np.array([0, 1], np.int32), w.block_table[b:b + 1],
+                                w.seq_lens[b:b + 1], ksc, vsc, sm, D, kv_dtype=kv)
+        assert_attn_close(out[k:k + 1], ref, f"{name} {kv} decode seq {b} (len {int(w.seq_lens[b])})")
