@@ -201,3 +201,40 @@ def test_full_size_fp8_decode_sampled(name, kv):
         ref = O.paged_attention(ref_pool, w.query[q0:q0 + 1], np.array([0, 1], np.int32), w.block_table[b:b + 1],
                                 w.seq_lens[b:b + 1], ksc, vsc, sm, D, kv_dtype=kv)
         assert_attn_close(out[k:k + 1], ref, f"{name} {kv} decode seq {b} (len {int(w.seq_lens[b])})")
+
+
+def test_full_size_fp8_chunked_prefill_sampled():
+    """An E4M3 cache at the full chunked-prefill size: 8192 cached tokens per
+    sequence appended, then the 2048-token chunks, and one causal prefill
+    call; single query rows of sampled sequences against the oracle."""
+    kv = "fp8_e4m3"
+    w = make_config(FULL["chunked_prefill"])
+    dev = torch.device("cuda")
+    ksc, vsc = fp8_kv_scales(w, kv)
+    ks, vs = scale_dev(ksc, dev), scale_dev(vsc, dev)
+    pool = nvk.alloc_pool(w.num_blocks, w.block_size, w.num_kv_heads, w.head_size, "HND", dev, kv_dtype=kv)
+    cached = w.cached_mask()
+    for sel in (cached, ~cached):
+        nvk.append(pool, bf16_dev(w.key[sel], dev), bf16_dev(w.value[sel], dev), i64_dev(w.slot_mapping[sel], dev),
+                   ks, vs)
+    Hq, D = w.num_q_heads, w.head_size
+    sm = np.float32(1.0 / math.sqrt(D))
+    out = torch.empty((int(w.cu_q[-1]), Hq, D), dtype=torch.bfloat16, device=dev)
+    nvk.paged_attention_prefill(pool, bf16_dev(w.query, dev), i32_dev(w.cu_q, dev), int(w.q_lens.max()),
+                                i32_dev(w.block_table, dev), i32_dev(w.seq_lens, dev), int(w.seq_lens.max()),
+                                ks, vs, float(sm), out)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(300)
+    sp = sample_seqs(np.arange(w.num_seqs), w.seq_lens, rng, 1)
+    off = w.token_offsets
+    toks = np.concatenate([np.arange(off[b], off[b + 1]) for b in sp])
+    ref_pool = np.zeros(O.pool_shape(w.num_blocks, w.block_size, w.num_kv_heads, D, kv), np.uint8)
+    O.append(ref_pool, w.key[toks], w.value[toks], w.slot_mapping[toks], ksc, vsc, kv)
+    for b in sp:
+        L, nq = int(w.seq_lens[b]), int(w.q_lens[b])
+        for i in sorted({0, nq - 1} | {int(x) for x in rng.integers(0, nq, size=2)}):
+            p = L - nq + i
+            qi = int(w.cu_q[b]) + i
+            ref = O.paged_attention(ref_pool, w.query[qi:qi + 1], np.array([0, 1], np.int32), w.block_table[b:b + 1],
+                                    np.array([p + 1], np.int32), ksc, vsc, sm, D, kv_dtype=kv)
+            assert_attn_close(out[qi:qi + 1], ref, f"chunked_prefill {kv} seq {b} row {i} (keys 0..{p})")
