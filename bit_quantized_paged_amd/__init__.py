@@ -105,11 +105,36 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
 
-def _dev(t, name, dtype=None):
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a device tensor")
-    if dtype is not None and t.dtype != dtype:
+# Every size the kernels read or write through a pointer is checked here,
+# against the pool descriptor and the batch size, before anything reaches the
+# C ABI (which sees pointers, not shapes). Checks take the order dtype,
+# shape, layout, device, so a mis-sized tensor is reported as such wherever
+# it lives.
+def _meta(t, name, dtype):
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _shape(t, name, want):
+    """want: a tuple of ints (None matches any size)."""
+    got = tuple(t.shape)
+    if len(got) != len(want) or any(w is not None and g != w for g, w in zip(got, want)):
+        shown = tuple("*" if w is None else w for w in want)
+        raise ValueError(f"{name} must have shape {shown}, got {got}")
+
+
+def _scalar(t, name):
+    _meta(t, name, torch.float32)
+    if t.numel() < 1:
+        raise ValueError(f"{name} must hold one float32 value")
+
+
+def _devices(*named):
+    for t, name in named:
+        if t is not None and not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
 
 
 def full_dim(head_size: int) -> int:
@@ -152,7 +177,9 @@ def kv_dtype_of(pool: torch.Tensor) -> int:
 
 
 def _desc(pool: torch.Tensor) -> CacheDesc:
-    _dev(pool, "pool")
+    """The C descriptor of a pool view (checked for shape, not for device)."""
+    if not isinstance(pool, torch.Tensor):
+        raise ValueError("pool must be a torch tensor")
     kv = kv_dtype_of(pool)
     if pool.dim() != 5 or pool.shape[1] != 2 or pool.stride(4) != 1:
         raise ValueError("pool must be a (num_blocks, 2, block_size, num_kv_heads, row) view "
@@ -169,16 +196,22 @@ def _desc(pool: torch.Tensor) -> CacheDesc:
 
 
 def append(pool, key, value, slot_mapping, k_scale, v_scale) -> None:
-    """Quantise bf16 key/value [N, Hkv, D] into the pool at slot_mapping (int64 [N])."""
-    _dev(key, "key", torch.bfloat16)
-    _dev(value, "value", torch.bfloat16)
-    _dev(slot_mapping, "slot_mapping", torch.int64)
-    _dev(k_scale, "k_scale", torch.float32)
-    _dev(v_scale, "v_scale", torch.float32)
+    """Quantise bf16 key/value [N, Hkv, D] into the pool at slot_mapping (int64 [>= N])."""
+    d = _desc(pool)
+    _meta(key, "key", torch.bfloat16)
+    _meta(value, "value", torch.bfloat16)
+    _meta(slot_mapping, "slot_mapping", torch.int64)
+    _scalar(k_scale, "k_scale")
+    _scalar(v_scale, "v_scale")
+    _shape(key, "key", (None, d.num_kv_heads, d.head_size))
+    n = key.shape[0]
+    _shape(value, "value", (n, d.num_kv_heads, d.head_size))
+    if slot_mapping.dim() != 1 or slot_mapping.numel() < n:
+        raise ValueError(f"slot_mapping must be 1-D with at least {n} entries, got {tuple(slot_mapping.shape)}")
     if key.stride(-1) != 1 or value.stride(-1) != 1 or not slot_mapping.is_contiguous():
         raise ValueError("key/value need a contiguous last axis and slot_mapping must be contiguous")
-    d = _desc(pool)
-    n = key.shape[0]
+    _devices((pool, "pool"), (key, "key"), (value, "value"), (slot_mapping, "slot_mapping"),
+             (k_scale, "k_scale"), (v_scale, "v_scale"))
     _check(library().nvfp4_kv_append(ctypes.byref(d), _ptr(key), key.stride(0), key.stride(1), _ptr(value),
                                       value.stride(0), value.stride(1), _ptr(slot_mapping), n, _ptr(k_scale),
                                       _ptr(v_scale), _stream()))
@@ -187,17 +220,29 @@ def append(pool, key, value, slot_mapping, k_scale, v_scale) -> None:
 def dequant_paged(pool, block_table, seq_lens, cu_seqlens_out, max_seq_len, k_scale, v_scale,
                   out_key, out_value) -> None:
     """Gather every sequence's cache as bf16 rows [sum(seq_lens), Hkv, D]."""
+    d = _desc(pool)
     for t, nm, dt in ((block_table, "block_table", torch.int32), (seq_lens, "seq_lens", torch.int32),
                       (cu_seqlens_out, "cu_seqlens_out", torch.int32), (out_key, "out_key", torch.bfloat16),
                       (out_value, "out_value", torch.bfloat16)):
-        _dev(t, nm, dt)
+        _meta(t, nm, dt)
+    _scalar(k_scale, "k_scale")
+    _scalar(v_scale, "v_scale")
+    B = seq_lens.numel()
+    _shape(seq_lens, "seq_lens", (B,))
+    _shape(cu_seqlens_out, "cu_seqlens_out", (B,))
+    if block_table.dim() != 2 or block_table.shape[0] < B or block_table.shape[1] < 1:
+        raise ValueError(f"block_table must be [>= {B}, >= 1], got {tuple(block_table.shape)}")
+    _shape(out_key, "out_key", (None, d.num_kv_heads, d.head_size))
+    _shape(out_value, "out_value", tuple(out_key.shape))
+    for t, nm in ((block_table, "block_table"), (seq_lens, "seq_lens"), (cu_seqlens_out, "cu_seqlens_out"),
+                  (out_key, "out_key"), (out_value, "out_value")):
         if not t.is_contiguous():
             raise ValueError(f"{nm} must be contiguous")
-    d = _desc(pool)
-    if out_key.shape != out_value.shape:
-        raise ValueError("out_key and out_value must have the same shape")
+    _devices((pool, "pool"), (block_table, "block_table"), (seq_lens, "seq_lens"),
+             (cu_seqlens_out, "cu_seqlens_out"), (out_key, "out_key"), (out_value, "out_value"),
+             (k_scale, "k_scale"), (v_scale, "v_scale"))
     _check(library().nvfp4_kv_dequant_paged(ctypes.byref(d), _ptr(block_table), block_table.shape[1],
-                                             _ptr(seq_lens), _ptr(cu_seqlens_out), seq_lens.shape[0],
+                                             _ptr(seq_lens), _ptr(cu_seqlens_out), B,
                                              int(max_seq_len), _ptr(k_scale), _ptr(v_scale), _ptr(out_key),
                                              _ptr(out_value), out_key.shape[0], _stream()))
 
@@ -208,14 +253,18 @@ def dequant_pages(pool, page_ids, k_scale, v_scale, out) -> None:
     block_size, num_kv_heads, head_size) with any strides (multiples of 8
     elements, last axis contiguous). ``page_ids`` int32 (None: pages
     0 .. num_blocks - 1)."""
-    _dev(out, "out", torch.bfloat16)
-    if page_ids is not None:
-        _dev(page_ids, "page_ids", torch.int32)
-        if not page_ids.is_contiguous():
-            raise ValueError("page_ids must be contiguous")
     d = _desc(pool)
-    if tuple(out.shape) != (d.num_blocks, 2, d.block_size, d.num_kv_heads, d.head_size) or out.stride(4) != 1:
-        raise ValueError("out must have the pool's logical shape with head_size contiguous")
+    _meta(out, "out", torch.bfloat16)
+    _scalar(k_scale, "k_scale")
+    _scalar(v_scale, "v_scale")
+    if page_ids is not None:
+        _meta(page_ids, "page_ids", torch.int32)
+        if page_ids.dim() != 1 or not page_ids.is_contiguous():
+            raise ValueError("page_ids must be 1-D and contiguous")
+    _shape(out, "out", (d.num_blocks, 2, d.block_size, d.num_kv_heads, d.head_size))
+    if out.stride(4) != 1:
+        raise ValueError("out needs a contiguous last axis")
+    _devices((pool, "pool"), (out, "out"), (page_ids, "page_ids"), (k_scale, "k_scale"), (v_scale, "v_scale"))
     n = page_ids.numel() if page_ids is not None else d.num_blocks
     st = out.stride()
     _check(library().nvfp4_kv_dequant_pages(ctypes.byref(d), _ptr(page_ids), n, _ptr(k_scale), _ptr(v_scale),
@@ -224,10 +273,16 @@ def dequant_pages(pool, page_ids, k_scale, v_scale, out) -> None:
 
 def qdq(key, value, k_scale, v_scale) -> None:
     """Quantize-dequantize emulation, in place: key, value bf16 [T, Hkv, D]."""
-    _dev(key, "key", torch.bfloat16)
-    _dev(value, "value", torch.bfloat16)
-    if key.shape != value.shape or key.dim() != 3 or key.stride(2) != 1 or value.stride(2) != 1:
-        raise ValueError("key and value must be [T, Hkv, D] with D contiguous")
+    _meta(key, "key", torch.bfloat16)
+    _meta(value, "value", torch.bfloat16)
+    _scalar(k_scale, "k_scale")
+    _scalar(v_scale, "v_scale")
+    if key.dim() != 3:
+        raise ValueError(f"key must be [T, Hkv, D], got {tuple(key.shape)}")
+    _shape(value, "value", tuple(key.shape))
+    if key.stride(2) != 1 or value.stride(2) != 1:
+        raise ValueError("key and value need a contiguous last axis")
+    _devices((key, "key"), (value, "value"), (k_scale, "k_scale"), (v_scale, "v_scale"))
     T, H, D = key.shape
     _check(library().nvfp4_kv_qdq(_ptr(key), key.stride(0), key.stride(1), _ptr(value), value.stride(0),
                                    value.stride(1), T, H, D, _ptr(k_scale), _ptr(v_scale), _stream()))
@@ -250,39 +305,67 @@ def decode_plan(num_seqs: int, num_kv_heads: int, head_size: int, block_size: in
                                                             KV_DTYPES[kv_dtype][0]))
 
 
+def _check_attention_args(d, q, out, block_table, seq_lens, o_scale, k_scale, v_scale):
+    """Shared checks of decode and prefill: q [T, Hq, D] with Hq a multiple
+    of the pool's kv heads, out of q's shape (bf16, or uint8 FP8 codes with an
+    output scale), a block table row for every sequence."""
+    _meta(q, "q", torch.bfloat16)
+    _meta(out, "out", torch.bfloat16 if o_scale is None else torch.uint8)
+    _meta(block_table, "block_table", torch.int32)
+    _meta(seq_lens, "seq_lens", torch.int32)
+    _scalar(k_scale, "k_scale")
+    _scalar(v_scale, "v_scale")
+    if o_scale is not None:
+        _scalar(o_scale, "o_scale")
+    if q.dim() != 3 or q.shape[2] != d.head_size or q.shape[1] < 1 or q.shape[1] % d.num_kv_heads != 0:
+        raise ValueError(f"q must be [tokens, Hq, {d.head_size}] with Hq a multiple of {d.num_kv_heads}, "
+                         f"got {tuple(q.shape)}")
+    _shape(out, "out", tuple(q.shape))
+    B = seq_lens.numel()
+    _shape(seq_lens, "seq_lens", (B,))
+    if block_table.dim() != 2 or block_table.shape[0] < B or block_table.shape[1] < 1:
+        raise ValueError(f"block_table must be [>= {B}, >= 1], got {tuple(block_table.shape)}")
+    for t, nm in ((block_table, "block_table"), (seq_lens, "seq_lens"), (out, "out")):
+        if not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous")
+    if q.stride(-1) != 1:
+        raise ValueError("q needs a contiguous last axis")
+    return B
+
+
 def paged_attention_decode(pool, q, block_table, seq_lens, max_seq_len, k_scale, v_scale, sm_scale,
                            out, workspace, o_scale=None) -> None:
     """One query token per sequence: q bf16 [B, Hq, D]; workspace uint8. out is
     bf16 [B, Hq, D], or, with an output scale ``o_scale`` (device fp32
     scalar), uint8 [B, Hq, D] of FP8-E4M3 codes (see fp8_to_bf16)."""
-    _dev(q, "q", torch.bfloat16)
-    _dev(out, "out", torch.bfloat16 if o_scale is None else torch.uint8)
-    _dev(workspace, "workspace", torch.uint8)
-    for t, nm in ((block_table, "block_table"), (seq_lens, "seq_lens")):
-        _dev(t, nm, torch.int32)
-        if not t.is_contiguous():
-            raise ValueError(f"{nm} must be contiguous")
-    if not out.is_contiguous() or q.stride(-1) != 1:
-        raise ValueError("out must be contiguous and q needs a contiguous last axis")
     d = _desc(pool)
+    B = _check_attention_args(d, q, out, block_table, seq_lens, o_scale, k_scale, v_scale)
+    if q.shape[0] != B:
+        raise ValueError(f"q must have one row per sequence ({B}), got {q.shape[0]}")
+    _meta(workspace, "workspace", torch.uint8)
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    _devices((pool, "pool"), (q, "q"), (out, "out"), (block_table, "block_table"), (seq_lens, "seq_lens"),
+             (workspace, "workspace"), (k_scale, "k_scale"), (v_scale, "v_scale"), (o_scale, "o_scale"))
+    args = (ctypes.byref(d), _ptr(q), q.stride(0), q.stride(1), q.shape[1], _ptr(block_table), block_table.shape[1],
+            _ptr(seq_lens), B, int(max_seq_len), _ptr(k_scale), _ptr(v_scale), float(sm_scale))
     if o_scale is None:
-        _check(library().nvfp4_paged_attention_decode(
-            ctypes.byref(d), _ptr(q), q.stride(0), q.stride(1), q.shape[1], _ptr(block_table), block_table.shape[1],
-            _ptr(seq_lens), seq_lens.shape[0], int(max_seq_len), _ptr(k_scale), _ptr(v_scale), float(sm_scale),
-            _ptr(out), _ptr(workspace), workspace.numel(), _stream()))
+        _check(library().nvfp4_paged_attention_decode(*args, _ptr(out), _ptr(workspace),
+                                                      workspace.numel(), _stream()))
     else:
-        _check(library().nvfp4_paged_attention_decode_fp8(
-            ctypes.byref(d), _ptr(q), q.stride(0), q.stride(1), q.shape[1], _ptr(block_table), block_table.shape[1],
-            _ptr(seq_lens), seq_lens.shape[0], int(max_seq_len), _ptr(k_scale), _ptr(v_scale), float(sm_scale),
-            _ptr(o_scale), _ptr(out), _ptr(workspace), workspace.numel(), _stream()))
+        _check(library().nvfp4_paged_attention_decode_fp8(*args, _ptr(o_scale), _ptr(out), _ptr(workspace),
+                                                          workspace.numel(), _stream()))
 
 
 def fp8_to_bf16(codes, o_scale, out) -> None:
     """The FP8 output's epilogue: uint8 codes -> bf16 of the same shape."""
-    _dev(codes, "codes", torch.uint8)
-    _dev(out, "out", torch.bfloat16)
-    if codes.shape != out.shape or not codes.is_contiguous() or not out.is_contiguous():
-        raise ValueError("codes and out must be contiguous and of one shape")
+    _meta(codes, "codes", torch.uint8)
+    _meta(out, "out", torch.bfloat16)
+    _scalar(o_scale, "o_scale")
+    _shape(out, "out", tuple(codes.shape))
+    if not codes.is_contiguous() or not out.is_contiguous():
+        raise ValueError("codes and out must be contiguous")
+    _devices((codes, "codes"), (out, "out"), (o_scale, "o_scale"))
     _check(library().nvfp4_fp8_to_bf16(_ptr(codes), codes.numel(), _ptr(o_scale), _ptr(out), _stream()))
 
 
@@ -293,23 +376,28 @@ def quant_activations_scale_bytes(m: int, k: int, swizzled: bool = True) -> int:
 def quant_activations(x, global_scale, swizzled: bool = True, codes=None, scales=None):
     """bf16 [m, k] -> (codes uint8 [m, k/2], scales uint8): the scales are
     [m, k/16] row-major, or the flat swizzled 128 x 4 tile buffer."""
-    _dev(x, "x", torch.bfloat16)
+    _meta(x, "x", torch.bfloat16)
+    _scalar(global_scale, "global_scale")
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be 2-D with a contiguous last axis")
     m, k = x.shape
     nbytes = quant_activations_scale_bytes(m, k, swizzled)
     if nbytes < 0:
         raise ValueError("k must be a positive multiple of 16")
+    if codes is not None:
+        _meta(codes, "codes", torch.uint8)
+        _shape(codes, "codes", (m, k // 2))
+        if not codes.is_contiguous():
+            raise ValueError("codes must be contiguous")
+    if scales is not None:
+        _meta(scales, "scales", torch.uint8)
+        if scales.numel() != nbytes or not scales.is_contiguous():
+            raise ValueError(f"scales must be contiguous with {nbytes} bytes")
+    _devices((x, "x"), (global_scale, "global_scale"), (codes, "codes"), (scales, "scales"))
     if codes is None:
         codes = torch.empty((m, k // 2), dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty(nbytes if swizzled else (m, k // 16), dtype=torch.uint8, device=x.device)
-    _dev(codes, "codes", torch.uint8)
-    _dev(scales, "scales", torch.uint8)
-    if codes.shape != (m, k // 2) or not codes.is_contiguous():
-        raise ValueError("codes must be contiguous [m, k/2]")
-    if scales.numel() != nbytes or not scales.is_contiguous():
-        raise ValueError(f"scales must be contiguous with {nbytes} bytes")
     _check(library().nvfp4_quant_activations(_ptr(x), x.stride(0), m, k, _ptr(global_scale), 1 if swizzled else 0,
                                              _ptr(codes), _ptr(scales), _stream()))
     return codes, scales
@@ -319,17 +407,16 @@ def paged_attention_prefill(pool, q, cu_seqlens_q, max_q_len, block_table, seq_l
                             k_scale, v_scale, sm_scale, out, causal: bool = True, o_scale=None) -> None:
     """Chunked prefill: q bf16 [total_q, Hq, D]; cu_seqlens_q int32 [B + 1]. out is
     bf16 [total_q, Hq, D], or with an output scale ``o_scale`` uint8 FP8-E4M3 codes."""
-    _dev(q, "q", torch.bfloat16)
-    _dev(out, "out", torch.bfloat16 if o_scale is None else torch.uint8)
-    for t, nm in ((block_table, "block_table"), (seq_lens, "seq_lens"), (cu_seqlens_q, "cu_seqlens_q")):
-        _dev(t, nm, torch.int32)
-        if not t.is_contiguous():
-            raise ValueError(f"{nm} must be contiguous")
-    if not out.is_contiguous() or q.stride(-1) != 1:
-        raise ValueError("out must be contiguous and q needs a contiguous last axis")
     d = _desc(pool)
+    B = _check_attention_args(d, q, out, block_table, seq_lens, o_scale, k_scale, v_scale)
+    _meta(cu_seqlens_q, "cu_seqlens_q", torch.int32)
+    _shape(cu_seqlens_q, "cu_seqlens_q", (B + 1,))
+    if not cu_seqlens_q.is_contiguous():
+        raise ValueError("cu_seqlens_q must be contiguous")
+    _devices((pool, "pool"), (q, "q"), (out, "out"), (block_table, "block_table"), (seq_lens, "seq_lens"),
+             (cu_seqlens_q, "cu_seqlens_q"), (k_scale, "k_scale"), (v_scale, "v_scale"), (o_scale, "o_scale"))
     common = (ctypes.byref(d), _ptr(q), q.stride(0), q.stride(1), q.shape[1], _ptr(cu_seqlens_q), int(max_q_len),
-              q.shape[0], _ptr(block_table), block_table.shape[1], _ptr(seq_lens), seq_lens.shape[0],
+              q.shape[0], _ptr(block_table), block_table.shape[1], _ptr(seq_lens), B,
               int(max_seq_len), _ptr(k_scale), _ptr(v_scale), float(sm_scale), 1 if causal else 0)
     if o_scale is None:
         _check(library().nvfp4_paged_attention_prefill(*common, _ptr(out), ctypes.c_void_p(0), 0, _stream()))
