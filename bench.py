@@ -8,7 +8,12 @@ rest). K steps are captured into one HIP graph and timed as a whole; pool
 copies rotate between steps so that no step finds its cache in the 256 MB
 Infinity Cache (every copy holds identical bytes). Decode-only and
 append-only graphs over the same rotation give the per-kernel times used for
-the roofline, and a paged-dequantize graph reports that operation's rate.
+the roofline, and a read-only stream of the same bytes over the same
+rotation gives the read ceiling the decode stream is judged against.
+
+The headline workload (default: the long-context decode batch, the largest
+decode stream) is measured in full; the mixed serving batch's decode half
+and prefill are measured beside it and reported as extra fields.
 
 Prints one JSON line. `value` is the decode attention's effective HBM
 bandwidth (cache bytes + q + out + block ids + lengths over the decode
@@ -31,6 +36,7 @@ HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0
 MALL_BYTES = 256 << 20
 WORKLOADS = {"tiny_decode": 1, "small_decode": 2, "long_decode": 3, "chunked_prefill": 4, "mixed_serving": 5}
+SERVING_BATCH = "mixed_serving"
 METRIC = "decode attention effective HBM GB/s (% of peak) + append Mtokens/s, NVFP4 KV"
 KERNEL_SOURCES = ["bit_quantized_paged_amd/csrc/attn.hip", "bit_quantized_paged_amd/csrc/attn_core.hpp",
                   "bit_quantized_paged_amd/csrc/device_common.hpp"]
@@ -41,9 +47,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="small_decode", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="long_decode", choices=sorted(WORKLOADS))
     ap.add_argument("--copies", type=int, default=0, help="pool copies to rotate (0: enough to exceed the MALL 3x)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-serving-batch", action="store_true",
+                    help="skip the mixed serving batch measured beside the headline workload")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 512 MiB device copy (to scale rocprofv3 FETCH_SIZE/WRITE_SIZE)")
     return ap.parse_args()
@@ -97,39 +105,79 @@ def read_traffic(kernel: str, workload: str):
     return float(rec["bytes_per_launch"])
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported (the NVFP4 KV path here is "
-              "single-GPU; see the design notes for how it would shard)", file=sys.stderr)
-        sys.exit(2)
+class Timer:
+    """Graph capture of K calls and replay timing on the current stream."""
 
+    def __init__(self, K):
+        import torch
+        self.K = K
+        self.cap_stream = torch.cuda.Stream()
+
+    def capture(self, fn, n):
+        """A graph of K calls fn(s % n)."""
+        import torch
+        g = torch.cuda.CUDAGraph()
+        self.cap_stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(self.cap_stream):
+            with torch.cuda.graph(g, stream=self.cap_stream):
+                for s in range(self.K):
+                    fn(s % n)
+        torch.cuda.current_stream().wait_stream(self.cap_stream)
+        return g
+
+    def time(self, g, reps=1):
+        """Seconds for one replay of g (K steps): the median of `reps` timed
+        replays on the current stream (the stream the kernels run on), after
+        untimed warm replays (the first replays on a fresh GPU run slower
+        while its clocks ramp up)."""
+        import torch
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        gpu, wall = [], []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            wall.append(time.perf_counter() - t0)
+            gpu.append(e0.elapsed_time(e1) / 1e3)
+        order = sorted(range(reps), key=lambda r: gpu[r])
+        mid = order[reps // 2]
+        return gpu[mid], wall[mid]
+
+    def per_call(self, fn, n, reps=3):
+        """Seconds per call of fn over a graph of K calls rotated over n."""
+        g = self.capture(fn, n)
+        t, _ = self.time(g, reps)
+        del g
+        return t / self.K
+
+
+def run_workload(args, name, full, dev):
+    """Time one workload's step and kernels. full: also the codec, FP8-cache,
+    activation-quantisation and bulk-append measurements and the read-stream
+    ceiling. Returns (results dict, workload, decode/prefill index arrays)."""
     import numpy as np
     import torch
 
     import bit_quantized_paged_amd as nvk
+    from bit_quantized_paged_amd import probe
     from workloads import fp8_kv_scales, make_activations, make_config
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-
-    if args.calibrate_copy:
-        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"calibrate_copy_bytes": src.numel()}))
-        return
-
-    cfg = WORKLOADS[args.workload]
+    cfg = WORKLOADS[name]
     t_gen = time.perf_counter()
     w = make_config(cfg)
     gen_s = time.perf_counter() - t_gen
     B, Hq, Hkv, D, bs = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_size, w.block_size
     fd = D // 2 + D // 16
     sm_scale = 1.0 / math.sqrt(D)
+    K = args.steps
+    T = Timer(K)
 
     bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
     i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
@@ -192,136 +240,106 @@ def main():
     ref_d = outd.clone() if wd is not None else None
     ref_p = outp.clone() if wp is not None else None
 
-    K = args.steps
-    cap_stream = torch.cuda.Stream()
-
-    def capture(fn, n=None):
-        """A graph of K calls fn(s % n), n defaulting to the pool copies."""
-        n = n or copies
-        g = torch.cuda.CUDAGraph()
-        cap_stream.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(cap_stream):
-            with torch.cuda.graph(g, stream=cap_stream):
-                for s in range(K):
-                    fn(s % n)
-        torch.cuda.current_stream().wait_stream(cap_stream)
-        return g
-
-    def time_graph(g, reps=1):
-        """Seconds for one replay of g (K steps): the median of `reps` timed
-        replays on the current stream, after untimed warm replays (the first
-        replays on a fresh GPU run slower while its clocks ramp up)."""
-        for _ in range(3):
-            g.replay()
-        torch.cuda.synchronize()
-        stream = torch.cuda.current_stream()
-        gpu, wall = [], []
-        for _ in range(reps):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            e0.record(stream)
-            g.replay()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            wall.append(time.perf_counter() - t0)
-            gpu.append(e0.elapsed_time(e1) / 1e3)
-        order = sorted(range(reps), key=lambda r: gpu[r])
-        mid = order[reps // 2]
-        return gpu[mid], wall[mid]
-
-    g_step = capture(step)
-    step_gpu_s, step_wall_s = time_graph(g_step)
+    g_step = T.capture(step, copies)
+    step_gpu_s, step_wall_s = T.time(g_step)
+    del g_step
     if wd is not None:
         assert torch.equal(outd, ref_d), "graph replay of the step differs from the eager decode"
     if wp is not None:
         assert torch.equal(outp, ref_p), "graph replay of the step differs from the eager prefill"
-    res = {}
-    g_app = capture(do_append)
-    res["append_s"], _ = time_graph(g_app, reps=3)
-    del g_app
+    res = {"name": w.name, "seed": cfg, "gen_s": gen_s, "K": K, "copies": copies, "pool_bytes": pool_bytes,
+           "step_gpu_s": step_gpu_s, "step_wall_s": step_wall_s, "n_new": n_new,
+           "append_s": T.per_call(do_append, copies), "B": B, "Hq": Hq, "Hkv": Hkv, "D": D, "bs": bs,
+           "total_tokens": int(w.seq_lens.sum()), "decode_seqs": int(len(dec_idx)), "prefill_seqs": int(len(pre_idx))}
+    res["append_bytes"] = n_new * (Hkv * (2 * 2 * D + 2 * fd) + 8)
+    extra = {}
     if wd is not None:
-        g_dec = capture(do_decode)
-        res["decode_s"], _ = time_graph(g_dec, reps=3)
+        res["decode_s"] = T.per_call(do_decode, copies)
         assert torch.equal(outd, ref_d), "graph replay of decode differs from eager"
-        del g_dec
+        res["decode_bytes"] = (int(wd.seq_lens.astype(np.int64).sum()) * Hkv * 2 * fd + 2 * wd.num_seqs * Hq * D * 2
+                               + 4 * int(np.sum((wd.seq_lens + bs - 1) // bs)) + 4 * wd.num_seqs)
+        plan = nvk.decode_plan(wd.num_seqs, Hkv, D, bs, int(wd.block_table.shape[1]), maxd, "nvfp4")
+        res["decode_kernel"] = "decode_pair_kernel" if plan == nvk.DECODE_PER_PAIR else "decode_split_kernel"
     if wp is not None:
-        g_pre = capture(do_prefill)
-        res["prefill_s"], _ = time_graph(g_pre, reps=3)
-        del g_pre
+        res["prefill_s"] = T.per_call(do_prefill, copies)
+        assert torch.equal(outp, ref_p), "graph replay of prefill differs from eager"
+        pairs = 0
+        for b in range(wp.num_seqs):
+            L, q = int(wp.seq_lens[b]), int(wp.q_lens[b])
+            pairs += q * (L - q) + q * (q + 1) // 2
+        res["prefill_flops"] = 4.0 * D * Hq * pairs
+    if not full:
+        return res, extra, w, dec_idx, pre_idx
 
-    # ---- paged dequantize of the decode batch (reported, not part of the step)
-    deq = None
     if wd is not None:
+        # ---- read ceiling: a plain read-only stream of the decode's bytes
+        # over the same pool rotation (each copy's first bytes, contiguous)
+        nb = min(res["decode_bytes"], pool_bytes) // 16 * 16
+        grid = 8 * torch.cuda.get_device_properties(dev).multi_processor_count
+        sink = torch.zeros(4 * grid, dtype=torch.int32, device=dev)
+        rs = T.per_call(lambda r: probe.read_stream(bases[r], nb, sink, grid), copies)
+        extra["read_stream_ceiling_gbs"] = round(nb / rs / 1e9, 1)
+        extra["read_stream_us"] = round(rs * 1e6, 2)
+        extra["read_stream_bytes"] = nb
+        del sink
+
+        # ---- paged dequantize of the decode batch (reported, not part of the step)
         rows = int(wd.seq_lens.sum())
         cu = np.zeros(wd.num_seqs, np.int32)
         cu[1:] = np.cumsum(wd.seq_lens)[:-1]
         cud = i32(cu)
         ok = torch.empty((rows, Hkv, D), dtype=torch.bfloat16, device=dev)
         ov = torch.empty_like(ok)
-        do_deq = lambda r: nvk.dequant_paged(pools[r], btd, sld, cud, maxd, k_scale, v_scale, ok, ov)
-        g_deq = capture(do_deq)
-        deq_s, _ = time_graph(g_deq, reps=3)
-        del g_deq
+        deq_s = T.per_call(lambda r: nvk.dequant_paged(pools[r], btd, sld, cud, maxd, k_scale, v_scale, ok, ov),
+                           copies)
         deq_bytes = rows * Hkv * 2 * (fd + 2 * D) + 4 * int(np.sum((wd.seq_lens + bs - 1) // bs))
-        deq = {"gbs": round(deq_bytes / (deq_s / K) / 1e9, 1), "us": round(deq_s / K * 1e6, 2)}
+        extra["dequant_gbs"] = round(deq_bytes / deq_s / 1e9, 1)
+        extra["dequant_us"] = round(deq_s * 1e6, 2)
         del ok, ov
 
-    # ---- the codec on its own (reported, not part of the step): page-form
-    # dequantize of the pages the decode batch uses, and quantize-dequantize
-    # emulation of the workload's K/V rows in place
-    codec = {}
-    if wd is not None:
+        # ---- page-form dequantize of the pages the decode batch uses
         used = np.unique(np.concatenate([wd.block_table[b, :(int(wd.seq_lens[b]) + bs - 1) // bs]
                                          for b in range(wd.num_seqs)])).astype(np.int32)
         ids = i32(used)
         pages_out = torch.empty((w.num_blocks, 2, bs, Hkv, D), dtype=torch.bfloat16, device=dev)
-        g_pg = capture(lambda r: nvk.dequant_pages(pools[r], ids, k_scale, v_scale, pages_out))
-        pg_s, _ = time_graph(g_pg, reps=3)
-        del g_pg, pages_out
+        pg_s = T.per_call(lambda r: nvk.dequant_pages(pools[r], ids, k_scale, v_scale, pages_out), copies)
+        del pages_out
         pg_bytes = len(used) * 2 * bs * Hkv * (fd + 2 * D) + 4 * len(used)
-        codec["dequant_pages_gbs"] = round(pg_bytes / (pg_s / K) / 1e9, 1)
-        codec["dequant_pages_us"] = round(pg_s / K * 1e6, 2)
-    if wd is not None:
-        # FP8-E4M3 output (output scale 1) and its bf16 epilogue; the extra
-        # rounding is measured against the bf16 output of the same decode
+        extra["dequant_pages_gbs"] = round(pg_bytes / pg_s / 1e9, 1)
+        extra["dequant_pages_us"] = round(pg_s * 1e6, 2)
+
+        # ---- FP8-E4M3 output (output scale 1) and its bf16 epilogue; the
+        # extra rounding is measured against the bf16 output of the same decode
         o_s = torch.ones(1, dtype=torch.float32, device=dev)
         codes = torch.empty(outd.shape, dtype=torch.uint8, device=dev)
-        g_f8 = capture(lambda r: nvk.paged_attention_decode(pools[r], qd, btd, sld, maxd, k_scale, v_scale, sm_scale,
-                                                            codes, wsd, o_scale=o_s))
-        f8_s, _ = time_graph(g_f8, reps=3)
-        del g_f8
+        f8_s = T.per_call(lambda r: nvk.paged_attention_decode(pools[r], qd, btd, sld, maxd, k_scale, v_scale,
+                                                               sm_scale, codes, wsd, o_scale=o_s), copies)
         back = torch.empty_like(outd)
-        g_ep = capture(lambda r: nvk.fp8_to_bf16(codes, o_s, back))
-        ep_s, _ = time_graph(g_ep, reps=3)
-        del g_ep
+        ep_s = T.per_call(lambda r: nvk.fp8_to_bf16(codes, o_s, back), copies)
         torch.cuda.synchronize()
         ref16 = ref_d.float()
         diff = (back.float() - ref16).abs()
         rel = diff / ref16.abs().clamp_min(1e-2)
-        codec["decode_fp8out_us"] = round(f8_s / K * 1e6, 2)
-        codec["fp8_epilogue_us"] = round(ep_s / K * 1e6, 2)
-        codec["fp8_out_extra_err"] = {"max_abs": round(float(diff.max()), 5), "rms_abs": round(float(diff.pow(2).mean().sqrt()), 6),
+        extra["decode_fp8out_us"] = round(f8_s * 1e6, 2)
+        extra["fp8_epilogue_us"] = round(ep_s * 1e6, 2)
+        extra["fp8_out_extra_err"] = {"max_abs": round(float(diff.max()), 5),
+                                      "rms_abs": round(float(diff.pow(2).mean().sqrt()), 6),
                                       "max_rel": round(float(rel.max()), 5), "ref": "bf16 output of the same decode"}
         del codes, back
-    # in place on copies of the workload's K/V, rotated so that no call finds
-    # its rows in the MALL
+
+    # ---- quantize-dequantize emulation in place on copies of the workload's
+    # K/V, rotated so that no call finds its rows in the MALL
     kq, vq = bf(w.key), bf(w.value)
     q_copies = max(2, math.ceil(3 * MALL_BYTES / (2 * kq.numel() * 2)))
     kvs = [(kq, vq)] + [(kq.clone(), vq.clone()) for _ in range(q_copies - 1)]
-    g_qdq = capture(lambda r: nvk.qdq(kvs[r % q_copies][0], kvs[r % q_copies][1], k_scale, v_scale), n=q_copies)
-    qdq_s, _ = time_graph(g_qdq, reps=3)
-    del g_qdq
-    qdq_bytes = 2 * 2 * kq.numel() * 2
-    codec["qdq_gbs"] = round(qdq_bytes / (qdq_s / K) / 1e9, 1)
-    codec["qdq_us"] = round(qdq_s / K * 1e6, 2)
-    codec["qdq_tokens"] = int(kq.shape[0])
+    qdq_s = T.per_call(lambda r: nvk.qdq(kvs[r][0], kvs[r][1], k_scale, v_scale), q_copies)
+    extra["qdq_gbs"] = round(2 * 2 * kq.numel() * 2 / qdq_s / 1e9, 1)
+    extra["qdq_us"] = round(qdq_s * 1e6, 2)
+    extra["qdq_tokens"] = int(kq.shape[0])
     del kq, vq, kvs
 
-    # ---- activation quantisation with swizzled scales (reported, not part
-    # of the step): the hidden states of a 4 x 2048-token prefill chunk,
-    # hidden size 32 heads x 128, rotated through enough copies to miss the
-    # MALL
+    # ---- activation quantisation with swizzled scales: the hidden states of a
+    # 4 x 2048-token prefill chunk, hidden size 32 heads x 128, rotated past the MALL
     am, ak = 8192, 4096
     abits, ag = make_activations(seed=4, m=am, k=ak)
     a0 = torch.from_numpy(abits.view(np.int16)).to(dev).view(torch.bfloat16)
@@ -329,27 +347,26 @@ def main():
     acts = [a0] + [a0.clone() for _ in range(a_copies - 1)]
     ags = torch.tensor([float(ag)], dtype=torch.float32, device=dev)
     a_codes, a_sf = nvk.quant_activations(a0, ags, True)
-    g_aq = capture(lambda r: nvk.quant_activations(acts[r % a_copies], ags, True, a_codes, a_sf), n=a_copies)
-    aq_s, _ = time_graph(g_aq, reps=3)
-    del g_aq, acts, a0
+    aq_s = T.per_call(lambda r: nvk.quant_activations(acts[r], ags, True, a_codes, a_sf), a_copies)
     aq_bytes = am * ak * 2 + am * ak // 2 + a_sf.numel()
-    codec["act_quant_us"] = round(aq_s / K * 1e6, 2)
-    codec["act_quant_gbs"] = round(aq_bytes / (aq_s / K) / 1e9, 1)
-    codec["act_quant_shape"] = [am, ak]
-    del a_codes, a_sf
+    extra["act_quant_us"] = round(aq_s * 1e6, 2)
+    extra["act_quant_gbs"] = round(aq_bytes / aq_s / 1e9, 1)
+    extra["act_quant_shape"] = [am, ak]
+    del acts, a0, a_codes, a_sf
 
-    # ---- the same decode over FP8 caches (E4M3, E5M2) of the same K/V, with
-    # the per-tensor scale amax / largest finite value: the kernel-level
-    # NVFP4-vs-FP8 comparison (reported, not part of the step)
-    if wd is not None:
-        exact = exact_decode(wd, sm_scale, dev)
+    # ---- the same decode and prefill over FP8 caches (E4M3, E5M2) of the same
+    # K/V, with the per-tensor scale amax / largest finite value: the
+    # kernel-level NVFP4-vs-FP8 comparison
+    if wd is not None or wp is not None:
+        exact = exact_decode(wd, sm_scale, dev) if wd is not None else None
 
         def err_vs_exact(o):
             e = (o.float() - exact).abs()
             return {"max_abs": round(float(e.max()), 5), "rms": round(float(e.pow(2).mean().sqrt()), 6)}
 
-        codec["nvfp4_decode_err_vs_exact"] = err_vs_exact(ref_d)
-        fp8 = {}
+        if wd is not None:
+            extra["nvfp4_decode_err_vs_exact"] = err_vs_exact(ref_d)
+        fp8d, fp8p = {}, {}
         all_k, all_v, all_s = bf(w.key), bf(w.value), i64(w.slot_mapping)
         for kv in ("fp8_e4m3", "fp8_e5m2"):
             ks8, vs8 = fp8_kv_scales(w, kv)
@@ -359,61 +376,50 @@ def main():
             nvk.append(b8.permute(0, 1, 3, 2, 4), all_k, all_v, all_s, ks8_t, vs8_t)
             n8 = max(2, math.ceil(3 * MALL_BYTES / b8.numel()))
             p8s = [b8.permute(0, 1, 3, 2, 4)] + [b8.clone().permute(0, 1, 3, 2, 4) for _ in range(n8 - 1)]
-            out8 = torch.empty_like(outd)
-            g8 = capture(lambda r: nvk.paged_attention_decode(p8s[r % n8], qd, btd, sld, maxd, ks8_t, vs8_t,
-                                                              sm_scale, out8, wsd), n=n8)
-            t8, _ = time_graph(g8, reps=3)
-            del g8
-            torch.cuda.synchronize()
-            b8_bytes = (int(wd.seq_lens.astype(np.int64).sum()) * Hkv * 2 * D + 2 * wd.num_seqs * Hq * D * 2
-                        + 4 * int(np.sum((wd.seq_lens + bs - 1) // bs)) + 4 * wd.num_seqs)
-            plan8 = nvk.decode_plan(wd.num_seqs, Hkv, D, bs, int(wd.block_table.shape[1]), maxd, kv)
-            fp8[kv] = {"decode_us": round(t8 / K * 1e6, 2), "gbs": round(b8_bytes / (t8 / K) / 1e9, 1),
-                       "cache_bytes_per_launch": b8_bytes, "pool_copies": n8,
-                       "kernel": "decode_pair_kernel" if plan8 == nvk.DECODE_PER_PAIR else "decode_split_kernel",
-                       "time_vs_nvfp4": round(t8 / res["decode_s"], 3), "err_vs_exact": err_vs_exact(out8)}
-            del p8s, b8, out8
-        codec["fp8_kv_decode"] = fp8
-        del all_k, all_v, all_s
-    if wp is not None:
-        # chunked prefill over FP8 caches of the same K/V (time only)
-        fp8p = {}
-        all_k, all_v, all_s = bf(w.key), bf(w.value), i64(w.slot_mapping)
-        for kv in ("fp8_e4m3", "fp8_e5m2"):
-            ks8, vs8 = fp8_kv_scales(w, kv)
-            ks8_t = torch.tensor([float(ks8)], dtype=torch.float32, device=dev)
-            vs8_t = torch.tensor([float(vs8)], dtype=torch.float32, device=dev)
-            b8 = torch.zeros((w.num_blocks, 2, Hkv, bs, D), dtype=nvk.KV_DTYPES[kv][1], device=dev)
-            nvk.append(b8.permute(0, 1, 3, 2, 4), all_k, all_v, all_s, ks8_t, vs8_t)
-            n8 = max(2, math.ceil(3 * MALL_BYTES / b8.numel()))
-            p8s = [b8.permute(0, 1, 3, 2, 4)] + [b8.clone().permute(0, 1, 3, 2, 4) for _ in range(n8 - 1)]
-            outp8 = torch.empty_like(outp)
-            g8 = capture(lambda r: nvk.paged_attention_prefill(p8s[r % n8], qp, cup, maxq, btp, slp, maxp, ks8_t,
-                                                               vs8_t, sm_scale, outp8), n=n8)
-            t8, _ = time_graph(g8, reps=3)
-            del g8, p8s, b8, outp8
-            fp8p[kv] = {"prefill_us": round(t8 / K * 1e6, 2), "time_vs_nvfp4": round(t8 / res["prefill_s"], 3)}
-        codec["fp8_kv_prefill"] = fp8p
+            if wd is not None:
+                out8 = torch.empty_like(outd)
+                t8 = T.per_call(lambda r: nvk.paged_attention_decode(p8s[r], qd, btd, sld, maxd, ks8_t, vs8_t,
+                                                                     sm_scale, out8, wsd), n8)
+                torch.cuda.synchronize()
+                b8_bytes = (int(wd.seq_lens.astype(np.int64).sum()) * Hkv * 2 * D + 2 * wd.num_seqs * Hq * D * 2
+                            + 4 * int(np.sum((wd.seq_lens + bs - 1) // bs)) + 4 * wd.num_seqs)
+                plan8 = nvk.decode_plan(wd.num_seqs, Hkv, D, bs, int(wd.block_table.shape[1]), maxd, kv)
+                fp8d[kv] = {"decode_us": round(t8 * 1e6, 2), "gbs": round(b8_bytes / t8 / 1e9, 1),
+                            "cache_bytes_per_launch": b8_bytes, "pool_copies": n8,
+                            "kernel": "decode_pair_kernel" if plan8 == nvk.DECODE_PER_PAIR else "decode_split_kernel",
+                            "time_vs_nvfp4": round(t8 / res["decode_s"], 3), "err_vs_exact": err_vs_exact(out8)}
+                del out8
+            if wp is not None:
+                outp8 = torch.empty_like(outp)
+                t8 = T.per_call(lambda r: nvk.paged_attention_prefill(p8s[r], qp, cup, maxq, btp, slp, maxp, ks8_t,
+                                                                      vs8_t, sm_scale, outp8), n8)
+                fp8p[kv] = {"prefill_us": round(t8 * 1e6, 2), "time_vs_nvfp4": round(t8 / res["prefill_s"], 3)}
+                del outp8
+            del p8s, b8
+        if fp8d:
+            extra["fp8_kv_decode"] = fp8d
+        if fp8p:
+            extra["fp8_kv_prefill"] = fp8p
         del all_k, all_v, all_s
 
     # ---- bulk append: every cached token of the workload in one call (the
-    # pool fill, K/V inputs rotated past the MALL), and the device-copy
-    # ceiling of this machine for reference
+    # pool fill, K/V inputs rotated past the MALL)
     n_cached = int(cached.sum())
     if n_cached:
         kc, vc, sc = bf(w.key[cached]), bf(w.value[cached]), i64(w.slot_mapping[cached])
         kv_bytes = 2 * kc.numel() * 2
         b_copies = max(1, math.ceil(3 * MALL_BYTES / kv_bytes))
         kvc = [(kc, vc)] + [(kc.clone(), vc.clone()) for _ in range(b_copies - 1)]
-        g_bulk = capture(lambda r: nvk.append(pools[r % copies], kvc[r % b_copies][0], kvc[r % b_copies][1], sc,
-                                              k_scale, v_scale), n=copies * b_copies)
-        bulk_s, _ = time_graph(g_bulk, reps=3)
-        del g_bulk, kvc, kc, vc, sc
+        bulk_s = T.per_call(lambda r: nvk.append(pools[r % copies], kvc[r % b_copies][0], kvc[r % b_copies][1], sc,
+                                                 k_scale, v_scale), copies * b_copies)
+        del kvc, kc, vc, sc
         bulk_bytes = n_cached * (Hkv * (2 * 2 * D + 2 * fd) + 8)
-        codec["bulk_append_tokens"] = n_cached
-        codec["bulk_append_us"] = round(bulk_s / K * 1e6, 2)
-        codec["bulk_append_mtok_s"] = round(n_cached / (bulk_s / K) / 1e6, 1)
-        codec["bulk_append_gbs"] = round(bulk_bytes / (bulk_s / K) / 1e9, 1)
+        extra["bulk_append_tokens"] = n_cached
+        extra["bulk_append_us"] = round(bulk_s * 1e6, 2)
+        extra["bulk_append_mtok_s"] = round(n_cached / bulk_s / 1e6, 1)
+        extra["bulk_append_gbs"] = round(bulk_bytes / bulk_s / 1e9, 1)
+
+    # ---- device-copy ceiling (1 GiB read + write), for reference
     csrc_t = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     cdst_t = torch.empty_like(csrc_t)
     for _ in range(3):
@@ -427,72 +433,107 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         ct.append(e0.elapsed_time(e1) / 1e3)
-    codec["device_copy_ceiling_gbs"] = round(2 * csrc_t.numel() / sorted(ct)[2] / 1e9, 1)
+    extra["device_copy_ceiling_gbs"] = round(2 * csrc_t.numel() / sorted(ct)[2] / 1e9, 1)
     del csrc_t, cdst_t
+    return res, extra, w, dec_idx, pre_idx
 
-    # ---- algorithmic work
+
+def rates(res):
+    """Per-launch rates of one workload's kernels."""
+    out = {"append_us": round(res["append_s"] * 1e6, 2),
+           "append_mtok_s": round(res["n_new"] / res["append_s"] / 1e6, 3),
+           "append_gbs": round(res["append_bytes"] / res["append_s"] / 1e9, 1),
+           "step_gpu_us": round(res["step_gpu_s"] / res["K"] * 1e6, 2)}
+    if "decode_s" in res:
+        gbs = res["decode_bytes"] / res["decode_s"] / 1e9
+        out.update({"decode_us": round(res["decode_s"] * 1e6, 2), "decode_gbs": round(gbs, 1),
+                    "decode_pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1), "decode_bytes": res["decode_bytes"],
+                    "decode_kernel": res["decode_kernel"]})
+    if "prefill_s" in res:
+        tf = res["prefill_flops"] / res["prefill_s"] / 1e12
+        out.update({"prefill_us": round(res["prefill_s"] * 1e6, 2), "prefill_tflops": round(tf, 2),
+                    "prefill_pct_of_mfma_peak": round(100 * tf / MFMA_F16_PEAK_TFLOPS, 2)})
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported (the NVFP4 KV path here is "
+              "single-GPU; see the design notes for how it would shard)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.calibrate_copy:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": src.numel()}))
+        return
+
+    res, extra, w, dec_idx, pre_idx = run_workload(args, args.workload, True, dev)
+    r = rates(res)
+    K = args.steps
     out = {"metric": METRIC, "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
-           "ms_per_step": round(step_wall_s / K * 1e3, 5), "higher_is_better": True, "scaling": "weak",
+           "ms_per_step": round(res["step_wall_s"] / K * 1e3, 5), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "f16", "data": "synthetic"}
-    app_bytes = n_new * (Hkv * (2 * 2 * D + 2 * fd) + 8)
-    app_us = res["append_s"] / K * 1e6
-    extra = {"append_mtok_s": round(n_new / (res["append_s"] / K) / 1e6, 3), "append_us": round(app_us, 2),
-             "append_gbs": round(app_bytes / (res["append_s"] / K) / 1e9, 1),
-             "step_gpu_us": round(step_gpu_s / K * 1e6, 2)}
     roof = None
-    if wd is not None:
-        dec_bytes = (int(wd.seq_lens.astype(np.int64).sum()) * Hkv * 2 * fd + 2 * wd.num_seqs * Hq * D * 2
-                     + 4 * int(np.sum((wd.seq_lens + bs - 1) // bs)) + 4 * wd.num_seqs)
-        dec_s = res["decode_s"] / K
-        gbs = dec_bytes / dec_s / 1e9
-        out["value"] = round(gbs, 1)
-        extra.update({"decode_us": round(dec_s * 1e6, 2), "decode_pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
-                      "decode_bytes": dec_bytes})
-        plan = nvk.decode_plan(wd.num_seqs, Hkv, D, bs, int(wd.block_table.shape[1]), maxd, "nvfp4")
-        dec_kernel = "decode_pair_kernel" if plan == nvk.DECODE_PER_PAIR else "decode_split_kernel"
-        traffic = read_traffic(dec_kernel, args.workload)
-        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": dec_kernel,
-                "bytes_per_launch": dec_bytes, "avg_launch_us": round(dec_s * 1e6, 3)}
-    if wp is not None:
-        pairs = 0
-        for b in range(wp.num_seqs):
-            L, q = int(wp.seq_lens[b]), int(wp.q_lens[b])
-            pairs += q * (L - q) + q * (q + 1) // 2
-        flops = 4.0 * D * Hq * pairs
-        pre_s = res["prefill_s"] / K
-        extra.update({"prefill_us": round(pre_s * 1e6, 2), "prefill_tflops": round(flops / pre_s / 1e12, 2),
-                      "prefill_pct_of_mfma_peak": round(100 * flops / pre_s / 1e12 / MFMA_F16_PEAK_TFLOPS, 2)})
-        if wd is None:
-            out["value"] = round(flops / pre_s / 1e12, 2)
-            out["unit"] = "TFLOP/s"
-            roof = {"bound": "mfma", "achieved": round(flops / pre_s / 1e12, 2), "peak": MFMA_F16_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(flops / pre_s / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
-                    "traffic": None, "kernel": "prefill_kernel", "flops_per_launch": flops,
-                    "avg_launch_us": round(pre_s * 1e6, 3)}
-    if deq is not None:
-        extra["dequant_gbs"] = deq["gbs"]
-        extra["dequant_us"] = deq["us"]
-    extra.update(codec)
-    out["config"] = {"workload": w.name, "num_seqs": B, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
-                     "block_size": bs, "total_tokens": int(w.seq_lens.sum()), "new_tokens": n_new,
-                     "decode_seqs": int(len(dec_idx)), "prefill_seqs": int(len(pre_idx)), "kv_dtype": "nvfp4",
-                     "pool_copies": copies, "pool_bytes": pool_bytes, "seed": cfg}
+    if "decode_s" in res:
+        out["value"] = r["decode_gbs"]
+        roof = {"bound": "hbm", "achieved": r["decode_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(r["decode_gbs"] / HBM_PEAK_GBS, 4),
+                "traffic": read_traffic(res["decode_kernel"], res["name"]), "kernel": res["decode_kernel"],
+                "bytes_per_launch": res["decode_bytes"], "avg_launch_us": round(res["decode_s"] * 1e6, 3)}
+        if "read_stream_ceiling_gbs" in extra:
+            roof["read_stream_ceiling_gbs"] = extra["read_stream_ceiling_gbs"]
+            roof["frac_of_read_stream_ceiling"] = round(r["decode_gbs"] / extra["read_stream_ceiling_gbs"], 4)
+    elif "prefill_s" in res:
+        out["value"] = r["prefill_tflops"]
+        out["unit"] = "TFLOP/s"
+        roof = {"bound": "mfma", "achieved": r["prefill_tflops"], "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(r["prefill_tflops"] / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+                "kernel": "prefill_kernel", "flops_per_launch": res["prefill_flops"],
+                "avg_launch_us": round(res["prefill_s"] * 1e6, 3)}
+    out["config"] = {"workload": res["name"], "num_seqs": res["B"], "num_q_heads": res["Hq"],
+                     "num_kv_heads": res["Hkv"], "head_dim": res["D"], "block_size": res["bs"],
+                     "total_tokens": res["total_tokens"], "new_tokens": res["n_new"],
+                     "decode_seqs": res["decode_seqs"], "prefill_seqs": res["prefill_seqs"], "kv_dtype": "nvfp4",
+                     "pool_copies": res["copies"], "pool_bytes": res["pool_bytes"], "seed": res["seed"]}
     out["roofline"] = roof
+    out.update(r)
     out.update(extra)
     out["source_hash"] = source_hash()
-    out["input_gen_s"] = round(gen_s, 2)
+    out["input_gen_s"] = round(res["gen_s"], 2)
 
+    if not args.no_serving_batch and args.workload != SERVING_BATCH:
+        # the mixed serving batch beside the headline: its decode half and its
+        # prefill, each timed as above (extra fields only)
+        torch.cuda.empty_cache()
+        sres, _, _, _, _ = run_workload(args, SERVING_BATCH, False, dev)
+        sr = rates(sres)
+        out["serving_batch"] = {"workload": sres["name"], "decode_seqs": sres["decode_seqs"],
+                                "prefill_seqs": sres["prefill_seqs"], **sr}
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, dec_idx, pre_idx, cached, sm_scale)
+        out["cpu_baseline"] = cpu_baseline(w, dec_idx, pre_idx, 1.0 / math.sqrt(w.head_size))
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(w, dec_idx, pre_idx, cached, sm_scale):
+def cpu_baseline(w, dec_idx, pre_idx, sm_scale):
     """The oracle, untuned, on a bounded sample of the same step: quantize-
     append of the sampled sequences' new tokens, then their attention. The
-    cached prefix of the sample is quantised beforehand (not timed)."""
+    cached prefix of the sample is quantised beforehand (not timed). `cores`
+    is the most threads the oracle can use: its matrix products run on the
+    BLAS thread pool, its elementwise NumPy work on one thread."""
     import numpy as np
+    import torch
     from oracle import nvfp4_oracle as O
     try:
         from threadpoolctl import threadpool_info
@@ -523,8 +564,14 @@ def cpu_baseline(w, dec_idx, pre_idx, cached, sm_scale):
             break
     per = el / reps
     dec_bytes = int(ws.seq_lens.astype(np.int64).sum()) * ws.num_kv_heads * 2 * fd
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        affinity = None
     return {"value": round(dec_bytes / per / 1e9, 4), "unit": "GB/s", "cores": int(blas_threads),
             "kind": "oracle", "seconds_per_step": round(per, 3),
+            "host": {"os_cpu_count": os.cpu_count(), "affinity_cpus": affinity,
+                     "torch_threads": torch.get_num_threads(), "blas_threads": int(blas_threads)},
             "sample": f"{len(picked)} of {w.num_seqs} sequences ({int(ws.seq_lens.sum())} tokens): oracle append "
                       f"of their new tokens + attention, {reps} reps; value = their cache bytes / time"}
 

@@ -331,7 +331,7 @@ static nvfp4kv_status prefill_impl(const nvfp4kv_cache* cache, const void* q, in
     return fail(NVFP4KV_INVALID_ARGUMENT, "num_q_heads must be a positive multiple of num_kv_heads");
   if (p.hkv > 65535) return fail(NVFP4KV_UNSUPPORTED, "num_kv_heads too large");
   if (max_q_len < 0 || total_q < 0) return fail(NVFP4KV_INVALID_ARGUMENT, "max_q_len and total_q must be >= 0");
-  if (num_seqs == 0 || max_q_len == 0 || total_q == 0) return ok();
+  if (num_seqs == 0 || total_q == 0) return ok();
   if ((s = check_bf16_rows(q, q_stride_token, q_stride_head, "q"))) return s;
   if (max_blocks_per_seq < 1) return fail(NVFP4KV_INVALID_ARGUMENT, "max_blocks_per_seq must be >= 1");
   if ((int64_t)max_blocks_per_seq * p.bs > INT32_MAX / 2)

@@ -851,37 +851,35 @@ struct PrefillStages {
 
 // Waves per SIMD the prefill register budget is sized for: without the hint
 // the compiler spends the whole 256-register budget of two waves (or more)
-// at head sizes 64 and 128; at 256 two waves would spill.
-template <int D, int FMT = kNvfp4>
+// at head sizes 64 and 128; at 256 two waves would spill. At head size 128
+// with bf16 output the kernel is held to three waves (168 registers); the
+// FP8-cache and 4-byte-copy variants then keep a few values in scratch, all
+// of them set before the step loop and read after it. FP8 output keeps two.
+template <int D, bool COMPACT, bool FP8OUT, int FMT>
 struct PrefillOcc {
-  static constexpr int waves = (D == 256) ? 1 : 2;
+  static constexpr int waves = (D == 256) ? 1 : (D == 128 && !FP8OUT) ? 3 : 2;
 };
 
+// Columns [wg_col, wg_col + 64 NT) of the chunk of sequence b (first query
+// row q0, qlen rows, L keys) for kv head h: the workgroup's four waves
+// share the dequantisation of each 32-key step and each runs its own 16 NT
+// columns' products (see the kernel below).
 template <int D, int NT, bool COMPACT, bool FP8OUT, int FMT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PrefillOcc<D, FMT>::waves))) void prefill_kernel(
-    PrefillArgs a) {
+__device__ __forceinline__ void prefill_columns(const PrefillArgs& a, uint8_t* ring, uint8_t* opbuf, int b, int h,
+                                                int q0, int qlen, int L, int wg_col) {
   using G = Geo<D>;
   using SG = StageGeo<D, COMPACT, FMT>;
   using OG = OpGeo<D>;
   constexpr int NS = PrefillStages<D, COMPACT, FMT>::NS;
-  extern __shared__ __align__(16) char smem[];
-  uint8_t* ring = reinterpret_cast<uint8_t*>(smem);  // [NS] raw steps
-  uint8_t* opbuf = ring + NS * SG::STAGE;             // [2] operand buffers
-
-  const int b = blockIdx.z, h = blockIdx.y, cb = blockIdx.x;
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  // Opaque per call: the lane offsets below are then derived again in each
+  // inlined call instead of being kept live from one call to the next.
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int i = lane & 15, j = lane >> 4;
-  int q0 = a.cu_q[b], q1 = a.cu_q[b + 1];
-  q0 = q0 < 0 ? 0 : (q0 > a.total_q ? a.total_q : q0);
-  q1 = q1 < q0 ? q0 : (q1 > a.total_q ? a.total_q : q1);
-  const int qlen = q1 - q0;
-  const int cap = a.max_blocks * a.pool.bs;
-  const int L = clamp_len(a.seq_lens[b], cap);
   const int grp = a.grp;
   const int ncols = qlen * grp;
-  const int wg_col = cb * 4 * 16 * NT;
-  if (wg_col >= ncols) return;  // the whole workgroup
   const int col_base = wg_col + w * 16 * NT;
 
   WaveAttn<D, NT> W;
@@ -979,6 +977,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PrefillOcc<
   }
 }
 
+template <int D, int NT, bool COMPACT, bool FP8OUT, int FMT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PrefillOcc<D, COMPACT, FP8OUT, FMT>::waves))) void prefill_kernel(
+    PrefillArgs a) {
+  using SG = StageGeo<D, COMPACT, FMT>;
+  constexpr int NS = PrefillStages<D, COMPACT, FMT>::NS;
+  extern __shared__ __align__(16) char smem[];
+  uint8_t* ring = reinterpret_cast<uint8_t*>(smem);  // [NS] raw steps
+  uint8_t* opbuf = ring + NS * SG::STAGE;             // [2] operand buffers
+
+  const int b = blockIdx.z, h = blockIdx.y;
+  int q0 = a.cu_q[b], q1 = a.cu_q[b + 1];
+  q0 = q0 < 0 ? 0 : (q0 > a.total_q ? a.total_q : q0);
+  q1 = q1 < q0 ? q0 : (q1 > a.total_q ? a.total_q : q1);
+  const int qlen = q1 - q0;
+  const int L = clamp_len(a.seq_lens[b], a.max_blocks * a.pool.bs);
+  const int ncols = qlen * a.grp;
+  constexpr int kCols = 4 * 16 * NT;  // columns per workgroup
+  if ((int)blockIdx.x * kCols < ncols)
+    prefill_columns<D, NT, COMPACT, FP8OUT, FMT>(a, ring, opbuf, b, h, q0, qlen, L, blockIdx.x * kCols);
+  // The grid is sized from the host's max_q_len hint. If a chunk is longer,
+  // the grid's last column block takes the columns past the grid, 64 at a
+  // time (one 16-column tile per wave: this rarely taken path then needs
+  // fewer registers than the main one), so a wrong hint costs speed, never
+  // rows. The workgroup's waves take the branch and the loop together.
+  if (blockIdx.x == gridDim.x - 1)
+    for (int c0 = gridDim.x * kCols; c0 < ncols; c0 += 64)
+      prefill_columns<D, 1, COMPACT, FP8OUT, FMT>(a, ring, opbuf, b, h, q0, qlen, L, c0);
+}
+
 template <int D, bool COMPACT, int FMT>
 size_t prefill_lds_bytes() {
   return (size_t)PrefillStages<D, COMPACT, FMT>::NS * StageGeo<D, COMPACT, FMT>::STAGE + 2 * OpGeo<D>::BYTES;
@@ -995,10 +1022,11 @@ static void launch_prefill_fp8(const PrefillArgs& a, const dim3& grid, hipStream
 
 template <int D, int NT>
 static hipError_t launch_prefill_t(const PrefillArgs& a, int num_seqs, int max_q_len, int fmt, hipStream_t stream) {
-  const int64_t cols = (int64_t)max_q_len * a.grp;
+  // max_q_len only sizes the grid: workgroups loop over the column tiles of
+  // the actual chunk lengths, so any hint (even 0) gives every row
+  const int64_t cols = (int64_t)(max_q_len > 0 ? max_q_len : 1) * a.grp;
   const int64_t per_wg = 4 * 16 * NT;
   const int64_t gx = (cols + per_wg - 1) / per_wg;
-  if (gx == 0) return hipSuccess;
   const dim3 grid((unsigned)gx, (unsigned)a.pool.hkv, (unsigned)num_seqs);
   if (fmt == kFp8E4M3 || fmt == kFp8E5M2) {
     // FP8 rows are copied in 16-byte chunks whatever their stride
@@ -1030,7 +1058,7 @@ hipError_t launch_prefill(const Pool& pool, int head_size, const void* q, int64_
                           float sm_scale, int causal, const float* o_scale, void* out, int fmt,
                           hipStream_t stream) {
   (void)max_seq_len;
-  if (num_seqs == 0 || max_q_len <= 0 || total_q <= 0) return hipSuccess;
+  if (num_seqs == 0 || total_q <= 0) return hipSuccess;
   PrefillArgs a;
   a.pool = pool;
   a.q = static_cast<const uint16_t*>(q);

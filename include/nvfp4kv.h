@@ -284,8 +284,10 @@ nvfp4kv_status nvfp4_fp8_to_bf16(const void* in, int64_t n, const float* o_scale
  *
  * q: bf16 [total_q, num_q_heads, head_size] (element strides, multiples of
  *   8, last axis contiguous); cu_seqlens_q: int32 [num_seqs + 1];
- *   max_q_len: host upper bound of the q_b (sizes the grid); rows past
- *   total_q are neither read nor written. out: bf16 [total_q, num_q_heads,
+ *   max_q_len: host hint of the largest q_b, used only to size the grid
+ *   (workgroups loop over the column tiles of the actual q_b, so a wrong
+ *   value, even 0, costs speed, not correctness); rows past total_q are
+ *   neither read nor written. out: bf16 [total_q, num_q_heads,
  *   head_size] contiguous. The workspace arguments are reserved: pass NULL, 0.
  */
 nvfp4kv_status nvfp4_paged_attention_prefill(const nvfp4kv_cache* cache,

@@ -115,3 +115,21 @@ def assert_attn_close(got: torch.Tensor, ref: np.ndarray, what=""):
     assert np.all(err <= bound), (f"{what}: max|err|={err.max():.3e} worst at {worst}: got {g[worst]:.6f} "
                                   f"ref {ref[worst]:.6f} ({(err <= bound).mean() * 100:.3f}% in band)")
     return float(err.max())
+
+
+def fp8_out_bound(got, ref, os):
+    """Largest |got - ref| a correct FP8 output can show.
+
+    The kernel's fp32 result y satisfies |y - ref| <= 2e-3 + 1e-2 |ref| (the
+    attention tolerance), and its code is E4M3 RNE of y / os, so the decoded
+    value got differs from y by at most half the E4M3 step of y's binade
+    (os times 2^(e - 3) for |y / os| in [2^e, 2^(e+1)), e >= -6; 2^-9 below
+    2^-6). Rounding to nearest either stays in y's binade or carries into the
+    next one up, never down, so the step at got's binade is at least the
+    step at y's and the bound needs no knowledge of y:
+    |got - ref| <= step(got) / 2 + 2e-3 + 1e-2 |ref|.
+    """
+    a = np.abs(got) / os
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -6)))
+    step = 2.0 ** (e - 3) * os
+    return step / 2 + 2e-3 + 1e-2 * np.abs(ref)

@@ -145,3 +145,19 @@ def test_quant_activations_sizes_and_rejects():
                                        ctypes.c_void_p(16), null) != 0
     # m = 0 is a no-op that touches nothing
     assert lib.nvfp4_quant_activations(null, 64, 0, 64, null, 1, null, null, null) == 0
+
+
+def test_probe_library_exports_and_rejects():
+    """The benchmark's read-stream measurement library: its header's one
+    function is exported and bad arguments are refused before any launch."""
+    from bit_quantized_paged_amd import probe
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "nvfp4kv_probe.h")).read(), flags=re.S)
+    names = sorted(set(re.findall(r"^\s*[a-z_0-9]+\s*\*?\s*(nvfp4[a-z_0-9]*)\s*\(", text, flags=re.M)))
+    assert names == probe.EXPORTS
+    lib = probe.library()
+    f = lib.nvfp4kv_probe_read_stream
+    assert f(None, 1024, 4, 64, 64, None) == 1          # NULL data
+    assert f(16, 1000, 4, 64, 64, None) == 1            # bytes not a multiple of 16
+    assert f(16, 1024, 0, 64, 64, None) == 1            # no workgroups
+    assert f(8, 1024, 4, 64, 64, None) == 1             # misaligned data
+    assert f(16, 1024, 8, 64, 64, None) == 1            # sink smaller than grid * 16 bytes

@@ -3,18 +3,18 @@ decode, long-context decode, chunked prefill, mixed serving batch), in the
 launch configuration the benchmark times: an HND pool filled with the cached
 prefix, then one append of the new tokens, decode over the 1-token sequences
 and chunked prefill over the rest, with the same batch splits and length
-hints. The oracle computes a sample of the outputs one by one:
+hints. The oracle quantises every token of the workload itself and then
+checks:
 
-- packed rows: every token of the sampled sequences plus a random sample of
-  all tokens, bit-exact against the oracle's own quantisation;
-- decode: every head of the sampled sequences (the longest, the shortest and
-  random ones);
-- prefill: single query rows of the sampled sequences (first, last and random
-  positions), each as a one-query sequence over its causal prefix (the key
-  limit L - q_len + i of bottom-right alignment);
+- the whole pool, bit-exact;
+- the whole decode output (every head of every decode sequence);
+- prefill: the whole output of the mixed batch's prefill half; for the
+  2048-token chunks, 64-row runs of every sequence at the chunk's start, at
+  its end and across a workgroup tile boundary in its middle (each run is
+  the last 64 queries of a sequence cut after the run's last token, which
+  is what bottom-right causal alignment makes it);
 - the paged dequantize of the decode batch and the page-form dequantize of
-  its pages, as the benchmark runs them: the sampled sequences' rows and
-  pages, bit-exact.
+  its pages, as the benchmark runs them, on sampled sequences, bit-exact.
 """
 import math
 
@@ -86,7 +86,8 @@ def dequant_like_bench(w, pool, dec_idx, dev):
 
 
 def sample_seqs(idx, lens, rng, n_random):
-    """The longest, the shortest and n_random other sequences of idx."""
+    """The longest, the shortest and n_random other sequences of idx (with
+    equal lengths: n_random + 1 distinct sequences)."""
     if len(idx) == 0:
         return []
     pick = {int(idx[np.argmax(lens[idx])]), int(idx[np.argmin(lens[idx])])}
@@ -96,42 +97,62 @@ def sample_seqs(idx, lens, rng, n_random):
     return sorted(pick)
 
 
+def prefill_runs(L, nq, run=64, tile_tokens=32):
+    """Query-row runs [a, a + n) of a chunk of nq queries: its start, its end,
+    and one across the workgroup tile boundary nearest its middle (a tile is
+    tile_tokens chunk tokens); the whole chunk when it is short."""
+    if nq <= 3 * run:
+        return [(0, nq)]
+    mid = (nq // 2) // tile_tokens * tile_tokens
+    starts = sorted({0, mid - run // 2, nq - run})
+    return [(a, run) for a in starts]
+
+
+def oracle_rows(ref_pool, w, b, a, n, sm, kv="nvfp4", ks=None, vs=None):
+    """The oracle's causal attention for query rows a .. a + n - 1 of
+    sequence b's chunk: the last n queries of the sequence cut after key
+    L - q_len + a + n - 1."""
+    L, nq = int(w.seq_lens[b]), int(w.q_lens[b])
+    q0 = int(w.cu_q[b]) + a
+    ks = w.k_scale if ks is None else ks
+    vs = w.v_scale if vs is None else vs
+    return O.paged_attention(ref_pool, w.query[q0:q0 + n], np.array([0, n], np.int32), w.block_table[b:b + 1],
+                             np.array([L - nq + a + n], np.int32), ks, vs, sm, w.head_size, kv_dtype=kv)
+
+
+def pool_bytes(pool):
+    """The pool's bytes in logical (num_blocks, 2, block_size, Hkv, row) order."""
+    return pool.contiguous().view(torch.uint8).cpu().numpy()
+
+
 @pytest.mark.parametrize("name", sorted(FULL))
-def test_full_size_sampled_parity(name):
+def test_full_size_parity(name):
     cfg = FULL[name]
     w = make_config(cfg)
     dev = torch.device("cuda")
     print(f"full-size parity: {name} ({w.num_seqs} seqs, {int(w.seq_lens.sum())} tokens)", flush=True)
     pool, dec_idx, outd, pre_idx, wp, outp = run_like_bench(w, dev)
     rng = np.random.default_rng(100 + cfg)
-    sd = sample_seqs(dec_idx, w.seq_lens, rng, 2)
-    sp = sample_seqs(pre_idx, w.seq_lens, rng, 1)
-    assert sd or sp
 
-    # ---- packed rows of the sampled sequences' tokens and of a random token sample
-    off = w.token_offsets
-    toks = [np.arange(off[b], off[b + 1]) for b in sd + sp]
-    toks.append(rng.choice(int(off[-1]), size=4096, replace=False))
-    toks = np.unique(np.concatenate(toks))
+    # ---- every packed row: the oracle quantises the whole workload
     ref_pool = np.zeros(O.pool_shape(w.num_blocks, w.block_size, w.num_kv_heads, w.head_size), np.uint8)
-    O.append(ref_pool, w.key[toks], w.value[toks], w.slot_mapping[toks], w.k_scale, w.v_scale)
-    slots = w.slot_mapping[toks]
-    blk, row = slots // w.block_size, slots % w.block_size
-    got_rows = pool[torch.from_numpy(blk).to(dev), :, torch.from_numpy(row).to(dev)].cpu().numpy()
-    ref_rows = ref_pool[blk, :, row]
-    bad = np.nonzero(np.any(got_rows != ref_rows, axis=(1, 2, 3)))[0]
-    assert bad.size == 0, f"{name}: {bad.size} of {toks.size} sampled tokens differ (first token {toks[bad[0]]})"
+    O.append(ref_pool, w.key, w.value, w.slot_mapping, w.k_scale, w.v_scale)
+    got_pool = pool_bytes(pool)
+    bad = np.argwhere(got_pool != ref_pool)
+    assert bad.size == 0, f"{name}: {len(bad)} pool bytes differ, first at {bad[:3].tolist()}"
+    del got_pool
 
     sm = np.float32(1.0 / math.sqrt(w.head_size))
-    # ---- decode: every head of each sampled sequence
-    for b in sd:
-        k = int(np.nonzero(dec_idx == b)[0][0])
-        q0 = int(w.cu_q[b])
-        ref = O.paged_attention(ref_pool, w.query[q0:q0 + 1], np.array([0, 1], np.int32), w.block_table[b:b + 1],
-                                w.seq_lens[b:b + 1], w.k_scale, w.v_scale, sm, w.head_size)
-        assert_attn_close(outd[k:k + 1], ref, f"{name} decode seq {b} (len {int(w.seq_lens[b])})")
+    # ---- decode: the whole output
+    if len(dec_idx):
+        wd = w.subset(dec_idx)
+        ref = O.paged_attention(ref_pool, wd.query, wd.cu_q, wd.block_table, wd.seq_lens, w.k_scale, w.v_scale, sm,
+                                w.head_size)
+        err = assert_attn_close(outd, ref, f"{name} decode ({wd.num_seqs} sequences)")
+        print(f"  decode: {ref.size} outputs, max |err| {err:.2e}", flush=True)
 
     # ---- paged and page-form dequantize of the decode batch
+    sd = sample_seqs(dec_idx, w.seq_lens, rng, 3)
     if sd:
         cu, ok, ov, pages = dequant_like_bench(w, pool, dec_idx, dev)
         bs = w.block_size
@@ -149,27 +170,32 @@ def test_full_size_sampled_parity(name):
             assert np.array_equal(g, want_pages), f"{name} page-form dequant of seq {b}'s pages differs"
         del ok, ov, pages
 
-    # ---- prefill: single query rows over their causal prefix
-    for b in sp:
-        k = int(np.nonzero(pre_idx == b)[0][0])
-        L, nq = int(w.seq_lens[b]), int(w.q_lens[b])
-        rows = {0, nq - 1} | {int(i) for i in rng.integers(0, nq, size=2)}
-        for i in sorted(rows):
-            p = L - nq + i  # absolute position of query row i: it sees keys 0..p
-            qi = int(w.cu_q[b]) + i
-            ref = O.paged_attention(ref_pool, w.query[qi:qi + 1], np.array([0, 1], np.int32), w.block_table[b:b + 1],
-                                    np.array([p + 1], np.int32), w.k_scale, w.v_scale, sm, w.head_size)
-            r = int(wp.cu_q[k]) + i
-            assert_attn_close(outp[r:r + 1], ref, f"{name} prefill seq {b} row {i} of {nq} (keys 0..{p})")
+    # ---- prefill: short chunks whole, long chunks by runs at both ends and across a tile boundary
+    if len(pre_idx):
+        if np.all(wp.q_lens <= 192):
+            ref = O.paged_attention(ref_pool, wp.query, wp.cu_q, wp.block_table, wp.seq_lens, w.k_scale, w.v_scale,
+                                    sm, w.head_size)
+            err = assert_attn_close(outp, ref, f"{name} prefill ({wp.num_seqs} sequences)")
+            print(f"  prefill: {ref.size} outputs, max |err| {err:.2e}", flush=True)
+        else:
+            rows = 0
+            for k in range(wp.num_seqs):
+                L, nq = int(wp.seq_lens[k]), int(wp.q_lens[k])
+                for a, n in prefill_runs(L, nq):
+                    ref = oracle_rows(ref_pool, wp, k, a, n, sm)
+                    r0 = int(wp.cu_q[k]) + a
+                    assert_attn_close(outp[r0:r0 + n], ref, f"{name} prefill seq {k} rows {a}..{a + n - 1} of {nq}")
+                    rows += n
+            print(f"  prefill: {rows} rows of {int(wp.cu_q[-1])}", flush=True)
 
 
 @pytest.mark.parametrize("name,kv", [("long_decode", "fp8_e4m3"), ("mixed_serving", "fp8_e4m3"),
                                      ("mixed_serving", "fp8_e5m2")])
-def test_full_size_fp8_decode_sampled(name, kv):
+def test_full_size_fp8_decode(name, kv):
     """FP8 caches at full size through the split decode kernel (D = 128 and
     D = 256): the whole batch appended into an FP8 pool, the decode
-    sequences decoded in one call, sampled sequences against the oracle on
-    its own FP8 pool of their tokens."""
+    sequences decoded in one call, the whole output against the oracle on
+    its own FP8 pool of the same tokens."""
     cfg = FULL[name]
     w = make_config(cfg)
     dev = torch.device("cuda")
@@ -177,9 +203,9 @@ def test_full_size_fp8_decode_sampled(name, kv):
     ksc, vsc = fp8_kv_scales(w, kv)
     ks, vs = scale_dev(ksc, dev), scale_dev(vsc, dev)
     pool = nvk.alloc_pool(w.num_blocks, w.block_size, w.num_kv_heads, w.head_size, "HND", dev, kv_dtype=kv)
-    nvk.append(pool, bf16_dev(w.key, dev), bf16_dev(w.value, dev), i64_dev(w.slot_mapping, dev), ks, vs)
     dec_idx = np.nonzero(w.q_lens == 1)[0]
     wd = w.subset(dec_idx)
+    nvk.append(pool, bf16_dev(wd.key, dev), bf16_dev(wd.value, dev), i64_dev(wd.slot_mapping, dev), ks, vs)
     Hq, Hkv, D = w.num_q_heads, w.num_kv_heads, w.head_size
     assert nvk.decode_plan(wd.num_seqs, Hkv, D, w.block_size, wd.block_table.shape[1], int(wd.seq_lens.max()),
                            kv) == nvk.DECODE_SPLIT_K
@@ -189,24 +215,18 @@ def test_full_size_fp8_decode_sampled(name, kv):
     nvk.paged_attention_decode(pool, bf16_dev(wd.query, dev), i32_dev(wd.block_table, dev), i32_dev(wd.seq_lens, dev),
                                int(wd.seq_lens.max()), ks, vs, float(sm), out, ws)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(200 + cfg)
-    sd = sample_seqs(dec_idx, w.seq_lens, rng, 2)
-    off = w.token_offsets
-    toks = np.concatenate([np.arange(off[b], off[b + 1]) for b in sd])
     ref_pool = np.zeros(O.pool_shape(w.num_blocks, w.block_size, Hkv, D, kv), np.uint8)
-    O.append(ref_pool, w.key[toks], w.value[toks], w.slot_mapping[toks], ksc, vsc, kv)
-    for b in sd:
-        k = int(np.nonzero(dec_idx == b)[0][0])
-        q0 = int(w.cu_q[b])
-        ref = O.paged_attention(ref_pool, w.query[q0:q0 + 1], np.array([0, 1], np.int32), w.block_table[b:b + 1],
-                                w.seq_lens[b:b + 1], ksc, vsc, sm, D, kv_dtype=kv)
-        assert_attn_close(out[k:k + 1], ref, f"{name} {kv} decode seq {b} (len {int(w.seq_lens[b])})")
+    O.append(ref_pool, wd.key, wd.value, wd.slot_mapping, ksc, vsc, kv)
+    assert np.array_equal(pool_bytes(pool), ref_pool), f"{name} {kv}: pool bytes differ"
+    ref = O.paged_attention(ref_pool, wd.query, wd.cu_q, wd.block_table, wd.seq_lens, ksc, vsc, sm, D, kv_dtype=kv)
+    assert_attn_close(out, ref, f"{name} {kv} decode ({wd.num_seqs} sequences)")
 
 
-def test_full_size_fp8_chunked_prefill_sampled():
+def test_full_size_fp8_chunked_prefill():
     """An E4M3 cache at the full chunked-prefill size: 8192 cached tokens per
     sequence appended, then the 2048-token chunks, and one causal prefill
-    call; single query rows of sampled sequences against the oracle."""
+    call; 64-row runs of every sequence (chunk start, end, a tile boundary)
+    against the oracle."""
     kv = "fp8_e4m3"
     w = make_config(FULL["chunked_prefill"])
     dev = torch.device("cuda")
@@ -224,17 +244,10 @@ def test_full_size_fp8_chunked_prefill_sampled():
                                 i32_dev(w.block_table, dev), i32_dev(w.seq_lens, dev), int(w.seq_lens.max()),
                                 ks, vs, float(sm), out)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(300)
-    sp = sample_seqs(np.arange(w.num_seqs), w.seq_lens, rng, 1)
-    off = w.token_offsets
-    toks = np.concatenate([np.arange(off[b], off[b + 1]) for b in sp])
     ref_pool = np.zeros(O.pool_shape(w.num_blocks, w.block_size, w.num_kv_heads, D, kv), np.uint8)
-    O.append(ref_pool, w.key[toks], w.value[toks], w.slot_mapping[toks], ksc, vsc, kv)
-    for b in sp:
-        L, nq = int(w.seq_lens[b]), int(w.q_lens[b])
-        for i in sorted({0, nq - 1} | {int(x) for x in rng.integers(0, nq, size=2)}):
-            p = L - nq + i
-            qi = int(w.cu_q[b]) + i
-            ref = O.paged_attention(ref_pool, w.query[qi:qi + 1], np.array([0, 1], np.int32), w.block_table[b:b + 1],
-                                    np.array([p + 1], np.int32), ksc, vsc, sm, D, kv_dtype=kv)
-            assert_attn_close(out[qi:qi + 1], ref, f"chunked_prefill {kv} seq {b} row {i} (keys 0..{p})")
+    O.append(ref_pool, w.key, w.value, w.slot_mapping, ksc, vsc, kv)
+    for b in range(w.num_seqs):
+        for a, n in prefill_runs(int(w.seq_lens[b]), int(w.q_lens[b])):
+            ref = oracle_rows(ref_pool, w, b, a, n, sm, kv, ksc, vsc)
+            r0 = int(w.cu_q[b]) + a
+            assert_attn_close(out[r0:r0 + n], ref, f"chunked_prefill {kv} seq {b} rows {a}..{a + n - 1}")

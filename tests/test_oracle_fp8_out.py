@@ -55,3 +55,30 @@ def test_fp8_roundtrip_error_is_within_half_a_step():
     a = np.abs(o)
     step = np.where(a < 2.0 ** -6, 2.0 ** -9, 2.0 ** (np.floor(np.log2(np.maximum(a, 2.0 ** -6))) - 3))
     assert np.all(np.abs(back - o) <= step / 2 + np.abs(o) * 2.0 ** -8 + 1e-12)
+
+
+def test_fp8_output_parity_bound_holds_and_has_no_slack():
+    """The bound the GPU tests put on FP8 attention outputs
+    (gpu_util.fp8_out_bound: half the E4M3 step at the decoded value's binade
+    plus the attention tolerance) against brute force on the oracle's own
+    encoder: for fp32 results y anywhere within the attention tolerance of a
+    reference, the decoded code stays inside it, including references just
+    below a power of two whose y rounds up into the next binade; and the
+    worst case reaches at least 97% of it, so the bound carries no padding."""
+    from gpu_util import fp8_out_bound
+    rng = np.random.default_rng(85)
+    for os in (1.0, 0.25, 0.03125):
+        edges = 2.0 ** np.arange(-12, 8)
+        ref = np.concatenate([edges * (1 - 1e-3), edges, edges * (1 + 1e-3), rng.uniform(-1, 1, 20000) *
+                              2.0 ** rng.integers(-12, 7, 20000)]) * os
+        ref = np.concatenate([ref, -ref])
+        ref = ref[np.abs(ref) < 400 * os]
+        tol = 2e-3 + 1e-2 * np.abs(ref)
+        worst = 0.0
+        for t in np.concatenate([np.linspace(-0.999, 0.999, 41), rng.uniform(-0.999, 0.999, 8)]):
+            y = (ref + t * tol).astype(np.float32)
+            got = O.e4m3_decode(O.fp8_out(y.astype(np.float64), os)) * os
+            ratio = np.abs(got - ref) / fp8_out_bound(got, ref, os)
+            assert np.all(ratio <= 1.0), (os, t, float(ratio.max()))
+            worst = max(worst, float(ratio.max()))
+        assert worst > 0.97, (os, worst)
