@@ -19,6 +19,7 @@ __all__ = [
     "NVFP4KVError", "library", "full_dim", "row_bytes", "KV_DTYPES", "kv_dtype_of", "alloc_pool", "append",
     "dequant_paged", "dequant_pages", "qdq", "decode_workspace_size", "decode_plan", "paged_attention_decode",
     "paged_attention_prefill", "fp8_to_bf16", "quant_activations", "quant_activations_scale_bytes",
+    "paged_attention_decode_noalloc",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -28,6 +29,7 @@ EXPORTS = [
     "nvfp4_kv_full_dim", "nvfp4_kv_append", "nvfp4_kv_dequant_paged", "nvfp4_kv_dequant_pages", "nvfp4_kv_qdq",
     "nvfp4_paged_attention_decode_workspace_size", "nvfp4_paged_attention_decode_plan",
     "nvfp4_paged_attention_decode", "nvfp4_paged_attention_decode_fp8", "nvfp4_fp8_to_bf16",
+    "nvfp4_paged_attention_decode_noalloc",
     "nvfp4_paged_attention_prefill_fp8",
     "nvfp4_paged_attention_prefill", "nvfp4_quant_activations", "nvfp4_quant_activations_scale_bytes",
     "nvfp4kv_status_string", "nvfp4kv_last_error",
@@ -74,6 +76,8 @@ def library():
             "nvfp4_paged_attention_decode_fp8": (_I32, [_DESC, _P, _I64, _I64, _I32, _P, _I32, _P, _I32, _I32, _P,
                                                         _P, _F32, _P, _P, _P, _SZ, _P]),
             "nvfp4_fp8_to_bf16": (_I32, [_P, _I64, _P, _P, _P]),
+            "nvfp4_paged_attention_decode_noalloc": (_I32, [_DESC, _P, _I64, _I64, _I32, _P, _I32, _P, _I32, _I32,
+                                                            _P, _P, _F32, _P, _P]),
             "nvfp4_paged_attention_prefill_fp8": (_I32, [_DESC, _P, _I64, _I64, _I32, _P, _I32, _I32, _P, _I32, _P,
                                                          _I32, _I32, _P, _P, _F32, _I32, _P, _P, _P, _SZ, _P]),
             "nvfp4_paged_attention_prefill": (_I32, [_DESC, _P, _I64, _I64, _I32, _P, _I32, _I32, _P, _I32, _P, _I32,
@@ -355,6 +359,22 @@ def paged_attention_decode(pool, q, block_table, seq_lens, max_seq_len, k_scale,
     else:
         _check(library().nvfp4_paged_attention_decode_fp8(*args, _ptr(o_scale), _ptr(out), _ptr(workspace),
                                                           workspace.numel(), _stream()))
+
+
+def paged_attention_decode_noalloc(pool, q, block_table, seq_lens, max_seq_len, k_scale, v_scale, sm_scale,
+                                   out) -> None:
+    """paged_attention_decode without a workspace: the split-K scratch is the
+    library's own fixed device array (32 MiB per GPU), so the call allocates
+    nothing. Calls that overlap on one GPU race on that array."""
+    d = _desc(pool)
+    B = _check_attention_args(d, q, out, block_table, seq_lens, None, k_scale, v_scale)
+    if q.shape[0] != B:
+        raise ValueError(f"q must have one row per sequence ({B}), got {q.shape[0]}")
+    _devices((pool, "pool"), (q, "q"), (out, "out"), (block_table, "block_table"), (seq_lens, "seq_lens"),
+             (k_scale, "k_scale"), (v_scale, "v_scale"))
+    _check(library().nvfp4_paged_attention_decode_noalloc(
+        ctypes.byref(d), _ptr(q), q.stride(0), q.stride(1), q.shape[1], _ptr(block_table), block_table.shape[1],
+        _ptr(seq_lens), B, int(max_seq_len), _ptr(k_scale), _ptr(v_scale), float(sm_scale), _ptr(out), _stream()))
 
 
 def fp8_to_bf16(codes, o_scale, out) -> None:

@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libnvfp4kv.so")
-SOURCES = ["append.hip", "dequant.hip", "codec.hip", "act_quant.hip", "attn.hip", "api.hip"]
+SOURCES = ["append.hip", "dequant.hip", "codec.hip", "act_quant.hip", "attn.hip", "noalloc.hip", "api.hip"]
 PROBE_LIB = os.path.join(HERE, "libnvfp4kv_probe.so")
 PROBE_SOURCES = ["probe.hip"]
 ARCH = "gfx950"

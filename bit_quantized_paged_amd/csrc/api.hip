@@ -208,15 +208,12 @@ int32_t nvfp4_paged_attention_decode_plan(int32_t num_seqs, int32_t num_kv_heads
   return nvfp4kv::decode_plan(num_seqs, num_kv_heads, head_size, block_size, max_blocks_per_seq, max_seq_len, fmt);
 }
 
-static nvfp4kv_status decode_impl(const nvfp4kv_cache* cache, const void* q, int64_t q_stride_token,
-                                            int64_t q_stride_head, int32_t num_q_heads,
-                                            const int32_t* block_table, int32_t max_blocks_per_seq,
-                                            const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
-                                            const float* k_scale, const float* v_scale, float sm_scale,
-                                            const float* o_scale, void* out, void* workspace,
-                                            size_t workspace_bytes, void* stream) {
-  nvfp4kv::Pool p;
-  int fmt = 0;
+// Checks shared by the decode entry points (everything but the workspace).
+static nvfp4kv_status decode_check(const nvfp4kv_cache* cache, const void* q, int64_t q_stride_token,
+                                   int64_t q_stride_head, int32_t num_q_heads, const int32_t* block_table,
+                                   int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs,
+                                   const float* k_scale, const float* v_scale, const void* out, nvfp4kv::Pool& p,
+                                   int& fmt) {
   nvfp4kv_status s = check_cache(cache, p, &fmt);
   if (s) return s;
   if (num_seqs < 0 || num_seqs > nvfp4kv::kDecodeMaxSeqs)
@@ -238,6 +235,20 @@ static nvfp4kv_status decode_impl(const nvfp4kv_cache* cache, const void* q, int
   if (out == nullptr || !aligned(out, 16)) return fail(NVFP4KV_INVALID_ARGUMENT, "out must be a 16-byte aligned pointer");
   if (nvfp4kv::decode_lds_bytes(num_seqs, grp, cache->head_size, fmt) > 163840)
     return fail(NVFP4KV_UNSUPPORTED, "num_seqs / group size / head_size combination exceeds the LDS budget");
+  return ok();
+}
+
+static nvfp4kv_status decode_impl(const nvfp4kv_cache* cache, const void* q, int64_t q_stride_token,
+                                  int64_t q_stride_head, int32_t num_q_heads, const int32_t* block_table,
+                                  int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs,
+                                  int32_t max_seq_len, const float* k_scale, const float* v_scale, float sm_scale,
+                                  const float* o_scale, void* out, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  nvfp4kv::Pool p;
+  int fmt = 0;
+  nvfp4kv_status s = decode_check(cache, q, q_stride_token, q_stride_head, num_q_heads, block_table,
+                                  max_blocks_per_seq, seq_lens, num_seqs, k_scale, v_scale, out, p, fmt);
+  if (s || num_seqs == 0) return s;
   const size_t need = nvfp4kv::decode_workspace_bytes(num_seqs, num_q_heads, p.hkv, cache->head_size);
   if (workspace == nullptr || workspace_bytes < need)
     return fail(NVFP4KV_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
@@ -258,6 +269,36 @@ nvfp4kv_status nvfp4_paged_attention_decode(const nvfp4kv_cache* cache, const vo
   return decode_impl(cache, q, q_stride_token, q_stride_head, num_q_heads, block_table, max_blocks_per_seq, seq_lens,
                      num_seqs, max_seq_len, k_scale, v_scale, sm_scale, nullptr, out, workspace, workspace_bytes,
                      stream);
+}
+
+nvfp4kv_status nvfp4_paged_attention_decode_noalloc(const nvfp4kv_cache* cache, const void* q,
+                                                    int64_t q_stride_token, int64_t q_stride_head,
+                                                    int32_t num_q_heads, const int32_t* block_table,
+                                                    int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                                    int32_t num_seqs, int32_t max_seq_len, const float* k_scale,
+                                                    const float* v_scale, float sm_scale, void* out, void* stream) {
+  nvfp4kv::Pool p;
+  int fmt = 0;
+  nvfp4kv_status s = decode_check(cache, q, q_stride_token, q_stride_head, num_q_heads, block_table,
+                                  max_blocks_per_seq, seq_lens, num_seqs, k_scale, v_scale, out, p, fmt);
+  if (s || num_seqs == 0) return s;
+  if ((int64_t)num_seqs * p.hkv > nvfp4kv::kScratchCounters)
+    return fail(NVFP4KV_WORKSPACE_TOO_SMALL, "num_seqs * num_kv_heads = %lld exceeds the %lld split counters of the "
+                "library's decode scratch", (long long)num_seqs * p.hkv, (long long)nvfp4kv::kScratchCounters);
+  const int64_t need = nvfp4kv::kScratchCounterBytes +
+                       (int64_t)nvfp4kv::decode_partial_bytes(num_seqs, num_q_heads, p.hkv, cache->head_size);
+  if (need > nvfp4kv::kScratchBytes)
+    return fail(NVFP4KV_WORKSPACE_TOO_SMALL, "this batch needs %lld bytes of decode scratch; the library's array "
+                "holds %lld (use nvfp4_paged_attention_decode with a workspace)", (long long)need,
+                (long long)nvfp4kv::kScratchBytes);
+  void* scratch = nullptr;
+  hipError_t e = nvfp4kv::scratch_for_current_device(static_cast<hipStream_t>(stream), &scratch);
+  if (e != hipSuccess) return hip_status(e, "nvfp4_paged_attention_decode_noalloc scratch set-up");
+  return hip_status(nvfp4kv::launch_decode(p, cache->head_size, q, q_stride_token, q_stride_head, num_q_heads,
+                                           block_table, max_blocks_per_seq, seq_lens, num_seqs, max_seq_len,
+                                           k_scale, v_scale, sm_scale, nullptr, out, scratch, fmt,
+                                           static_cast<hipStream_t>(stream), nvfp4kv::kScratchCounterBytes),
+                    "nvfp4_paged_attention_decode_noalloc launch");
 }
 
 nvfp4kv_status nvfp4_paged_attention_decode_fp8(const nvfp4kv_cache* cache, const void* q, int64_t q_stride_token,

@@ -604,10 +604,14 @@ static int64_t counter_bytes(int num_kv_heads) {
   return (((int64_t)kDecodeMaxSeqs * num_kv_heads * 4 + 255) / 256) * 256;
 }
 
-size_t decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_size) {
+size_t decode_partial_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_size) {
   const int64_t grp = num_q_heads / num_kv_heads;
   const int64_t slots = kDecodeTargetMax + (int64_t)num_seqs * num_kv_heads;
-  return (size_t)(counter_bytes(num_kv_heads) + slots * grp * head_size * 4 + slots * grp * 2 * 4);
+  return (size_t)(slots * grp * head_size * 4 + slots * grp * 2 * 4);
+}
+
+size_t decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_size) {
+  return (size_t)counter_bytes(num_kv_heads) + decode_partial_bytes(num_seqs, num_q_heads, num_kv_heads, head_size);
 }
 
 template <int D, int MODE>
@@ -738,7 +742,7 @@ hipError_t launch_decode(const Pool& pool, int head_size, const void* q, int64_t
                          int num_q_heads, const int32_t* block_table, int32_t max_blocks,
                          const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len, const float* k_scale,
                          const float* v_scale, float sm_scale, const float* o_scale, void* out, void* workspace,
-                         int fmt, hipStream_t stream) {
+                         int fmt, hipStream_t stream, int64_t counter_region_bytes) {
   if (num_seqs == 0) return hipSuccess;
   DecodeArgs a;
   a.pool = pool;
@@ -759,7 +763,8 @@ hipError_t launch_decode(const Pool& pool, int head_size, const void* q, int64_t
   a.o_scale = o_scale;
   const int64_t slots = kDecodeTargetMax + (int64_t)num_seqs * pool.hkv;
   a.ws_cnt = static_cast<uint32_t*>(workspace);
-  a.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + counter_bytes(pool.hkv));
+  const int64_t cbytes = counter_region_bytes >= 0 ? counter_region_bytes : counter_bytes(pool.hkv);
+  a.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + cbytes);
   a.ws_ml = a.ws_o + slots * a.grp * head_size;
   switch (head_size) {
     case 64: return launch_decode_t<64>(a, max_seq_len, fmt, stream);

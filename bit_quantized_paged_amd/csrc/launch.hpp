@@ -39,13 +39,29 @@ hipError_t launch_qdq(int head_size, void* key, int64_t k_st, int64_t k_sh, void
 // Largest batch of one decode call.
 constexpr int kDecodeMaxSeqs = 4096;
 
+// Decode workspace: [arrival counters][partial outputs][partial (max, sum)].
+// The counter region takes counter_region_bytes (by default 4096 sequences'
+// worth for num_kv_heads, a place that depends only on num_kv_heads); the
+// partials need decode_partial_bytes after it.
 size_t decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_size);
+size_t decode_partial_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_size);
 
 hipError_t launch_decode(const Pool& pool, int head_size, const void* q, int64_t q_st, int64_t q_sh,
                          int num_q_heads, const int32_t* block_table, int32_t max_blocks,
                          const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len, const float* k_scale,
                          const float* v_scale, float sm_scale, const float* o_scale, void* out, void* workspace,
-                         int fmt, hipStream_t stream);
+                         int fmt, hipStream_t stream, int64_t counter_region_bytes = -1);
+
+// The library-owned decode scratch of nvfp4_paged_attention_decode_noalloc:
+// kScratchCounterBytes of arrival counters (one per (sequence, kv head),
+// index b * num_kv_heads + h < kScratchCounters), then the partials, in all
+// at most kScratchBytes. scratch_for_current_device returns its address on
+// the current device, set up on the first call there (counters cleared by a
+// kernel on `stream`).
+constexpr int64_t kScratchBytes = 32ll << 20;
+constexpr int64_t kScratchCounters = 65536;
+constexpr int64_t kScratchCounterBytes = kScratchCounters * 4;
+hipError_t scratch_for_current_device(hipStream_t stream, void** ptr);
 
 // FP8-E4M3 bytes -> bf16: bf16 RNE of fp32(e4m3 * o_scale); n a multiple of 8.
 hipError_t launch_fp8_to_bf16(const void* in, int64_t n, const float* o_scale, void* out, hipStream_t stream);

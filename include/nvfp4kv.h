@@ -246,6 +246,31 @@ nvfp4kv_status nvfp4_paged_attention_decode(const nvfp4kv_cache* cache,
                                             void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Decode attention that allocates nothing and takes no workspace, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc. Same inputs,
+ * kernels, output and contract as nvfp4_paged_attention_decode (bit-identical
+ * results), except that the split-K counters and partials live in a
+ * device-resident array the library owns: 32 MiB on each GPU it runs on,
+ * set up by the first call on that GPU (which also clears its counters with
+ * a kernel on `stream`) and held until the process ends. Counters occupy
+ * the first 256 KiB (one per (sequence, kv head): num_seqs * num_kv_heads
+ * must be <= 65536), partials the rest; a batch whose partials do not fit
+ * (about 2048 + num_seqs * num_kv_heads slots of num_q_heads / num_kv_heads
+ * * (head_size + 2) floats) returns NVFP4KV_WORKSPACE_TOO_SMALL and launches
+ * nothing. Every call on one GPU shares that GPU's array and leaves its
+ * counters at zero; calls that overlap on one GPU (other streams, other
+ * host threads) race on it and give wrong results.
+ */
+nvfp4kv_status nvfp4_paged_attention_decode_noalloc(const nvfp4kv_cache* cache,
+                                                    const void* q, int64_t q_stride_token, int64_t q_stride_head,
+                                                    int32_t num_q_heads,
+                                                    const int32_t* block_table, int32_t max_blocks_per_seq,
+                                                    const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
+                                                    const float* k_scale, const float* v_scale, float sm_scale,
+                                                    void* out, void* stream);
+
+/*
  * Decode attention with FP8-E4M3 output [P40177 "Implementation breakdown"
  * item 2: the NVFP4 attention kernel emits FP8 into a preallocated buffer
  * and the forward pass dequantises it to the model dtype; "Risks and
