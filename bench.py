@@ -273,14 +273,19 @@ def run_workload(args, name, full, dev):
 
     if wd is not None:
         # ---- read ceiling: a plain read-only stream of the decode's bytes
-        # over the same pool rotation (each copy's first bytes, contiguous)
+        # over the same pool rotation (each copy's first bytes, contiguous),
+        # the fastest of a few grid sizes (one to eight workgroups per CU)
         nb = min(res["decode_bytes"], pool_bytes) // 16 * 16
-        grid = 8 * torch.cuda.get_device_properties(dev).multi_processor_count
-        sink = torch.zeros(4 * grid, dtype=torch.int32, device=dev)
-        rs = T.per_call(lambda r: probe.read_stream(bases[r], nb, sink, grid), copies)
-        extra["read_stream_ceiling_gbs"] = round(nb / rs / 1e9, 1)
-        extra["read_stream_us"] = round(rs * 1e6, 2)
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        sink = torch.zeros(4 * 8 * cus, dtype=torch.int32, device=dev)
+        sweep = {}
+        for per_cu in (1, 2, 4, 8):
+            sweep[per_cu] = T.per_call(lambda r: probe.read_stream(bases[r], nb, sink, per_cu * cus), copies)
+        best = min(sweep, key=sweep.get)
+        extra["read_stream_ceiling_gbs"] = round(nb / sweep[best] / 1e9, 1)
+        extra["read_stream_us"] = round(sweep[best] * 1e6, 2)
         extra["read_stream_bytes"] = nb
+        extra["read_stream_sweep_us"] = {f"{k}_wg_per_cu": round(v * 1e6, 2) for k, v in sweep.items()}
         del sink
 
         # ---- paged dequantize of the decode batch (reported, not part of the step)
