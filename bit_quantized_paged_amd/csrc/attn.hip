@@ -187,36 +187,17 @@ __device__ __forceinline__ f4 ld_agent4(const float* base, uint32_t off) {
 }
 
 // Merge the n partial results of (b, h) (slots slot0, slot0 + hkv, ...) into
-// the bf16 output with log-sum-exp weights. s_w: LDS scratch of `cap` floats.
-// One wave per column finds the max and the per-split weights (lanes over
-// splits); then every thread owns 4 consecutive outputs and sums its splits
-// with 16-byte loads, several in flight.
+// the output with log-sum-exp weights. Every thread owns 4 consecutive
+// outputs of one column and merges the splits itself, kSplitBatch at a time
+// with an online maximum: the (max, sum) pairs and the partial outputs of a
+// batch are all requested before any is used, so a batch costs one round trip
+// to the agent-coherent level, not one per load.
+constexpr int kSplitBatch = 16;
+
 template <int D, int NW>
-__device__ void combine_splits(const DecodeArgs& a, int b, int h, int64_t slot0, int n, float* s_w, int cap) {
+__device__ void combine_splits(const DecodeArgs& a, int b, int h, int64_t slot0, int n) {
   const int hkv = a.pool.hkv;
   const int grp = a.grp;
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  const int nw = (cap - 32) / grp;  // splits whose weights fit in LDS
-  for (int col = w; col < grp; col += NW) {
-    float mloc = -__builtin_inff();
-    for (int s = lane; s < n; s += 64) mloc = __builtin_fmaxf(mloc, ld_agent(a.ws_ml + ((slot0 + (int64_t)s * hkv) * grp + col) * 2));
-    const float M = wave_max64(mloc);
-    float lloc = 0.0f;
-    for (int s = lane; s < n; s += 64) {
-      const float* ml = a.ws_ml + ((slot0 + (int64_t)s * hkv) * grp + col) * 2;
-      const float m0 = ld_agent(ml);
-      const float f = (m0 == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(m0 - M) * ld_agent(ml + 1);
-      lloc += f;
-      if (s < nw) s_w[32 + col * nw + s] = f;
-    }
-    const float lt = wave_sum64(lloc);
-    if (lane == 0) {
-      s_w[2 * col] = M;
-      s_w[2 * col + 1] = lt > 0.0f ? 1.0f / lt : 0.0f;
-    }
-  }
-  __syncthreads();
   const float gv = *a.v_scale;
   const float os = a.o_scale ? *a.o_scale : 1.0f;
   const int64_t out0 = ((int64_t)b * a.hq + h * grp) * D;
@@ -224,29 +205,37 @@ __device__ void combine_splits(const DecodeArgs& a, int b, int h, int64_t slot0,
   for (int e = threadIdx.x; e < grp * D4; e += 64 * NW) {
     const int col = e / D4;
     const int d4 = e - col * D4;
-    const float M = s_w[2 * col];
     const uint32_t off = (uint32_t)((col * D + 4 * d4) * 4);
+    float M = -__builtin_inff(), lt = 0.0f;
     f4 o = {0.f, 0.f, 0.f, 0.f};
-    int s = 0;
-    for (; s + 4 <= n && s + 4 <= nw; s += 4) {
-      f4 v[4];
+    for (int s0 = 0; s0 < n; s0 += kSplitBatch) {
+      float m[kSplitBatch], l[kSplitBatch];
+      f4 v[kSplitBatch];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = ld_agent4(a.ws_o + (slot0 + (int64_t)(s + u) * hkv) * grp * D, off);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) o += s_w[32 + col * nw + s + u] * v[u];
-    }
-    for (; s < n; ++s) {
-      float f;
-      if (s < nw) {
-        f = s_w[32 + col * nw + s];
-      } else {
-        const float* ml = a.ws_ml + ((slot0 + (int64_t)s * hkv) * grp + col) * 2;
-        const float m0 = ld_agent(ml);
-        f = (m0 == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(m0 - M) * ld_agent(ml + 1);
+      for (int u = 0; u < kSplitBatch; ++u) {
+        const int s = s0 + u < n ? s0 + u : n - 1;  // clamped: past-the-end entries are dropped below
+        const int64_t slot = slot0 + (int64_t)s * hkv;
+        const float* ml = a.ws_ml + (slot * grp + col) * 2;
+        m[u] = ld_agent(ml);
+        l[u] = ld_agent(ml + 1);
+        v[u] = ld_agent4(a.ws_o + slot * grp * D, off);
       }
-      o += f * ld_agent4(a.ws_o + (slot0 + (int64_t)s * hkv) * grp * D, off);
+      float bm = M;
+#pragma unroll
+      for (int u = 0; u < kSplitBatch; ++u) bm = (s0 + u < n) ? __builtin_fmaxf(bm, m[u]) : bm;
+      // rescale what is merged so far to the batch's maximum, then add the batch
+      const float r = (M == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(M - bm);
+      lt *= r;
+      o *= r;
+#pragma unroll
+      for (int u = 0; u < kSplitBatch; ++u) {
+        const float f = (s0 + u < n && m[u] != -__builtin_inff()) ? __builtin_amdgcn_exp2f(m[u] - bm) * l[u] : 0.0f;
+        lt += f;
+        o += f * v[u];
+      }
+      M = bm;
     }
-    const float sc = s_w[2 * col + 1] * gv;
+    const float sc = (lt > 0.0f ? 1.0f / lt : 0.0f) * gv;
     const int64_t idx = out0 + col * D + 4 * d4;
     if (a.o_scale) {
       *reinterpret_cast<uint32_t*>(a.out8 + idx) =
@@ -512,7 +501,7 @@ decode_split_kernel(DecodeArgs a) {
                                            __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(nsplit - 1));
       __syncthreads();
       if (s_red[15]) {
-        combine_splits<D, NW>(a, b, h, (int64_t)s_pref[b] * hkv + h, nsplit, s_o, DecodeLds<D, MODE>::area / 4);
+        combine_splits<D, NW>(a, b, h, (int64_t)s_pref[b] * hkv + h, nsplit);
         if (threadIdx.x == 0)
           __hip_atomic_store(&a.ws_cnt[(int64_t)b * hkv + h], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
@@ -854,15 +843,27 @@ struct PrefillStages {
   static constexpr int NS = (63 / NC + 1) < NS_MAX ? (63 / NC + 1) : NS_MAX;
 };
 
+// Waves per prefill workgroup (NW) and 16-column tiles per wave (NT): a
+// workgroup shares the dequantisation of each step among its NW waves and
+// owns NW * 16 * NT query columns. At head size 256 the accumulators of two
+// tiles would leave one wave per SIMD; eight waves of one tile each keep the
+// 128 columns per workgroup at two waves per SIMD.
+template <int D>
+struct PrefillGeo {
+  static constexpr int NW = (D == 256) ? 8 : 4;
+  static constexpr int NT = (D == 64) ? 4 : (D == 128) ? 2 : 1;
+  static constexpr int kCols = NW * 16 * NT;
+};
+
 // Waves per SIMD the prefill register budget is sized for: without the hint
 // the compiler spends the whole 256-register budget of two waves (or more)
-// at head sizes 64 and 128; at 256 two waves would spill. At head size 128
+// at head sizes 64 and 128. At head size 128
 // with bf16 output the kernel is held to three waves (168 registers); the
 // FP8-cache and 4-byte-copy variants then keep a few values in scratch, all
 // of them set before the step loop and read after it. FP8 output keeps two.
 template <int D, bool COMPACT, bool FP8OUT, int FMT>
 struct PrefillOcc {
-  static constexpr int waves = (D == 256) ? 1 : (D == 128 && !FP8OUT) ? 3 : 2;
+  static constexpr int waves = (D == 128 && !FP8OUT) ? 3 : 2;
 };
 
 // Columns [wg_col, wg_col + 64 NT) of the chunk of sequence b (first query
@@ -903,7 +904,8 @@ __device__ __forceinline__ void prefill_columns(const PrefillArgs& a, uint8_t* r
     W.lim[n] = valid ? lim : -1;
   }
   // keys the workgroup streams: up to the last visible key of its last column
-  const int wg_last = ((wg_col + 64 * NT < ncols) ? wg_col + 64 * NT : ncols) - 1;
+  constexpr int kWgCols = PrefillGeo<D>::NW * 16 * NT;
+  const int wg_last = ((wg_col + kWgCols < ncols) ? wg_col + kWgCols : ncols) - 1;
   int kmax = a.causal ? L - qlen + wg_last / grp + 1 : L;
   kmax = kmax > L ? L : (kmax < 0 ? 0 : kmax);
   const int steps = ceil_div(kmax, kStep);
@@ -949,7 +951,7 @@ __device__ __forceinline__ void prefill_columns(const PrefillArgs& a, uint8_t* r
     make_pairs(R[0], vp[0]);
     make_pairs(R[1], vp[1]);
     const uint32_t slot = op_lane + (uint32_t)((k & 1) * OG::BYTES);
-    make_ops<D, 0>(R, vp, w, slot);
+    make_ops<D, 0, PrefillGeo<D>::NW>(R, vp, w, slot);
     lds_barrier();          // every operand of step k is in place
     if (kb < kw) {
       h8 ka[2][G::KW], va[G::DPL];
@@ -983,7 +985,7 @@ __device__ __forceinline__ void prefill_columns(const PrefillArgs& a, uint8_t* r
 }
 
 template <int D, int NT, bool COMPACT, bool FP8OUT, int FMT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PrefillOcc<D, COMPACT, FP8OUT, FMT>::waves))) void prefill_kernel(
+__global__ __launch_bounds__(64 * PrefillGeo<D>::NW) __attribute__((amdgpu_waves_per_eu(PrefillOcc<D, COMPACT, FP8OUT, FMT>::waves))) void prefill_kernel(
     PrefillArgs a) {
   using SG = StageGeo<D, COMPACT, FMT>;
   constexpr int NS = PrefillStages<D, COMPACT, FMT>::NS;
@@ -998,16 +1000,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PrefillOcc<
   const int qlen = q1 - q0;
   const int L = clamp_len(a.seq_lens[b], a.max_blocks * a.pool.bs);
   const int ncols = qlen * a.grp;
-  constexpr int kCols = 4 * 16 * NT;  // columns per workgroup
+  constexpr int kCols = PrefillGeo<D>::NW * 16 * NT;  // columns per workgroup
   if ((int)blockIdx.x * kCols < ncols)
     prefill_columns<D, NT, COMPACT, FP8OUT, FMT>(a, ring, opbuf, b, h, q0, qlen, L, blockIdx.x * kCols);
   // The grid is sized from the host's max_q_len hint. If a chunk is longer,
-  // the grid's last column block takes the columns past the grid, 64 at a
-  // time (one 16-column tile per wave: this rarely taken path then needs
-  // fewer registers than the main one), so a wrong hint costs speed, never
+  // the grid's last column block takes the columns past the grid, one
+  // 16-column tile per wave at a time (this rarely taken path then needs no
+  // more registers than the main one), so a wrong hint costs speed, never
   // rows. The workgroup's waves take the branch and the loop together.
   if (blockIdx.x == gridDim.x - 1)
-    for (int c0 = gridDim.x * kCols; c0 < ncols; c0 += 64)
+    for (int c0 = gridDim.x * kCols; c0 < ncols; c0 += PrefillGeo<D>::NW * 16)
       prefill_columns<D, 1, COMPACT, FP8OUT, FMT>(a, ring, opbuf, b, h, q0, qlen, L, c0);
 }
 
@@ -1020,9 +1022,9 @@ template <int D, int NT, int FMT>
 static void launch_prefill_fp8(const PrefillArgs& a, const dim3& grid, hipStream_t stream) {
   const size_t lds = prefill_lds_bytes<D, false, FMT>();
   if (a.o_scale == nullptr)
-    prefill_kernel<D, NT, false, false, FMT><<<grid, 256, lds, stream>>>(a);
+    prefill_kernel<D, NT, false, false, FMT><<<grid, 64 * PrefillGeo<D>::NW, lds, stream>>>(a);
   else
-    prefill_kernel<D, NT, false, true, FMT><<<grid, 256, lds, stream>>>(a);
+    prefill_kernel<D, NT, false, true, FMT><<<grid, 64 * PrefillGeo<D>::NW, lds, stream>>>(a);
 }
 
 template <int D, int NT>
@@ -1030,7 +1032,7 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, int num_seqs, int max_q
   // max_q_len only sizes the grid: workgroups loop over the column tiles of
   // the actual chunk lengths, so any hint (even 0) gives every row
   const int64_t cols = (int64_t)(max_q_len > 0 ? max_q_len : 1) * a.grp;
-  const int64_t per_wg = 4 * 16 * NT;
+  const int64_t per_wg = PrefillGeo<D>::NW * 16 * NT;
   const int64_t gx = (cols + per_wg - 1) / per_wg;
   const dim3 grid((unsigned)gx, (unsigned)a.pool.hkv, (unsigned)num_seqs);
   if (fmt == kFp8E4M3 || fmt == kFp8E5M2) {
@@ -1046,13 +1048,13 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, int num_seqs, int max_q
                        a.pool.sh % 16 == 0 && (reinterpret_cast<uintptr_t>(a.pool.data) % 16) == 0;
   const bool fp8 = a.o_scale != nullptr;
   if (compact && !fp8)
-    prefill_kernel<D, NT, true, false, kNvfp4><<<grid, 256, prefill_lds_bytes<D, true, kNvfp4>(), stream>>>(a);
+    prefill_kernel<D, NT, true, false, kNvfp4><<<grid, 64 * PrefillGeo<D>::NW, prefill_lds_bytes<D, true, kNvfp4>(), stream>>>(a);
   else if (compact)
-    prefill_kernel<D, NT, true, true, kNvfp4><<<grid, 256, prefill_lds_bytes<D, true, kNvfp4>(), stream>>>(a);
+    prefill_kernel<D, NT, true, true, kNvfp4><<<grid, 64 * PrefillGeo<D>::NW, prefill_lds_bytes<D, true, kNvfp4>(), stream>>>(a);
   else if (!fp8)
-    prefill_kernel<D, NT, false, false, kNvfp4><<<grid, 256, prefill_lds_bytes<D, false, kNvfp4>(), stream>>>(a);
+    prefill_kernel<D, NT, false, false, kNvfp4><<<grid, 64 * PrefillGeo<D>::NW, prefill_lds_bytes<D, false, kNvfp4>(), stream>>>(a);
   else
-    prefill_kernel<D, NT, false, true, kNvfp4><<<grid, 256, prefill_lds_bytes<D, false, kNvfp4>(), stream>>>(a);
+    prefill_kernel<D, NT, false, true, kNvfp4><<<grid, 64 * PrefillGeo<D>::NW, prefill_lds_bytes<D, false, kNvfp4>(), stream>>>(a);
   return hipGetLastError();
 }
 
@@ -1084,9 +1086,9 @@ hipError_t launch_prefill(const Pool& pool, int head_size, const void* q, int64_
   a.out8 = static_cast<uint8_t*>(out);
   a.o_scale = o_scale;
   switch (head_size) {
-    case 64: return launch_prefill_t<64, 4>(a, num_seqs, max_q_len, fmt, stream);
-    case 128: return launch_prefill_t<128, 2>(a, num_seqs, max_q_len, fmt, stream);
-    case 256: return launch_prefill_t<256, 2>(a, num_seqs, max_q_len, fmt, stream);
+    case 64: return launch_prefill_t<64, PrefillGeo<64>::NT>(a, num_seqs, max_q_len, fmt, stream);
+    case 128: return launch_prefill_t<128, PrefillGeo<128>::NT>(a, num_seqs, max_q_len, fmt, stream);
+    case 256: return launch_prefill_t<256, PrefillGeo<256>::NT>(a, num_seqs, max_q_len, fmt, stream);
     default: return hipErrorInvalidValue;
   }
 }

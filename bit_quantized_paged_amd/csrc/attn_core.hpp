@@ -1011,14 +1011,15 @@ __device__ __forceinline__ h8 make_op(const SubRaw<D, FMT> (&R)[2], const VPairs
   }
 }
 
-// Build and store this wave's share of the step's operands (E = w, w + 4, ...)
-// at slot + E * 1024 (slot: this lane's place in the operand buffer).
-template <int D, int E, int FMT>
+// Build and store this wave's share of the step's operands (E = w, w + NW,
+// ... for NW waves) at slot + E * 1024 (slot: this lane's place in the
+// operand buffer).
+template <int D, int E, int NW, int FMT>
 __device__ __forceinline__ void make_ops(const SubRaw<D, FMT> (&R)[2], const VPairs<D, FMT> (&vp)[2], int w,
                                          uint32_t slot) {
   if constexpr (E < OpGeo<D>::NE) {
-    if ((E & 3) == w) lds_store_op(slot + E * 1024, make_op<D, E>(R, vp));
-    make_ops<D, E + 1>(R, vp, w, slot);
+    if (E % NW == w) lds_store_op(slot + E * 1024, make_op<D, E>(R, vp));
+    make_ops<D, E + 1, NW>(R, vp, w, slot);
   }
 }
 
