@@ -286,6 +286,21 @@ def run_workload(args, name, full, dev):
         extra["read_stream_us"] = round(sweep[best] * 1e6, 2)
         extra["read_stream_bytes"] = nb
         extra["read_stream_sweep_us"] = {f"{k}_wg_per_cu": round(v * 1e6, 2) for k, v in sweep.items()}
+        # ---- the same pages the decode reads, read as a plain gather through
+        # its block table (every K and V slab of every page, whole last pages)
+        gsweep = {}
+        for per_cu in (2, 4, 6, 8):
+            splits = max(1, per_cu * cus // (wd.num_seqs * Hkv))
+            gsink = torch.zeros(4 * wd.num_seqs * Hkv * splits, dtype=torch.int32, device=dev)
+            gsweep[per_cu] = T.per_call(lambda r: probe.read_pages(pools[r], btd, sld, gsink, splits), copies)
+            del gsink
+        gbest = min(gsweep, key=gsweep.get)
+        pages = int(np.sum((wd.seq_lens + bs - 1) // bs))
+        g_bytes = pages * Hkv * 2 * bs * fd
+        extra["page_gather_us"] = round(gsweep[gbest] * 1e6, 2)
+        extra["page_gather_gbs"] = round(g_bytes / gsweep[gbest] / 1e9, 1)
+        extra["page_gather_bytes"] = g_bytes
+        extra["page_gather_sweep_us"] = {f"{k}_wg_per_cu": round(v * 1e6, 2) for k, v in gsweep.items()}
         del sink
 
         # ---- paged dequantize of the decode batch (reported, not part of the step)
@@ -497,8 +512,13 @@ def main():
                 "traffic": read_traffic(res["decode_kernel"], res["name"]), "kernel": res["decode_kernel"],
                 "bytes_per_launch": res["decode_bytes"], "avg_launch_us": round(res["decode_s"] * 1e6, 3)}
         if "read_stream_ceiling_gbs" in extra:
+            # ceilings measured in the same run: a contiguous read of the
+            # decode's byte count, and a plain gather of the decode's own pages
+            # (time ratio: that gather's time over the decode's)
             roof["read_stream_ceiling_gbs"] = extra["read_stream_ceiling_gbs"]
             roof["frac_of_read_stream_ceiling"] = round(r["decode_gbs"] / extra["read_stream_ceiling_gbs"], 4)
+            roof["page_gather_us"] = extra["page_gather_us"]
+            roof["frac_of_page_gather_time"] = round(extra["page_gather_us"] / r["decode_us"], 4)
     elif "prefill_s" in res:
         out["value"] = r["prefill_tflops"]
         out["unit"] = "TFLOP/s"

@@ -68,6 +68,49 @@ __device__ __forceinline__ int block_excl_scan(int v, int* s_red, int& total) {
   return incl - v + off;
 }
 
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// The schedule of a batch of at most 64 sequences, built by wave 0 alone
+// (lane b holds sequence b) with wave-level scans; the other waves wait at
+// one barrier. Same result as the block-wide version below.
+__device__ void decode_schedule_small(const int32_t* __restrict__ seq_lens, int B, int cap, int hkv, int target,
+                                      int* s_pref, int* s_len, int& total_units) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const int L = lane < B ? clamp_len(seq_lens[lane], cap) : 0;
+    const int st = ceil_div(L, kStep);
+    const int total_steps = wave_sum_i(st);
+    const int64_t work = (int64_t)total_steps * hkv;
+    int t = (int)((work + target - 1) / target);
+    int tps = t < kDecodeMinTps ? kDecodeMinTps : t;
+    auto units = [&](int tt) { return lane < B ? max(1, ceil_div(st, tt)) : 0; };
+    int total = wave_sum_i(units(tps));
+    if ((int64_t)total * hkv > target && (int64_t)B * hkv <= target && total_steps > tps) {
+      int lo = tps, hi = total_steps;  // lo does not fit, hi fits
+      while (hi - lo > 1) {
+        const int mid = lo + (hi - lo) / 2;
+        if ((int64_t)wave_sum_i(units(mid)) * hkv <= target) hi = mid;
+        else lo = mid;
+      }
+      tps = hi;
+      total = wave_sum_i(units(tps));
+    }
+    const int n = units(tps);
+    const int incl = wave_incl_scan(n);
+    if (lane < B) {
+      s_len[lane] = L;
+      s_pref[lane] = incl - n;
+    }
+    if (lane == 0) s_pref[B] = total;
+  }
+  __syncthreads();
+  total_units = s_pref[B];
+}
+
 // s_pref[b] = first unit (per head) of sequence b, s_pref[B] = units per head.
 template <int NW>
 __device__ void decode_schedule(const int32_t* __restrict__ seq_lens, int B, int cap, int hkv, int target,
@@ -158,11 +201,14 @@ __device__ __forceinline__ uint32_t fp8_e4m3_out(float y, float os) {
   const float q = __fdiv_rn(y, os);
   return e4m3_from_f32_sat(__builtin_fabsf(q)) | ((__float_as_uint(q) >> 24) & 0x80u);
 }
-__device__ __forceinline__ void store_out(const DecodeArgs& a, float os, int64_t idx, float y) {
+// Output elements idx .. idx + 3 (idx a multiple of 4) with values y * g.
+__device__ __forceinline__ void store_out4(const DecodeArgs& a, float os, int64_t idx, f4 y, float g) {
   if (a.o_scale)
-    a.out8[idx] = (uint8_t)fp8_e4m3_out(y, os);
+    *reinterpret_cast<uint32_t*>(a.out8 + idx) = fp8_e4m3_out(y[0] * g, os) | (fp8_e4m3_out(y[1] * g, os) << 8) |
+                                                 (fp8_e4m3_out(y[2] * g, os) << 16) |
+                                                 (fp8_e4m3_out(y[3] * g, os) << 24);
   else
-    a.out[idx] = (uint16_t)(pack_bf16x2(y, 0.0f) & 0xFFFFu);
+    *reinterpret_cast<u32x2*>(a.out + idx) = u32x2{pack_bf16x2(y[0] * g, y[1] * g), pack_bf16x2(y[2] * g, y[3] * g)};
 }
 
 // LDS ints of the schedule: unit prefix [B + 1] and clamped lengths [B],
@@ -184,6 +230,12 @@ __device__ __forceinline__ float wave_sum64(float v) {
 __device__ __forceinline__ f4 ld_agent4(const float* base, uint32_t off) {
   const rsrc_t r = make_rsrc(reinterpret_cast<const uint8_t*>(base), 0x7FFFFFFF);
   return __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 16 /* sc1 */));
+}
+// The agent-coherent (sc1, written through to the device's coherence point)
+// store of 16 bytes at byte offset `off` from the wave-uniform base.
+__device__ __forceinline__ void st_agent4(float* base, uint32_t off, f4 v) {
+  const rsrc_t r = make_rsrc(reinterpret_cast<const uint8_t*>(base), 0x7FFFFFFF);
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, 16 /* sc1 */);
 }
 
 // Merge the n partial results of (b, h) (slots slot0, slot0 + hkv, ...) into
@@ -355,15 +407,20 @@ __device__ __forceinline__ void decode_stream(WaveAttn<D, 1, FMT>& W, uint8_t* r
   wait_vmcnt<0>();
 }
 
-// Merge the NWS waves' softmax states of a unit through LDS (s_ml: [NWS][16]
-// (max, sum); s_o: [NWS][kMergeCols][D], which may overlap the drained
-// rings), kMergeCols columns at a time. emit(col, d, on, M, lt) gets every
-// output element: on = o / lt (0 when lt == 0), with the column's merged max
-// M and sum lt.
+// Merge the NWS waves' softmax states of a unit through LDS (s_ml: [NWS + 1]
+// [16] (max, sum), the last row the merged (max, sum) of each column; s_o:
+// [NWS][kMergeCols][D], which may overlap the drained rings), kMergeCols
+// columns at a time: one thread per column turns the waves' maxima into
+// normalised weights (written over the maxima), then every thread merges 4
+// consecutive outputs of a column. emit(col, d, on, M, lt) gets outputs d ..
+// d + 3 of column col: on = o / lt (0 when lt == 0), with the column's merged
+// max M and sum lt.
 template <int D, int NWS, int FMT, typename Emit>
 __device__ __forceinline__ void merge_waves(const WaveAttn<D, 1, FMT>& W, float* s_ml, float* s_o, int grp, int w,
                                             int i, int j, Emit&& emit) {
   using G = Geo<D>;
+  constexpr int D4 = D / 4;
+  float* s_st = s_ml + NWS * 16 * 2;
   const float lsum = W.lsum(0);
   if (j == 0) {
     s_ml[(w * 16 + i) * 2] = W.m[0];
@@ -379,22 +436,35 @@ __device__ __forceinline__ void merge_waves(const WaveAttn<D, 1, FMT>& W, float*
         for (int r = 0; r < 4; ++r) dst[(4 * j + r) * G::DPL + t] = W.acc[0][t][r];
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < nc * D; e += 64 * NWS) {
-      const int cc = e / D;
-      const int col = c0 + cc;
-      const int d = e - cc * D;
+    if ((int)threadIdx.x < nc) {
+      const int col = c0 + threadIdx.x;
       float M = -__builtin_inff();
 #pragma unroll
       for (int ww = 0; ww < NWS; ++ww) M = __builtin_fmaxf(M, s_ml[(ww * 16 + col) * 2]);
-      float lt = 0.0f, o = 0.0f;
+      float f[NWS];
+      float lt = 0.0f;
 #pragma unroll
       for (int ww = 0; ww < NWS; ++ww) {
         const float mw = s_ml[(ww * 16 + col) * 2];
-        const float f = (mw == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
-        lt += f * s_ml[(ww * 16 + col) * 2 + 1];
-        o += f * s_o[(ww * kMergeCols + cc) * D + d];
+        f[ww] = (mw == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
+        lt += f[ww] * s_ml[(ww * 16 + col) * 2 + 1];
       }
-      emit(col, d, lt > 0.0f ? o / lt : 0.0f, M, lt);
+      const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+#pragma unroll
+      for (int ww = 0; ww < NWS; ++ww) s_ml[(ww * 16 + col) * 2] = f[ww] * inv;
+      s_st[col * 2] = M;
+      s_st[col * 2 + 1] = lt;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < nc * D4; e += 64 * NWS) {
+      const int cc = e / D4;
+      const int col = c0 + cc;
+      const int d = 4 * (e - cc * D4);
+      f4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ww = 0; ww < NWS; ++ww)
+        o += s_ml[(ww * 16 + col) * 2] * *reinterpret_cast<const f4*>(s_o + (ww * kMergeCols + cc) * D + d);
+      emit(col, d, o, s_st[col * 2], s_st[col * 2 + 1]);
     }
     __syncthreads();
   }
@@ -412,8 +482,8 @@ decode_split_kernel(DecodeArgs a) {
   int* s_pref = reinterpret_cast<int*>(smem);
   int* s_len = s_pref + ((a.B + 1 + 3) / 4) * 4;
   int* s_red = s_pref + decode_lds_pref_ints(a.B);
-  float* s_ml = reinterpret_cast<float*>(s_red + 16);  // [NW waves][16 cols][2]
-  uint8_t* rings = reinterpret_cast<uint8_t*>(s_ml + NW * 16 * 2);  // per-wave stream area
+  float* s_ml = reinterpret_cast<float*>(s_red + 16);  // [NW waves + merged][16 cols][2]
+  uint8_t* rings = reinterpret_cast<uint8_t*>(s_ml + (NW + 1) * 16 * 2);  // per-wave stream area
   float* s_o = reinterpret_cast<float*>(rings);         // [NW waves][kMergeCols][D], after the streams
 
   // The scales are read with vector loads issued first: their latency then
@@ -426,7 +496,10 @@ decode_split_kernel(DecodeArgs a) {
   const int hkv = a.pool.hkv;
   const int cap = a.max_blocks * a.pool.bs;
   int tps, total;
-  decode_schedule<NW>(a.seq_lens, a.B, cap, hkv, a.target, s_pref, s_len, s_red, tps, total);
+  if (a.B <= 64)
+    decode_schedule_small(a.seq_lens, a.B, cap, hkv, a.target, s_pref, s_len, total);
+  else
+    decode_schedule<NW>(a.seq_lens, a.B, cap, hkv, a.target, s_pref, s_len, s_red, tps, total);
   total = __builtin_amdgcn_readfirstlane(total);
   const float qk_factor = a.sm_scale * uniform_f32(ksc) * kLog2e;
   const float gv = uniform_f32(vsc);
@@ -476,12 +549,12 @@ decode_split_kernel(DecodeArgs a) {
     decode_stream<D, COMPACT, FMT, NS, NW>(W, ring, a.pool, bt_row, a.max_blocks, L, h, k0, st1, qrow, qk_factor, dof,
                                            ll, j);
     __syncthreads();  // every wave's ring is drained before the rings become the merge buffer
-    merge_waves<D, NW>(W, s_ml, s_o, grp, w, i, j, [&](int col, int d, float on, float M, float lt) {
+    merge_waves<D, NW>(W, s_ml, s_o, grp, w, i, j, [&](int col, int d, f4 on, float M, float lt) {
       if (nsplit == 1) {
-        store_out(a, os, ((int64_t)b * a.hq + h * grp + col) * D + d, on * gv);
+        store_out4(a, os, ((int64_t)b * a.hq + h * grp + col) * D + d, on, gv);
       } else {
         const int64_t slot = (int64_t)ubs * hkv + h;
-        st_agent(a.ws_o + (slot * grp + col) * D + d, on);
+        st_agent4(a.ws_o + slot * grp * D, (uint32_t)((col * D + d) * 4), on);
         if (d == 0) {
           st_agent(a.ws_ml + (slot * grp + col) * 2, M);
           st_agent(a.ws_ml + (slot * grp + col) * 2 + 1, lt);
@@ -537,7 +610,7 @@ struct PairLds {
   static constexpr int stream =
       NW * DecodeStages<D>::NS * StageGeo<D, MODE == kModeDmaCompact, mode_fmt(MODE)>::STAGE;
   static constexpr int merge = NW * kMergeCols * D * 4;
-  static constexpr int bytes = NW * 16 * 2 * 4 + (stream > merge ? stream : merge);
+  static constexpr int bytes = (NW + 1) * 16 * 2 * 4 + (stream > merge ? stream : merge);
   static_assert(bytes <= 160 * 1024, "one workgroup per CU");
 };
 
@@ -549,8 +622,8 @@ __global__ __launch_bounds__((64 * PairGeo<D, mode_fmt(MODE)>::NW)) void decode_
   using SG = StageGeo<D, COMPACT, FMT>;
   constexpr int NS = DecodeStages<D>::NS;
   extern __shared__ __align__(16) char smem[];
-  float* s_ml = reinterpret_cast<float*>(smem);                     // [NW waves][16 cols][2]
-  uint8_t* rings = reinterpret_cast<uint8_t*>(s_ml + NW * 16 * 2);  // per-wave stream area
+  float* s_ml = reinterpret_cast<float*>(smem);                     // [NW waves + merged][16 cols][2]
+  uint8_t* rings = reinterpret_cast<uint8_t*>(s_ml + (NW + 1) * 16 * 2);  // per-wave stream area
   float* s_o = reinterpret_cast<float*>(rings);                     // [NW][kMergeCols][D], after the streams
 
   const float ksc = __builtin_bit_cast(
@@ -580,8 +653,8 @@ __global__ __launch_bounds__((64 * PairGeo<D, mode_fmt(MODE)>::NW)) void decode_
   decode_stream<D, COMPACT, FMT, NS, NW>(W, ring, a.pool, a.bt + (int64_t)b * a.max_blocks, a.max_blocks, L, h, w, ceil_div(L, kStep),
                                     qrow, qk_factor, dof, ll, j);
   __syncthreads();  // every wave's ring is drained before the rings become the merge buffer
-  merge_waves<D, NW>(W, s_ml, s_o, grp, w, i, j, [&](int col, int d, float on, float, float) {
-    store_out(a, os, ((int64_t)b * a.hq + h * grp + col) * D + d, on * gv);
+  merge_waves<D, NW>(W, s_ml, s_o, grp, w, i, j, [&](int col, int d, f4 on, float, float) {
+    store_out4(a, os, ((int64_t)b * a.hq + h * grp + col) * D + d, on, gv);
   });
 }
 
@@ -605,7 +678,8 @@ size_t decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, i
 
 template <int D, int MODE>
 static size_t decode_lds_bytes_m(int num_seqs) {
-  return (size_t)(decode_lds_pref_ints(num_seqs) + 16) * 4 + SplitWaves<D>::NW * 16 * 2 * 4 + DecodeLds<D, MODE>::area;
+  return (size_t)(decode_lds_pref_ints(num_seqs) + 16) * 4 + (SplitWaves<D>::NW + 1) * 16 * 2 * 4 +
+         DecodeLds<D, MODE>::area;
 }
 
 template <int D>
@@ -787,7 +861,39 @@ struct PrefillArgs {
   uint16_t* out;         // bf16 output (when o_scale is null)
   uint8_t* out8;         // FP8-E4M3 output (when o_scale is set)
   const float* o_scale;  // per-tensor FP8 output scale, or null
+  int num_seqs;
+  int longest_first;     // blockIdx.z is a rank in order of decreasing length (num_seqs <= kPrefillRankMax)
 };
+
+// Batches of up to this many sequences are walked longest first: the grid's
+// sequence axis is a rank, so the longest sequences' workgroups are
+// dispatched first and the short ones fill in behind them (longest-
+// processing-time order), instead of a long sequence late in the batch
+// setting the end.
+constexpr int kPrefillRankMax = 256;
+
+// The sequence of rank r in order of decreasing key length (ties: lower
+// index first), ranked by the workgroup through s (kPrefillRankMax + 1 ints
+// of LDS that are free until the function returns).
+__device__ int prefill_seq_of_rank(const PrefillArgs& a, int r, int* s) {
+  const int B = a.num_seqs;
+  const int cap = a.max_blocks * a.pool.bs;
+  for (int t = threadIdx.x; t < B; t += blockDim.x) s[t] = clamp_len(a.seq_lens[t], cap);
+  __syncthreads();
+  for (int t = threadIdx.x; t < B; t += blockDim.x) {
+    const int kt = s[t];
+    int rank = 0;
+    for (int u = 0; u < B; ++u) {
+      const int ku = s[u];
+      rank += (ku > kt || (ku == kt && u < t)) ? 1 : 0;
+    }
+    if (rank == r) s[B] = t;
+  }
+  __syncthreads();
+  const int b = s[B];
+  __syncthreads();  // s is reused (the copies' ring) from here on
+  return b;
+}
 
 template <int D>
 __device__ __forceinline__ void store_column(uint16_t* orow, const f4 (&acc)[Geo<D>::DPL], float scale, int j) {
@@ -993,7 +1099,8 @@ __global__ __launch_bounds__(64 * PrefillGeo<D>::NW) __attribute__((amdgpu_waves
   uint8_t* ring = reinterpret_cast<uint8_t*>(smem);  // [NS] raw steps
   uint8_t* opbuf = ring + NS * SG::STAGE;             // [2] operand buffers
 
-  const int b = blockIdx.z, h = blockIdx.y;
+  const int h = blockIdx.y;
+  const int b = a.longest_first ? prefill_seq_of_rank(a, blockIdx.z, reinterpret_cast<int*>(ring)) : (int)blockIdx.z;
   int q0 = a.cu_q[b], q1 = a.cu_q[b + 1];
   q0 = q0 < 0 ? 0 : (q0 > a.total_q ? a.total_q : q0);
   q1 = q1 < q0 ? q0 : (q1 > a.total_q ? a.total_q : q1);
@@ -1085,6 +1192,8 @@ hipError_t launch_prefill(const Pool& pool, int head_size, const void* q, int64_
   a.out = static_cast<uint16_t*>(out);
   a.out8 = static_cast<uint8_t*>(out);
   a.o_scale = o_scale;
+  a.num_seqs = num_seqs;
+  a.longest_first = (num_seqs > 1 && num_seqs <= kPrefillRankMax) ? 1 : 0;
   switch (head_size) {
     case 64: return launch_prefill_t<64, PrefillGeo<64>::NT>(a, num_seqs, max_q_len, fmt, stream);
     case 128: return launch_prefill_t<128, PrefillGeo<128>::NT>(a, num_seqs, max_q_len, fmt, stream);

@@ -33,6 +33,65 @@ __global__ __launch_bounds__(256) void read_stream_kernel(const u32x4* __restric
   if ((threadIdx.x & 63) == 0) sink[blockIdx.x * 4 + (threadIdx.x >> 6)] = acc;
 }
 
+
+// The pages a decode batch reads, as a plain gather: workgroup u owns unit
+// (sequence b, kv head h, split) of `splits` equal page ranges per sequence;
+// its four waves take pages p0 + w, p0 + w + 4, ... and each reads a page's
+// K slab and V slab (slab_bytes contiguous bytes each: page rows are
+// contiguous), 16 bytes per lane and load, kPagesInFlight pages at a time.
+constexpr int kPagesInFlight = 4;
+
+__global__ __launch_bounds__(256) void read_pages_kernel(const uint8_t* __restrict__ pool, int64_t stride_block,
+                                                         int64_t stride_kv, int64_t stride_head,
+                                                         const int32_t* __restrict__ block_table, int max_blocks,
+                                                         const int32_t* __restrict__ seq_lens, int num_kv_heads,
+                                                         int splits, int block_size, int slab_bytes,
+                                                         int64_t num_blocks, uint32_t* __restrict__ sink) {
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int u = blockIdx.x;
+  const int split = u % splits;
+  const int h = (u / splits) % num_kv_heads;
+  const int b = u / (splits * num_kv_heads);
+  const int L = seq_lens[b] < 0 ? 0 : seq_lens[b];
+  int pages = (L + block_size - 1) / block_size;
+  pages = pages > max_blocks ? max_blocks : pages;
+  const int p0 = (int)((int64_t)pages * split / splits), p1 = (int)((int64_t)pages * (split + 1) / splits);
+  const int nc = slab_bytes / 16;
+  const int32_t* row = block_table + (int64_t)b * max_blocks;
+  uint32_t acc = 0;
+  for (int p = p0 + w; p < p1; p += 4 * kPagesInFlight) {
+    u32x4 v[kPagesInFlight][2][2];
+#pragma unroll
+    for (int k = 0; k < kPagesInFlight; ++k) {
+      const int pk = p + 4 * k;
+#pragma unroll
+      for (int kv = 0; kv < 2; ++kv) v[k][kv][0] = v[k][kv][1] = u32x4{0u, 0u, 0u, 0u};
+      if (pk < p1) {
+        int64_t id = row[pk];
+        id = id < 0 ? 0 : (id >= num_blocks ? num_blocks - 1 : id);
+#pragma unroll
+        for (int kv = 0; kv < 2; ++kv) {
+          const u32x4* src = reinterpret_cast<const u32x4*>(pool + id * stride_block + kv * stride_kv +
+                                                            (int64_t)h * stride_head);
+          if (lane < nc) v[k][kv][0] = src[lane];
+          if (lane + 64 < nc) v[k][kv][1] = src[lane + 64];
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kPagesInFlight; ++k)
+#pragma unroll
+      for (int kv = 0; kv < 2; ++kv) {
+        const u32x4 x = v[k][kv][0] ^ v[k][kv][1];
+        acc ^= x[0] ^ x[1] ^ x[2] ^ x[3];
+      }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, o);
+  if (lane == 0) sink[blockIdx.x * 4 + w] = acc;
+}
+
 }  // namespace
 
 extern "C" int32_t nvfp4kv_probe_read_stream(const void* data, int64_t bytes, int32_t grid, void* sink,
@@ -43,5 +102,23 @@ extern "C" int32_t nvfp4kv_probe_read_stream(const void* data, int64_t bytes, in
     return 1;
   read_stream_kernel<<<grid, 256, 0, static_cast<hipStream_t>(stream)>>>(static_cast<const u32x4*>(data), bytes / 16,
                                                                       static_cast<uint32_t*>(sink));
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+extern "C" int32_t nvfp4kv_probe_read_pages(const void* pool, int64_t num_blocks, int64_t stride_block,
+                                            int64_t stride_kv, int64_t stride_head, int32_t slab_bytes,
+                                            int32_t block_size, int32_t num_kv_heads, const int32_t* block_table,
+                                            int32_t max_blocks, const int32_t* seq_lens, int32_t num_seqs,
+                                            int32_t splits, void* sink, int64_t sink_bytes, void* stream) {
+  const int64_t grid = (int64_t)num_seqs * num_kv_heads * splits;
+  if (pool == nullptr || block_table == nullptr || seq_lens == nullptr || sink == nullptr || splits < 1 ||
+      num_blocks < 1 || max_blocks < 1 || num_seqs < 1 || block_size < 1 || num_kv_heads < 1 || slab_bytes < 16 ||
+      slab_bytes % 16 != 0 || slab_bytes > 2048 || (reinterpret_cast<uintptr_t>(pool) % 16) != 0 ||
+      stride_block % 16 != 0 || stride_kv % 16 != 0 || stride_head % 16 != 0 || grid > INT32_MAX ||
+      (reinterpret_cast<uintptr_t>(sink) % 4) != 0 || sink_bytes < grid * 16)
+    return 1;
+  read_pages_kernel<<<(unsigned)grid, 256, 0, static_cast<hipStream_t>(stream)>>>(
+      static_cast<const uint8_t*>(pool), stride_block, stride_kv, stride_head, block_table, max_blocks, seq_lens,
+      num_kv_heads, splits, block_size, slab_bytes, num_blocks, static_cast<uint32_t*>(sink));
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }

@@ -161,3 +161,12 @@ def test_probe_library_exports_and_rejects():
     assert f(16, 1024, 0, 64, 64, None) == 1            # no workgroups
     assert f(8, 1024, 4, 64, 64, None) == 1             # misaligned data
     assert f(16, 1024, 8, 64, 64, None) == 1            # sink smaller than grid * 16 bytes
+    g = lib.nvfp4kv_probe_read_pages
+    ok = dict(pool=64, nb=4, sb=2304, skv=1152, sh=1152 * 2, slab=1152, bs=16, hkv=1, bt=64, mb=2, sl=64, B=1,
+              splits=4, sink=64, sink_bytes=64)
+    call = lambda **k: g(*({**ok, **k}.values()), None)
+    assert call(pool=0) == 1                            # NULL pool
+    assert call(slab=1000) == 1                         # slab not a multiple of 16
+    assert call(slab=4096) == 1                         # slab above 2048 bytes
+    assert call(sb=2300) == 1                           # strides must be multiples of 16
+    assert call(splits=8) == 1                          # sink smaller than 16 bytes per workgroup

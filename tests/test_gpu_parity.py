@@ -637,3 +637,24 @@ def test_prefill_any_max_q_len_hint(hint):
     ref = O.paged_attention(oracle_pool(w), w.query, w.cu_q, w.block_table, w.seq_lens, w.k_scale, w.v_scale,
                             np.float32(d.sm_scale), 128)
     assert_attn_close(out, ref, f"prefill with max_q_len hint {mq}")
+
+
+@pytest.mark.parametrize("num_seqs", [300, 37])
+def test_prefill_batch_order(num_seqs):
+    """Batches of up to 256 sequences are walked longest first (the grid's
+    sequence axis is a rank the workgroups compute from the lengths, ties
+    in index order); larger ones in index order. Both against the oracle,
+    with repeated lengths among ragged ones."""
+    rng = np.random.default_rng(25 + num_seqs)
+    lens = rng.integers(1, 200, size=num_seqs).astype(np.int32)
+    lens[::7] = 150  # ties
+    q = np.minimum(lens, rng.integers(1, 24, size=num_seqs)).astype(np.int32)
+    w = make_workload(seed=26, name="x", rng=rng, seq_lens=lens, q_lens=q, num_q_heads=8, num_kv_heads=2,
+                      head_size=128, block_size=16)
+    d = Dev(w, "HND")
+    d.append_all()
+    out = d.prefill()
+    torch.cuda.synchronize()
+    ref = O.paged_attention(oracle_pool(w), w.query, w.cu_q, w.block_table, w.seq_lens, w.k_scale, w.v_scale,
+                            np.float32(d.sm_scale), 128)
+    assert_attn_close(out, ref, f"prefill of {num_seqs} sequences")
