@@ -331,10 +331,14 @@ struct SplitStages {
   static constexpr int NS = (D == 256 && mode_fmt(MODE) != kNvfp4) ? 1 : DecodeStages<D>::NS;
 };
 
-// Waves per split-kernel workgroup.
+// Waves per split-kernel workgroup. At head sizes up to 128 one 8-wave
+// workgroup per CU (two waves per SIMD, the CU's units four times longer)
+// streams faster than three 4-wave workgroups (three waves per SIMD): at the
+// long-context batch 62 us against 66, with 4 splits per (sequence, kv head)
+// to combine instead of 12. At 256 two 4-wave workgroups per CU.
 template <int D>
 struct SplitWaves {
-  static constexpr int NW = 4;
+  static constexpr int NW = (D == 256) ? 4 : 8;
 };
 
 template <int D, int MODE>
