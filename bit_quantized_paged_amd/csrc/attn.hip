@@ -1,6 +1,10 @@
 // Paged attention over the NVFP4 cache: split-K decode (the split merge is
 // done by the last-arriving workgroup of each sequence) and chunked prefill [P40177 "Implementation breakdown" 1 and 3; RFC47684
 // "Cause analysis": the paged read path].
+#include <atomic>
+#include <map>
+#include <mutex>
+
 #include "attn_core.hpp"
 #include "launch.hpp"
 
@@ -704,37 +708,52 @@ size_t decode_lds_bytes(int num_seqs, int grp, int head_size, int fmt) {
   }
 }
 
-// Workgroups of a decode kernel variant that the device holds at once
-// (cached per device and variant; an occupancy query, not a device sync).
+// Workgroups of a decode kernel variant that the device holds at once (an
+// occupancy query, not a device sync), cached per device, variant and LDS
+// size: the split kernel's LDS grows with the batch, so a few sizes recur.
+// Host threads may call concurrently; the cache is guarded by a mutex.
+constexpr int kMaxDevices = 64;
+
+struct OccupancyCache {
+  std::mutex mu;
+  std::map<size_t, int> by_lds[kMaxDevices];
+};
+
+static int current_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
+  return dev;
+}
+
+static int device_cus() {
+  static std::atomic<int> cached[kMaxDevices];
+  const int dev = current_device();
+  int cus = cached[dev].load(std::memory_order_relaxed);
+  if (cus > 0) return cus;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+  cached[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
 template <int D, int MODE>
 static int resident_workgroups(size_t lds) {
-  static int cached[64] = {0};
-  static size_t cached_lds[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (cached[dev] > 0 && cached_lds[dev] == lds) return cached[dev];
-  int per_cu = 0, cus = 0;
+  static OccupancyCache cache;
+  const int dev = current_device();
+  {
+    std::lock_guard<std::mutex> lock(cache.mu);
+    const auto it = cache.by_lds[dev].find(lds);
+    if (it != cache.by_lds[dev].end()) return it->second;
+  }
+  int per_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<D, MODE>, 64 * SplitWaves<D>::NW,
                                                    lds) != hipSuccess ||
       per_cu < 1)
     per_cu = 1;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
-  int n = per_cu * cus;
+  int n = per_cu * device_cus();
   n = n > kDecodeTargetMax ? kDecodeTargetMax : n;
-  cached[dev] = n;
-  cached_lds[dev] = lds;
+  std::lock_guard<std::mutex> lock(cache.mu);
+  cache.by_lds[dev][lds] = n;
   return n;
-}
-
-static int device_cus() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (cached[dev] > 0) return cached[dev];
-  int cus = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
-  cached[dev] = cus;
-  return cus;
 }
 
 // 32-key steps of the longest sequence, as far as the host knows it.

@@ -40,6 +40,7 @@ __global__ __launch_bounds__(256) void read_stream_kernel(const u32x4* __restric
 // K slab and V slab (slab_bytes contiguous bytes each: page rows are
 // contiguous), 16 bytes per lane and load, kPagesInFlight pages at a time.
 constexpr int kPagesInFlight = 4;
+constexpr int kChunksPerLane = 4;  // slabs of up to 4 KB
 
 __global__ __launch_bounds__(256) void read_pages_kernel(const uint8_t* __restrict__ pool, int64_t stride_block,
                                                          int64_t stride_kv, int64_t stride_head,
@@ -61,12 +62,14 @@ __global__ __launch_bounds__(256) void read_pages_kernel(const uint8_t* __restri
   const int32_t* row = block_table + (int64_t)b * max_blocks;
   uint32_t acc = 0;
   for (int p = p0 + w; p < p1; p += 4 * kPagesInFlight) {
-    u32x4 v[kPagesInFlight][2][2];
+    u32x4 v[kPagesInFlight][2][kChunksPerLane];
 #pragma unroll
     for (int k = 0; k < kPagesInFlight; ++k) {
       const int pk = p + 4 * k;
 #pragma unroll
-      for (int kv = 0; kv < 2; ++kv) v[k][kv][0] = v[k][kv][1] = u32x4{0u, 0u, 0u, 0u};
+      for (int kv = 0; kv < 2; ++kv)
+#pragma unroll
+        for (int c = 0; c < kChunksPerLane; ++c) v[k][kv][c] = u32x4{0u, 0u, 0u, 0u};
       if (pk < p1) {
         int64_t id = row[pk];
         id = id < 0 ? 0 : (id >= num_blocks ? num_blocks - 1 : id);
@@ -74,18 +77,21 @@ __global__ __launch_bounds__(256) void read_pages_kernel(const uint8_t* __restri
         for (int kv = 0; kv < 2; ++kv) {
           const u32x4* src = reinterpret_cast<const u32x4*>(pool + id * stride_block + kv * stride_kv +
                                                             (int64_t)h * stride_head);
-          if (lane < nc) v[k][kv][0] = src[lane];
-          if (lane + 64 < nc) v[k][kv][1] = src[lane + 64];
+#pragma unroll
+          for (int c = 0; c < kChunksPerLane; ++c)
+            if (lane + 64 * c < nc) v[k][kv][c] = src[lane + 64 * c];
         }
       }
     }
 #pragma unroll
     for (int k = 0; k < kPagesInFlight; ++k)
 #pragma unroll
-      for (int kv = 0; kv < 2; ++kv) {
-        const u32x4 x = v[k][kv][0] ^ v[k][kv][1];
-        acc ^= x[0] ^ x[1] ^ x[2] ^ x[3];
-      }
+      for (int kv = 0; kv < 2; ++kv)
+#pragma unroll
+        for (int c = 0; c < kChunksPerLane; ++c) {
+          const u32x4 x = v[k][kv][c];
+          acc ^= x[0] ^ x[1] ^ x[2] ^ x[3];
+        }
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, o);
@@ -113,7 +119,7 @@ extern "C" int32_t nvfp4kv_probe_read_pages(const void* pool, int64_t num_blocks
   const int64_t grid = (int64_t)num_seqs * num_kv_heads * splits;
   if (pool == nullptr || block_table == nullptr || seq_lens == nullptr || sink == nullptr || splits < 1 ||
       num_blocks < 1 || max_blocks < 1 || num_seqs < 1 || block_size < 1 || num_kv_heads < 1 || slab_bytes < 16 ||
-      slab_bytes % 16 != 0 || slab_bytes > 2048 || (reinterpret_cast<uintptr_t>(pool) % 16) != 0 ||
+      slab_bytes % 16 != 0 || slab_bytes > 64 * 16 * kChunksPerLane || (reinterpret_cast<uintptr_t>(pool) % 16) != 0 ||
       stride_block % 16 != 0 || stride_kv % 16 != 0 || stride_head % 16 != 0 || grid > INT32_MAX ||
       (reinterpret_cast<uintptr_t>(sink) % 4) != 0 || sink_bytes < grid * 16)
     return 1;

@@ -31,7 +31,7 @@ int32_t nvfp4kv_probe_read_stream(const void* data, int64_t bytes, int32_t grid,
  * the page's K slab and V slab, slab_bytes contiguous bytes each at pool +
  * id * stride_block + kv * stride_kv + head * stride_head (a page's rows
  * must be contiguous: row stride = row bytes, slab_bytes = block_size * row
- * bytes, a multiple of 16, at most 2048). Each sequence's pages are cut into
+ * bytes, a multiple of 16, at most 4096). Each sequence's pages are cut into
  * `splits` equal ranges, one workgroup of 256 lanes per (sequence, kv head,
  * range): num_seqs * num_kv_heads * splits workgroups. Block ids are clamped
  * to [0, num_blocks). One XOR fold per wave goes to sink (at least 16 bytes

@@ -167,6 +167,6 @@ def test_probe_library_exports_and_rejects():
     call = lambda **k: g(*({**ok, **k}.values()), None)
     assert call(pool=0) == 1                            # NULL pool
     assert call(slab=1000) == 1                         # slab not a multiple of 16
-    assert call(slab=4096) == 1                         # slab above 2048 bytes
+    assert call(slab=4112) == 1                         # slab above 4096 bytes
     assert call(sb=2300) == 1                           # strides must be multiples of 16
     assert call(splits=8) == 1                          # sink smaller than 16 bytes per workgroup

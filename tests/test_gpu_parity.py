@@ -658,3 +658,44 @@ def test_prefill_batch_order(num_seqs):
     ref = O.paged_attention(oracle_pool(w), w.query, w.cu_q, w.block_table, w.seq_lens, w.k_scale, w.v_scale,
                             np.float32(d.sm_scale), 128)
     assert_attn_close(out, ref, f"prefill of {num_seqs} sequences")
+
+
+def test_decode_from_concurrent_host_threads():
+    """Decode calls from two host threads at once, each on its own stream with
+    its own workspace, alternating two batch sizes (two LDS sizes of the split
+    kernel, so its per-device occupancy cache is filled and read
+    concurrently): every result equals the single-threaded one."""
+    import threading
+    ws_ = [make_workload(seed=61 + k, name="x", seq_lens=lens, q_lens=[1] * len(lens), num_q_heads=8,
+                         num_kv_heads=2, head_size=128, block_size=16)
+           for k, lens in enumerate(([3000, 17, 900], [1500] * 70))]
+    devs = []
+    for w in ws_:
+        d = Dev(w, "HND")
+        d.append_all()
+        devs.append(d)
+    want = [d.decode() for d in devs]
+    torch.cuda.synchronize()
+    errors = []
+
+    def worker(tid):
+        try:
+            stream = torch.cuda.Stream()
+            with torch.cuda.stream(stream):
+                wss = [torch.zeros(nvk.decode_workspace_size(d.w.num_seqs, 8, 2, 128), dtype=torch.uint8,
+                                   device="cuda") for d in devs]
+                for it in range(20):
+                    k = (it + tid) % 2
+                    out = devs[k].decode(ws=wss[k])
+                    stream.synchronize()
+                    if not torch.equal(out, want[k]):
+                        errors.append((tid, it, k))
+        except Exception as e:  # pragma: no cover - reported below
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors[:4]
