@@ -960,16 +960,15 @@ __device__ __forceinline__ void store_column_fp8(uint8_t* orow, const f4 (&acc)[
   }
 }
 
-// Prefill ring stages: the step being dequantised and up to three in flight
-// (as many as the 6-bit wait counter can cover).
-// NVFP4: as many stages (up to 4) as the vmcnt counter can track. FP8
-// stages are 1.8x larger: 2 at D >= 128 keep three workgroups per CU at
-// D = 128 (48 KB each), as NVFP4 has.
+// Prefill ring stages: the step being dequantised and the ones in flight.
+// NVFP4: as many stages (up to 4) as the 6-bit vmcnt counter can cover; FP8
+// stages are 1.8x larger: 2 at D >= 128.
 template <int D, bool COMPACT, int FMT = kNvfp4>
 struct PrefillStages {
   static constexpr int NC = StageGeo<D, COMPACT, FMT>::NC;
   static constexpr int NS_MAX = (FMT == kNvfp4 || D == 64) ? 4 : 2;
   static constexpr int NS = (63 / NC + 1) < NS_MAX ? (63 / NC + 1) : NS_MAX;
+  static_assert(NS >= 2, "the prefill pipeline reads one stage while the next lands");
 };
 
 // Waves per prefill workgroup (NW) and 16-column tiles per wave (NT): a
@@ -982,20 +981,233 @@ struct PrefillGeo {
   static constexpr int NW = (D == 256) ? 8 : 4;
   static constexpr int NT = (D == 64) ? 4 : (D == 128) ? 2 : 1;
   static constexpr int kCols = NW * 16 * NT;
+  // One workgroup fills a CU at head size 256, so a third operand buffer
+  // (for the deferred PV product) costs no occupancy there; at the smaller
+  // head sizes it would cost a workgroup per CU.
+  static constexpr bool kDeferPV = (D == 256);
+  static constexpr int kOpBufs = kDeferPV ? 3 : 2;
 };
 
 // Waves per SIMD the prefill register budget is sized for: without the hint
-// the compiler spends the whole 256-register budget of two waves (or more)
-// at head sizes 64 and 128. At head size 128
-// with bf16 output the kernel is held to three waves (168 registers); the
-// FP8-cache and 4-byte-copy variants then keep a few values in scratch, all
-// of them set before the step loop and read after it. FP8 output keeps two.
+// the compiler spends the whole register file of one wave. Head size 128
+// with bf16 output fits three workgroups per CU in LDS and is held to three
+// waves (168 registers); the rest to two.
 template <int D, bool COMPACT, bool FP8OUT, int FMT>
 struct PrefillOcc {
   static constexpr int waves = (D == 128 && !FP8OUT) ? 3 : 2;
 };
 
-// Columns [wg_col, wg_col + 64 NT) of the chunk of sequence b (first query
+// NVFP4 at head sizes 128 and 256, where a workgroup has as many waves (NW)
+// as a lane has K chunks (KW) and twice as many V^T tiles: wave w's share of
+// a step is K chunk w of both subtiles and V^T tiles w and w + NW. Lane
+// (i, j) then needs, per subtile, one code word of K row i (chunk w of its
+// quarter j) with that chunk's block-scale byte, and its four V rows' codes
+// and scale bytes, as the whole-step reader takes them.
+template <int D>
+struct ShareRaw {
+  uint32_t k[2];
+  uint32_t ks[2];
+  SubRaw<D, kNvfp4> v[2];  // the V rows (k, ks unused)
+};
+
+template <int D>
+__device__ __forceinline__ void lds_read_share(ShareRaw<D>& R, const uint8_t* stage, int w) {
+  static_assert(D == 128 || D == 256, "share reader: head sizes 128 and 256");
+  // The lane offsets are derived here, each step, rather than held in
+  // registers for the whole loop (the step loop is at its register budget).
+  int lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  asm volatile("" : "+v"(lane));  // not loop-invariant to the compiler
+  const LdsLane o = lds_lane<D, kNvfp4>(lane & 15, lane >> 4);
+  constexpr int FD = D / 2 + D / 16;
+  constexpr int SUB = StageGeo<D, true>::SUB;
+  static_assert(StageGeo<D, true>::SUB == StageGeo<D, false>::SUB, "subtile size is the copy's");
+  const uint32_t s0 = lds_addr(stage);
+  // chunk w of quarter j: code word w of the lane's run, block (j D/4 + 8 w) / 16
+  const uint32_t ak = s0 + o.k + 4u * (uint32_t)w, aks = s0 + o.ks + ((uint32_t)w >> 1);
+  const uint32_t av = s0 + o.v, avs = s0 + o.vs;
+  if constexpr (D == 256) {
+    u32x2 v0[4], v1[4];
+    asm volatile(
+        "ds_read_b32 %0, %20\n\t"
+        "ds_read_u8 %1, %21\n\t"
+        "ds_read_b64 %2, %22\n\t"
+        "ds_read_b64 %3, %22 offset:144\n\t"
+        "ds_read_b64 %4, %22 offset:288\n\t"
+        "ds_read_b64 %5, %22 offset:432\n\t"
+        "ds_read_u8 %6, %23\n\t"
+        "ds_read_u8 %7, %23 offset:144\n\t"
+        "ds_read_u8 %8, %23 offset:288\n\t"
+        "ds_read_u8 %9, %23 offset:432\n\t"
+        "ds_read_b32 %10, %20 offset:4608\n\t"
+        "ds_read_u8 %11, %21 offset:4608\n\t"
+        "ds_read_b64 %12, %22 offset:4608\n\t"
+        "ds_read_b64 %13, %22 offset:4752\n\t"
+        "ds_read_b64 %14, %22 offset:4896\n\t"
+        "ds_read_b64 %15, %22 offset:5040\n\t"
+        "ds_read_u8 %16, %23 offset:4608\n\t"
+        "ds_read_u8 %17, %23 offset:4752\n\t"
+        "ds_read_u8 %18, %23 offset:4896\n\t"
+        "ds_read_u8 %19, %23 offset:5040\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(R.k[0]), "=&v"(R.ks[0]), "=&v"(v0[0]), "=&v"(v0[1]), "=&v"(v0[2]), "=&v"(v0[3]),
+          "=&v"(R.v[0].vs[0]), "=&v"(R.v[0].vs[1]), "=&v"(R.v[0].vs[2]), "=&v"(R.v[0].vs[3]), "=&v"(R.k[1]),
+          "=&v"(R.ks[1]), "=&v"(v1[0]), "=&v"(v1[1]), "=&v"(v1[2]), "=&v"(v1[3]), "=&v"(R.v[1].vs[0]),
+          "=&v"(R.v[1].vs[1]), "=&v"(R.v[1].vs[2]), "=&v"(R.v[1].vs[3])
+        : "v"(ak), "v"(aks), "v"(av), "v"(avs)
+        : "memory");
+    static_assert(FD == 144 && SUB == 4608, "D = 256 share reader offsets");
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      R.v[0].v[r][0] = v0[r][0];
+      R.v[0].v[r][1] = v0[r][1];
+      R.v[1].v[r][0] = v1[r][0];
+      R.v[1].v[r][1] = v1[r][1];
+    }
+  } else {
+    asm volatile(
+        "ds_read_b32 %0, %20\n\t"
+        "ds_read_u8 %1, %21\n\t"
+        "ds_read_b32 %2, %22\n\t"
+        "ds_read_b32 %3, %22 offset:72\n\t"
+        "ds_read_b32 %4, %22 offset:144\n\t"
+        "ds_read_b32 %5, %22 offset:216\n\t"
+        "ds_read_u8 %6, %23\n\t"
+        "ds_read_u8 %7, %23 offset:72\n\t"
+        "ds_read_u8 %8, %23 offset:144\n\t"
+        "ds_read_u8 %9, %23 offset:216\n\t"
+        "ds_read_b32 %10, %20 offset:2304\n\t"
+        "ds_read_u8 %11, %21 offset:2304\n\t"
+        "ds_read_b32 %12, %22 offset:2304\n\t"
+        "ds_read_b32 %13, %22 offset:2376\n\t"
+        "ds_read_b32 %14, %22 offset:2448\n\t"
+        "ds_read_b32 %15, %22 offset:2520\n\t"
+        "ds_read_u8 %16, %23 offset:2304\n\t"
+        "ds_read_u8 %17, %23 offset:2376\n\t"
+        "ds_read_u8 %18, %23 offset:2448\n\t"
+        "ds_read_u8 %19, %23 offset:2520\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(R.k[0]), "=&v"(R.ks[0]), "=&v"(R.v[0].v[0][0]), "=&v"(R.v[0].v[1][0]), "=&v"(R.v[0].v[2][0]),
+          "=&v"(R.v[0].v[3][0]), "=&v"(R.v[0].vs[0]), "=&v"(R.v[0].vs[1]), "=&v"(R.v[0].vs[2]),
+          "=&v"(R.v[0].vs[3]), "=&v"(R.k[1]), "=&v"(R.ks[1]), "=&v"(R.v[1].v[0][0]), "=&v"(R.v[1].v[1][0]),
+          "=&v"(R.v[1].v[2][0]), "=&v"(R.v[1].v[3][0]), "=&v"(R.v[1].vs[0]), "=&v"(R.v[1].vs[1]),
+          "=&v"(R.v[1].vs[2]), "=&v"(R.v[1].vs[3])
+        : "v"(ak), "v"(aks), "v"(av), "v"(avs)
+        : "memory");
+    static_assert(FD == 72 && SUB == 2304, "D = 128 share reader offsets");
+  }
+}
+
+// V^T tiles T of this wave's share (T % NW == w) into the operand buffer.
+template <int D, int T, int NW>
+__device__ __forceinline__ void store_v_share(const SubRaw<D, kNvfp4> (&R)[2], const VPairs<D, kNvfp4> (&vp)[2],
+                                              int w, uint32_t slot) {
+  if constexpr (T < Geo<D>::DPL) {
+    if (T % NW == w) lds_store_op(slot + (2 * Geo<D>::KW + T) * 1024, make_op<D, 2 * Geo<D>::KW + T>(R, vp));
+    store_v_share<D, T + 1, NW>(R, vp, w, slot);
+  }
+}
+
+// This wave's share of the step's MFMA operands (NVFP4, head size 128 or
+// 256) from its own raw bytes: the same values make_ops stores.
+template <int D, int NW>
+__device__ __forceinline__ void prefill_dequant_share(const uint8_t* stage, int kb, int L, int j, int w,
+                                                      uint32_t slot) {
+  static_assert(Geo<D>::KW == NW && Geo<D>::DPL == 2 * NW, "share layout");
+  ShareRaw<D> R;
+  lds_read_share<D>(R, stage, w);
+  if (kb + kStep > L) mask_step(R.v, kb, L, j);
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb) {
+    const h2 sp = fp8x2_to_h2<false>(R.ks[sb]);
+    const h2 ss = {sp[0], sp[0]};
+    const uint32_t c = R.k[sb];
+    const h2 a0 = fp4x2_to_h2<0>(c) * ss;
+    const h2 a1 = fp4x2_to_h2<1>(c) * ss;
+    const h2 a2 = fp4x2_to_h2<2>(c) * ss;
+    const h2 a3 = fp4x2_to_h2<3>(c) * ss;
+    lds_store_op(slot + (uint32_t)(sb * Geo<D>::KW + w) * 1024u,
+                 h8{a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]});
+  }
+  VPairs<D, kNvfp4> vp[2];
+  make_pairs(R.v[0], vp[0]);
+  make_pairs(R.v[1], vp[1]);
+  store_v_share<D, 0, NW>(R.v, vp, w, slot);
+}
+
+// This wave's share of the MFMA operands of the raw step at `stage` (first
+// key kb), dequantised into the operand buffer whose lane slot is `slot`.
+template <int D, int FMT, int NW>
+__device__ __forceinline__ void prefill_dequant(const uint8_t* stage, const LdsLane& ll, int kb, int L, int j, int w,
+                                                uint32_t slot) {
+  if constexpr (FMT == kNvfp4 && (D == 128 || D == 256)) {
+    (void)ll;
+    prefill_dequant_share<D, NW>(stage, kb, L, j, w, slot);
+  } else {
+    SubRaw<D, FMT> R[2];
+    lds_read_step<D, FMT>(R, stage, ll);
+    if (kb + kStep > L) mask_step(R, kb, L, j);
+    VPairs<D, FMT> vp[2];
+    make_pairs(R[0], vp[0]);
+    make_pairs(R[1], vp[1]);
+    make_ops<D, 0, NW>(R, vp, w, slot);
+  }
+}
+
+// S^T of a step for this wave's column tiles from the K operands of its
+// operand buffer (E = subtile * KW + chunk), eight (head size 64: four) at a
+// time.
+template <int D, int NT, int FMT>
+__device__ __forceinline__ void prefill_scores(WaveAttn<D, NT, FMT>& W, uint32_t slot, f4 (&s)[2][NT]) {
+  using G = Geo<D>;
+  constexpr int NK = 2 * G::KW;
+  // four at a time at head size 128, whose step loop is at its register budget
+  constexpr int GS = (NK < 8 || D == 128) ? 4 : 8;
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+    for (int n = 0; n < NT; ++n) s[sb][n] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int g = 0; g < NK / GS; ++g) {
+    h8 t[GS];
+    if constexpr (GS == 8)
+      lds_load_ops8(t, slot + g * GS * 1024);
+    else
+      lds_load_ops4(t, slot + g * GS * 1024);
+#pragma unroll
+    for (int e = 0; e < GS; ++e) {
+      const int E = g * GS + e;
+#pragma unroll
+      for (int n = 0; n < NT; ++n)
+        s[E / G::KW][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(t[e], W.q[n][E % G::KW], s[E / G::KW][n], 0, 0, 0);
+    }
+  }
+}
+
+// O^T += V^T . P^T of a step from the V^T operands of its operand buffer
+// (E = 2 KW + tile), with the running sums when they come from the matrix
+// unit.
+template <int D, int NT, int FMT>
+__device__ __forceinline__ void prefill_pv(WaveAttn<D, NT, FMT>& W, uint32_t slot, const h8 (&p)[NT]) {
+  using G = Geo<D>;
+  constexpr int GS = G::DPL < 8 ? G::DPL : 8;
+  const uint32_t v0 = slot + 2 * G::KW * 1024;
+#pragma unroll
+  for (int g = 0; g < G::DPL / GS; ++g) {
+    h8 t[GS];
+    if constexpr (GS == 8)
+      lds_load_ops8(t, v0 + g * GS * 1024);
+    else
+      lds_load_ops4(t, v0 + g * GS * 1024);
+#pragma unroll
+    for (int e = 0; e < GS; ++e)
+#pragma unroll
+      for (int n = 0; n < NT; ++n)
+        W.acc[n][g * GS + e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(t[e], p[n], W.acc[n][g * GS + e], 0, 0, 0);
+  }
+  if constexpr (WaveAttn<D, NT, FMT>::kMfmaSum) W.sum_ops(p);
+}
+
+// Columns [wg_col, wg_col + 64 NT) of the chunk of sequence b// Columns [wg_col, wg_col + 64 NT) of the chunk of sequence b (first query
 // row q0, qlen rows, L keys) for kv head h: the workgroup's four waves
 // share the dequantisation of each 32-key step and each runs its own 16 NT
 // columns' products (see the kernel below).
@@ -1046,55 +1258,86 @@ __device__ __forceinline__ void prefill_columns(const PrefillArgs& a, uint8_t* r
   kw = kw > L ? L : (kw < 0 ? 0 : kw);
   const int min_full = a.causal ? L - qlen + col_base / grp + 1 : L;
   const int32_t* bt_row = a.bt + (int64_t)b * a.max_blocks;
-  const DmaOffsets<D, COMPACT, FMT> dof = dma_offsets<D, COMPACT, FMT>(a.pool.st, a.pool.skv, lane);
   const LdsLane ll = lds_lane<D, FMT>(i, j);
   const uint32_t op_lane = lds_addr(opbuf) + lane * 16;
 
-  // ---- the four waves share each 32-key step: wave 0 copies it into the
-  // ring (NS - 1 steps ahead), every wave reads the raw step
-  // and dequantises a quarter of its MFMA operands into the step's operand
-  // buffer, and every wave then runs its own columns' products from all of
-  // them. Two barriers per step: the raw step has landed; the operands are
-  // in place. Ring stage k % NS is refilled only after the second barrier of
-  // step k (every wave has read it), operand buffer k % 2 only after the
-  // first barrier of step k + 1 (every wave has used step k's).
+  // ---- the waves share each 32-key step, in a pipeline with one barrier
+  // per step. Wave 0 copies raw steps into the NS-stage ring (NS - 1 ahead);
+  // each wave dequantises its share of a step's MFMA operands into that
+  // step's operand buffer one iteration before the step's products, so the
+  // dequantisation of step k + 1 overlaps the products of step k on the
+  // matrix unit. Iteration k runs, per wave: the scores of step k; with a
+  // deferred PV product (three operand buffers, step s in buffer s % 3) the
+  // PV product of step k - 1, whose probabilities the previous iteration
+  // left; the dequantisation of step k + 1; the softmax of step k, and
+  // without deferral (two buffers, s % 2) the PV product of step k; then the
+  // barrier. At the barrier that opens iteration k every operand of step k is
+  // in place and raw step k + 1 has landed; ring stage k % NS (raw step k,
+  // dequantised in iteration k - 1) is free, and so is the buffer that step
+  // k + 1 takes (it held step k - 2, or step k - 1 without deferral, both
+  // last read in iteration k - 1).
   const bool copier = w == 0;
   if (copier) {
+    const DmaOffsets<D, COMPACT, FMT> dof = dma_offsets<D, COMPACT, FMT>(a.pool.st, a.pool.skv, lane);
 #pragma unroll
-    for (int s = 0; s < NS - 1; ++s)
+    for (int s = 0; s < NS; ++s)
       dma_step<D, COMPACT, FMT>(ring + s * SG::STAGE, a.pool, ids_for_step(bt_row, s, steps, L, a.max_blocks, a.pool), h,
                                 s * kStep, dof);
   }
-  StepIds nxt = ids_for_step(bt_row, NS - 1, steps, L, a.max_blocks, a.pool);
+  StepIds nxt = ids_for_step(bt_row, NS, steps, L, a.max_blocks, a.pool);
+  wait_vmcnt<(NS - 1) * SG::NC>();  // the copier: step 0 has landed (others: no-op)
+  lds_barrier();
+  if (steps > 0) prefill_dequant<D, FMT, PrefillGeo<D>::NW>(ring, ll, 0, L, j, w, op_lane);
+  constexpr bool kDefer = PrefillGeo<D>::kDeferPV;
+  // The upper half of the waves dequantise before their products and the
+  // lower half after, so that the two waves a SIMD holds tend to be in
+  // different phases (matrix unit and LDS reads / vector ALU) after each
+  // barrier instead of contending for the same unit.
+  const bool deq_first = w >= PrefillGeo<D>::NW / 2;
+  h8 p[NT];
+  bool pv_pending = false;  // wave-uniform: the previous step's PV product is due (deferral only)
+  // operand buffers of steps k, k + 1 and (deferral) k - 1
+  uint32_t buf_cur = 0, buf_next = OG::BYTES, buf_prev = 2 * OG::BYTES;
   for (int k = 0; k < steps; ++k) {
-    if (copier)
-      dma_step<D, COMPACT, FMT>(ring + ((k + NS - 1) % NS) * SG::STAGE, a.pool, nxt, h, (k + NS - 1) * kStep, dof);
-    nxt = ids_for_step(bt_row, k + NS, steps, L, a.max_blocks, a.pool);
-    wait_vmcnt<(NS - 1) * SG::NC>();  // the copier: step k has landed (others: no-op)
-    lds_barrier();          // every wave may read step k
-    SubRaw<D, FMT> R[2];
-    lds_read_step<D, FMT>(R, ring + (k % NS) * SG::STAGE, ll);
+    wait_vmcnt<(NS - 2) * SG::NC>();  // the copier: step k + 1 has landed
+    lds_barrier();
+    if (copier) {
+      // per-lane copy offsets, derived again each step (registers)
+      int t = threadIdx.x;
+      asm volatile("" : "+v"(t));
+      const DmaOffsets<D, COMPACT, FMT> dof = dma_offsets<D, COMPACT, FMT>(a.pool.st, a.pool.skv, t & 63);
+      dma_step<D, COMPACT, FMT>(ring + (k % NS) * SG::STAGE, a.pool, nxt, h, (k + NS) * kStep, dof);
+    }
+    nxt = ids_for_step(bt_row, k + NS + 1, steps, L, a.max_blocks, a.pool);
     const int kb = k * kStep;
-    if (kb + kStep > L) mask_step(R, kb, L, j);
-    VPairs<D, FMT> vp[2];
-    make_pairs(R[0], vp[0]);
-    make_pairs(R[1], vp[1]);
-    const uint32_t slot = op_lane + (uint32_t)((k & 1) * OG::BYTES);
-    make_ops<D, 0, PrefillGeo<D>::NW>(R, vp, w, slot);
-    lds_barrier();          // every operand of step k is in place
-    if (kb < kw) {
-      h8 ka[2][G::KW], va[G::DPL];
-      f4 sc[2][NT];
-      // K operands first (D = 64: one group of 8 holds K and V), then V
-      constexpr int KEND = OG::NK < 8 ? 8 : OG::NK;
-      load_ops<D, 0, KEND>(ka, va, slot);
-      W.scores_ops(ka, sc);
-      h8 p[NT];
+    const bool mine = kb < kw;
+    f4 sc[2][NT];
+    const bool deq = k + 1 < steps;
+    if (deq_first && deq)
+      prefill_dequant<D, FMT, PrefillGeo<D>::NW>(ring + ((k + 1) % NS) * SG::STAGE, ll, kb + kStep, L, j, w,
+                                                  op_lane + buf_next);
+    if (mine) prefill_scores(W, op_lane + buf_cur, sc);
+    if (kDefer && pv_pending) prefill_pv(W, op_lane + buf_prev, p);
+    if (!deq_first && deq)
+      prefill_dequant<D, FMT, PrefillGeo<D>::NW>(ring + ((k + 1) % NS) * SG::STAGE, ll, kb + kStep, L, j, w,
+                                                  op_lane + buf_next);
+    if (mine) {
       W.softmax(sc, kb, j, kb + kStep > min_full, p);
-      load_ops<D, KEND, OG::NE>(ka, va, slot);
-      W.pv_ops(va, p);
+      if (!kDefer) prefill_pv(W, op_lane + buf_cur, p);
+    }
+    pv_pending = kDefer && mine;
+    if constexpr (kDefer) {
+      const uint32_t t = buf_prev;
+      buf_prev = buf_cur;
+      buf_cur = buf_next;
+      buf_next = t;
+    } else {
+      const uint32_t t = buf_cur;
+      buf_cur = buf_next;
+      buf_next = t;
     }
   }
+  if (kDefer && pv_pending) prefill_pv(W, op_lane + buf_prev, p);
   wait_vmcnt<0>();
 
   const float gv = *a.v_scale;
@@ -1120,7 +1363,7 @@ __global__ __launch_bounds__(64 * PrefillGeo<D>::NW) __attribute__((amdgpu_waves
   constexpr int NS = PrefillStages<D, COMPACT, FMT>::NS;
   extern __shared__ __align__(16) char smem[];
   uint8_t* ring = reinterpret_cast<uint8_t*>(smem);  // [NS] raw steps
-  uint8_t* opbuf = ring + NS * SG::STAGE;             // [2] operand buffers
+  uint8_t* opbuf = ring + NS * SG::STAGE;             // [kOpBufs] operand buffers
 
   const int h = blockIdx.y;
   const int b = a.longest_first ? prefill_seq_of_rank(a, blockIdx.z, reinterpret_cast<int*>(ring)) : (int)blockIdx.z;
@@ -1145,7 +1388,7 @@ __global__ __launch_bounds__(64 * PrefillGeo<D>::NW) __attribute__((amdgpu_waves
 
 template <int D, bool COMPACT, int FMT>
 size_t prefill_lds_bytes() {
-  return (size_t)PrefillStages<D, COMPACT, FMT>::NS * StageGeo<D, COMPACT, FMT>::STAGE + 2 * OpGeo<D>::BYTES;
+  return (size_t)PrefillStages<D, COMPACT, FMT>::NS * StageGeo<D, COMPACT, FMT>::STAGE + PrefillGeo<D>::kOpBufs * OpGeo<D>::BYTES;
 }
 
 template <int D, int NT, int FMT>

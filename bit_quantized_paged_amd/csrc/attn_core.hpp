@@ -214,13 +214,23 @@ __device__ __forceinline__ h4 v_operand(const VPairs<D, FMT>& P) {
   return h4{a[0], a[1], b[0], b[1]};
 }
 
+// Reductions over j (lane bits 4 and 5): lanes l and l ^ 16, then l and
+// l ^ 32. The row swap (16-lane rows 0 <-> 1, 2 <-> 3) and the half swap of
+// gfx950 exchange a register's rows in the VALU without an LDS round trip;
+// with both operands the same value, the two results of a swap hold, in every
+// lane, x[l] and x[l ^ 16] (x[l ^ 32]) in the same order for both lanes of a
+// pair, so every lane of a pair gets the same bits.
 __device__ __forceinline__ float wave_max_j(float v) {
-  v = __builtin_fmaxf(v, __shfl_xor(v, 16));
-  return __builtin_fmaxf(v, __shfl_xor(v, 32));
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __builtin_fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __builtin_fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float wave_sum_j(float v) {
-  v += __shfl_xor(v, 16);
-  return v + __shfl_xor(v, 32);
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 template <int D, int NT, int FMT = kNvfp4>
@@ -982,6 +992,19 @@ __device__ __forceinline__ void lds_load_ops8(h8 (&o)[8], uint32_t addr) {
       "ds_read_b128 %7, %8 offset:7168\n\t"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7])
+      : "v"(addr)
+      : "memory");
+}
+
+// Four consecutive operands (head size 64: a step's K or V operands).
+__device__ __forceinline__ void lds_load_ops4(h8 (&o)[4], uint32_t addr) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %4 offset:1024\n\t"
+      "ds_read_b128 %2, %4 offset:2048\n\t"
+      "ds_read_b128 %3, %4 offset:3072\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3])
       : "v"(addr)
       : "memory");
 }
