@@ -990,132 +990,103 @@ struct PrefillGeo {
 
 // Waves per SIMD the prefill register budget is sized for: without the hint
 // the compiler spends the whole register file of one wave. Head size 128
-// with bf16 output fits three workgroups per CU in LDS and is held to three
-// waves (168 registers); the rest to two.
+// fits three workgroups per CU in LDS and is held to three waves (168
+// registers); the rest to two.
 template <int D, bool COMPACT, bool FP8OUT, int FMT>
 struct PrefillOcc {
-  static constexpr int waves = (D == 128 && !FP8OUT) ? 3 : 2;
+  static constexpr int waves = (D == 128) ? 3 : 2;
 };
 
 // NVFP4 at head sizes 128 and 256, where a workgroup has as many waves (NW)
 // as a lane has K chunks (KW) and twice as many V^T tiles: wave w's share of
-// a step is K chunk w of both subtiles and V^T tiles w and w + NW. Lane
-// (i, j) then needs, per subtile, one code word of K row i (chunk w of its
-// quarter j) with that chunk's block-scale byte, and its four V rows' codes
-// and scale bytes, as the whole-step reader takes them.
+// a step is K chunk w of both subtiles and V^T tiles 2w and 2w + 1. Both
+// tiles take, from each of the lane's four V rows, the two nibbles of one
+// byte: byte B = w % 4 of the row's code word W = w / 4 (the lane's D/32
+// code bytes of a row are D/128 words). Lane (i, j) reads, per subtile, the
+// code word of K chunk w of row i with that chunk's block-scale byte, and
+// word W of its four V rows with their scale bytes.
 template <int D>
 struct ShareRaw {
   uint32_t k[2];
   uint32_t ks[2];
-  SubRaw<D, kNvfp4> v[2];  // the V rows (k, ks unused)
+  uint32_t v[2][4];
+  uint32_t vs[2][4];
 };
 
 template <int D>
-__device__ __forceinline__ void lds_read_share(ShareRaw<D>& R, const uint8_t* stage, int w) {
+__device__ __forceinline__ void lds_read_share(ShareRaw<D>& R, const uint8_t* stage, LdsLane o, int w) {
   static_assert(D == 128 || D == 256, "share reader: head sizes 128 and 256");
-  // The lane offsets are derived here, each step, rather than held in
-  // registers for the whole loop (the step loop is at its register budget).
-  int lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-  asm volatile("" : "+v"(lane));  // not loop-invariant to the compiler
-  const LdsLane o = lds_lane<D, kNvfp4>(lane & 15, lane >> 4);
   constexpr int FD = D / 2 + D / 16;
   constexpr int SUB = StageGeo<D, true>::SUB;
   static_assert(StageGeo<D, true>::SUB == StageGeo<D, false>::SUB, "subtile size is the copy's");
+  static_assert((D == 256 && FD == 144 && SUB == 4608) || (D == 128 && FD == 72 && SUB == 2304), "reader offsets");
+  if constexpr (D == 128) {
+    // The lane offsets are derived here, each step, rather than held in
+    // registers for the whole loop (at this head size the step loop is at its
+    // register budget); the asm keeps the compiler from hoisting them.
+    int lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    asm volatile("" : "+v"(lane));
+    o = lds_lane<D, kNvfp4>(lane & 15, lane >> 4);
+  }
   const uint32_t s0 = lds_addr(stage);
   // chunk w of quarter j: code word w of the lane's run, block (j D/4 + 8 w) / 16
   const uint32_t ak = s0 + o.k + 4u * (uint32_t)w, aks = s0 + o.ks + ((uint32_t)w >> 1);
-  const uint32_t av = s0 + o.v, avs = s0 + o.vs;
-  if constexpr (D == 256) {
-    u32x2 v0[4], v1[4];
-    asm volatile(
-        "ds_read_b32 %0, %20\n\t"
-        "ds_read_u8 %1, %21\n\t"
-        "ds_read_b64 %2, %22\n\t"
-        "ds_read_b64 %3, %22 offset:144\n\t"
-        "ds_read_b64 %4, %22 offset:288\n\t"
-        "ds_read_b64 %5, %22 offset:432\n\t"
-        "ds_read_u8 %6, %23\n\t"
-        "ds_read_u8 %7, %23 offset:144\n\t"
-        "ds_read_u8 %8, %23 offset:288\n\t"
-        "ds_read_u8 %9, %23 offset:432\n\t"
-        "ds_read_b32 %10, %20 offset:4608\n\t"
-        "ds_read_u8 %11, %21 offset:4608\n\t"
-        "ds_read_b64 %12, %22 offset:4608\n\t"
-        "ds_read_b64 %13, %22 offset:4752\n\t"
-        "ds_read_b64 %14, %22 offset:4896\n\t"
-        "ds_read_b64 %15, %22 offset:5040\n\t"
-        "ds_read_u8 %16, %23 offset:4608\n\t"
-        "ds_read_u8 %17, %23 offset:4752\n\t"
-        "ds_read_u8 %18, %23 offset:4896\n\t"
-        "ds_read_u8 %19, %23 offset:5040\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(R.k[0]), "=&v"(R.ks[0]), "=&v"(v0[0]), "=&v"(v0[1]), "=&v"(v0[2]), "=&v"(v0[3]),
-          "=&v"(R.v[0].vs[0]), "=&v"(R.v[0].vs[1]), "=&v"(R.v[0].vs[2]), "=&v"(R.v[0].vs[3]), "=&v"(R.k[1]),
-          "=&v"(R.ks[1]), "=&v"(v1[0]), "=&v"(v1[1]), "=&v"(v1[2]), "=&v"(v1[3]), "=&v"(R.v[1].vs[0]),
-          "=&v"(R.v[1].vs[1]), "=&v"(R.v[1].vs[2]), "=&v"(R.v[1].vs[3])
-        : "v"(ak), "v"(aks), "v"(av), "v"(avs)
-        : "memory");
-    static_assert(FD == 144 && SUB == 4608, "D = 256 share reader offsets");
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      R.v[0].v[r][0] = v0[r][0];
-      R.v[0].v[r][1] = v0[r][1];
-      R.v[1].v[r][0] = v1[r][0];
-      R.v[1].v[r][1] = v1[r][1];
-    }
-  } else {
-    asm volatile(
-        "ds_read_b32 %0, %20\n\t"
-        "ds_read_u8 %1, %21\n\t"
-        "ds_read_b32 %2, %22\n\t"
-        "ds_read_b32 %3, %22 offset:72\n\t"
-        "ds_read_b32 %4, %22 offset:144\n\t"
-        "ds_read_b32 %5, %22 offset:216\n\t"
-        "ds_read_u8 %6, %23\n\t"
-        "ds_read_u8 %7, %23 offset:72\n\t"
-        "ds_read_u8 %8, %23 offset:144\n\t"
-        "ds_read_u8 %9, %23 offset:216\n\t"
-        "ds_read_b32 %10, %20 offset:2304\n\t"
-        "ds_read_u8 %11, %21 offset:2304\n\t"
-        "ds_read_b32 %12, %22 offset:2304\n\t"
-        "ds_read_b32 %13, %22 offset:2376\n\t"
-        "ds_read_b32 %14, %22 offset:2448\n\t"
-        "ds_read_b32 %15, %22 offset:2520\n\t"
-        "ds_read_u8 %16, %23 offset:2304\n\t"
-        "ds_read_u8 %17, %23 offset:2376\n\t"
-        "ds_read_u8 %18, %23 offset:2448\n\t"
-        "ds_read_u8 %19, %23 offset:2520\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(R.k[0]), "=&v"(R.ks[0]), "=&v"(R.v[0].v[0][0]), "=&v"(R.v[0].v[1][0]), "=&v"(R.v[0].v[2][0]),
-          "=&v"(R.v[0].v[3][0]), "=&v"(R.v[0].vs[0]), "=&v"(R.v[0].vs[1]), "=&v"(R.v[0].vs[2]),
-          "=&v"(R.v[0].vs[3]), "=&v"(R.k[1]), "=&v"(R.ks[1]), "=&v"(R.v[1].v[0][0]), "=&v"(R.v[1].v[1][0]),
-          "=&v"(R.v[1].v[2][0]), "=&v"(R.v[1].v[3][0]), "=&v"(R.v[1].vs[0]), "=&v"(R.v[1].vs[1]),
-          "=&v"(R.v[1].vs[2]), "=&v"(R.v[1].vs[3])
-        : "v"(ak), "v"(aks), "v"(av), "v"(avs)
-        : "memory");
-    static_assert(FD == 72 && SUB == 2304, "D = 128 share reader offsets");
-  }
-}
-
-// V^T tiles T of this wave's share (T % NW == w) into the operand buffer.
-template <int D, int T, int NW>
-__device__ __forceinline__ void store_v_share(const SubRaw<D, kNvfp4> (&R)[2], const VPairs<D, kNvfp4> (&vp)[2],
-                                              int w, uint32_t slot) {
-  if constexpr (T < Geo<D>::DPL) {
-    if (T % NW == w) lds_store_op(slot + (2 * Geo<D>::KW + T) * 1024, make_op<D, 2 * Geo<D>::KW + T>(R, vp));
-    store_v_share<D, T + 1, NW>(R, vp, w, slot);
-  }
+  const uint32_t av = s0 + o.v + 4u * (uint32_t)(w >> 2), avs = s0 + o.vs;
+#define NVFP4KV_SHARE_READ(R1, R2, R3, SB0, SB1)                                                              \
+  asm volatile("ds_read_b32 %0, %20\n\t"                                                                   \
+               "ds_read_u8 %1, %21\n\t"                                                                    \
+               "ds_read_b32 %2, %22\n\t"                                                                   \
+               "ds_read_b32 %3, %22 offset:" #R1 "\n\t"                                                    \
+               "ds_read_b32 %4, %22 offset:" #R2 "\n\t"                                                    \
+               "ds_read_b32 %5, %22 offset:" #R3 "\n\t"                                                    \
+               "ds_read_u8 %6, %23\n\t"                                                                    \
+               "ds_read_u8 %7, %23 offset:" #R1 "\n\t"                                                     \
+               "ds_read_u8 %8, %23 offset:" #R2 "\n\t"                                                     \
+               "ds_read_u8 %9, %23 offset:" #R3 "\n\t"                                                     \
+               "ds_read_b32 %10, %20 offset:" #SB0 "\n\t"                                                  \
+               "ds_read_u8 %11, %21 offset:" #SB0 "\n\t"                                                   \
+               "ds_read_b32 %12, %22 offset:" #SB0 "\n\t"                                                  \
+               "ds_read_b32 %13, %22 offset:" #SB1 "+" #R1 "\n\t"                                          \
+               "ds_read_b32 %14, %22 offset:" #SB1 "+" #R2 "\n\t"                                          \
+               "ds_read_b32 %15, %22 offset:" #SB1 "+" #R3 "\n\t"                                          \
+               "ds_read_u8 %16, %23 offset:" #SB0 "\n\t"                                                   \
+               "ds_read_u8 %17, %23 offset:" #SB1 "+" #R1 "\n\t"                                           \
+               "ds_read_u8 %18, %23 offset:" #SB1 "+" #R2 "\n\t"                                           \
+               "ds_read_u8 %19, %23 offset:" #SB1 "+" #R3 "\n\t"                                           \
+               "s_waitcnt lgkmcnt(0)"                                                                      \
+               : "=&v"(R.k[0]), "=&v"(R.ks[0]), "=&v"(R.v[0][0]), "=&v"(R.v[0][1]), "=&v"(R.v[0][2]),     \
+                 "=&v"(R.v[0][3]), "=&v"(R.vs[0][0]), "=&v"(R.vs[0][1]), "=&v"(R.vs[0][2]), "=&v"(R.vs[0][3]), \
+                 "=&v"(R.k[1]), "=&v"(R.ks[1]), "=&v"(R.v[1][0]), "=&v"(R.v[1][1]), "=&v"(R.v[1][2]),      \
+                 "=&v"(R.v[1][3]), "=&v"(R.vs[1][0]), "=&v"(R.vs[1][1]), "=&v"(R.vs[1][2]), "=&v"(R.vs[1][3]) \
+               : "v"(ak), "v"(aks), "v"(av), "v"(avs)                                                      \
+               : "memory")
+  if constexpr (D == 256)
+    NVFP4KV_SHARE_READ(144, 288, 432, 4608, 4608);
+  else
+    NVFP4KV_SHARE_READ(72, 144, 216, 2304, 2304);
+#undef NVFP4KV_SHARE_READ
 }
 
 // This wave's share of the step's MFMA operands (NVFP4, head size 128 or
 // 256) from its own raw bytes: the same values make_ops stores.
 template <int D, int NW>
-__device__ __forceinline__ void prefill_dequant_share(const uint8_t* stage, int kb, int L, int j, int w,
-                                                      uint32_t slot) {
+__device__ __forceinline__ void prefill_dequant_share(const uint8_t* stage, const LdsLane& ll, int kb, int L, int j,
+                                                      int w, uint32_t slot) {
   static_assert(Geo<D>::KW == NW && Geo<D>::DPL == 2 * NW, "share layout");
   ShareRaw<D> R;
-  lds_read_share<D>(R, stage, w);
-  if (kb + kStep > L) mask_step(R.v, kb, L, j);
+  lds_read_share<D>(R, stage, ll, w);
+  if (kb + kStep > L) {
+    // value rows (codes and scales) of keys >= L read as zeros
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool ok = kb + 16 * sb + 4 * j + r < L;
+        R.v[sb][r] = ok ? R.v[sb][r] : 0u;
+        R.vs[sb][r] = ok ? R.vs[sb][r] : 0u;
+      }
+  }
+  // K chunk w of each subtile: 8 codes times their block scale
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb) {
     const h2 sp = fp8x2_to_h2<false>(R.ks[sb]);
@@ -1128,10 +1099,31 @@ __device__ __forceinline__ void prefill_dequant_share(const uint8_t* stage, int 
     lds_store_op(slot + (uint32_t)(sb * Geo<D>::KW + w) * 1024u,
                  h8{a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]});
   }
-  VPairs<D, kNvfp4> vp[2];
-  make_pairs(R.v[0], vp[0]);
-  make_pairs(R.v[1], vp[1]);
-  store_v_share<D, 0, NW>(R.v, vp, w, slot);
+  // V^T tiles 2w (low nibbles, d even) and 2w + 1 (high nibbles): for the key
+  // pair (a, b) = (4j + 2p, 4j + 2p + 1) of a subtile, one byte permute puts
+  // byte B of the two rows side by side, each byte converts to its two
+  // values times its row's block scale, and two half-word permutes pair the
+  // keys' d-even and d-odd values.
+  const uint32_t B = (uint32_t)w & 3u;
+  const uint32_t sel = 0x0C0C0000u | ((4u + B) << 8) | B;
+  h4 t0[2], t1[2];
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb) {
+    h2 ca[2], cb[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const uint32_t x = __builtin_amdgcn_perm(R.v[sb][2 * p + 1], R.v[sb][2 * p], sel);
+      const h2 sc = fp8x2_to_h2<false>(__builtin_amdgcn_perm(R.vs[sb][2 * p + 1], R.vs[sb][2 * p], 0x0C0C0400u));
+      const h2 sa = {sc[0], sc[0]}, sbb = {sc[1], sc[1]};
+      ca[p] = fp4x2_to_h2<0>(x) * sa;   // (a d-even, a d-odd)
+      cb[p] = fp4x2_to_h2<1>(x) * sbb;  // (b d-even, b d-odd)
+    }
+    t0[sb] = h4{ca[0][0], cb[0][0], ca[1][0], cb[1][0]};
+    t1[sb] = h4{ca[0][1], cb[0][1], ca[1][1], cb[1][1]};
+  }
+  const uint32_t vslot = slot + (uint32_t)(2 * Geo<D>::KW + 2 * w) * 1024u;
+  lds_store_op(vslot, h8{t0[0][0], t0[0][1], t0[0][2], t0[0][3], t0[1][0], t0[1][1], t0[1][2], t0[1][3]});
+  lds_store_op(vslot + 1024u, h8{t1[0][0], t1[0][1], t1[0][2], t1[0][3], t1[1][0], t1[1][1], t1[1][2], t1[1][3]});
 }
 
 // This wave's share of the MFMA operands of the raw step at `stage` (first
@@ -1140,8 +1132,7 @@ template <int D, int FMT, int NW>
 __device__ __forceinline__ void prefill_dequant(const uint8_t* stage, const LdsLane& ll, int kb, int L, int j, int w,
                                                 uint32_t slot) {
   if constexpr (FMT == kNvfp4 && (D == 128 || D == 256)) {
-    (void)ll;
-    prefill_dequant_share<D, NW>(stage, kb, L, j, w, slot);
+    prefill_dequant_share<D, NW>(stage, ll, kb, L, j, w, slot);
   } else {
     SubRaw<D, FMT> R[2];
     lds_read_step<D, FMT>(R, stage, ll);
@@ -1289,11 +1280,15 @@ __device__ __forceinline__ void prefill_columns(const PrefillArgs& a, uint8_t* r
   lds_barrier();
   if (steps > 0) prefill_dequant<D, FMT, PrefillGeo<D>::NW>(ring, ll, 0, L, j, w, op_lane);
   constexpr bool kDefer = PrefillGeo<D>::kDeferPV;
-  // The upper half of the waves dequantise before their products and the
-  // lower half after, so that the two waves a SIMD holds tend to be in
-  // different phases (matrix unit and LDS reads / vector ALU) after each
-  // barrier instead of contending for the same unit.
-  const bool deq_first = w >= PrefillGeo<D>::NW / 2;
+  // With the deferred PV product (head size 256, one workgroup per CU) the
+  // waves dequantise after their products, which then queue on the matrix
+  // unit while the vector ALU works; at the smaller head sizes several
+  // workgroups share a CU and every wave dequantises first, which keeps the
+  // scores out of registers during the dequantisation (measured on
+  // mixed_serving 890 us against 904 us with the dequantisation first and
+  // 912 us with half the waves each way; chunked_prefill 1616 us against
+  // 1707 us with it last).
+  const bool deq_first = !kDefer;
   h8 p[NT];
   bool pv_pending = false;  // wave-uniform: the previous step's PV product is due (deferral only)
   // operand buffers of steps k, k + 1 and (deferral) k - 1
@@ -1302,9 +1297,10 @@ __device__ __forceinline__ void prefill_columns(const PrefillArgs& a, uint8_t* r
     wait_vmcnt<(NS - 2) * SG::NC>();  // the copier: step k + 1 has landed
     lds_barrier();
     if (copier) {
-      // per-lane copy offsets, derived again each step (registers)
+      // per-lane copy offsets (at head size 128 derived again each step: the
+      // step loop there is at its register budget)
       int t = threadIdx.x;
-      asm volatile("" : "+v"(t));
+      if constexpr (D == 128) asm volatile("" : "+v"(t));
       const DmaOffsets<D, COMPACT, FMT> dof = dma_offsets<D, COMPACT, FMT>(a.pool.st, a.pool.skv, t & 63);
       dma_step<D, COMPACT, FMT>(ring + (k % NS) * SG::STAGE, a.pool, nxt, h, (k + NS) * kStep, dof);
     }
