@@ -39,9 +39,13 @@ __global__ __launch_bounds__(256) void read_stream_kernel(const u32x4* __restric
 // its four waves take pages p0 + w, p0 + w + 4, ... and each reads a page's
 // K slab and V slab (slab_bytes contiguous bytes each: page rows are
 // contiguous), 16 bytes per lane and load, kPagesInFlight pages at a time.
+// CPL 16-byte chunks per lane and slab: 2 (slabs of up to 2 KB: head sizes
+// up to 128 at 16-row pages) or 4 (up to 4 KB); the smaller form holds half
+// the registers, so it keeps more waves in flight where it suffices.
 constexpr int kPagesInFlight = 4;
-constexpr int kChunksPerLane = 4;  // slabs of up to 4 KB
+constexpr int kMaxChunksPerLane = 4;
 
+template <int CPL>
 __global__ __launch_bounds__(256) void read_pages_kernel(const uint8_t* __restrict__ pool, int64_t stride_block,
                                                          int64_t stride_kv, int64_t stride_head,
                                                          const int32_t* __restrict__ block_table, int max_blocks,
@@ -62,14 +66,14 @@ __global__ __launch_bounds__(256) void read_pages_kernel(const uint8_t* __restri
   const int32_t* row = block_table + (int64_t)b * max_blocks;
   uint32_t acc = 0;
   for (int p = p0 + w; p < p1; p += 4 * kPagesInFlight) {
-    u32x4 v[kPagesInFlight][2][kChunksPerLane];
+    u32x4 v[kPagesInFlight][2][CPL];
 #pragma unroll
     for (int k = 0; k < kPagesInFlight; ++k) {
       const int pk = p + 4 * k;
 #pragma unroll
       for (int kv = 0; kv < 2; ++kv)
 #pragma unroll
-        for (int c = 0; c < kChunksPerLane; ++c) v[k][kv][c] = u32x4{0u, 0u, 0u, 0u};
+        for (int c = 0; c < CPL; ++c) v[k][kv][c] = u32x4{0u, 0u, 0u, 0u};
       if (pk < p1) {
         int64_t id = row[pk];
         id = id < 0 ? 0 : (id >= num_blocks ? num_blocks - 1 : id);
@@ -78,7 +82,7 @@ __global__ __launch_bounds__(256) void read_pages_kernel(const uint8_t* __restri
           const u32x4* src = reinterpret_cast<const u32x4*>(pool + id * stride_block + kv * stride_kv +
                                                             (int64_t)h * stride_head);
 #pragma unroll
-          for (int c = 0; c < kChunksPerLane; ++c)
+          for (int c = 0; c < CPL; ++c)
             if (lane + 64 * c < nc) v[k][kv][c] = src[lane + 64 * c];
         }
       }
@@ -88,7 +92,7 @@ __global__ __launch_bounds__(256) void read_pages_kernel(const uint8_t* __restri
 #pragma unroll
       for (int kv = 0; kv < 2; ++kv)
 #pragma unroll
-        for (int c = 0; c < kChunksPerLane; ++c) {
+        for (int c = 0; c < CPL; ++c) {
           const u32x4 x = v[k][kv][c];
           acc ^= x[0] ^ x[1] ^ x[2] ^ x[3];
         }
@@ -119,12 +123,20 @@ extern "C" int32_t nvfp4kv_probe_read_pages(const void* pool, int64_t num_blocks
   const int64_t grid = (int64_t)num_seqs * num_kv_heads * splits;
   if (pool == nullptr || block_table == nullptr || seq_lens == nullptr || sink == nullptr || splits < 1 ||
       num_blocks < 1 || max_blocks < 1 || num_seqs < 1 || block_size < 1 || num_kv_heads < 1 || slab_bytes < 16 ||
-      slab_bytes % 16 != 0 || slab_bytes > 64 * 16 * kChunksPerLane || (reinterpret_cast<uintptr_t>(pool) % 16) != 0 ||
+      slab_bytes % 16 != 0 || slab_bytes > 64 * 16 * kMaxChunksPerLane || (reinterpret_cast<uintptr_t>(pool) % 16) != 0 ||
       stride_block % 16 != 0 || stride_kv % 16 != 0 || stride_head % 16 != 0 || grid > INT32_MAX ||
       (reinterpret_cast<uintptr_t>(sink) % 4) != 0 || sink_bytes < grid * 16)
     return 1;
-  read_pages_kernel<<<(unsigned)grid, 256, 0, static_cast<hipStream_t>(stream)>>>(
-      static_cast<const uint8_t*>(pool), stride_block, stride_kv, stride_head, block_table, max_blocks, seq_lens,
-      num_kv_heads, splits, block_size, slab_bytes, num_blocks, static_cast<uint32_t*>(sink));
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (slab_bytes <= 64 * 16 * 2)
+    read_pages_kernel<2><<<(unsigned)grid, 256, 0, st>>>(static_cast<const uint8_t*>(pool), stride_block, stride_kv,
+                                                          stride_head, block_table, max_blocks, seq_lens, num_kv_heads,
+                                                          splits, block_size, slab_bytes, num_blocks,
+                                                          static_cast<uint32_t*>(sink));
+  else
+    read_pages_kernel<4><<<(unsigned)grid, 256, 0, st>>>(static_cast<const uint8_t*>(pool), stride_block, stride_kv,
+                                                          stride_head, block_table, max_blocks, seq_lens, num_kv_heads,
+                                                          splits, block_size, slab_bytes, num_blocks,
+                                                          static_cast<uint32_t*>(sink));
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }
