@@ -1361,7 +1361,11 @@ __global__ __launch_bounds__(64 * PrefillGeo<D>::NW) __attribute__((amdgpu_waves
   uint8_t* ring = reinterpret_cast<uint8_t*>(smem);  // [NS] raw steps
   uint8_t* opbuf = ring + NS * SG::STAGE;             // [kOpBufs] operand buffers
 
-  const int h = blockIdx.y;
+  // Dispatch order (x fastest): kv heads, then column blocks from the last
+  // one back (under a causal mask the later columns see the most keys), then
+  // sequences longest first, so the longest jobs start first.
+  const int h = blockIdx.x;
+  const int cb = (int)(gridDim.y - 1 - blockIdx.y);
   const int b = a.longest_first ? prefill_seq_of_rank(a, blockIdx.z, reinterpret_cast<int*>(ring)) : (int)blockIdx.z;
   int q0 = a.cu_q[b], q1 = a.cu_q[b + 1];
   q0 = q0 < 0 ? 0 : (q0 > a.total_q ? a.total_q : q0);
@@ -1370,15 +1374,15 @@ __global__ __launch_bounds__(64 * PrefillGeo<D>::NW) __attribute__((amdgpu_waves
   const int L = clamp_len(a.seq_lens[b], a.max_blocks * a.pool.bs);
   const int ncols = qlen * a.grp;
   constexpr int kCols = PrefillGeo<D>::NW * 16 * NT;  // columns per workgroup
-  if ((int)blockIdx.x * kCols < ncols)
-    prefill_columns<D, NT, COMPACT, FP8OUT, FMT>(a, ring, opbuf, b, h, q0, qlen, L, blockIdx.x * kCols);
+  if (cb * kCols < ncols)
+    prefill_columns<D, NT, COMPACT, FP8OUT, FMT>(a, ring, opbuf, b, h, q0, qlen, L, cb * kCols);
   // The grid is sized from the host's max_q_len hint. If a chunk is longer,
   // the grid's last column block takes the columns past the grid, one
   // 16-column tile per wave at a time (this rarely taken path then needs no
   // more registers than the main one), so a wrong hint costs speed, never
   // rows. The workgroup's waves take the branch and the loop together.
-  if (blockIdx.x == gridDim.x - 1)
-    for (int c0 = gridDim.x * kCols; c0 < ncols; c0 += PrefillGeo<D>::NW * 16)
+  if (cb == (int)gridDim.y - 1)
+    for (int c0 = (int)gridDim.y * kCols; c0 < ncols; c0 += PrefillGeo<D>::NW * 16)
       prefill_columns<D, 1, COMPACT, FP8OUT, FMT>(a, ring, opbuf, b, h, q0, qlen, L, c0);
 }
 
@@ -1402,8 +1406,11 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, int num_seqs, int max_q
   // the actual chunk lengths, so any hint (even 0) gives every row
   const int64_t cols = (int64_t)(max_q_len > 0 ? max_q_len : 1) * a.grp;
   const int64_t per_wg = PrefillGeo<D>::NW * 16 * NT;
-  const int64_t gx = (cols + per_wg - 1) / per_wg;
-  const dim3 grid((unsigned)gx, (unsigned)a.pool.hkv, (unsigned)num_seqs);
+  // column blocks on the grid's y axis (at most 65535; a longer chunk's
+  // remaining columns go to the last block's loop)
+  int64_t gy = (cols + per_wg - 1) / per_wg;
+  gy = gy > 65535 ? 65535 : gy;
+  const dim3 grid((unsigned)a.pool.hkv, (unsigned)gy, (unsigned)num_seqs);
   if (fmt == kFp8E4M3 || fmt == kFp8E5M2) {
     // FP8 rows are copied in 16-byte chunks whatever their stride
     if (fmt == kFp8E4M3)
