@@ -862,10 +862,10 @@ hipError_t launch_decode(const Pool& pool, int head_size, const void* q, int64_t
 
 // ---------------------------------------------------------------------------
 // Chunked prefill. Columns of (sequence b, kv head h) are (token, group head)
-// pairs, token-major; a workgroup owns 64*NT consecutive columns (16*NT per
-// wave) and walks keys 0 .. the last key its columns see, its four waves
-// sharing the dequantisation of each step. No split-K: long chunks already
-// give many workgroups.
+// pairs, token-major; a workgroup owns NW*16*NT consecutive columns (16*NT
+// per wave) and walks keys 0 .. the last key its columns see, its waves
+// sharing the dequantisation of each step. No split along the keys: long
+// chunks already give many workgroups.
 // ---------------------------------------------------------------------------
 struct PrefillArgs {
   Pool pool;
@@ -1198,10 +1198,10 @@ __device__ __forceinline__ void prefill_pv(WaveAttn<D, NT, FMT>& W, uint32_t slo
   if constexpr (WaveAttn<D, NT, FMT>::kMfmaSum) W.sum_ops(p);
 }
 
-// Columns [wg_col, wg_col + 64 NT) of the chunk of sequence b// Columns [wg_col, wg_col + 64 NT) of the chunk of sequence b (first query
-// row q0, qlen rows, L keys) for kv head h: the workgroup's four waves
+// Columns [wg_col, wg_col + NW 16 NT) of the chunk of sequence b (first
+// query row q0, qlen rows, L keys) for kv head h: the workgroup's NW waves
 // share the dequantisation of each 32-key step and each runs its own 16 NT
-// columns' products (see the kernel below).
+// columns' products.
 template <int D, int NT, bool COMPACT, bool FP8OUT, int FMT>
 __device__ __forceinline__ void prefill_columns(const PrefillArgs& a, uint8_t* ring, uint8_t* opbuf, int b, int h,
                                                 int q0, int qlen, int L, int wg_col) {

@@ -967,7 +967,7 @@ __device__ __forceinline__ void mask_step(SubRaw<D, FMT> (&R)[2], int kb, int L,
 namespace nvfp4kv {
 
 // ---------------------------------------------------------------------------
-// Shared operand tiles (prefill). The four waves of a workgroup dequantise a
+// Shared operand tiles (prefill). The waves of a workgroup dequantise a
 // step together: operand e of the step (K chunks e < 2 * KW, in the order
 // (subtile, chunk); then the V^T tiles) is 64 lanes x 16 bytes in the lane
 // layout the MFMA takes, stored at e * 1024 + lane * 16 of an operand
