@@ -699,3 +699,25 @@ def test_decode_from_concurrent_host_threads():
     for t in threads:
         t.join()
     assert not errors, errors[:4]
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("head_size,num_q_heads,num_kv_heads", [(64, 4, 2), (128, 8, 2), (256, 16, 2)])
+def test_prefill_edge_shapes(head_size, num_q_heads, num_kv_heads, causal):
+    """The prefill pipeline at its edges, at every head size (two operand
+    buffers below 256, three with the deferred PV product at 256): chunks
+    with no rows and with one key, keys one below, at and above a 32-key
+    step, a sequence of one step and of many, and chunks whose columns end
+    inside a workgroup's last tile and just past a workgroup boundary
+    (grp x q_len around 128 columns). Every row against the oracle."""
+    lens = [1, 31, 32, 33, 64, 65, 97, 500, 300, 129]
+    qs = [1, 31, 1, 33, 0, 17, 64, 129, 33, 0]
+    w = make_workload(seed=27, name="x", seq_lens=lens, q_lens=qs, num_q_heads=num_q_heads,
+                      num_kv_heads=num_kv_heads, head_size=head_size, block_size=16)
+    d = Dev(w, "HND")
+    d.append_all()
+    out = d.prefill(causal=causal)
+    torch.cuda.synchronize()
+    ref = O.paged_attention(oracle_pool(w), w.query, w.cu_q, w.block_table, w.seq_lens, w.k_scale, w.v_scale,
+                            np.float32(d.sm_scale), head_size, causal=causal)
+    assert_attn_close(out, ref, f"prefill edges D={head_size} causal={causal}")
