@@ -215,7 +215,11 @@ def run_workload(args, name, full, dev):
     if wp is not None:
         qp, btp, slp, cup = bf(wp.query), i32(wp.block_table), i32(wp.seq_lens), i32(wp.cu_q)
         outp = torch.empty((int(wp.cu_q[-1]), Hq, D), dtype=torch.bfloat16, device=dev)
+        outp_grid = torch.empty_like(outp)
         maxq, maxp = int(wp.q_lens.max()), int(wp.seq_lens.max())
+        # the key split's workspace: zero-filled once, its counters are left
+        # at zero by every call
+        wsp = torch.zeros(nvk.prefill_workspace_size(D), dtype=torch.uint8, device=dev)
 
     def do_append(r):
         nvk.append(pools[r], k_new, v_new, s_new, k_scale, v_scale)
@@ -224,7 +228,12 @@ def run_workload(args, name, full, dev):
         nvk.paged_attention_decode(pools[r], qd, btd, sld, maxd, k_scale, v_scale, sm_scale, outd, wsd)
 
     def do_prefill(r):
-        nvk.paged_attention_prefill(pools[r], qp, cup, maxq, btp, slp, maxp, k_scale, v_scale, sm_scale, outp)
+        nvk.paged_attention_prefill(pools[r], qp, cup, maxq, btp, slp, maxp, k_scale, v_scale, sm_scale, outp,
+                                    workspace=wsp)
+
+    def do_prefill_grid(r):
+        # one workgroup per job, no key split (reported beside it)
+        nvk.paged_attention_prefill(pools[r], qp, cup, maxq, btp, slp, maxp, k_scale, v_scale, sm_scale, outp_grid)
 
     def step(r):
         do_append(r)
@@ -263,6 +272,7 @@ def run_workload(args, name, full, dev):
     if wp is not None:
         res["prefill_s"] = T.per_call(do_prefill, copies)
         assert torch.equal(outp, ref_p), "graph replay of prefill differs from eager"
+        res["prefill_grid_s"] = T.per_call(do_prefill_grid, copies)
         pairs = 0
         for b in range(wp.num_seqs):
             L, q = int(wp.seq_lens[b]), int(wp.q_lens[b])
@@ -412,7 +422,7 @@ def run_workload(args, name, full, dev):
             if wp is not None:
                 outp8 = torch.empty_like(outp)
                 t8 = T.per_call(lambda r: nvk.paged_attention_prefill(p8s[r], qp, cup, maxq, btp, slp, maxp, ks8_t,
-                                                                      vs8_t, sm_scale, outp8), n8)
+                                                                      vs8_t, sm_scale, outp8, workspace=wsp), n8)
                 fp8p[kv] = {"prefill_us": round(t8 * 1e6, 2), "time_vs_nvfp4": round(t8 / res["prefill_s"], 3)}
                 del outp8
             del p8s, b8
@@ -472,7 +482,9 @@ def rates(res):
     if "prefill_s" in res:
         tf = res["prefill_flops"] / res["prefill_s"] / 1e12
         out.update({"prefill_us": round(res["prefill_s"] * 1e6, 2), "prefill_tflops": round(tf, 2),
-                    "prefill_pct_of_mfma_peak": round(100 * tf / MFMA_F16_PEAK_TFLOPS, 2)})
+                    "prefill_pct_of_mfma_peak": round(100 * tf / MFMA_F16_PEAK_TFLOPS, 2),
+                    "prefill_kernel": "prefill_plan_kernel + prefill_kernel (key split)",
+                    "prefill_grid_us": round(res["prefill_grid_s"] * 1e6, 2)})
     return out
 
 

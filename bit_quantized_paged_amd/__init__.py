@@ -17,7 +17,8 @@ import torch
 
 __all__ = [
     "NVFP4KVError", "library", "full_dim", "row_bytes", "KV_DTYPES", "kv_dtype_of", "alloc_pool", "append",
-    "dequant_paged", "dequant_pages", "qdq", "decode_workspace_size", "decode_plan", "paged_attention_decode",
+    "dequant_paged", "dequant_pages", "qdq", "decode_workspace_size", "prefill_workspace_size", "decode_plan",
+    "paged_attention_decode",
     "paged_attention_prefill", "fp8_to_bf16", "quant_activations", "quant_activations_scale_bytes",
     "paged_attention_decode_noalloc",
 ]
@@ -27,7 +28,8 @@ LIB_PATH = os.path.join(_HERE, "libnvfp4kv.so")
 
 EXPORTS = [
     "nvfp4_kv_full_dim", "nvfp4_kv_append", "nvfp4_kv_dequant_paged", "nvfp4_kv_dequant_pages", "nvfp4_kv_qdq",
-    "nvfp4_paged_attention_decode_workspace_size", "nvfp4_paged_attention_decode_plan",
+    "nvfp4_paged_attention_decode_workspace_size", "nvfp4_paged_attention_prefill_workspace_size",
+    "nvfp4_paged_attention_decode_plan",
     "nvfp4_paged_attention_decode", "nvfp4_paged_attention_decode_fp8", "nvfp4_fp8_to_bf16",
     "nvfp4_paged_attention_decode_noalloc",
     "nvfp4_paged_attention_prefill_fp8",
@@ -70,6 +72,7 @@ def library():
             "nvfp4_kv_dequant_pages": (_I32, [_DESC, _P, _I32, _P, _P, _P, _I64, _I64, _I64, _I64, _P]),
             "nvfp4_kv_qdq": (_I32, [_P, _I64, _I64, _P, _I64, _I64, _I64, _I32, _I32, _P, _P, _P]),
             "nvfp4_paged_attention_decode_workspace_size": (_SZ, [_I32, _I32, _I32, _I32]),
+            "nvfp4_paged_attention_prefill_workspace_size": (_SZ, [_I32]),
             "nvfp4_paged_attention_decode_plan": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
             "nvfp4_paged_attention_decode": (_I32, [_DESC, _P, _I64, _I64, _I32, _P, _I32, _P, _I32, _I32, _P, _P,
                                                     _F32, _P, _P, _SZ, _P]),
@@ -297,6 +300,11 @@ def decode_workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, he
                                                                       head_size))
 
 
+def prefill_workspace_size(head_size: int) -> int:
+    """Bytes of the key-split prefill's workspace on the current device (0 for a head size not built)."""
+    return int(library().nvfp4_paged_attention_prefill_workspace_size(head_size))
+
+
 DECODE_SPLIT_K, DECODE_PER_PAIR = 0, 1
 
 
@@ -424,22 +432,32 @@ def quant_activations(x, global_scale, swizzled: bool = True, codes=None, scales
 
 
 def paged_attention_prefill(pool, q, cu_seqlens_q, max_q_len, block_table, seq_lens, max_seq_len,
-                            k_scale, v_scale, sm_scale, out, causal: bool = True, o_scale=None) -> None:
+                            k_scale, v_scale, sm_scale, out, causal: bool = True, o_scale=None,
+                            workspace=None) -> None:
     """Chunked prefill: q bf16 [total_q, Hq, D]; cu_seqlens_q int32 [B + 1]. out is
-    bf16 [total_q, Hq, D], or with an output scale ``o_scale`` uint8 FP8-E4M3 codes."""
+    bf16 [total_q, Hq, D], or with an output scale ``o_scale`` uint8 FP8-E4M3 codes.
+    ``workspace`` (uint8, zero-filled once, at least ``prefill_workspace_size(D)``
+    bytes) selects the key split: every workgroup takes an equal share of the steps."""
     d = _desc(pool)
     B = _check_attention_args(d, q, out, block_table, seq_lens, o_scale, k_scale, v_scale)
     _meta(cu_seqlens_q, "cu_seqlens_q", torch.int32)
     _shape(cu_seqlens_q, "cu_seqlens_q", (B + 1,))
     if not cu_seqlens_q.is_contiguous():
         raise ValueError("cu_seqlens_q must be contiguous")
+    ws_ptr, ws_bytes = ctypes.c_void_p(0), 0
+    if workspace is not None:
+        _meta(workspace, "workspace", torch.uint8)
+        if not workspace.is_contiguous():
+            raise ValueError("workspace must be contiguous")
+        ws_ptr, ws_bytes = _ptr(workspace), workspace.numel()
     _devices((pool, "pool"), (q, "q"), (out, "out"), (block_table, "block_table"), (seq_lens, "seq_lens"),
-             (cu_seqlens_q, "cu_seqlens_q"), (k_scale, "k_scale"), (v_scale, "v_scale"), (o_scale, "o_scale"))
+             (cu_seqlens_q, "cu_seqlens_q"), (k_scale, "k_scale"), (v_scale, "v_scale"), (o_scale, "o_scale"),
+             (workspace, "workspace"))
     common = (ctypes.byref(d), _ptr(q), q.stride(0), q.stride(1), q.shape[1], _ptr(cu_seqlens_q), int(max_q_len),
               q.shape[0], _ptr(block_table), block_table.shape[1], _ptr(seq_lens), B,
               int(max_seq_len), _ptr(k_scale), _ptr(v_scale), float(sm_scale), 1 if causal else 0)
     if o_scale is None:
-        _check(library().nvfp4_paged_attention_prefill(*common, _ptr(out), ctypes.c_void_p(0), 0, _stream()))
+        _check(library().nvfp4_paged_attention_prefill(*common, _ptr(out), ws_ptr, ws_bytes, _stream()))
     else:
-        _check(library().nvfp4_paged_attention_prefill_fp8(*common, _ptr(o_scale), _ptr(out), ctypes.c_void_p(0), 0,
+        _check(library().nvfp4_paged_attention_prefill_fp8(*common, _ptr(o_scale), _ptr(out), ws_ptr, ws_bytes,
                                                            _stream()))

@@ -361,8 +361,6 @@ static nvfp4kv_status prefill_impl(const nvfp4kv_cache* cache, const void* q, in
                                              const float* k_scale, const float* v_scale, float sm_scale,
                                              int32_t causal, const float* o_scale, void* out, void* workspace,
                                              size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   nvfp4kv::Pool p;
   int fmt = 0;
   nvfp4kv_status s = check_cache(cache, p, &fmt);
@@ -382,11 +380,27 @@ static nvfp4kv_status prefill_impl(const nvfp4kv_cache* cache, const void* q, in
   if (!cu_seqlens_q || !block_table || !seq_lens) return fail(NVFP4KV_INVALID_ARGUMENT, "metadata pointer is NULL");
   if (!k_scale || !v_scale) return fail(NVFP4KV_INVALID_ARGUMENT, "k_scale/v_scale is NULL");
   if (out == nullptr || !aligned(out, 16)) return fail(NVFP4KV_INVALID_ARGUMENT, "out must be a 16-byte aligned pointer");
+  if (workspace == nullptr && workspace_bytes != 0)
+    return fail(NVFP4KV_INVALID_ARGUMENT, "workspace is NULL but workspace_bytes is not 0");
+  if (workspace != nullptr) {
+    if (!aligned(workspace, 256)) return fail(NVFP4KV_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+    if (workspace_bytes < nvfp4kv::prefill_workspace_bytes(cache->head_size))
+      return fail(NVFP4KV_INVALID_ARGUMENT,
+                  "workspace smaller than nvfp4_paged_attention_prefill_workspace_size(head_size)");
+    if (num_seqs > nvfp4kv::kPrefillSplitSeqsMax)
+      return fail(NVFP4KV_INVALID_ARGUMENT, "num_seqs must be <= 4096 with a workspace");
+  }
   return hip_status(nvfp4kv::launch_prefill(p, cache->head_size, q, q_stride_token, q_stride_head, num_q_heads,
                                             cu_seqlens_q, max_q_len, total_q, block_table, max_blocks_per_seq,
                                             seq_lens, num_seqs, max_seq_len, k_scale, v_scale, sm_scale,
-                                            causal ? 1 : 0, o_scale, out, fmt, static_cast<hipStream_t>(stream)),
+                                            causal ? 1 : 0, o_scale, out, fmt, workspace,
+                                            static_cast<hipStream_t>(stream)),
                     "nvfp4_paged_attention_prefill launch");
+}
+
+size_t nvfp4_paged_attention_prefill_workspace_size(int32_t head_size) {
+  if (head_size != 64 && head_size != 128 && head_size != 256) return 0;
+  return nvfp4kv::prefill_workspace_bytes(head_size);
 }
 
 nvfp4kv_status nvfp4_paged_attention_prefill(const nvfp4kv_cache* cache, const void* q, int64_t q_stride_token,

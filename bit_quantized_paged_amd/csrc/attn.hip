@@ -867,6 +867,8 @@ hipError_t launch_decode(const Pool& pool, int head_size, const void* q, int64_t
 // sharing the dequantisation of each step. No split along the keys: long
 // chunks already give many workgroups.
 // ---------------------------------------------------------------------------
+struct PrefillPlanRow;
+
 struct PrefillArgs {
   Pool pool;
   const uint16_t* q;
@@ -886,7 +888,42 @@ struct PrefillArgs {
   const float* o_scale;  // per-tensor FP8 output scale, or null
   int num_seqs;
   int longest_first;     // blockIdx.z is a rank in order of decreasing length (num_seqs <= kPrefillRankMax)
+  const PrefillPlanRow* plan;  // key split: the plan of every rank (null: no split)
+  uint32_t* ws_cnt;            // key split: arrival counters of cut jobs, zero between calls
+  float* ws_part;              // key split: part records (PrefillPartGeo<D>::BYTES each)
 };
+
+// Query rows [q0, q0 + qlen) of the batch that are sequence b's chunk, and
+// its key count L (cu_seqlens_q clamped to [0, total_q], lengths to the
+// block table's capacity).
+__device__ __forceinline__ void prefill_seq_geom(const PrefillArgs& a, int b, int& q0, int& qlen, int& L) {
+  int x0 = a.cu_q[b], x1 = a.cu_q[b + 1];
+  x0 = x0 < 0 ? 0 : (x0 > a.total_q ? a.total_q : x0);
+  x1 = x1 < x0 ? x0 : (x1 > a.total_q ? a.total_q : x1);
+  q0 = x0;
+  qlen = x1 - x0;
+  L = clamp_len(a.seq_lens[b], a.max_blocks * a.pool.bs);
+}
+
+// The same, as wave-uniform values (scalar registers).
+__device__ __forceinline__ void prefill_seq_geom_u(const PrefillArgs& a, int b, int& q0, int& qlen, int& L) {
+  prefill_seq_geom(a, b, q0, qlen, L);
+  q0 = __builtin_amdgcn_readfirstlane(q0);
+  qlen = __builtin_amdgcn_readfirstlane(qlen);
+  L = __builtin_amdgcn_readfirstlane(L);
+}
+
+// 32-key steps a workgroup of kCols columns starting at column wg_col walks:
+// up to the last key its last column sees (all L keys without the causal
+// mask).
+template <int kCols>
+__device__ __forceinline__ int prefill_job_steps(int causal, int grp, int L, int qlen, int wg_col) {
+  const int ncols = qlen * grp;
+  const int wg_last = ((wg_col + kCols < ncols) ? wg_col + kCols : ncols) - 1;
+  int kmax = causal ? L - qlen + wg_last / grp + 1 : L;
+  kmax = kmax > L ? L : (kmax < 0 ? 0 : kmax);
+  return ceil_div(kmax, kStep);
+}
 
 // Batches of up to this many sequences are walked longest first: the grid's
 // sequence axis is a rank, so the longest sequences' workgroups are
@@ -1195,16 +1232,38 @@ __device__ __forceinline__ void prefill_pv(WaveAttn<D, NT, FMT>& W, uint32_t slo
       for (int n = 0; n < NT; ++n)
         W.acc[n][g * GS + e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(t[e], p[n], W.acc[n][g * GS + e], 0, 0, 0);
   }
-  if constexpr (WaveAttn<D, NT, FMT>::kMfmaSum) W.sum_ops(p);
+  if constexpr (WaveAttn<D, NT>::kMfmaSum) W.sum_ops(p);
 }
 
+// One workgroup's part of a job (sequence, column block, kv head) under the
+// key split: the job's steps are cut into n consecutive ranges, each its own
+// workgroup; this one is part self. Part p leaves its state in record rec0 +
+// p of the workspace, and arrival counter cnt counts the parts done. With
+// n = 1 the workgroup writes the output itself.
+struct PrefillPart {
+  int n;
+  int self;
+  int rec0;
+  int cnt;
+};
+
+template <int D, int NT>
+__device__ __forceinline__ void prefill_put_part(const PrefillArgs& a, const WaveAttn<D, NT>& W, const PrefillPart& pt, int w, int lane);
+template <int D, int NT>
+__device__ __forceinline__ void prefill_merge_parts(const PrefillArgs& a, WaveAttn<D, NT>& W, const PrefillPart& pt, int w, int lane);
+
 // Columns [wg_col, wg_col + NW 16 NT) of the chunk of sequence b (first
-// query row q0, qlen rows, L keys) for kv head h: the workgroup's NW waves
-// share the dequantisation of each 32-key step and each runs its own 16 NT
-// columns' products.
+// query row q0, qlen rows, L keys) for kv head h, over the job's steps
+// [k_lo, k_hi) (clamped to the steps the columns see): the workgroup's NW
+// waves share the dequantisation of each 32-key step and each runs its own
+// 16 NT columns' products. A part of a split job (pt.n > 1) leaves its state
+// in the workspace; the last part to arrive merges them all and writes the
+// output. s_flag: one int of LDS for the arrival result (the ring's first
+// word: the ring is idle once the step loop is done).
 template <int D, int NT, bool COMPACT, bool FP8OUT, int FMT>
 __device__ __forceinline__ void prefill_columns(const PrefillArgs& a, uint8_t* ring, uint8_t* opbuf, int b, int h,
-                                                int q0, int qlen, int L, int wg_col) {
+                                                int q0, int qlen, int L, int wg_col, int k_lo, int k_hi,
+                                                const PrefillPart& pt, int* s_flag) {
   using G = Geo<D>;
   using SG = StageGeo<D, COMPACT, FMT>;
   using OG = OpGeo<D>;
@@ -1235,12 +1294,12 @@ __device__ __forceinline__ void prefill_columns(const PrefillArgs& a, uint8_t* r
     lim = lim > L - 1 ? L - 1 : lim;
     W.lim[n] = valid ? lim : -1;
   }
-  // keys the workgroup streams: up to the last visible key of its last column
+  // the steps of this range: the job's steps (up to the last visible key of
+  // its last column) within [k_lo, k_hi)
   constexpr int kWgCols = PrefillGeo<D>::NW * 16 * NT;
-  const int wg_last = ((wg_col + kWgCols < ncols) ? wg_col + kWgCols : ncols) - 1;
-  int kmax = a.causal ? L - qlen + wg_last / grp + 1 : L;
-  kmax = kmax > L ? L : (kmax < 0 ? 0 : kmax);
-  const int steps = ceil_div(kmax, kStep);
+  const int job_steps = prefill_job_steps<kWgCols>(a.causal, grp, L, qlen, wg_col);
+  const int kend = k_hi < job_steps ? k_hi : job_steps;
+  const int kbeg = k_lo < kend ? k_lo : kend;
   // keys this wave's columns see (none if it has no column), and below
   // min_full every valid column of the wave sees every key
   const bool has_cols = col_base < ncols;
@@ -1267,18 +1326,20 @@ __device__ __forceinline__ void prefill_columns(const PrefillArgs& a, uint8_t* r
   // dequantised in iteration k - 1) is free, and so is the buffer that step
   // k + 1 takes (it held step k - 2, or step k - 1 without deferral, both
   // last read in iteration k - 1).
+  // Ring stage and operand buffer indices count from kbeg.
   const bool copier = w == 0;
   if (copier) {
     const DmaOffsets<D, COMPACT, FMT> dof = dma_offsets<D, COMPACT, FMT>(a.pool.st, a.pool.skv, lane);
 #pragma unroll
     for (int s = 0; s < NS; ++s)
-      dma_step<D, COMPACT, FMT>(ring + s * SG::STAGE, a.pool, ids_for_step(bt_row, s, steps, L, a.max_blocks, a.pool), h,
-                                s * kStep, dof);
+      dma_step<D, COMPACT, FMT>(ring + s * SG::STAGE, a.pool,
+                                ids_for_step(bt_row, kbeg + s, kend, L, a.max_blocks, a.pool), h, (kbeg + s) * kStep,
+                                dof);
   }
-  StepIds nxt = ids_for_step(bt_row, NS, steps, L, a.max_blocks, a.pool);
-  wait_vmcnt<(NS - 1) * SG::NC>();  // the copier: step 0 has landed (others: no-op)
+  StepIds nxt = ids_for_step(bt_row, kbeg + NS, kend, L, a.max_blocks, a.pool);
+  wait_vmcnt<(NS - 1) * SG::NC>();  // the copier: step kbeg has landed (others: no-op)
   lds_barrier();
-  if (steps > 0) prefill_dequant<D, FMT, PrefillGeo<D>::NW>(ring, ll, 0, L, j, w, op_lane);
+  if (kbeg < kend) prefill_dequant<D, FMT, PrefillGeo<D>::NW>(ring, ll, kbeg * kStep, L, j, w, op_lane);
   constexpr bool kDefer = PrefillGeo<D>::kDeferPV;
   // With the deferred PV product (head size 256, one workgroup per CU) the
   // waves dequantise after their products, which then queue on the matrix
@@ -1293,29 +1354,30 @@ __device__ __forceinline__ void prefill_columns(const PrefillArgs& a, uint8_t* r
   bool pv_pending = false;  // wave-uniform: the previous step's PV product is due (deferral only)
   // operand buffers of steps k, k + 1 and (deferral) k - 1
   uint32_t buf_cur = 0, buf_next = OG::BYTES, buf_prev = 2 * OG::BYTES;
-  for (int k = 0; k < steps; ++k) {
+  for (int k = kbeg; k < kend; ++k) {
     wait_vmcnt<(NS - 2) * SG::NC>();  // the copier: step k + 1 has landed
     lds_barrier();
+    const int kk = k - kbeg;
     if (copier) {
       // per-lane copy offsets (at head size 128 derived again each step: the
       // step loop there is at its register budget)
       int t = threadIdx.x;
       if constexpr (D == 128) asm volatile("" : "+v"(t));
       const DmaOffsets<D, COMPACT, FMT> dof = dma_offsets<D, COMPACT, FMT>(a.pool.st, a.pool.skv, t & 63);
-      dma_step<D, COMPACT, FMT>(ring + (k % NS) * SG::STAGE, a.pool, nxt, h, (k + NS) * kStep, dof);
+      dma_step<D, COMPACT, FMT>(ring + (kk % NS) * SG::STAGE, a.pool, nxt, h, (k + NS) * kStep, dof);
     }
-    nxt = ids_for_step(bt_row, k + NS + 1, steps, L, a.max_blocks, a.pool);
+    nxt = ids_for_step(bt_row, k + NS + 1, kend, L, a.max_blocks, a.pool);
     const int kb = k * kStep;
     const bool mine = kb < kw;
     f4 sc[2][NT];
-    const bool deq = k + 1 < steps;
+    const bool deq = k + 1 < kend;
     if (deq_first && deq)
-      prefill_dequant<D, FMT, PrefillGeo<D>::NW>(ring + ((k + 1) % NS) * SG::STAGE, ll, kb + kStep, L, j, w,
+      prefill_dequant<D, FMT, PrefillGeo<D>::NW>(ring + ((kk + 1) % NS) * SG::STAGE, ll, kb + kStep, L, j, w,
                                                   op_lane + buf_next);
     if (mine) prefill_scores(W, op_lane + buf_cur, sc);
     if (kDefer && pv_pending) prefill_pv(W, op_lane + buf_prev, p);
     if (!deq_first && deq)
-      prefill_dequant<D, FMT, PrefillGeo<D>::NW>(ring + ((k + 1) % NS) * SG::STAGE, ll, kb + kStep, L, j, w,
+      prefill_dequant<D, FMT, PrefillGeo<D>::NW>(ring + ((kk + 1) % NS) * SG::STAGE, ll, kb + kStep, L, j, w,
                                                   op_lane + buf_next);
     if (mine) {
       W.softmax(sc, kb, j, kb + kStep > min_full, p);
@@ -1336,6 +1398,31 @@ __device__ __forceinline__ void prefill_columns(const PrefillArgs& a, uint8_t* r
   if (kDefer && pv_pending) prefill_pv(W, op_lane + buf_prev, p);
   wait_vmcnt<0>();
 
+  // (split jobs run the main column tiling only)
+  if (NT == PrefillGeo<D>::NT && pt.n > 1) {
+    // Every part leaves its state; the last to arrive (the count before its
+    // increment is n - 1) merges the n states in part order, so the result
+    // does not depend on the order of arrival, and resets the counter. The
+    // states travel through agent-coherent stores and loads (they bypass the
+    // per-XCD L2), so the hand-off needs every store complete before the
+    // counter moves, not an L2 flush.
+    if constexpr (NT == PrefillGeo<D>::NT) prefill_put_part<D, NT>(a, W, pt, w, lane);
+    wait_stores();
+    __syncthreads();
+    if (threadIdx.x == 0)
+      *s_flag = (__hip_atomic_fetch_add(&a.ws_cnt[pt.cnt], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                 (uint32_t)(pt.n - 1))
+                    ? 1
+                    : 0;
+    __syncthreads();
+    const bool last = *s_flag != 0;
+    __syncthreads();  // every wave has read the flag before the ring is written again
+    if (!last) return;
+    if constexpr (NT == PrefillGeo<D>::NT) prefill_merge_parts<D, NT>(a, W, pt, w, lane);
+    if (threadIdx.x == 0)
+      __hip_atomic_store(&a.ws_cnt[pt.cnt], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
   const float gv = *a.v_scale;
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
@@ -1352,6 +1439,291 @@ __device__ __forceinline__ void prefill_columns(const PrefillArgs& a, uint8_t* r
   }
 }
 
+// ---------------------------------------------------------------------------
+// Key split of the prefill grid. The grid's dispatch order stays: kv heads,
+// then column blocks from the last one back, then sequences longest first,
+// so the workgroups of one sequence run side by side and read the same keys
+// from the same L2 (measured at chunked_prefill: 94% L2 hits in this order
+// against 13-20% when every workgroup took an equal share of one line of all
+// the jobs' steps). A job of the sequence of rank r is cut into P_r
+// consecutive key ranges, each its own workgroup: grid z runs over slices,
+// the P_r parts of rank 0, then those of rank 1, ..., so a rank's parts run
+// side by side too, and the slices past the last part (the grid holds as
+// many as the records could need) are empty and come last. P_r is guided by the
+// work left: the parts are about max(kPrefillMinPart, 2 R / (3 slots))
+// steps, R the steps of ranks r .. last and slots the workgroups the device
+// holds at once, so the long early ranks stay whole and the last rounds are
+// cut fine enough to end together. Cut jobs need part records; when the
+// tail's records would exceed the workspace's, the earlier of those ranks
+// stay whole, and so do they when the cut ranks' extra slices would exceed
+// the grid's. One workgroup (prefill_plan_kernel) derives the slices, with
+// each rank's sequence, P_r and record and counter bases, into a table the
+// prefill workgroups read.
+// ---------------------------------------------------------------------------
+constexpr int kPrefillParts = 3;     // parts per job at most
+constexpr int kPrefillMinPart = 32;  // steps
+
+struct PrefillPlanRow {  // one grid z slice
+  int32_t seq;       // sequence of the slice's rank
+  int32_t parts;     // P_r (0: an empty slice)
+  int32_t part;      // which part of the rank's jobs
+  int32_t rec_base;  // first part record of the rank's cut jobs
+  int32_t cnt_base;  // first arrival counter of the rank's cut jobs
+  int32_t pad[3];
+};
+
+// A part's state in the workspace, lane-major so that every store and load
+// is a whole 64-lane row: per (wave, column tile, accumulator quad) the
+// lanes' 16-byte O^T quads, then per (wave, column tile) the lanes' (running
+// max, running sum) pairs.
+template <int D>
+struct PrefillPartGeo {
+  static constexpr int NW = PrefillGeo<D>::NW, NT = PrefillGeo<D>::NT, DPL = Geo<D>::DPL;
+  static constexpr int ACC_BYTES = NW * NT * DPL * 64 * 16;
+  static constexpr int BYTES = ACC_BYTES + NW * NT * 64 * 8;
+  static_assert(BYTES % 256 == 0, "records stay 256-byte aligned");
+};
+
+
+template <int D>
+__device__ __forceinline__ rsrc_t prefill_part_rsrc(const PrefillArgs& a, const PrefillPart& pt, int p) {
+  using PG = PrefillPartGeo<D>;
+  return make_rsrc(reinterpret_cast<const uint8_t*>(a.ws_part) + (int64_t)(pt.rec0 + p) * PG::BYTES, PG::BYTES);
+}
+
+template <int D, int NT>
+__device__ __forceinline__ void prefill_put_part(const PrefillArgs& a, const WaveAttn<D, NT>& W, const PrefillPart& pt, int w, int lane) {
+  using PG = PrefillPartGeo<D>;
+  static_assert(NT == PG::NT, "split jobs use the main column tiling");
+  constexpr int DPL = Geo<D>::DPL;
+  const rsrc_t r = prefill_part_rsrc<D>(a, pt, pt.self);
+#pragma unroll
+  for (int n = 0; n < NT; ++n)
+#pragma unroll
+    for (int t = 0; t < DPL; ++t)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, W.acc[n][t]), r,
+                                             (uint32_t)((((w * NT + n) * DPL + t) * 64 + lane) * 16), 0, 16 /* sc1 */);
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    float lv;
+    if constexpr (WaveAttn<D, NT>::kMfmaSum) lv = W.lacc[n][0];
+    else lv = W.l[n];
+    // two 4-byte stores: a pair built from W.m[n] would be read as one
+    // 8-byte load across the array, which keeps W.m out of registers
+    const uint32_t off = (uint32_t)(PG::ACC_BYTES + ((w * NT + n) * 64 + lane) * 8);
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, W.m[n]), r, off, 0, 16 /* sc1 */);
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, lv), r, off + 4, 0, 16 /* sc1 */);
+  }
+}
+
+// The job's state from its n parts, in part order: the maximum over the
+// parts' running maxima, then the sum of each part's accumulators and
+// running sum weighted by 2^(its max - that maximum). Each lane merges its
+// own entries (every part ran the same columns on the same lanes).
+template <int D, int NT>
+__device__ __forceinline__ void prefill_merge_parts(const PrefillArgs& a, WaveAttn<D, NT>& W, const PrefillPart& pt, int w, int lane) {
+  using PG = PrefillPartGeo<D>;
+  constexpr int DPL = Geo<D>::DPL;
+  float M[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) M[n] = -__builtin_inff();
+  for (int p = 0; p < pt.n; ++p) {
+    const rsrc_t r = prefill_part_rsrc<D>(a, pt, p);
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const u32x2 ml = __builtin_amdgcn_raw_buffer_load_b64(r, (uint32_t)(PG::ACC_BYTES + ((w * NT + n) * 64 + lane) * 8),
+                                                            0, 16 /* sc1 */);
+      M[n] = __builtin_fmaxf(M[n], __uint_as_float(ml[0]));
+    }
+  }
+  float lt[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    lt[n] = 0.0f;
+#pragma unroll
+    for (int t = 0; t < DPL; ++t) W.acc[n][t] = f4{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int p = 0; p < pt.n; ++p) {
+    const rsrc_t r = prefill_part_rsrc<D>(a, pt, p);
+    u32x2 ml[NT];
+    f4 v[NT][DPL];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      ml[n] = __builtin_amdgcn_raw_buffer_load_b64(r, (uint32_t)(PG::ACC_BYTES + ((w * NT + n) * 64 + lane) * 8), 0,
+                                                   16 /* sc1 */);
+#pragma unroll
+      for (int t = 0; t < DPL; ++t)
+        v[n][t] = __builtin_bit_cast(
+            f4, __builtin_amdgcn_raw_buffer_load_b128(r, (uint32_t)((((w * NT + n) * DPL + t) * 64 + lane) * 16), 0,
+                                                      16 /* sc1 */));
+    }
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const float mp = __uint_as_float(ml[n][0]);
+      const float f = (mp == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mp - M[n]);
+      lt[n] += f * __uint_as_float(ml[n][1]);
+#pragma unroll
+      for (int t = 0; t < DPL; ++t) W.acc[n][t] += f * v[n][t];
+    }
+  }
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    W.m[n] = M[n];
+    if constexpr (WaveAttn<D, NT>::kMfmaSum) W.lacc[n] = f4{lt[n], lt[n], lt[n], lt[n]};
+    else W.l[n] = lt[n];
+  }
+}
+
+__device__ __forceinline__ int64_t wave_incl_scan64(int64_t v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int64_t t = __shfl_up(v, d);
+    if (lane >= d) v += t;
+  }
+  return v;
+}
+
+template <int NW>
+__device__ __forceinline__ int64_t block_excl_scan64(int64_t v, int64_t* s_red, int64_t& total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t incl = wave_incl_scan64(v);
+  if (lane == 63) s_red[w] = incl;
+  __syncthreads();
+  int64_t off = 0;
+  total = 0;
+#pragma unroll
+  for (int k = 0; k < NW; ++k) {
+    const int64_t t = s_red[k];
+    off += (k < w) ? t : 0;
+    total += t;
+  }
+  __syncthreads();
+  return incl - v + off;
+}
+
+// The plan (one workgroup of 1024 threads). LDS: per rank its work (int64),
+// sequence, longest job, column blocks, and the lengths the ranking reads.
+constexpr int kPlanThreads = 1024;
+
+__host__ __device__ inline size_t prefill_plan_lds_bytes(int B) {
+  return (size_t)B * 8 + (size_t)B * 4 * 4 + (kPlanThreads / 64) * 8 + 16;
+}
+
+template <int D>
+__global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(PrefillArgs a, PrefillPlanRow* plan, int slots,
+                                                                    int rec_cap, int extra_cap) {
+  constexpr int kCols = PrefillGeo<D>::kCols;
+  constexpr int NWP = kPlanThreads / 64;
+  extern __shared__ __align__(16) char smem[];
+  const int B = a.num_seqs;
+  const int hkv = a.pool.hkv;
+  int64_t* s_w = reinterpret_cast<int64_t*>(smem);  // [B] work of rank r
+  int* s_len = reinterpret_cast<int*>(s_w + B);     // [B] clamped length of sequence b
+  int* s_seq = s_len + B;                           // [B] sequence of rank r
+  int* s_nmax = s_seq + B;                          // [B] steps of rank r's longest job
+  int* s_nblk = s_nmax + B;                         // [B] column blocks of rank r
+  int64_t* s_red = reinterpret_cast<int64_t*>(s_nblk + B);  // [NWP] (offset 24 B: 8-byte aligned)
+
+  const int cap = a.max_blocks * a.pool.bs;
+  for (int t = threadIdx.x; t < B; t += kPlanThreads) s_len[t] = clamp_len(a.seq_lens[t], cap);
+  __syncthreads();
+  // ranks: longest first, ties in index order (the order prefill_seq_of_rank
+  // gives); index order for batches the grid does not rank
+  for (int t = threadIdx.x; t < B; t += kPlanThreads) {
+    int rank = t;
+    if (a.longest_first) {
+      const int kt = s_len[t];
+      rank = 0;
+      for (int u = 0; u < B; ++u) {
+        const int ku = s_len[u];
+        rank += (ku > kt || (ku == kt && u < t)) ? 1 : 0;
+      }
+    }
+    s_seq[rank] = t;
+  }
+  __syncthreads();
+  // each thread a contiguous run of ranks
+  const int per = (B + kPlanThreads - 1) / kPlanThreads;
+  const int r0 = threadIdx.x * per;
+  const int r1 = (r0 + per < B) ? r0 + per : B;
+  int64_t loc = 0;
+  for (int r = r0; r < r1; ++r) {
+    int q0, qlen, L;
+    prefill_seq_geom(a, s_seq[r], q0, qlen, L);
+    const int nblk = ceil_div(qlen * a.grp, kCols);
+    int64_t work = 0;
+    int nmax = 0;
+    for (int cb = 0; cb < nblk; ++cb) {
+      const int n = max(1, prefill_job_steps<kCols>(a.causal, a.grp, L, qlen, cb * kCols));
+      work += n;
+      nmax = n > nmax ? n : nmax;
+    }
+    s_w[r] = work * hkv;
+    s_nmax[r] = nmax;
+    s_nblk[r] = nblk;
+    loc += work * hkv;
+  }
+  int64_t total;
+  int64_t run = block_excl_scan64<NWP>(loc, s_red, total);
+  // P_r from the work of ranks r .. last
+  constexpr int kPer = kPrefillSplitSeqsMax / kPlanThreads;
+  static_assert(kPer * kPlanThreads == kPrefillSplitSeqsMax, "ranks per thread");
+  int P[kPer];
+  int64_t rec_loc = 0;
+  for (int r = r0; r < r1; ++r) {
+    const int64_t rest = total - run;  // ranks r .. last
+    run += s_w[r];
+    int64_t part = (2 * rest + 3 * (int64_t)slots - 1) / (3 * (int64_t)slots);
+    part = part < kPrefillMinPart ? kPrefillMinPart : part;
+    int pr = (int)((s_nmax[r] + part - 1) / part);
+    pr = pr < 1 ? 1 : (pr > kPrefillParts ? kPrefillParts : pr);
+    P[r - r0] = pr;
+    rec_loc += pr > 1 ? (int64_t)s_nblk[r] * hkv * pr : 0;
+  }
+  // tail first: a rank is cut only if its records and extra slices and those
+  // of every later cut rank fit in rec_cap and extra_cap
+  int64_t ext_loc = 0;
+  for (int r = r0; r < r1; ++r) ext_loc += P[r - r0] - 1;
+  int64_t rec_total, ext_total;
+  int64_t rec_run = block_excl_scan64<NWP>(rec_loc, s_red, rec_total);
+  int64_t ext_run = block_excl_scan64<NWP>(ext_loc, s_red, ext_total);
+  int64_t rec_kept = 0, cnt_kept = 0, ext_kept = 0;
+  for (int r = r0; r < r1; ++r) {
+    const int64_t rec = P[r - r0] > 1 ? (int64_t)s_nblk[r] * hkv * P[r - r0] : 0;
+    const int64_t ext = P[r - r0] - 1;
+    if (rec_total - rec_run > rec_cap || ext_total - ext_run > extra_cap) P[r - r0] = 1;  // ranks r .. last
+    rec_run += rec;
+    ext_run += ext;
+    rec_kept += P[r - r0] > 1 ? (int64_t)s_nblk[r] * hkv * P[r - r0] : 0;
+    cnt_kept += P[r - r0] > 1 ? (int64_t)s_nblk[r] * hkv : 0;
+    ext_kept += P[r - r0] - 1;
+  }
+  int64_t t1, t2, used_extra;
+  int64_t rec_base = block_excl_scan64<NWP>(rec_kept, s_red, t1);
+  int64_t cnt_base = block_excl_scan64<NWP>(cnt_kept, s_red, t2);
+  int64_t z = block_excl_scan64<NWP>(ext_kept, s_red, used_extra) + r0;  // first slice of rank r0
+  for (int r = r0; r < r1; ++r) {
+    PrefillPlanRow row = {};
+    row.seq = s_seq[r];
+    row.parts = P[r - r0];
+    row.rec_base = (int32_t)rec_base;
+    row.cnt_base = (int32_t)cnt_base;
+    for (int p = 0; p < row.parts; ++p) {
+      row.part = p;
+      plan[z + p] = row;
+    }
+    z += row.parts;
+    if (row.parts > 1) {
+      rec_base += (int64_t)s_nblk[r] * hkv * row.parts;
+      cnt_base += (int64_t)s_nblk[r] * hkv;
+    }
+  }
+  // the slices past the last part: empty
+  const PrefillPlanRow none = {};
+  for (int64_t e = B + used_extra + threadIdx.x; e < (int64_t)B + extra_cap; e += kPlanThreads) plan[e] = none;
+}
+
 template <int D, int NT, bool COMPACT, bool FP8OUT, int FMT>
 __global__ __launch_bounds__(64 * PrefillGeo<D>::NW) __attribute__((amdgpu_waves_per_eu(PrefillOcc<D, COMPACT, FP8OUT, FMT>::waves))) void prefill_kernel(
     PrefillArgs a) {
@@ -1363,27 +1735,53 @@ __global__ __launch_bounds__(64 * PrefillGeo<D>::NW) __attribute__((amdgpu_waves
 
   // Dispatch order (x fastest): kv heads, then column blocks from the last
   // one back (under a causal mask the later columns see the most keys), then
-  // sequences longest first, so the longest jobs start first.
+  // sequences longest first, so the longest jobs start first. With the key
+  // split, grid z runs over the plan's slices (a rank's parts in turn; an
+  // empty slice has nothing to do).
   const int h = blockIdx.x;
   const int cb = (int)(gridDim.y - 1 - blockIdx.y);
-  const int b = a.longest_first ? prefill_seq_of_rank(a, blockIdx.z, reinterpret_cast<int*>(ring)) : (int)blockIdx.z;
-  int q0 = a.cu_q[b], q1 = a.cu_q[b + 1];
-  q0 = q0 < 0 ? 0 : (q0 > a.total_q ? a.total_q : q0);
-  q1 = q1 < q0 ? q0 : (q1 > a.total_q ? a.total_q : q1);
-  const int qlen = q1 - q0;
-  const int L = clamp_len(a.seq_lens[b], a.max_blocks * a.pool.bs);
+  int b, parts = 1, part = 0, rec_base = 0, cnt_base = 0;
+  if (a.plan != nullptr) {
+    const PrefillPlanRow row = a.plan[blockIdx.z];
+    parts = __builtin_amdgcn_readfirstlane(row.parts);
+    if (parts == 0) return;
+    part = __builtin_amdgcn_readfirstlane(row.part);
+    b = __builtin_amdgcn_readfirstlane(row.seq);
+    rec_base = __builtin_amdgcn_readfirstlane(row.rec_base);
+    cnt_base = __builtin_amdgcn_readfirstlane(row.cnt_base);
+  } else {
+    b = a.longest_first ? prefill_seq_of_rank(a, blockIdx.z, reinterpret_cast<int*>(ring)) : (int)blockIdx.z;
+  }
+  int q0, qlen, L;
+  prefill_seq_geom(a, b, q0, qlen, L);
   const int ncols = qlen * a.grp;
   constexpr int kCols = PrefillGeo<D>::NW * 16 * NT;  // columns per workgroup
-  if (cb * kCols < ncols)
-    prefill_columns<D, NT, COMPACT, FP8OUT, FMT>(a, ring, opbuf, b, h, q0, qlen, L, cb * kCols);
+  const PrefillPart whole = {1, 0, 0, 0};
+  if (cb * kCols < ncols) {
+    int k_lo = 0, k_hi = INT32_MAX;
+    PrefillPart pt = whole;
+    if (parts > 1) {
+      // part p of the job's steps; record (cb hkv + h) P + p and counter
+      // cb hkv + h of the rank's block
+      const int n = prefill_job_steps<kCols>(a.causal, a.grp, L, qlen, cb * kCols);
+      k_lo = (int)((int64_t)n * part / parts);
+      k_hi = (int)((int64_t)n * (part + 1) / parts);
+      pt.n = parts;
+      pt.self = part;
+      pt.rec0 = rec_base + (cb * a.pool.hkv + h) * parts;
+      pt.cnt = cnt_base + cb * a.pool.hkv + h;
+    }
+    prefill_columns<D, NT, COMPACT, FP8OUT, FMT>(a, ring, opbuf, b, h, q0, qlen, L, cb * kCols, k_lo, k_hi, pt,
+                                                 reinterpret_cast<int*>(ring));
+  }
   // The grid is sized from the host's max_q_len hint. If a chunk is longer,
   // the grid's last column block takes the columns past the grid, one
   // 16-column tile per wave at a time (this rarely taken path then needs no
   // more registers than the main one), so a wrong hint costs speed, never
   // rows. The workgroup's waves take the branch and the loop together.
-  if (cb == (int)gridDim.y - 1)
+  if (cb == (int)gridDim.y - 1 && part == 0)
     for (int c0 = (int)gridDim.y * kCols; c0 < ncols; c0 += PrefillGeo<D>::NW * 16)
-      prefill_columns<D, 1, COMPACT, FP8OUT, FMT>(a, ring, opbuf, b, h, q0, qlen, L, c0);
+      prefill_columns<D, 1, COMPACT, FP8OUT, FMT>(a, ring, opbuf, b, h, q0, qlen, L, c0, 0, INT32_MAX, whole, nullptr);
 }
 
 template <int D, bool COMPACT, int FMT>
@@ -1400,17 +1798,24 @@ static void launch_prefill_fp8(const PrefillArgs& a, const dim3& grid, hipStream
     prefill_kernel<D, NT, false, true, FMT><<<grid, 64 * PrefillGeo<D>::NW, lds, stream>>>(a);
 }
 
+// Column blocks on the grid's y axis: from the host's max_q_len hint (at
+// most 65535; a longer chunk's remaining columns go to the last block's loop)
 template <int D, int NT>
-static hipError_t launch_prefill_t(const PrefillArgs& a, int num_seqs, int max_q_len, int fmt, hipStream_t stream) {
+static int64_t prefill_grid_y(int grp, int max_q_len) {
+  const int64_t cols = (int64_t)(max_q_len > 0 ? max_q_len : 1) * grp;
+  const int64_t per_wg = PrefillGeo<D>::NW * 16 * NT;
+  const int64_t gy = (cols + per_wg - 1) / per_wg;
+  return gy > 65535 ? 65535 : gy;
+}
+
+template <int D, int NT>
+static hipError_t launch_prefill_t(const PrefillArgs& a, int num_seqs, int max_q_len, int fmt, int extra_slices,
+                                   hipStream_t stream) {
   // max_q_len only sizes the grid: workgroups loop over the column tiles of
   // the actual chunk lengths, so any hint (even 0) gives every row
-  const int64_t cols = (int64_t)(max_q_len > 0 ? max_q_len : 1) * a.grp;
-  const int64_t per_wg = PrefillGeo<D>::NW * 16 * NT;
-  // column blocks on the grid's y axis (at most 65535; a longer chunk's
-  // remaining columns go to the last block's loop)
-  int64_t gy = (cols + per_wg - 1) / per_wg;
-  gy = gy > 65535 ? 65535 : gy;
-  const dim3 grid((unsigned)a.pool.hkv, (unsigned)gy, (unsigned)num_seqs);
+  const int64_t gy = prefill_grid_y<D, NT>(a.grp, max_q_len);
+  const unsigned gz = (unsigned)num_seqs + (a.plan != nullptr ? (unsigned)extra_slices : 0u);
+  const dim3 grid((unsigned)a.pool.hkv, (unsigned)gy, gz);
   if (fmt == kFp8E4M3 || fmt == kFp8E5M2) {
     // FP8 rows are copied in 16-byte chunks whatever their stride
     if (fmt == kFp8E4M3)
@@ -1434,11 +1839,42 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, int num_seqs, int max_q
   return hipGetLastError();
 }
 
+// Workgroups per CU the prefill kernel holds (LDS and register budget):
+// head size 256 one 8-wave workgroup, 128 three 4-wave ones, 64 two. The key
+// split's plan sizes its parts for that many slots, and its workspace holds
+// two part records per slot.
+static int prefill_wg_per_cu(int head_size) { return head_size == 256 ? 1 : head_size == 128 ? 3 : 2; }
+
+static int64_t prefill_slots(int head_size) { return (int64_t)prefill_wg_per_cu(head_size) * device_cus(); }
+
+// slices: B ranks plus at most 2 B extra parts
+constexpr int64_t kPrefillPlanBytes = 3 * (int64_t)kPrefillSplitSeqsMax * sizeof(PrefillPlanRow);
+
+static int64_t prefill_counter_bytes(int head_size) { return ((prefill_slots(head_size) * 4 + 255) / 256) * 256; }
+
+static int64_t prefill_part_bytes(int head_size) {
+  switch (head_size) {
+    case 64: return PrefillPartGeo<64>::BYTES;
+    case 128: return PrefillPartGeo<128>::BYTES;
+    case 256: return PrefillPartGeo<256>::BYTES;
+    default: return 0;
+  }
+}
+
+// Workspace: [plan slices of 3 kPrefillSplitSeqsMax][arrival counters, one
+// per slot][part records, two per slot]. Cut jobs have at least two parts,
+// so the counters cover every cut job the records allow.
+size_t prefill_workspace_bytes(int head_size) {
+  const int64_t part = prefill_part_bytes(head_size);
+  if (part == 0) return 0;
+  return (size_t)(kPrefillPlanBytes + prefill_counter_bytes(head_size) + 2 * prefill_slots(head_size) * part);
+}
+
 hipError_t launch_prefill(const Pool& pool, int head_size, const void* q, int64_t q_st, int64_t q_sh,
                           int num_q_heads, const int32_t* cu_q, int32_t max_q_len, int32_t total_q,
                           const int32_t* block_table, int32_t max_blocks, const int32_t* seq_lens,
                           int32_t num_seqs, int32_t max_seq_len, const float* k_scale, const float* v_scale,
-                          float sm_scale, int causal, const float* o_scale, void* out, int fmt,
+                          float sm_scale, int causal, const float* o_scale, void* out, int fmt, void* workspace,
                           hipStream_t stream) {
   (void)max_seq_len;
   if (num_seqs == 0 || total_q <= 0) return hipSuccess;
@@ -1463,10 +1899,43 @@ hipError_t launch_prefill(const Pool& pool, int head_size, const void* q, int64_
   a.o_scale = o_scale;
   a.num_seqs = num_seqs;
   a.longest_first = (num_seqs > 1 && num_seqs <= kPrefillRankMax) ? 1 : 0;
+  a.plan = nullptr;
+  a.ws_cnt = nullptr;
+  a.ws_part = nullptr;
+  int extra = 0;
+  if (workspace != nullptr) {
+    // the key split: the plan first (one workgroup), then the grid with
+    // kPrefillParts part slots per sequence
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    PrefillPlanRow* plan = reinterpret_cast<PrefillPlanRow*>(ws);
+    a.ws_cnt = reinterpret_cast<uint32_t*>(ws + kPrefillPlanBytes);
+    a.ws_part = reinterpret_cast<float*>(ws + kPrefillPlanBytes + prefill_counter_bytes(head_size));
+    const int slots = (int)prefill_slots(head_size);
+    const int rec_cap = 2 * slots;
+    // extra slices: a cut rank of gy column blocks takes at least 2 gy hkv
+    // records per extra part, so rec_cap / (gy hkv) extra slices cover the
+    // records' worth (the plan keeps within it; at most 2 per sequence)
+    int64_t gy = head_size == 64    ? prefill_grid_y<64, PrefillGeo<64>::NT>(a.grp, max_q_len)
+                 : head_size == 128 ? prefill_grid_y<128, PrefillGeo<128>::NT>(a.grp, max_q_len)
+                                    : prefill_grid_y<256, PrefillGeo<256>::NT>(a.grp, max_q_len);
+    int64_t x = rec_cap / (gy * pool.hkv);
+    x = x < 1 ? 1 : (x > 2 * (int64_t)num_seqs ? 2 * (int64_t)num_seqs : x);
+    extra = (int)x;
+    const size_t plds = prefill_plan_lds_bytes(num_seqs);
+    switch (head_size) {
+      case 64: prefill_plan_kernel<64><<<1, kPlanThreads, plds, stream>>>(a, plan, slots, rec_cap, extra); break;
+      case 128: prefill_plan_kernel<128><<<1, kPlanThreads, plds, stream>>>(a, plan, slots, rec_cap, extra); break;
+      case 256: prefill_plan_kernel<256><<<1, kPlanThreads, plds, stream>>>(a, plan, slots, rec_cap, extra); break;
+      default: return hipErrorInvalidValue;
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    a.plan = plan;
+  }
   switch (head_size) {
-    case 64: return launch_prefill_t<64, PrefillGeo<64>::NT>(a, num_seqs, max_q_len, fmt, stream);
-    case 128: return launch_prefill_t<128, PrefillGeo<128>::NT>(a, num_seqs, max_q_len, fmt, stream);
-    case 256: return launch_prefill_t<256, PrefillGeo<256>::NT>(a, num_seqs, max_q_len, fmt, stream);
+    case 64: return launch_prefill_t<64, PrefillGeo<64>::NT>(a, num_seqs, max_q_len, fmt, extra, stream);
+    case 128: return launch_prefill_t<128, PrefillGeo<128>::NT>(a, num_seqs, max_q_len, fmt, extra, stream);
+    case 256: return launch_prefill_t<256, PrefillGeo<256>::NT>(a, num_seqs, max_q_len, fmt, extra, stream);
     default: return hipErrorInvalidValue;
   }
 }

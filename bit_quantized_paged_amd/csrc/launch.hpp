@@ -80,6 +80,14 @@ hipError_t launch_prefill(const Pool& pool, int head_size, const void* q, int64_
                           int num_q_heads, const int32_t* cu_q, int32_t max_q_len, int32_t total_q,
                           const int32_t* block_table, int32_t max_blocks, const int32_t* seq_lens,
                           int32_t num_seqs, int32_t max_seq_len, const float* k_scale, const float* v_scale,
-                          float sm_scale, int causal, const float* o_scale, void* out, int fmt, hipStream_t stream);
+                          float sm_scale, int causal, const float* o_scale, void* out, int fmt, void* workspace,
+                          hipStream_t stream);
+
+// Workspace bytes of the key-split prefill on the current device (0 for a
+// head size the library does not build).
+size_t prefill_workspace_bytes(int head_size);
+
+// Sequences a key-split prefill launch takes at most.
+constexpr int kPrefillSplitSeqsMax = 4096;
 
 }  // namespace nvfp4kv

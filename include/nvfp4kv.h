@@ -299,6 +299,14 @@ nvfp4kv_status nvfp4_paged_attention_decode_fp8(const nvfp4kv_cache* cache,
 nvfp4kv_status nvfp4_fp8_to_bf16(const void* in, int64_t n, const float* o_scale, void* out, void* stream);
 
 /*
+ * Workspace (bytes) that nvfp4_paged_attention_prefill (and _fp8) needs for
+ * the key split on the current device: arrival counters and two part
+ * records for each workgroup the device holds at once. It depends only on
+ * the device and head_size (0 for a head size the library does not build).
+ */
+size_t nvfp4_paged_attention_prefill_workspace_size(int32_t head_size);
+
+/*
  * Chunked-prefill attention over the quantised pages [P40177
  * "Implementation breakdown" 1 and 3]. Sequence b has q_b = cu_seqlens_q[b+1]
  * - cu_seqlens_q[b] new query tokens, the last q_b of its seq_lens[b]
@@ -313,7 +321,19 @@ nvfp4kv_status nvfp4_fp8_to_bf16(const void* in, int64_t n, const float* o_scale
  *   (workgroups loop over the column tiles of the actual q_b, so a wrong
  *   value, even 0, costs speed, not correctness); rows past total_q are
  *   neither read nor written. out: bf16 [total_q, num_q_heads,
- *   head_size] contiguous. The workspace arguments are reserved: pass NULL, 0.
+ *   head_size] contiguous.
+ * workspace: NULL (workspace_bytes 0) runs one workgroup per (sequence,
+ *   column block of the chunk, kv head), each over all the keys its
+ *   columns see. Otherwise device scratch of at least
+ *   nvfp4_paged_attention_prefill_workspace_size(head_size) bytes, 256-byte
+ *   aligned, ZERO-FILLED before its first use, with num_seqs <= 4096: the
+ *   launch then has one workgroup per resident slot, each taking an equal
+ *   share of all the jobs' 32-key steps, and a job cut between workgroups
+ *   is merged by its last part to finish (its arrival counter, in the
+ *   workspace, is left at zero again, so one zero fill suffices). Calls that
+ *   share a workspace must be ordered on one stream. Both forms are
+ *   deterministic and agree within the attention tolerance; their bits may
+ *   differ. A bad workspace argument returns NVFP4KV_INVALID_ARGUMENT.
  */
 nvfp4kv_status nvfp4_paged_attention_prefill(const nvfp4kv_cache* cache,
                                              const void* q, int64_t q_stride_token, int64_t q_stride_head,

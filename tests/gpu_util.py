@@ -72,15 +72,24 @@ class Dev:
                                    self.sm_scale, out, ws)
         return out
 
-    def prefill(self, causal=True, o_scale=None):
-        """bf16 output, or FP8-E4M3 codes (uint8) with an output scale."""
+    def prefill_ws(self):
+        """A zero-filled key-split workspace for this head size (one per Dev)."""
+        if getattr(self, "_pws", None) is None:
+            self._pws = torch.zeros(nvk.prefill_workspace_size(self.w.head_size), dtype=torch.uint8,
+                                    device=self.query.device)
+        return self._pws
+
+    def prefill(self, causal=True, o_scale=None, split=False):
+        """bf16 output, or FP8-E4M3 codes (uint8) with an output scale; with
+        split, through the key split (the Dev's workspace)."""
         w = self.w
         out = torch.empty((int(w.cu_q[-1]), w.num_q_heads, w.head_size),
                           dtype=torch.bfloat16 if o_scale is None else torch.uint8, device=self.query.device)
         os_t = None if o_scale is None else torch.tensor([o_scale], dtype=torch.float32, device=self.query.device)
         nvk.paged_attention_prefill(self.pool, self.query, self.cu_q, int(w.q_lens.max(initial=0)), self.bt,
                                     self.seq_lens, int(w.seq_lens.max(initial=0)), self.k_scale, self.v_scale,
-                                    self.sm_scale, out, causal=causal, o_scale=os_t)
+                                    self.sm_scale, out, causal=causal, o_scale=os_t,
+                                    workspace=self.prefill_ws() if split else None)
         return out
 
     def dequant(self):

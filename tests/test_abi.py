@@ -115,6 +115,25 @@ def test_prefill_and_dequant_validation():
     assert r == 1
 
 
+def test_prefill_workspace_validation():
+    """The key split's workspace is checked on the host before any launch: a
+    size without a pointer, a pointer not 256-byte aligned, one below the size
+    query, or more than 4096 sequences with a workspace are argument errors;
+    the size query answers 0 for a head size the library does not build."""
+    lib = nvk.library()
+    d = _desc()
+    need = lib.nvfp4_paged_attention_prefill_workspace_size(128)
+    assert need > 0 and lib.nvfp4_paged_attention_prefill_workspace_size(96) == 0
+
+    def call(ws, nbytes, B=1):
+        return lib.nvfp4_paged_attention_prefill(ctypes.byref(d), 4096, 1024, 128, 8, 128, 16, 16, 64, 4, 96, B, 64,
+                                                 32, 48, 0.1, 1, 8192, ws, nbytes, None)
+    assert call(None, 5) == 1
+    assert call(4096 + 16, need) == 1
+    assert call(4096, need - 1) == 1
+    assert call(4096, need, B=4097) == 1
+
+
 def test_decode_plan_rejects_bad_sizes():
     """The plan query validates its sizes on the host (no device needed for
     these paths)."""

@@ -195,18 +195,36 @@ PREFILL_CASES = {
 }
 
 
+@pytest.mark.parametrize("split", [False, True], ids=["grid", "split"])
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("kv", KV)
 @pytest.mark.parametrize("name", sorted(PREFILL_CASES))
-def test_fp8_prefill_parity(name, kv, causal):
+def test_fp8_prefill_parity(name, kv, causal, split):
     w = _fp8(PREFILL_CASES[name](), kv)
     d = Dev(w, "NHD" if causal else "HND", kv_dtype=kv)
     d.append_all()
-    out = d.prefill(causal=causal)
+    out = d.prefill(causal=causal, split=split)
     torch.cuda.synchronize()
     ref = O.paged_attention(oracle_pool(w, kv), w.query, w.cu_q, w.block_table, w.seq_lens, w.k_scale, w.v_scale,
                             np.float32(d.sm_scale), w.head_size, causal=causal, kv_dtype=kv)
-    assert_attn_close(out, ref, f"{name}/{kv}/causal={causal} prefill")
+    assert_attn_close(out, ref, f"{name}/{kv}/causal={causal} split={split} prefill")
+
+
+@pytest.mark.parametrize("kv", KV)
+def test_fp8_prefill_split_long(kv):
+    """An FP8 cache through the key split with jobs long enough to be cut
+    (the part records hold the same state as for NVFP4)."""
+    w = _fp8(make_workload(seed=31, name="x", seq_lens=[3000, 900, 40], q_lens=[64, 30, 40], num_q_heads=8,
+                           num_kv_heads=2, head_size=128, block_size=16), kv)
+    d = Dev(w, "HND", kv_dtype=kv)
+    d.append_all()
+    out = d.prefill(split=True)
+    torch.cuda.synchronize()
+    parts = d.prefill_ws()[:w.num_seqs * 32].view(torch.int32).view(-1, 8)[:, 1]
+    assert int(parts.max()) > 1, "no rank was cut"
+    ref = O.paged_attention(oracle_pool(w, kv), w.query, w.cu_q, w.block_table, w.seq_lens, w.k_scale, w.v_scale,
+                            np.float32(d.sm_scale), w.head_size, kv_dtype=kv)
+    assert_attn_close(out, ref, f"{kv} split prefill")
 
 
 @pytest.mark.parametrize("kv", KV)

@@ -58,9 +58,10 @@ def run_like_bench(w, dev):
     if len(pre_idx):
         wp = w.subset(pre_idx)
         outp = torch.empty((int(wp.cu_q[-1]), Hq, D), dtype=torch.bfloat16, device=dev)
+        wsp = torch.zeros(nvk.prefill_workspace_size(D), dtype=torch.uint8, device=dev)  # key split, as timed
         nvk.paged_attention_prefill(pool, bf16_dev(wp.query, dev), i32_dev(wp.cu_q, dev), int(wp.q_lens.max()),
                                     i32_dev(wp.block_table, dev), i32_dev(wp.seq_lens, dev), int(wp.seq_lens.max()),
-                                    ks, vs, sm, outp)
+                                    ks, vs, sm, outp, workspace=wsp)
     torch.cuda.synchronize()
     return pool, dec_idx, outd, pre_idx, wp, outp
 

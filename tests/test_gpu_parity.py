@@ -99,17 +99,21 @@ def test_decode_parity(case, layout):
     assert_attn_close(out, ref, f"{name}/{layout} decode")
 
 
+@pytest.mark.parametrize("split", [False, True], ids=["grid", "split"])
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("layout", ["HND", "NHD"])
-def test_prefill_parity(case, causal, layout):
+def test_prefill_parity(case, causal, layout, split):
+    """Both prefill launch forms: one workgroup per job, and the key split
+    (at these sizes every workgroup's share is the 16-step minimum, so the
+    share boundaries cut jobs of all lengths into parts)."""
     name, w, ref_pool = case
     d = Dev(w, layout)
     d.append_all()
-    out = d.prefill(causal=causal)
+    out = d.prefill(causal=causal, split=split)
     torch.cuda.synchronize()
     ref = O.paged_attention(ref_pool, w.query, w.cu_q, w.block_table, w.seq_lens, w.k_scale, w.v_scale,
                             np.float32(d.sm_scale), w.head_size, causal=causal)
-    assert_attn_close(out, ref, f"{name} {layout} prefill causal={causal}")
+    assert_attn_close(out, ref, f"{name} {layout} prefill causal={causal} split={split}")
 
 
 def test_decode_equals_prefill_with_one_query(case):
@@ -701,9 +705,10 @@ def test_decode_from_concurrent_host_threads():
     assert not errors, errors[:4]
 
 
+@pytest.mark.parametrize("split", [False, True], ids=["grid", "split"])
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("head_size,num_q_heads,num_kv_heads", [(64, 4, 2), (128, 8, 2), (256, 16, 2)])
-def test_prefill_edge_shapes(head_size, num_q_heads, num_kv_heads, causal):
+def test_prefill_edge_shapes(head_size, num_q_heads, num_kv_heads, causal, split):
     """The prefill pipeline at its edges, at every head size (two operand
     buffers below 256, three with the deferred PV product at 256): chunks
     with no rows and with one key, keys one below, at and above a 32-key
@@ -716,8 +721,153 @@ def test_prefill_edge_shapes(head_size, num_q_heads, num_kv_heads, causal):
                       num_kv_heads=num_kv_heads, head_size=head_size, block_size=16)
     d = Dev(w, "HND")
     d.append_all()
-    out = d.prefill(causal=causal)
+    out = d.prefill(causal=causal, split=split)
     torch.cuda.synchronize()
     ref = O.paged_attention(oracle_pool(w), w.query, w.cu_q, w.block_table, w.seq_lens, w.k_scale, w.v_scale,
                             np.float32(d.sm_scale), head_size, causal=causal)
-    assert_attn_close(out, ref, f"prefill edges D={head_size} causal={causal}")
+    assert_attn_close(out, ref, f"prefill edges D={head_size} causal={causal} split={split}")
+
+
+PLAN_SLICES = 3 * 4096  # plan slices at the workspace's start (32 bytes each)
+PARTS_MAX, MIN_PART = 3, 32
+KCOLS = {64: 256, 128: 128, 256: 128}  # query columns per workgroup
+
+
+def _slots(D):
+    """Workgroups the prefill kernel holds at once: 2, 3, 1 per CU at head size 64, 128, 256."""
+    return {64: 2, 128: 3, 256: 1}[D] * torch.cuda.get_device_properties(0).multi_processor_count
+
+
+def _prefill_layout(D):
+    """(counter offset, counter bytes, record offset, record bytes) of the key
+    split's workspace: the plan slices, one arrival counter per slot (padded
+    to 256), two part records per slot (lane-major accumulator quads, then the
+    lanes' (max, sum) pairs). Checked against the library's size query."""
+    nw, nt = {64: (4, 4), 128: (4, 2), 256: (8, 1)}[D]
+    g = _slots(D)
+    cnt = (4 * g + 255) // 256 * 256
+    part = nw * nt * (D // 16) * 64 * 16 + nw * nt * 64 * 8
+    assert nvk.prefill_workspace_size(D) == PLAN_SLICES * 32 + cnt + 2 * g * part
+    return PLAN_SLICES * 32, cnt, PLAN_SLICES * 32 + cnt, part
+
+
+def _prefill_counters_zero(d):
+    """The key split's arrival counters are all zero again after a call."""
+    off, n, _, _ = _prefill_layout(d.w.head_size)
+    cnt = d.prefill_ws()[off:off + n].view(torch.int32)
+    assert int(torch.count_nonzero(cnt)) == 0
+
+
+def expected_plan(w, D, causal, max_q_len):
+    """The key split's plan, restated from its rule. Ranks longest first (ties
+    in index order; index order above 256 sequences). Per rank its work R_r
+    (32-key steps of all its jobs, a job that sees no key counting one) and
+    longest job n_r; parts P_r = min(3, ceil(n_r / max(32, ceil(2 R / (3
+    slots))))), R the work of ranks r .. last. The grid has B + X slices, X =
+    clamp(2 slots // (gy hkv), 1, 2 B) with gy the column blocks of the
+    max_q_len hint; ranks are cut only while the cut tail's part records fit
+    two per slot and its extra slices fit X. Slices: each rank's P_r parts in
+    rank order, then empty ones. Rows (seq, parts, part, rec_base, cnt_base)."""
+    B, grp, hkv = w.num_seqs, w.num_q_heads // w.num_kv_heads, w.num_kv_heads
+    kcols = KCOLS[D]
+    lens = [int(x) for x in w.seq_lens]
+    order = sorted(range(B), key=lambda b: (-lens[b], b)) if 1 < B <= 256 else list(range(B))
+    rows = []
+    for b in order:
+        q, L = int(w.q_lens[b]), lens[b]
+        nblk = -(-q * grp // kcols)
+        steps = []
+        for cb in range(nblk):
+            last = min((cb + 1) * kcols, q * grp) - 1
+            kmax = min(L, L - q + last // grp + 1) if causal else L
+            steps.append(max(1, -(-max(kmax, 0) // 32)))
+        rows.append([b, sum(steps) * hkv, max(steps, default=0), nblk])
+    slots = _slots(D)
+    gy = min(-(-max(max_q_len, 1) * grp // kcols), 65535)
+    x = min(max(2 * slots // (gy * hkv), 1), 2 * B)
+    rest = sum(r[1] for r in rows)
+    P = []
+    for b, work, nmax, nblk in rows:
+        part = max(MIN_PART, -(-2 * rest // (3 * slots)))
+        P.append(min(PARTS_MAX, max(1, -(-nmax // part))))
+        rest -= work
+    rec = [nblk * hkv * p if p > 1 else 0 for (b, _, _, nblk), p in zip(rows, P)]
+    ext = [p - 1 for p in P]
+    tail_rec = tail_ext = 0
+    for i in reversed(range(len(rows))):
+        tail_rec += rec[i]
+        tail_ext += ext[i]
+        if tail_rec > 2 * slots or tail_ext > x:
+            P[i] = 1
+    out, rb, cbase = [], 0, 0
+    for (b, _, _, nblk), p in zip(rows, P):
+        out += [(b, p, k, rb, cbase) for k in range(p)]
+        if p > 1:
+            rb += nblk * hkv * p
+            cbase += nblk * hkv
+    out += [(0, 0, 0, 0, 0)] * (B + x - len(out))
+    return out
+
+
+def _plan_rows(d, n):
+    return [tuple(int(v) for v in r[:5]) for r in d.prefill_ws()[:n * 32].view(torch.int32).view(-1, 8).cpu().numpy()]
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("head_size,num_q_heads,num_kv_heads", [(64, 8, 4), (128, 32, 8), (256, 16, 2)])
+def test_prefill_split_long_sequences(head_size, num_q_heads, num_kv_heads, causal):
+    """Sequences long enough to be cut (jobs above 32 and 64 steps: two and
+    three parts), beside short and one-token chunks: the device's plan rows
+    equal the rule's, and at least one rank is cut; the output matches the
+    oracle; a second call with the same workspace gives the same bits (parts
+    merge in part order) and leaves every arrival counter at zero."""
+    w = make_workload(seed=28, name="x", seq_lens=[4000, 1500, 70, 2200, 1], q_lens=[40, 33, 70, 129, 1],
+                      num_q_heads=num_q_heads, num_kv_heads=num_kv_heads, head_size=head_size, block_size=16)
+    d = Dev(w, "HND")
+    d.append_all()
+    out = d.prefill(causal=causal, split=True)
+    torch.cuda.synchronize()
+    want = expected_plan(w, head_size, causal, int(w.q_lens.max()))
+    assert _plan_rows(d, len(want)) == want
+    assert max(r[1] for r in want) > 1, "no rank was cut"
+    _prefill_counters_zero(d)
+    again = d.prefill(causal=causal, split=True)
+    torch.cuda.synchronize()
+    _prefill_counters_zero(d)
+    assert torch.equal(out.view(torch.int16), again.view(torch.int16)), "split prefill is not deterministic"
+    ref = O.paged_attention(oracle_pool(w), w.query, w.cu_q, w.block_table, w.seq_lens, w.k_scale, w.v_scale,
+                            np.float32(d.sm_scale), head_size, causal=causal)
+    assert_attn_close(out, ref, f"split prefill D={head_size} causal={causal}")
+
+
+def test_prefill_split_fp8_output():
+    """The key split's merged result through the FP8-E4M3 output path."""
+    w = make_workload(seed=29, name="x", seq_lens=[2500, 300], q_lens=[100, 64], num_q_heads=8, num_kv_heads=2,
+                      head_size=128, block_size=16)
+    d = Dev(w, "HND")
+    d.append_all()
+    os = 0.03125
+    codes = d.prefill(o_scale=os, split=True)
+    torch.cuda.synchronize()
+    ref = O.paged_attention(oracle_pool(w), w.query, w.cu_q, w.block_table, w.seq_lens, w.k_scale, w.v_scale,
+                            np.float32(d.sm_scale), 128)
+    _fp8_close(codes, ref, os, "split prefill fp8 out")
+
+
+def test_prefill_split_workspace_errors():
+    """A workspace below the size query, misaligned, or with more than 4096
+    sequences is an argument error, raised before any launch."""
+    w = make_workload(seed=30, name="x", seq_lens=[100], q_lens=[10], num_q_heads=4, num_kv_heads=2,
+                      head_size=128, block_size=16)
+    d = Dev(w, "HND")
+    d.append_all()
+    need = nvk.prefill_workspace_size(128)
+    assert need > 0
+    out = torch.empty((10, 4, 128), dtype=torch.bfloat16, device="cuda")
+    args = (d.pool, d.query, d.cu_q, 10, d.bt, d.seq_lens, 100, d.k_scale, d.v_scale, d.sm_scale, out)
+    small = torch.zeros(need - 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(nvk.NVFP4KVError, match="workspace smaller"):
+        nvk.paged_attention_prefill(*args, workspace=small)
+    big = torch.zeros(need + 512, dtype=torch.uint8, device="cuda")
+    with pytest.raises(nvk.NVFP4KVError, match="256-byte aligned"):
+        nvk.paged_attention_prefill(*args, workspace=big[16:])
