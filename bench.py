@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--workload", default="long_decode", choices=sorted(WORKLOADS))
     ap.add_argument("--copies", type=int, default=0, help="pool copies to rotate (0: enough to exceed the MALL 3x)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill-grid", action="store_true",
+                    help="also time the prefill without the key split (one workgroup per job), as prefill_grid_us")
     ap.add_argument("--no-serving-batch", action="store_true",
                     help="skip the mixed serving batch measured beside the headline workload")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -272,7 +274,8 @@ def run_workload(args, name, full, dev):
     if wp is not None:
         res["prefill_s"] = T.per_call(do_prefill, copies)
         assert torch.equal(outp, ref_p), "graph replay of prefill differs from eager"
-        res["prefill_grid_s"] = T.per_call(do_prefill_grid, copies)
+        if args.prefill_grid:
+            res["prefill_grid_s"] = T.per_call(do_prefill_grid, copies)
         pairs = 0
         for b in range(wp.num_seqs):
             L, q = int(wp.seq_lens[b]), int(wp.q_lens[b])
@@ -483,8 +486,9 @@ def rates(res):
         tf = res["prefill_flops"] / res["prefill_s"] / 1e12
         out.update({"prefill_us": round(res["prefill_s"] * 1e6, 2), "prefill_tflops": round(tf, 2),
                     "prefill_pct_of_mfma_peak": round(100 * tf / MFMA_F16_PEAK_TFLOPS, 2),
-                    "prefill_kernel": "prefill_plan_kernel + prefill_kernel (key split)",
-                    "prefill_grid_us": round(res["prefill_grid_s"] * 1e6, 2)})
+                    "prefill_kernel": "prefill_plan_kernel + prefill_kernel (key split)"})
+        if "prefill_grid_s" in res:
+            out["prefill_grid_us"] = round(res["prefill_grid_s"] * 1e6, 2)
     return out
 
 

@@ -1449,8 +1449,8 @@ __device__ __forceinline__ void prefill_columns(const PrefillArgs& a, uint8_t* r
 // consecutive key ranges, each its own workgroup: grid z runs over slices,
 // the P_r parts of rank 0, then those of rank 1, ..., so a rank's parts run
 // side by side too, and the slices past the last part (the grid holds as
-// many as the records could need) are empty and come last. P_r is guided by the
-// work left: the parts are about max(kPrefillMinPart, 2 R / (3 slots))
+// many as the records could need) are empty and come last. P_r is guided by
+// the work left: the parts are about max(kPrefillMinPart, 2 R / (3 slots))
 // steps, R the steps of ranks r .. last and slots the workgroups the device
 // holds at once, so the long early ranks stay whole and the last rounds are
 // cut fine enough to end together. Cut jobs need part records; when the
@@ -1584,30 +1584,41 @@ __device__ __forceinline__ int64_t wave_incl_scan64(int64_t v) {
   return v;
 }
 
-template <int NW>
-__device__ __forceinline__ int64_t block_excl_scan64(int64_t v, int64_t* s_red, int64_t& total) {
+
+// Block-wide exclusive scans of K int64 values at once (one pair of
+// barriers for all K); also returns the totals. s_red: K * NW int64.
+template <int NW, int K>
+__device__ __forceinline__ void block_excl_scan64x(int64_t (&v)[K], int64_t* s_red, int64_t (&total)[K]) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int64_t incl = wave_incl_scan64(v);
-  if (lane == 63) s_red[w] = incl;
-  __syncthreads();
-  int64_t off = 0;
-  total = 0;
+  int64_t incl[K];
 #pragma unroll
-  for (int k = 0; k < NW; ++k) {
-    const int64_t t = s_red[k];
-    off += (k < w) ? t : 0;
-    total += t;
+  for (int k = 0; k < K; ++k) {
+    incl[k] = wave_incl_scan64(v[k]);
+    if (lane == 63) s_red[k * NW + w] = incl[k];
   }
   __syncthreads();
-  return incl - v + off;
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    int64_t off = 0;
+    total[k] = 0;
+#pragma unroll
+    for (int u = 0; u < NW; ++u) {
+      const int64_t t = s_red[k * NW + u];
+      off += (u < w) ? t : 0;
+      total[k] += t;
+    }
+    v[k] = incl[k] - v[k] + off;
+  }
+  __syncthreads();
 }
 
-// The plan (one workgroup of 1024 threads). LDS: per rank its work (int64),
-// sequence, longest job, column blocks, and the lengths the ranking reads.
-constexpr int kPlanThreads = 1024;
+// The plan (one workgroup of kPlanThreads). LDS: per rank its work (int64),
+// sequence, longest job and column blocks; per sequence its clamped length
+// and chunk length (all loaded in one pass).
+constexpr int kPlanThreads = 256;
 
 __host__ __device__ inline size_t prefill_plan_lds_bytes(int B) {
-  return (size_t)B * 8 + (size_t)B * 4 * 4 + (kPlanThreads / 64) * 8 + 16;
+  return (size_t)B * 8 + (size_t)B * 4 * 5 + 3 * (kPlanThreads / 64) * 8 + 16;
 }
 
 template <int D>
@@ -1620,13 +1631,18 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(PrefillArgs 
   const int hkv = a.pool.hkv;
   int64_t* s_w = reinterpret_cast<int64_t*>(smem);  // [B] work of rank r
   int* s_len = reinterpret_cast<int*>(s_w + B);     // [B] clamped length of sequence b
-  int* s_seq = s_len + B;                           // [B] sequence of rank r
+  int* s_qlen = s_len + B;                          // [B] chunk length of sequence b
+  int* s_seq = s_qlen + B;                          // [B] sequence of rank r
   int* s_nmax = s_seq + B;                          // [B] steps of rank r's longest job
   int* s_nblk = s_nmax + B;                         // [B] column blocks of rank r
-  int64_t* s_red = reinterpret_cast<int64_t*>(s_nblk + B);  // [NWP] (offset 24 B: 8-byte aligned)
+  int64_t* s_red = reinterpret_cast<int64_t*>(s_nblk + B + (B & 1));  // [3 NWP], 8-byte aligned
 
-  const int cap = a.max_blocks * a.pool.bs;
-  for (int t = threadIdx.x; t < B; t += kPlanThreads) s_len[t] = clamp_len(a.seq_lens[t], cap);
+  for (int t = threadIdx.x; t < B; t += kPlanThreads) {
+    int q0, qlen, L;
+    prefill_seq_geom(a, t, q0, qlen, L);
+    s_len[t] = L;
+    s_qlen[t] = qlen;
+  }
   __syncthreads();
   // ranks: longest first, ties in index order (the order prefill_seq_of_rank
   // gives); index order for batches the grid does not rank
@@ -1647,62 +1663,83 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(PrefillArgs 
   const int per = (B + kPlanThreads - 1) / kPlanThreads;
   const int r0 = threadIdx.x * per;
   const int r1 = (r0 + per < B) ? r0 + per : B;
-  int64_t loc = 0;
+  const int grp = a.grp;
+  const int dq = kCols / grp, dr = kCols - (kCols / grp) * grp;  // kCols = dq grp + dr
+  int64_t sc1[1] = {0};
   for (int r = r0; r < r1; ++r) {
-    int q0, qlen, L;
-    prefill_seq_geom(a, s_seq[r], q0, qlen, L);
-    const int nblk = ceil_div(qlen * a.grp, kCols);
+    const int b = s_seq[r];
+    const int L = s_len[b], qlen = s_qlen[b];
+    const int nblk = ceil_div(qlen * grp, kCols);
     int64_t work = 0;
     int nmax = 0;
-    for (int cb = 0; cb < nblk; ++cb) {
-      const int n = max(1, prefill_job_steps<kCols>(a.causal, a.grp, L, qlen, cb * kCols));
-      work += n;
-      nmax = n > nmax ? n : nmax;
+    if (!a.causal || nblk == 0) {
+      nmax = nblk > 0 ? max(1, ceil_div(L, kStep)) : 0;  // every block sees all L keys
+      work = (int64_t)nblk * nmax;
+    } else {
+      // prefill_job_steps of each block without a division per block: the
+      // token of block cb's last column is tq = ((cb + 1) kCols - 1) / grp,
+      // stepped by dq (plus one when the remainder tr carries); the last
+      // block ends at the chunk's last token
+      int tq = (kCols - 1) / grp, tr = (kCols - 1) - ((kCols - 1) / grp) * grp;
+      for (int cb = 0; cb < nblk; ++cb) {
+        const int tok = cb == nblk - 1 ? qlen - 1 : tq;
+        int kmax = L - qlen + tok + 1;
+        kmax = kmax > L ? L : (kmax < 0 ? 0 : kmax);
+        const int n = max(1, (kmax + kStep - 1) / kStep);
+        work += n;
+        nmax = n > nmax ? n : nmax;
+        tq += dq;
+        tr += dr;
+        if (tr >= grp) {
+          tr -= grp;
+          ++tq;
+        }
+      }
     }
     s_w[r] = work * hkv;
     s_nmax[r] = nmax;
     s_nblk[r] = nblk;
-    loc += work * hkv;
+    sc1[0] += work * hkv;
   }
-  int64_t total;
-  int64_t run = block_excl_scan64<NWP>(loc, s_red, total);
+  int64_t total[1];
+  block_excl_scan64x<NWP, 1>(sc1, s_red, total);
+  int64_t run = sc1[0];
   // P_r from the work of ranks r .. last
   constexpr int kPer = kPrefillSplitSeqsMax / kPlanThreads;
   static_assert(kPer * kPlanThreads == kPrefillSplitSeqsMax, "ranks per thread");
   int P[kPer];
-  int64_t rec_loc = 0;
+  int64_t sc2[2] = {0, 0};  // records, extra slices
   for (int r = r0; r < r1; ++r) {
-    const int64_t rest = total - run;  // ranks r .. last
+    const int64_t rest = total[0] - run;  // ranks r .. last
     run += s_w[r];
     int64_t part = (2 * rest + 3 * (int64_t)slots - 1) / (3 * (int64_t)slots);
     part = part < kPrefillMinPart ? kPrefillMinPart : part;
     int pr = (int)((s_nmax[r] + part - 1) / part);
     pr = pr < 1 ? 1 : (pr > kPrefillParts ? kPrefillParts : pr);
     P[r - r0] = pr;
-    rec_loc += pr > 1 ? (int64_t)s_nblk[r] * hkv * pr : 0;
+    sc2[0] += pr > 1 ? (int64_t)s_nblk[r] * hkv * pr : 0;
+    sc2[1] += pr - 1;
   }
   // tail first: a rank is cut only if its records and extra slices and those
   // of every later cut rank fit in rec_cap and extra_cap
-  int64_t ext_loc = 0;
-  for (int r = r0; r < r1; ++r) ext_loc += P[r - r0] - 1;
-  int64_t rec_total, ext_total;
-  int64_t rec_run = block_excl_scan64<NWP>(rec_loc, s_red, rec_total);
-  int64_t ext_run = block_excl_scan64<NWP>(ext_loc, s_red, ext_total);
-  int64_t rec_kept = 0, cnt_kept = 0, ext_kept = 0;
+  int64_t tot2[2];
+  block_excl_scan64x<NWP, 2>(sc2, s_red, tot2);
+  int64_t rec_run = sc2[0], ext_run = sc2[1];
+  int64_t sc3[3] = {0, 0, 0};  // kept records, counters, extra slices
   for (int r = r0; r < r1; ++r) {
     const int64_t rec = P[r - r0] > 1 ? (int64_t)s_nblk[r] * hkv * P[r - r0] : 0;
     const int64_t ext = P[r - r0] - 1;
-    if (rec_total - rec_run > rec_cap || ext_total - ext_run > extra_cap) P[r - r0] = 1;  // ranks r .. last
+    if (tot2[0] - rec_run > rec_cap || tot2[1] - ext_run > extra_cap) P[r - r0] = 1;  // ranks r .. last
     rec_run += rec;
     ext_run += ext;
-    rec_kept += P[r - r0] > 1 ? (int64_t)s_nblk[r] * hkv * P[r - r0] : 0;
-    cnt_kept += P[r - r0] > 1 ? (int64_t)s_nblk[r] * hkv : 0;
-    ext_kept += P[r - r0] - 1;
+    sc3[0] += P[r - r0] > 1 ? (int64_t)s_nblk[r] * hkv * P[r - r0] : 0;
+    sc3[1] += P[r - r0] > 1 ? (int64_t)s_nblk[r] * hkv : 0;
+    sc3[2] += P[r - r0] - 1;
   }
-  int64_t t1, t2, used_extra;
-  int64_t rec_base = block_excl_scan64<NWP>(rec_kept, s_red, t1);
-  int64_t cnt_base = block_excl_scan64<NWP>(cnt_kept, s_red, t2);
-  int64_t z = block_excl_scan64<NWP>(ext_kept, s_red, used_extra) + r0;  // first slice of rank r0
+  int64_t tot3[3];
+  block_excl_scan64x<NWP, 3>(sc3, s_red, tot3);
+  int64_t rec_base = sc3[0], cnt_base = sc3[1];
+  int64_t z = sc3[2] + r0;  // first slice of rank r0
   for (int r = r0; r < r1; ++r) {
     PrefillPlanRow row = {};
     row.seq = s_seq[r];
@@ -1721,7 +1758,7 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(PrefillArgs 
   }
   // the slices past the last part: empty
   const PrefillPlanRow none = {};
-  for (int64_t e = B + used_extra + threadIdx.x; e < (int64_t)B + extra_cap; e += kPlanThreads) plan[e] = none;
+  for (int64_t e = B + tot3[2] + threadIdx.x; e < (int64_t)B + extra_cap; e += kPlanThreads) plan[e] = none;
 }
 
 template <int D, int NT, bool COMPACT, bool FP8OUT, int FMT>
