@@ -840,6 +840,57 @@ def test_prefill_split_long_sequences(head_size, num_q_heads, num_kv_heads, caus
     assert_attn_close(out, ref, f"split prefill D={head_size} causal={causal}")
 
 
+@pytest.mark.parametrize("hint", [0, 1, 37, None])
+def test_prefill_split_any_max_q_len_hint(hint):
+    """The key split with a max_q_len hint of 0, 1, well below the longest
+    chunk, or exact: the grid's column blocks (and so the extra slices) follow
+    the hint, the columns past the grid run whole in part 0 of their rank,
+    and every row matches the oracle; the plan rows match the rule."""
+    w = make_workload(seed=32, name="x", seq_lens=[3000, 90, 2700, 5], q_lens=[200, 90, 333, 1], num_q_heads=8,
+                      num_kv_heads=2, head_size=128, block_size=16)
+    d = Dev(w, "HND")
+    d.append_all()
+    out = torch.full((int(w.cu_q[-1]), 8, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    mq = int(w.q_lens.max()) if hint is None else hint
+    nvk.paged_attention_prefill(d.pool, d.query, d.cu_q, mq, d.bt, d.seq_lens, int(w.seq_lens.max()), d.k_scale,
+                                d.v_scale, d.sm_scale, out, workspace=d.prefill_ws())
+    torch.cuda.synchronize()
+    want = expected_plan(w, 128, True, mq)
+    assert _plan_rows(d, len(want)) == want
+    assert max(r[1] for r in want) > 1, "no rank was cut"
+    _prefill_counters_zero(d)
+    ref = O.paged_attention(oracle_pool(w), w.query, w.cu_q, w.block_table, w.seq_lens, w.k_scale, w.v_scale,
+                            np.float32(d.sm_scale), 128)
+    assert_attn_close(out, ref, f"split prefill with max_q_len hint {mq}")
+
+
+def test_prefill_split_index_order_and_empty_rows():
+    """More than 256 sequences (index order, no ranking) through the key
+    split, with sequences long enough to be cut among chunks of no rows,
+    sequences without keys before their chunk and one-token chunks: plan
+    rows against the rule, every row against the oracle."""
+    rng = np.random.default_rng(33)
+    B = 300
+    lens = rng.integers(1, 120, size=B).astype(np.int32)
+    q = np.minimum(lens, rng.integers(0, 9, size=B)).astype(np.int32)
+    lens[[5, 150, 299]] = [2600, 3100, 2300]
+    q[[5, 150, 299]] = [40, 7, 65]
+    q[[6, 7]] = 0
+    w = make_workload(seed=34, name="x", rng=rng, seq_lens=lens, q_lens=q, num_q_heads=8, num_kv_heads=2,
+                      head_size=128, block_size=16)
+    d = Dev(w, "HND")
+    d.append_all()
+    out = d.prefill(split=True)
+    torch.cuda.synchronize()
+    want = expected_plan(w, 128, True, int(w.q_lens.max()))
+    assert _plan_rows(d, len(want)) == want
+    assert max(r[1] for r in want) > 1, "no rank was cut"
+    _prefill_counters_zero(d)
+    ref = O.paged_attention(oracle_pool(w), w.query, w.cu_q, w.block_table, w.seq_lens, w.k_scale, w.v_scale,
+                            np.float32(d.sm_scale), 128)
+    assert_attn_close(out, ref, f"split prefill of {B} sequences")
+
+
 def test_prefill_split_fp8_output():
     """The key split's merged result through the FP8-E4M3 output path."""
     w = make_workload(seed=29, name="x", seq_lens=[2500, 300], q_lens=[100, 64], num_q_heads=8, num_kv_heads=2,
