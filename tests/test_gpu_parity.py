@@ -323,11 +323,13 @@ def test_decode_graph_replays_match_eager():
         assert torch.equal(tmp, eager)
 
 
-def test_prefill_graph_replays_match_eager():
+@pytest.mark.parametrize("split", [False, True], ids=["grid", "split"])
+def test_prefill_graph_replays_match_eager(split):
     """Chunked prefill with hundreds of workgroups, captured into a HIP graph
     over two pool copies (append then prefill, as the benchmark runs it): every
     replay reproduces the eager result bit for bit, with eager work between
-    replays."""
+    replays. With the key split the graph holds the plan and prefill kernels
+    of both calls on one workspace, whose counters are zero after the replays."""
     import bit_quantized_paged_amd as nvk
     w = make_config(4, scale=0.5)
     cached = w.cached_mask()
@@ -345,7 +347,8 @@ def test_prefill_graph_replays_match_eager():
     def step(r):
         nvk.append(pools[r], kn, vn, sn, d.k_scale, d.v_scale)
         nvk.paged_attention_prefill(pools[r], d.query, d.cu_q, int(w.q_lens.max()), d.bt, d.seq_lens,
-                                    int(w.seq_lens.max()), d.k_scale, d.v_scale, d.sm_scale, outs[r], causal=True)
+                                    int(w.seq_lens.max()), d.k_scale, d.v_scale, d.sm_scale, outs[r], causal=True,
+                                    workspace=d.prefill_ws() if split else None)
 
     step(0)
     step(1)
@@ -369,6 +372,8 @@ def test_prefill_graph_replays_match_eager():
         step(0)
         torch.cuda.synchronize()
         assert torch.equal(outs[0], eager)
+    if split:
+        _prefill_counters_zero(d)
 
 
 def _decode_batch(seed, lens, hq, hkv, D, bs):
