@@ -896,6 +896,31 @@ def test_prefill_split_index_order_and_empty_rows():
     assert_attn_close(out, ref, f"split prefill of {B} sequences")
 
 
+def test_prefill_split_largest_batch():
+    """The key split at its largest batch, 4096 sequences (the plan's LDS and
+    slice table at their largest, index order): short chunks over short
+    contexts and empty chunks, with one long sequence that is cut. Plan rows
+    against the rule, the whole output against the oracle, counters zero."""
+    rng = np.random.default_rng(35)
+    B = 4096
+    lens = rng.integers(1, 65, size=B).astype(np.int32)
+    q = np.minimum(lens, rng.integers(0, 4, size=B)).astype(np.int32)
+    lens[2345], q[2345] = 3000, 40
+    w = make_workload(seed=36, name="x", rng=rng, seq_lens=lens, q_lens=q, num_q_heads=8, num_kv_heads=2,
+                      head_size=128, block_size=16)
+    d = Dev(w, "HND")
+    d.append_all()
+    out = d.prefill(split=True)
+    torch.cuda.synchronize()
+    want = expected_plan(w, 128, True, int(w.q_lens.max()))
+    assert _plan_rows(d, len(want)) == want
+    assert max(r[1] for r in want) > 1, "no rank was cut"
+    _prefill_counters_zero(d)
+    ref = O.paged_attention(oracle_pool(w), w.query, w.cu_q, w.block_table, w.seq_lens, w.k_scale, w.v_scale,
+                            np.float32(d.sm_scale), 128)
+    assert_attn_close(out, ref, f"split prefill of {B} sequences")
+
+
 def test_prefill_split_fp8_output():
     """The key split's merged result through the FP8-E4M3 output path."""
     w = make_workload(seed=29, name="x", seq_lens=[2500, 300], q_lens=[100, 64], num_q_heads=8, num_kv_heads=2,
