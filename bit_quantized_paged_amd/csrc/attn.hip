@@ -1063,7 +1063,7 @@ __device__ __forceinline__ void lds_read_share(ShareRaw<D>& R, const uint8_t* st
     // register budget); the asm keeps the compiler from hoisting them.
     int lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
     asm volatile("" : "+v"(lane));
-    o = lds_lane<D, kNvfp4>(lane & 15, lane >> 4);
+    o = lds_lane<D, kNvfp4>(lane & 15, (lane >> 4) & 3);  // (& 3: a 24-bit multiply suffices)
   }
   const uint32_t s0 = lds_addr(stage);
   // chunk w of quarter j: code word w of the lane's run, block (j D/4 + 8 w) / 16

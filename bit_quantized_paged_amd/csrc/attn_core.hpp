@@ -226,6 +226,28 @@ __device__ __forceinline__ float wave_max_j(float v) {
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __builtin_fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
+// Maxima of scores. fmaxf first quiets signalling NaNs: on values the
+// compiler cannot prove canonical (matrix-unit results, lane swaps) that is
+// two extra v_max per call. Scores are never NaN here (every visible key has
+// finite codes and scales, and hidden keys are set to -inf before any
+// maximum), and for other inputs the raw instructions give fmaxf's value, so
+// the softmax takes them as they are.
+__device__ __forceinline__ float max_raw(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float max3_raw(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float wave_max_j_raw(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = max_raw(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return max_raw(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
 __device__ __forceinline__ float wave_sum_j(float v) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
@@ -398,11 +420,11 @@ struct WaveAttn {
           x[k] = (key <= lim[n]) ? x[k] : -__builtin_inff();
         }
       }
-      float rmx = x[0];
-#pragma unroll
-      for (int k = 1; k < 8; ++k) rmx = __builtin_fmaxf(rmx, x[k]);
-      rmx = wave_max_j(rmx);
-      const float mx = (rmx == -__builtin_inff()) ? rmx : rmx * sf[n];
+      float rmx = max3_raw(x[0], x[1], x[2]);
+      rmx = max3_raw(rmx, x[3], x[4]);
+      rmx = max3_raw(rmx, x[5], x[6]);
+      rmx = wave_max_j_raw(max_raw(rmx, x[7]));
+      const float mx = rmx * sf[n];  // sf > 0: a column with no visible key keeps -inf
       const bool grow = mx > m[n] + kLazyMax;
       if (__builtin_amdgcn_ballot_w64(grow) != 0) {
         const float mnew = grow ? mx : m[n];
