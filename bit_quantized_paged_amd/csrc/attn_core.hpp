@@ -423,10 +423,16 @@ struct WaveAttn {
       float rmx = max3_raw(x[0], x[1], x[2]);
       rmx = max3_raw(rmx, x[3], x[4]);
       rmx = max3_raw(rmx, x[5], x[6]);
-      rmx = wave_max_j_raw(max_raw(rmx, x[7]));
-      const float mx = rmx * sf[n];  // sf > 0: a column with no visible key keeps -inf
-      const bool grow = mx > m[n] + kLazyMax;
-      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      rmx = max_raw(rmx, x[7]);
+      // A column's running max moves only when the step's maximum, scaled,
+      // exceeds it by more than kLazyMax. Scaling by sf > 0 is monotone (also
+      // after rounding), so that holds exactly when it holds for the maximum
+      // of some lane's own scores: each lane tests its own, and the maxima
+      // across the column's lanes are formed only on the rare steps where a
+      // test holds somewhere in the wave (a wave-uniform branch).
+      if (__builtin_amdgcn_ballot_w64(rmx * sf[n] > m[n] + kLazyMax) != 0) {
+        const float mx = wave_max_j_raw(rmx) * sf[n];  // sf > 0: a column with no visible key keeps -inf
+        const bool grow = mx > m[n] + kLazyMax;
         const float mnew = grow ? mx : m[n];
         const float alpha = grow ? __builtin_amdgcn_exp2f(m[n] - mnew) : 1.0f;  // exp2(-inf) = 0
         if constexpr (kMfmaSum) lacc[n] *= alpha;
