@@ -262,7 +262,7 @@ struct WaveAttn {
   float sf[NT];          // per-column factor |sm_scale * g_K| * log2(e) / qscale (> 0)
   int lim[NT];           // last visible key of the column (-1: none)
   f4 acc[NT][G::DPL];    // O^T accumulators
-  float m[NT];           // running max (base-2 scores)
+  float m[NT];           // running max (base-2 scores); -FLT_MAX until the column has a visible key
   // Running sums. With one column tile (decode) they come from the matrix
   // unit: a ones tile times P^T (every entry = the lane's column sum). With
   // several (prefill) the four extra accumulators per tile would cost
@@ -274,7 +274,13 @@ struct WaveAttn {
   __device__ __forceinline__ void init() {
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
-      m[n] = -__builtin_inff();
+      // finite, so that -m is a usable exp2 offset from the first step on:
+      // a hidden score (-inf) still gives exp2(-inf) = 0, and the first
+      // visible one always moves the max (alpha then underflows to 0, as
+      // exp2(-inf) would). Merges weight such an empty state by
+      // exp2(-FLT_MAX - M) = 0, or by 1 when every state is empty, with zero
+      // sums and accumulators either way.
+      m[n] = -3.40282347e38f;
       if constexpr (kMfmaSum) lacc[n] = f4{0.f, 0.f, 0.f, 0.f};
       else l[n] = 0.0f;
 #pragma unroll
@@ -431,17 +437,17 @@ struct WaveAttn {
       // across the column's lanes are formed only on the rare steps where a
       // test holds somewhere in the wave (a wave-uniform branch).
       if (__builtin_amdgcn_ballot_w64(rmx * sf[n] > m[n] + kLazyMax) != 0) {
-        const float mx = wave_max_j_raw(rmx) * sf[n];  // sf > 0: a column with no visible key keeps -inf
+        const float mx = wave_max_j_raw(rmx) * sf[n];  // sf > 0: a column with no visible key has -inf
         const bool grow = mx > m[n] + kLazyMax;
         const float mnew = grow ? mx : m[n];
-        const float alpha = grow ? __builtin_amdgcn_exp2f(m[n] - mnew) : 1.0f;  // exp2(-inf) = 0
+        const float alpha = grow ? __builtin_amdgcn_exp2f(m[n] - mnew) : 1.0f;  // 0 from the initial max
         if constexpr (kMfmaSum) lacc[n] *= alpha;
         else l[n] *= alpha;
 #pragma unroll
         for (int t = 0; t < G::DPL; ++t) acc[n][t] *= alpha;
         m[n] = mnew;
       }
-      const float nmu = (m[n] == -__builtin_inff()) ? 0.0f : -m[n];
+      const float nmu = -m[n];
       // the sum adds exactly the f16 values the PV product uses (dot with
       // (1, 1)), so constant values come back unchanged
       const h2 one = {(_Float16)1.0f, (_Float16)1.0f};
