@@ -1051,20 +1051,12 @@ struct ShareRaw {
 };
 
 template <int D>
-__device__ __forceinline__ void lds_read_share(ShareRaw<D>& R, const uint8_t* stage, LdsLane o, int w) {
+__device__ __forceinline__ void lds_read_share(ShareRaw<D>& R, const uint8_t* stage, const LdsLane& o, int w) {
   static_assert(D == 128 || D == 256, "share reader: head sizes 128 and 256");
   constexpr int FD = D / 2 + D / 16;
   constexpr int SUB = StageGeo<D, true>::SUB;
   static_assert(StageGeo<D, true>::SUB == StageGeo<D, false>::SUB, "subtile size is the copy's");
   static_assert((D == 256 && FD == 144 && SUB == 4608) || (D == 128 && FD == 72 && SUB == 2304), "reader offsets");
-  if constexpr (D == 128) {
-    // The lane offsets are derived here, each step, rather than held in
-    // registers for the whole loop (at this head size the step loop is at its
-    // register budget); the asm keeps the compiler from hoisting them.
-    int lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-    asm volatile("" : "+v"(lane));
-    o = lds_lane<D, kNvfp4>(lane & 15, (lane >> 4) & 3);  // (& 3: a 24-bit multiply suffices)
-  }
   const uint32_t s0 = lds_addr(stage);
   // chunk w of quarter j: code word w of the lane's run, block (j D/4 + 8 w) / 16
   const uint32_t ak = s0 + o.k + 4u * (uint32_t)w, aks = s0 + o.ks + ((uint32_t)w >> 1);
