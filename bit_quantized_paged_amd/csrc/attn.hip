@@ -1351,10 +1351,11 @@ __device__ __forceinline__ void prefill_columns(const PrefillArgs& a, uint8_t* r
     lds_barrier();
     const int kk = k - kbeg;
     if (copier) {
-      // per-lane copy offsets (at head size 128 derived again each step: the
-      // step loop there is at its register budget)
+      // per-lane copy offsets: held for NVFP4 rows in 16-byte copies; in the
+      // other copy forms at head size 128 derived again each step (held, they
+      // would spill: the step loop there is at its register budget)
       int t = threadIdx.x;
-      if constexpr (D == 128) asm volatile("" : "+v"(t));
+      if constexpr (D == 128 && !(COMPACT && FMT == kNvfp4)) asm volatile("" : "+v"(t));
       const DmaOffsets<D, COMPACT, FMT> dof = dma_offsets<D, COMPACT, FMT>(a.pool.st, a.pool.skv, t & 63);
       dma_step<D, COMPACT, FMT>(ring + (kk % NS) * SG::STAGE, a.pool, nxt, h, (k + NS) * kStep, dof);
     }
