@@ -1358,8 +1358,10 @@ __device__ __forceinline__ void prefill_columns(const PrefillArgs& a, uint8_t* r
       if constexpr (D == 128 && !(COMPACT && FMT == kNvfp4)) asm volatile("" : "+v"(t));
       const DmaOffsets<D, COMPACT, FMT> dof = dma_offsets<D, COMPACT, FMT>(a.pool.st, a.pool.skv, t & 63);
       dma_step<D, COMPACT, FMT>(ring + (kk % NS) * SG::STAGE, a.pool, nxt, h, (k + NS) * kStep, dof);
+      // the ids of the copier's next step, read one iteration ahead (the
+      // other waves never use them; the scalar unit is shared by the CU)
+      nxt = ids_for_step(bt_row, k + NS + 1, kend, L, a.max_blocks, a.pool);
     }
-    nxt = ids_for_step(bt_row, k + NS + 1, kend, L, a.max_blocks, a.pool);
     const int kb = k * kStep;
     const bool mine = kb < kw;
     f4 sc[2][NT];

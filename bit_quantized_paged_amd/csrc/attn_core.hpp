@@ -624,6 +624,17 @@ __device__ __forceinline__ void dma_sub(uint8_t* dst, rsrc_t r, const DmaOffsets
   }
 }
 
+// Address of the first K row of a subtile: row row0 of block id (clamped to
+// the pool), kv head h. The clamped block index is below 2^31, so its product
+// with the block stride needs no sign extension, and the row term fits 32
+// bits (row0 < 64 and row strides are below 2^26 by the descriptor checks):
+// fewer scalar instructions per copy than full 64-bit products.
+__device__ __forceinline__ const uint8_t* subtile_base(const Pool& pool, int32_t id, int h, int row0) {
+  const uint32_t blk = (uint32_t)clamp_block(id, pool.num_blocks);
+  return pool.data + (uint64_t)blk * (uint64_t)pool.sb + (int64_t)h * pool.sh +
+         (uint64_t)((uint32_t)row0 * (uint32_t)pool.st);
+}
+
 // Copy the step at kb (ids from step_ids) into the stage at dst.
 template <int D, bool COMPACT, int FMT = kNvfp4>
 __device__ __forceinline__ void dma_step(uint8_t* dst, const Pool& pool, const StepIds& ids, int h, int kb,
@@ -632,9 +643,7 @@ __device__ __forceinline__ void dma_step(uint8_t* dst, const Pool& pool, const S
   const int extent = (int)pool.skv + 15 * (int)pool.st + SG::FD;
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb) {
-    const int row0 = (kb + 16 * sb) & (pool.bs - 1);
-    const int64_t blk = clamp_block(ids.id[sb], pool.num_blocks);
-    const uint8_t* base = pool.data + blk * pool.sb + (int64_t)h * pool.sh + (int64_t)row0 * pool.st;
+    const uint8_t* base = subtile_base(pool, ids.id[sb], h, (kb + 16 * sb) & (pool.bs - 1));
     dma_sub<D, COMPACT, FMT, 0>(dst + sb * SG::SUB, make_rsrc(base, ids.ok[sb] ? extent : 0), o);
   }
 }
