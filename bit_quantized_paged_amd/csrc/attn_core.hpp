@@ -226,27 +226,27 @@ __device__ __forceinline__ float wave_max_j(float v) {
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __builtin_fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
-// Maxima of scores. fmaxf first quiets signalling NaNs: on values the
+// Maxima of scores. fmaxf first quiets signalling NaNs: on operands the
 // compiler cannot prove canonical (matrix-unit results, lane swaps) that is
-// two extra v_max per call. Scores are never NaN here (every visible key has
-// finite codes and scales, and hidden keys are set to -inf before any
-// maximum), and for other inputs the raw instructions give fmaxf's value, so
-// the softmax takes them as they are.
-__device__ __forceinline__ float max_raw(float a, float b) {
-  float r;
-  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-  return r;
+// two extra v_max per call. The median of a, b and +inf is their maximum
+// (v_med3_f32, no quieting), and its result lets the compiler chain further
+// maxima (v_max3_f32) without quieting either. pinf must hold +inf in a
+// register the compiler cannot see into, or it folds the median back into
+// fmaxf. Scores are never NaN here (every visible key has finite codes and
+// scales; hidden keys are set to -inf before any maximum). Written in C, not
+// as assembly, so that the compiler keeps the wait states a vector read of
+// matrix-unit results needs.
+__device__ __forceinline__ float opaque_pinf() {
+  float pinf = __builtin_inff();
+  asm volatile("" : "+s"(pinf));
+  return pinf;
 }
-__device__ __forceinline__ float max3_raw(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
-__device__ __forceinline__ float wave_max_j_raw(float v) {
+__device__ __forceinline__ float max_med3(float a, float b, float pinf) { return __builtin_amdgcn_fmed3f(a, b, pinf); }
+__device__ __forceinline__ float wave_max_j_med3(float v, float pinf) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = max_raw(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  v = max_med3(__uint_as_float(a[0]), __uint_as_float(a[1]), pinf);
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return max_raw(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return max_med3(__uint_as_float(b[0]), __uint_as_float(b[1]), pinf);
 }
 __device__ __forceinline__ float wave_sum_j(float v) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -426,10 +426,10 @@ struct WaveAttn {
           x[k] = (key <= lim[n]) ? x[k] : -__builtin_inff();
         }
       }
-      float rmx = max3_raw(x[0], x[1], x[2]);
-      rmx = max3_raw(rmx, x[3], x[4]);
-      rmx = max3_raw(rmx, x[5], x[6]);
-      rmx = max_raw(rmx, x[7]);
+      const float pinf = opaque_pinf();
+      float rmx = max_med3(x[0], x[1], pinf);
+#pragma unroll
+      for (int k = 2; k < 8; ++k) rmx = __builtin_fmaxf(rmx, x[k]);
       // A column's running max moves only when the step's maximum, scaled,
       // exceeds it by more than kLazyMax. Scaling by sf > 0 is monotone (also
       // after rounding), so that holds exactly when it holds for the maximum
@@ -437,7 +437,7 @@ struct WaveAttn {
       // across the column's lanes are formed only on the rare steps where a
       // test holds somewhere in the wave (a wave-uniform branch).
       if (__builtin_amdgcn_ballot_w64(rmx * sf[n] > m[n] + kLazyMax) != 0) {
-        const float mx = wave_max_j_raw(rmx) * sf[n];  // sf > 0: a column with no visible key has -inf
+        const float mx = wave_max_j_med3(rmx, pinf) * sf[n];  // sf > 0: a column with no visible key has -inf
         const bool grow = mx > m[n] + kLazyMax;
         const float mnew = grow ? mx : m[n];
         const float alpha = grow ? __builtin_amdgcn_exp2f(m[n] - mnew) : 1.0f;  // 0 from the initial max
