@@ -1008,6 +1008,11 @@ struct PrefillStages {
   static_assert(NS >= 2, "the prefill pipeline reads one stage while the next lands");
 };
 
+template <bool B>
+struct SteadyTag {
+  static constexpr bool value = B;
+};
+
 // Waves per prefill workgroup (NW) and 16-column tiles per wave (NT): a
 // workgroup shares the dequantisation of each step among its NW waves and
 // owns NW * 16 * NT query columns. At head size 256 the accumulators of two
@@ -1098,13 +1103,13 @@ __device__ __forceinline__ void lds_read_share(ShareRaw<D>& R, const uint8_t* st
 
 // This wave's share of the step's MFMA operands (NVFP4, head size 128 or
 // 256) from its own raw bytes: the same values make_ops stores.
-template <int D, int NW>
+template <int D, int NW, bool FULL = false>
 __device__ __forceinline__ void prefill_dequant_share(const uint8_t* stage, const LdsLane& ll, int kb, int L, int j,
                                                       int w, uint32_t slot) {
   static_assert(Geo<D>::KW == NW && Geo<D>::DPL == 2 * NW, "share layout");
   ShareRaw<D> R;
   lds_read_share<D>(R, stage, ll, w);
-  if (kb + kStep > L) {
+  if (!FULL && kb + kStep > L) {
     // value rows (codes and scales) of keys >= L read as zeros
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
@@ -1157,15 +1162,16 @@ __device__ __forceinline__ void prefill_dequant_share(const uint8_t* stage, cons
 
 // This wave's share of the MFMA operands of the raw step at `stage` (first
 // key kb), dequantised into the operand buffer whose lane slot is `slot`.
-template <int D, int FMT, int NW>
+// FULL: the caller knows every key of the step is below L.
+template <int D, int FMT, int NW, bool FULL = false>
 __device__ __forceinline__ void prefill_dequant(const uint8_t* stage, const LdsLane& ll, int kb, int L, int j, int w,
                                                 uint32_t slot) {
   if constexpr (FMT == kNvfp4 && (D == 128 || D == 256)) {
-    prefill_dequant_share<D, NW>(stage, ll, kb, L, j, w, slot);
+    prefill_dequant_share<D, NW, FULL>(stage, ll, kb, L, j, w, slot);
   } else {
     SubRaw<D, FMT> R[2];
     lds_read_step<D, FMT>(R, stage, ll);
-    if (kb + kStep > L) mask_step(R, kb, L, j);
+    if (!FULL && kb + kStep > L) mask_step(R, kb, L, j);
     VPairs<D, FMT> vp[2];
     make_pairs(R[0], vp[0]);
     make_pairs(R[1], vp[1]);
@@ -1346,48 +1352,114 @@ __device__ __forceinline__ void prefill_columns(const PrefillArgs& a, uint8_t* r
   bool pv_pending = false;  // wave-uniform: the previous step's PV product is due (deferral only)
   // operand buffers of steps k, k + 1 and (deferral) k - 1
   uint32_t buf_cur = 0, buf_next = OG::BYTES, buf_prev = 2 * OG::BYTES;
-  for (int k = kbeg; k < kend; ++k) {
-    wait_vmcnt<(NS - 2) * SG::NC>();  // the copier: step k + 1 has landed
-    lds_barrier();
-    const int kk = k - kbeg;
-    if (copier) {
-      // per-lane copy offsets: held for NVFP4 rows in 16-byte copies; in the
-      // other copy forms at head size 128 derived again each step (held, they
-      // would spill: the step loop there is at its register budget)
-      int t = threadIdx.x;
-      if constexpr (D == 128 && !(COMPACT && FMT == kNvfp4)) asm volatile("" : "+v"(t));
-      const DmaOffsets<D, COMPACT, FMT> dof = dma_offsets<D, COMPACT, FMT>(a.pool.st, a.pool.skv, t & 63);
-      dma_step<D, COMPACT, FMT>(ring + (kk % NS) * SG::STAGE, a.pool, nxt, h, (k + NS) * kStep, dof);
-      // the ids of the copier's next step, read one iteration ahead (the
-      // other waves never use them; the scalar unit is shared by the CU)
-      nxt = ids_for_step(bt_row, k + NS + 1, kend, L, a.max_blocks, a.pool);
-    }
-    const int kb = k * kStep;
-    const bool mine = kb < kw;
-    f4 sc[2][NT];
-    const bool deq = k + 1 < kend;
-    if (deq_first && deq)
-      prefill_dequant<D, FMT, PrefillGeo<D>::NW>(ring + ((kk + 1) % NS) * SG::STAGE, ll, kb + kStep, L, j, w,
-                                                  op_lane + buf_next);
-    if (mine) prefill_scores(W, op_lane + buf_cur, sc);
-    if (kDefer && pv_pending) prefill_pv(W, op_lane + buf_prev, p);
-    if (!deq_first && deq)
-      prefill_dequant<D, FMT, PrefillGeo<D>::NW>(ring + ((kk + 1) % NS) * SG::STAGE, ll, kb + kStep, L, j, w,
-                                                  op_lane + buf_next);
-    if (mine) {
-      W.softmax(sc, kb, j, kb + kStep > min_full, p);
-      if (!kDefer) prefill_pv(W, op_lane + buf_cur, p);
-    }
-    pv_pending = kDefer && mine;
-    if constexpr (kDefer) {
-      const uint32_t t = buf_prev;
-      buf_prev = buf_cur;
-      buf_cur = buf_next;
-      buf_next = t;
-    } else {
-      const uint32_t t = buf_cur;
-      buf_cur = buf_next;
-      buf_next = t;
+  if constexpr (D != 256) {
+    // Iterations in the middle of the range, where every wave has columns,
+    // step k needs no mask for any of them and a next step is dequantised
+    // (needing none either), run without the branches on these conditions:
+    // every wave of the CU runs those on the one scalar unit they share. The
+    // bound is workgroup-uniform (wave 0's columns are the earliest, so its
+    // first masked key is the lowest).
+    const int wg_min_full = a.causal ? L - qlen + wg_col / grp + 1 : L;
+    const bool all_cols = wg_col + (PrefillGeo<D>::NW - 1) * 16 * NT < ncols;
+    int ks = wg_min_full / kStep;
+    ks = ks < L / kStep - 1 ? ks : L / kStep - 1;
+    ks = ks < kend - 1 ? ks : kend - 1;
+    if (!all_cols) ks = kbeg;
+    auto iteration = [&](const int k, auto steady_tag) {
+      constexpr bool S = decltype(steady_tag)::value;
+      wait_vmcnt<(NS - 2) * SG::NC>();  // the copier: step k + 1 has landed
+      lds_barrier();
+      const int kk = k - kbeg;
+      if (copier) {
+        // per-lane copy offsets: held for NVFP4 rows in 16-byte copies; in the
+        // other copy forms at head size 128 derived again each step (held, they
+        // would spill: the step loop there is at its register budget)
+        int t = threadIdx.x;
+        if constexpr (D == 128 && !(COMPACT && FMT == kNvfp4)) asm volatile("" : "+v"(t));
+        const DmaOffsets<D, COMPACT, FMT> dof = dma_offsets<D, COMPACT, FMT>(a.pool.st, a.pool.skv, t & 63);
+        dma_step<D, COMPACT, FMT>(ring + (kk % NS) * SG::STAGE, a.pool, nxt, h, (k + NS) * kStep, dof);
+        // the ids of the copier's next step, read one iteration ahead (the
+        // other waves never use them; the scalar unit is shared by the CU)
+        nxt = ids_for_step(bt_row, k + NS + 1, kend, L, a.max_blocks, a.pool);
+      }
+      const int kb = k * kStep;
+      const bool mine = S || kb < kw;
+      f4 sc[2][NT];
+      const bool deq = S || k + 1 < kend;
+      if (deq_first && deq)
+        prefill_dequant<D, FMT, PrefillGeo<D>::NW, S>(ring + ((kk + 1) % NS) * SG::STAGE, ll, kb + kStep, L, j, w,
+                                                       op_lane + buf_next);
+      if (mine) prefill_scores(W, op_lane + buf_cur, sc);
+      if (kDefer && (S || pv_pending)) prefill_pv(W, op_lane + buf_prev, p);
+      if (!deq_first && deq)
+        prefill_dequant<D, FMT, PrefillGeo<D>::NW, S>(ring + ((kk + 1) % NS) * SG::STAGE, ll, kb + kStep, L, j, w,
+                                                       op_lane + buf_next);
+      if (mine) {
+        W.softmax(sc, kb, j, !S && kb + kStep > min_full, p);
+        if (!kDefer) prefill_pv(W, op_lane + buf_cur, p);
+      }
+      pv_pending = kDefer && mine;
+      if constexpr (kDefer) {
+        const uint32_t t = buf_prev;
+        buf_prev = buf_cur;
+        buf_cur = buf_next;
+        buf_next = t;
+      } else {
+        const uint32_t t = buf_cur;
+        buf_cur = buf_next;
+        buf_next = t;
+      }
+    };
+    int k = kbeg;
+    for (; k < ks; ++k) iteration(k, SteadyTag<true>{});
+    for (; k < kend; ++k) iteration(k, SteadyTag<false>{});
+  } else {
+    // head size 256: the plain loop (the two-form version above takes this
+    // kernel to the whole register file, with spills, and even in its
+    // general form alone compiles to a slower schedule)
+    for (int k = kbeg; k < kend; ++k) {
+      wait_vmcnt<(NS - 2) * SG::NC>();  // the copier: step k + 1 has landed
+      lds_barrier();
+      const int kk = k - kbeg;
+      if (copier) {
+        // per-lane copy offsets: held for NVFP4 rows in 16-byte copies; in the
+        // other copy forms at head size 128 derived again each step (held, they
+        // would spill: the step loop there is at its register budget)
+        int t = threadIdx.x;
+        if constexpr (D == 128 && !(COMPACT && FMT == kNvfp4)) asm volatile("" : "+v"(t));
+        const DmaOffsets<D, COMPACT, FMT> dof = dma_offsets<D, COMPACT, FMT>(a.pool.st, a.pool.skv, t & 63);
+        dma_step<D, COMPACT, FMT>(ring + (kk % NS) * SG::STAGE, a.pool, nxt, h, (k + NS) * kStep, dof);
+        // the ids of the copier's next step, read one iteration ahead (the
+        // other waves never use them; the scalar unit is shared by the CU)
+        nxt = ids_for_step(bt_row, k + NS + 1, kend, L, a.max_blocks, a.pool);
+      }
+      const int kb = k * kStep;
+      const bool mine = kb < kw;
+      f4 sc[2][NT];
+      const bool deq = k + 1 < kend;
+      if (deq_first && deq)
+        prefill_dequant<D, FMT, PrefillGeo<D>::NW>(ring + ((kk + 1) % NS) * SG::STAGE, ll, kb + kStep, L, j, w,
+                                                    op_lane + buf_next);
+      if (mine) prefill_scores(W, op_lane + buf_cur, sc);
+      if (kDefer && pv_pending) prefill_pv(W, op_lane + buf_prev, p);
+      if (!deq_first && deq)
+        prefill_dequant<D, FMT, PrefillGeo<D>::NW>(ring + ((kk + 1) % NS) * SG::STAGE, ll, kb + kStep, L, j, w,
+                                                    op_lane + buf_next);
+      if (mine) {
+        W.softmax(sc, kb, j, kb + kStep > min_full, p);
+        if (!kDefer) prefill_pv(W, op_lane + buf_cur, p);
+      }
+      pv_pending = kDefer && mine;
+      if constexpr (kDefer) {
+        const uint32_t t = buf_prev;
+        buf_prev = buf_cur;
+        buf_cur = buf_next;
+        buf_next = t;
+      } else {
+        const uint32_t t = buf_cur;
+        buf_cur = buf_next;
+        buf_next = t;
+      }
     }
   }
   if (kDefer && pv_pending) prefill_pv(W, op_lane + buf_prev, p);
