@@ -91,8 +91,8 @@ def exact_decode(wd, sm_scale, dev):
 
 
 def read_traffic(kernel: str, workload: str):
-    """HBM bytes per decode launch from the committed counter summary, if it
-    was taken on the current kernel sources (else None)."""
+    """HBM bytes per launch of a workload's main kernel from the committed
+    counter summary, if it was taken on the current kernel sources (else None)."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.md")
     if not os.path.exists(path):
         return None
@@ -281,6 +281,12 @@ def run_workload(args, name, full, dev):
             L, q = int(wp.seq_lens[b]), int(wp.q_lens[b])
             pairs += q * (L - q) + q * (q + 1) // 2
         res["prefill_flops"] = 4.0 * D * Hq * pairs
+        # every cached row of a prefill sequence once per kv head, the bf16
+        # queries in and outputs out, the block ids and the per-sequence
+        # lengths and offsets (the same accounting as the decode's)
+        res["prefill_bytes"] = (int(wp.seq_lens.astype(np.int64).sum()) * Hkv * 2 * fd
+                                + 2 * int(wp.q_lens.astype(np.int64).sum()) * Hq * D * 2
+                                + 4 * int(np.sum((wp.seq_lens + bs - 1) // bs)) + 4 * (2 * wp.num_seqs + 1))
     if not full:
         return res, extra, w, dec_idx, pre_idx
 
@@ -486,6 +492,7 @@ def rates(res):
         tf = res["prefill_flops"] / res["prefill_s"] / 1e12
         out.update({"prefill_us": round(res["prefill_s"] * 1e6, 2), "prefill_tflops": round(tf, 2),
                     "prefill_pct_of_mfma_peak": round(100 * tf / MFMA_F16_PEAK_TFLOPS, 2),
+                    "prefill_bytes": res["prefill_bytes"],
                     "prefill_kernel": "prefill_plan_kernel + prefill_kernel (key split)"})
         if "prefill_grid_s" in res:
             out["prefill_grid_us"] = round(res["prefill_grid_s"] * 1e6, 2)
@@ -539,7 +546,8 @@ def main():
         out["value"] = r["prefill_tflops"]
         out["unit"] = "TFLOP/s"
         roof = {"bound": "mfma", "achieved": r["prefill_tflops"], "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(r["prefill_tflops"] / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+                "frac": round(r["prefill_tflops"] / MFMA_F16_PEAK_TFLOPS, 4),
+                "traffic": read_traffic("prefill_kernel", res["name"]), "bytes_per_launch": res["prefill_bytes"],
                 "kernel": "prefill_kernel", "flops_per_launch": res["prefill_flops"],
                 "avg_launch_us": round(res["prefill_s"] * 1e6, 3)}
     out["config"] = {"workload": res["name"], "num_seqs": res["B"], "num_q_heads": res["Hq"],
